@@ -1,0 +1,248 @@
+#!/usr/bin/env python3
+"""Benchmark of the TBE hot path on one MI355X: one step = bounds check + forward + backward
+(exact row-wise Adagrad) over one synthetic batch of the skewed large workload (T=32 tables of
+2M x 128 fp16 rows, B=131072, L ~ Poisson(20), Zipf(0.91) over 95000 ranks per table: about
+83.9M lookups, 3.03M unique rows, hottest row about 128K lookups).
+
+Prints one JSON line (metric, value, ..., roofline, cpu_baseline).
+
+  python bench.py [--steps K] [--warmup W] [--config 5] [--no-cpu-baseline]
+  python bench.py --calib-copy      # plain copy kernel of known size (rocprofv3 byte calibration)
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import bwd_tbe_fwd_amd as tbe  # noqa: E402
+import tbe_inputs as ti  # noqa: E402
+
+METRIC = "TBE fwd+bwd lookups/s and achieved HBM GB/s vs peak, 1 MI355X"
+HBM_PEAK_GBS = 8000.0
+KERNELS = ["bounds_offsets", "bounds_indices", "fwd_gather", "fwd_hist", "linearize",
+           "radix_upsweep", "radix_scan", "radix_downsweep", "rle", "classify", "short_run",
+           "grad_accum", "long_apply"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def batch_stats(bt: ti.Batch, threshold=256, chunk=256):
+    """Host-side statistics of the drawn batch (from the inputs only)."""
+    idx = bt.indices.cpu().numpy().astype(np.int64)
+    off = bt.offsets.cpu().numpy().astype(np.int64)
+    B = bt.B
+    U = 0
+    short_lookups = 0
+    short_runs = 0
+    long_lookups = 0
+    long_runs = 0
+    chunks = 0
+    hottest = 0
+    for t in range(bt.T):
+        c = np.bincount(idx[off[t * B]:off[(t + 1) * B]], minlength=bt.E[t])
+        c = c[c > 0]
+        U += c.size
+        hottest = max(hottest, int(c.max()) if c.size else 0)
+        lg = c >= threshold
+        long_runs += int(lg.sum())
+        long_lookups += int(c[lg].sum())
+        short_runs += int((~lg).sum())
+        short_lookups += int(c[~lg].sum())
+        chunks += int(((c[lg] + chunk - 1) // chunk).sum())
+    return dict(N=int(idx.size), TB=bt.T * B, U=U, hottest=hottest, short_runs=short_runs,
+                short_lookups=short_lookups, long_runs=long_runs, long_lookups=long_lookups,
+                chunks=chunks)
+
+
+def algorithmic_bytes(bt: ti.Batch, st: dict, passes: int):
+    """What each kernel must move per launch (no credit for cache reuse)."""
+    s_w = bt.weights.element_size()
+    s_i = bt.indices.element_size()
+    s_o = bt.offsets.element_size()
+    D = bt.D[0]
+    N, TB, U = st["N"], st["TB"], st["U"]
+    return {
+        # per lookup: index + row; per bag: offset + output row
+        "fwd_gather": N * (s_i + D * s_w) + TB * (s_o + D * 4),
+        # per lookup: index read, key + payload written; per bag: offset
+        "linearize": N * (s_i + 8) + TB * s_o,
+        # per pass: keys + payloads read and written
+        "radix_downsweep": N * 16,
+        "radix_upsweep": N * 4,
+        # per lookup of a short run: payload + fp32 gradient row; per short run: descriptor,
+        # weight row read + write, Adagrad state read + write
+        "short_run": st["short_lookups"] * (4 + D * 4) + st["short_runs"] * (16 + 2 * D * s_w + 8),
+        # per lookup of a long run: payload + gradient row; per chunk: partial row written
+        "grad_accum": st["long_lookups"] * (4 + D * 4) + st["chunks"] * (8 + D * 4),
+        # per chunk: partial row read; per long run: descriptor, weight row r/w, state r/w
+        "long_apply": st["chunks"] * D * 4 + st["long_runs"] * (20 + 2 * D * s_w + 8),
+        "bounds_indices": N * s_i,
+        "bounds_offsets": 3 * (TB + 1) * s_o,
+        "rle": 3 * N * 4 + U * 8,
+        "classify": U * 8 + U * 16,
+    }
+
+
+def calib_copy():
+    """A plain device copy of known size, for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE."""
+    n = 1 << 30  # 4 GiB of fp32
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calib_copy_bytes_read": n * 4, "calib_copy_bytes_written": n * 4,
+                      "launches": 3}))
+
+
+def cpu_baseline(spec: ti.BatchSpec, seed: int):
+    """The CPU oracle, single-threaded, on a bounded sample of the same workload: 2 of the 32
+    tables with every bag (same B, L and Zipf recipe).  Returns lookups/s of forward+backward."""
+    import oracle
+    sample = ti.scaled(spec, T=2, name_suffix=" (2-table sample)")
+    bt = ti.make_batch(sample, seed, device="cuda")
+    a = dict(E=np.array(bt.E), D=np.array(bt.D), W=bt.weights.double().cpu().numpy(),
+             idx=bt.indices.long().cpu().numpy(), off=bt.offsets.long().cpu().numpy(),
+             grad=bt.grad_out.double().cpu().numpy(), mom=bt.momentum.double().cpu().numpy())
+    del bt
+    torch.cuda.empty_cache()
+    t0 = time.perf_counter()
+    oracle.forward(sample.T, sample.B, a["E"], a["D"], a["W"], a["idx"], a["off"])
+    oracle.backward(sample.T, sample.B, a["E"], a["D"], oracle.F16, a["W"], a["idx"], a["off"], None,
+                    a["grad"], oracle.ROWWISE_ADAGRAD, oracle.f32_literal(spec.lr),
+                    oracle.f32_literal(spec.eps), a["mom"])
+    dt = time.perf_counter() - t0
+    n = int(a["idx"].size)
+    return {"value": n / dt, "unit": "lookups/s", "cores": 1, "kind": "oracle",
+            "sample": f"2 of 32 tables, all {sample.B} bags: {n} lookups, forward + transpose + "
+                      f"row-wise Adagrad backward in fp64, single thread, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-bounds", action="store_true", help="leave the bounds check out of the step")
+    ap.add_argument("--calib-copy", action="store_true")
+    ap.add_argument("--breakdown", action="store_true", help="time every kernel once (extra steps)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if args.calib_copy:
+        calib_copy()
+        return
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    spec = ti.CONFIGS[args.config]
+    seed = ti.config_seed(args.config)
+    t0 = time.perf_counter()
+    bt = ti.make_batch(spec, seed, device=dev)
+    torch.cuda.synchronize()
+    log(f"generated {spec.name}: {bt.num_indices} lookups in {time.perf_counter() - t0:.1f} s")
+    st = batch_stats(bt)
+    log(f"batch: {st}")
+    tables = tbe.Tables(bt.E, bt.D, bt.B, bt.w_dtype, device=dev, pooling_hint=spec.pooling_hint)
+    out = torch.empty(bt.B, sum(bt.D), dtype=torch.float32, device=dev)
+    weighted = bt.psw is not None
+    ws = tbe.workspace(tbe.tbe_backward_workspace_bytes(tables, bt.num_indices, weighted), dev)
+    bws = tbe.workspace(tbe.tbe_bounds_check_workspace_bytes(tables), dev)
+    counts = torch.zeros(2, dtype=torch.int64, device=dev)
+    lr, eps = float(np.float32(spec.lr)), float(np.float32(spec.eps))
+    if bt.momentum is None:
+        bt.momentum = torch.zeros(sum(bt.E), dtype=torch.float32, device=dev)
+
+    def step():
+        if not args.no_bounds:
+            tbe.tbe_bounds_check(tables, bt.indices, bt.offsets, counts, bws)
+        tbe.tbe_forward(tables, bt.weights, bt.indices, bt.offsets, bt.psw, out)
+        if spec.optimizer == "sgd":
+            tbe.tbe_backward_sgd(tables, bt.weights, bt.indices, bt.offsets, bt.psw, bt.grad_out,
+                                 lr, ws)
+        else:
+            tbe.tbe_backward_rowwise_adagrad(tables, bt.weights, bt.momentum, bt.indices, bt.offsets,
+                                             bt.psw, bt.grad_out, lr, eps, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # which kernel dominates: one profiled step per kernel (outside the timed region)
+    per_kernel = {}
+    for k in KERNELS:
+        tbe.tbe_profile_select(k)
+        step()
+        n, ms = tbe.tbe_profile_read()
+        if n:
+            per_kernel[k] = ms
+    tbe.tbe_profile_select(None)
+    dominant = max(per_kernel, key=per_kernel.get)
+    log("one step per kernel (ms): " + ", ".join(f"{k} {v:.3f}" for k, v in per_kernel.items()))
+    # timed region; the dominant kernel's launches are bracketed by HIP events on its stream
+    tbe.tbe_profile_select(dominant)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    launches, dom_ms = tbe.tbe_profile_read()
+    tbe.tbe_profile_select(None)
+    ms_per_step = elapsed * 1e3 / args.steps
+    N = st["N"]
+    ab = algorithmic_bytes(bt, st, 3)
+    dom_avg_ms = dom_ms / max(launches, 1)
+    dom_bytes = ab.get(dominant, 0)
+    achieved = dom_bytes / (dom_avg_ms * 1e-3) / 1e9 if dom_avg_ms > 0 else 0.0
+    step_bytes = sum(ab[k] for k in ("fwd_gather", "linearize", "short_run", "grad_accum", "long_apply")) \
+        + 3 * ab["radix_downsweep"] + 3 * ab["radix_upsweep"]
+    res = {
+        "metric": METRIC,
+        "value": N / (ms_per_step * 1e-3),
+        "unit": "lookups/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "lookups": N, "unique_rows": st["U"], "hottest_run": st["hottest"],
+                   "bags": st["TB"], "weights": str(bt.w_dtype).replace("torch.", ""),
+                   "indices": str(bt.indices.dtype).replace("torch.", ""), "optimizer": spec.optimizer,
+                   "step": ("" if args.no_bounds else "bounds_check + ") + "forward + backward"},
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_ms": dom_avg_ms,
+                     "launches_timed": launches},
+        "step_algorithmic_GBps": step_bytes / (ms_per_step * 1e-3) / 1e9,
+        "kernel_ms_one_step": per_kernel,
+    }
+    if not args.no_cpu_baseline:
+        del ws, out
+        torch.cuda.empty_cache()
+        log("timing the CPU oracle on a bounded sample ...")
+        res["cpu_baseline"] = cpu_baseline(spec, seed)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,459 @@
+// C ABI of the TBE library: argument validation, workspace layout, dispatch.
+// Declarations and the meaning of every argument are in include/tbe.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "tbe_device.h"
+#include "tbe_internal.h"
+
+namespace tbe {
+
+// ---------------------------------------------------------------------------
+// errors
+// ---------------------------------------------------------------------------
+static thread_local char g_error[512] = "";
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_error, sizeof(g_error), fmt, ap);
+  va_end(ap);
+}
+
+tbe_status check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_error("%s: %s", what, hipGetErrorString(e));
+    return TBE_ERR_HIP;
+  }
+  return TBE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// kernel timing
+// ---------------------------------------------------------------------------
+namespace {
+struct ProfState {
+  std::mutex mu;
+  std::string selected;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> events;
+  size_t used = 0;
+};
+ProfState& prof() {
+  static ProfState* p = new ProfState();  // never destroyed: events outlive static teardown
+  return *p;
+}
+}  // namespace
+
+ProfScope::ProfScope(const char* kernel, hipStream_t s) : slot(-1), stream(s) {
+  ProfState& P = prof();
+  std::lock_guard<std::mutex> lk(P.mu);
+  if (P.selected.empty() || P.selected != kernel) return;
+  if (P.used == P.events.size()) {
+    hipEvent_t a, b;
+    if (hipEventCreate(&a) != hipSuccess) return;
+    if (hipEventCreate(&b) != hipSuccess) {
+      (void)hipEventDestroy(a);
+      return;
+    }
+    P.events.emplace_back(a, b);
+  }
+  slot = static_cast<int>(P.used++);
+  (void)hipEventRecord(P.events[slot].first, s);
+}
+
+ProfScope::~ProfScope() {
+  if (slot < 0) return;
+  ProfState& P = prof();
+  std::lock_guard<std::mutex> lk(P.mu);
+  (void)hipEventRecord(P.events[slot].second, stream);
+}
+
+// ---------------------------------------------------------------------------
+// device properties
+// ---------------------------------------------------------------------------
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// ---------------------------------------------------------------------------
+// config and workspace layout
+// ---------------------------------------------------------------------------
+Config resolve_config(const tbe_config* c) {
+  tbe_config d;
+  tbe_config_default(&d);
+  if (!c) c = &d;
+  Config r;
+  r.threshold = c->long_threshold > 0 ? c->long_threshold : d.long_threshold;
+  r.chunk = c->chunk > 0 ? c->chunk : d.chunk;
+  r.hist_enable = c->hist_enable;
+  r.fwd_unroll = c->fwd_unroll > 0 ? c->fwd_unroll : d.fwd_unroll;
+  r.bwd_unroll = c->bwd_unroll > 0 ? c->bwd_unroll : d.bwd_unroll;
+  r.sort_blocks = c->sort_blocks;
+  return r;
+}
+
+namespace {
+constexpr size_t kAlign = 256;
+struct Carver {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    const size_t at = off;
+    off += (bytes + kAlign - 1) / kAlign * kAlign;
+    return at;
+  }
+};
+constexpr int kDefaultSortBlocks = 1024;
+constexpr int kMaxSortBlocks = 4096;
+}  // namespace
+
+BwdLayout bwd_layout(const tbe_tables* tb, int64_t N, int weighted, const Config& cfg) {
+  BwdLayout L;
+  std::memset(&L, 0, sizeof(L));
+  L.N = N;
+  const int64_t n1 = N > 0 ? N : 1;
+  Carver c;
+  for (int i = 0; i < 2; ++i) {
+    L.keys[i] = c.take(n1 * 4);
+    L.pay[i] = c.take(n1 * 4);
+  }
+  L.bag_of = weighted ? c.take(n1 * 4) : 0;
+  L.run_key = c.take(n1 * 4);
+  L.run_start = c.take((n1 + 1) * 4);
+  L.cap_long = N / cfg.threshold + 1;
+  L.cap_chunk = N / cfg.chunk + L.cap_long;
+  L.long_list = c.take(L.cap_long * 16);
+  L.long_table = c.take(L.cap_long * 4);
+  L.chunk_list = c.take(L.cap_chunk * 8);
+  L.partial = c.take(static_cast<size_t>(L.cap_chunk) * tb->max_D * 4);
+  for (int b = 0; b < TBE_NUM_BUCKETS; ++b) {
+    L.cap_short[b] = tb->bucket_rows[b] > 0 ? (tb->bucket_rows[b] < N ? tb->bucket_rows[b] : N) : 0;
+    L.short_list[b] = L.cap_short[b] ? c.take(L.cap_short[b] * 16) : 0;
+  }
+  const int64_t tiles = (n1 + kRadixTile - 1) / kRadixTile;
+  int64_t want = cfg.sort_blocks > 0 ? cfg.sort_blocks : kDefaultSortBlocks;
+  if (want > kMaxSortBlocks) want = kMaxSortBlocks;
+  if (want > tiles) want = tiles;
+  const int64_t per = (tiles + want - 1) / want;  // tiles per block
+  L.seg = per * kRadixTile;
+  L.nblocks = static_cast<int>((n1 + L.seg - 1) / L.seg);
+  L.sort_hist = c.take((static_cast<size_t>(kRadixDigits) * L.nblocks + kRadixDigits) * 4);
+  L.seg_cnt = c.take(static_cast<size_t>(L.nblocks) * 4);
+  L.counters = c.take(kNumCounters * 4);
+  L.total = c.off;
+  // keys are in [0, total_rows]; total_rows itself marks an id outside its table
+  uint32_t maxkey = static_cast<uint32_t>(tb->total_rows);
+  int kb = 1;
+  while (kb < 32 && (maxkey >> kb) != 0) ++kb;
+  L.key_bits = kb;
+  L.passes = (kb + kRadixMaxBits - 1) / kRadixMaxBits;
+  int shift = 0;
+  for (int p = 0; p < L.passes; ++p) {
+    const int bits = kb / L.passes + (p < kb % L.passes ? 1 : 0);
+    L.shift[p] = shift;
+    L.bits[p] = bits;
+    shift += bits;
+  }
+  return L;
+}
+
+}  // namespace tbe
+
+using namespace tbe;
+
+// ---------------------------------------------------------------------------
+// validation helpers
+// ---------------------------------------------------------------------------
+namespace {
+
+tbe_status check_tables(const tbe_tables* tb) {
+  if (!tb) { set_error("tables is NULL"); return TBE_ERR_ARG; }
+  if (tb->T < 1 || tb->B < 0) { set_error("bad geometry T=%d B=%d", tb->T, tb->B); return TBE_ERR_ARG; }
+  if (tb->w_dtype < TBE_F32 || tb->w_dtype > TBE_BF16) { set_error("bad w_dtype %d", tb->w_dtype); return TBE_ERR_UNSUPPORTED; }
+  if (!tb->meta) { set_error("tables->meta (device copy of the table metadata) is NULL"); return TBE_ERR_ARG; }
+  if (tb->max_D < 4 || tb->max_D > TBE_MAX_D) { set_error("max_D %d outside [4, %d]", tb->max_D, TBE_MAX_D); return TBE_ERR_UNSUPPORTED; }
+  if (tb->total_rows < 1 || tb->total_rows >= (1ll << 31) - 1) { set_error("total rows %lld outside [1, 2^31-1)", (long long)tb->total_rows); return TBE_ERR_UNSUPPORTED; }
+  if (static_cast<int64_t>(tb->T) * tb->B >= (1ll << 31)) { set_error("T*B must be < 2^31"); return TBE_ERR_UNSUPPORTED; }
+  return TBE_OK;
+}
+
+tbe_status check_index_args(const tbe_tables* tb, const void* indices, int itype, const void* offsets,
+                            int otype, int64_t N) {
+  if (itype != TBE_I32 && itype != TBE_I64) { set_error("bad index type %d", itype); return TBE_ERR_ARG; }
+  if (otype != TBE_I32 && otype != TBE_I64) { set_error("bad offset type %d", otype); return TBE_ERR_ARG; }
+  if (N < 0 || N >= (1ll << 31)) { set_error("num_indices %lld outside [0, 2^31)", (long long)N); return TBE_ERR_UNSUPPORTED; }
+  if (N > 0 && !indices) { set_error("indices is NULL"); return TBE_ERR_ARG; }
+  if (!offsets) { set_error("offsets is NULL"); return TBE_ERR_ARG; }
+  if (itype == TBE_I32 && N > 0 && (reinterpret_cast<uintptr_t>(indices) & 3)) { set_error("indices misaligned"); return TBE_ERR_ARG; }
+  if (reinterpret_cast<uintptr_t>(offsets) & (otype == TBE_I32 ? 3 : 7)) { set_error("offsets misaligned"); return TBE_ERR_ARG; }
+  (void)tb;
+  return TBE_OK;
+}
+
+tbe_status check_rows(const void* p, const char* what, size_t align) {
+  if (!p) { set_error("%s is NULL", what); return TBE_ERR_ARG; }
+  if (reinterpret_cast<uintptr_t>(p) % align) { set_error("%s is not %zu-byte aligned", what, align); return TBE_ERR_ARG; }
+  return TBE_OK;
+}
+
+size_t weight_align(const tbe_tables* tb) { return tb->w_dtype == TBE_F32 ? 16 : (tb->all_D_mult8 ? 16 : 8); }
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+extern "C" {
+
+const char* tbe_status_string(tbe_status s) {
+  switch (s) {
+    case TBE_OK: return "ok";
+    case TBE_ERR_ARG: return "invalid argument";
+    case TBE_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case TBE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case TBE_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+const char* tbe_last_error(void) { return g_error; }
+
+void tbe_config_default(tbe_config* cfg) {
+  if (!cfg) return;
+  cfg->long_threshold = 256;
+  cfg->chunk = 256;
+  cfg->hist_enable = 1;
+  cfg->fwd_unroll = 8;
+  cfg->bwd_unroll = 4;
+  cfg->sort_blocks = 0;
+}
+
+int64_t tbe_meta_entries(int32_t T) { return T >= 0 ? static_cast<int64_t>(TBE_META_FIELDS) * (T + 1) : 0; }
+
+tbe_status tbe_tables_derive(int32_t T, int32_t B, int32_t w_dtype, const int64_t* E_host,
+                             const int32_t* D_host, const int32_t* pooling_hint_host,
+                             int64_t* meta_host, tbe_tables* out) {
+  g_error[0] = 0;
+  if (!out || !E_host || !D_host || !meta_host) { set_error("NULL argument"); return TBE_ERR_ARG; }
+  if (T < 1 || B < 0) { set_error("bad geometry T=%d B=%d", T, B); return TBE_ERR_ARG; }
+  if (w_dtype < TBE_F32 || w_dtype > TBE_BF16) { set_error("bad w_dtype %d", w_dtype); return TBE_ERR_UNSUPPORTED; }
+  std::memset(out, 0, sizeof(*out));
+  out->T = T;
+  out->B = B;
+  out->w_dtype = w_dtype;
+  out->hist_table = -1;
+  out->all_D_mult8 = 1;
+  int64_t rows = 0, elems = 0, cols = 0;
+  int maxD = 0;
+  for (int t = 0; t < T; ++t) {
+    const int64_t E = E_host[t];
+    const int32_t D = D_host[t];
+    if (E < 1) { set_error("table %d has %lld rows", t, (long long)E); return TBE_ERR_ARG; }
+    if (D < 4 || D > TBE_MAX_D || D % 4) { set_error("table %d: D=%d not in [4, %d] or not a multiple of 4", t, D, TBE_MAX_D); return TBE_ERR_UNSUPPORTED; }
+    meta_host[4 * t + 0] = rows;
+    meta_host[4 * t + 1] = elems;
+    meta_host[4 * t + 2] = cols;
+    meta_host[4 * t + 3] = D;
+    if (D % 8) out->all_D_mult8 = 0;
+    if (D > maxD) maxD = D;
+    out->bucket_rows[bucket_of_D(D)] += E;
+    if (out->hist_table < 0 && pooling_hint_host && E <= 64 && D >= 64 && D <= 128 && D % 16 == 0 &&
+        w_dtype == TBE_F16 && pooling_hint_host[t] >= 64) {
+      out->hist_table = t;
+      out->hist_E = static_cast<int32_t>(E);
+      out->hist_D = D;
+      out->hist_col = static_cast<int32_t>(cols);
+      out->hist_w_base = elems;
+    }
+    rows += E;
+    elems += E * D;
+    cols += D;
+    if (rows >= (1ll << 31) - 1) { set_error("sum of rows must be < 2^31 - 1"); return TBE_ERR_UNSUPPORTED; }
+    if (cols >= (1ll << 31)) { set_error("sum of D too large"); return TBE_ERR_UNSUPPORTED; }
+  }
+  meta_host[4 * T + 0] = rows;
+  meta_host[4 * T + 1] = elems;
+  meta_host[4 * T + 2] = cols;
+  meta_host[4 * T + 3] = 0;
+  out->max_D = maxD;
+  out->out_width = static_cast<int32_t>(cols);
+  out->total_rows = rows;
+  out->total_elems = elems;
+  out->meta = nullptr;
+  return TBE_OK;
+}
+
+size_t tbe_bounds_check_workspace_bytes(const tbe_tables* tables) { return bounds_workspace(tables); }
+
+tbe_status tbe_bounds_check(const tbe_tables* tables, void* indices, int32_t index_type, void* offsets,
+                            int32_t offset_type, int64_t num_indices, int64_t* error_counts,
+                            void* workspace, size_t workspace_bytes, tbe_stream_t stream) {
+  g_error[0] = 0;
+  if (tbe_status st = check_tables(tables)) return st;
+  if (tbe_status st = check_index_args(tables, indices, index_type, offsets, offset_type, num_indices)) return st;
+  if (!error_counts) { set_error("error_counts is NULL"); return TBE_ERR_ARG; }
+  if (!workspace || workspace_bytes < bounds_workspace(tables) || (reinterpret_cast<uintptr_t>(workspace) & 255)) {
+    set_error("bounds workspace needs %zu bytes, 256-byte aligned", bounds_workspace(tables));
+    return TBE_ERR_WORKSPACE;
+  }
+  return launch_bounds(tables, indices, index_type, offsets, offset_type, num_indices, error_counts,
+                       workspace, static_cast<hipStream_t>(stream));
+}
+
+tbe_status tbe_forward(const tbe_tables* tables, const void* weights, const void* indices,
+                       int32_t index_type, const void* offsets, int32_t offset_type, int64_t num_indices,
+                       const float* per_sample_weights, float* out, const tbe_config* config,
+                       tbe_stream_t stream) {
+  g_error[0] = 0;
+  if (tbe_status st = check_tables(tables)) return st;
+  if (tbe_status st = check_index_args(tables, indices, index_type, offsets, offset_type, num_indices)) return st;
+  if (tables->B == 0) return TBE_OK;
+  if (tbe_status st = check_rows(weights, "weights", weight_align(tables))) return st;
+  if (tbe_status st = check_rows(out, "out", 16)) return st;
+  const Config cfg = resolve_config(config);
+  IndexArgs ia{indices, index_type, offsets, offset_type, num_indices};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int hist = (cfg.hist_enable && !per_sample_weights && tables->hist_table >= 0) ? tables->hist_table : -1;
+  if (hist >= 0)
+    if (tbe_status st = launch_forward_hist(tables, weights, ia, out, s)) return st;
+  return launch_forward_gather(tables, weights, ia, per_sample_weights, out, hist, cfg.fwd_unroll, s);
+}
+
+size_t tbe_backward_workspace_bytes(const tbe_tables* tables, int64_t num_indices, int32_t weighted,
+                                    const tbe_config* config) {
+  if (!tables || num_indices < 0) return 0;
+  return bwd_layout(tables, num_indices, weighted ? 1 : 0, resolve_config(config)).total;
+}
+
+static tbe_status backward_common(const tbe_tables* tables, void* weights, float* momentum, int opt,
+                                  const void* indices, int32_t index_type, const void* offsets,
+                                  int32_t offset_type, int64_t num_indices, const float* psw,
+                                  const float* grad_out, float lr, float eps, void* workspace,
+                                  size_t workspace_bytes, const tbe_config* config, tbe_stream_t stream) {
+  g_error[0] = 0;
+  if (tbe_status st = check_tables(tables)) return st;
+  if (tbe_status st = check_index_args(tables, indices, index_type, offsets, offset_type, num_indices)) return st;
+  if (tables->B == 0 || num_indices == 0) return TBE_OK;
+  if (tbe_status st = check_rows(weights, "weights", weight_align(tables))) return st;
+  if (tbe_status st = check_rows(grad_out, "grad_out", 16)) return st;
+  if (opt == kOptAdagrad && !momentum) { set_error("momentum is NULL"); return TBE_ERR_ARG; }
+  const Config cfg = resolve_config(config);
+  const BwdLayout L = bwd_layout(tables, num_indices, psw ? 1 : 0, cfg);
+  if (!workspace || workspace_bytes < L.total || (reinterpret_cast<uintptr_t>(workspace) & 255)) {
+    set_error("backward workspace needs %zu bytes, 256-byte aligned (got %zu)", L.total, workspace_bytes);
+    return TBE_ERR_WORKSPACE;
+  }
+  IndexArgs ia{indices, index_type, offsets, offset_type, num_indices};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  int final_buf = 0;
+  if (tbe_status st = launch_transpose(tables, ia, psw ? 1 : 0, ws, L, cfg, &final_buf, s)) return st;
+  return launch_backward_update(tables, weights, momentum, opt, psw, grad_out, lr, eps, ws, L, final_buf, cfg, s);
+}
+
+tbe_status tbe_backward_sgd(const tbe_tables* tables, void* weights, const void* indices,
+                            int32_t index_type, const void* offsets, int32_t offset_type,
+                            int64_t num_indices, const float* per_sample_weights, const float* grad_out,
+                            float lr, void* workspace, size_t workspace_bytes, const tbe_config* config,
+                            tbe_stream_t stream) {
+  return backward_common(tables, weights, nullptr, kOptSGD, indices, index_type, offsets, offset_type,
+                         num_indices, per_sample_weights, grad_out, lr, 0.f, workspace, workspace_bytes,
+                         config, stream);
+}
+
+tbe_status tbe_backward_rowwise_adagrad(const tbe_tables* tables, void* weights, float* momentum,
+                                        const void* indices, int32_t index_type, const void* offsets,
+                                        int32_t offset_type, int64_t num_indices,
+                                        const float* per_sample_weights, const float* grad_out, float lr,
+                                        float eps, void* workspace, size_t workspace_bytes,
+                                        const tbe_config* config, tbe_stream_t stream) {
+  return backward_common(tables, weights, momentum, kOptAdagrad, indices, index_type, offsets,
+                         offset_type, num_indices, per_sample_weights, grad_out, lr, eps, workspace,
+                         workspace_bytes, config, stream);
+}
+
+tbe_status tbe_transpose(const tbe_tables* tables, const void* indices, int32_t index_type,
+                         const void* offsets, int32_t offset_type, int64_t num_indices, int32_t weighted,
+                         void* workspace, size_t workspace_bytes, const tbe_config* config,
+                         tbe_runs_view* view, tbe_stream_t stream) {
+  g_error[0] = 0;
+  if (tbe_status st = check_tables(tables)) return st;
+  if (tbe_status st = check_index_args(tables, indices, index_type, offsets, offset_type, num_indices)) return st;
+  if (!view) { set_error("view is NULL"); return TBE_ERR_ARG; }
+  const Config cfg = resolve_config(config);
+  const BwdLayout L = bwd_layout(tables, num_indices, weighted ? 1 : 0, cfg);
+  if (!workspace || workspace_bytes < L.total || (reinterpret_cast<uintptr_t>(workspace) & 255)) {
+    set_error("transpose workspace needs %zu bytes, 256-byte aligned (got %zu)", L.total, workspace_bytes);
+    return TBE_ERR_WORKSPACE;
+  }
+  IndexArgs ia{indices, index_type, offsets, offset_type, num_indices};
+  char* ws = static_cast<char*>(workspace);
+  int final_buf = 0;
+  tbe_status st = launch_transpose(tables, ia, weighted ? 1 : 0, ws, L, cfg, &final_buf,
+                                   static_cast<hipStream_t>(stream));
+  std::memset(view, 0, sizeof(*view));
+  view->sorted_keys = reinterpret_cast<const uint32_t*>(ws + L.keys[final_buf]);
+  view->sorted_payload = reinterpret_cast<const uint32_t*>(ws + L.pay[final_buf]);
+  view->run_key = reinterpret_cast<const uint32_t*>(ws + L.run_key);
+  view->run_start = reinterpret_cast<const uint32_t*>(ws + L.run_start);
+  view->counters = reinterpret_cast<const int32_t*>(ws + L.counters);
+  view->long_list = reinterpret_cast<const uint32_t*>(ws + L.long_list);
+  view->long_table = reinterpret_cast<const uint32_t*>(ws + L.long_table);
+  view->chunk_list = reinterpret_cast<const uint32_t*>(ws + L.chunk_list);
+  for (int b = 0; b < TBE_NUM_BUCKETS; ++b) {
+    view->short_list[b] = L.cap_short[b] ? reinterpret_cast<const uint32_t*>(ws + L.short_list[b]) : nullptr;
+    view->short_capacity[b] = L.cap_short[b];
+  }
+  view->long_capacity = L.cap_long;
+  view->chunk_capacity = L.cap_chunk;
+  view->payload_is_position = weighted ? 1 : 0;
+  view->radix_passes = L.passes;
+  return st;
+}
+
+tbe_status tbe_profile_select(const char* kernel_name) {
+  ProfState& P = prof();
+  std::lock_guard<std::mutex> lk(P.mu);
+  P.selected = kernel_name ? kernel_name : "";
+  P.used = 0;
+  return TBE_OK;
+}
+
+tbe_status tbe_profile_read(int64_t* launches, double* total_ms) {
+  ProfState& P = prof();
+  std::lock_guard<std::mutex> lk(P.mu);
+  double ms = 0.0;
+  for (size_t i = 0; i < P.used; ++i) {
+    if (hipEventSynchronize(P.events[i].second) != hipSuccess) {
+      set_error("hipEventSynchronize failed");
+      return TBE_ERR_HIP;
+    }
+    float f = 0.f;
+    if (hipEventElapsedTime(&f, P.events[i].first, P.events[i].second) != hipSuccess) {
+      set_error("hipEventElapsedTime failed");
+      return TBE_ERR_HIP;
+    }
+    ms += f;
+  }
+  if (launches) *launches = static_cast<int64_t>(P.used);
+  if (total_ms) *total_ms = ms;
+  P.used = 0;
+  return TBE_OK;
+}
+
+}  // extern "C"

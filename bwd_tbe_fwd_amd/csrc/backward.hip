@@ -1,0 +1,145 @@
+// Long-run gradient accumulation (split into fixed-size chunks) and the
+// backward's update orchestration.
+//
+// PyTorch blog "Modernizing Table Batched Embeddings with FBTriton", section 4,
+// problem 1: a run at or above the threshold becomes fixed 256-lookup chunks,
+// split-K style, so one hot row's work spreads over the whole machine; the
+// chunk partials land in a workspace and a second kernel applies the optimizer
+// (section 3, grad_accum + apply).  Here every chunk writes its own partial
+// row (no atomics), and the apply kernel adds a run's partials in a fixed
+// order, so the result does not depend on scheduling.
+#include "backward_kernels.h"
+
+namespace tbe {
+namespace {
+
+// One wave per chunk.  Lanes form groups of D/4 (at most 64) lanes; each group
+// reads one gradient row per instruction as float4 per lane, UNROLL
+// instructions in flight; the groups' sums are combined with xor shuffles.
+template <bool WEIGHTED, int UNROLL>
+__global__ __launch_bounds__(kBlock) void grad_accum_kernel(
+    const float* __restrict__ grad_out, const uint32_t* __restrict__ pay,
+    const uint32_t* __restrict__ bag_of, const float* __restrict__ psw,
+    const uint4* __restrict__ long_list, const uint32_t* __restrict__ long_table,
+    const uint2* __restrict__ chunk_list, const int32_t* __restrict__ counters,
+    const int64_t* __restrict__ meta, int32_t B, int32_t out_width, int chunk, int max_D,
+    float* __restrict__ partial) {
+  const int lane = lane_id();
+  const int64_t wave = (static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x) >> 6;
+  const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * kBlock) >> 6;
+  const int64_t n = counters[kChunks];
+  for (int64_t cix = wave; cix < n; cix += nwaves) {
+    const uint2 ch = chunk_list[cix];
+    const uint4 L = long_list[ch.x];
+    const int t = static_cast<int>(long_table[ch.x]);
+    const TableMeta m = load_meta(meta, t);
+    const int D = static_cast<int>(m.D);
+    const uint32_t lo = L.y + ch.y * static_cast<uint32_t>(chunk);
+    const uint32_t hi = min(lo + static_cast<uint32_t>(chunk), L.y + L.z);
+    const int64_t bag_lo = static_cast<int64_t>(t) * B;
+    float* dst = partial + cix * max_D;
+    for (int cb = 0; cb < D; cb += 4 * kWave) {
+      const int wcols = min(D - cb, 4 * kWave);
+      const int lpr = pow2_ceil(wcols / 4);
+      const int lg = __builtin_ctz(lpr);
+      const int G = kWave >> lg;
+      const int g = lane >> lg;
+      const int cc = lane & (lpr - 1);
+      const int col = cb + cc * 4;
+      const bool act = cc * 4 < wcols;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (uint32_t j0 = lo; j0 < hi; j0 += kWave) {
+        const int nb = static_cast<int>(min<uint32_t>(kWave, hi - j0));
+        int32_t myb = -1;
+        float myw = 1.f;
+        if (lane < nb) {
+          const uint32_t pv = pay[j0 + lane];
+          int64_t bag;
+          if constexpr (WEIGHTED) {
+            bag = bag_of[pv];
+            myw = psw[pv];
+          } else {
+            bag = pv;
+          }
+          const int64_t br = bag - bag_lo;
+          myb = (br >= 0 && br < B) ? static_cast<int32_t>(br) : -1;
+        }
+        for (int q0 = 0; q0 < nb; q0 += G * UNROLL) {
+          f32x4 v[UNROLL];
+          float wq[UNROLL];
+#pragma unroll
+          for (int u = 0; u < UNROLL; ++u) {
+            const int q = q0 + u * G + g;
+            const int b = __shfl(myb, q & (kWave - 1));
+            wq[u] = WEIGHTED ? __shfl(myw, q & (kWave - 1)) : 1.f;
+            if (q < nb && b >= 0 && act)
+              v[u] = load_f4(grad_out + static_cast<int64_t>(b) * out_width + m.col_base + col);
+            else
+              v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+#pragma unroll
+          for (int u = 0; u < UNROLL; ++u) {
+            if constexpr (WEIGHTED) acc += wq[u] * v[u];
+            else acc += v[u];
+          }
+        }
+      }
+      for (int msk = lpr; msk < kWave; msk <<= 1) {
+        acc.x += __shfl_xor(acc.x, msk);
+        acc.y += __shfl_xor(acc.y, msk);
+        acc.z += __shfl_xor(acc.z, msk);
+        acc.w += __shfl_xor(acc.w, msk);
+      }
+      if (g == 0 && act) store_f4(dst + col, acc);
+    }
+  }
+}
+
+template <bool WEIGHTED>
+tbe_status accum_go(const tbe_tables* tb, const float* psw, const float* grad_out, char* ws,
+                    const BwdLayout& L, int final_buf, const Config& cfg, hipStream_t s) {
+  const int64_t maxb = static_cast<int64_t>(device_cu_count()) * 8;
+  const int grid = static_cast<int>(
+      hmax(1, hmin((L.cap_chunk + kWavesPerBlock - 1) / kWavesPerBlock, maxb)));
+  const uint32_t* pay = reinterpret_cast<const uint32_t*>(ws + L.pay[final_buf]);
+  const uint32_t* bag_of = WEIGHTED ? reinterpret_cast<const uint32_t*>(ws + L.bag_of) : nullptr;
+  ProfScope ps("grad_accum", s);
+#define TBE_ACC(U)                                                                                 \
+  hipLaunchKernelGGL((grad_accum_kernel<WEIGHTED, U>), dim3(grid), dim3(kBlock), 0, s, grad_out, pay, \
+                     bag_of, psw, reinterpret_cast<const uint4*>(ws + L.long_list),               \
+                     reinterpret_cast<const uint32_t*>(ws + L.long_table),                        \
+                     reinterpret_cast<const uint2*>(ws + L.chunk_list),                           \
+                     reinterpret_cast<const int32_t*>(ws + L.counters), tb->meta, tb->B,           \
+                     tb->out_width, cfg.chunk, tb->max_D, reinterpret_cast<float*>(ws + L.partial))
+  if (cfg.bwd_unroll <= 2) TBE_ACC(2);
+  else if (cfg.bwd_unroll <= 4) TBE_ACC(4);
+  else TBE_ACC(8);
+#undef TBE_ACC
+  return check_launch("grad_accum");
+}
+
+}  // namespace
+
+tbe_status launch_grad_accum(const tbe_tables* tb, const float* psw, const float* grad_out,
+                             char* ws, const BwdLayout& L, int final_buf, const Config& cfg,
+                             hipStream_t s) {
+  if (psw) return accum_go<true>(tb, psw, grad_out, ws, L, final_buf, cfg, s);
+  return accum_go<false>(tb, psw, grad_out, ws, L, final_buf, cfg, s);
+}
+
+tbe_status launch_backward_update(const tbe_tables* tb, void* W, float* momentum, int opt,
+                                  const float* psw, const float* grad_out, float lr, float eps,
+                                  char* ws, const BwdLayout& L, int final_buf, const Config& cfg,
+                                  hipStream_t s) {
+  if (L.N == 0) return TBE_OK;
+  switch (tb->w_dtype) {
+    case TBE_F32:
+      return launch_short_and_apply<0>(tb, W, momentum, opt, psw, grad_out, lr, eps, ws, L, final_buf, cfg, s);
+    case TBE_F16:
+      return launch_short_and_apply<1>(tb, W, momentum, opt, psw, grad_out, lr, eps, ws, L, final_buf, cfg, s);
+    default:
+      return launch_short_and_apply<2>(tb, W, momentum, opt, psw, grad_out, lr, eps, ws, L, final_buf, cfg, s);
+  }
+}
+
+}  // namespace tbe

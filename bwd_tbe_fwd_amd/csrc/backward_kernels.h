@@ -1,0 +1,216 @@
+// Backward gradient reduction and optimizer kernels (templates; instantiated
+// per weight format in backward_f32.hip / backward_f16.hip / backward_bf16.hip).
+//
+// PyTorch blog "Modernizing Table Batched Embeddings with FBTriton", section 3:
+// a short run (SL < 256) is owned start to finish by one program (gather,
+// accumulate in registers, optimizer, plain store, no atomics); a long run is
+// cut into 256-lookup chunks whose partial sums land in a workspace, and a
+// second kernel applies the optimizer.  Weighted tables scale each gradient
+// row by its per-sample weight before accumulating.  Section 4, problem 3:
+// short runs are launched per next_pow2(D) bucket so each bucket uses its own
+// lane count.  The optimizer is the backward's epilogue: SGD (w - lr*g) or
+// exact row-wise Adagrad ("Table-Batched Embeddings in Triton", section 5:
+// m += mean_d g_d^2, w -= lr*g/(sqrt(m)+eps) with the new m).
+//
+// gfx950 mapping: gradients are fp32 rows of D floats, read as float4 per lane,
+// so a run of bucket BD is served by BD/4 lanes (BD >= 256: all 64 lanes with
+// BD/256 column passes) and a wave owns 64/(BD/4) short runs at once - no lane
+// is masked off for D = BD, and the per-run metadata (one 16-byte descriptor)
+// is amortized over the lanes of the run.  UNROLL gradient rows are in flight
+// per lane before they are summed.  The weight row and the Adagrad state are
+// loaded before the gradient loop so their latency overlaps it.  Accumulation
+// is fp32 throughout; no float atomics anywhere, so results are deterministic.
+#pragma once
+
+#include "tbe_device.h"
+#include "tbe_internal.h"
+
+namespace tbe {
+
+template <int DT, int BD, int OPT, bool WEIGHTED, int UNROLL>
+__global__ __launch_bounds__(kBlock) void short_run_kernel(
+    typename Fmt<DT>::S* __restrict__ W, float* __restrict__ momentum,
+    const float* __restrict__ grad_out, const uint32_t* __restrict__ pay,
+    const uint32_t* __restrict__ bag_of, const float* __restrict__ psw,
+    const uint4* __restrict__ list, const int32_t* __restrict__ count_ptr,
+    const int64_t* __restrict__ meta, int32_t B, int32_t out_width, float lr, float eps) {
+  using S = typename Fmt<DT>::S;
+  constexpr int NP = BD > 256 ? BD / 256 : 1;   // column passes of 64 lanes x 4 floats
+  constexpr int LPR = BD >= 256 ? 64 : BD / 4;  // lanes per run
+  constexpr int RPW = kWave / LPR;              // runs per wave
+  const int lane = lane_id();
+  const int g = lane / LPR;
+  const int c = lane % LPR;
+  const int64_t n = *count_ptr;
+  const int64_t sub = ((static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x) >> 6) * RPW + g;
+  const int64_t nsub = ((static_cast<int64_t>(gridDim.x) * kBlock) >> 6) * RPW;
+  for (int64_t i = sub; i < n; i += nsub) {
+    const uint4 dsc = list[i];
+    const uint32_t key = dsc.x, start = dsc.y, len = dsc.z;
+    const int t = static_cast<int>(dsc.w);
+    const TableMeta m = load_meta(meta, t);
+    const int D = static_cast<int>(m.D);
+    S* wrow = W + m.w_base + (static_cast<int64_t>(key) - m.row_base) * D;
+    const int64_t bag_lo = static_cast<int64_t>(t) * B;
+    float w[NP][4];
+    bool act[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int col = p * 256 + c * 4;
+      act[p] = col < D;
+      if (act[p]) {
+        load_vec<DT, 4>(wrow + col, w[p]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) w[p][q] = 0.f;
+      }
+    }
+    float mom = 0.f;
+    if constexpr (OPT == kOptAdagrad) mom = momentum[key];
+    float acc[NP][4];
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[p][q] = 0.f;
+    for (uint32_t j0 = 0; j0 < len; j0 += LPR) {
+      const int nb = static_cast<int>(min<uint32_t>(LPR, len - j0));
+      int32_t myb = -1;
+      float myw = 1.f;
+      if (c < nb) {
+        const uint32_t pv = pay[start + j0 + c];
+        int64_t bag;
+        if constexpr (WEIGHTED) {
+          bag = bag_of[pv];
+          myw = psw[pv];
+        } else {
+          bag = pv;
+        }
+        const int64_t br = bag - bag_lo;
+        myb = (br >= 0 && br < B) ? static_cast<int32_t>(br) : -1;
+      }
+      for (int q0 = 0; q0 < nb; q0 += UNROLL) {
+        float v[UNROLL][NP][4];
+        float wq[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+          const int q = q0 + u;
+          const int b = __shfl(myb, q, LPR);
+          wq[u] = WEIGHTED ? __shfl(myw, q, LPR) : 1.f;
+          const bool ok = q < nb && b >= 0;
+          const float* grow = grad_out + static_cast<int64_t>(b) * out_width + m.col_base;
+#pragma unroll
+          for (int p = 0; p < NP; ++p) {
+            if (ok && act[p]) {
+              const f32x4 x = load_f4(grow + p * 256 + c * 4);
+              v[u][p][0] = x.x; v[u][p][1] = x.y; v[u][p][2] = x.z; v[u][p][3] = x.w;
+            } else {
+#pragma unroll
+              for (int q2 = 0; q2 < 4; ++q2) v[u][p][q2] = 0.f;
+            }
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+          for (int p = 0; p < NP; ++p)
+#pragma unroll
+            for (int q2 = 0; q2 < 4; ++q2) {
+              if constexpr (WEIGHTED) acc[p][q2] += wq[u] * v[u][p][q2];
+              else acc[p][q2] += v[u][p][q2];
+            }
+      }
+    }
+    if constexpr (OPT == kOptSGD) {
+#pragma unroll
+      for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) w[p][q] -= lr * acc[p][q];
+    } else {
+      float ss = 0.f;
+#pragma unroll
+      for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) ss += act[p] ? acc[p][q] * acc[p][q] : 0.f;
+#pragma unroll
+      for (int msk = 1; msk < LPR; msk <<= 1) ss += __shfl_xor(ss, msk);
+      const float mnew = mom + ss / static_cast<float>(D);
+      const float denom = sqrtf(mnew) + eps;
+#pragma unroll
+      for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) w[p][q] -= lr * acc[p][q] / denom;
+      if (c == 0) momentum[key] = mnew;
+    }
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+      if (act[p]) store_vec4<DT>(wrow + p * 256 + c * 4, w[p]);
+  }
+}
+
+// One workgroup per long run: the four waves sum interleaved chunk partials
+// (chunk k goes to wave k % 4, always in increasing k), the four sums are added
+// in wave order, and the optimizer is applied by all 256 threads, 4 columns each.
+template <int DT, int OPT>
+__global__ __launch_bounds__(kBlock) void long_apply_kernel(
+    typename Fmt<DT>::S* __restrict__ W, float* __restrict__ momentum,
+    const uint4* __restrict__ long_list, const uint32_t* __restrict__ long_table,
+    const int32_t* __restrict__ counters, const int64_t* __restrict__ meta, int chunk, int max_D,
+    const float* __restrict__ partial, float lr, float eps) {
+  using S = typename Fmt<DT>::S;
+  __shared__ __align__(16) float s_red[kWavesPerBlock][TBE_MAX_D];
+  __shared__ float s_tmp[kWavesPerBlock];
+  const int lane = lane_id(), w = threadIdx.x >> 6;
+  const int64_t n = counters[kLong];
+  for (int64_t li = blockIdx.x; li < n; li += gridDim.x) {
+    const uint4 L = long_list[li];
+    const int t = static_cast<int>(long_table[li]);
+    const TableMeta m = load_meta(meta, t);
+    const int D = static_cast<int>(m.D);
+    const uint32_t nch = (L.z + chunk - 1) / chunk;
+    const int64_t cb = L.w;
+    for (int col = 4 * lane; col < D; col += 4 * kWave) {
+      f32x4 a = {0.f, 0.f, 0.f, 0.f};
+      for (uint32_t k = w; k < nch; k += kWavesPerBlock) a += load_f4(partial + (cb + k) * max_D + col);
+      *reinterpret_cast<f32x4*>(&s_red[w][col]) = a;
+    }
+    __syncthreads();
+    const int col = 4 * threadIdx.x;
+    const bool act = col < D;
+    float gv[4] = {0.f, 0.f, 0.f, 0.f};
+    float wv[4] = {0.f, 0.f, 0.f, 0.f};
+    S* wrow = W + m.w_base + (static_cast<int64_t>(L.x) - m.row_base) * D;
+    if (act) {
+      load_vec<DT, 4>(wrow + col, wv);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        gv[q] = ((s_red[0][col + q] + s_red[1][col + q]) + s_red[2][col + q]) + s_red[3][col + q];
+    }
+    if constexpr (OPT == kOptSGD) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) wv[q] -= lr * gv[q];
+    } else {
+      float ss = gv[0] * gv[0] + gv[1] * gv[1] + gv[2] * gv[2] + gv[3] * gv[3];
+      for (int msk = 1; msk < kWave; msk <<= 1) ss += __shfl_xor(ss, msk);
+      if (lane == 0) s_tmp[w] = ss;
+      __syncthreads();
+      ss = ((s_tmp[0] + s_tmp[1]) + s_tmp[2]) + s_tmp[3];
+      const float mnew = momentum[L.x] + ss / static_cast<float>(D);
+      const float denom = sqrtf(mnew) + eps;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) wv[q] -= lr * gv[q] / denom;
+      __syncthreads();
+      if (threadIdx.x == 0) momentum[L.x] = mnew;
+    }
+    if (act) store_vec4<DT>(wrow + col, wv);
+    __syncthreads();
+  }
+}
+
+// launchers per weight format (backward_f32/f16/bf16.hip)
+template <int DT>
+tbe_status launch_short_and_apply(const tbe_tables* tb, void* W, float* momentum, int opt,
+                                  const float* psw, const float* grad_out, float lr, float eps,
+                                  char* ws, const BwdLayout& L, int final_buf, const Config& cfg,
+                                  hipStream_t s);
+
+}  // namespace tbe

@@ -1,0 +1,100 @@
+// Host launcher of the short-run and long-apply kernels for one weight format.
+#pragma once
+
+#include "backward_kernels.h"
+
+namespace tbe {
+
+namespace detail {
+
+constexpr int kShortUnroll = 4;
+
+template <int DT, int BD, int OPT, bool WEIGHTED>
+tbe_status short_go(void* W, float* momentum, const float* psw, const float* grad_out,
+                    const uint32_t* pay, const uint32_t* bag_of, const uint4* list,
+                    const int32_t* count, int64_t cap, const tbe_tables* tb, float lr, float eps,
+                    hipStream_t s) {
+  using S = typename Fmt<DT>::S;
+  constexpr int LPR = BD >= 256 ? 64 : BD / 4;
+  constexpr int RPW = kWave / LPR;
+  const int64_t waves = (cap + RPW - 1) / RPW;
+  const int64_t maxb = static_cast<int64_t>(device_cu_count()) * 8;
+  const int grid = static_cast<int>(hmax(1, hmin((waves + kWavesPerBlock - 1) / kWavesPerBlock, maxb)));
+  ProfScope ps("short_run", s);
+  hipLaunchKernelGGL((short_run_kernel<DT, BD, OPT, WEIGHTED, kShortUnroll>), dim3(grid), dim3(kBlock), 0, s,
+                     static_cast<S*>(W), momentum, grad_out, pay, bag_of, psw, list, count, tb->meta,
+                     tb->B, tb->out_width, lr, eps);
+  return check_launch("short_run");
+}
+
+template <int DT, int OPT, bool WEIGHTED>
+tbe_status short_bucket(int b, void* W, float* momentum, const float* psw, const float* grad_out,
+                        const uint32_t* pay, const uint32_t* bag_of, const uint4* list,
+                        const int32_t* count, int64_t cap, const tbe_tables* tb, float lr, float eps,
+                        hipStream_t s) {
+#define TBE_SB(BD) short_go<DT, BD, OPT, WEIGHTED>(W, momentum, psw, grad_out, pay, bag_of, list, count, cap, tb, lr, eps, s)
+  switch (b) {
+    case 0: return TBE_SB(4);
+    case 1: return TBE_SB(8);
+    case 2: return TBE_SB(16);
+    case 3: return TBE_SB(32);
+    case 4: return TBE_SB(64);
+    case 5: return TBE_SB(128);
+    case 6: return TBE_SB(256);
+    case 7: return TBE_SB(512);
+    default: return TBE_SB(1024);
+  }
+#undef TBE_SB
+}
+
+template <int DT, int OPT>
+tbe_status apply_go(void* W, float* momentum, const uint4* long_list, const uint32_t* long_table,
+                    const int32_t* counters, int64_t cap, const tbe_tables* tb, int chunk,
+                    const float* partial, float lr, float eps, hipStream_t s) {
+  using S = typename Fmt<DT>::S;
+  const int64_t maxb = static_cast<int64_t>(device_cu_count()) * 8;
+  const int grid = static_cast<int>(hmax(1, hmin(cap, maxb)));
+  ProfScope ps("long_apply", s);
+  hipLaunchKernelGGL((long_apply_kernel<DT, OPT>), dim3(grid), dim3(kBlock), 0, s, static_cast<S*>(W),
+                     momentum, long_list, long_table, counters, tb->meta, chunk, tb->max_D, partial, lr, eps);
+  return check_launch("long_apply");
+}
+
+}  // namespace detail
+
+tbe_status launch_grad_accum(const tbe_tables* tb, const float* psw, const float* grad_out,
+                             char* ws, const BwdLayout& L, int final_buf, const Config& cfg,
+                             hipStream_t s);
+
+template <int DT>
+tbe_status launch_short_and_apply(const tbe_tables* tb, void* W, float* momentum, int opt,
+                                  const float* psw, const float* grad_out, float lr, float eps,
+                                  char* ws, const BwdLayout& L, int final_buf, const Config& cfg,
+                                  hipStream_t s) {
+  const int32_t* counters = reinterpret_cast<const int32_t*>(ws + L.counters);
+  const uint32_t* pay = reinterpret_cast<const uint32_t*>(ws + L.pay[final_buf]);
+  const uint32_t* bag_of = psw ? reinterpret_cast<const uint32_t*>(ws + L.bag_of) : nullptr;
+  for (int b = 0; b < TBE_NUM_BUCKETS; ++b) {
+    if (!L.cap_short[b]) continue;
+    const uint4* list = reinterpret_cast<const uint4*>(ws + L.short_list[b]);
+    const int32_t* cnt = counters + kShort0 + b;
+    tbe_status st;
+    if (opt == kOptSGD)
+      st = psw ? detail::short_bucket<DT, kOptSGD, true>(b, W, momentum, psw, grad_out, pay, bag_of, list, cnt, L.cap_short[b], tb, lr, eps, s)
+               : detail::short_bucket<DT, kOptSGD, false>(b, W, momentum, psw, grad_out, pay, bag_of, list, cnt, L.cap_short[b], tb, lr, eps, s);
+    else
+      st = psw ? detail::short_bucket<DT, kOptAdagrad, true>(b, W, momentum, psw, grad_out, pay, bag_of, list, cnt, L.cap_short[b], tb, lr, eps, s)
+               : detail::short_bucket<DT, kOptAdagrad, false>(b, W, momentum, psw, grad_out, pay, bag_of, list, cnt, L.cap_short[b], tb, lr, eps, s);
+    if (st) return st;
+  }
+  if (L.cap_long == 0) return TBE_OK;
+  if (tbe_status st = launch_grad_accum(tb, psw, grad_out, ws, L, final_buf, cfg, s)) return st;
+  const uint4* long_list = reinterpret_cast<const uint4*>(ws + L.long_list);
+  const uint32_t* long_table = reinterpret_cast<const uint32_t*>(ws + L.long_table);
+  const float* partial = reinterpret_cast<const float*>(ws + L.partial);
+  if (opt == kOptSGD)
+    return detail::apply_go<DT, kOptSGD>(W, momentum, long_list, long_table, counters, L.cap_long, tb, cfg.chunk, partial, lr, eps, s);
+  return detail::apply_go<DT, kOptAdagrad>(W, momentum, long_list, long_table, counters, L.cap_long, tb, cfg.chunk, partial, lr, eps, s);
+}
+
+}  // namespace tbe

@@ -1,0 +1,337 @@
+// TBE forward: pooled gather-sum over T tables in one launch, plus the
+// small-table histogram path on MFMA.
+//
+// PyTorch blog "Modernizing Table Batched Embeddings with FBTriton", section 2:
+// every bag of every table gathers its rows, scales each by its per-sample
+// weight when there is one, and sums them into one D-wide output row; fp16 /
+// bf16 tables accumulate in fp32 and fp32 tables in fp64.  "The general gather
+// path" there keeps several independent row loads in flight per program and
+// lets each program walk the tables for its bags; "The small-table histogram
+// and tensor-core path" counts the first 256 ids of each bag of a table with at
+// most 64 rows and multiplies the counts by the table on tensor cores.
+//
+// gfx950 mapping (generic path): one wave pools one bag at a time.  A row of D
+// elements is read by a group of D/VEC lanes with 16-byte (fp16/bf16: 8
+// elements, fp32: 4) or 8-byte vector loads, so one wave instruction fetches
+// 64/(D/VEC) rows; UNROLL such instructions are issued before any is summed.
+// The bag's ids are loaded coalesced, one per lane, and handed to the row
+// groups with lane shuffles; the 64 bags a wave walks in a row have their
+// offsets fetched in one coalesced load.  Per-group partial sums are combined
+// with xor shuffles and one group writes the output row.
+#include "tbe_device.h"
+#include "tbe_internal.h"
+
+namespace tbe {
+namespace {
+
+template <int DT, typename IT, bool PSW, int VEC, typename ACC, int UNROLL>
+__device__ __forceinline__ void pool_bag(const typename Fmt<DT>::S* __restrict__ Wt, int64_t E,
+                                         int D, const IT* __restrict__ indices,
+                                         const float* __restrict__ psw, int64_t s, int64_t e,
+                                         int lg, int col, bool act, ACC (&acc)[VEC]) {
+  const int lane = lane_id();
+  const int G = kWave >> lg;  // rows per wave instruction
+  const int g = lane >> lg;   // this lane's row group
+  for (int64_t j0 = s; j0 < e; j0 += kWave) {
+    const int n = static_cast<int>(min<int64_t>(kWave, e - j0));
+    int32_t myrow = -1;
+    float myw = 0.f;
+    if (lane < n) {
+      const int64_t r = static_cast<int64_t>(indices[j0 + lane]);
+      myrow = (static_cast<uint64_t>(r) < static_cast<uint64_t>(E)) ? static_cast<int32_t>(r) : -1;
+      if constexpr (PSW) myw = psw[j0 + lane];
+    }
+    for (int q0 = 0; q0 < n; q0 += G * UNROLL) {
+      float v[UNROLL][VEC];
+      float wq[UNROLL];
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        const int q = q0 + u * G + g;
+        const int row = __shfl(myrow, q & (kWave - 1));
+        if constexpr (PSW) wq[u] = __shfl(myw, q & (kWave - 1));
+        if (q < n && row >= 0 && act) {
+          load_vec<DT, VEC>(Wt + static_cast<int64_t>(row) * D + col, v[u]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) v[u][i] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+          if constexpr (PSW) acc[i] += static_cast<ACC>(wq[u]) * static_cast<ACC>(v[u][i]);
+          else acc[i] += static_cast<ACC>(v[u][i]);
+        }
+      }
+    }
+  }
+}
+
+template <int DT, typename IT, typename OT, bool PSW, int VEC, typename ACC, int UNROLL>
+__global__ __launch_bounds__(kBlock) void fwd_gather_kernel(
+    const typename Fmt<DT>::S* __restrict__ W, const IT* __restrict__ indices,
+    const OT* __restrict__ offsets, const float* __restrict__ psw, float* __restrict__ out,
+    const int64_t* __restrict__ meta, int32_t skip_t, int32_t n_tables, int32_t B,
+    int32_t out_width, int64_t N) {
+  const int lane = lane_id();
+  const int64_t wave = (static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x) >> 6;
+  const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * kBlock) >> 6;
+  const int64_t slots = static_cast<int64_t>(n_tables) * B;
+  int cur_t = -1;
+  TableMeta m{};
+  for (int64_t base = wave * kWave; base < slots; base += nwaves * kWave) {
+    // one bag per lane: its table, batch row and clamped [start, end)
+    const int64_t slot = base + lane;
+    int64_t s = 0, e = 0;
+    int32_t bt = 0, bb = 0;
+    if (slot < slots) {
+      const int32_t ti = static_cast<int32_t>(slot / B);
+      bb = static_cast<int32_t>(slot - static_cast<int64_t>(ti) * B);
+      bt = (skip_t >= 0 && ti >= skip_t) ? ti + 1 : ti;  // every table but skip_t
+      const int64_t bag = static_cast<int64_t>(bt) * B + bb;
+      s = static_cast<int64_t>(offsets[bag]);
+      e = static_cast<int64_t>(offsets[bag + 1]);
+      s = min(max(s, static_cast<int64_t>(0)), N);
+      e = min(max(e, s), N);
+    }
+    const int nb = static_cast<int>(min<int64_t>(kWave, slots - base));
+    for (int k = 0; k < nb; ++k) {
+      const int64_t sk = read_lane64(s, k), ek = read_lane64(e, k);
+      const int t = read_lane(bt, k), b = read_lane(bb, k);
+      if (t != cur_t) {
+        m = load_meta(meta, t);
+        cur_t = t;
+      }
+      const int D = static_cast<int>(m.D);
+      float* orow = out + static_cast<int64_t>(b) * out_width + m.col_base;
+      for (int cb = 0; cb < D; cb += kWave * VEC) {
+        const int w = min(D - cb, kWave * VEC);
+        const int lpr = pow2_ceil((w + VEC - 1) / VEC);
+        const int lg = __builtin_ctz(lpr);
+        const int c = lane & (lpr - 1);
+        const int col = cb + c * VEC;
+        const bool act = c * VEC < w;
+        ACC acc[VEC];
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) acc[i] = 0;
+        pool_bag<DT, IT, PSW, VEC, ACC, UNROLL>(W + m.w_base, m.E, D, indices, psw, sk, ek, lg,
+                                                col, act, acc);
+        for (int msk = lpr; msk < kWave; msk <<= 1) {
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) acc[i] += __shfl_xor(acc[i], msk);
+        }
+        if ((lane >> lg) == 0 && act) {
+#pragma unroll
+          for (int i = 0; i < VEC; i += 4) {
+            f32x4 o = {static_cast<float>(acc[i]), static_cast<float>(acc[i + 1]),
+                       static_cast<float>(acc[i + 2]), static_cast<float>(acc[i + 3])};
+            store_f4(orow + col + i, o);
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// histogram + MFMA path for one small table (E <= 64, 64 <= D <= 128, fp16)
+// ---------------------------------------------------------------------------
+// One wave owns 16 consecutive bags (one 16-row MFMA tile).  The wave counts
+// each bag's first 256 ids into an LDS histogram (16 x 64), turns it into the
+// fp16 A operand (counts <= 256 are exact in fp16), and multiplies it by the
+// table held transposed in LDS as the B operand with v_mfma_f32_16x16x16_f16
+// (fp32 accumulation).  The products count * w are exact in fp32; only the
+// accumulation rounds.  Ids beyond the first 256 of a bag are gathered and
+// added to the tile; the finished 16 x D tile leaves through LDS as 16-byte
+// row-contiguous stores.
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kHistRows = 64;   // K of the contraction (table rows, zero padded)
+constexpr int kHistCols = 128;  // max D
+constexpr int kHistBags = 16;   // M of one MFMA tile
+constexpr int kHistHead = 256;  // ids per bag counted into the histogram
+
+template <typename IT, typename OT>
+__global__ __launch_bounds__(kBlock) void fwd_hist_kernel(
+    const uint16_t* __restrict__ Wt, const IT* __restrict__ indices, const OT* __restrict__ offsets,
+    float* __restrict__ out, int64_t bag0, int32_t B, int32_t E, int32_t D, int64_t col_base,
+    int32_t out_width, int64_t N) {
+  __shared__ __align__(16) uint16_t s_wT[kHistCols * kHistRows];            // [col][row]
+  __shared__ __align__(16) float s_tile[kWavesPerBlock][kHistBags * kHistCols];
+  const int lane = lane_id();
+  const int w = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < kHistCols * kHistRows; i += kBlock) {
+    const int col = i / kHistRows, row = i % kHistRows;
+    s_wT[i] = (row < E && col < D) ? Wt[static_cast<int64_t>(row) * D + col] : 0;
+  }
+  __syncthreads();
+  uint32_t* cnt = reinterpret_cast<uint32_t*>(s_tile[w]);
+  float* otile = s_tile[w];
+  const int64_t tiles = (static_cast<int64_t>(B) + kHistBags - 1) / kHistBags;
+  for (int64_t tile = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + w; tile < tiles;
+       tile += static_cast<int64_t>(gridDim.x) * kWavesPerBlock) {
+    const int64_t b0 = tile * kHistBags;
+    const int nbag = static_cast<int>(min<int64_t>(kHistBags, B - b0));
+    for (int i = lane; i < kHistBags * kHistRows; i += kWave) cnt[i] = 0u;
+    int64_t o = 0;
+    if (lane <= nbag) {
+      o = static_cast<int64_t>(offsets[bag0 + b0 + lane]);
+      o = min(max(o, static_cast<int64_t>(0)), N);
+    }
+    __builtin_amdgcn_wave_barrier();
+    for (int i = 0; i < nbag; ++i) {
+      const int64_t s = read_lane64(o, i);
+      const int64_t e = max(read_lane64(o, i + 1), s);
+      const int64_t eh = min(e, s + kHistHead);
+      for (int64_t j = s + lane; j < eh; j += kWave) {
+        const int64_t r = static_cast<int64_t>(indices[j]);
+        if (static_cast<uint64_t>(r) < static_cast<uint64_t>(E)) atomicAdd(&cnt[i * kHistRows + r], 1u);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    // A operand: lane l holds bag l%16, rows 16s + 4(l/16) + [0, 4)
+    half4_t a[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int base = (lane & 15) * kHistRows + 16 * s + 4 * (lane >> 4);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) a[s][q] = static_cast<_Float16>(static_cast<float>(cnt[base + q]));
+    }
+    __builtin_amdgcn_wave_barrier();
+    for (int n = 0; n < D / 16; ++n) {
+      float4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        // B operand: lane l holds column 16n + l%16, rows 16s + 4(l/16) + [0, 4)
+        const half4_t bf = *reinterpret_cast<const half4_t*>(
+            &s_wT[(16 * n + (lane & 15)) * kHistRows + 16 * s + 4 * (lane >> 4)]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x16f16(a[s], bf, acc, 0, 0, 0);
+      }
+      // result: lane l holds column 16n + l%16 of bags 4(l/16) + [0, 4)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) otile[(4 * (lane >> 4) + q) * kHistCols + 16 * n + (lane & 15)] = acc[q];
+    }
+    __builtin_amdgcn_wave_barrier();
+    // ids past the first 256 of a bag: gathered from the LDS copy of the table
+    for (int i = 0; i < nbag; ++i) {
+      const int64_t s = read_lane64(o, i);
+      const int64_t e = max(read_lane64(o, i + 1), s);
+      for (int64_t j = s + kHistHead; j < e; ++j) {
+        const int64_t r = static_cast<int64_t>(indices[j]);
+        if (static_cast<uint64_t>(r) >= static_cast<uint64_t>(E)) continue;
+        for (int col = lane; col < D; col += kWave)
+          otile[i * kHistCols + col] += static_cast<float>(
+              __builtin_bit_cast(_Float16, s_wT[col * kHistRows + r]));
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    const int c4n = D / 4;
+    for (int x = lane; x < nbag * c4n; x += kWave) {
+      const int i = x / c4n, c4 = x - i * c4n;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(&otile[i * kHistCols + 4 * c4]);
+      store_f4(out + (b0 + i) * out_width + col_base + 4 * c4, v);
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+int grid_for(int64_t work_waves) {
+  const int64_t cap = static_cast<int64_t>(device_cu_count()) * 8;  // 8 workgroups (32 waves) per CU
+  int64_t blocks = (work_waves + kWavesPerBlock - 1) / kWavesPerBlock;
+  if (blocks > cap) blocks = cap;
+  if (blocks < 1) blocks = 1;
+  return static_cast<int>(blocks);
+}
+
+template <int DT, typename IT, typename OT, bool PSW, int VEC, typename ACC>
+tbe_status gather_go(const tbe_tables* tb, const void* W, const IndexArgs& ia, const float* psw,
+                     float* out, int skip, int nt, int unroll, hipStream_t s) {
+  const int64_t slots = static_cast<int64_t>(nt) * tb->B;
+  const int grid = grid_for((slots + kWave - 1) / kWave);
+  using S = typename Fmt<DT>::S;
+  ProfScope ps("fwd_gather", s);
+#define TBE_FWD_LAUNCH(U)                                                                      \
+  hipLaunchKernelGGL((fwd_gather_kernel<DT, IT, OT, PSW, VEC, ACC, U>), dim3(grid), dim3(kBlock), \
+                     0, s, static_cast<const S*>(W), static_cast<const IT*>(ia.indices),        \
+                     static_cast<const OT*>(ia.offsets), psw, out, tb->meta, skip, nt, tb->B,      \
+                     tb->out_width, ia.N)
+  if (unroll <= 2) TBE_FWD_LAUNCH(2);
+  else if (unroll <= 4) TBE_FWD_LAUNCH(4);
+  else TBE_FWD_LAUNCH(8);
+#undef TBE_FWD_LAUNCH
+  return check_launch("fwd_gather");
+}
+
+template <int DT, typename IT, typename OT>
+tbe_status gather_dispatch_psw(const tbe_tables* tb, const void* W, const IndexArgs& ia,
+                               const float* psw, float* out, int skip, int nt, int unroll,
+                               hipStream_t s) {
+  if constexpr (DT == 0) {
+    if (psw) return gather_go<DT, IT, OT, true, 4, double>(tb, W, ia, psw, out, skip, nt, unroll, s);
+    return gather_go<DT, IT, OT, false, 4, double>(tb, W, ia, psw, out, skip, nt, unroll, s);
+  } else {
+    if (tb->all_D_mult8) {
+      if (psw) return gather_go<DT, IT, OT, true, 8, float>(tb, W, ia, psw, out, skip, nt, unroll, s);
+      return gather_go<DT, IT, OT, false, 8, float>(tb, W, ia, psw, out, skip, nt, unroll, s);
+    }
+    if (psw) return gather_go<DT, IT, OT, true, 4, float>(tb, W, ia, psw, out, skip, nt, unroll, s);
+    return gather_go<DT, IT, OT, false, 4, float>(tb, W, ia, psw, out, skip, nt, unroll, s);
+  }
+}
+
+template <int DT>
+tbe_status gather_dispatch_idx(const tbe_tables* tb, const void* W, const IndexArgs& ia,
+                               const float* psw, float* out, int skip, int nt, int unroll,
+                               hipStream_t s) {
+  if (ia.itype == TBE_I32) {
+    if (ia.otype == TBE_I32)
+      return gather_dispatch_psw<DT, int32_t, int32_t>(tb, W, ia, psw, out, skip, nt, unroll, s);
+    return gather_dispatch_psw<DT, int32_t, int64_t>(tb, W, ia, psw, out, skip, nt, unroll, s);
+  }
+  if (ia.otype == TBE_I32)
+    return gather_dispatch_psw<DT, int64_t, int32_t>(tb, W, ia, psw, out, skip, nt, unroll, s);
+  return gather_dispatch_psw<DT, int64_t, int64_t>(tb, W, ia, psw, out, skip, nt, unroll, s);
+}
+
+template <typename IT, typename OT>
+tbe_status hist_go(const tbe_tables* tb, const void* W, const IndexArgs& ia, float* out,
+                   hipStream_t s) {
+  const int64_t tiles = (static_cast<int64_t>(tb->B) + kHistBags - 1) / kHistBags;
+  const int grid = grid_for(tiles);
+  ProfScope ps("fwd_hist", s);
+  hipLaunchKernelGGL((fwd_hist_kernel<IT, OT>), dim3(grid), dim3(kBlock), 0, s,
+                     static_cast<const uint16_t*>(W) + tb->hist_w_base,
+                     static_cast<const IT*>(ia.indices), static_cast<const OT*>(ia.offsets), out,
+                     static_cast<int64_t>(tb->hist_table) * tb->B, tb->B, tb->hist_E, tb->hist_D,
+                     static_cast<int64_t>(tb->hist_col), tb->out_width, ia.N);
+  return check_launch("fwd_hist");
+}
+
+}  // namespace
+
+tbe_status launch_forward_gather(const tbe_tables* tb, const void* W, const IndexArgs& ia,
+                                 const float* psw, float* out, int skip_table,
+                                 int unroll, hipStream_t s) {
+  const int n_tables = skip_table >= 0 ? tb->T - 1 : tb->T;
+  if (n_tables <= 0 || tb->B == 0) return TBE_OK;
+  switch (tb->w_dtype) {
+    case TBE_F32: return gather_dispatch_idx<0>(tb, W, ia, psw, out, skip_table, n_tables, unroll, s);
+    case TBE_F16: return gather_dispatch_idx<1>(tb, W, ia, psw, out, skip_table, n_tables, unroll, s);
+    default: return gather_dispatch_idx<2>(tb, W, ia, psw, out, skip_table, n_tables, unroll, s);
+  }
+}
+
+tbe_status launch_forward_hist(const tbe_tables* tb, const void* W, const IndexArgs& ia,
+                               float* out, hipStream_t s) {
+  if (tb->B == 0 || tb->hist_table < 0) return TBE_OK;
+  if (ia.itype == TBE_I32) {
+    if (ia.otype == TBE_I32) return hist_go<int32_t, int32_t>(tb, W, ia, out, s);
+    return hist_go<int32_t, int64_t>(tb, W, ia, out, s);
+  }
+  if (ia.otype == TBE_I32) return hist_go<int64_t, int32_t>(tb, W, ia, out, s);
+  return hist_go<int64_t, int64_t>(tb, W, ia, out, s);
+}
+
+}  // namespace tbe

@@ -1,0 +1,97 @@
+// Host-side internals shared by the TBE translation units (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/tbe.h"
+
+namespace tbe {
+
+// ---------------------------------------------------------------------------
+// errors and kernel timing
+// ---------------------------------------------------------------------------
+void set_error(const char* fmt, ...);
+tbe_status check_launch(const char* what);
+
+// Records a pair of events around a launch when the kernel is the one
+// selected with tbe_profile_select.
+struct ProfScope {
+  ProfScope(const char* kernel, hipStream_t s);
+  ~ProfScope();
+  int slot;
+  hipStream_t stream;
+};
+
+// ---------------------------------------------------------------------------
+// launch geometry
+// ---------------------------------------------------------------------------
+constexpr int kBlock = 256;            // threads per workgroup in every kernel
+constexpr int kWavesPerBlock = kBlock / 64;
+int device_cu_count();                 // compute units of the current device (cached)
+inline int64_t hmin(int64_t a, int64_t b) { return a < b ? a : b; }
+inline int64_t hmax(int64_t a, int64_t b) { return a > b ? a : b; }
+
+// Radix sort geometry (least-significant digit first, up to 9 bits a pass)
+constexpr int kRadixMaxBits = 9;
+constexpr int kRadixDigits = 1 << kRadixMaxBits;
+constexpr int kRadixItems = 16;                       // keys per thread per tile
+constexpr int kRadixTile = kBlock * kRadixItems;      // 4096 keys
+
+struct Config {
+  int threshold, chunk, hist_enable, fwd_unroll, bwd_unroll, sort_blocks;
+};
+Config resolve_config(const tbe_config* c);
+
+// Workspace carve-up of the backward / transpose (byte offsets, 256-aligned)
+struct BwdLayout {
+  int64_t N;
+  size_t keys[2], pay[2], bag_of, run_key, run_start;
+  size_t long_list, long_table, chunk_list, partial, short_list[TBE_NUM_BUCKETS];
+  size_t sort_hist, seg_cnt, counters, total;
+  int64_t cap_long, cap_chunk, cap_short[TBE_NUM_BUCKETS];
+  int64_t seg;        // keys per sort / RLE block (multiple of kRadixTile)
+  int nblocks;        // sort / RLE blocks
+  int passes;         // radix passes
+  int shift[4], bits[4];
+  int key_bits;
+};
+BwdLayout bwd_layout(const tbe_tables* tb, int64_t N, int weighted, const Config& cfg);
+
+constexpr int kOptSGD = 0;
+constexpr int kOptAdagrad = 1;
+
+enum Counter { kRuns = 0, kLong = 1, kChunks = 2, kShort0 = 3, kNumCounters = 16 };
+
+// ---------------------------------------------------------------------------
+// launchers (each returns TBE_OK or the launch error)
+// ---------------------------------------------------------------------------
+struct IndexArgs {
+  const void* indices; int itype;
+  const void* offsets; int otype;
+  int64_t N;
+};
+
+tbe_status launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
+
+tbe_status launch_forward_gather(const tbe_tables* tb, const void* W, const IndexArgs& ia,
+                                 const float* psw, float* out, int skip_table, int unroll,
+                                 hipStream_t s);
+tbe_status launch_forward_hist(const tbe_tables* tb, const void* W, const IndexArgs& ia,
+                               float* out, hipStream_t s);
+
+tbe_status launch_bounds(const tbe_tables* tb, void* indices, int itype, void* offsets, int otype,
+                         int64_t N, int64_t* counts, void* ws, hipStream_t s);
+size_t bounds_workspace(const tbe_tables* tb);
+
+tbe_status launch_transpose(const tbe_tables* tb, const IndexArgs& ia, int weighted,
+                            char* ws, const BwdLayout& L, const Config& cfg, int* final_buf,
+                            hipStream_t s);
+
+tbe_status launch_backward_update(const tbe_tables* tb, void* W, float* momentum, int opt,
+                                  const float* psw, const float* grad_out, float lr, float eps,
+                                  char* ws, const BwdLayout& L, int final_buf, const Config& cfg,
+                                  hipStream_t s);
+
+}  // namespace tbe

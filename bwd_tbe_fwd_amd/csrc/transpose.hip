@@ -1,0 +1,556 @@
+// Backward transpose and routing: linearize, stable LSD radix sort, run-length
+// encoding, and classification of runs by segment length with D buckets.
+//
+// PyTorch blog "Modernizing Table Batched Embeddings with FBTriton", section 3:
+// transpose_embedding_input inverts the batch into runs, each one unique
+// (table, row) with the lookups that touched it, so that no two runs write the
+// same row; runs are routed by segment length (SL, the lookups of a run):
+// SL < 256 to short_run, longer runs to 256-lookup chunks.  Section 4, problem 3:
+// short runs are bucketed by next_pow2(D) during classification, and run counts
+// stay on the device (stream compaction with one atomic per block and a
+// prefix sum inside the block), so nothing is read back.
+// "Table-Batched Embeddings in Triton", section 2: the linearized id is the
+// table's first row plus the local id, sorted stably.
+//
+// gfx950 design:
+//  - linearize: a wave takes 64 consecutive bags (their offsets in one load),
+//    and its lanes walk the contiguous lookups of those bags, each lane finding
+//    its bag by a 6-step binary search over the 64 end offsets (lane shuffles).
+//  - sort: reduce-then-scan LSD radix, up to 9 bits a pass (26-bit keys take 3
+//    passes).  A fixed number of blocks each own a contiguous segment; per pass:
+//    upsweep (digit counts per block), a per-digit scan across blocks, and a
+//    downsweep that ranks each 4096-key tile stably in LDS (wave ballots find
+//    the lanes holding the same digit; the lowest lane adds the count), sorts
+//    the tile by digit in LDS and writes each digit's keys contiguously.  No
+//    inter-block waiting, so every wave always finishes.
+//  - RLE: head flags counted per block, scanned, then written in order.
+//  - classify: one thread per run, LDS counters per category, one global
+//    atomic per category per block.
+#include "tbe_device.h"
+#include "tbe_internal.h"
+
+namespace tbe {
+namespace {
+
+// ---------------------------------------------------------------------------
+// block-wide scans (256 threads)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t block_exclusive_sum(uint32_t v, uint32_t* s_tmp,
+                                                        uint32_t* total) {
+  const int lane = lane_id(), w = threadIdx.x >> 6;
+  uint32_t inc = v;
+  for (int d = 1; d < kWave; d <<= 1) {
+    const uint32_t u = __shfl_up(inc, d);
+    if (lane >= d) inc += u;
+  }
+  if (lane == kWave - 1) s_tmp[w] = inc;
+  __syncthreads();
+  uint32_t pre = 0, tot = 0;
+#pragma unroll
+  for (int k = 0; k < kWavesPerBlock; ++k) {
+    const uint32_t x = s_tmp[k];
+    if (k < w) pre += x;
+    tot += x;
+  }
+  __syncthreads();
+  if (total) *total = tot;
+  return pre + inc - v;
+}
+
+__device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t* s_tmp) {
+  for (int m = 1; m < kWave; m <<= 1) v += __shfl_xor(v, m);
+  const int w = threadIdx.x >> 6;
+  if (lane_id() == 0) s_tmp[w] = v;
+  __syncthreads();
+  uint32_t t = 0;
+#pragma unroll
+  for (int k = 0; k < kWavesPerBlock; ++k) t += s_tmp[k];
+  __syncthreads();
+  return t;
+}
+
+// lanes whose digit equals this lane's digit, among the lanes in `valid`
+__device__ __forceinline__ uint64_t match_digit(uint32_t d, int bits, uint64_t valid) {
+  uint64_t peers = valid;
+  for (int b = 0; b < bits; ++b) {
+    const bool bit = (d >> b) & 1u;
+    const uint64_t m = __ballot(bit);
+    peers &= bit ? m : ~m;
+  }
+  return peers;
+}
+
+// ---------------------------------------------------------------------------
+// linearize
+// ---------------------------------------------------------------------------
+template <typename IT, typename OT, bool WEIGHTED>
+__global__ __launch_bounds__(kBlock) void linearize_kernel(
+    const IT* __restrict__ indices, const OT* __restrict__ offsets, const int64_t* __restrict__ meta,
+    int32_t B, int64_t nbags, int32_t N, uint32_t sentinel, uint32_t* __restrict__ keys,
+    uint32_t* __restrict__ pay, uint32_t* __restrict__ bag_of) {
+  const int lane = lane_id();
+  const int64_t wave = (static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x) >> 6;
+  const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * kBlock) >> 6;
+  for (int64_t g0 = wave * kWave; g0 < nbags; g0 += nwaves * kWave) {
+    const int64_t bag = g0 + lane;
+    const int32_t S = static_cast<int32_t>(
+        min(max(static_cast<int64_t>(offsets[g0]), static_cast<int64_t>(0)), static_cast<int64_t>(N)));
+    int32_t e = S;
+    int64_t rb = 0, E = 0;
+    if (bag < nbags) {
+      e = static_cast<int32_t>(min(max(static_cast<int64_t>(offsets[bag + 1]), static_cast<int64_t>(S)),
+                                   static_cast<int64_t>(N)));
+      const int t = static_cast<int>(bag / B);
+      rb = meta[4 * t];
+      E = meta[4 * (t + 1)] - rb;
+    }
+    // monotone end offsets across the 64 lanes (inclusive running max)
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int32_t u = __shfl_up(e, d);
+      if (lane >= d) e = max(e, u);
+    }
+    const int32_t Eend = __shfl(e, kWave - 1);
+    for (int32_t base = S; base < Eend; base += kWave) {
+      const int32_t p = base + lane;
+      const bool valid = p < Eend;
+      // first lane l with e_l > p
+      int lo = 0, hi = kWave - 1;
+#pragma unroll
+      for (int step = 0; step < 6; ++step) {
+        const int mid = (lo + hi) >> 1;
+        const int32_t em = __shfl(e, mid);
+        if (em > p) hi = mid; else lo = mid + 1;
+      }
+      const int k = lo;
+      const int64_t rbk = __shfl(rb, k);
+      const int64_t Ek = __shfl(E, k);
+      if (valid) {
+        const int64_t r = static_cast<int64_t>(indices[p]);
+        const uint32_t key = (static_cast<uint64_t>(r) < static_cast<uint64_t>(Ek))
+                                 ? static_cast<uint32_t>(rbk + r) : sentinel;
+        keys[p] = key;
+        const uint32_t b = static_cast<uint32_t>(g0 + k);
+        if constexpr (WEIGHTED) {
+          pay[p] = static_cast<uint32_t>(p);
+          bag_of[p] = b;
+        } else {
+          pay[p] = b;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// radix sort
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kBlock) void radix_upsweep(const uint32_t* __restrict__ keys, int64_t N,
+                                                        int64_t seg, int shift, int bits,
+                                                        uint32_t* __restrict__ hist, int nblk) {
+  __shared__ uint32_t s_cnt[kWavesPerBlock][kRadixDigits];
+  const int lane = lane_id(), w = threadIdx.x >> 6;
+  const int ndig = 1 << bits;
+  const uint32_t mask = static_cast<uint32_t>(ndig - 1);
+  for (int i = lane; i < ndig; i += kWave) s_cnt[w][i] = 0;
+  __builtin_amdgcn_wave_barrier();
+  const int64_t lo = blockIdx.x * seg, hi = min(lo + seg, N);
+  // each wave reads 4 x 64 consecutive keys per step
+  for (int64_t base = lo + w * 4 * kWave; base < hi; base += 4 * kBlock) {
+    uint32_t k[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int64_t i = base + s * kWave + lane;
+      k[s] = i < hi ? keys[i] : 0u;
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int64_t i = base + s * kWave + lane;
+      const bool valid = i < hi;
+      const uint32_t d = (k[s] >> shift) & mask;
+      const uint64_t peers = match_digit(d, bits, __ballot(valid));
+      if (valid && lane == __ffsll(static_cast<long long>(peers)) - 1) s_cnt[w][d] += __popcll(peers);
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+  __syncthreads();
+  for (int d = threadIdx.x; d < ndig; d += kBlock) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int q = 0; q < kWavesPerBlock; ++q) c += s_cnt[q][d];
+    hist[static_cast<int64_t>(d) * nblk + blockIdx.x] = c;
+  }
+}
+
+// per digit (one workgroup each): exclusive scan of its per-block counts, total to tot[d]
+__global__ __launch_bounds__(kBlock) void radix_scan(uint32_t* __restrict__ hist, int nblk,
+                                                     uint32_t* __restrict__ tot) {
+  __shared__ uint32_t s_tmp[kWavesPerBlock];
+  uint32_t* row = hist + static_cast<int64_t>(blockIdx.x) * nblk;
+  const int ipt = (nblk + kBlock - 1) / kBlock;
+  const int i0 = threadIdx.x * ipt;
+  uint32_t v[16];
+  uint32_t sum = 0;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    v[q] = (q < ipt && i0 + q < nblk) ? row[i0 + q] : 0u;
+    sum += v[q];
+  }
+  uint32_t total;
+  uint32_t run = block_exclusive_sum(sum, s_tmp, &total);
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    if (q < ipt && i0 + q < nblk) row[i0 + q] = run;
+    run += v[q];
+  }
+  if (threadIdx.x == 0) tot[blockIdx.x] = total;
+}
+
+__global__ __launch_bounds__(kBlock) void radix_downsweep(
+    const uint32_t* __restrict__ kin, const uint32_t* __restrict__ pin, uint32_t* __restrict__ kout,
+    uint32_t* __restrict__ pout, int64_t N, int64_t seg, int shift, int bits,
+    const uint32_t* __restrict__ hist, const uint32_t* __restrict__ tot, int nblk) {
+  __shared__ uint32_t s_base[kRadixDigits];
+  __shared__ uint32_t s_wcnt[kWavesPerBlock][kRadixDigits];
+  __shared__ uint32_t s_toff[kRadixDigits];
+  __shared__ uint32_t s_tcnt[kRadixDigits];
+  __shared__ uint32_t s_key[kRadixTile];
+  __shared__ uint32_t s_pay[kRadixTile];
+  __shared__ uint32_t s_tmp[kWavesPerBlock];
+  const int lane = lane_id(), w = threadIdx.x >> 6;
+  const int ndig = 1 << bits;
+  const uint32_t mask = static_cast<uint32_t>(ndig - 1);
+  // global base of each digit for this block: digits below + earlier blocks
+  {
+    const int d0 = 2 * threadIdx.x, d1 = d0 + 1;
+    const uint32_t a = d0 < ndig ? tot[d0] : 0u, b = d1 < ndig ? tot[d1] : 0u;
+    const uint32_t ex = block_exclusive_sum(a + b, s_tmp, nullptr);
+    if (d0 < ndig) s_base[d0] = ex + hist[static_cast<int64_t>(d0) * nblk + blockIdx.x];
+    if (d1 < ndig) s_base[d1] = ex + a + hist[static_cast<int64_t>(d1) * nblk + blockIdx.x];
+  }
+  __syncthreads();
+  const int64_t lo = blockIdx.x * seg, hi = min(lo + seg, N);
+  for (int64_t tile = lo; tile < hi; tile += kRadixTile) {
+    const int tn = static_cast<int>(min<int64_t>(kRadixTile, hi - tile));
+    for (int i = lane; i < ndig; i += kWave) s_wcnt[w][i] = 0;
+    uint32_t k[kRadixItems], p[kRadixItems], r[kRadixItems];
+    const int64_t wbase = tile + w * (kRadixItems * kWave);
+#pragma unroll
+    for (int s = 0; s < kRadixItems; ++s) {
+      const int64_t i = wbase + s * kWave + lane;
+      const bool valid = i < hi;
+      k[s] = valid ? kin[i] : 0u;
+      p[s] = valid ? pin[i] : 0u;
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int s = 0; s < kRadixItems; ++s) {
+      const bool valid = wbase + s * kWave + lane < hi;
+      const uint32_t d = (k[s] >> shift) & mask;
+      const uint64_t peers = match_digit(d, bits, __ballot(valid));
+      const uint32_t prior = valid ? s_wcnt[w][d] : 0u;
+      r[s] = prior + __popcll(peers & lanemask_lt());
+      __builtin_amdgcn_wave_barrier();
+      if (valid && lane == __ffsll(static_cast<long long>(peers)) - 1)
+        s_wcnt[w][d] = prior + __popcll(peers);
+      __builtin_amdgcn_wave_barrier();
+    }
+    __syncthreads();
+    for (int d = threadIdx.x; d < ndig; d += kBlock) {
+      const uint32_t c0 = s_wcnt[0][d], c1 = s_wcnt[1][d], c2 = s_wcnt[2][d], c3 = s_wcnt[3][d];
+      s_wcnt[0][d] = 0;
+      s_wcnt[1][d] = c0;
+      s_wcnt[2][d] = c0 + c1;
+      s_wcnt[3][d] = c0 + c1 + c2;
+      s_tcnt[d] = c0 + c1 + c2 + c3;
+    }
+    __syncthreads();
+    {
+      const int d0 = 2 * threadIdx.x, d1 = d0 + 1;
+      const uint32_t a = d0 < ndig ? s_tcnt[d0] : 0u, b = d1 < ndig ? s_tcnt[d1] : 0u;
+      const uint32_t ex = block_exclusive_sum(a + b, s_tmp, nullptr);
+      if (d0 < ndig) s_toff[d0] = ex;
+      if (d1 < ndig) s_toff[d1] = ex + a;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < kRadixItems; ++s) {
+      if (wbase + s * kWave + lane < hi) {
+        const uint32_t d = (k[s] >> shift) & mask;
+        const uint32_t pos = s_toff[d] + s_wcnt[w][d] + r[s];
+        s_key[pos] = k[s];
+        s_pay[pos] = p[s];
+      }
+    }
+    __syncthreads();
+    for (int j = threadIdx.x; j < tn; j += kBlock) {
+      const uint32_t key = s_key[j];
+      const uint32_t d = (key >> shift) & mask;
+      const uint32_t g = s_base[d] + (static_cast<uint32_t>(j) - s_toff[d]);
+      kout[g] = key;
+      pout[g] = s_pay[j];
+    }
+    __syncthreads();
+    for (int d = threadIdx.x; d < ndig; d += kBlock) s_base[d] += s_tcnt[d];
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// run-length encoding
+// ---------------------------------------------------------------------------
+constexpr int kRleItems = 4;
+
+__global__ __launch_bounds__(kBlock) void rle_count(const uint32_t* __restrict__ keys, int64_t N,
+                                                    int64_t seg, uint32_t* __restrict__ cnt) {
+  __shared__ uint32_t s_tmp[kWavesPerBlock];
+  const int64_t lo = blockIdx.x * seg, hi = min(lo + seg, N);
+  uint32_t c = 0;
+  for (int64_t i = lo + threadIdx.x; i < hi; i += kBlock)
+    c += (i == 0 || keys[i] != keys[i - 1]) ? 1u : 0u;
+  c = block_sum(c, s_tmp);
+  if (threadIdx.x == 0) cnt[blockIdx.x] = c;
+}
+
+// exclusive scan of the per-block head counts (one workgroup); run count to counters
+__global__ __launch_bounds__(kBlock) void rle_scan(uint32_t* __restrict__ cnt, int nblk,
+                                                   int32_t* __restrict__ counters,
+                                                   uint32_t* __restrict__ run_start, int64_t N) {
+  __shared__ uint32_t s_tmp[kWavesPerBlock];
+  const int ipt = (nblk + kBlock - 1) / kBlock;
+  const int i0 = threadIdx.x * ipt;
+  uint32_t v[16];
+  uint32_t sum = 0;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    v[q] = (q < ipt && i0 + q < nblk) ? cnt[i0 + q] : 0u;
+    sum += v[q];
+  }
+  uint32_t total;
+  uint32_t run = block_exclusive_sum(sum, s_tmp, &total);
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    if (q < ipt && i0 + q < nblk) cnt[i0 + q] = run;
+    run += v[q];
+  }
+  if (threadIdx.x == 0) {
+    counters[kRuns] = static_cast<int32_t>(total);
+    run_start[total] = static_cast<uint32_t>(N);
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void rle_write(const uint32_t* __restrict__ keys, int64_t N,
+                                                    int64_t seg, const uint32_t* __restrict__ cnt,
+                                                    uint32_t* __restrict__ run_key,
+                                                    uint32_t* __restrict__ run_start) {
+  __shared__ uint32_t s_tmp[kWavesPerBlock];
+  __shared__ uint32_t s_base;
+  const int64_t lo = blockIdx.x * seg, hi = min(lo + seg, N);
+  if (threadIdx.x == 0) s_base = cnt[blockIdx.x];
+  __syncthreads();
+  for (int64_t tile = lo; tile < hi; tile += kBlock * kRleItems) {
+    const int64_t i0 = tile + threadIdx.x * kRleItems;
+    uint32_t k[kRleItems];
+    bool head[kRleItems];
+    uint32_t c = 0;
+    uint32_t prev = (i0 > 0 && i0 < hi) ? keys[i0 - 1] : 0u;
+#pragma unroll
+    for (int q = 0; q < kRleItems; ++q) {
+      const int64_t i = i0 + q;
+      k[q] = i < hi ? keys[i] : 0u;
+      head[q] = i < hi && (i == 0 || k[q] != prev);
+      prev = k[q];
+      c += head[q] ? 1u : 0u;
+    }
+    uint32_t total;
+    uint32_t r = s_base + block_exclusive_sum(c, s_tmp, &total);
+#pragma unroll
+    for (int q = 0; q < kRleItems; ++q) {
+      if (head[q]) {
+        run_key[r] = k[q];
+        run_start[r] = static_cast<uint32_t>(i0 + q);
+        ++r;
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) s_base += total;
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// classification: long runs (with chunk plan) and short runs per D bucket
+// ---------------------------------------------------------------------------
+struct ShortLists {
+  uint4* p[TBE_NUM_BUCKETS];
+  int64_t cap[TBE_NUM_BUCKETS];
+};
+
+__global__ __launch_bounds__(kBlock) void classify_kernel(
+    const uint32_t* __restrict__ run_key, const uint32_t* __restrict__ run_start,
+    int32_t* __restrict__ counters, const int64_t* __restrict__ meta, int T, uint32_t total_rows,
+    int threshold, int chunk, uint4* __restrict__ long_list, uint32_t* __restrict__ long_table,
+    uint2* __restrict__ chunk_list, int64_t cap_long, int64_t cap_chunk, ShortLists lists) {
+  constexpr int kCats = 1 + TBE_NUM_BUCKETS;
+  __shared__ int32_t s_cnt[kCats];
+  __shared__ int32_t s_base[kCats];
+  __shared__ int32_t s_chunks, s_chunk_base;
+  const int64_t n = counters[kRuns];
+  for (int64_t r0 = static_cast<int64_t>(blockIdx.x) * kBlock; r0 < n;
+       r0 += static_cast<int64_t>(gridDim.x) * kBlock) {
+    if (threadIdx.x < kCats) s_cnt[threadIdx.x] = 0;
+    if (threadIdx.x == 0) s_chunks = 0;
+    __syncthreads();
+    const int64_t r = r0 + threadIdx.x;
+    int cat = -1, rank = 0, t = 0;
+    uint32_t key = 0, start = 0, len = 0, nch = 0;
+    int32_t my_cb = 0;
+    if (r < n) {
+      key = run_key[r];
+      start = run_start[r];
+      len = run_start[r + 1] - start;
+      if (key < total_rows) {
+        t = table_of_key(meta, T, key);
+        if (len >= static_cast<uint32_t>(threshold)) {
+          cat = 0;
+          nch = (len + chunk - 1) / chunk;
+          my_cb = atomicAdd(&s_chunks, static_cast<int32_t>(nch));
+        } else {
+          cat = 1 + bucket_of_D(static_cast<int>(meta[4 * t + 3]));
+        }
+        rank = atomicAdd(&s_cnt[cat], 1);
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x < kCats && s_cnt[threadIdx.x] > 0)
+      s_base[threadIdx.x] = atomicAdd(&counters[threadIdx.x == 0 ? kLong : kShort0 + threadIdx.x - 1],
+                                      s_cnt[threadIdx.x]);
+    if (threadIdx.x == kCats && s_chunks > 0) s_chunk_base = atomicAdd(&counters[kChunks], s_chunks);
+    __syncthreads();
+    if (cat == 0) {
+      const int64_t li = static_cast<int64_t>(s_base[0]) + rank;
+      const int64_t cb = static_cast<int64_t>(s_chunk_base) + my_cb;
+      if (li < cap_long) {
+        long_list[li] = make_uint4(key, start, len, static_cast<uint32_t>(cb));
+        long_table[li] = static_cast<uint32_t>(t);
+        for (uint32_t c = 0; c < nch; ++c)
+          if (cb + c < cap_chunk) chunk_list[cb + c] = make_uint2(static_cast<uint32_t>(li), c);
+      }
+    } else if (cat > 0) {
+      const int b = cat - 1;
+      const int64_t slot = static_cast<int64_t>(s_base[cat]) + rank;
+      if (slot < lists.cap[b]) lists.p[b][slot] = make_uint4(key, start, len, static_cast<uint32_t>(t));
+    }
+    __syncthreads();
+  }
+}
+
+__global__ void fill_i32_kernel(int32_t* p, int32_t v, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+template <typename IT, typename OT>
+tbe_status linearize_go(const tbe_tables* tb, const IndexArgs& ia, int weighted, uint32_t* keys,
+                        uint32_t* pay, uint32_t* bag_of, hipStream_t s) {
+  const int64_t nbags = static_cast<int64_t>(tb->T) * tb->B;
+  const int64_t groups = (nbags + kWave - 1) / kWave;
+  const int64_t cap = static_cast<int64_t>(device_cu_count()) * 8 * kWavesPerBlock;
+  const int grid = static_cast<int>(hmax(1, (hmin(groups, cap) + kWavesPerBlock - 1) / kWavesPerBlock));
+  const uint32_t sentinel = static_cast<uint32_t>(tb->total_rows);
+  ProfScope ps("linearize", s);
+  if (weighted)
+    hipLaunchKernelGGL((linearize_kernel<IT, OT, true>), dim3(grid), dim3(kBlock), 0, s,
+                       static_cast<const IT*>(ia.indices), static_cast<const OT*>(ia.offsets), tb->meta,
+                       tb->B, nbags, static_cast<int32_t>(ia.N), sentinel, keys, pay, bag_of);
+  else
+    hipLaunchKernelGGL((linearize_kernel<IT, OT, false>), dim3(grid), dim3(kBlock), 0, s,
+                       static_cast<const IT*>(ia.indices), static_cast<const OT*>(ia.offsets), tb->meta,
+                       tb->B, nbags, static_cast<int32_t>(ia.N), sentinel, keys, pay, bag_of);
+  return check_launch("linearize");
+}
+
+}  // namespace
+
+tbe_status launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s) {
+  if (n <= 0) return TBE_OK;
+  ProfScope ps("init", s);
+  hipLaunchKernelGGL(fill_i32_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, p, v, n);
+  return check_launch("init");
+}
+
+tbe_status launch_transpose(const tbe_tables* tb, const IndexArgs& ia, int weighted, char* ws,
+                            const BwdLayout& L, const Config& cfg, int* final_buf, hipStream_t s) {
+  int32_t* counters = reinterpret_cast<int32_t*>(ws + L.counters);
+  if (tbe_status st = launch_fill_i32(counters, 0, kNumCounters, s)) return st;
+  const int64_t N = L.N;
+  *final_buf = 0;
+  if (N == 0) {
+    uint32_t* rs = reinterpret_cast<uint32_t*>(ws + L.run_start);
+    return launch_fill_i32(reinterpret_cast<int32_t*>(rs), 0, 1, s);
+  }
+  uint32_t* keys[2] = {reinterpret_cast<uint32_t*>(ws + L.keys[0]), reinterpret_cast<uint32_t*>(ws + L.keys[1])};
+  uint32_t* pay[2] = {reinterpret_cast<uint32_t*>(ws + L.pay[0]), reinterpret_cast<uint32_t*>(ws + L.pay[1])};
+  uint32_t* bag_of = weighted ? reinterpret_cast<uint32_t*>(ws + L.bag_of) : nullptr;
+  tbe_status st;
+  if (ia.itype == TBE_I32)
+    st = ia.otype == TBE_I32 ? linearize_go<int32_t, int32_t>(tb, ia, weighted, keys[0], pay[0], bag_of, s)
+                             : linearize_go<int32_t, int64_t>(tb, ia, weighted, keys[0], pay[0], bag_of, s);
+  else
+    st = ia.otype == TBE_I32 ? linearize_go<int64_t, int32_t>(tb, ia, weighted, keys[0], pay[0], bag_of, s)
+                             : linearize_go<int64_t, int64_t>(tb, ia, weighted, keys[0], pay[0], bag_of, s);
+  if (st) return st;
+  uint32_t* hist = reinterpret_cast<uint32_t*>(ws + L.sort_hist);
+  uint32_t* tot = hist + static_cast<int64_t>(kRadixDigits) * L.nblocks;
+  int cur = 0;
+  for (int pass = 0; pass < L.passes; ++pass) {
+    const int ndig = 1 << L.bits[pass];
+    {
+      ProfScope ps("radix_upsweep", s);
+      hipLaunchKernelGGL(radix_upsweep, dim3(L.nblocks), dim3(kBlock), 0, s, keys[cur], N, L.seg,
+                         L.shift[pass], L.bits[pass], hist, L.nblocks);
+    }
+    if ((st = check_launch("radix_upsweep"))) return st;
+    {
+      ProfScope ps("radix_scan", s);
+      hipLaunchKernelGGL(radix_scan, dim3(ndig), dim3(kBlock), 0, s, hist, L.nblocks, tot);
+    }
+    if ((st = check_launch("radix_scan"))) return st;
+    {
+      ProfScope ps("radix_downsweep", s);
+      hipLaunchKernelGGL(radix_downsweep, dim3(L.nblocks), dim3(kBlock), 0, s, keys[cur], pay[cur],
+                         keys[cur ^ 1], pay[cur ^ 1], N, L.seg, L.shift[pass], L.bits[pass], hist,
+                         tot, L.nblocks);
+    }
+    if ((st = check_launch("radix_downsweep"))) return st;
+    cur ^= 1;
+  }
+  *final_buf = cur;
+  uint32_t* run_key = reinterpret_cast<uint32_t*>(ws + L.run_key);
+  uint32_t* run_start = reinterpret_cast<uint32_t*>(ws + L.run_start);
+  uint32_t* seg_cnt = reinterpret_cast<uint32_t*>(ws + L.seg_cnt);
+  {
+    ProfScope ps("rle", s);
+    hipLaunchKernelGGL(rle_count, dim3(L.nblocks), dim3(kBlock), 0, s, keys[cur], N, L.seg, seg_cnt);
+    hipLaunchKernelGGL(rle_scan, dim3(1), dim3(kBlock), 0, s, seg_cnt, L.nblocks, counters, run_start, N);
+    hipLaunchKernelGGL(rle_write, dim3(L.nblocks), dim3(kBlock), 0, s, keys[cur], N, L.seg, seg_cnt,
+                       run_key, run_start);
+  }
+  if ((st = check_launch("rle"))) return st;
+  ShortLists lists;
+  for (int b = 0; b < TBE_NUM_BUCKETS; ++b) {
+    lists.p[b] = L.cap_short[b] ? reinterpret_cast<uint4*>(ws + L.short_list[b]) : nullptr;
+    lists.cap[b] = L.cap_short[b];
+  }
+  {
+    const int64_t want = (N + kBlock - 1) / kBlock;
+    const int grid = static_cast<int>(hmax(1, hmin(want, static_cast<int64_t>(device_cu_count()) * 8)));
+    ProfScope ps("classify", s);
+    hipLaunchKernelGGL(classify_kernel, dim3(grid), dim3(kBlock), 0, s, run_key, run_start, counters,
+                       tb->meta, tb->T, static_cast<uint32_t>(tb->total_rows), cfg.threshold, cfg.chunk,
+                       reinterpret_cast<uint4*>(ws + L.long_list), reinterpret_cast<uint32_t*>(ws + L.long_table),
+                       reinterpret_cast<uint2*>(ws + L.chunk_list), L.cap_long, L.cap_chunk, lists);
+  }
+  return check_launch("classify");
+}
+
+}  // namespace tbe

@@ -1,0 +1,244 @@
+/*
+ * tbe.h - C ABI of the table-batched embedding (TBE) library for MI355X (gfx950).
+ *
+ * What the library computes (PyTorch blog "Modernizing Table Batched Embeddings
+ * with FBTriton", sections 2 and 3; layout of "Table-Batched Embeddings in
+ * Triton: Gather, Pool, and Run-Length Backward", section 1):
+ *
+ *   forward   out[b][col_t + d] = sum_{j in bag(t,b)} psw_j * W_t[idx_j][d]
+ *   backward  for every unique (table, row) touched by the batch, sum the
+ *             upstream gradient rows of every lookup that touched it (each
+ *             scaled by its per-sample weight when there is one), then apply
+ *             exactly one optimizer step (SGD or exact row-wise Adagrad) to
+ *             that row, in place.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers are DEVICE pointers unless the comment says [host].  The caller
+ *    allocates and owns every buffer.  The library never allocates device
+ *    memory, never synchronizes the stream and never copies device data to the
+ *    host; every kernel is launched on the caller's stream, in stream order.
+ *  - Every call returns a tbe_status.  Argument errors are found on the host
+ *    before anything is launched (TBE_ERR_ARG / TBE_ERR_UNSUPPORTED /
+ *    TBE_ERR_WORKSPACE); a failed launch is TBE_ERR_HIP.  tbe_last_error()
+ *    then holds a one-line description (thread-local).  No C++ exception
+ *    crosses this interface and nothing aborts.
+ *  - Layout: T tables ("features"), table t has E_t rows of width D_t, B bags
+ *    per table.  Weights of all tables are one buffer, table after table,
+ *    each row-major E_t x D_t.  offsets has T*B+1 entries, table-major: bag
+ *    (t, b) owns indices[offsets[t*B+b] .. offsets[t*B+b+1]).  Indices are row
+ *    ids local to their table.  The pooled output and the upstream gradient
+ *    are B x sum_t D_t fp32, row-major; table t's slice starts at column
+ *    sum_{t'<t} D_t'.
+ *  - Limits: 1 <= T; 0 <= B; 4 <= D_t <= 1024 with D_t % 4 == 0;
+ *    sum_t E_t < 2^31 - 1 (linearized row ids are 32-bit); number of lookups
+ *    < 2^31; T*B < 2^31.
+ *  - Invalid input with bounds checking off: an index outside [0, E_t)
+ *    contributes nothing to the forward and nothing to the backward, and no
+ *    memory outside the weights is touched; the pages leave this case to an
+ *    optional repair step (tbe_bounds_check).  Offsets must be non-decreasing
+ *    with offsets[0] = 0 and offsets[T*B] = num_indices; otherwise results are
+ *    undefined (but every access stays inside the caller's buffers).
+ */
+#ifndef TBE_H_
+#define TBE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* A hipStream_t passed as an opaque pointer; NULL is the default stream. */
+typedef void* tbe_stream_t;
+
+typedef enum { TBE_F32 = 0, TBE_F16 = 1, TBE_BF16 = 2 } tbe_dtype;   /* weight storage */
+typedef enum { TBE_I32 = 0, TBE_I64 = 1 } tbe_itype;                 /* indices / offsets */
+typedef enum {
+  TBE_OK = 0,
+  TBE_ERR_ARG = 1,          /* null pointer, negative size, inconsistent geometry */
+  TBE_ERR_UNSUPPORTED = 2,  /* D or dtype outside the supported range */
+  TBE_ERR_WORKSPACE = 3,    /* workspace null, misaligned or smaller than required */
+  TBE_ERR_HIP = 4           /* a HIP launch failed */
+} tbe_status;
+
+#define TBE_MAX_D 1024
+#define TBE_NUM_BUCKETS 9   /* short-run buckets next_pow2(D) = 4, 8, ..., 1024 */
+#define TBE_META_FIELDS 4   /* per table: row base, weight base, column base, D */
+
+/*
+ * Table geometry, filled by tbe_tables_derive.  Only `meta` must be set by
+ * the caller afterwards: a device copy of the int64 array that
+ * tbe_tables_derive wrote to meta_host (TBE_META_FIELDS * (T + 1) entries).
+ */
+typedef struct {
+  int32_t T;                 /* tables */
+  int32_t B;                 /* bags per table */
+  int32_t w_dtype;           /* tbe_dtype of every table */
+  int32_t max_D;             /* max_t D_t */
+  int32_t out_width;         /* sum_t D_t: row length of out and grad_out */
+  int32_t all_D_mult8;       /* 1 when every D_t % 8 == 0 (wider vector loads) */
+  int32_t hist_table;        /* table eligible for the histogram forward, or -1 */
+  int32_t hist_E;            /* rows of that table */
+  int32_t hist_D;            /* width of that table */
+  int32_t hist_col;          /* its first output column */
+  int32_t reserved;
+  int64_t hist_w_base;       /* its first element in the weight buffer */
+  int64_t total_rows;        /* sum_t E_t: linearized row ids are [0, total_rows) */
+  int64_t total_elems;       /* sum_t E_t * D_t: elements of the weight buffer */
+  int64_t bucket_rows[TBE_NUM_BUCKETS]; /* rows of the tables in each short-run bucket */
+  const int64_t* meta;       /* device: [T+1][4] = {row base, weight base, column base, D};
+                                entry T = {total_rows, total_elems, out_width, 0} */
+} tbe_tables;
+
+/*
+ * Knobs ("every fix is a config value": blog section 5).  tbe_config_default
+ * gives the pages' defaults; a NULL config pointer means the defaults.
+ */
+typedef struct {
+  int32_t long_threshold;  /* a run with >= this many lookups is long (default 256) */
+  int32_t chunk;           /* lookups per long-run chunk (default 256) */
+  int32_t hist_enable;     /* 1: histogram + MFMA forward for the eligible table (default 1) */
+  int32_t fwd_unroll;      /* forward row loads in flight per lane group: 2, 4 or 8 (default 8) */
+  int32_t bwd_unroll;      /* backward gradient-row loads in flight: 2, 4 or 8 (default 4) */
+  int32_t sort_blocks;     /* workgroups of each radix pass (default 0 = automatic) */
+} tbe_config;
+
+/* Device-side view of the transpose, for inspection by tests (tbe_transpose). */
+typedef struct {
+  const uint32_t* sorted_keys;     /* [N] linearized row id, ascending */
+  const uint32_t* sorted_payload;  /* [N] bag id t*B+b, or lookup position when weighted */
+  const uint32_t* run_key;         /* [N] key of run r (first num_runs used) */
+  const uint32_t* run_start;       /* [N+1] first sorted position of run r; run_start[num_runs] = N */
+  const int32_t* counters;         /* [16]: 0 runs, 1 long runs, 2 chunks, 3..11 short runs per
+                                      bucket (next_pow2(D) = 4 .. 1024) */
+  const uint32_t* long_list;       /* [cap][4] {key, start, len, first chunk} per long run */
+  const uint32_t* long_table;      /* [cap] table of each long run */
+  const uint32_t* chunk_list;      /* [cap][2] {long-run slot, chunk number} per chunk */
+  const uint32_t* short_list[TBE_NUM_BUCKETS]; /* [cap][4] {key, start, len, table}, or NULL */
+  int64_t long_capacity, chunk_capacity;
+  int64_t short_capacity[TBE_NUM_BUCKETS];
+  int32_t payload_is_position;     /* 1 for weighted calls */
+  int32_t radix_passes;
+} tbe_runs_view;
+
+/* Static description of a status code. */
+const char* tbe_status_string(tbe_status s);
+
+/* Last error message of the calling thread ("" when none). */
+const char* tbe_last_error(void);
+
+/* Fills *cfg with the defaults listed in tbe_config. */
+void tbe_config_default(tbe_config* cfg);
+
+/* Number of int64 entries tbe_tables_derive writes to meta_host: 4 * (T + 1). */
+int64_t tbe_meta_entries(int32_t T);
+
+/*
+ * Host only.  Derives the geometry of T tables of E_host[t] rows and
+ * D_host[t] columns, B bags each, weights of dtype w_dtype.  Writes the
+ * per-table bases to meta_host [host, tbe_meta_entries(T) int64] and the
+ * summary to *out (out->meta is set to NULL: the caller uploads meta_host and
+ * stores the device pointer there).  pooling_hint_host [host, T, nullable] is
+ * the expected lookups per bag of each table; the histogram forward is
+ * offered for the first table with E <= 64, 64 <= D <= 128, D % 16 == 0,
+ * fp16 weights and a hint >= 64 (blog section 2, small-table path).
+ */
+tbe_status tbe_tables_derive(int32_t T, int32_t B, int32_t w_dtype, const int64_t* E_host,
+                             const int32_t* D_host, const int32_t* pooling_hint_host,
+                             int64_t* meta_host, tbe_tables* out);
+
+/*
+ * Bounds check and repair (blog section 2, "Bounds checking"; tutorial
+ * Pitfalls: an id outside its table silently reads another table's row).
+ * Repairs in place: offsets become their running maximum after clamping to
+ * [0, num_indices], with offsets[0] = 0 and offsets[T*B] = num_indices; then
+ * every index outside [0, E_t) of the table that owns its position becomes 0.
+ * error_counts [device, 2 x int64] is overwritten with {indices repaired,
+ * offsets entries changed}.  workspace: tbe_bounds_check_workspace_bytes().
+ */
+size_t tbe_bounds_check_workspace_bytes(const tbe_tables* tables);
+tbe_status tbe_bounds_check(const tbe_tables* tables, void* indices, int32_t index_type,
+                            void* offsets, int32_t offset_type, int64_t num_indices,
+                            int64_t* error_counts, void* workspace, size_t workspace_bytes,
+                            tbe_stream_t stream);
+
+/*
+ * Forward (blog section 2).  weights: the table buffer (w_dtype); indices
+ * [num_indices] and offsets [T*B+1] of index_type / offset_type;
+ * per_sample_weights [num_indices] fp32 or NULL; out [B][out_width] fp32,
+ * fully overwritten (an empty bag gives zeros).  fp16 / bf16 tables
+ * accumulate in fp32, fp32 tables in fp64.  When the config enables it, the
+ * call has no per-sample weights, and tables->hist_table >= 0, that table's
+ * bags are pooled by the histogram + MFMA kernel (counts of each bag's first
+ * 256 ids times the table; remaining ids gathered).
+ */
+tbe_status tbe_forward(const tbe_tables* tables, const void* weights, const void* indices,
+                       int32_t index_type, const void* offsets, int32_t offset_type,
+                       int64_t num_indices, const float* per_sample_weights, float* out,
+                       const tbe_config* config, tbe_stream_t stream);
+
+/*
+ * Bytes of workspace the backward (and tbe_transpose) needs for num_indices
+ * lookups; weighted = 1 when per-sample weights will be passed.  Bounded by
+ * the index count alone (blog section 4: workspace preallocated to a bound
+ * computed from the index count), so no device count is read back.
+ */
+size_t tbe_backward_workspace_bytes(const tbe_tables* tables, int64_t num_indices,
+                                    int32_t weighted, const tbe_config* config);
+
+/*
+ * Backward with SGD (blog section 3): w <- w - lr * g for every touched row,
+ * in place, rounded to the storage dtype (nearest even).  grad_out
+ * [B][out_width] fp32.  per_sample_weights as in the forward (NULL =
+ * unweighted).  workspace: at least tbe_backward_workspace_bytes, 256-byte
+ * aligned; its contents are undefined after the call.
+ */
+tbe_status tbe_backward_sgd(const tbe_tables* tables, void* weights, const void* indices,
+                            int32_t index_type, const void* offsets, int32_t offset_type,
+                            int64_t num_indices, const float* per_sample_weights,
+                            const float* grad_out, float lr, void* workspace,
+                            size_t workspace_bytes, const tbe_config* config, tbe_stream_t stream);
+
+/*
+ * Backward with exact row-wise Adagrad ("Table-Batched Embeddings in Triton",
+ * section 5): per touched row, m <- m + sum_d g_d^2 / D_t, then
+ * w <- w - lr * g / (sqrt(m) + eps) with the new m.  momentum [total_rows]
+ * fp32, in place; untouched rows keep weights and momentum.
+ */
+tbe_status tbe_backward_rowwise_adagrad(const tbe_tables* tables, void* weights, float* momentum,
+                                        const void* indices, int32_t index_type,
+                                        const void* offsets, int32_t offset_type,
+                                        int64_t num_indices, const float* per_sample_weights,
+                                        const float* grad_out, float lr, float eps,
+                                        void* workspace, size_t workspace_bytes,
+                                        const tbe_config* config, tbe_stream_t stream);
+
+/*
+ * The backward's transpose and routing alone (blog section 3,
+ * transpose_embedding_input, and section 4, run classification): linearize,
+ * stable radix sort, run-length encoding, long/short routing with D buckets
+ * and chunk plan.  Fills *view [host] with device pointers into workspace;
+ * nothing is read back.  weighted selects the payload (see tbe_runs_view).
+ */
+tbe_status tbe_transpose(const tbe_tables* tables, const void* indices, int32_t index_type,
+                         const void* offsets, int32_t offset_type, int64_t num_indices,
+                         int32_t weighted, void* workspace, size_t workspace_bytes,
+                         const tbe_config* config, tbe_runs_view* view, tbe_stream_t stream);
+
+/*
+ * Kernel timing for measurement.  tbe_profile_select(name) makes the library
+ * record a pair of HIP events on the launch stream around every later launch
+ * of the kernel called `name` (NULL stops recording);
+ * tbe_profile_read waits for the recorded events and returns the number of
+ * timed launches and their total milliseconds, then forgets them.
+ */
+tbe_status tbe_profile_select(const char* kernel_name);
+tbe_status tbe_profile_read(int64_t* launches, double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TBE_H_ */

@@ -1,0 +1,103 @@
+"""The C-ABI library loads, exports every symbol include/tbe.h declares, its structs have the
+layout the binding assumes, and host-side validation works - no GPU needed (no kernel runs)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+import bwd_tbe_fwd_amd as tbe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tbe.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tbe_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = tbe.lib()
+    names = declared_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(tbe._SIGS), set(names) ^ set(tbe._SIGS)
+
+
+def test_struct_layout_matches_header(tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text(f"""
+#include <stdio.h>
+#include <stddef.h>
+#include "{HEADER}"
+int main(void) {{
+  printf("%zu %zu %zu %zu %zu %zu %zu\\n", sizeof(tbe_tables), offsetof(tbe_tables, hist_w_base),
+         offsetof(tbe_tables, bucket_rows), offsetof(tbe_tables, meta), sizeof(tbe_config),
+         sizeof(tbe_runs_view), offsetof(tbe_runs_view, short_capacity));
+  return 0;
+}}
+""")
+    exe = tmp_path / "layout"
+    subprocess.check_call(["gcc", "-std=c11", "-o", str(exe), str(src)])
+    got = [int(x) for x in subprocess.check_output([str(exe)]).split()]
+    exp = [ctypes.sizeof(tbe.tbe_tables), tbe.tbe_tables.hist_w_base.offset,
+           tbe.tbe_tables.bucket_rows.offset, tbe.tbe_tables.meta.offset, ctypes.sizeof(tbe.tbe_config),
+           ctypes.sizeof(tbe.tbe_runs_view), tbe.tbe_runs_view.short_capacity.offset]
+    assert got == exp
+
+
+def test_tables_derive_host_logic():
+    t = tbe.Tables([100, 64, 4_000_000, 7], [32, 128, 256, 1024], 512, torch.float16, device=None,
+                   pooling_hint=[10, 128, 30, 100])
+    c = t.c
+    assert (c.T, c.B, c.max_D, c.out_width) == (4, 512, 1024, 32 + 128 + 256 + 1024)
+    assert c.total_rows == 100 + 64 + 4_000_000 + 7
+    assert c.total_elems == 100 * 32 + 64 * 128 + 4_000_000 * 256 + 7 * 1024
+    assert c.hist_table == 1 and c.hist_E == 64 and c.hist_D == 128 and c.hist_col == 32
+    assert c.hist_w_base == 100 * 32
+    assert list(c.bucket_rows) == [0, 0, 0, 100, 0, 64, 4_000_000, 0, 7]
+    meta = t.meta_host.view(-1, 4).tolist()
+    assert meta[1] == [100, 3200, 32, 128] and meta[4] == [c.total_rows, c.total_elems, c.out_width, 0]
+    # no histogram path without a pooling hint, for bf16, or with E > 64
+    assert tbe.Tables([64], [128], 8, torch.float16, device=None).c.hist_table == -1
+    assert tbe.Tables([64], [128], 8, torch.bfloat16, device=None, pooling_hint=[100]).c.hist_table == -1
+    assert tbe.Tables([65], [128], 8, torch.float16, device=None, pooling_hint=[100]).c.hist_table == -1
+
+
+def test_derive_rejects_bad_geometry():
+    for E, D in [([10], [3]), ([10], [1028]), ([0], [8]), ([2 ** 31], [8])]:
+        with pytest.raises(tbe.TbeError):
+            tbe.Tables(E, D, 4, torch.float32, device=None)
+
+
+def test_calls_validate_before_launching():
+    t = tbe.Tables([10], [8], 4, torch.float32, device=None)
+    L = tbe.lib()
+    # meta not uploaded -> argument error, nothing launched
+    st = L.tbe_forward(t.ref, None, None, 1, None, 1, 0, None, None, None, None)
+    assert st == 1 and b"meta" in L.tbe_last_error()
+    t.c.meta = 256  # any non-null address: the following calls must fail on the host first
+    st = L.tbe_forward(t.ref, None, None, 1, ctypes.c_void_p(4096), 1, 4, None, None, None, None)
+    assert st == 1 and b"indices" in L.tbe_last_error()
+    st = L.tbe_backward_sgd(t.ref, ctypes.c_void_p(4096), ctypes.c_void_p(4096), 1,
+                            ctypes.c_void_p(4096), 1, 4, None, ctypes.c_void_p(4096), 0.1,
+                            ctypes.c_void_p(4096), 16, None, None)
+    assert st == 3  # workspace too small
+    assert L.tbe_status_string(3) == b"workspace missing, misaligned or too small"
+    st = L.tbe_forward(t.ref, None, None, 7, ctypes.c_void_p(4096), 1, 4, None, None, None, None)
+    assert st == 1 and b"index type" in L.tbe_last_error()
+
+
+def test_workspace_bound_from_index_count():
+    t = tbe.Tables([2_000_000] * 32, [128] * 32, 131072, torch.float16, device=None)
+    n = 83_897_668
+    b = tbe.tbe_backward_workspace_bytes(t, n, False)
+    # sort ping-pong 16 + runs 8 + short descriptors 16 + chunk partials 4 (N/128 rows of 128
+    # floats) + long lists: about 45 bytes per lookup, 3.8 GB of the 288 GB
+    assert 40 * n < b < 48 * n
+    assert tbe.tbe_backward_workspace_bytes(t, n, True) > b

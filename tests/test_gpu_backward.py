@@ -1,0 +1,133 @@
+"""Backward parity: one optimizer step per touched row, SGD and exact row-wise Adagrad,
+against the oracle; routing invariance; gradient extraction; determinism."""
+import numpy as np
+import pytest
+import torch
+
+import bwd_tbe_fwd_amd as tbe
+import oracle
+import tbe_inputs as ti
+from gpu_util import (DevBatch, check_momentum, check_weights, flush_print, host_arrays,
+                      oracle_backward, row_g_abs_sq, step_bound)
+from test_gpu_forward import mixed_spec, small_spec
+
+pytestmark = pytest.mark.gpu
+
+
+def run_and_check(bt, cfg=None, optimizer=None, lr=None, what=""):
+    optimizer = optimizer or bt.spec.optimizer
+    db = DevBatch(bt)
+    if optimizer == "rowwise_adagrad" and db.mom is None:
+        db.mom = torch.zeros(sum(bt.E), dtype=torch.float32, device="cuda")
+        bt.momentum = torch.zeros(sum(bt.E), dtype=torch.float32)
+    W, mom = db.backward(cfg, optimizer=optimizer, lr=lr)
+    torch.cuda.synchronize()
+    r = oracle_backward(bt, lr=lr, optimizer=optimizer)
+    lr32 = oracle.f32_literal(bt.spec.lr if lr is None else lr)
+    ada = optimizer == "rowwise_adagrad"
+    sb = step_bound(r, bt.E, bt.D, lr32, oracle.f32_literal(bt.spec.eps), ada)
+    check_weights(W, r, bt.w_dtype, sb, what)
+    if ada:
+        gsq, Dr = row_g_abs_sq(r, bt.E, bt.D)
+        check_momentum(mom, r, Dr, gsq, what)
+    return db, W, mom, r
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
+def test_backward_configs_small(n):
+    spec = small_spec(n)
+    flush_print(f"backward config {n}: {spec.name} ({spec.optimizer})")
+    bt = ti.make_batch(spec, ti.config_seed(n))
+    run_and_check(bt, what=f"config {n}")
+
+
+@pytest.mark.parametrize("w_dtype", [torch.float32, torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("optimizer", ["sgd", "rowwise_adagrad"])
+@pytest.mark.parametrize("weighted", [False, True])
+def test_backward_dtypes_mixed_D(w_dtype, optimizer, weighted):
+    spec = mixed_spec(w_dtype, torch.int64, torch.int32, weighted).replace(optimizer=optimizer)
+    bt = ti.make_batch(spec, 19)
+    run_and_check(bt, tbe.make_config(long_threshold=32, chunk=16), what=f"{w_dtype} {optimizer} {weighted}")
+
+
+@pytest.mark.parametrize("optimizer", ["sgd", "rowwise_adagrad"])
+@pytest.mark.parametrize("threshold,chunk", [(10 ** 9, 256), (256, 256), (8, 8), (4, 2), (1, 1)])
+def test_routing_invariance(optimizer, threshold, chunk):
+    """Same batch, every split point: all match the oracle (tutorial section 3's sweep)."""
+    bt = ti.make_batch(small_spec(5).replace(optimizer=optimizer), 23)
+    cfg = tbe.make_config(long_threshold=threshold, chunk=chunk)
+    run_and_check(bt, cfg, what=f"{optimizer} t={threshold} c={chunk}")
+
+
+@pytest.mark.parametrize("weighted", [False, True])
+def test_gradient_extraction(weighted):
+    """SGD with lr = -1 on all-zero fp32 weights writes the summed gradient itself."""
+    spec = small_spec(4 if weighted else 5).replace(w_dtype=torch.float32, optimizer="sgd")
+    bt = ti.make_batch(spec, 29)
+    bt.weights = torch.zeros_like(bt.weights)
+    db = DevBatch(bt)
+    W, _ = db.backward(tbe.make_config(long_threshold=64, chunk=32), lr=-1.0)
+    r = oracle_backward(bt, lr=-1.0)
+    got = W.double().cpu().numpy()
+    err = np.abs(got - r["g"])
+    assert np.all(err <= 1e-5 * r["g_abs"]), float((err - 1e-5 * r["g_abs"]).max())
+
+
+def test_backward_deterministic():
+    bt = ti.make_batch(small_spec(5), 31)
+    cfg = tbe.make_config(long_threshold=16, chunk=16)
+    outs = []
+    for _ in range(2):
+        db = DevBatch(bt)
+        W, mom = db.backward(cfg)
+        outs.append((W.cpu().clone(), mom.cpu().clone()))
+    assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16))
+    assert torch.equal(outs[0][1].view(torch.int32), outs[1][1].view(torch.int32))
+
+
+def test_untouched_rows_bit_identical():
+    bt = ti.make_batch(small_spec(5), 37)
+    db = DevBatch(bt)
+    W0 = db.W.clone()
+    m0 = db.mom.clone()
+    W, mom = db.backward(tbe.make_config(long_threshold=16, chunk=16))
+    a = host_arrays(bt)
+    tr = oracle.transpose(a["T"], a["B"], a["E"], a["idx"], a["off"])
+    touched = np.zeros(sum(bt.E), dtype=bool)
+    touched[tr["run_key"]] = True
+    D = bt.D[0]
+    W2 = W.view(-1, D).cpu()
+    W02 = W0.view(-1, D).cpu()
+    t = torch.from_numpy(touched)
+    assert torch.equal(W2[~t].view(torch.int16), W02[~t].view(torch.int16))
+    assert torch.equal(mom.cpu()[~t], m0.cpu()[~t])
+    assert (mom.cpu()[t] > m0.cpu()[t]).all()
+
+
+def test_backward_no_lookups_and_no_bags():
+    spec = ti.BatchSpec("empty", (ti.TableSpec(10, 8, ("fixed", 0)),), B=50, w_dtype=torch.float16,
+                        w_range=0.5, optimizer="rowwise_adagrad")
+    bt = ti.make_batch(spec, 1)
+    db = DevBatch(bt)
+    W0 = db.W.clone()
+    W, mom = db.backward()
+    assert torch.equal(W.cpu(), W0.cpu()) and torch.equal(mom.cpu(), torch.zeros_like(mom.cpu()))
+
+
+def test_backward_out_of_range_ids_dropped():
+    spec = ti.BatchSpec("bad ids", (ti.TableSpec(20, 16, ("fixed", 6)), ti.TableSpec(30, 32, ("fixed", 3))),
+                        B=40, w_dtype=torch.float32, w_range=0.5, optimizer="sgd")
+    bt = ti.make_batch(spec, 2)
+    idx = bt.indices.clone()
+    bad = torch.zeros(idx.numel(), dtype=torch.bool)
+    bad[::7] = True
+    idx[bad] = 99999
+    bt.indices = idx
+    db = DevBatch(bt)
+    W, _ = db.backward()
+    a = host_arrays(bt)
+    keep = (~bad).double().numpy()
+    ids = np.where(bad.numpy(), 0, a["idx"])
+    r = oracle.backward(a["T"], a["B"], a["E"], a["D"], oracle.F32, a["W"], ids, a["off"], keep,
+                        a["grad"], oracle.SGD, oracle.f32_literal(0.01))
+    check_weights(W, r, torch.float32, 0.01 * r["g_abs"], "dropped ids")

@@ -1,0 +1,71 @@
+"""Bounds check and repair: repaired indices, offsets and counts equal the oracle's exactly."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import bwd_tbe_fwd_amd as tbe
+import oracle
+import tbe_inputs as ti
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def gpu_bounds(E, D, B, indices, offsets, itype, otype):
+    tables = tbe.Tables(E, D, B, torch.float32, device="cuda")
+    idx = torch.as_tensor(np.asarray(indices), dtype=itype).cuda()
+    off = torch.as_tensor(np.asarray(offsets), dtype=otype).cuda()
+    counts = torch.full((2,), -1, dtype=torch.int64, device="cuda")
+    ws = tbe.workspace(tbe.tbe_bounds_check_workspace_bytes(tables))
+    tbe.tbe_bounds_check(tables, idx, off, counts, ws)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy().astype(np.int64), off.cpu().numpy().astype(np.int64), counts.cpu().numpy()
+
+
+@pytest.mark.parametrize("itype,otype", [(torch.int64, torch.int64), (torch.int32, torch.int32),
+                                         (torch.int32, torch.int64)])
+def test_bounds_golden_example(itype, otype):
+    with open(os.path.join(GOLDEN, "bounds_example.json")) as f:
+        g = json.load(f)
+    idx, off, cnt = gpu_bounds(g["E"], [4] * g["T"], g["B"], g["indices"], g["offsets"], itype, otype)
+    assert idx.tolist() == g["expected_indices"]
+    assert off.tolist() == g["expected_offsets"]
+    assert cnt.tolist() == g["expected_counts"]
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+@pytest.mark.parametrize("itype", [torch.int32, torch.int64])
+def test_bounds_injected_faults(seed, itype):
+    spec = ti.BatchSpec("faults", (ti.TableSpec(1000, 8, ("poisson", 6.0, None, None)),
+                                   ti.TableSpec(50, 8, ("poisson", 2.0, None, None)),
+                                   ti.TableSpec(7, 8, ("fixed", 3))),
+                        B=2999, w_dtype=torch.float32, w_range=0.5)
+    bt = ti.make_batch(spec, seed, with_grad=False)
+    rng = np.random.default_rng(seed)
+    idx = bt.indices.numpy().astype(np.int64)
+    off = bt.offsets.numpy().astype(np.int64)
+    N = idx.size
+    bad = rng.random(N) < 0.05
+    idx[bad] = rng.choice([-1, -1000, 7, 50, 1000, 2 ** 30], size=int(bad.sum()))
+    ob = rng.random(off.size) < 0.01
+    off[ob] = rng.integers(-5, N + 50, size=int(ob.sum()))
+    off[0] = rng.integers(-3, 3)
+    off[-1] = N - rng.integers(0, 5)
+    exp_idx, exp_off, exp_cnt = oracle.bounds_check(3, spec.B, bt.E, idx, off)
+    assert exp_cnt[0] > 0 and exp_cnt[1] > 0
+    got_idx, got_off, got_cnt = gpu_bounds(bt.E, bt.D, spec.B, idx, off, itype, torch.int64)
+    assert np.array_equal(got_off, exp_off)
+    assert np.array_equal(got_idx, exp_idx)
+    assert got_cnt.tolist() == exp_cnt.tolist()
+
+
+def test_bounds_valid_input_unchanged():
+    bt = ti.make_batch(ti.scaled(ti.CONFIGS[5], B=4000, E_div=100, T=3), 5, with_grad=False)
+    got_idx, got_off, cnt = gpu_bounds(bt.E, bt.D, bt.B, bt.indices.numpy(), bt.offsets.numpy(),
+                                       torch.int64, torch.int64)
+    assert cnt.tolist() == [0, 0]
+    assert np.array_equal(got_idx, bt.indices.numpy())
+    assert np.array_equal(got_off, bt.offsets.numpy())

@@ -1,0 +1,133 @@
+"""Transpose and routing parity: sorted keys, payload order, runs and classification are
+compared with the oracle bit for bit (compacted lists as sorted sets with exact counts)."""
+import numpy as np
+import pytest
+import torch
+
+import bwd_tbe_fwd_amd as tbe
+import oracle
+import tbe_inputs as ti
+from gpu_util import DevBatch, flush_print, host_arrays
+from test_gpu_forward import mixed_spec, small_spec
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_transpose(db: DevBatch, weighted: bool, cfg=None):
+    ws = db.workspace(cfg, weighted)
+    view = tbe.tbe_transpose(db.tables, db.idx, db.off, weighted, ws, cfg)
+    torch.cuda.synchronize()
+    N = db.idx.numel()
+    cnt = tbe.device_view(view.counters, 16, torch.int32, ws).cpu().numpy()
+    runs = int(cnt[tbe.COUNTER_RUNS])
+    res = dict(
+        counters=cnt,
+        keys=tbe.device_view(view.sorted_keys, N, torch.int32, ws).cpu().numpy().view(np.uint32),
+        payload=tbe.device_view(view.sorted_payload, N, torch.int32, ws).cpu().numpy().view(np.uint32),
+        run_key=tbe.device_view(view.run_key, runs, torch.int32, ws).cpu().numpy().view(np.uint32),
+        run_start=tbe.device_view(view.run_start, runs + 1, torch.int32, ws).cpu().numpy().view(np.uint32),
+    )
+    nl = int(cnt[tbe.COUNTER_LONG])
+    nc = int(cnt[tbe.COUNTER_CHUNKS])
+    res["long"] = tbe.device_view(view.long_list, 4 * nl, torch.int32, ws).cpu().numpy().view(np.uint32).reshape(nl, 4)
+    res["long_table"] = tbe.device_view(view.long_table, nl, torch.int32, ws).cpu().numpy()
+    res["chunks"] = tbe.device_view(view.chunk_list, 2 * nc, torch.int32, ws).cpu().numpy().view(np.uint32).reshape(nc, 2)
+    res["short"] = {}
+    for b in range(tbe.NUM_BUCKETS):
+        ns = int(cnt[tbe.COUNTER_SHORT0 + b])
+        if view.short_list[b]:
+            res["short"][b] = tbe.device_view(view.short_list[b], 4 * ns, torch.int32, ws).cpu().numpy().view(np.uint32).reshape(ns, 4)
+        else:
+            assert ns == 0
+    res["view"] = view
+    return res
+
+
+def check_transpose(bt, weighted, cfg=None, threshold=256, chunk=256, what=""):
+    db = DevBatch(bt)
+    g = gpu_transpose(db, weighted, cfg)
+    a = host_arrays(bt)
+    tr = oracle.transpose(a["T"], a["B"], a["E"], a["idx"], a["off"])
+    N = a["idx"].size
+    assert np.array_equal(g["keys"].astype(np.int64), tr["sorted_key"]), what
+    exp_pay = tr["sorted_pos"] if weighted else tr["sorted_bag"]
+    assert np.array_equal(g["payload"].astype(np.int64), exp_pay), what
+    assert g["counters"][tbe.COUNTER_RUNS] == tr["num_runs"]
+    assert np.array_equal(g["run_key"].astype(np.int64), tr["run_key"])
+    assert np.array_equal(g["run_start"][:-1].astype(np.int64), tr["run_start"])
+    assert int(g["run_start"][-1]) == N
+    c = oracle.classify(a["T"], a["E"], a["D"], tr["run_key"], tr["run_len"], threshold, chunk)
+    # long runs: same set of (key, start, len), chunk plan consistent
+    exp_long = np.stack([tr["run_key"], tr["run_start"], tr["run_len"]], 1)[c["is_long"]]
+    got_long = g["long"][:, :3].astype(np.int64)
+    assert got_long.shape[0] == exp_long.shape[0]
+    assert np.array_equal(got_long[np.lexsort(got_long.T[::-1])], exp_long[np.lexsort(exp_long.T[::-1])])
+    assert g["counters"][tbe.COUNTER_CHUNKS] == c["num_chunks"]
+    seen = np.zeros(c["num_chunks"], dtype=bool)
+    base = np.concatenate([[0], np.cumsum(a["E"])])
+    for li, (key, start, ln, cb) in enumerate(g["long"]):
+        nch = -(-int(ln) // chunk)
+        assert int(g["long_table"][li]) == int(np.searchsorted(base, key, side="right") - 1)
+        for k in range(nch):
+            assert tuple(g["chunks"][cb + k]) == (li, k)
+            seen[cb + k] = True
+    assert seen.all()
+    # short runs per bucket
+    for b in range(tbe.NUM_BUCKETS):
+        want = ~c["is_long"] & (c["bucket"] == tbe.BUCKET_D[b])
+        exp = np.stack([tr["run_key"], tr["run_start"], tr["run_len"]], 1)[want]
+        got = g["short"].get(b, np.zeros((0, 4), np.uint32))[:, :3].astype(np.int64)
+        assert got.shape == exp.shape, (what, b, got.shape, exp.shape)
+        if exp.size:
+            assert np.array_equal(got[np.lexsort(got.T[::-1])], exp[np.lexsort(exp.T[::-1])])
+    return g, tr
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("weighted", [False, True])
+def test_transpose_configs_small(n, weighted):
+    spec = small_spec(n)
+    flush_print(f"transpose config {n} weighted={weighted}")
+    bt = ti.make_batch(spec, ti.config_seed(n))
+    check_transpose(bt, weighted, what=f"config {n}")
+
+
+@pytest.mark.parametrize("threshold,chunk", [(10 ** 9, 256), (256, 256), (8, 8), (4, 2), (1, 1)])
+def test_transpose_routing_sweep(threshold, chunk):
+    bt = ti.make_batch(small_spec(5), 15)
+    cfg = tbe.make_config(long_threshold=threshold, chunk=chunk)
+    check_transpose(bt, False, cfg, threshold, chunk, f"t={threshold} c={chunk}")
+
+
+def test_transpose_mixed_D_buckets_and_int32():
+    bt = ti.make_batch(mixed_spec(torch.float16, torch.int32, torch.int32, False), 5)
+    g, _ = check_transpose(bt, False, tbe.make_config(long_threshold=16, chunk=8), 16, 8, "mixed")
+    assert len(g["short"]) >= 6
+
+
+def test_transpose_many_sort_blocks():
+    # more radix blocks than tiles per block: exercises block boundaries inside runs
+    bt = ti.make_batch(ti.scaled(ti.CONFIGS[5], B=3000, E_div=400, T=3), 8)
+    check_transpose(bt, False, tbe.make_config(sort_blocks=7), what="7 sort blocks")
+    check_transpose(bt, True, tbe.make_config(sort_blocks=4096), what="max sort blocks")
+
+
+def test_transpose_tutorial_batch_statistics():
+    """The tutorial's seed-1 batch (regenerated from its prose): the GPU routing reproduces the
+    printed short/long/chunk counts of the threshold sweep."""
+    from test_oracle_pins import _golden, _tutorial_batch
+    gold = _golden("tutorial_stats.json")
+    T, E, B, D, ids, off = _tutorial_batch()
+    spec = ti.BatchSpec("tutorial", tuple(ti.TableSpec(E, D) for _ in range(T)), B=B,
+                        w_dtype=torch.float32, w_range=0.1)
+    bt = ti.make_batch(spec, 0)
+    bt.indices = torch.from_numpy(ids)
+    bt.offsets = torch.from_numpy(off)
+    for row in gold["sweep"]:
+        cfg = tbe.make_config(long_threshold=min(row["threshold"], 2 ** 31 - 1), chunk=row["chunk"])
+        g, tr = check_transpose(bt, False, cfg, row["threshold"], row["chunk"], str(row))
+        cnt = g["counters"]
+        assert int(cnt[tbe.COUNTER_LONG]) == row["long"]
+        assert int(cnt[tbe.COUNTER_SHORT0:tbe.COUNTER_SHORT0 + tbe.NUM_BUCKETS].sum()) == row["short"]
+        assert int(cnt[tbe.COUNTER_CHUNKS]) == row["chunks"]
+        assert int(cnt[tbe.COUNTER_RUNS]) == gold["unique_rows"]
