@@ -6,7 +6,7 @@
 
 Prints one JSON line (metric, value, ..., roofline, cpu_baseline).
 
-  python bench.py [--steps K] [--warmup W] [--config 5] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--workload skewed] [--no-cpu-baseline]
   python bench.py --calib-copy      # plain copy kernel of known size (rocprofv3 byte calibration)
 """
 from __future__ import annotations
@@ -31,6 +31,46 @@ HBM_PEAK_GBS = 8000.0
 KERNELS = ["bounds_offsets", "bounds_indices", "fwd_gather", "fwd_hist", "linearize",
            "radix_upsweep", "radix_scan", "radix_downsweep", "rle", "classify", "short_run",
            "grad_accum", "long_apply"]
+
+
+# sources each timed kernel is built from: its counters in profiles/ are valid only while
+# these files are unchanged
+KERNEL_SOURCES = {
+    "fwd_gather": ["forward.hip", "tbe_device.h"],
+    "fwd_hist": ["forward.hip", "tbe_device.h"],
+    "short_run": ["backward_kernels.h", "backward_launch.h", "tbe_device.h"],
+    "grad_accum": ["backward.hip", "backward_kernels.h", "tbe_device.h"],
+    "long_apply": ["backward_kernels.h", "backward_launch.h", "tbe_device.h"],
+    "linearize": ["transpose.hip", "tbe_device.h"],
+    "radix_upsweep": ["transpose.hip", "tbe_device.h"],
+    "radix_downsweep": ["transpose.hip", "tbe_device.h"],
+    "bounds_indices": ["bounds.hip", "tbe_device.h"],
+}
+
+
+def kernel_sources_hash(kernel: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES.get(kernel, []):
+        with open(os.path.join(ROOT, "bwd_tbe_fwd_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str):
+    """Bytes beyond L2 per launch from the committed rocprofv3 counters, scaled by the copy
+    calibration; None if there are none or the kernel's sources changed since."""
+    path = os.path.join(ROOT, "profiles", "skewed_large_traffic.json")
+    try:
+        with open(path) as f:
+            prof = json.load(f)
+        k = prof["kernels"][kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if k.get("sources_sha256") != kernel_sources_hash(kernel):
+        return None
+    c = prof["calibration"]
+    return (k["fetch_kib"] * c["fetch_factor"] + k["write_kib"] * c["write_factor"]) * 1024
 
 
 def log(*a):
@@ -95,15 +135,15 @@ def algorithmic_bytes(bt: ti.Batch, st: dict, passes: int):
 
 
 def calib_copy():
-    """A plain device copy of known size, for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE."""
-    n = 1 << 30  # 4 GiB of fp32
-    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    """The library's plain 16-byte-per-lane copy of 1 GiB, three times: rocprofv3 byte counters
+    of this known-size copy calibrate FETCH_SIZE / WRITE_SIZE of the other kernels."""
+    n = 1 << 30
+    a = torch.zeros(n, dtype=torch.uint8, device="cuda")
     b = torch.empty_like(a)
     for _ in range(3):
-        b.copy_(a)
+        tbe.tbe_calibration_copy(a, b, n)
     torch.cuda.synchronize()
-    print(json.dumps({"calib_copy_bytes_read": n * 4, "calib_copy_bytes_written": n * 4,
-                      "launches": 3}))
+    print(json.dumps({"calib_copy_bytes_read": n, "calib_copy_bytes_written": n, "launches": 3}))
 
 
 def cpu_baseline(spec: ti.BatchSpec, seed: int):
@@ -134,11 +174,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=5)
+    ap.add_argument("--workload", default="skewed", choices=sorted(ti.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bounds", action="store_true", help="leave the bounds check out of the step")
     ap.add_argument("--calib-copy", action="store_true")
-    ap.add_argument("--breakdown", action="store_true", help="time every kernel once (extra steps)")
+    ap.add_argument("--dominant", default=None,
+                    help="kernel to time inside the timed region (skips the one-step-per-kernel scan)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -149,8 +190,8 @@ def main():
         return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    spec = ti.CONFIGS[args.config]
-    seed = ti.config_seed(args.config)
+    spec = ti.WORKLOADS[args.workload]
+    seed = spec.seed
     t0 = time.perf_counter()
     bt = ti.make_batch(spec, seed, device=dev)
     torch.cuda.synchronize()
@@ -183,14 +224,14 @@ def main():
     torch.cuda.synchronize()
     # which kernel dominates: one profiled step per kernel (outside the timed region)
     per_kernel = {}
-    for k in KERNELS:
+    for k in ([] if args.dominant else KERNELS):
         tbe.tbe_profile_select(k)
         step()
         n, ms = tbe.tbe_profile_read()
         if n:
             per_kernel[k] = ms
     tbe.tbe_profile_select(None)
-    dominant = max(per_kernel, key=per_kernel.get)
+    dominant = args.dominant or max(per_kernel, key=per_kernel.get)
     log("one step per kernel (ms): " + ", ".join(f"{k} {v:.3f}" for k, v in per_kernel.items()))
     # timed region; the dominant kernel's launches are bracketed by HIP events on its stream
     tbe.tbe_profile_select(dominant)
@@ -228,7 +269,8 @@ def main():
                    "indices": str(bt.indices.dtype).replace("torch.", ""), "optimizer": spec.optimizer,
                    "step": ("" if args.no_bounds else "bounds_check + ") + "forward + backward"},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(dominant) if args.workload == "skewed" else None,
                      "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_ms": dom_avg_ms,
                      "launches_timed": launches},
         "step_algorithmic_GBps": step_bytes / (ms_per_step * 1e-3) / 1e9,

@@ -44,7 +44,8 @@ class tbe_tables(ctypes.Structure):
 class tbe_config(ctypes.Structure):
     _fields_ = [("long_threshold", ctypes.c_int32), ("chunk", ctypes.c_int32),
                 ("hist_enable", ctypes.c_int32), ("fwd_unroll", ctypes.c_int32),
-                ("bwd_unroll", ctypes.c_int32), ("sort_blocks", ctypes.c_int32)]
+                ("bwd_unroll", ctypes.c_int32), ("sort_blocks", ctypes.c_int32),
+                ("bag_windows", ctypes.c_int32)]
 
 
 class tbe_runs_view(ctypes.Structure):
@@ -82,6 +83,7 @@ _SIGS = {
                        _P, ctypes.c_size_t, _P, _P, _P], ctypes.c_int),
     "tbe_profile_select": ([ctypes.c_char_p], ctypes.c_int),
     "tbe_profile_read": ([_P, _P], ctypes.c_int),
+    "tbe_calibration_copy": ([_P, _P, ctypes.c_int64, _P], ctypes.c_int),
 }
 
 _lib = None
@@ -239,6 +241,11 @@ def tbe_profile_read():
     ms = ctypes.c_double(0.0)
     _check(lib().tbe_profile_read(ctypes.byref(n), ctypes.byref(ms)), "tbe_profile_read")
     return int(n.value), float(ms.value)
+
+
+def tbe_calibration_copy(src: torch.Tensor, dst: torch.Tensor, nbytes: int, stream=None):
+    _check(lib().tbe_calibration_copy(_ptr(src), _ptr(dst), int(nbytes), _stream(stream)),
+           "tbe_calibration_copy")
 
 
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:

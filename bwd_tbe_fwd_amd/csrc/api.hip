@@ -105,6 +105,7 @@ Config resolve_config(const tbe_config* c) {
   r.fwd_unroll = c->fwd_unroll > 0 ? c->fwd_unroll : d.fwd_unroll;
   r.bwd_unroll = c->bwd_unroll > 0 ? c->bwd_unroll : d.bwd_unroll;
   r.sort_blocks = c->sort_blocks;
+  r.bag_windows = c->bag_windows;
   return r;
 }
 
@@ -118,7 +119,7 @@ struct Carver {
     return at;
   }
 };
-constexpr int kDefaultSortBlocks = 1024;
+constexpr int kDefaultSortBlocks = 4096;
 constexpr int kMaxSortBlocks = 4096;
 }  // namespace
 
@@ -154,6 +155,22 @@ BwdLayout bwd_layout(const tbe_tables* tb, int64_t N, int weighted, const Config
   L.nblocks = static_cast<int>((n1 + L.seg - 1) / L.seg);
   L.sort_hist = c.take((static_cast<size_t>(kRadixDigits) * L.nblocks + kRadixDigits) * 4);
   L.seg_cnt = c.take(static_cast<size_t>(L.nblocks) * 4);
+  L.cls_blocks = static_cast<int>(hmax(1, hmin(1024, (n1 + kBlock - 1) / kBlock)));
+  L.cls_cnt = c.take(static_cast<size_t>(TBE_NUM_BUCKETS + 2) * L.cls_blocks * 4);
+  // long-run chunks grouped by (table, window of bags); at most 4096 groups
+  L.nwin = 1;
+  if (cfg.bag_windows > 1 && tb->B > 1) {
+    int64_t nw = hmin(cfg.bag_windows, hmax(1, 4096 / tb->T));
+    nw = hmin(nw, tb->B);
+    L.nwin = static_cast<int>(nw);
+  }
+  if (L.nwin > 1) {
+    L.win_size = static_cast<int>((tb->B + L.nwin - 1) / L.nwin);
+    L.units = tb->T * L.nwin;
+    L.chunk_unit = c.take(L.cap_chunk * 4);
+    L.chunk_order = c.take(L.cap_chunk * 4);
+    L.unit_cnt = c.take(static_cast<size_t>(L.units) * 4);
+  }
   L.counters = c.take(kNumCounters * 4);
   L.total = c.off;
   // keys are in [0, total_rows]; total_rows itself marks an id outside its table
@@ -239,8 +256,9 @@ void tbe_config_default(tbe_config* cfg) {
   cfg->chunk = 256;
   cfg->hist_enable = 1;
   cfg->fwd_unroll = 8;
-  cfg->bwd_unroll = 4;
+  cfg->bwd_unroll = 2;
   cfg->sort_blocks = 0;
+  cfg->bag_windows = 32;
 }
 
 int64_t tbe_meta_entries(int32_t T) { return T >= 0 ? static_cast<int64_t>(TBE_META_FIELDS) * (T + 1) : 0; }

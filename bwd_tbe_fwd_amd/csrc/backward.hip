@@ -23,12 +23,13 @@ __global__ __launch_bounds__(kBlock) void grad_accum_kernel(
     const uint4* __restrict__ long_list, const uint32_t* __restrict__ long_table,
     const uint2* __restrict__ chunk_list, const int32_t* __restrict__ counters,
     const int64_t* __restrict__ meta, int32_t B, int32_t out_width, int chunk, int max_D,
-    float* __restrict__ partial) {
+    const uint32_t* __restrict__ order, float* __restrict__ partial) {
   const int lane = lane_id();
   const int64_t wave = (static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x) >> 6;
   const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * kBlock) >> 6;
   const int64_t n = counters[kChunks];
-  for (int64_t cix = wave; cix < n; cix += nwaves) {
+  for (int64_t i = wave; i < n; i += nwaves) {
+    const int64_t cix = order ? order[i] : i;
     const uint2 ch = chunk_list[cix];
     const uint4 L = long_list[ch.x];
     const int t = static_cast<int>(long_table[ch.x]);
@@ -95,6 +96,70 @@ __global__ __launch_bounds__(kBlock) void grad_accum_kernel(
   }
 }
 
+// Long-run chunk ordering: the chunks are regrouped by (table, window of bags of
+// their first lookup), so that chunks processed at the same time read gradient
+// rows of the same few thousand bags - rows that many long runs share - and find
+// them in L2.  A counting sort: units counted, scanned, then chunks scattered.
+__global__ __launch_bounds__(kBlock) void chunk_units_kernel(
+    const uint2* __restrict__ chunk_list, const uint4* __restrict__ long_list,
+    const uint32_t* __restrict__ long_table, const uint32_t* __restrict__ pay,
+    const uint32_t* __restrict__ bag_of, const int32_t* __restrict__ counters, int chunk, int B,
+    int nwin, int win_size, uint32_t* __restrict__ chunk_unit, uint32_t* __restrict__ unit_cnt) {
+  const int64_t n = counters[kChunks];
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
+  for (int64_t c = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; c < n; c += stride) {
+    const uint2 ch = chunk_list[c];
+    const uint4 L = long_list[ch.x];
+    const uint32_t t = long_table[ch.x];
+    const uint32_t p = pay[L.y + ch.y * static_cast<uint32_t>(chunk)];
+    const int64_t bag = bag_of ? static_cast<int64_t>(bag_of[p]) : static_cast<int64_t>(p);
+    int64_t b = bag - static_cast<int64_t>(t) * B;
+    b = min(max(b, static_cast<int64_t>(0)), static_cast<int64_t>(B - 1));
+    const uint32_t u = t * static_cast<uint32_t>(nwin) + static_cast<uint32_t>(b / win_size);
+    chunk_unit[c] = u;
+    atomicAdd(&unit_cnt[u], 1u);
+  }
+}
+
+// exclusive scan of the unit counts in place (one workgroup, units <= 4096)
+__global__ __launch_bounds__(kBlock) void unit_scan_kernel(uint32_t* __restrict__ cnt, int units) {
+  __shared__ uint32_t s_tmp[kWavesPerBlock];
+  const int lane = lane_id(), w = threadIdx.x >> 6;
+  const int ipt = (units + kBlock - 1) / kBlock;
+  const int i0 = threadIdx.x * ipt;
+  uint32_t v[16];
+  uint32_t sum = 0;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    v[q] = (q < ipt && i0 + q < units) ? cnt[i0 + q] : 0u;
+    sum += v[q];
+  }
+  uint32_t inc = sum;
+  for (int d = 1; d < kWave; d <<= 1) {
+    const uint32_t u = __shfl_up(inc, d);
+    if (lane >= d) inc += u;
+  }
+  if (lane == kWave - 1) s_tmp[w] = inc;
+  __syncthreads();
+  uint32_t run = inc - sum;
+  for (int k = 0; k < w; ++k) run += s_tmp[k];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    if (q < ipt && i0 + q < units) cnt[i0 + q] = run;
+    run += v[q];
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void chunk_scatter_kernel(const uint32_t* __restrict__ chunk_unit,
+                                                               uint32_t* __restrict__ unit_pos,
+                                                               const int32_t* __restrict__ counters,
+                                                               uint32_t* __restrict__ order) {
+  const int64_t n = counters[kChunks];
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
+  for (int64_t c = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; c < n; c += stride)
+    order[atomicAdd(&unit_pos[chunk_unit[c]], 1u)] = static_cast<uint32_t>(c);
+}
+
 template <bool WEIGHTED>
 tbe_status accum_go(const tbe_tables* tb, const float* psw, const float* grad_out, char* ws,
                     const BwdLayout& L, int final_buf, const Config& cfg, hipStream_t s) {
@@ -103,6 +168,26 @@ tbe_status accum_go(const tbe_tables* tb, const float* psw, const float* grad_ou
       hmax(1, hmin((L.cap_chunk + kWavesPerBlock - 1) / kWavesPerBlock, maxb)));
   const uint32_t* pay = reinterpret_cast<const uint32_t*>(ws + L.pay[final_buf]);
   const uint32_t* bag_of = WEIGHTED ? reinterpret_cast<const uint32_t*>(ws + L.bag_of) : nullptr;
+  const uint32_t* order = nullptr;
+  if (L.nwin > 1) {
+    uint32_t* unit_cnt = reinterpret_cast<uint32_t*>(ws + L.unit_cnt);
+    uint32_t* chunk_unit = reinterpret_cast<uint32_t*>(ws + L.chunk_unit);
+    uint32_t* chunk_order = reinterpret_cast<uint32_t*>(ws + L.chunk_order);
+    if (tbe_status st = launch_fill_i32(reinterpret_cast<int32_t*>(unit_cnt), 0, L.units, s)) return st;
+    const int g2 = static_cast<int>(hmax(1, hmin((L.cap_chunk + kBlock - 1) / kBlock, maxb)));
+    ProfScope ps("chunk_order", s);
+    hipLaunchKernelGGL(chunk_units_kernel, dim3(g2), dim3(kBlock), 0, s,
+                       reinterpret_cast<const uint2*>(ws + L.chunk_list),
+                       reinterpret_cast<const uint4*>(ws + L.long_list),
+                       reinterpret_cast<const uint32_t*>(ws + L.long_table), pay, bag_of,
+                       reinterpret_cast<const int32_t*>(ws + L.counters), cfg.chunk, tb->B, L.nwin,
+                       L.win_size, chunk_unit, unit_cnt);
+    hipLaunchKernelGGL(unit_scan_kernel, dim3(1), dim3(kBlock), 0, s, unit_cnt, L.units);
+    hipLaunchKernelGGL(chunk_scatter_kernel, dim3(g2), dim3(kBlock), 0, s, chunk_unit, unit_cnt,
+                       reinterpret_cast<const int32_t*>(ws + L.counters), chunk_order);
+    if (tbe_status st = check_launch("chunk_order")) return st;
+    order = chunk_order;
+  }
   ProfScope ps("grad_accum", s);
 #define TBE_ACC(U)                                                                                 \
   hipLaunchKernelGGL((grad_accum_kernel<WEIGHTED, U>), dim3(grid), dim3(kBlock), 0, s, grad_out, pay, \
@@ -110,7 +195,8 @@ tbe_status accum_go(const tbe_tables* tb, const float* psw, const float* grad_ou
                      reinterpret_cast<const uint32_t*>(ws + L.long_table),                        \
                      reinterpret_cast<const uint2*>(ws + L.chunk_list),                           \
                      reinterpret_cast<const int32_t*>(ws + L.counters), tb->meta, tb->B,           \
-                     tb->out_width, cfg.chunk, tb->max_D, reinterpret_cast<float*>(ws + L.partial))
+                     tb->out_width, cfg.chunk, tb->max_D, order,                                  \
+                     reinterpret_cast<float*>(ws + L.partial))
   if (cfg.bwd_unroll <= 2) TBE_ACC(2);
   else if (cfg.bwd_unroll <= 4) TBE_ACC(4);
   else TBE_ACC(8);

@@ -153,29 +153,45 @@ __device__ __forceinline__ int owner_table(const OT* off, const int64_t* s_start
 
 constexpr int kLdsTables = 2048;
 
+// Each thread checks 4 positions per step, a grid stride apart, so four
+// independent loads are in flight; the owning table is found by binary search
+// over the repaired table starts held in LDS.
 template <typename IT, typename OT>
 __global__ __launch_bounds__(kBlock) void bounds_indices(IT* __restrict__ idx, int64_t N,
                                                           const OT* __restrict__ off,
                                                           const int64_t* __restrict__ meta, int T,
                                                           int64_t B, int64_t* __restrict__ counts) {
   __shared__ int64_t s_start[kLdsTables + 1];
+  __shared__ int64_t s_E[kLdsTables];
   __shared__ int64_t s_cnt[kWavesPerBlock];
   const bool lds = T <= kLdsTables;
   if (lds)
-    for (int t = threadIdx.x; t <= T; t += kBlock) s_start[t] = static_cast<int64_t>(off[t * B]);
+    for (int t = threadIdx.x; t <= T; t += kBlock) {
+      s_start[t] = static_cast<int64_t>(off[t * B]);
+      if (t < T) s_E[t] = meta[4 * (t + 1)] - meta[4 * t];
+    }
   __syncthreads();
+  const int64_t lo_t = lds ? s_start[0] : static_cast<int64_t>(off[0]);
+  const int64_t hi_t = lds ? s_start[T] : static_cast<int64_t>(off[T * B]);
   int64_t fixed = 0;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
-  for (int64_t p = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; p < N; p += stride) {
-    const int64_t v = static_cast<int64_t>(idx[p]);
-    const int64_t lo_t = lds ? s_start[0] : static_cast<int64_t>(off[0]);
-    const int64_t hi_t = lds ? s_start[T] : static_cast<int64_t>(off[T * B]);
-    if (p < lo_t || p >= hi_t) continue;  // not in any bag (cannot happen after the repair)
-    const int t = owner_table(off, lds ? s_start : nullptr, T, B, p);
-    const int64_t E = meta[4 * (t + 1)] - meta[4 * t];
-    if (static_cast<uint64_t>(v) >= static_cast<uint64_t>(E)) {
-      idx[p] = 0;
-      ++fixed;
+  for (int64_t p0 = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; p0 < N; p0 += 4 * stride) {
+    int64_t v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int64_t p = p0 + k * stride;
+      v[k] = p < N ? static_cast<int64_t>(idx[p]) : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int64_t p = p0 + k * stride;
+      if (p >= N || p < lo_t || p >= hi_t) continue;  // outside every bag: cannot happen after repair
+      const int t = owner_table(off, lds ? s_start : nullptr, T, B, p);
+      const int64_t E = lds ? s_E[t] : meta[4 * (t + 1)] - meta[4 * t];
+      if (static_cast<uint64_t>(v[k]) >= static_cast<uint64_t>(E)) {
+        idx[p] = 0;
+        ++fixed;
+      }
     }
   }
   for (int m = 1; m < kWave; m <<= 1) fixed += __shfl_xor(fixed, m);
@@ -213,7 +229,7 @@ tbe_status bounds_go(const tbe_tables* tb, void* indices, void* offsets, int64_t
   }
   if (tbe_status st = check_launch("bounds_offsets")) return st;
   if (N > 0) {
-    const int64_t want = (N + kBlock * 4 - 1) / (kBlock * 4);
+    const int64_t want = (N + kBlock * 16 - 1) / (kBlock * 16);
     const int grid = static_cast<int>(hmax(1, hmin(want, static_cast<int64_t>(device_cu_count()) * 8)));
     ProfScope ps("bounds_indices", s);
     hipLaunchKernelGGL((bounds_indices<IT, OT>), dim3(grid), dim3(kBlock), 0, s,

@@ -24,44 +24,48 @@
 namespace tbe {
 namespace {
 
+// Pools the lookups [s, e) of one bag into acc (this lane's VEC columns, row group
+// lane >> lg).  The bag's first 64 ids (and weights) arrive already loaded in
+// first_id / first_w: they were fetched while the previous bag's rows were in
+// flight.
 template <int DT, typename IT, bool PSW, int VEC, typename ACC, int UNROLL>
 __device__ __forceinline__ void pool_bag(const typename Fmt<DT>::S* __restrict__ Wt, int64_t E,
                                          int D, const IT* __restrict__ indices,
                                          const float* __restrict__ psw, int64_t s, int64_t e,
-                                         int lg, int col, bool act, ACC (&acc)[VEC]) {
+                                         int lg, int col, bool act, int64_t first_id, float first_w,
+                                         ACC (&acc)[VEC]) {
   const int lane = lane_id();
   const int G = kWave >> lg;  // rows per wave instruction
   const int g = lane >> lg;   // this lane's row group
   for (int64_t j0 = s; j0 < e; j0 += kWave) {
     const int n = static_cast<int>(min<int64_t>(kWave, e - j0));
-    int32_t myrow = -1;
-    float myw = 0.f;
-    if (lane < n) {
-      const int64_t r = static_cast<int64_t>(indices[j0 + lane]);
-      myrow = (static_cast<uint64_t>(r) < static_cast<uint64_t>(E)) ? static_cast<int32_t>(r) : -1;
-      if constexpr (PSW) myw = psw[j0 + lane];
+    int64_t r = first_id;
+    float myw = first_w;
+    if (j0 != s) {
+      r = lane < n ? static_cast<int64_t>(indices[j0 + lane]) : -1;
+      if constexpr (PSW) myw = lane < n ? psw[j0 + lane] : 0.f;
     }
+    const int32_t myrow =
+        (lane < n && static_cast<uint64_t>(r) < static_cast<uint64_t>(E)) ? static_cast<int32_t>(r) : -1;
     for (int q0 = 0; q0 < n; q0 += G * UNROLL) {
-      float v[UNROLL][VEC];
+      RawVec<DT, VEC> raw[UNROLL];
       float wq[UNROLL];
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) {
         const int q = q0 + u * G + g;
         const int row = __shfl(myrow, q & (kWave - 1));
         if constexpr (PSW) wq[u] = __shfl(myw, q & (kWave - 1));
-        if (q < n && row >= 0 && act) {
-          load_vec<DT, VEC>(Wt + static_cast<int64_t>(row) * D + col, v[u]);
-        } else {
-#pragma unroll
-          for (int i = 0; i < VEC; ++i) v[u][i] = 0.f;
-        }
+        if (q < n && row >= 0 && act) load_raw<DT, VEC>(Wt + static_cast<int64_t>(row) * D + col, raw[u]);
+        else zero_raw(raw[u]);
       }
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) {
+        float v[VEC];
+        unpack_raw(raw[u], v);
 #pragma unroll
         for (int i = 0; i < VEC; ++i) {
-          if constexpr (PSW) acc[i] += static_cast<ACC>(wq[u]) * static_cast<ACC>(v[u][i]);
-          else acc[i] += static_cast<ACC>(v[u][i]);
+          if constexpr (PSW) acc[i] += static_cast<ACC>(wq[u]) * static_cast<ACC>(v[i]);
+          else acc[i] += static_cast<ACC>(v[i]);
         }
       }
     }
@@ -96,9 +100,29 @@ __global__ __launch_bounds__(kBlock) void fwd_gather_kernel(
       e = min(max(e, s), N);
     }
     const int nb = static_cast<int>(min<int64_t>(kWave, slots - base));
+    // ids of the first bag; each later bag's first ids are fetched one bag ahead
+    int64_t nxt_id = -1;
+    float nxt_w = 0.f;
+    {
+      const int64_t s0 = read_lane64(s, 0), e0 = read_lane64(e, 0);
+      if (lane < e0 - s0) {
+        nxt_id = static_cast<int64_t>(indices[s0 + lane]);
+        if constexpr (PSW) nxt_w = psw[s0 + lane];
+      }
+    }
     for (int k = 0; k < nb; ++k) {
       const int64_t sk = read_lane64(s, k), ek = read_lane64(e, k);
       const int t = read_lane(bt, k), b = read_lane(bb, k);
+      const int64_t cur_id = nxt_id;
+      const float cur_w = nxt_w;
+      if (k + 1 < nb) {
+        const int64_t s1 = read_lane64(s, k + 1), e1 = read_lane64(e, k + 1);
+        nxt_id = -1;
+        if (lane < e1 - s1) {
+          nxt_id = static_cast<int64_t>(indices[s1 + lane]);
+          if constexpr (PSW) nxt_w = psw[s1 + lane];
+        }
+      }
       if (t != cur_t) {
         m = load_meta(meta, t);
         cur_t = t;
@@ -116,7 +140,7 @@ __global__ __launch_bounds__(kBlock) void fwd_gather_kernel(
 #pragma unroll
         for (int i = 0; i < VEC; ++i) acc[i] = 0;
         pool_bag<DT, IT, PSW, VEC, ACC, UNROLL>(W + m.w_base, m.E, D, indices, psw, sk, ek, lg,
-                                                col, act, acc);
+                                                col, act, cur_id, cur_w, acc);
         for (int msk = lpr; msk < kWave; msk <<= 1) {
 #pragma unroll
           for (int i = 0; i < VEC; ++i) acc[i] += __shfl_xor(acc[i], msk);

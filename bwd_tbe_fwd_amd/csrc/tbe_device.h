@@ -81,6 +81,50 @@ __device__ __forceinline__ void load_vec(const typename Fmt<DT>::S* p, float (&v
   }
 }
 
+// VEC elements of format DT kept as loaded (32-bit words), so that rows in
+// flight cost VEC*sizeof(S)/4 registers rather than VEC.
+template <int DT, int VEC>
+struct RawVec {
+  static constexpr int kWords = VEC * static_cast<int>(sizeof(typename Fmt<DT>::S)) / 4;
+  uint32_t w[kWords];
+};
+
+template <int DT, int VEC>
+__device__ __forceinline__ void load_raw(const typename Fmt<DT>::S* p, RawVec<DT, VEC>& r) {
+  constexpr int W = RawVec<DT, VEC>::kWords;
+  if constexpr (W == 2) {
+    const u32x2 x = *reinterpret_cast<const u32x2*>(p);
+    r.w[0] = x.x; r.w[1] = x.y;
+  } else {
+    static_assert(W % 4 == 0, "vectors of 8 or 16k bytes");
+#pragma unroll
+    for (int i = 0; i < W; i += 4) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint32_t*>(p) + i);
+      r.w[i] = x.x; r.w[i + 1] = x.y; r.w[i + 2] = x.z; r.w[i + 3] = x.w;
+    }
+  }
+}
+
+template <int DT, int VEC>
+__device__ __forceinline__ void zero_raw(RawVec<DT, VEC>& r) {
+#pragma unroll
+  for (int i = 0; i < RawVec<DT, VEC>::kWords; ++i) r.w[i] = 0u;
+}
+
+template <int DT, int VEC>
+__device__ __forceinline__ void unpack_raw(const RawVec<DT, VEC>& r, float (&v)[VEC]) {
+  if constexpr (DT == 0) {
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) v[i] = __uint_as_float(r.w[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < VEC / 2; ++i) {
+      v[2 * i] = Fmt<DT>::to_f(static_cast<uint16_t>(r.w[i]));
+      v[2 * i + 1] = Fmt<DT>::to_f(static_cast<uint16_t>(r.w[i] >> 16));
+    }
+  }
+}
+
 // Stores 4 floats rounded to format DT at p (aligned to the vector size).
 template <int DT>
 __device__ __forceinline__ void store_vec4(typename Fmt<DT>::S* p, const float (&v)[4]) {

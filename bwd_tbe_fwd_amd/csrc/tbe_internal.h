@@ -40,7 +40,7 @@ constexpr int kRadixItems = 16;                       // keys per thread per til
 constexpr int kRadixTile = kBlock * kRadixItems;      // 4096 keys
 
 struct Config {
-  int threshold, chunk, hist_enable, fwd_unroll, bwd_unroll, sort_blocks;
+  int threshold, chunk, hist_enable, fwd_unroll, bwd_unroll, sort_blocks, bag_windows;
 };
 Config resolve_config(const tbe_config* c);
 
@@ -49,10 +49,13 @@ struct BwdLayout {
   int64_t N;
   size_t keys[2], pay[2], bag_of, run_key, run_start;
   size_t long_list, long_table, chunk_list, partial, short_list[TBE_NUM_BUCKETS];
-  size_t sort_hist, seg_cnt, counters, total;
+  size_t sort_hist, seg_cnt, cls_cnt, counters, total;
+  size_t chunk_unit, chunk_order, unit_cnt;  // long-run chunk ordering by (table, bag window)
+  int nwin, win_size, units;
   int64_t cap_long, cap_chunk, cap_short[TBE_NUM_BUCKETS];
   int64_t seg;        // keys per sort / RLE block (multiple of kRadixTile)
   int nblocks;        // sort / RLE blocks
+  int cls_blocks;     // classification blocks
   int passes;         // radix passes
   int shift[4], bits[4];
   int key_bits;

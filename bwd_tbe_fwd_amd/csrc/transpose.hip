@@ -24,8 +24,8 @@
 //    the tile by digit in LDS and writes each digit's keys contiguously.  No
 //    inter-block waiting, so every wave always finishes.
 //  - RLE: head flags counted per block, scanned, then written in order.
-//  - classify: one thread per run, LDS counters per category, one global
-//    atomic per category per block.
+//  - classify: per-block category counts, a scan across blocks, an ordered
+//    write: lists in key order, no global atomics.
 #include "tbe_device.h"
 #include "tbe_internal.h"
 
@@ -154,19 +154,25 @@ __global__ __launch_bounds__(kBlock) void radix_upsweep(const uint32_t* __restri
   for (int i = lane; i < ndig; i += kWave) s_cnt[w][i] = 0;
   __builtin_amdgcn_wave_barrier();
   const int64_t lo = blockIdx.x * seg, hi = min(lo + seg, N);
-  // each wave reads 4 x 64 consecutive keys per step
-  for (int64_t base = lo + w * 4 * kWave; base < hi; base += 4 * kBlock) {
-    uint32_t k[4];
+  // each wave reads 4 x 256 consecutive keys per step, 16 bytes per lane per load
+  for (int64_t base = lo + w * 16 * kWave; base < hi; base += 16 * kBlock) {
+    uint32_t k[16];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const int64_t i = base + s * kWave + lane;
-      k[s] = i < hi ? keys[i] : 0u;
+      const int64_t i = base + s * 4 * kWave + 4 * lane;
+      if (i + 3 < hi) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(keys + i);
+        k[4 * s] = v.x; k[4 * s + 1] = v.y; k[4 * s + 2] = v.z; k[4 * s + 3] = v.w;
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) k[4 * s + q] = i + q < hi ? keys[i + q] : 0u;
+      }
     }
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int64_t i = base + s * kWave + lane;
+    for (int j = 0; j < 16; ++j) {
+      const int64_t i = base + (j >> 2) * 4 * kWave + 4 * lane + (j & 3);
       const bool valid = i < hi;
-      const uint32_t d = (k[s] >> shift) & mask;
+      const uint32_t d = (k[j] >> shift) & mask;
       const uint64_t peers = match_digit(d, bits, __ballot(valid));
       if (valid && lane == __ffsll(static_cast<long long>(peers)) - 1) s_cnt[w][d] += __popcll(peers);
       __builtin_amdgcn_wave_barrier();
@@ -305,8 +311,21 @@ __global__ __launch_bounds__(kBlock) void rle_count(const uint32_t* __restrict__
   __shared__ uint32_t s_tmp[kWavesPerBlock];
   const int64_t lo = blockIdx.x * seg, hi = min(lo + seg, N);
   uint32_t c = 0;
-  for (int64_t i = lo + threadIdx.x; i < hi; i += kBlock)
-    c += (i == 0 || keys[i] != keys[i - 1]) ? 1u : 0u;
+  // four keys (and their predecessors) in flight per thread
+  for (int64_t i0 = lo + threadIdx.x; i0 < hi; i0 += 4 * kBlock) {
+    uint32_t k[4], pk[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t i = i0 + q * kBlock;
+      k[q] = i < hi ? keys[i] : 0u;
+      pk[q] = (i < hi && i > 0) ? keys[i - 1] : ~0u;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t i = i0 + q * kBlock;
+      c += (i < hi && (i == 0 || k[q] != pk[q])) ? 1u : 0u;
+    }
+  }
   c = block_sum(c, s_tmp);
   if (threadIdx.x == 0) cnt[blockIdx.x] = c;
 }
@@ -380,66 +399,181 @@ __global__ __launch_bounds__(kBlock) void rle_write(const uint32_t* __restrict__
 // ---------------------------------------------------------------------------
 // classification: long runs (with chunk plan) and short runs per D bucket
 // ---------------------------------------------------------------------------
+// Three passes over the runs, with no atomics on global memory: per-block counts
+// of every category, an exclusive scan of those counts across blocks, then an
+// ordered write.  The lists come out in run (= key) order, so runs of one table
+// stay together, and the result is the same on every run.  The block segments
+// are derived on the device from the run count.
 struct ShortLists {
   uint4* p[TBE_NUM_BUCKETS];
   int64_t cap[TBE_NUM_BUCKETS];
 };
 
-__global__ __launch_bounds__(kBlock) void classify_kernel(
+constexpr int kCats = 1 + TBE_NUM_BUCKETS;  // 0: long, 1 + b: short bucket b
+constexpr int kClsRows = kCats + 1;         // + chunks of long runs
+constexpr int kLdsTables = 2048;
+
+struct TableLds {
+  int64_t rb[kLdsTables + 1];
+  int32_t D[kLdsTables];
+};
+
+__device__ __forceinline__ void load_tables(TableLds& s, const int64_t* __restrict__ meta, int T) {
+  if (T <= kLdsTables)
+    for (int t = threadIdx.x; t <= T; t += kBlock) {
+      s.rb[t] = meta[4 * t];
+      if (t < T) s.D[t] = static_cast<int32_t>(meta[4 * t + 3]);
+    }
+  __syncthreads();
+}
+
+__device__ __forceinline__ int lds_table_of_key(const TableLds& s, const int64_t* __restrict__ meta, int T,
+                                                uint32_t key, int& D) {
+  if (T > kLdsTables) {
+    const int t = table_of_key(meta, T, key);
+    D = static_cast<int>(meta[4 * t + 3]);
+    return t;
+  }
+  int lo = 0, hi = T - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (s.rb[mid] <= static_cast<int64_t>(key)) lo = mid; else hi = mid - 1;
+  }
+  D = s.D[lo];
+  return lo;
+}
+
+__device__ __forceinline__ void block_segment(int64_t n, int64_t& lo, int64_t& hi) {
+  int64_t seg = (n + gridDim.x - 1) / gridDim.x;
+  seg = (seg + kBlock - 1) / kBlock * kBlock;
+  lo = min(n, static_cast<int64_t>(blockIdx.x) * seg);
+  hi = min(n, lo + seg);
+}
+
+// category of a run (-1: ids outside their table, dropped) and its chunk count
+__device__ __forceinline__ int run_category(const TableLds& s, const int64_t* __restrict__ meta, int T,
+                                            uint32_t total_rows, int threshold, int chunk, uint32_t key,
+                                            uint32_t len, int& t, uint32_t& nch) {
+  nch = 0;
+  t = 0;
+  if (key >= total_rows) return -1;
+  int D;
+  t = lds_table_of_key(s, meta, T, key, D);
+  if (len >= static_cast<uint32_t>(threshold)) {
+    nch = (len + chunk - 1) / chunk;
+    return 0;
+  }
+  return 1 + bucket_of_D(D);
+}
+
+__global__ __launch_bounds__(kBlock) void classify_count(
     const uint32_t* __restrict__ run_key, const uint32_t* __restrict__ run_start,
-    int32_t* __restrict__ counters, const int64_t* __restrict__ meta, int T, uint32_t total_rows,
-    int threshold, int chunk, uint4* __restrict__ long_list, uint32_t* __restrict__ long_table,
-    uint2* __restrict__ chunk_list, int64_t cap_long, int64_t cap_chunk, ShortLists lists) {
-  constexpr int kCats = 1 + TBE_NUM_BUCKETS;
-  __shared__ int32_t s_cnt[kCats];
-  __shared__ int32_t s_base[kCats];
-  __shared__ int32_t s_chunks, s_chunk_base;
-  const int64_t n = counters[kRuns];
-  for (int64_t r0 = static_cast<int64_t>(blockIdx.x) * kBlock; r0 < n;
-       r0 += static_cast<int64_t>(gridDim.x) * kBlock) {
-    if (threadIdx.x < kCats) s_cnt[threadIdx.x] = 0;
-    if (threadIdx.x == 0) s_chunks = 0;
-    __syncthreads();
-    const int64_t r = r0 + threadIdx.x;
-    int cat = -1, rank = 0, t = 0;
+    const int32_t* __restrict__ counters, const int64_t* __restrict__ meta, int T,
+    uint32_t total_rows, int threshold, int chunk, uint32_t* __restrict__ cls_cnt) {
+  __shared__ TableLds s_tab;
+  __shared__ uint32_t s_cnt[kClsRows];
+  if (threadIdx.x < kClsRows) s_cnt[threadIdx.x] = 0;
+  load_tables(s_tab, meta, T);
+  int64_t lo, hi;
+  block_segment(counters[kRuns], lo, hi);
+  for (int64_t r = lo + threadIdx.x; r < hi; r += kBlock) {
+    const uint32_t key = run_key[r];
+    const uint32_t len = run_start[r + 1] - run_start[r];
+    int t;
+    uint32_t nch;
+    const int cat = run_category(s_tab, meta, T, total_rows, threshold, chunk, key, len, t, nch);
+    if (cat >= 0) atomicAdd(&s_cnt[cat], 1u);
+    if (nch) atomicAdd(&s_cnt[kCats], nch);
+  }
+  __syncthreads();
+  if (threadIdx.x < kClsRows) cls_cnt[threadIdx.x * gridDim.x + blockIdx.x] = s_cnt[threadIdx.x];
+}
+
+// one workgroup per category row: exclusive scan over blocks, total into counters
+__global__ __launch_bounds__(kBlock) void classify_scan(uint32_t* __restrict__ cls_cnt, int nblk,
+                                                        int32_t* __restrict__ counters) {
+  __shared__ uint32_t s_tmp[kWavesPerBlock];
+  uint32_t* row = cls_cnt + static_cast<int64_t>(blockIdx.x) * nblk;
+  const int ipt = (nblk + kBlock - 1) / kBlock;
+  const int i0 = threadIdx.x * ipt;
+  uint32_t v[16];
+  uint32_t sum = 0;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    v[q] = (q < ipt && i0 + q < nblk) ? row[i0 + q] : 0u;
+    sum += v[q];
+  }
+  uint32_t total;
+  uint32_t run = block_exclusive_sum(sum, s_tmp, &total);
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    if (q < ipt && i0 + q < nblk) row[i0 + q] = run;
+    run += v[q];
+  }
+  if (threadIdx.x == 0) {
+    const int c = blockIdx.x;
+    const int dst = c == 0 ? kLong : (c == kCats ? kChunks : kShort0 + c - 1);
+    counters[dst] = static_cast<int32_t>(total);
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void classify_write(
+    const uint32_t* __restrict__ run_key, const uint32_t* __restrict__ run_start,
+    const int32_t* __restrict__ counters, const int64_t* __restrict__ meta, int T,
+    uint32_t total_rows, int threshold, int chunk, const uint32_t* __restrict__ cls_cnt,
+    uint4* __restrict__ long_list, uint32_t* __restrict__ long_table, uint2* __restrict__ chunk_list,
+    int64_t cap_long, int64_t cap_chunk, ShortLists lists) {
+  __shared__ TableLds s_tab;
+  __shared__ uint32_t s_base[kClsRows];
+  __shared__ uint32_t s_wcnt[kWavesPerBlock][kCats];
+  __shared__ uint32_t s_tmp[kWavesPerBlock];
+  const int lane = lane_id(), w = threadIdx.x >> 6;
+  if (threadIdx.x < kClsRows) s_base[threadIdx.x] = cls_cnt[threadIdx.x * gridDim.x + blockIdx.x];
+  load_tables(s_tab, meta, T);
+  int64_t lo, hi;
+  block_segment(counters[kRuns], lo, hi);
+  for (int64_t tile = lo; tile < hi; tile += kBlock) {
+    const int64_t r = tile + threadIdx.x;
+    int cat = -1, t = 0;
     uint32_t key = 0, start = 0, len = 0, nch = 0;
-    int32_t my_cb = 0;
-    if (r < n) {
+    if (r < hi) {
       key = run_key[r];
       start = run_start[r];
       len = run_start[r + 1] - start;
-      if (key < total_rows) {
-        t = table_of_key(meta, T, key);
-        if (len >= static_cast<uint32_t>(threshold)) {
-          cat = 0;
-          nch = (len + chunk - 1) / chunk;
-          my_cb = atomicAdd(&s_chunks, static_cast<int32_t>(nch));
-        } else {
-          cat = 1 + bucket_of_D(static_cast<int>(meta[4 * t + 3]));
+      cat = run_category(s_tab, meta, T, total_rows, threshold, chunk, key, len, t, nch);
+    }
+    uint32_t wrank = 0;
+#pragma unroll
+    for (int c = 0; c < kCats; ++c) {
+      const uint64_t m = __ballot(cat == c);
+      if (cat == c) wrank = __popcll(m & lanemask_lt());
+      if (lane == 0) s_wcnt[w][c] = __popcll(m);
+    }
+    uint32_t ch_total;
+    const uint32_t ch_off = block_exclusive_sum(nch, s_tmp, &ch_total);  // synchronizes
+    if (cat >= 0) {
+      uint32_t pre = s_base[cat];
+      for (int k = 0; k < w; ++k) pre += s_wcnt[k][cat];
+      const int64_t slot = static_cast<int64_t>(pre) + wrank;
+      if (cat == 0) {
+        const int64_t cb = static_cast<int64_t>(s_base[kCats]) + ch_off;
+        if (slot < cap_long) {
+          long_list[slot] = make_uint4(key, start, len, static_cast<uint32_t>(cb));
+          long_table[slot] = static_cast<uint32_t>(t);
+          for (uint32_t c = 0; c < nch; ++c)
+            if (cb + c < cap_chunk) chunk_list[cb + c] = make_uint2(static_cast<uint32_t>(slot), c);
         }
-        rank = atomicAdd(&s_cnt[cat], 1);
+      } else if (slot < lists.cap[cat - 1]) {
+        lists.p[cat - 1][slot] = make_uint4(key, start, len, static_cast<uint32_t>(t));
       }
     }
     __syncthreads();
-    if (threadIdx.x < kCats && s_cnt[threadIdx.x] > 0)
-      s_base[threadIdx.x] = atomicAdd(&counters[threadIdx.x == 0 ? kLong : kShort0 + threadIdx.x - 1],
-                                      s_cnt[threadIdx.x]);
-    if (threadIdx.x == kCats && s_chunks > 0) s_chunk_base = atomicAdd(&counters[kChunks], s_chunks);
-    __syncthreads();
-    if (cat == 0) {
-      const int64_t li = static_cast<int64_t>(s_base[0]) + rank;
-      const int64_t cb = static_cast<int64_t>(s_chunk_base) + my_cb;
-      if (li < cap_long) {
-        long_list[li] = make_uint4(key, start, len, static_cast<uint32_t>(cb));
-        long_table[li] = static_cast<uint32_t>(t);
-        for (uint32_t c = 0; c < nch; ++c)
-          if (cb + c < cap_chunk) chunk_list[cb + c] = make_uint2(static_cast<uint32_t>(li), c);
-      }
-    } else if (cat > 0) {
-      const int b = cat - 1;
-      const int64_t slot = static_cast<int64_t>(s_base[cat]) + rank;
-      if (slot < lists.cap[b]) lists.p[b][slot] = make_uint4(key, start, len, static_cast<uint32_t>(t));
+    if (threadIdx.x < kCats) {
+      uint32_t add = 0;
+      for (int k = 0; k < kWavesPerBlock; ++k) add += s_wcnt[k][threadIdx.x];
+      s_base[threadIdx.x] += add;
     }
+    if (threadIdx.x == kCats) s_base[kCats] += ch_total;
     __syncthreads();
   }
 }
@@ -542,11 +676,14 @@ tbe_status launch_transpose(const tbe_tables* tb, const IndexArgs& ia, int weigh
     lists.cap[b] = L.cap_short[b];
   }
   {
-    const int64_t want = (N + kBlock - 1) / kBlock;
-    const int grid = static_cast<int>(hmax(1, hmin(want, static_cast<int64_t>(device_cu_count()) * 8)));
+    uint32_t* cls_cnt = reinterpret_cast<uint32_t*>(ws + L.cls_cnt);
+    const uint32_t total_rows = static_cast<uint32_t>(tb->total_rows);
     ProfScope ps("classify", s);
-    hipLaunchKernelGGL(classify_kernel, dim3(grid), dim3(kBlock), 0, s, run_key, run_start, counters,
-                       tb->meta, tb->T, static_cast<uint32_t>(tb->total_rows), cfg.threshold, cfg.chunk,
+    hipLaunchKernelGGL(classify_count, dim3(L.cls_blocks), dim3(kBlock), 0, s, run_key, run_start,
+                       counters, tb->meta, tb->T, total_rows, cfg.threshold, cfg.chunk, cls_cnt);
+    hipLaunchKernelGGL(classify_scan, dim3(kClsRows), dim3(kBlock), 0, s, cls_cnt, L.cls_blocks, counters);
+    hipLaunchKernelGGL(classify_write, dim3(L.cls_blocks), dim3(kBlock), 0, s, run_key, run_start,
+                       counters, tb->meta, tb->T, total_rows, cfg.threshold, cfg.chunk, cls_cnt,
                        reinterpret_cast<uint4*>(ws + L.long_list), reinterpret_cast<uint32_t*>(ws + L.long_table),
                        reinterpret_cast<uint2*>(ws + L.chunk_list), L.cap_long, L.cap_chunk, lists);
   }

@@ -101,8 +101,11 @@ typedef struct {
   int32_t chunk;           /* lookups per long-run chunk (default 256) */
   int32_t hist_enable;     /* 1: histogram + MFMA forward for the eligible table (default 1) */
   int32_t fwd_unroll;      /* forward row loads in flight per lane group: 2, 4 or 8 (default 8) */
-  int32_t bwd_unroll;      /* backward gradient-row loads in flight: 2, 4 or 8 (default 4) */
+  int32_t bwd_unroll;      /* long-run chunk gradient rows in flight per lane group: 2, 4 or 8 (default 2) */
   int32_t sort_blocks;     /* workgroups of each radix pass (default 0 = automatic) */
+  int32_t bag_windows;     /* long-run chunks are processed grouped by (table, bag window of their
+                              first lookup), B / bag_windows bags per window, so that chunks that
+                              read the same gradient rows run together (default 32; <= 1: off) */
 } tbe_config;
 
 /* Device-side view of the transpose, for inspection by tests (tbe_transpose). */
@@ -236,6 +239,14 @@ tbe_status tbe_transpose(const tbe_tables* tables, const void* indices, int32_t 
  */
 tbe_status tbe_profile_select(const char* kernel_name);
 tbe_status tbe_profile_read(int64_t* launches, double* total_ms);
+
+/*
+ * Measurement support: copies `bytes` (a multiple of 16, buffers 16-byte aligned)
+ * from src to dst with one 16-byte load and store per lane, like the library's
+ * kernels.  Its hardware byte counters, for a copy of known size, calibrate the
+ * counters read for the other kernels.
+ */
+tbe_status tbe_calibration_copy(const void* src, void* dst, int64_t bytes, tbe_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -33,7 +33,12 @@ import torch
 _GOLDEN = 0x9E3779B97F4A7C15
 _M1 = 0xBF58476D1CE4E5B9
 _M2 = 0x94D049BB133111EB
-_CHUNK = 1 << 24  # elements drawn per step, bounds temporaries
+_CHUNK = 1 << 24  # elements drawn per step on the host, bounds temporaries
+_CHUNK_GPU = 1 << 27  # on a GPU (fewer, larger launches)
+
+
+def _chunk(device) -> int:
+    return _CHUNK_GPU if torch.device(device).type == "cuda" else _CHUNK
 
 
 def _s64(x: int) -> int:
@@ -189,6 +194,7 @@ class BatchSpec:
     lr: float = 0.01
     eps: float = 1e-8
     pooling_hint: Optional[tuple] = None  # per-table expected L (plan-time hint)
+    seed: int = 0                # default seed of make_batch
 
     @property
     def T(self) -> int:
@@ -207,31 +213,28 @@ def _c4_tables():
     return tuple(out)
 
 
-CONFIGS = {
-    1: BatchSpec("tiny: T=4 E=1000 D=64 fp32, B=256, L=8, SGD",
+WORKLOADS = {
+    "tiny": BatchSpec("tiny: T=4 E=1000 D=64 fp32, B=256, L=8, SGD",
                  tuple(TableSpec(1000, 64, ("fixed", 8)) for _ in range(4)),
-                 B=256, w_dtype=torch.float32, w_range=0.1, optimizer="sgd"),
-    2: BatchSpec("uniform mid-size: T=26 E=1M D=128 fp16, B=65536, L~Poisson(20) in [1,100], int32",
+                 B=256, w_dtype=torch.float32, w_range=0.1, optimizer="sgd", seed=1001),
+    "uniform": BatchSpec("uniform mid-size: T=26 E=1M D=128 fp16, B=65536, L~Poisson(20) in [1,100], int32",
                  tuple(TableSpec(1_000_000, 128, ("poisson", 20.0, 1, 100)) for _ in range(26)),
                  B=65536, w_dtype=torch.float16, w_range=0.05, itype=torch.int32,
-                 otype=torch.int32, optimizer="rowwise_adagrad"),
-    3: BatchSpec("histogram + companion: E=64 L=128 and E=100K L~Poisson(10), D=128 fp16, B=131072",
+                 otype=torch.int32, optimizer="rowwise_adagrad", seed=1002),
+    "histogram": BatchSpec("histogram + companion: E=64 L=128 and E=100K L~Poisson(10), D=128 fp16, B=131072",
                  (TableSpec(64, 128, ("fixed", 128)),
                   TableSpec(100_000, 128, ("poisson", 10.0, None, None))),
                  B=131072, w_dtype=torch.float16, w_range=0.05, optimizer="rowwise_adagrad",
-                 pooling_hint=(128, 10)),
-    4: BatchSpec("mixed-width weighted: T=16 D in {32,64,128,256}, E 1e5..4e6, bf16, Zipf(1.1), B=32768",
+                 pooling_hint=(128, 10), seed=1003),
+    "mixed": BatchSpec("mixed-width weighted: T=16 D in {32,64,128,256}, E 1e5..4e6, bf16, Zipf(1.1), B=32768",
                  _c4_tables(), B=32768, w_dtype=torch.bfloat16, w_range=0.05, weighted=True,
-                 optimizer="sgd"),
-    5: BatchSpec("skewed large: T=32 E=2M D=128 fp16, B=131072, L~Poisson(20), Zipf(0.91, 95000)",
+                 optimizer="sgd", seed=1004),
+    "skewed": BatchSpec("skewed large: T=32 E=2M D=128 fp16, B=131072, L~Poisson(20), Zipf(0.91, 95000)",
                  tuple(TableSpec(2_000_000, 128, ("poisson", 20.0, None, None),
                                  ("zipf", 0.91, 95_000)) for _ in range(32)),
-                 B=131072, w_dtype=torch.float16, w_range=0.05, optimizer="rowwise_adagrad"),
+                 B=131072, w_dtype=torch.float16, w_range=0.05, optimizer="rowwise_adagrad",
+                 seed=1005),
 }
-
-
-def config_seed(n: int) -> int:
-    return 1000 + n
 
 
 # ----------------------------------------------------------------------------
@@ -301,8 +304,9 @@ def _draw_indices(ts: TableSpec, seed: int, t: int, n: int, device) -> torch.Ten
         alpha, S = ts.idx[1], ts.idx[2] or ts.E
         cdf = torch.from_numpy(zipf_cdf(alpha, S)).to(device)
         a, c = _scatter_params(seed, t, ts.E)
-    for s in range(0, n, _CHUNK):
-        m = min(_CHUNK, n - s)
+    ch = _chunk(device)
+    for s in range(0, n, ch):
+        m = min(ch, n - s)
         bits = draw_bits(base, s, m, device)
         if kind == "uniform":
             out[s:s + m] = below(bits, ts.E)
@@ -316,14 +320,17 @@ def _draw_indices(ts: TableSpec, seed: int, t: int, n: int, device) -> torch.Ten
 
 def _fill_weights(w: torch.Tensor, base: int, a: float, dtype, device):
     n = w.numel()
-    for s in range(0, n, _CHUNK):
-        m = min(_CHUNK, n - s)
+    ch = _chunk(device)
+    for s in range(0, n, ch):
+        m = min(ch, n - s)
         w[s:s + m] = uniform_sym(draw_bits(base, s, m, device), a, dtype)
 
 
-def make_batch(spec: BatchSpec, seed: int, device="cpu", with_grad=True,
+def make_batch(spec: BatchSpec, seed: Optional[int] = None, device="cpu", with_grad=True,
                with_weights=True) -> Batch:
-    """Draws every tensor of ``spec`` with ``seed`` on ``device``."""
+    """Draws every tensor of ``spec`` with ``seed`` (default: the spec's own) on ``device``."""
+    if seed is None:
+        seed = spec.seed
     dev = torch.device(device)
     bt = Batch(spec, seed)
     T, B = spec.T, spec.B
@@ -352,15 +359,15 @@ def make_batch(spec: BatchSpec, seed: int, device="cpu", with_grad=True,
     if spec.weighted:
         bt.psw = torch.empty(N, dtype=torch.float32, device=dev)
         base = stream_base(seed, "psw")
-        for s in range(0, N, _CHUNK):
-            m = min(_CHUNK, N - s)
+        for s in range(0, N, _chunk(dev)):
+            m = min(_chunk(dev), N - s)
             bt.psw[s:s + m] = uniform01_f32(draw_bits(base, s, m, dev))
     if with_grad:
         W = sum(spec_t.D for spec_t in spec.tables)
         g = torch.empty(B * W, dtype=torch.float32, device=dev)
         base = stream_base(seed, "grad")
-        for s in range(0, B * W, _CHUNK):
-            m = min(_CHUNK, B * W - s)
+        for s in range(0, B * W, _chunk(dev)):
+            m = min(_chunk(dev), B * W - s)
             g[s:s + m] = normal_f32(draw_bits(base, s, m, dev))
         bt.grad_out = g.view(B, W)
     if spec.optimizer == "rowwise_adagrad":

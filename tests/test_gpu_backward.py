@@ -9,7 +9,7 @@ import oracle
 import tbe_inputs as ti
 from gpu_util import (DevBatch, check_momentum, check_weights, flush_print, host_arrays,
                       oracle_backward, row_g_abs_sq, step_bound)
-from test_gpu_forward import mixed_spec, small_spec
+from test_gpu_forward import WORKLOAD_NAMES, mixed_spec, small_spec
 
 pytestmark = pytest.mark.gpu
 
@@ -33,12 +33,12 @@ def run_and_check(bt, cfg=None, optimizer=None, lr=None, what=""):
     return db, W, mom, r
 
 
-@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("n", WORKLOAD_NAMES)
 def test_backward_configs_small(n):
     spec = small_spec(n)
-    flush_print(f"backward config {n}: {spec.name} ({spec.optimizer})")
-    bt = ti.make_batch(spec, ti.config_seed(n))
-    run_and_check(bt, what=f"config {n}")
+    flush_print(f"backward {n}: {spec.name} ({spec.optimizer})")
+    bt = ti.make_batch(spec)
+    run_and_check(bt, what=n)
 
 
 @pytest.mark.parametrize("w_dtype", [torch.float32, torch.float16, torch.bfloat16])
@@ -54,7 +54,7 @@ def test_backward_dtypes_mixed_D(w_dtype, optimizer, weighted):
 @pytest.mark.parametrize("threshold,chunk", [(10 ** 9, 256), (256, 256), (8, 8), (4, 2), (1, 1)])
 def test_routing_invariance(optimizer, threshold, chunk):
     """Same batch, every split point: all match the oracle (tutorial section 3's sweep)."""
-    bt = ti.make_batch(small_spec(5).replace(optimizer=optimizer), 23)
+    bt = ti.make_batch(small_spec("skewed").replace(optimizer=optimizer), 23)
     cfg = tbe.make_config(long_threshold=threshold, chunk=chunk)
     run_and_check(bt, cfg, what=f"{optimizer} t={threshold} c={chunk}")
 
@@ -62,7 +62,7 @@ def test_routing_invariance(optimizer, threshold, chunk):
 @pytest.mark.parametrize("weighted", [False, True])
 def test_gradient_extraction(weighted):
     """SGD with lr = -1 on all-zero fp32 weights writes the summed gradient itself."""
-    spec = small_spec(4 if weighted else 5).replace(w_dtype=torch.float32, optimizer="sgd")
+    spec = small_spec("mixed" if weighted else "skewed").replace(w_dtype=torch.float32, optimizer="sgd")
     bt = ti.make_batch(spec, 29)
     bt.weights = torch.zeros_like(bt.weights)
     db = DevBatch(bt)
@@ -74,7 +74,7 @@ def test_gradient_extraction(weighted):
 
 
 def test_backward_deterministic():
-    bt = ti.make_batch(small_spec(5), 31)
+    bt = ti.make_batch(small_spec("skewed"), 31)
     cfg = tbe.make_config(long_threshold=16, chunk=16)
     outs = []
     for _ in range(2):
@@ -86,7 +86,7 @@ def test_backward_deterministic():
 
 
 def test_untouched_rows_bit_identical():
-    bt = ti.make_batch(small_spec(5), 37)
+    bt = ti.make_batch(small_spec("skewed"), 37)
     db = DevBatch(bt)
     W0 = db.W.clone()
     m0 = db.mom.clone()

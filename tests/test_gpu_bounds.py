@@ -63,7 +63,7 @@ def test_bounds_injected_faults(seed, itype):
 
 
 def test_bounds_valid_input_unchanged():
-    bt = ti.make_batch(ti.scaled(ti.CONFIGS[5], B=4000, E_div=100, T=3), 5, with_grad=False)
+    bt = ti.make_batch(ti.scaled(ti.WORKLOADS["skewed"], B=4000, E_div=100, T=3), 5, with_grad=False)
     got_idx, got_off, cnt = gpu_bounds(bt.E, bt.D, bt.B, bt.indices.numpy(), bt.offsets.numpy(),
                                        torch.int64, torch.int64)
     assert cnt.tolist() == [0, 0]

@@ -11,20 +11,24 @@ from gpu_util import DevBatch, check_forward, flush_print, host_arrays
 pytestmark = pytest.mark.gpu
 
 
-def small_spec(n: int) -> ti.BatchSpec:
-    """Config n's recipe at a size the oracle finishes in about a second; ragged B and N."""
-    if n == 1:
-        return ti.CONFIGS[1]
-    if n == 2:
-        return ti.scaled(ti.CONFIGS[2], B=1500, E_div=500, T=5)
-    if n == 3:
-        c3 = ti.CONFIGS[3]
-        return c3.replace(name="hist+companion small",
-                          tables=(c3.tables[0], ti.TableSpec(1000, 128, ("poisson", 10.0, None, None))),
-                          B=700)
-    if n == 4:
-        return ti.scaled(ti.CONFIGS[4], B=700, E_div=200, T=8)
-    return ti.scaled(ti.CONFIGS[5], B=1500, E_div=200, T=4)
+def small_spec(name: str) -> ti.BatchSpec:
+    """A workload's recipe at a size the oracle finishes in about a second; ragged B and N."""
+    W = ti.WORKLOADS
+    if name == "tiny":
+        return W["tiny"]
+    if name == "uniform":
+        return ti.scaled(W["uniform"], B=1500, E_div=500, T=5)
+    if name == "histogram":
+        h = W["histogram"]
+        return h.replace(name="hist+companion small",
+                         tables=(h.tables[0], ti.TableSpec(1000, 128, ("poisson", 10.0, None, None))),
+                         B=700)
+    if name == "mixed":
+        return ti.scaled(W["mixed"], B=700, E_div=200, T=8)
+    return ti.scaled(W["skewed"], B=1500, E_div=200, T=4)
+
+
+WORKLOAD_NAMES = ["tiny", "uniform", "histogram", "mixed", "skewed"]
 
 
 def mixed_spec(w_dtype, itype, otype, weighted, B=333):
@@ -44,16 +48,16 @@ def _oracle_forward(bt):
     return oracle.forward(a["T"], a["B"], a["E"], a["D"], a["W"], a["idx"], a["off"], a["psw"])
 
 
-@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("n", WORKLOAD_NAMES)
 def test_forward_configs_small(n):
     spec = small_spec(n)
-    flush_print(f"forward config {n}: {spec.name}")
-    bt = ti.make_batch(spec, ti.config_seed(n))
+    flush_print(f"forward {n}: {spec.name}")
+    bt = ti.make_batch(spec)
     db = DevBatch(bt)
     out = db.forward()
     torch.cuda.synchronize()
     ref, ref_abs = _oracle_forward(bt)
-    check_forward(out.cpu().numpy(), ref, ref_abs, bt.w_dtype == torch.float32, f"config {n}")
+    check_forward(out.cpu().numpy(), ref, ref_abs, bt.w_dtype == torch.float32, n)
 
 
 @pytest.mark.parametrize("w_dtype", [torch.float32, torch.float16, torch.bfloat16])
@@ -85,7 +89,7 @@ def test_forward_D_not_multiple_of_8():
 
 
 def test_forward_unroll_knob_is_bitwise_neutral():
-    bt = ti.make_batch(small_spec(5), 9)
+    bt = ti.make_batch(small_spec("skewed"), 9)
     db = DevBatch(bt)
     outs = [db.forward(tbe.make_config(fwd_unroll=u)).cpu() for u in (2, 4, 8)]
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[1], outs[2])
@@ -115,13 +119,13 @@ def test_histogram_path_exact(L):
     assert np.array_equal(on.double().numpy(), ref)
 
 
-def test_histogram_path_matches_oracle_config3_recipe():
-    bt = ti.make_batch(small_spec(3), ti.config_seed(3))
+def test_histogram_path_matches_oracle_histogram_recipe():
+    bt = ti.make_batch(small_spec("histogram"))
     db = DevBatch(bt)
     assert db.tables.c.hist_table == 0
     out = db.forward()
     ref, ref_abs = _oracle_forward(bt)
-    check_forward(out.cpu().numpy(), ref, ref_abs, False, "hist config 3")
+    check_forward(out.cpu().numpy(), ref, ref_abs, False, "histogram workload")
 
 
 def test_histogram_not_used_with_per_sample_weights():

@@ -1,0 +1,206 @@
+"""Parity at the full workload sizes, in the launch configuration the benchmark times.
+
+The oracle cannot redo an 84M-lookup batch in seconds, so at these sizes:
+  * forward:   sampled bags (random, longest, empty, first/last) are recomputed one by one
+               by the oracle from host copies of exactly the rows they touch;
+  * backward:  sampled rows (the hottest of each table, random touched rows, short and long
+               runs) are recomputed by the oracle from every lookup that touched them; every
+               untouched row of every table must be bit-identical after the step;
+  * transpose: properties that fix a stable sort uniquely - positions are a permutation,
+               each key is the linearized id of its position, (key, position) strictly
+               increases - plus exact run / routing counts from a host histogram.
+"""
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import bwd_tbe_fwd_amd as tbe
+import oracle
+import tbe_inputs as ti
+from gpu_util import ODT, DevBatch, check_forward, check_momentum, check_weights, flush_print
+
+pytestmark = pytest.mark.gpu
+
+_cache = {}
+
+
+def full_batch(n):
+    if n not in _cache:
+        _cache.clear()
+        gc.collect()
+        torch.cuda.empty_cache()
+        spec = ti.WORKLOADS[n]
+        flush_print(f"drawing full workload {n}: {spec.name}")
+        bt = ti.make_batch(spec, device="cuda")
+        db = DevBatch.__new__(DevBatch)
+        db.bt, db.device = bt, "cuda"
+        db.tables = tbe.Tables(bt.E, bt.D, bt.B, bt.w_dtype, device="cuda", pooling_hint=spec.pooling_hint)
+        db.W, db.idx, db.off, db.psw, db.grad, db.mom = (bt.weights, bt.indices, bt.offsets, bt.psw,
+                                                          bt.grad_out, bt.momentum)
+        host = dict(idx=bt.indices.long().cpu().numpy(), off=bt.offsets.long().cpu().numpy(),
+                    psw=None if bt.psw is None else bt.psw.double().cpu().numpy())
+        _cache[n] = (db, host)
+    return _cache[n]
+
+
+def table_rows(db, t, rows):
+    """Host fp64 copy of rows of table t (W still holds the values before any update)."""
+    bt = db.bt
+    Wt = db.W[sum(e * d for e, d in zip(bt.E[:t], bt.D[:t])):][:bt.E[t] * bt.D[t]].view(bt.E[t], bt.D[t])
+    return Wt[torch.as_tensor(rows, device="cuda", dtype=torch.long)].double().cpu().numpy()
+
+
+@pytest.mark.parametrize("n", ["uniform", "histogram", "mixed", "skewed"])
+def test_full_forward_sampled_bags(n):
+    db, h = full_batch(n)
+    bt = db.bt
+    out = torch.full((bt.B, sum(bt.D)), float("nan"), dtype=torch.float32, device="cuda")
+    tbe.tbe_forward(db.tables, db.W, db.idx, db.off, db.psw, out)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(len(n))
+    off = h["off"]
+    lens = np.diff(off)
+    picks = set(rng.integers(0, bt.T * bt.B, 300).tolist())
+    picks |= set(np.argsort(lens)[-20:].tolist()) | set(np.flatnonzero(lens == 0)[:10].tolist())
+    picks |= {0, bt.T * bt.B - 1}
+    cols = np.concatenate([[0], np.cumsum(bt.D)])
+    for bag in sorted(picks):
+        t, b = divmod(bag, bt.B)
+        s, e = off[bag], off[bag + 1]
+        ids = h["idx"][s:e]
+        uniq, local = np.unique(ids, return_inverse=True)
+        Wsub = table_rows(db, t, uniq) if uniq.size else np.zeros((0, bt.D[t]))
+        psw = None if h["psw"] is None else h["psw"][s:e]
+        ref, ref_abs = oracle.forward(1, 1, [max(uniq.size, 1)], [bt.D[t]],
+                                      Wsub if uniq.size else np.zeros(bt.D[t]), local, [0, e - s], psw)
+        got = out[b, cols[t]:cols[t + 1]].double().cpu().numpy()[None, :]
+        check_forward(got, ref, ref_abs, bt.w_dtype == torch.float32, f"{n} bag ({t},{b})")
+
+
+@pytest.mark.parametrize("n", ["uniform", "histogram", "mixed", "skewed"])
+def test_full_transpose_properties(n):
+    db, h = full_batch(n)
+    bt = db.bt
+    N = bt.num_indices
+    res = {}
+    for weighted in (True, False):
+        ws = db.workspace(None, weighted)
+        view = tbe.tbe_transpose(db.tables, db.idx, db.off, weighted, ws)
+        torch.cuda.synchronize()
+        cnt = tbe.device_view(view.counters, 16, torch.int32, ws).cpu().numpy()
+        res[weighted] = dict(
+            cnt=cnt,
+            keys=tbe.device_view(view.sorted_keys, N, torch.int32, ws).cpu().numpy().view(np.uint32),
+            pay=tbe.device_view(view.sorted_payload, N, torch.int32, ws).cpu().numpy().view(np.uint32),
+            run_key=tbe.device_view(view.run_key, int(cnt[0]), torch.int32, ws).cpu().numpy().view(np.uint32),
+            run_start=tbe.device_view(view.run_start, int(cnt[0]) + 1, torch.int32, ws).cpu().numpy().view(np.uint32))
+        del ws
+    off = h["off"]
+    bag_of = np.repeat(np.arange(bt.T * bt.B, dtype=np.int64), np.diff(off))
+    rowbase = np.concatenate([[0], np.cumsum(bt.E)])
+    key_of = rowbase[bag_of // bt.B] + h["idx"]
+    w = res[True]
+    pos = w["pay"].astype(np.int64)
+    keys = w["keys"].astype(np.int64)
+    assert np.all(np.bincount(pos, minlength=N) == 1)                 # a permutation
+    assert np.array_equal(keys, key_of[pos])                           # keys follow their lookups
+    step = np.diff(keys) * (N + 1) + np.diff(pos)                      # (key, position) increasing
+    assert np.all(step > 0)
+    u = res[False]
+    assert np.array_equal(u["keys"], w["keys"])
+    assert np.array_equal(u["pay"].astype(np.int64), bag_of[pos])     # bag payload of each lookup
+    heads = np.flatnonzero(np.concatenate([[True], keys[1:] != keys[:-1]]))
+    for r in (w, u):
+        assert int(r["cnt"][tbe.COUNTER_RUNS]) == heads.size
+        assert np.array_equal(r["run_start"][:-1].astype(np.int64), heads)
+        assert np.array_equal(r["run_key"].astype(np.int64), keys[heads])
+    lens = np.diff(np.concatenate([heads, [N]]))
+    is_long = lens >= 256
+    assert int(w["cnt"][tbe.COUNTER_LONG]) == int(is_long.sum())
+    assert int(w["cnt"][tbe.COUNTER_CHUNKS]) == int(((lens[is_long] + 255) // 256).sum())
+    t_of_run = np.searchsorted(rowbase, keys[heads], side="right") - 1
+    Dk = np.array(bt.D)[t_of_run]
+    for b in range(tbe.NUM_BUCKETS):
+        want = int((~is_long & (np.maximum(4, 2 ** np.ceil(np.log2(Dk))) == tbe.BUCKET_D[b])).sum())
+        assert int(w["cnt"][tbe.COUNTER_SHORT0 + b]) == want
+    flush_print(f"{n}: {N} lookups, {heads.size} runs, {int(is_long.sum())} long, "
+                f"max run {int(lens.max())}")
+
+
+@pytest.mark.parametrize("n", ["uniform", "histogram", "mixed", "skewed"])
+def test_full_backward_sampled_rows(n):
+    db, h = full_batch(n)
+    bt = db.bt
+    spec = bt.spec
+    rng = np.random.default_rng(100 + len(n))
+    off = h["off"]
+    samples = []   # (t, row)
+    untouched = []
+    counts = []
+    for t in range(bt.T):
+        s, e = off[t * bt.B], off[(t + 1) * bt.B]
+        c = np.bincount(h["idx"][s:e], minlength=bt.E[t])
+        counts.append(c)
+        touched = np.flatnonzero(c)
+        hot = touched[np.argsort(c[touched])[-2:]]
+        mid = touched[(c[touched] >= 256)][:2]
+        rnd = rng.choice(touched, size=min(4, touched.size), replace=False)
+        samples += [(t, int(r)) for r in set(hot.tolist() + mid.tolist() + rnd.tolist())]
+        free = np.flatnonzero(c == 0)
+        if free.size:
+            untouched += [(t, int(r)) for r in rng.choice(free, size=min(2, free.size), replace=False)]
+    # host copies of the sampled rows, their state and their lookups' gradient rows, before the step
+    before = {(t, r): table_rows(db, t, [r])[0] for (t, r) in samples + untouched}
+    rowbase = np.concatenate([[0], np.cumsum(bt.E)])
+    cols = np.concatenate([[0], np.cumsum(bt.D)])
+    mom0 = None if db.mom is None else db.mom.double().cpu().numpy()
+    grads = {}
+    for (t, r) in samples:
+        s, e = off[t * bt.B], off[(t + 1) * bt.B]
+        p = s + np.flatnonzero(h["idx"][s:e] == r)
+        b = np.searchsorted(off, p, side="right") - 1 - t * bt.B
+        g = db.grad[:, cols[t]:cols[t + 1]][torch.as_tensor(b, device="cuda")].double().cpu().numpy()
+        grads[(t, r)] = (g, None if h["psw"] is None else h["psw"][p])
+    W0 = db.W.clone()
+    m0 = None if db.mom is None else db.mom.clone()
+    ws = db.workspace()
+    lr, eps = oracle.f32_literal(spec.lr), oracle.f32_literal(spec.eps)
+    if spec.optimizer == "sgd":
+        tbe.tbe_backward_sgd(db.tables, db.W, db.idx, db.off, db.psw, db.grad, lr, ws)
+    else:
+        tbe.tbe_backward_rowwise_adagrad(db.tables, db.W, db.mom, db.idx, db.off, db.psw, db.grad,
+                                         lr, eps, ws)
+    torch.cuda.synchronize()
+    del ws
+    # every untouched row of every table is bit-identical
+    pos = 0
+    for t in range(bt.T):
+        E, D = bt.E[t], bt.D[t]
+        free = torch.from_numpy(counts[t] == 0).cuda()
+        a = db.W[pos:pos + E * D].view(E, D)[free]
+        b0 = W0[pos:pos + E * D].view(E, D)[free]
+        assert torch.equal(a.view(torch.int16) if a.dtype != torch.float32 else a.view(torch.int32),
+                           b0.view(torch.int16) if b0.dtype != torch.float32 else b0.view(torch.int32))
+        if m0 is not None:
+            assert torch.equal(db.mom[rowbase[t]:rowbase[t] + E][free], m0[rowbase[t]:rowbase[t] + E][free])
+        pos += E * D
+    # sampled rows: one oracle step from every lookup that touched them
+    opt = oracle.SGD if spec.optimizer == "sgd" else oracle.ROWWISE_ADAGRAD
+    for (t, r) in samples:
+        g, psw = grads[(t, r)]
+        L, D = g.shape[0], bt.D[t]
+        m_in = None if mom0 is None else np.array([mom0[rowbase[t] + r]])
+        res = oracle.backward(1, L, [1], [D], ODT[bt.w_dtype], before[(t, r)], np.zeros(L, np.int64),
+                              np.arange(L + 1), psw, g, opt, lr, eps, m_in)
+        got = table_rows(db, t, [r])[0]
+        Wrow = torch.from_numpy(got).to(bt.w_dtype)
+        denom = np.sqrt(res["m_new"][0]) + eps if opt == oracle.ROWWISE_ADAGRAD else 1.0
+        step_abs = abs(lr) * res["g_abs"] / denom
+        check_weights(Wrow, res, bt.w_dtype, step_abs, f"{n} row ({t},{r}) SL={L}")
+        if opt == oracle.ROWWISE_ADAGRAD:
+            mg = db.mom[rowbase[t] + r:rowbase[t] + r + 1]
+            check_momentum(mg, res, np.array([D], float), np.array([(res["g_abs"] ** 2).sum()]),
+                           f"{n} state ({t},{r})")
+    flush_print(f"{n}: {len(samples)} sampled rows and all untouched rows match")

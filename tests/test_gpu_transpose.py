@@ -8,7 +8,7 @@ import bwd_tbe_fwd_amd as tbe
 import oracle
 import tbe_inputs as ti
 from gpu_util import DevBatch, flush_print, host_arrays
-from test_gpu_forward import mixed_spec, small_spec
+from test_gpu_forward import WORKLOAD_NAMES, mixed_spec, small_spec
 
 pytestmark = pytest.mark.gpu
 
@@ -83,18 +83,18 @@ def check_transpose(bt, weighted, cfg=None, threshold=256, chunk=256, what=""):
     return g, tr
 
 
-@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("n", WORKLOAD_NAMES)
 @pytest.mark.parametrize("weighted", [False, True])
 def test_transpose_configs_small(n, weighted):
     spec = small_spec(n)
-    flush_print(f"transpose config {n} weighted={weighted}")
-    bt = ti.make_batch(spec, ti.config_seed(n))
-    check_transpose(bt, weighted, what=f"config {n}")
+    flush_print(f"transpose {n} weighted={weighted}")
+    bt = ti.make_batch(spec)
+    check_transpose(bt, weighted, what=n)
 
 
 @pytest.mark.parametrize("threshold,chunk", [(10 ** 9, 256), (256, 256), (8, 8), (4, 2), (1, 1)])
 def test_transpose_routing_sweep(threshold, chunk):
-    bt = ti.make_batch(small_spec(5), 15)
+    bt = ti.make_batch(small_spec("skewed"), 15)
     cfg = tbe.make_config(long_threshold=threshold, chunk=chunk)
     check_transpose(bt, False, cfg, threshold, chunk, f"t={threshold} c={chunk}")
 
@@ -107,7 +107,7 @@ def test_transpose_mixed_D_buckets_and_int32():
 
 def test_transpose_many_sort_blocks():
     # more radix blocks than tiles per block: exercises block boundaries inside runs
-    bt = ti.make_batch(ti.scaled(ti.CONFIGS[5], B=3000, E_div=400, T=3), 8)
+    bt = ti.make_batch(ti.scaled(ti.WORKLOADS["skewed"], B=3000, E_div=400, T=3), 8)
     check_transpose(bt, False, tbe.make_config(sort_blocks=7), what="7 sort blocks")
     check_transpose(bt, True, tbe.make_config(sort_blocks=4096), what="max sort blocks")
 

@@ -19,7 +19,7 @@ def test_slices_are_independent_of_what_precedes_them():
 
 
 def test_batch_is_reproducible_and_values_exact_in_dtype():
-    sp = ti.scaled(ti.CONFIGS[4], B=64, E_div=1000, T=4)
+    sp = ti.scaled(ti.WORKLOADS["mixed"], B=64, E_div=1000, T=4)
     a = ti.make_batch(sp, 5)
     b = ti.make_batch(sp, 5)
     for x, y in [(a.weights, b.weights), (a.indices, b.indices), (a.offsets, b.offsets),
@@ -33,8 +33,8 @@ def test_batch_is_reproducible_and_values_exact_in_dtype():
 
 def test_skewed_config_statistics_at_reduced_size():
     # C5 recipe with 1/16 of the bags and 4 tables: Poisson(20) bag sizes, Zipf-skewed rows
-    sp = ti.scaled(ti.CONFIGS[5], B=8192, T=4)
-    bt = ti.make_batch(sp, ti.config_seed(5), with_grad=False, with_weights=False)
+    sp = ti.scaled(ti.WORKLOADS["skewed"], B=8192, T=4)
+    bt = ti.make_batch(sp, ti.WORKLOADS["skewed"].seed, with_grad=False, with_weights=False)
     L = np.diff(bt.offsets.numpy())
     assert abs(L.mean() - 20.0) < 0.2
     idx = bt.indices.numpy()

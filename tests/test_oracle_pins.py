@@ -163,7 +163,7 @@ def test_tutorial_printed_statistics():
 
 
 def test_transpose_matches_numpy_stable_sort():
-    bt = ti.make_batch(ti.scaled(ti.CONFIGS[5], B=300, E_div=20000, T=3), seed=21)
+    bt = ti.make_batch(ti.scaled(ti.WORKLOADS["skewed"], B=300, E_div=20000, T=3), seed=21)
     a = _np_batch(bt)
     tr = oracle.transpose(a["T"], a["B"], a["E"], a["idx"], a["off"])
     base = np.concatenate([[0], np.cumsum(a["E"])])
