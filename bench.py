@@ -176,7 +176,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="skewed", choices=sorted(ti.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-bounds", action="store_true", help="leave the bounds check out of the step")
+    ap.add_argument("--bounds", default="fused", choices=["fused", "standalone", "off"],
+                    help="bounds check in the step: fused into the forward gather (offsets repaired "
+                         "by their own kernel), the standalone kernels, or none")
     ap.add_argument("--calib-copy", action="store_true")
     ap.add_argument("--dominant", default=None,
                     help="kernel to time inside the timed region (skips the one-step-per-kernel scan)")
@@ -209,9 +211,12 @@ def main():
         bt.momentum = torch.zeros(sum(bt.E), dtype=torch.float32, device=dev)
 
     def step():
-        if not args.no_bounds:
-            tbe.tbe_bounds_check(tables, bt.indices, bt.offsets, counts, bws)
-        tbe.tbe_forward(tables, bt.weights, bt.indices, bt.offsets, bt.psw, out)
+        if args.bounds == "fused":
+            tbe.tbe_forward_repair(tables, bt.weights, bt.indices, bt.offsets, bt.psw, out, counts, bws)
+        else:
+            if args.bounds == "standalone":
+                tbe.tbe_bounds_check(tables, bt.indices, bt.offsets, counts, bws)
+            tbe.tbe_forward(tables, bt.weights, bt.indices, bt.offsets, bt.psw, out)
         if spec.optimizer == "sgd":
             tbe.tbe_backward_sgd(tables, bt.weights, bt.indices, bt.offsets, bt.psw, bt.grad_out,
                                  lr, ws)
@@ -267,7 +272,9 @@ def main():
         "config": {"workload": spec.name, "lookups": N, "unique_rows": st["U"], "hottest_run": st["hottest"],
                    "bags": st["TB"], "weights": str(bt.w_dtype).replace("torch.", ""),
                    "indices": str(bt.indices.dtype).replace("torch.", ""), "optimizer": spec.optimizer,
-                   "step": ("" if args.no_bounds else "bounds_check + ") + "forward + backward"},
+                   "step": {"fused": "offsets repair + forward with fused id check + backward",
+                            "standalone": "bounds check + forward + backward",
+                            "off": "forward + backward"}[args.bounds]},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": measured_traffic(dominant) if args.workload == "skewed" else None,

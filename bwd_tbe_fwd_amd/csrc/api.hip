@@ -106,6 +106,7 @@ Config resolve_config(const tbe_config* c) {
   r.bwd_unroll = c->bwd_unroll > 0 ? c->bwd_unroll : d.bwd_unroll;
   r.sort_blocks = c->sort_blocks;
   r.bag_windows = c->bag_windows;
+  r.fused_long = c->fused_long;
   return r;
 }
 
@@ -140,6 +141,7 @@ BwdLayout bwd_layout(const tbe_tables* tb, int64_t N, int weighted, const Config
   L.cap_chunk = N / cfg.chunk + L.cap_long;
   L.long_list = c.take(L.cap_long * 16);
   L.long_table = c.take(L.cap_long * 4);
+  L.long_count = c.take(L.cap_long * 4);
   L.chunk_list = c.take(L.cap_chunk * 8);
   L.partial = c.take(static_cast<size_t>(L.cap_chunk) * tb->max_D * 4);
   for (int b = 0; b < TBE_NUM_BUCKETS; ++b) {
@@ -259,6 +261,7 @@ void tbe_config_default(tbe_config* cfg) {
   cfg->bwd_unroll = 2;
   cfg->sort_blocks = 0;
   cfg->bag_windows = 32;
+  cfg->fused_long = 0;
 }
 
 int64_t tbe_meta_entries(int32_t T) { return T >= 0 ? static_cast<int64_t>(TBE_META_FIELDS) * (T + 1) : 0; }
@@ -349,7 +352,47 @@ tbe_status tbe_forward(const tbe_tables* tables, const void* weights, const void
   const int hist = (cfg.hist_enable && !per_sample_weights && tables->hist_table >= 0) ? tables->hist_table : -1;
   if (hist >= 0)
     if (tbe_status st = launch_forward_hist(tables, weights, ia, out, s)) return st;
-  return launch_forward_gather(tables, weights, ia, per_sample_weights, out, hist, cfg.fwd_unroll, s);
+  return launch_forward_gather(tables, weights, ia, per_sample_weights, out, hist, cfg.fwd_unroll,
+                               nullptr, s);
+}
+
+tbe_status tbe_forward_repair(const tbe_tables* tables, const void* weights, void* indices,
+                              int32_t index_type, void* offsets, int32_t offset_type, int64_t num_indices,
+                              const float* per_sample_weights, float* out, int64_t* error_counts,
+                              void* workspace, size_t workspace_bytes, const tbe_config* config,
+                              tbe_stream_t stream) {
+  g_error[0] = 0;
+  if (tbe_status st = check_tables(tables)) return st;
+  if (tbe_status st = check_index_args(tables, indices, index_type, offsets, offset_type, num_indices)) return st;
+  if (!error_counts) { set_error("error_counts is NULL"); return TBE_ERR_ARG; }
+  if (!workspace || workspace_bytes < bounds_workspace(tables) || (reinterpret_cast<uintptr_t>(workspace) & 255)) {
+    set_error("bounds workspace needs %zu bytes, 256-byte aligned", bounds_workspace(tables));
+    return TBE_ERR_WORKSPACE;
+  }
+  if (tables->B > 0) {
+    if (tbe_status st = check_rows(weights, "weights", weight_align(tables))) return st;
+    if (tbe_status st = check_rows(out, "out", 16)) return st;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (tbe_status st = launch_bounds_offsets(tables, offsets, offset_type, num_indices, error_counts,
+                                            workspace, s))
+    return st;
+  if (tables->B == 0) return launch_bounds_indices(tables, indices, index_type, offsets, offset_type,
+                                                   num_indices, error_counts, s);
+  const Config cfg = resolve_config(config);
+  IndexArgs ia{indices, index_type, offsets, offset_type, num_indices};
+  const int hist = (cfg.hist_enable && !per_sample_weights && tables->hist_table >= 0) ? tables->hist_table : -1;
+  if (hist >= 0) {
+    // the histogram kernel does not repair: standalone validation first
+    if (tbe_status st = launch_bounds_indices(tables, indices, index_type, offsets, offset_type,
+                                              num_indices, error_counts, s))
+      return st;
+    if (tbe_status st = launch_forward_hist(tables, weights, ia, out, s)) return st;
+    return launch_forward_gather(tables, weights, ia, per_sample_weights, out, hist, cfg.fwd_unroll,
+                                 nullptr, s);
+  }
+  return launch_forward_gather(tables, weights, ia, per_sample_weights, out, -1, cfg.fwd_unroll,
+                               error_counts, s);
 }
 
 size_t tbe_backward_workspace_bytes(const tbe_tables* tables, int64_t num_indices, int32_t weighted,

@@ -13,9 +13,7 @@
 namespace tbe {
 namespace {
 
-// One wave per chunk.  Lanes form groups of D/4 (at most 64) lanes; each group
-// reads one gradient row per instruction as float4 per lane, UNROLL
-// instructions in flight; the groups' sums are combined with xor shuffles.
+// One wave per chunk (accumulate_chunk in backward_kernels.h).
 template <bool WEIGHTED, int UNROLL>
 __global__ __launch_bounds__(kBlock) void grad_accum_kernel(
     const float* __restrict__ grad_out, const uint32_t* __restrict__ pay,
@@ -24,7 +22,6 @@ __global__ __launch_bounds__(kBlock) void grad_accum_kernel(
     const uint2* __restrict__ chunk_list, const int32_t* __restrict__ counters,
     const int64_t* __restrict__ meta, int32_t B, int32_t out_width, int chunk, int max_D,
     const uint32_t* __restrict__ order, float* __restrict__ partial) {
-  const int lane = lane_id();
   const int64_t wave = (static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x) >> 6;
   const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * kBlock) >> 6;
   const int64_t n = counters[kChunks];
@@ -34,65 +31,10 @@ __global__ __launch_bounds__(kBlock) void grad_accum_kernel(
     const uint4 L = long_list[ch.x];
     const int t = static_cast<int>(long_table[ch.x]);
     const TableMeta m = load_meta(meta, t);
-    const int D = static_cast<int>(m.D);
     const uint32_t lo = L.y + ch.y * static_cast<uint32_t>(chunk);
     const uint32_t hi = min(lo + static_cast<uint32_t>(chunk), L.y + L.z);
-    const int64_t bag_lo = static_cast<int64_t>(t) * B;
-    float* dst = partial + cix * max_D;
-    for (int cb = 0; cb < D; cb += 4 * kWave) {
-      const int wcols = min(D - cb, 4 * kWave);
-      const int lpr = pow2_ceil(wcols / 4);
-      const int lg = __builtin_ctz(lpr);
-      const int G = kWave >> lg;
-      const int g = lane >> lg;
-      const int cc = lane & (lpr - 1);
-      const int col = cb + cc * 4;
-      const bool act = cc * 4 < wcols;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (uint32_t j0 = lo; j0 < hi; j0 += kWave) {
-        const int nb = static_cast<int>(min<uint32_t>(kWave, hi - j0));
-        int32_t myb = -1;
-        float myw = 1.f;
-        if (lane < nb) {
-          const uint32_t pv = pay[j0 + lane];
-          int64_t bag;
-          if constexpr (WEIGHTED) {
-            bag = bag_of[pv];
-            myw = psw[pv];
-          } else {
-            bag = pv;
-          }
-          const int64_t br = bag - bag_lo;
-          myb = (br >= 0 && br < B) ? static_cast<int32_t>(br) : -1;
-        }
-        for (int q0 = 0; q0 < nb; q0 += G * UNROLL) {
-          f32x4 v[UNROLL];
-          float wq[UNROLL];
-#pragma unroll
-          for (int u = 0; u < UNROLL; ++u) {
-            const int q = q0 + u * G + g;
-            const int b = __shfl(myb, q & (kWave - 1));
-            wq[u] = WEIGHTED ? __shfl(myw, q & (kWave - 1)) : 1.f;
-            if (q < nb && b >= 0 && act)
-              v[u] = load_f4(grad_out + static_cast<int64_t>(b) * out_width + m.col_base + col);
-            else
-              v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-          }
-#pragma unroll
-          for (int u = 0; u < UNROLL; ++u) {
-            if constexpr (WEIGHTED) acc += wq[u] * v[u];
-            else acc += v[u];
-          }
-        }
-      }
-      for (int msk = lpr; msk < kWave; msk <<= 1) {
-        acc.x += __shfl_xor(acc.x, msk);
-        acc.y += __shfl_xor(acc.y, msk);
-        acc.z += __shfl_xor(acc.z, msk);
-        acc.w += __shfl_xor(acc.w, msk);
-      }
-      if (g == 0 && act) store_f4(dst + col, acc);
-    }
+    accumulate_chunk<WEIGHTED, UNROLL>(grad_out, pay, bag_of, psw, m, t, B, out_width, lo, hi,
+                                       partial + cix * max_D);
   }
 }
 
@@ -169,25 +111,7 @@ tbe_status accum_go(const tbe_tables* tb, const float* psw, const float* grad_ou
   const uint32_t* pay = reinterpret_cast<const uint32_t*>(ws + L.pay[final_buf]);
   const uint32_t* bag_of = WEIGHTED ? reinterpret_cast<const uint32_t*>(ws + L.bag_of) : nullptr;
   const uint32_t* order = nullptr;
-  if (L.nwin > 1) {
-    uint32_t* unit_cnt = reinterpret_cast<uint32_t*>(ws + L.unit_cnt);
-    uint32_t* chunk_unit = reinterpret_cast<uint32_t*>(ws + L.chunk_unit);
-    uint32_t* chunk_order = reinterpret_cast<uint32_t*>(ws + L.chunk_order);
-    if (tbe_status st = launch_fill_i32(reinterpret_cast<int32_t*>(unit_cnt), 0, L.units, s)) return st;
-    const int g2 = static_cast<int>(hmax(1, hmin((L.cap_chunk + kBlock - 1) / kBlock, maxb)));
-    ProfScope ps("chunk_order", s);
-    hipLaunchKernelGGL(chunk_units_kernel, dim3(g2), dim3(kBlock), 0, s,
-                       reinterpret_cast<const uint2*>(ws + L.chunk_list),
-                       reinterpret_cast<const uint4*>(ws + L.long_list),
-                       reinterpret_cast<const uint32_t*>(ws + L.long_table), pay, bag_of,
-                       reinterpret_cast<const int32_t*>(ws + L.counters), cfg.chunk, tb->B, L.nwin,
-                       L.win_size, chunk_unit, unit_cnt);
-    hipLaunchKernelGGL(unit_scan_kernel, dim3(1), dim3(kBlock), 0, s, unit_cnt, L.units);
-    hipLaunchKernelGGL(chunk_scatter_kernel, dim3(g2), dim3(kBlock), 0, s, chunk_unit, unit_cnt,
-                       reinterpret_cast<const int32_t*>(ws + L.counters), chunk_order);
-    if (tbe_status st = check_launch("chunk_order")) return st;
-    order = chunk_order;
-  }
+  if (tbe_status st = launch_chunk_order(tb, psw, ws, L, final_buf, cfg, &order, s)) return st;
   ProfScope ps("grad_accum", s);
 #define TBE_ACC(U)                                                                                 \
   hipLaunchKernelGGL((grad_accum_kernel<WEIGHTED, U>), dim3(grid), dim3(kBlock), 0, s, grad_out, pay, \
@@ -205,6 +129,33 @@ tbe_status accum_go(const tbe_tables* tb, const float* psw, const float* grad_ou
 }
 
 }  // namespace
+
+tbe_status launch_chunk_order(const tbe_tables* tb, const float* psw, char* ws, const BwdLayout& L,
+                              int final_buf, const Config& cfg, const uint32_t** order, hipStream_t s) {
+  *order = nullptr;
+  if (L.nwin <= 1) return TBE_OK;
+  const int64_t maxb = static_cast<int64_t>(device_cu_count()) * 8;
+  const uint32_t* pay = reinterpret_cast<const uint32_t*>(ws + L.pay[final_buf]);
+  const uint32_t* bag_of = psw ? reinterpret_cast<const uint32_t*>(ws + L.bag_of) : nullptr;
+  uint32_t* unit_cnt = reinterpret_cast<uint32_t*>(ws + L.unit_cnt);
+  uint32_t* chunk_unit = reinterpret_cast<uint32_t*>(ws + L.chunk_unit);
+  uint32_t* chunk_order = reinterpret_cast<uint32_t*>(ws + L.chunk_order);
+  if (tbe_status st = launch_fill_i32(reinterpret_cast<int32_t*>(unit_cnt), 0, L.units, s)) return st;
+  const int g2 = static_cast<int>(hmax(1, hmin((L.cap_chunk + kBlock - 1) / kBlock, maxb)));
+  ProfScope ps("chunk_order", s);
+  hipLaunchKernelGGL(chunk_units_kernel, dim3(g2), dim3(kBlock), 0, s,
+                     reinterpret_cast<const uint2*>(ws + L.chunk_list),
+                     reinterpret_cast<const uint4*>(ws + L.long_list),
+                     reinterpret_cast<const uint32_t*>(ws + L.long_table), pay, bag_of,
+                     reinterpret_cast<const int32_t*>(ws + L.counters), cfg.chunk, tb->B, L.nwin,
+                     L.win_size, chunk_unit, unit_cnt);
+  hipLaunchKernelGGL(unit_scan_kernel, dim3(1), dim3(kBlock), 0, s, unit_cnt, L.units);
+  hipLaunchKernelGGL(chunk_scatter_kernel, dim3(g2), dim3(kBlock), 0, s, chunk_unit, unit_cnt,
+                     reinterpret_cast<const int32_t*>(ws + L.counters), chunk_order);
+  if (tbe_status st = check_launch("chunk_order")) return st;
+  *order = chunk_order;
+  return TBE_OK;
+}
 
 tbe_status launch_grad_accum(const tbe_tables* tb, const float* psw, const float* grad_out,
                              char* ws, const BwdLayout& L, int final_buf, const Config& cfg,

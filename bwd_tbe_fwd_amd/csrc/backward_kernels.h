@@ -147,6 +147,179 @@ __global__ __launch_bounds__(kBlock) void short_run_kernel(
   }
 }
 
+// Sums the gradient rows of lookups [lo, hi) of one long run (table t) into
+// dst[0 .. D).  One wave: lanes form groups of D/4 (at most 64) lanes; each group
+// reads one gradient row per instruction as float4 per lane, UNROLL
+// instructions in flight; the groups' sums are combined with xor shuffles.
+template <bool WEIGHTED, int UNROLL>
+__device__ __forceinline__ void accumulate_chunk(const float* __restrict__ grad_out,
+                                                 const uint32_t* __restrict__ pay,
+                                                 const uint32_t* __restrict__ bag_of,
+                                                 const float* __restrict__ psw, const TableMeta& m,
+                                                 int t, int32_t B, int32_t out_width, uint32_t lo,
+                                                 uint32_t hi, float* __restrict__ dst) {
+  const int lane = lane_id();
+  const int D = static_cast<int>(m.D);
+  const int64_t bag_lo = static_cast<int64_t>(t) * B;
+  for (int cb = 0; cb < D; cb += 4 * kWave) {
+    const int wcols = min(D - cb, 4 * kWave);
+    const int lpr = pow2_ceil(wcols / 4);
+    const int lg = __builtin_ctz(lpr);
+    const int G = kWave >> lg;
+    const int g = lane >> lg;
+    const int cc = lane & (lpr - 1);
+    const int col = cb + cc * 4;
+    const bool act = cc * 4 < wcols;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (uint32_t j0 = lo; j0 < hi; j0 += kWave) {
+      const int nb = static_cast<int>(min<uint32_t>(kWave, hi - j0));
+      int32_t myb = -1;
+      float myw = 1.f;
+      if (lane < nb) {
+        const uint32_t pv = pay[j0 + lane];
+        int64_t bag;
+        if constexpr (WEIGHTED) {
+          bag = bag_of[pv];
+          myw = psw[pv];
+        } else {
+          bag = pv;
+        }
+        const int64_t br = bag - bag_lo;
+        myb = (br >= 0 && br < B) ? static_cast<int32_t>(br) : -1;
+      }
+      for (int q0 = 0; q0 < nb; q0 += G * UNROLL) {
+        f32x4 v[UNROLL];
+        float wq[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+          const int q = q0 + u * G + g;
+          const int b = __shfl(myb, q & (kWave - 1));
+          wq[u] = WEIGHTED ? __shfl(myw, q & (kWave - 1)) : 1.f;
+          if (q < nb && b >= 0 && act)
+            v[u] = load_f4(grad_out + static_cast<int64_t>(b) * out_width + m.col_base + col);
+          else
+            v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+          if constexpr (WEIGHTED) acc += wq[u] * v[u];
+          else acc += v[u];
+        }
+      }
+    }
+    for (int msk = lpr; msk < kWave; msk <<= 1) {
+      acc.x += __shfl_xor(acc.x, msk);
+      acc.y += __shfl_xor(acc.y, msk);
+      acc.z += __shfl_xor(acc.z, msk);
+      acc.w += __shfl_xor(acc.w, msk);
+    }
+    if (g == 0 && act) store_f4(dst + col, acc);
+  }
+}
+
+// Fused long runs (blog section 4, problem 5: fence, then countdown): chunks write
+// their partial rows, a device-scope fence makes them visible, then each run's
+// countdown (initialised to its chunk count) is decremented; the wave that takes
+// a run's count to zero sums all of its partials in chunk order and applies the
+// optimizer in the same launch.  No wave ever waits for another.  On gfx950 a
+// device-scope release writes back the XCD's L2, so a wave fences once per batch
+// of kFusedBatch chunks rather than once per chunk.
+constexpr int kFusedBatch = 16;
+
+template <int DT, int OPT>
+__device__ __forceinline__ void apply_long_run(typename Fmt<DT>::S* __restrict__ W,
+                                               float* __restrict__ momentum, const uint4& L,
+                                               const TableMeta& m, int chunk, int max_D,
+                                               const float* __restrict__ partial, float lr,
+                                               float eps) {
+  using S = typename Fmt<DT>::S;
+  constexpr int NP = TBE_MAX_D / (4 * kWave);  // column blocks of 256
+  const int lane = lane_id();
+  const int D = static_cast<int>(m.D);
+  const uint32_t nch = (L.z + chunk - 1) / chunk;
+  const int64_t cb = L.w;
+  f32x4 g[NP];
+  float ss = 0.f;
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    g[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int col = p * 4 * kWave + 4 * lane;
+    if (col < D) {
+      for (uint32_t k = 0; k < nch; ++k) g[p] += load_f4(partial + (cb + k) * max_D + col);
+      ss += g[p].x * g[p].x + g[p].y * g[p].y + g[p].z * g[p].z + g[p].w * g[p].w;
+    }
+  }
+  S* wrow = W + m.w_base + (static_cast<int64_t>(L.x) - m.row_base) * D;
+  float denom = 1.f;  // SGD: w - lr * g; Adagrad: w - lr * g / (sqrt(m) + eps)
+  if constexpr (OPT == kOptAdagrad) {
+    for (int msk = 1; msk < kWave; msk <<= 1) ss += __shfl_xor(ss, msk);
+    const float mnew = momentum[L.x] + ss / static_cast<float>(D);
+    if (lane == 0) momentum[L.x] = mnew;
+    denom = sqrtf(mnew) + eps;
+  }
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int col = p * 4 * kWave + 4 * lane;
+    if (col < D) {
+      float wv[4];
+      load_vec<DT, 4>(wrow + col, wv);
+      if constexpr (OPT == kOptAdagrad) {
+        wv[0] -= lr * g[p].x / denom; wv[1] -= lr * g[p].y / denom;
+        wv[2] -= lr * g[p].z / denom; wv[3] -= lr * g[p].w / denom;
+      } else {
+        wv[0] -= lr * g[p].x; wv[1] -= lr * g[p].y; wv[2] -= lr * g[p].z; wv[3] -= lr * g[p].w;
+      }
+      store_vec4<DT>(wrow + col, wv);
+    }
+  }
+}
+
+template <int DT, int OPT, bool WEIGHTED>
+__global__ __launch_bounds__(kBlock) void long_fused_kernel(
+    typename Fmt<DT>::S* __restrict__ W, float* __restrict__ momentum,
+    const float* __restrict__ grad_out, const uint32_t* __restrict__ pay,
+    const uint32_t* __restrict__ bag_of, const float* __restrict__ psw,
+    const uint4* __restrict__ long_list, const uint32_t* __restrict__ long_table,
+    uint32_t* __restrict__ countdown, const uint2* __restrict__ chunk_list,
+    const uint32_t* __restrict__ order, const int32_t* __restrict__ counters,
+    const int64_t* __restrict__ meta, int32_t B, int32_t out_width, int chunk, int max_D,
+    float* __restrict__ partial, float lr, float eps) {
+  const int lane = lane_id();
+  const int64_t wave = (static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x) >> 6;
+  const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * kBlock) >> 6;
+  const int64_t n = counters[kChunks];
+  for (int64_t i0 = wave * kFusedBatch; i0 < n; i0 += nwaves * kFusedBatch) {
+    const int nb = static_cast<int>(min<int64_t>(kFusedBatch, n - i0));
+    uint32_t my_run = 0;  // lane j < nb: long-run slot of the batch's j-th chunk
+    for (int j = 0; j < nb; ++j) {
+      const int64_t cix = order ? order[i0 + j] : i0 + j;
+      const uint2 ch = chunk_list[cix];
+      const uint4 L = long_list[ch.x];
+      const int t = static_cast<int>(long_table[ch.x]);
+      const TableMeta m = load_meta(meta, t);
+      const uint32_t lo = L.y + ch.y * static_cast<uint32_t>(chunk);
+      const uint32_t hi = min(lo + static_cast<uint32_t>(chunk), L.y + L.z);
+      accumulate_chunk<WEIGHTED, 2>(grad_out, pay, bag_of, psw, m, t, B, out_width, lo, hi,
+                                    partial + cix * max_D);
+      if (lane == j) my_run = ch.x;
+    }
+    __threadfence();  // this batch's partials are visible device-wide before its countdowns
+    uint32_t left = 0;
+    if (lane < nb) left = atomicSub(&countdown[my_run], 1u);
+    uint64_t last = __ballot(lane < nb && left == 1u);
+    if (!last) continue;
+    __threadfence();  // the other chunks' partials of those runs are visible to this wave
+    while (last) {
+      const int j = __ffsll(static_cast<long long>(last)) - 1;
+      last &= last - 1;
+      const uint32_t li = __shfl(my_run, j);
+      const uint4 L = long_list[li];
+      const TableMeta m = load_meta(meta, static_cast<int>(long_table[li]));
+      apply_long_run<DT, OPT>(W, momentum, L, m, chunk, max_D, partial, lr, eps);
+    }
+  }
+}
+
 // One workgroup per long run: the four waves sum interleaved chunk partials
 // (chunk k goes to wave k % 4, always in increasing k), the four sums are added
 // in wave order, and the optimizer is applied by all 256 threads, 4 columns each.

@@ -60,6 +60,28 @@ tbe_status apply_go(void* W, float* momentum, const uint4* long_list, const uint
   return check_launch("long_apply");
 }
 
+template <int DT, int OPT, bool WEIGHTED>
+tbe_status fused_go(void* W, float* momentum, const float* psw, const float* grad_out, char* ws,
+                    const BwdLayout& L, int final_buf, const Config& cfg, const uint32_t* order,
+                    const tbe_tables* tb, float lr, float eps, hipStream_t s) {
+  using S = typename Fmt<DT>::S;
+  const int64_t maxb = static_cast<int64_t>(device_cu_count()) * 8;
+  const int64_t batches = (L.cap_chunk + kFusedBatch - 1) / kFusedBatch;
+  const int grid = static_cast<int>(hmax(1, hmin((batches + kWavesPerBlock - 1) / kWavesPerBlock, maxb)));
+  ProfScope ps("long_fused", s);
+  hipLaunchKernelGGL((long_fused_kernel<DT, OPT, WEIGHTED>), dim3(grid), dim3(kBlock), 0, s,
+                     static_cast<S*>(W), momentum, grad_out,
+                     reinterpret_cast<const uint32_t*>(ws + L.pay[final_buf]),
+                     WEIGHTED ? reinterpret_cast<const uint32_t*>(ws + L.bag_of) : nullptr, psw,
+                     reinterpret_cast<const uint4*>(ws + L.long_list),
+                     reinterpret_cast<const uint32_t*>(ws + L.long_table),
+                     reinterpret_cast<uint32_t*>(ws + L.long_count),
+                     reinterpret_cast<const uint2*>(ws + L.chunk_list), order,
+                     reinterpret_cast<const int32_t*>(ws + L.counters), tb->meta, tb->B, tb->out_width,
+                     cfg.chunk, tb->max_D, reinterpret_cast<float*>(ws + L.partial), lr, eps);
+  return check_launch("long_fused");
+}
+
 }  // namespace detail
 
 tbe_status launch_grad_accum(const tbe_tables* tb, const float* psw, const float* grad_out,
@@ -88,6 +110,15 @@ tbe_status launch_short_and_apply(const tbe_tables* tb, void* W, float* momentum
     if (st) return st;
   }
   if (L.cap_long == 0) return TBE_OK;
+  if (cfg.fused_long) {
+    const uint32_t* order = nullptr;
+    if (tbe_status st = launch_chunk_order(tb, psw, ws, L, final_buf, cfg, &order, s)) return st;
+    if (opt == kOptSGD)
+      return psw ? detail::fused_go<DT, kOptSGD, true>(W, momentum, psw, grad_out, ws, L, final_buf, cfg, order, tb, lr, eps, s)
+                 : detail::fused_go<DT, kOptSGD, false>(W, momentum, psw, grad_out, ws, L, final_buf, cfg, order, tb, lr, eps, s);
+    return psw ? detail::fused_go<DT, kOptAdagrad, true>(W, momentum, psw, grad_out, ws, L, final_buf, cfg, order, tb, lr, eps, s)
+               : detail::fused_go<DT, kOptAdagrad, false>(W, momentum, psw, grad_out, ws, L, final_buf, cfg, order, tb, lr, eps, s);
+  }
   if (tbe_status st = launch_grad_accum(tb, psw, grad_out, ws, L, final_buf, cfg, s)) return st;
   const uint4* long_list = reinterpret_cast<const uint4*>(ws + L.long_list);
   const uint32_t* long_table = reinterpret_cast<const uint32_t*>(ws + L.long_table);

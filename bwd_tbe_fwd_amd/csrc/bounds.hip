@@ -205,9 +205,9 @@ __global__ __launch_bounds__(kBlock) void bounds_indices(IT* __restrict__ idx, i
   }
 }
 
-template <typename IT, typename OT>
-tbe_status bounds_go(const tbe_tables* tb, void* indices, void* offsets, int64_t N, int64_t* counts,
-                     void* ws, hipStream_t s) {
+template <typename OT>
+tbe_status offsets_go(const tbe_tables* tb, void* offsets, int64_t N, int64_t* counts, void* ws,
+                      hipStream_t s) {
   const int64_t nb = static_cast<int64_t>(tb->T) * tb->B;
   int64_t* bmax = static_cast<int64_t*>(ws);
   int64_t* prefix = bmax + kBoundsBlocks;
@@ -219,23 +219,25 @@ tbe_status bounds_go(const tbe_tables* tb, void* indices, void* offsets, int64_t
     hipLaunchKernelGGL(bounds_init_kernel, dim3(1), dim3(64), 0, s, counts);
   }
   if (tbe_status st = check_launch("bounds_init")) return st;
-  {
-    ProfScope ps("bounds_offsets", s);
-    hipLaunchKernelGGL((bounds_offsets_reduce<OT>), dim3(nblk), dim3(kBlock), 0, s,
-                       static_cast<const OT*>(offsets), nb, N, seg, bmax);
-    hipLaunchKernelGGL(bounds_offsets_scan, dim3(1), dim3(kBlock), 0, s, bmax, prefix, nblk);
-    hipLaunchKernelGGL((bounds_offsets_apply<OT>), dim3(nblk), dim3(kBlock), 0, s,
-                       static_cast<OT*>(offsets), nb, N, seg, prefix, counts);
-  }
-  if (tbe_status st = check_launch("bounds_offsets")) return st;
-  if (N > 0) {
-    const int64_t want = (N + kBlock * 16 - 1) / (kBlock * 16);
-    const int grid = static_cast<int>(hmax(1, hmin(want, static_cast<int64_t>(device_cu_count()) * 8)));
-    ProfScope ps("bounds_indices", s);
-    hipLaunchKernelGGL((bounds_indices<IT, OT>), dim3(grid), dim3(kBlock), 0, s,
-                       static_cast<IT*>(indices), N, static_cast<const OT*>(offsets), tb->meta,
-                       tb->T, static_cast<int64_t>(tb->B), counts);
-  }
+  ProfScope ps("bounds_offsets", s);
+  hipLaunchKernelGGL((bounds_offsets_reduce<OT>), dim3(nblk), dim3(kBlock), 0, s,
+                     static_cast<const OT*>(offsets), nb, N, seg, bmax);
+  hipLaunchKernelGGL(bounds_offsets_scan, dim3(1), dim3(kBlock), 0, s, bmax, prefix, nblk);
+  hipLaunchKernelGGL((bounds_offsets_apply<OT>), dim3(nblk), dim3(kBlock), 0, s,
+                     static_cast<OT*>(offsets), nb, N, seg, prefix, counts);
+  return check_launch("bounds_offsets");
+}
+
+template <typename IT, typename OT>
+tbe_status indices_go(const tbe_tables* tb, void* indices, const void* offsets, int64_t N,
+                      int64_t* counts, hipStream_t s) {
+  if (N <= 0) return TBE_OK;
+  const int64_t want = (N + kBlock * 16 - 1) / (kBlock * 16);
+  const int grid = static_cast<int>(hmax(1, hmin(want, static_cast<int64_t>(device_cu_count()) * 8)));
+  ProfScope ps("bounds_indices", s);
+  hipLaunchKernelGGL((bounds_indices<IT, OT>), dim3(grid), dim3(kBlock), 0, s,
+                     static_cast<IT*>(indices), N, static_cast<const OT*>(offsets), tb->meta,
+                     tb->T, static_cast<int64_t>(tb->B), counts);
   return check_launch("bounds_indices");
 }
 
@@ -243,14 +245,26 @@ tbe_status bounds_go(const tbe_tables* tb, void* indices, void* offsets, int64_t
 
 size_t bounds_workspace(const tbe_tables*) { return 2 * kBoundsBlocks * sizeof(int64_t); }
 
+tbe_status launch_bounds_offsets(const tbe_tables* tb, void* offsets, int otype, int64_t N,
+                                 int64_t* counts, void* ws, hipStream_t s) {
+  if (otype == TBE_I32) return offsets_go<int32_t>(tb, offsets, N, counts, ws, s);
+  return offsets_go<int64_t>(tb, offsets, N, counts, ws, s);
+}
+
+tbe_status launch_bounds_indices(const tbe_tables* tb, void* indices, int itype, const void* offsets,
+                                 int otype, int64_t N, int64_t* counts, hipStream_t s) {
+  if (itype == TBE_I32) {
+    if (otype == TBE_I32) return indices_go<int32_t, int32_t>(tb, indices, offsets, N, counts, s);
+    return indices_go<int32_t, int64_t>(tb, indices, offsets, N, counts, s);
+  }
+  if (otype == TBE_I32) return indices_go<int64_t, int32_t>(tb, indices, offsets, N, counts, s);
+  return indices_go<int64_t, int64_t>(tb, indices, offsets, N, counts, s);
+}
+
 tbe_status launch_bounds(const tbe_tables* tb, void* indices, int itype, void* offsets, int otype,
                          int64_t N, int64_t* counts, void* ws, hipStream_t s) {
-  if (itype == TBE_I32) {
-    if (otype == TBE_I32) return bounds_go<int32_t, int32_t>(tb, indices, offsets, N, counts, ws, s);
-    return bounds_go<int32_t, int64_t>(tb, indices, offsets, N, counts, ws, s);
-  }
-  if (otype == TBE_I32) return bounds_go<int64_t, int32_t>(tb, indices, offsets, N, counts, ws, s);
-  return bounds_go<int64_t, int64_t>(tb, indices, offsets, N, counts, ws, s);
+  if (tbe_status st = launch_bounds_offsets(tb, offsets, otype, N, counts, ws, s)) return st;
+  return launch_bounds_indices(tb, indices, itype, offsets, otype, N, counts, s);
 }
 
 }  // namespace tbe

@@ -27,13 +27,14 @@ namespace {
 // Pools the lookups [s, e) of one bag into acc (this lane's VEC columns, row group
 // lane >> lg).  The bag's first 64 ids (and weights) arrive already loaded in
 // first_id / first_w: they were fetched while the previous bag's rows were in
-// flight.
-template <int DT, typename IT, bool PSW, int VEC, typename ACC, int UNROLL>
+// flight.  REPAIR (fused bounds check): an id outside [0, E) is read as row 0,
+// rewritten to 0 in place (once, on the first column block) and counted.
+template <int DT, typename IT, bool PSW, int VEC, typename ACC, int UNROLL, bool REPAIR>
 __device__ __forceinline__ void pool_bag(const typename Fmt<DT>::S* __restrict__ Wt, int64_t E,
-                                         int D, const IT* __restrict__ indices,
+                                         int D, IT* __restrict__ indices,
                                          const float* __restrict__ psw, int64_t s, int64_t e,
                                          int lg, int col, bool act, int64_t first_id, float first_w,
-                                         ACC (&acc)[VEC]) {
+                                         bool first_block, int64_t& fixed, ACC (&acc)[VEC]) {
   const int lane = lane_id();
   const int G = kWave >> lg;  // rows per wave instruction
   const int g = lane >> lg;   // this lane's row group
@@ -45,8 +46,17 @@ __device__ __forceinline__ void pool_bag(const typename Fmt<DT>::S* __restrict__
       r = lane < n ? static_cast<int64_t>(indices[j0 + lane]) : -1;
       if constexpr (PSW) myw = lane < n ? psw[j0 + lane] : 0.f;
     }
-    const int32_t myrow =
-        (lane < n && static_cast<uint64_t>(r) < static_cast<uint64_t>(E)) ? static_cast<int32_t>(r) : -1;
+    const bool bad = lane < n && static_cast<uint64_t>(r) >= static_cast<uint64_t>(E);
+    int32_t myrow = (lane < n && !bad) ? static_cast<int32_t>(r) : -1;
+    if constexpr (REPAIR) {
+      if (bad) {
+        myrow = 0;
+        if (first_block) {
+          indices[j0 + lane] = 0;
+          ++fixed;
+        }
+      }
+    }
     for (int q0 = 0; q0 < n; q0 += G * UNROLL) {
       RawVec<DT, VEC> raw[UNROLL];
       float wq[UNROLL];
@@ -72,18 +82,19 @@ __device__ __forceinline__ void pool_bag(const typename Fmt<DT>::S* __restrict__
   }
 }
 
-template <int DT, typename IT, typename OT, bool PSW, int VEC, typename ACC, int UNROLL>
+template <int DT, typename IT, typename OT, bool PSW, int VEC, typename ACC, int UNROLL, bool REPAIR>
 __global__ __launch_bounds__(kBlock) void fwd_gather_kernel(
-    const typename Fmt<DT>::S* __restrict__ W, const IT* __restrict__ indices,
+    const typename Fmt<DT>::S* __restrict__ W, IT* __restrict__ indices,
     const OT* __restrict__ offsets, const float* __restrict__ psw, float* __restrict__ out,
     const int64_t* __restrict__ meta, int32_t skip_t, int32_t n_tables, int32_t B,
-    int32_t out_width, int64_t N) {
+    int32_t out_width, int64_t N, int64_t* __restrict__ counts) {
   const int lane = lane_id();
   const int64_t wave = (static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x) >> 6;
   const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * kBlock) >> 6;
   const int64_t slots = static_cast<int64_t>(n_tables) * B;
   int cur_t = -1;
   TableMeta m{};
+  int64_t fixed = 0;
   for (int64_t base = wave * kWave; base < slots; base += nwaves * kWave) {
     // one bag per lane: its table, batch row and clamped [start, end)
     const int64_t slot = base + lane;
@@ -139,8 +150,9 @@ __global__ __launch_bounds__(kBlock) void fwd_gather_kernel(
         ACC acc[VEC];
 #pragma unroll
         for (int i = 0; i < VEC; ++i) acc[i] = 0;
-        pool_bag<DT, IT, PSW, VEC, ACC, UNROLL>(W + m.w_base, m.E, D, indices, psw, sk, ek, lg,
-                                                col, act, cur_id, cur_w, acc);
+        pool_bag<DT, IT, PSW, VEC, ACC, UNROLL, REPAIR>(W + m.w_base, m.E, D, indices, psw, sk, ek,
+                                                        lg, col, act, cur_id, cur_w, cb == 0, fixed,
+                                                        acc);
         for (int msk = lpr; msk < kWave; msk <<= 1) {
 #pragma unroll
           for (int i = 0; i < VEC; ++i) acc[i] += __shfl_xor(acc[i], msk);
@@ -155,6 +167,11 @@ __global__ __launch_bounds__(kBlock) void fwd_gather_kernel(
         }
       }
     }
+  }
+  if constexpr (REPAIR) {  // one atomic per wave
+    for (int msk = 1; msk < kWave; msk <<= 1) fixed += __shfl_xor(fixed, msk);
+    if (lane == 0 && fixed)
+      atomicAdd(reinterpret_cast<unsigned long long*>(counts), static_cast<unsigned long long>(fixed));
   }
 }
 
@@ -271,19 +288,21 @@ int grid_for(int64_t work_waves) {
 
 template <int DT, typename IT, typename OT, bool PSW, int VEC, typename ACC>
 tbe_status gather_go(const tbe_tables* tb, const void* W, const IndexArgs& ia, const float* psw,
-                     float* out, int skip, int nt, int unroll, hipStream_t s) {
+                     float* out, int skip, int nt, int unroll, int64_t* repair_counts, hipStream_t s) {
   const int64_t slots = static_cast<int64_t>(nt) * tb->B;
   const int grid = grid_for((slots + kWave - 1) / kWave);
   using S = typename Fmt<DT>::S;
   ProfScope ps("fwd_gather", s);
-#define TBE_FWD_LAUNCH(U)                                                                      \
-  hipLaunchKernelGGL((fwd_gather_kernel<DT, IT, OT, PSW, VEC, ACC, U>), dim3(grid), dim3(kBlock), \
-                     0, s, static_cast<const S*>(W), static_cast<const IT*>(ia.indices),        \
-                     static_cast<const OT*>(ia.offsets), psw, out, tb->meta, skip, nt, tb->B,      \
-                     tb->out_width, ia.N)
-  if (unroll <= 2) TBE_FWD_LAUNCH(2);
-  else if (unroll <= 4) TBE_FWD_LAUNCH(4);
-  else TBE_FWD_LAUNCH(8);
+#define TBE_FWD_LAUNCH(U, R)                                                                     \
+  hipLaunchKernelGGL((fwd_gather_kernel<DT, IT, OT, PSW, VEC, ACC, U, R>), dim3(grid), dim3(kBlock), \
+                     0, s, static_cast<const S*>(W),                                                \
+                     const_cast<IT*>(static_cast<const IT*>(ia.indices)),                           \
+                     static_cast<const OT*>(ia.offsets), psw, out, tb->meta, skip, nt, tb->B,         \
+                     tb->out_width, ia.N, repair_counts)
+  if (repair_counts) TBE_FWD_LAUNCH(8, true);
+  else if (unroll <= 2) TBE_FWD_LAUNCH(2, false);
+  else if (unroll <= 4) TBE_FWD_LAUNCH(4, false);
+  else TBE_FWD_LAUNCH(8, false);
 #undef TBE_FWD_LAUNCH
   return check_launch("fwd_gather");
 }
@@ -291,32 +310,32 @@ tbe_status gather_go(const tbe_tables* tb, const void* W, const IndexArgs& ia, c
 template <int DT, typename IT, typename OT>
 tbe_status gather_dispatch_psw(const tbe_tables* tb, const void* W, const IndexArgs& ia,
                                const float* psw, float* out, int skip, int nt, int unroll,
-                               hipStream_t s) {
+                               int64_t* rc, hipStream_t s) {
   if constexpr (DT == 0) {
-    if (psw) return gather_go<DT, IT, OT, true, 4, double>(tb, W, ia, psw, out, skip, nt, unroll, s);
-    return gather_go<DT, IT, OT, false, 4, double>(tb, W, ia, psw, out, skip, nt, unroll, s);
+    if (psw) return gather_go<DT, IT, OT, true, 4, double>(tb, W, ia, psw, out, skip, nt, unroll, rc, s);
+    return gather_go<DT, IT, OT, false, 4, double>(tb, W, ia, psw, out, skip, nt, unroll, rc, s);
   } else {
     if (tb->all_D_mult8) {
-      if (psw) return gather_go<DT, IT, OT, true, 8, float>(tb, W, ia, psw, out, skip, nt, unroll, s);
-      return gather_go<DT, IT, OT, false, 8, float>(tb, W, ia, psw, out, skip, nt, unroll, s);
+      if (psw) return gather_go<DT, IT, OT, true, 8, float>(tb, W, ia, psw, out, skip, nt, unroll, rc, s);
+      return gather_go<DT, IT, OT, false, 8, float>(tb, W, ia, psw, out, skip, nt, unroll, rc, s);
     }
-    if (psw) return gather_go<DT, IT, OT, true, 4, float>(tb, W, ia, psw, out, skip, nt, unroll, s);
-    return gather_go<DT, IT, OT, false, 4, float>(tb, W, ia, psw, out, skip, nt, unroll, s);
+    if (psw) return gather_go<DT, IT, OT, true, 4, float>(tb, W, ia, psw, out, skip, nt, unroll, rc, s);
+    return gather_go<DT, IT, OT, false, 4, float>(tb, W, ia, psw, out, skip, nt, unroll, rc, s);
   }
 }
 
 template <int DT>
 tbe_status gather_dispatch_idx(const tbe_tables* tb, const void* W, const IndexArgs& ia,
                                const float* psw, float* out, int skip, int nt, int unroll,
-                               hipStream_t s) {
+                               int64_t* rc, hipStream_t s) {
   if (ia.itype == TBE_I32) {
     if (ia.otype == TBE_I32)
-      return gather_dispatch_psw<DT, int32_t, int32_t>(tb, W, ia, psw, out, skip, nt, unroll, s);
-    return gather_dispatch_psw<DT, int32_t, int64_t>(tb, W, ia, psw, out, skip, nt, unroll, s);
+      return gather_dispatch_psw<DT, int32_t, int32_t>(tb, W, ia, psw, out, skip, nt, unroll, rc, s);
+    return gather_dispatch_psw<DT, int32_t, int64_t>(tb, W, ia, psw, out, skip, nt, unroll, rc, s);
   }
   if (ia.otype == TBE_I32)
-    return gather_dispatch_psw<DT, int64_t, int32_t>(tb, W, ia, psw, out, skip, nt, unroll, s);
-  return gather_dispatch_psw<DT, int64_t, int64_t>(tb, W, ia, psw, out, skip, nt, unroll, s);
+    return gather_dispatch_psw<DT, int64_t, int32_t>(tb, W, ia, psw, out, skip, nt, unroll, rc, s);
+  return gather_dispatch_psw<DT, int64_t, int64_t>(tb, W, ia, psw, out, skip, nt, unroll, rc, s);
 }
 
 template <typename IT, typename OT>
@@ -337,13 +356,13 @@ tbe_status hist_go(const tbe_tables* tb, const void* W, const IndexArgs& ia, flo
 
 tbe_status launch_forward_gather(const tbe_tables* tb, const void* W, const IndexArgs& ia,
                                  const float* psw, float* out, int skip_table,
-                                 int unroll, hipStream_t s) {
+                                 int unroll, int64_t* rc, hipStream_t s) {
   const int n_tables = skip_table >= 0 ? tb->T - 1 : tb->T;
   if (n_tables <= 0 || tb->B == 0) return TBE_OK;
   switch (tb->w_dtype) {
-    case TBE_F32: return gather_dispatch_idx<0>(tb, W, ia, psw, out, skip_table, n_tables, unroll, s);
-    case TBE_F16: return gather_dispatch_idx<1>(tb, W, ia, psw, out, skip_table, n_tables, unroll, s);
-    default: return gather_dispatch_idx<2>(tb, W, ia, psw, out, skip_table, n_tables, unroll, s);
+    case TBE_F32: return gather_dispatch_idx<0>(tb, W, ia, psw, out, skip_table, n_tables, unroll, rc, s);
+    case TBE_F16: return gather_dispatch_idx<1>(tb, W, ia, psw, out, skip_table, n_tables, unroll, rc, s);
+    default: return gather_dispatch_idx<2>(tb, W, ia, psw, out, skip_table, n_tables, unroll, rc, s);
   }
 }
 

@@ -40,7 +40,7 @@ constexpr int kRadixItems = 16;                       // keys per thread per til
 constexpr int kRadixTile = kBlock * kRadixItems;      // 4096 keys
 
 struct Config {
-  int threshold, chunk, hist_enable, fwd_unroll, bwd_unroll, sort_blocks, bag_windows;
+  int threshold, chunk, hist_enable, fwd_unroll, bwd_unroll, sort_blocks, bag_windows, fused_long;
 };
 Config resolve_config(const tbe_config* c);
 
@@ -48,7 +48,7 @@ Config resolve_config(const tbe_config* c);
 struct BwdLayout {
   int64_t N;
   size_t keys[2], pay[2], bag_of, run_key, run_start;
-  size_t long_list, long_table, chunk_list, partial, short_list[TBE_NUM_BUCKETS];
+  size_t long_list, long_table, long_count, chunk_list, partial, short_list[TBE_NUM_BUCKETS];
   size_t sort_hist, seg_cnt, cls_cnt, counters, total;
   size_t chunk_unit, chunk_order, unit_cnt;  // long-run chunk ordering by (table, bag window)
   int nwin, win_size, units;
@@ -80,17 +80,25 @@ tbe_status launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
 
 tbe_status launch_forward_gather(const tbe_tables* tb, const void* W, const IndexArgs& ia,
                                  const float* psw, float* out, int skip_table, int unroll,
-                                 hipStream_t s);
+                                 int64_t* repair_counts, hipStream_t s);
 tbe_status launch_forward_hist(const tbe_tables* tb, const void* W, const IndexArgs& ia,
                                float* out, hipStream_t s);
 
 tbe_status launch_bounds(const tbe_tables* tb, void* indices, int itype, void* offsets, int otype,
                          int64_t N, int64_t* counts, void* ws, hipStream_t s);
 size_t bounds_workspace(const tbe_tables* tb);
+tbe_status launch_bounds_offsets(const tbe_tables* tb, void* offsets, int otype, int64_t N,
+                                 int64_t* counts, void* ws, hipStream_t s);
+tbe_status launch_bounds_indices(const tbe_tables* tb, void* indices, int itype, const void* offsets,
+                                 int otype, int64_t N, int64_t* counts, hipStream_t s);
 
 tbe_status launch_transpose(const tbe_tables* tb, const IndexArgs& ia, int weighted,
                             char* ws, const BwdLayout& L, const Config& cfg, int* final_buf,
                             hipStream_t s);
+
+// groups long-run chunks by (table, bag window); *order = NULL when not grouped
+tbe_status launch_chunk_order(const tbe_tables* tb, const float* psw, char* ws, const BwdLayout& L,
+                              int final_buf, const Config& cfg, const uint32_t** order, hipStream_t s);
 
 tbe_status launch_backward_update(const tbe_tables* tb, void* W, float* momentum, int opt,
                                   const float* psw, const float* grad_out, float lr, float eps,

@@ -521,8 +521,8 @@ __global__ __launch_bounds__(kBlock) void classify_write(
     const uint32_t* __restrict__ run_key, const uint32_t* __restrict__ run_start,
     const int32_t* __restrict__ counters, const int64_t* __restrict__ meta, int T,
     uint32_t total_rows, int threshold, int chunk, const uint32_t* __restrict__ cls_cnt,
-    uint4* __restrict__ long_list, uint32_t* __restrict__ long_table, uint2* __restrict__ chunk_list,
-    int64_t cap_long, int64_t cap_chunk, ShortLists lists) {
+    uint4* __restrict__ long_list, uint32_t* __restrict__ long_table, uint32_t* __restrict__ long_count,
+    uint2* __restrict__ chunk_list, int64_t cap_long, int64_t cap_chunk, ShortLists lists) {
   __shared__ TableLds s_tab;
   __shared__ uint32_t s_base[kClsRows];
   __shared__ uint32_t s_wcnt[kWavesPerBlock][kCats];
@@ -560,6 +560,7 @@ __global__ __launch_bounds__(kBlock) void classify_write(
         if (slot < cap_long) {
           long_list[slot] = make_uint4(key, start, len, static_cast<uint32_t>(cb));
           long_table[slot] = static_cast<uint32_t>(t);
+          long_count[slot] = nch;  // countdown of the fused long-run kernel
           for (uint32_t c = 0; c < nch; ++c)
             if (cb + c < cap_chunk) chunk_list[cb + c] = make_uint2(static_cast<uint32_t>(slot), c);
         }
@@ -685,6 +686,7 @@ tbe_status launch_transpose(const tbe_tables* tb, const IndexArgs& ia, int weigh
     hipLaunchKernelGGL(classify_write, dim3(L.cls_blocks), dim3(kBlock), 0, s, run_key, run_start,
                        counters, tb->meta, tb->T, total_rows, cfg.threshold, cfg.chunk, cls_cnt,
                        reinterpret_cast<uint4*>(ws + L.long_list), reinterpret_cast<uint32_t*>(ws + L.long_table),
+                       reinterpret_cast<uint32_t*>(ws + L.long_count),
                        reinterpret_cast<uint2*>(ws + L.chunk_list), L.cap_long, L.cap_chunk, lists);
   }
   return check_launch("classify");

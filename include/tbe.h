@@ -106,6 +106,9 @@ typedef struct {
   int32_t bag_windows;     /* long-run chunks are processed grouped by (table, bag window of their
                               first lookup), B / bag_windows bags per window, so that chunks that
                               read the same gradient rows run together (default 32; <= 1: off) */
+  int32_t fused_long;      /* 1: long runs in one launch - each chunk writes its partial, a device-scope
+                              fence, then a per-run countdown; the last chunk applies the optimizer
+                              (blog section 4, problem 5).  0: chunk kernel + apply kernel (default) */
 } tbe_config;
 
 /* Device-side view of the transpose, for inspection by tests (tbe_transpose). */
@@ -181,6 +184,22 @@ tbe_status tbe_forward(const tbe_tables* tables, const void* weights, const void
                        int32_t index_type, const void* offsets, int32_t offset_type,
                        int64_t num_indices, const float* per_sample_weights, float* out,
                        const tbe_config* config, tbe_stream_t stream);
+
+/*
+ * Forward with the bounds check fused into the gather (blog section 2,
+ * "Bounds checking": with the fused option the eligible kernel validates and
+ * repairs ids while it looks them up; offsets keep their own small repair
+ * step).  Same results as tbe_bounds_check followed by tbe_forward: offsets
+ * and indices repaired in place by the same rules, error_counts [device, 2 x
+ * int64] overwritten with {indices repaired, offsets changed}, out as in
+ * tbe_forward.  When the histogram path is used, its ids are validated by the
+ * standalone step instead.  workspace: tbe_bounds_check_workspace_bytes().
+ */
+tbe_status tbe_forward_repair(const tbe_tables* tables, const void* weights, void* indices,
+                              int32_t index_type, void* offsets, int32_t offset_type,
+                              int64_t num_indices, const float* per_sample_weights, float* out,
+                              int64_t* error_counts, void* workspace, size_t workspace_bytes,
+                              const tbe_config* config, tbe_stream_t stream);
 
 /*
  * Bytes of workspace the backward (and tbe_transpose) needs for num_indices

@@ -131,3 +131,24 @@ def test_backward_out_of_range_ids_dropped():
     r = oracle.backward(a["T"], a["B"], a["E"], a["D"], oracle.F32, a["W"], ids, a["off"], keep,
                         a["grad"], oracle.SGD, oracle.f32_literal(0.01))
     check_weights(W, r, torch.float32, 0.01 * r["g_abs"], "dropped ids")
+
+
+@pytest.mark.parametrize("optimizer", ["sgd", "rowwise_adagrad"])
+@pytest.mark.parametrize("w_dtype", [torch.float32, torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("threshold,chunk,windows", [(256, 256, 32), (8, 8, 1), (4, 2, 32), (1, 1, 0)])
+def test_fused_long_runs(optimizer, w_dtype, threshold, chunk, windows):
+    """Long runs in one launch (fence, then countdown; the last chunk applies the update):
+    same results as the oracle, and bitwise repeatable."""
+    spec = small_spec("skewed").replace(optimizer=optimizer, w_dtype=w_dtype)
+    bt = ti.make_batch(spec, 41)
+    cfg = tbe.make_config(long_threshold=threshold, chunk=chunk, fused_long=1, bag_windows=windows)
+    _, W1, m1, _ = run_and_check(bt, cfg, what=f"fused {optimizer} {w_dtype} t={threshold} c={chunk}")
+    _, W2, m2, _ = run_and_check(bt, cfg, what="fused again")
+    assert torch.equal(W1.cpu().view(torch.uint8), W2.cpu().view(torch.uint8))
+
+
+@pytest.mark.parametrize("weighted", [False, True])
+def test_fused_long_runs_mixed_D(weighted):
+    spec = mixed_spec(torch.bfloat16, torch.int64, torch.int64, weighted).replace(optimizer="rowwise_adagrad")
+    bt = ti.make_batch(spec, 43)
+    run_and_check(bt, tbe.make_config(long_threshold=16, chunk=8, fused_long=1), what=f"fused mixed {weighted}")

@@ -69,3 +69,50 @@ def test_bounds_valid_input_unchanged():
     assert cnt.tolist() == [0, 0]
     assert np.array_equal(got_idx, bt.indices.numpy())
     assert np.array_equal(got_off, bt.offsets.numpy())
+
+
+def _faulty_batch(spec, seed):
+    bt = ti.make_batch(spec, seed, with_grad=False)
+    rng = np.random.default_rng(seed)
+    idx = bt.indices.numpy().astype(np.int64)
+    off = bt.offsets.numpy().astype(np.int64)
+    N = idx.size
+    bad = rng.random(N) < 0.05
+    idx[bad] = rng.choice([-1, -77, 10 ** 6, 2 ** 31 - 1], size=int(bad.sum()))
+    ob = rng.random(off.size) < 0.01
+    off[ob] = rng.integers(-5, N + 50, size=int(ob.sum()))
+    off[-1] = N - 3
+    return bt, idx, off
+
+
+@pytest.mark.parametrize("weighted", [False, True])
+@pytest.mark.parametrize("hist", [False, True])
+@pytest.mark.parametrize("itype", [torch.int32, torch.int64])
+def test_fused_bounds_forward_equals_check_then_forward(weighted, hist, itype):
+    """tbe_forward_repair == tbe_bounds_check + tbe_forward: repaired arrays and counts exact,
+    pooled output within the forward tolerance of the oracle on the repaired input."""
+    from gpu_util import check_forward
+    tables = (ti.TableSpec(64, 128, ("poisson", 70.0, None, None)),
+              ti.TableSpec(500, 32, ("poisson", 5.0, None, None), ("zipf", 1.1, None)),
+              ti.TableSpec(3000, 128, ("poisson", 12.0, None, None)))
+    spec = ti.BatchSpec("fused bounds", tables, B=1111, w_dtype=torch.float16, w_range=0.05,
+                        weighted=weighted, itype=itype, pooling_hint=(70, 5, 12) if hist else None)
+    bt, idx, off = _faulty_batch(spec, 3)
+    exp_idx, exp_off, exp_cnt = oracle.bounds_check(spec.T, spec.B, bt.E, idx, off)
+    t = tbe.Tables(bt.E, bt.D, bt.B, bt.w_dtype, device="cuda", pooling_hint=spec.pooling_hint)
+    assert (t.c.hist_table == 0) == hist  # used only without per-sample weights
+    W = bt.weights.cuda()
+    d_idx = torch.as_tensor(idx).to(itype).cuda()
+    d_off = torch.as_tensor(off).cuda()
+    psw = None if bt.psw is None else bt.psw.cuda()
+    out = torch.full((bt.B, sum(bt.D)), float("nan"), device="cuda")
+    counts = torch.full((2,), -1, dtype=torch.int64, device="cuda")
+    ws = tbe.workspace(tbe.tbe_bounds_check_workspace_bytes(t))
+    tbe.tbe_forward_repair(t, W, d_idx, d_off, psw, out, counts, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(d_off.cpu().numpy(), exp_off)
+    assert np.array_equal(d_idx.cpu().numpy().astype(np.int64), exp_idx)
+    assert counts.cpu().tolist() == exp_cnt.tolist()
+    ref, ref_abs = oracle.forward(spec.T, spec.B, bt.E, bt.D, bt.weights.double().numpy(), exp_idx,
+                                  exp_off, None if bt.psw is None else bt.psw.double().numpy())
+    check_forward(out.cpu().numpy(), ref, ref_abs, False, "fused bounds forward")
