@@ -173,6 +173,10 @@ BwdLayout bwd_layout(const tbe_tables* tb, int64_t N, int weighted, const Config
     L.chunk_order = c.take(L.cap_chunk * 4);
     L.unit_cnt = c.take(static_cast<size_t>(L.units) * 4);
   }
+  if (tb->hist_table >= 0 && !weighted) {
+    L.hist_partial = c.take(static_cast<size_t>(kHistBwdBlocks) * 64 * 128 * 4);
+    L.hist_count = c.take(static_cast<size_t>(kHistBwdBlocks) * 64 * 4);
+  }
   L.counters = c.take(kNumCounters * 4);
   L.total = c.off;
   // keys are in [0, total_rows]; total_rows itself marks an id outside its table
@@ -423,7 +427,12 @@ static tbe_status backward_common(const tbe_tables* tables, void* weights, float
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   int final_buf = 0;
-  if (tbe_status st = launch_transpose(tables, ia, psw ? 1 : 0, ws, L, cfg, &final_buf, s)) return st;
+  // the small table's rows are updated from per-bag counts x gradient (MFMA) instead of runs
+  const int hist = (cfg.hist_enable && !psw && tables->hist_table >= 0) ? tables->hist_table : -1;
+  if (tbe_status st = launch_transpose(tables, ia, psw ? 1 : 0, ws, L, cfg, hist, &final_buf, s)) return st;
+  if (hist >= 0)
+    if (tbe_status st = launch_hist_backward(tables, weights, momentum, opt, ia, grad_out, lr, eps, ws, L, s))
+      return st;
   return launch_backward_update(tables, weights, momentum, opt, psw, grad_out, lr, eps, ws, L, final_buf, cfg, s);
 }
 
@@ -465,7 +474,7 @@ tbe_status tbe_transpose(const tbe_tables* tables, const void* indices, int32_t 
   IndexArgs ia{indices, index_type, offsets, offset_type, num_indices};
   char* ws = static_cast<char*>(workspace);
   int final_buf = 0;
-  tbe_status st = launch_transpose(tables, ia, weighted ? 1 : 0, ws, L, cfg, &final_buf,
+  tbe_status st = launch_transpose(tables, ia, weighted ? 1 : 0, ws, L, cfg, -1, &final_buf,
                                    static_cast<hipStream_t>(stream));
   std::memset(view, 0, sizeof(*view));
   view->sorted_keys = reinterpret_cast<const uint32_t*>(ws + L.keys[final_buf]);

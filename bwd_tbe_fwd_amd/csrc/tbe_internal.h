@@ -51,6 +51,7 @@ struct BwdLayout {
   size_t long_list, long_table, long_count, chunk_list, partial, short_list[TBE_NUM_BUCKETS];
   size_t sort_hist, seg_cnt, cls_cnt, counters, total;
   size_t chunk_unit, chunk_order, unit_cnt;  // long-run chunk ordering by (table, bag window)
+  size_t hist_partial, hist_count;             // histogram backward: per-block partial sums
   int nwin, win_size, units;
   int64_t cap_long, cap_chunk, cap_short[TBE_NUM_BUCKETS];
   int64_t seg;        // keys per sort / RLE block (multiple of kRadixTile)
@@ -92,9 +93,17 @@ tbe_status launch_bounds_offsets(const tbe_tables* tb, void* offsets, int otype,
 tbe_status launch_bounds_indices(const tbe_tables* tb, void* indices, int itype, const void* offsets,
                                  int otype, int64_t N, int64_t* counts, hipStream_t s);
 
+// skip_table >= 0: that table's lookups are left out of the runs (its rows are
+// updated by the histogram backward)
 tbe_status launch_transpose(const tbe_tables* tb, const IndexArgs& ia, int weighted,
-                            char* ws, const BwdLayout& L, const Config& cfg, int* final_buf,
-                            hipStream_t s);
+                            char* ws, const BwdLayout& L, const Config& cfg, int skip_table,
+                            int* final_buf, hipStream_t s);
+
+// histogram backward of the small table (counts x gradient on MFMA, then the optimizer)
+constexpr int kHistBwdBlocks = 512;  // max partials (workgroups) of the histogram backward
+tbe_status launch_hist_backward(const tbe_tables* tb, void* W, float* momentum, int opt,
+                                const IndexArgs& ia, const float* grad_out, float lr, float eps,
+                                char* ws, const BwdLayout& L, hipStream_t s);
 
 // groups long-run chunks by (table, bag window); *order = NULL when not grouped
 tbe_status launch_chunk_order(const tbe_tables* tb, const float* psw, char* ws, const BwdLayout& L,

@@ -86,7 +86,7 @@ __device__ __forceinline__ uint64_t match_digit(uint32_t d, int bits, uint64_t v
 template <typename IT, typename OT, bool WEIGHTED>
 __global__ __launch_bounds__(kBlock) void linearize_kernel(
     const IT* __restrict__ indices, const OT* __restrict__ offsets, const int64_t* __restrict__ meta,
-    int32_t B, int64_t nbags, int32_t N, uint32_t sentinel, uint32_t* __restrict__ keys,
+    int32_t B, int64_t nbags, int32_t N, uint32_t sentinel, int skip_t, uint32_t* __restrict__ keys,
     uint32_t* __restrict__ pay, uint32_t* __restrict__ bag_of) {
   const int lane = lane_id();
   const int64_t wave = (static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x) >> 6;
@@ -102,7 +102,7 @@ __global__ __launch_bounds__(kBlock) void linearize_kernel(
                                    static_cast<int64_t>(N)));
       const int t = static_cast<int>(bag / B);
       rb = meta[4 * t];
-      E = meta[4 * (t + 1)] - rb;
+      E = t == skip_t ? 0 : meta[4 * (t + 1)] - rb;  // skip_t's lookups are left out
     }
     // monotone end offsets across the 64 lanes (inclusive running max)
     for (int d = 1; d < kWave; d <<= 1) {
@@ -586,7 +586,7 @@ __global__ void fill_i32_kernel(int32_t* p, int32_t v, int64_t n) {
 
 template <typename IT, typename OT>
 tbe_status linearize_go(const tbe_tables* tb, const IndexArgs& ia, int weighted, uint32_t* keys,
-                        uint32_t* pay, uint32_t* bag_of, hipStream_t s) {
+                        uint32_t* pay, uint32_t* bag_of, int skip_t, hipStream_t s) {
   const int64_t nbags = static_cast<int64_t>(tb->T) * tb->B;
   const int64_t groups = (nbags + kWave - 1) / kWave;
   const int64_t cap = static_cast<int64_t>(device_cu_count()) * 8 * kWavesPerBlock;
@@ -596,11 +596,11 @@ tbe_status linearize_go(const tbe_tables* tb, const IndexArgs& ia, int weighted,
   if (weighted)
     hipLaunchKernelGGL((linearize_kernel<IT, OT, true>), dim3(grid), dim3(kBlock), 0, s,
                        static_cast<const IT*>(ia.indices), static_cast<const OT*>(ia.offsets), tb->meta,
-                       tb->B, nbags, static_cast<int32_t>(ia.N), sentinel, keys, pay, bag_of);
+                       tb->B, nbags, static_cast<int32_t>(ia.N), sentinel, skip_t, keys, pay, bag_of);
   else
     hipLaunchKernelGGL((linearize_kernel<IT, OT, false>), dim3(grid), dim3(kBlock), 0, s,
                        static_cast<const IT*>(ia.indices), static_cast<const OT*>(ia.offsets), tb->meta,
-                       tb->B, nbags, static_cast<int32_t>(ia.N), sentinel, keys, pay, bag_of);
+                       tb->B, nbags, static_cast<int32_t>(ia.N), sentinel, skip_t, keys, pay, bag_of);
   return check_launch("linearize");
 }
 
@@ -614,7 +614,8 @@ tbe_status launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s) {
 }
 
 tbe_status launch_transpose(const tbe_tables* tb, const IndexArgs& ia, int weighted, char* ws,
-                            const BwdLayout& L, const Config& cfg, int* final_buf, hipStream_t s) {
+                            const BwdLayout& L, const Config& cfg, int skip_table, int* final_buf,
+                            hipStream_t s) {
   int32_t* counters = reinterpret_cast<int32_t*>(ws + L.counters);
   if (tbe_status st = launch_fill_i32(counters, 0, kNumCounters, s)) return st;
   const int64_t N = L.N;
@@ -628,11 +629,11 @@ tbe_status launch_transpose(const tbe_tables* tb, const IndexArgs& ia, int weigh
   uint32_t* bag_of = weighted ? reinterpret_cast<uint32_t*>(ws + L.bag_of) : nullptr;
   tbe_status st;
   if (ia.itype == TBE_I32)
-    st = ia.otype == TBE_I32 ? linearize_go<int32_t, int32_t>(tb, ia, weighted, keys[0], pay[0], bag_of, s)
-                             : linearize_go<int32_t, int64_t>(tb, ia, weighted, keys[0], pay[0], bag_of, s);
+    st = ia.otype == TBE_I32 ? linearize_go<int32_t, int32_t>(tb, ia, weighted, keys[0], pay[0], bag_of, skip_table, s)
+                             : linearize_go<int32_t, int64_t>(tb, ia, weighted, keys[0], pay[0], bag_of, skip_table, s);
   else
-    st = ia.otype == TBE_I32 ? linearize_go<int64_t, int32_t>(tb, ia, weighted, keys[0], pay[0], bag_of, s)
-                             : linearize_go<int64_t, int64_t>(tb, ia, weighted, keys[0], pay[0], bag_of, s);
+    st = ia.otype == TBE_I32 ? linearize_go<int64_t, int32_t>(tb, ia, weighted, keys[0], pay[0], bag_of, skip_table, s)
+                             : linearize_go<int64_t, int64_t>(tb, ia, weighted, keys[0], pay[0], bag_of, skip_table, s);
   if (st) return st;
   uint32_t* hist = reinterpret_cast<uint32_t*>(ws + L.sort_hist);
   uint32_t* tot = hist + static_cast<int64_t>(kRadixDigits) * L.nblocks;

@@ -152,3 +152,110 @@ def test_fused_long_runs_mixed_D(weighted):
     spec = mixed_spec(torch.bfloat16, torch.int64, torch.int64, weighted).replace(optimizer="rowwise_adagrad")
     bt = ti.make_batch(spec, 43)
     run_and_check(bt, tbe.make_config(long_threshold=16, chunk=8, fused_long=1), what=f"fused mixed {weighted}")
+
+
+def _hist_spec(E=64, D=128, L=("fixed", 128), B=517, optimizer="rowwise_adagrad", weighted=False,
+               itype=torch.int64, otype=torch.int64):
+    """Histogram-eligible table 0 (E <= 64, 64 <= D <= 128, fp16, long bags) plus two generic
+    companions, one of them hit often enough to form long runs."""
+    tables = (ti.TableSpec(E, D, L),
+              ti.TableSpec(900, 64, ("poisson", 6.0, None, None), ("zipf", 1.1, None)),
+              ti.TableSpec(5000, 128, ("poisson", 4.0, None, None)))
+    return ti.BatchSpec(f"hist bwd E={E} D={D} L={L} B={B}", tables, B=B, w_dtype=torch.float16,
+                        w_range=0.05, optimizer=optimizer, weighted=weighted, itype=itype, otype=otype,
+                        pooling_hint=(128, 6, 4))
+
+
+@pytest.mark.parametrize("optimizer", ["sgd", "rowwise_adagrad"])
+@pytest.mark.parametrize("E,D,L,B", [(64, 128, ("fixed", 128), 517),
+                                     (40, 80, ("poisson", 100.0, None, None), 333),   # ragged rows, cols
+                                     (64, 64, ("poisson", 300.0, None, None), 130),   # bags > 256
+                                     (17, 96, ("fixed", 64), 10),                     # one partial step
+                                     (64, 128, ("fixed", 70), 4099)])                 # many steps
+def test_hist_backward_matches_oracle(optimizer, E, D, L, B):
+    """Counts x gradient on MFMA for the small table, generic runs for the rest: the updated
+    weights and Adagrad state equal the oracle's within the stated bounds."""
+    bt = ti.make_batch(_hist_spec(E, D, L, B, optimizer), 51)
+    db, W, mom, r = run_and_check(bt, what=f"hist {optimizer} E={E} D={D} B={B}")
+    assert db.tables.c.hist_table == 0
+
+
+@pytest.mark.parametrize("itype,otype", [(torch.int32, torch.int32), (torch.int64, torch.int32)])
+def test_hist_backward_index_types(itype, otype):
+    bt = ti.make_batch(_hist_spec(B=700, itype=itype, otype=otype), 53)
+    run_and_check(bt, what=f"hist {itype} {otype}")
+
+
+def test_hist_backward_exact_with_integer_gradients():
+    """Integer gradients in {-1, 0, 1}, zero fp16 weights, SGD with lr = -1: every sum is an
+    integer below 2^11, so the histogram path, the generic run path and the oracle agree bit
+    for bit."""
+    spec = _hist_spec(B=300, optimizer="sgd", L=("poisson", 90.0, None, None))
+    bt = ti.make_batch(spec, 57)
+    g = torch.Generator().manual_seed(5)
+    bt.grad_out = torch.randint(-1, 2, bt.grad_out.shape, generator=g).float()
+    bt.weights = torch.zeros_like(bt.weights)
+    outs = []
+    for hist in (1, 0):
+        db = DevBatch(bt)
+        W, _ = db.backward(tbe.make_config(hist_enable=hist), lr=-1.0)
+        outs.append(W.cpu())
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    r = oracle_backward(bt, lr=-1.0)
+    E0, D0 = bt.E[0], bt.D[0]
+    assert np.array_equal(outs[0][:E0 * D0].double().numpy(), r["g"][:E0 * D0])
+    assert np.abs(r["g"][:E0 * D0]).max() > 8  # not trivially zero
+
+
+def test_hist_backward_deterministic_and_untouched_rows():
+    spec = _hist_spec(E=64, D=128, L=("fixed", 1), B=40)   # 40 lookups over 64 rows: some untouched
+    bt = ti.make_batch(spec, 59)
+    outs = []
+    for _ in range(2):
+        db = DevBatch(bt)
+        W0, m0 = db.W.clone(), db.mom.clone()
+        W, mom = db.backward()
+        outs.append((W.cpu(), mom.cpu()))
+    assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16))
+    assert torch.equal(outs[0][1], outs[1][1])
+    ids = bt.indices[bt.offsets[0]:bt.offsets[bt.B]].numpy().astype(np.int64)
+    touched = np.zeros(bt.E[0], dtype=bool)
+    touched[ids] = True
+    assert 0 < touched.sum() < bt.E[0]
+    Wt, W0t = outs[0][0][:bt.E[0] * 128].view(-1, 128), W0.cpu()[:bt.E[0] * 128].view(-1, 128)
+    t = torch.from_numpy(touched)
+    assert torch.equal(Wt[~t].view(torch.int16), W0t[~t].view(torch.int16))
+    assert torch.equal(outs[0][1][:bt.E[0]][~t], m0.cpu()[:bt.E[0]][~t])
+    assert (outs[0][1][:bt.E[0]][t] > m0.cpu()[:bt.E[0]][t]).all()
+    run_and_check(bt, what="hist sparse")
+
+
+def test_hist_backward_out_of_range_ids_dropped():
+    spec = _hist_spec(B=200, optimizer="sgd")
+    bt = ti.make_batch(spec, 61)
+    idx = bt.indices.clone()
+    bad = torch.zeros(idx.numel(), dtype=torch.bool)
+    bad[::5] = True
+    # one past the last row of the lookup's table, or negative
+    t_of = torch.zeros(idx.numel(), dtype=torch.int64)
+    for t in range(1, bt.T):
+        t_of[int(bt.offsets[t * bt.B]):] = t
+    past = torch.tensor(bt.E)[t_of]
+    idx[bad] = torch.where(torch.arange(idx.numel())[bad] % 2 == 0, torch.tensor(-2), past[bad]).to(idx.dtype)
+    bt.indices = idx
+    db = DevBatch(bt)
+    W, _ = db.backward()
+    a = host_arrays(bt)
+    keep = (~bad).double().numpy()
+    ids = np.where(bad.numpy(), 0, a["idx"])
+    r = oracle.backward(a["T"], a["B"], a["E"], a["D"], oracle.F16, a["W"], ids, a["off"], keep,
+                        a["grad"], oracle.SGD, oracle.f32_literal(spec.lr))
+    lr32 = oracle.f32_literal(spec.lr)
+    check_weights(W, r, torch.float16, step_bound(r, bt.E, bt.D, lr32, 0.0, False), "hist bad ids")
+
+
+def test_hist_backward_not_used_with_per_sample_weights():
+    """With per-sample weights the small table goes through the generic runs (weighted counts
+    are not integers); results still match the oracle."""
+    bt = ti.make_batch(_hist_spec(B=300, weighted=True), 67)
+    run_and_check(bt, what="hist table weighted")
