@@ -264,7 +264,7 @@ void tbe_config_default(tbe_config* cfg) {
   cfg->fwd_unroll = 8;
   cfg->bwd_unroll = 2;
   cfg->sort_blocks = 0;
-  cfg->bag_windows = 32;
+  cfg->bag_windows = 1;
   cfg->fused_long = 0;
 }
 

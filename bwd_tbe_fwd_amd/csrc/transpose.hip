@@ -83,26 +83,59 @@ __device__ __forceinline__ uint64_t match_digit(uint32_t d, int bits, uint64_t v
 // ---------------------------------------------------------------------------
 // linearize
 // ---------------------------------------------------------------------------
+// One wave takes 64 consecutive bags; lane l finds, for each lookup position p
+// of the group, the bag that owns it by a 6-step search of the lanes' end
+// offsets.  Lookups of table skip_t (>= 0: its rows are updated elsewhere) are
+// left out and the positions after them close up, so the sort sees
+// N - (lookups of skip_t) keys; that count goes to *n_eff.  Positions that no
+// bag covers (possible only with offsets that break the documented contract)
+// get the sentinel key, so every key and payload the sort reads is defined.
 template <typename IT, typename OT, bool WEIGHTED>
 __global__ __launch_bounds__(kBlock) void linearize_kernel(
     const IT* __restrict__ indices, const OT* __restrict__ offsets, const int64_t* __restrict__ meta,
     int32_t B, int64_t nbags, int32_t N, uint32_t sentinel, int skip_t, uint32_t* __restrict__ keys,
-    uint32_t* __restrict__ pay, uint32_t* __restrict__ bag_of) {
+    uint32_t* __restrict__ pay, uint32_t* __restrict__ bag_of, int32_t* __restrict__ n_eff) {
   const int lane = lane_id();
   const int64_t wave = (static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x) >> 6;
   const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * kBlock) >> 6;
+  auto clampN = [N](int64_t v, int64_t lo) {
+    return static_cast<int32_t>(min(max(v, lo), static_cast<int64_t>(N)));
+  };
+  // the skipped table's lookups [skip_lo, skip_lo + skip_len)
+  int32_t skip_lo = 0, skip_len = 0;
+  if (skip_t >= 0) {
+    skip_lo = clampN(static_cast<int64_t>(offsets[static_cast<int64_t>(skip_t) * B]), 0);
+    skip_len = clampN(static_cast<int64_t>(offsets[static_cast<int64_t>(skip_t + 1) * B]), skip_lo) - skip_lo;
+    if (wave == 0 && lane == 0) *n_eff = N - skip_len;
+  }
+  auto compact = [skip_lo, skip_len](int32_t p) { return p - min(max(p - skip_lo, 0), skip_len); };
+  auto fill = [&](int32_t lo, int32_t hi) {
+    for (int32_t p = lo + lane; p < hi; p += kWave) {
+      const int32_t q = compact(p);
+      keys[q] = sentinel;
+      if constexpr (WEIGHTED) {
+        pay[q] = static_cast<uint32_t>(p);
+        bag_of[p] = 0u;
+      } else {
+        pay[q] = 0u;
+      }
+    }
+  };
+  if (nbags == 0 && wave == 0) fill(0, N);
   for (int64_t g0 = wave * kWave; g0 < nbags; g0 += nwaves * kWave) {
+    const int64_t glast = min(g0 + kWave, nbags) - 1;
+    if (skip_t >= 0 && g0 / B == skip_t && glast / B == skip_t) continue;  // all 64 bags skipped
     const int64_t bag = g0 + lane;
-    const int32_t S = static_cast<int32_t>(
-        min(max(static_cast<int64_t>(offsets[g0]), static_cast<int64_t>(0)), static_cast<int64_t>(N)));
+    const int32_t S = clampN(static_cast<int64_t>(offsets[g0]), 0);
     int32_t e = S;
     int64_t rb = 0, E = 0;
+    bool skip = false;
     if (bag < nbags) {
-      e = static_cast<int32_t>(min(max(static_cast<int64_t>(offsets[bag + 1]), static_cast<int64_t>(S)),
-                                   static_cast<int64_t>(N)));
+      e = clampN(static_cast<int64_t>(offsets[bag + 1]), S);
       const int t = static_cast<int>(bag / B);
       rb = meta[4 * t];
-      E = t == skip_t ? 0 : meta[4 * (t + 1)] - rb;  // skip_t's lookups are left out
+      E = meta[4 * (t + 1)] - rb;
+      skip = t == skip_t;
     }
     // monotone end offsets across the 64 lanes (inclusive running max)
     for (int d = 1; d < kWave; d <<= 1) {
@@ -110,6 +143,7 @@ __global__ __launch_bounds__(kBlock) void linearize_kernel(
       if (lane >= d) e = max(e, u);
     }
     const int32_t Eend = __shfl(e, kWave - 1);
+    const uint64_t skip_mask = __ballot(skip);
     for (int32_t base = S; base < Eend; base += kWave) {
       const int32_t p = base + lane;
       const bool valid = p < Eend;
@@ -124,20 +158,26 @@ __global__ __launch_bounds__(kBlock) void linearize_kernel(
       const int k = lo;
       const int64_t rbk = __shfl(rb, k);
       const int64_t Ek = __shfl(E, k);
-      if (valid) {
+      if (valid && !((skip_mask >> k) & 1ull)) {
         const int64_t r = static_cast<int64_t>(indices[p]);
         const uint32_t key = (static_cast<uint64_t>(r) < static_cast<uint64_t>(Ek))
                                  ? static_cast<uint32_t>(rbk + r) : sentinel;
-        keys[p] = key;
+        const int32_t q = compact(p);
+        keys[q] = key;
         const uint32_t b = static_cast<uint32_t>(g0 + k);
         if constexpr (WEIGHTED) {
-          pay[p] = static_cast<uint32_t>(p);
+          pay[q] = static_cast<uint32_t>(p);
           bag_of[p] = b;
         } else {
-          pay[p] = b;
+          pay[q] = b;
         }
       }
     }
+    // positions no bag covers: before the first bag, and between this group's end
+    // and the next group's start
+    if (g0 == 0) fill(0, S);
+    const int32_t Snext = g0 + kWave < nbags ? clampN(static_cast<int64_t>(offsets[g0 + kWave]), 0) : N;
+    fill(Eend, Snext);
   }
 }
 
@@ -145,8 +185,10 @@ __global__ __launch_bounds__(kBlock) void linearize_kernel(
 // radix sort
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kBlock) void radix_upsweep(const uint32_t* __restrict__ keys, int64_t N,
+                                                        const int32_t* __restrict__ n_eff,
                                                         int64_t seg, int shift, int bits,
                                                         uint32_t* __restrict__ hist, int nblk) {
+  if (n_eff) N = min(N, static_cast<int64_t>(*n_eff));
   __shared__ uint32_t s_cnt[kWavesPerBlock][kRadixDigits];
   const int lane = lane_id(), w = threadIdx.x >> 6;
   const int ndig = 1 << bits;
@@ -213,8 +255,10 @@ __global__ __launch_bounds__(kBlock) void radix_scan(uint32_t* __restrict__ hist
 
 __global__ __launch_bounds__(kBlock) void radix_downsweep(
     const uint32_t* __restrict__ kin, const uint32_t* __restrict__ pin, uint32_t* __restrict__ kout,
-    uint32_t* __restrict__ pout, int64_t N, int64_t seg, int shift, int bits,
-    const uint32_t* __restrict__ hist, const uint32_t* __restrict__ tot, int nblk) {
+    uint32_t* __restrict__ pout, int64_t N, const int32_t* __restrict__ n_eff, int64_t seg,
+    int shift, int bits, const uint32_t* __restrict__ hist, const uint32_t* __restrict__ tot,
+    int nblk) {
+  if (n_eff) N = min(N, static_cast<int64_t>(*n_eff));
   __shared__ uint32_t s_base[kRadixDigits];
   __shared__ uint32_t s_wcnt[kWavesPerBlock][kRadixDigits];
   __shared__ uint32_t s_toff[kRadixDigits];
@@ -307,7 +351,9 @@ __global__ __launch_bounds__(kBlock) void radix_downsweep(
 constexpr int kRleItems = 4;
 
 __global__ __launch_bounds__(kBlock) void rle_count(const uint32_t* __restrict__ keys, int64_t N,
+                                                    const int32_t* __restrict__ n_eff,
                                                     int64_t seg, uint32_t* __restrict__ cnt) {
+  if (n_eff) N = min(N, static_cast<int64_t>(*n_eff));
   __shared__ uint32_t s_tmp[kWavesPerBlock];
   const int64_t lo = blockIdx.x * seg, hi = min(lo + seg, N);
   uint32_t c = 0;
@@ -333,7 +379,9 @@ __global__ __launch_bounds__(kBlock) void rle_count(const uint32_t* __restrict__
 // exclusive scan of the per-block head counts (one workgroup); run count to counters
 __global__ __launch_bounds__(kBlock) void rle_scan(uint32_t* __restrict__ cnt, int nblk,
                                                    int32_t* __restrict__ counters,
-                                                   uint32_t* __restrict__ run_start, int64_t N) {
+                                                   uint32_t* __restrict__ run_start, int64_t N,
+                                                   const int32_t* __restrict__ n_eff) {
+  if (n_eff) N = min(N, static_cast<int64_t>(*n_eff));
   __shared__ uint32_t s_tmp[kWavesPerBlock];
   const int ipt = (nblk + kBlock - 1) / kBlock;
   const int i0 = threadIdx.x * ipt;
@@ -358,9 +406,11 @@ __global__ __launch_bounds__(kBlock) void rle_scan(uint32_t* __restrict__ cnt, i
 }
 
 __global__ __launch_bounds__(kBlock) void rle_write(const uint32_t* __restrict__ keys, int64_t N,
+                                                    const int32_t* __restrict__ n_eff,
                                                     int64_t seg, const uint32_t* __restrict__ cnt,
                                                     uint32_t* __restrict__ run_key,
                                                     uint32_t* __restrict__ run_start) {
+  if (n_eff) N = min(N, static_cast<int64_t>(*n_eff));
   __shared__ uint32_t s_tmp[kWavesPerBlock];
   __shared__ uint32_t s_base;
   const int64_t lo = blockIdx.x * seg, hi = min(lo + seg, N);
@@ -586,7 +636,7 @@ __global__ void fill_i32_kernel(int32_t* p, int32_t v, int64_t n) {
 
 template <typename IT, typename OT>
 tbe_status linearize_go(const tbe_tables* tb, const IndexArgs& ia, int weighted, uint32_t* keys,
-                        uint32_t* pay, uint32_t* bag_of, int skip_t, hipStream_t s) {
+                        uint32_t* pay, uint32_t* bag_of, int skip_t, int32_t* n_eff, hipStream_t s) {
   const int64_t nbags = static_cast<int64_t>(tb->T) * tb->B;
   const int64_t groups = (nbags + kWave - 1) / kWave;
   const int64_t cap = static_cast<int64_t>(device_cu_count()) * 8 * kWavesPerBlock;
@@ -596,11 +646,13 @@ tbe_status linearize_go(const tbe_tables* tb, const IndexArgs& ia, int weighted,
   if (weighted)
     hipLaunchKernelGGL((linearize_kernel<IT, OT, true>), dim3(grid), dim3(kBlock), 0, s,
                        static_cast<const IT*>(ia.indices), static_cast<const OT*>(ia.offsets), tb->meta,
-                       tb->B, nbags, static_cast<int32_t>(ia.N), sentinel, skip_t, keys, pay, bag_of);
+                       tb->B, nbags, static_cast<int32_t>(ia.N), sentinel, skip_t, keys, pay, bag_of,
+                       n_eff);
   else
     hipLaunchKernelGGL((linearize_kernel<IT, OT, false>), dim3(grid), dim3(kBlock), 0, s,
                        static_cast<const IT*>(ia.indices), static_cast<const OT*>(ia.offsets), tb->meta,
-                       tb->B, nbags, static_cast<int32_t>(ia.N), sentinel, skip_t, keys, pay, bag_of);
+                       tb->B, nbags, static_cast<int32_t>(ia.N), sentinel, skip_t, keys, pay, bag_of,
+                       n_eff);
   return check_launch("linearize");
 }
 
@@ -627,13 +679,20 @@ tbe_status launch_transpose(const tbe_tables* tb, const IndexArgs& ia, int weigh
   uint32_t* keys[2] = {reinterpret_cast<uint32_t*>(ws + L.keys[0]), reinterpret_cast<uint32_t*>(ws + L.keys[1])};
   uint32_t* pay[2] = {reinterpret_cast<uint32_t*>(ws + L.pay[0]), reinterpret_cast<uint32_t*>(ws + L.pay[1])};
   uint32_t* bag_of = weighted ? reinterpret_cast<uint32_t*>(ws + L.bag_of) : nullptr;
+  // with a skipped table the sort covers only the other tables' lookups, a count
+  // known on the device once linearize has run
+  if (skip_table >= 0 && weighted) {
+    set_error("a table can be left out of the runs only without per-sample weights");
+    return TBE_ERR_ARG;
+  }
+  int32_t* n_eff = skip_table >= 0 ? counters + kNeff : nullptr;
   tbe_status st;
   if (ia.itype == TBE_I32)
-    st = ia.otype == TBE_I32 ? linearize_go<int32_t, int32_t>(tb, ia, weighted, keys[0], pay[0], bag_of, skip_table, s)
-                             : linearize_go<int32_t, int64_t>(tb, ia, weighted, keys[0], pay[0], bag_of, skip_table, s);
+    st = ia.otype == TBE_I32 ? linearize_go<int32_t, int32_t>(tb, ia, weighted, keys[0], pay[0], bag_of, skip_table, n_eff, s)
+                             : linearize_go<int32_t, int64_t>(tb, ia, weighted, keys[0], pay[0], bag_of, skip_table, n_eff, s);
   else
-    st = ia.otype == TBE_I32 ? linearize_go<int64_t, int32_t>(tb, ia, weighted, keys[0], pay[0], bag_of, skip_table, s)
-                             : linearize_go<int64_t, int64_t>(tb, ia, weighted, keys[0], pay[0], bag_of, skip_table, s);
+    st = ia.otype == TBE_I32 ? linearize_go<int64_t, int32_t>(tb, ia, weighted, keys[0], pay[0], bag_of, skip_table, n_eff, s)
+                             : linearize_go<int64_t, int64_t>(tb, ia, weighted, keys[0], pay[0], bag_of, skip_table, n_eff, s);
   if (st) return st;
   uint32_t* hist = reinterpret_cast<uint32_t*>(ws + L.sort_hist);
   uint32_t* tot = hist + static_cast<int64_t>(kRadixDigits) * L.nblocks;
@@ -642,7 +701,7 @@ tbe_status launch_transpose(const tbe_tables* tb, const IndexArgs& ia, int weigh
     const int ndig = 1 << L.bits[pass];
     {
       ProfScope ps("radix_upsweep", s);
-      hipLaunchKernelGGL(radix_upsweep, dim3(L.nblocks), dim3(kBlock), 0, s, keys[cur], N, L.seg,
+      hipLaunchKernelGGL(radix_upsweep, dim3(L.nblocks), dim3(kBlock), 0, s, keys[cur], N, n_eff, L.seg,
                          L.shift[pass], L.bits[pass], hist, L.nblocks);
     }
     if ((st = check_launch("radix_upsweep"))) return st;
@@ -654,7 +713,7 @@ tbe_status launch_transpose(const tbe_tables* tb, const IndexArgs& ia, int weigh
     {
       ProfScope ps("radix_downsweep", s);
       hipLaunchKernelGGL(radix_downsweep, dim3(L.nblocks), dim3(kBlock), 0, s, keys[cur], pay[cur],
-                         keys[cur ^ 1], pay[cur ^ 1], N, L.seg, L.shift[pass], L.bits[pass], hist,
+                         keys[cur ^ 1], pay[cur ^ 1], N, n_eff, L.seg, L.shift[pass], L.bits[pass], hist,
                          tot, L.nblocks);
     }
     if ((st = check_launch("radix_downsweep"))) return st;
@@ -666,9 +725,9 @@ tbe_status launch_transpose(const tbe_tables* tb, const IndexArgs& ia, int weigh
   uint32_t* seg_cnt = reinterpret_cast<uint32_t*>(ws + L.seg_cnt);
   {
     ProfScope ps("rle", s);
-    hipLaunchKernelGGL(rle_count, dim3(L.nblocks), dim3(kBlock), 0, s, keys[cur], N, L.seg, seg_cnt);
-    hipLaunchKernelGGL(rle_scan, dim3(1), dim3(kBlock), 0, s, seg_cnt, L.nblocks, counters, run_start, N);
-    hipLaunchKernelGGL(rle_write, dim3(L.nblocks), dim3(kBlock), 0, s, keys[cur], N, L.seg, seg_cnt,
+    hipLaunchKernelGGL(rle_count, dim3(L.nblocks), dim3(kBlock), 0, s, keys[cur], N, n_eff, L.seg, seg_cnt);
+    hipLaunchKernelGGL(rle_scan, dim3(1), dim3(kBlock), 0, s, seg_cnt, L.nblocks, counters, run_start, N, n_eff);
+    hipLaunchKernelGGL(rle_write, dim3(L.nblocks), dim3(kBlock), 0, s, keys[cur], N, n_eff, L.seg, seg_cnt,
                        run_key, run_start);
   }
   if ((st = check_launch("rle"))) return st;

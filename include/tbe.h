@@ -99,13 +99,15 @@ typedef struct {
 typedef struct {
   int32_t long_threshold;  /* a run with >= this many lookups is long (default 256) */
   int32_t chunk;           /* lookups per long-run chunk (default 256) */
-  int32_t hist_enable;     /* 1: histogram + MFMA forward for the eligible table (default 1) */
+  int32_t hist_enable;     /* 1: the eligible small table takes the histogram paths - counts x table
+                              on MFMA forward, counts^T x grad_out on MFMA backward (default 1) */
   int32_t fwd_unroll;      /* forward row loads in flight per lane group: 2, 4 or 8 (default 8) */
   int32_t bwd_unroll;      /* long-run chunk gradient rows in flight per lane group: 2, 4 or 8 (default 2) */
   int32_t sort_blocks;     /* workgroups of each radix pass (default 0 = automatic) */
   int32_t bag_windows;     /* long-run chunks are processed grouped by (table, bag window of their
                               first lookup), B / bag_windows bags per window, so that chunks that
-                              read the same gradient rows run together (default 32; <= 1: off) */
+                              read the same gradient rows run together (<= 1: off, the default;
+                              measured no faster on gfx950, where these reads come from HBM) */
   int32_t fused_long;      /* 1: long runs in one launch - each chunk writes its partial, a device-scope
                               fence, then a per-run countdown; the last chunk applies the optimizer
                               (blog section 4, problem 5).  0: chunk kernel + apply kernel (default) */
@@ -215,7 +217,11 @@ size_t tbe_backward_workspace_bytes(const tbe_tables* tables, int64_t num_indice
  * in place, rounded to the storage dtype (nearest even).  grad_out
  * [B][out_width] fp32.  per_sample_weights as in the forward (NULL =
  * unweighted).  workspace: at least tbe_backward_workspace_bytes, 256-byte
- * aligned; its contents are undefined after the call.
+ * aligned; its contents are undefined after the call.  When hist_enable is
+ * set, there are no per-sample weights and tables->hist_table >= 0, that
+ * table's rows take their gradient from per-bag lookup counts times grad_out
+ * on MFMA (blog section 2, forward-state reuse) and its lookups stay out of the
+ * sort; the other tables go through the sorted runs.
  */
 tbe_status tbe_backward_sgd(const tbe_tables* tables, void* weights, const void* indices,
                             int32_t index_type, const void* offsets, int32_t offset_type,

@@ -101,3 +101,23 @@ def test_workspace_bound_from_index_count():
     # floats) + long lists: about 45 bytes per lookup, 3.8 GB of the 288 GB
     assert 40 * n < b < 48 * n
     assert tbe.tbe_backward_workspace_bytes(t, n, True) > b
+
+
+def test_config_defaults():
+    c = tbe.make_config()
+    # the pages' long/short split and chunk size; histogram paths on; the optional paths off
+    assert (c.long_threshold, c.chunk, c.hist_enable) == (256, 256, 1)
+    assert c.bag_windows <= 1 and c.fused_long == 0 and c.sort_blocks == 0
+
+
+def test_workspace_histogram_table_partials():
+    """A histogram-eligible table adds its per-workgroup partials (512 x 64 x 128 floats and
+    512 x 64 counts) to the unweighted workspace only."""
+    E, D, B, n = [64, 1000], [128, 64], 4096, 600_000
+    plain = tbe.Tables(E, D, B, torch.float16, device=None)
+    hist = tbe.Tables(E, D, B, torch.float16, device=None, pooling_hint=[128, 5])
+    assert plain.c.hist_table == -1 and hist.c.hist_table == 0
+    extra = 512 * 64 * 128 * 4 + 512 * 64 * 4
+    d = tbe.tbe_backward_workspace_bytes(hist, n, False) - tbe.tbe_backward_workspace_bytes(plain, n, False)
+    assert extra <= d < extra + 1024
+    assert tbe.tbe_backward_workspace_bytes(hist, n, True) == tbe.tbe_backward_workspace_bytes(plain, n, True)

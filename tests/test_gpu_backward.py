@@ -259,3 +259,17 @@ def test_hist_backward_not_used_with_per_sample_weights():
     are not integers); results still match the oracle."""
     bt = ti.make_batch(_hist_spec(B=300, weighted=True), 67)
     run_and_check(bt, what="hist table weighted")
+
+
+@pytest.mark.parametrize("B", [97, 1000])
+def test_hist_backward_middle_table(B):
+    """The histogram table between two generic ones: its lookups leave the sorted key space and
+    the later tables' positions close up (groups of 64 bags straddle both table boundaries)."""
+    tables = (ti.TableSpec(3000, 64, ("poisson", 5.0, None, None), ("zipf", 1.2, None)),
+              ti.TableSpec(50, 112, ("poisson", 80.0, None, None)),
+              ti.TableSpec(700, 32, ("poisson", 3.0, None, None)))
+    spec = ti.BatchSpec(f"hist middle B={B}", tables, B=B, w_dtype=torch.float16, w_range=0.05,
+                        optimizer="rowwise_adagrad", pooling_hint=(5, 80, 3))
+    bt = ti.make_batch(spec, 71)
+    db, _, _, _ = run_and_check(bt, tbe.make_config(long_threshold=32, chunk=16), what=f"hist middle B={B}")
+    assert db.tables.c.hist_table == 1
