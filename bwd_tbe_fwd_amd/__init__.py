@@ -45,7 +45,8 @@ class tbe_config(ctypes.Structure):
     _fields_ = [("long_threshold", ctypes.c_int32), ("chunk", ctypes.c_int32),
                 ("hist_enable", ctypes.c_int32), ("fwd_unroll", ctypes.c_int32),
                 ("bwd_unroll", ctypes.c_int32), ("sort_blocks", ctypes.c_int32),
-                ("bag_windows", ctypes.c_int32), ("fused_long", ctypes.c_int32)]
+                ("bag_windows", ctypes.c_int32), ("fused_long", ctypes.c_int32),
+                ("pretransposed", ctypes.c_int32)]
 
 
 class tbe_runs_view(ctypes.Structure):
@@ -75,6 +76,8 @@ _SIGS = {
                     ctypes.c_int),
     "tbe_forward_repair": ([_P, _P, _P, ctypes.c_int32, _P, ctypes.c_int32, ctypes.c_int64, _P, _P,
                             _P, _P, ctypes.c_size_t, _P, _P], ctypes.c_int),
+    "tbe_forward_hoisted": ([_P, _P, _P, ctypes.c_int32, _P, ctypes.c_int32, ctypes.c_int64, _P, _P,
+                             _P, _P, ctypes.c_size_t, _P, ctypes.c_size_t, _P, _P], ctypes.c_int),
     "tbe_backward_workspace_bytes": ([_P, ctypes.c_int64, ctypes.c_int32, _P], ctypes.c_size_t),
     "tbe_backward_sgd": ([_P, _P, _P, ctypes.c_int32, _P, ctypes.c_int32, ctypes.c_int64, _P, _P,
                           ctypes.c_float, _P, ctypes.c_size_t, _P, _P], ctypes.c_int),
@@ -197,6 +200,21 @@ def tbe_forward_repair(tables: Tables, weights: torch.Tensor, indices: torch.Ten
                                   _ptr(workspace), workspace.numel() * workspace.element_size(),
                                   None if config is None else ctypes.byref(config), _stream(stream))
     _check(st, "tbe_forward_repair")
+
+
+def tbe_forward_hoisted(tables: Tables, weights: torch.Tensor, indices: torch.Tensor,
+                        offsets: torch.Tensor, per_sample_weights: Optional[torch.Tensor],
+                        out: torch.Tensor, error_counts: Optional[torch.Tensor],
+                        bounds_workspace: Optional[torch.Tensor], bwd_workspace: torch.Tensor,
+                        config: Optional[tbe_config] = None, stream=None):
+    bws = 0 if bounds_workspace is None else bounds_workspace.numel() * bounds_workspace.element_size()
+    st = lib().tbe_forward_hoisted(tables.ref, _ptr(weights), _ptr(indices), _I_DTYPE[indices.dtype],
+                                   _ptr(offsets), _I_DTYPE[offsets.dtype], indices.numel(),
+                                   _ptr(per_sample_weights), _ptr(out), _ptr(error_counts),
+                                   _ptr(bounds_workspace), bws, _ptr(bwd_workspace),
+                                   bwd_workspace.numel() * bwd_workspace.element_size(),
+                                   None if config is None else ctypes.byref(config), _stream(stream))
+    _check(st, "tbe_forward_hoisted")
 
 
 def tbe_backward_workspace_bytes(tables: Tables, num_indices: int, weighted: bool,

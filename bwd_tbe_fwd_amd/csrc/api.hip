@@ -107,6 +107,7 @@ Config resolve_config(const tbe_config* c) {
   r.sort_blocks = c->sort_blocks;
   r.bag_windows = c->bag_windows;
   r.fused_long = c->fused_long;
+  r.pretransposed = c->pretransposed;
   return r;
 }
 
@@ -266,6 +267,7 @@ void tbe_config_default(tbe_config* cfg) {
   cfg->sort_blocks = 0;
   cfg->bag_windows = 1;
   cfg->fused_long = 0;
+  cfg->pretransposed = 0;
 }
 
 int64_t tbe_meta_entries(int32_t T) { return T >= 0 ? static_cast<int64_t>(TBE_META_FIELDS) * (T + 1) : 0; }
@@ -360,6 +362,32 @@ tbe_status tbe_forward(const tbe_tables* tables, const void* weights, const void
                                nullptr, s);
 }
 
+// Forward after the offsets are final: the histogram table (if used) and the
+// gather; with error_counts, out-of-range ids are repaired on the way.
+static tbe_status forward_body(const tbe_tables* tables, const void* weights, const IndexArgs& ia,
+                               const float* psw, float* out, int64_t* error_counts, const Config& cfg,
+                               hipStream_t s) {
+  const int hist = (cfg.hist_enable && !psw && tables->hist_table >= 0) ? tables->hist_table : -1;
+  if (hist >= 0) {
+    // the histogram kernel does not repair: standalone validation first
+    if (error_counts)
+      if (tbe_status st = launch_bounds_indices(tables, const_cast<void*>(ia.indices), ia.itype,
+                                                ia.offsets, ia.otype, ia.N, error_counts, s))
+        return st;
+    if (tbe_status st = launch_forward_hist(tables, weights, ia, out, s)) return st;
+    return launch_forward_gather(tables, weights, ia, psw, out, hist, cfg.fwd_unroll, nullptr, s);
+  }
+  return launch_forward_gather(tables, weights, ia, psw, out, -1, cfg.fwd_unroll, error_counts, s);
+}
+
+static tbe_status check_bounds_ws(const tbe_tables* tables, const void* workspace, size_t bytes) {
+  if (!workspace || bytes < bounds_workspace(tables) || (reinterpret_cast<uintptr_t>(workspace) & 255)) {
+    set_error("bounds workspace needs %zu bytes, 256-byte aligned", bounds_workspace(tables));
+    return TBE_ERR_WORKSPACE;
+  }
+  return TBE_OK;
+}
+
 tbe_status tbe_forward_repair(const tbe_tables* tables, const void* weights, void* indices,
                               int32_t index_type, void* offsets, int32_t offset_type, int64_t num_indices,
                               const float* per_sample_weights, float* out, int64_t* error_counts,
@@ -369,10 +397,7 @@ tbe_status tbe_forward_repair(const tbe_tables* tables, const void* weights, voi
   if (tbe_status st = check_tables(tables)) return st;
   if (tbe_status st = check_index_args(tables, indices, index_type, offsets, offset_type, num_indices)) return st;
   if (!error_counts) { set_error("error_counts is NULL"); return TBE_ERR_ARG; }
-  if (!workspace || workspace_bytes < bounds_workspace(tables) || (reinterpret_cast<uintptr_t>(workspace) & 255)) {
-    set_error("bounds workspace needs %zu bytes, 256-byte aligned", bounds_workspace(tables));
-    return TBE_ERR_WORKSPACE;
-  }
+  if (tbe_status st = check_bounds_ws(tables, workspace, workspace_bytes)) return st;
   if (tables->B > 0) {
     if (tbe_status st = check_rows(weights, "weights", weight_align(tables))) return st;
     if (tbe_status st = check_rows(out, "out", 16)) return st;
@@ -385,18 +410,100 @@ tbe_status tbe_forward_repair(const tbe_tables* tables, const void* weights, voi
                                                    num_indices, error_counts, s);
   const Config cfg = resolve_config(config);
   IndexArgs ia{indices, index_type, offsets, offset_type, num_indices};
-  const int hist = (cfg.hist_enable && !per_sample_weights && tables->hist_table >= 0) ? tables->hist_table : -1;
-  if (hist >= 0) {
-    // the histogram kernel does not repair: standalone validation first
-    if (tbe_status st = launch_bounds_indices(tables, indices, index_type, offsets, offset_type,
-                                              num_indices, error_counts, s))
-      return st;
-    if (tbe_status st = launch_forward_hist(tables, weights, ia, out, s)) return st;
-    return launch_forward_gather(tables, weights, ia, per_sample_weights, out, hist, cfg.fwd_unroll,
-                                 nullptr, s);
+  return forward_body(tables, weights, ia, per_sample_weights, out, error_counts, cfg, s);
+}
+
+// ---------------------------------------------------------------------------
+// second stream for the hoisted transpose (one per device, made on first use)
+// ---------------------------------------------------------------------------
+namespace {
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_side_mu;
+SideStream g_side[kMaxDevices];
+
+// Returns the current device's side stream with g_side_mu held by the caller.
+tbe_status side_stream(SideStream** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    set_error("hipGetDevice failed or device id out of range");
+    return TBE_ERR_HIP;
   }
-  return launch_forward_gather(tables, weights, ia, per_sample_weights, out, -1, cfg.fwd_unroll,
-                               error_counts, s);
+  SideStream& ss = g_side[dev];
+  if (!ss.stream) {
+    // default priority; does not synchronize with the null stream
+    if (hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess) {
+      set_error("could not create the side stream or its events");
+      return TBE_ERR_HIP;
+    }
+  }
+  *out = &ss;
+  return TBE_OK;
+}
+}  // namespace
+
+tbe_status tbe_forward_hoisted(const tbe_tables* tables, const void* weights, void* indices,
+                               int32_t index_type, void* offsets, int32_t offset_type,
+                               int64_t num_indices, const float* per_sample_weights, float* out,
+                               int64_t* error_counts, void* bounds_workspace,
+                               size_t bounds_workspace_bytes, void* bwd_workspace,
+                               size_t bwd_workspace_bytes, const tbe_config* config,
+                               tbe_stream_t stream) {
+  g_error[0] = 0;
+  if (tbe_status st = check_tables(tables)) return st;
+  if (tbe_status st = check_index_args(tables, indices, index_type, offsets, offset_type, num_indices)) return st;
+  if (error_counts)
+    if (tbe_status st = check_bounds_ws(tables, bounds_workspace, bounds_workspace_bytes)) return st;
+  if (tables->B > 0) {
+    if (tbe_status st = check_rows(weights, "weights", weight_align(tables))) return st;
+    if (tbe_status st = check_rows(out, "out", 16)) return st;
+  }
+  const Config cfg = resolve_config(config);
+  const int weighted = per_sample_weights ? 1 : 0;
+  const BwdLayout L = bwd_layout(tables, num_indices, weighted, cfg);
+  if (!bwd_workspace || bwd_workspace_bytes < L.total || (reinterpret_cast<uintptr_t>(bwd_workspace) & 255)) {
+    set_error("backward workspace needs %zu bytes, 256-byte aligned (got %zu)", L.total, bwd_workspace_bytes);
+    return TBE_ERR_WORKSPACE;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (error_counts)
+    if (tbe_status st = launch_bounds_offsets(tables, offsets, offset_type, num_indices, error_counts,
+                                              bounds_workspace, s))
+      return st;
+  IndexArgs ia{indices, index_type, offsets, offset_type, num_indices};
+  // the backward skips the transpose when there are no bags or no lookups
+  if (tables->B == 0 || num_indices == 0) {
+    if (tables->B == 0)
+      return error_counts ? launch_bounds_indices(tables, indices, index_type, offsets, offset_type,
+                                                  num_indices, error_counts, s)
+                          : TBE_OK;
+    return forward_body(tables, weights, ia, per_sample_weights, out, error_counts, cfg, s);
+  }
+  const int hist = (cfg.hist_enable && !per_sample_weights && tables->hist_table >= 0) ? tables->hist_table : -1;
+  std::lock_guard<std::mutex> lk(g_side_mu);
+  SideStream* ss = nullptr;
+  if (tbe_status st = side_stream(&ss)) return st;
+  if (hipEventRecord(ss->fork, s) != hipSuccess || hipStreamWaitEvent(ss->stream, ss->fork, 0) != hipSuccess) {
+    set_error("fork to the side stream failed");
+    return TBE_ERR_HIP;
+  }
+  int final_buf = 0;
+  const tbe_status st_t = launch_transpose(tables, ia, weighted, static_cast<char*>(bwd_workspace), L,
+                                           cfg, hist, error_counts ? 1 : 0, &final_buf, ss->stream);
+  // join even after a failed launch, so that the streams stay ordered
+  const bool rec_ok = hipEventRecord(ss->join, ss->stream) == hipSuccess;
+  const tbe_status st_f = st_t ? TBE_OK
+                               : forward_body(tables, weights, ia, per_sample_weights, out, error_counts, cfg, s);
+  if (!rec_ok || hipStreamWaitEvent(s, ss->join, 0) != hipSuccess) {
+    set_error("join of the side stream failed");
+    return TBE_ERR_HIP;
+  }
+  return st_t ? st_t : st_f;
 }
 
 size_t tbe_backward_workspace_bytes(const tbe_tables* tables, int64_t num_indices, int32_t weighted,
@@ -426,10 +533,13 @@ static tbe_status backward_common(const tbe_tables* tables, void* weights, float
   IndexArgs ia{indices, index_type, offsets, offset_type, num_indices};
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  int final_buf = 0;
   // the small table's rows are updated from per-bag counts x gradient (MFMA) instead of runs
   const int hist = (cfg.hist_enable && !psw && tables->hist_table >= 0) ? tables->hist_table : -1;
-  if (tbe_status st = launch_transpose(tables, ia, psw ? 1 : 0, ws, L, cfg, hist, &final_buf, s)) return st;
+  // pretransposed: tbe_forward_hoisted left the sorted runs in the workspace; the
+  // radix passes alternate buffers starting from buffer 0
+  int final_buf = L.passes & 1;
+  if (!cfg.pretransposed)
+    if (tbe_status st = launch_transpose(tables, ia, psw ? 1 : 0, ws, L, cfg, hist, 0, &final_buf, s)) return st;
   if (hist >= 0)
     if (tbe_status st = launch_hist_backward(tables, weights, momentum, opt, ia, grad_out, lr, eps, ws, L, s))
       return st;
@@ -474,7 +584,7 @@ tbe_status tbe_transpose(const tbe_tables* tables, const void* indices, int32_t 
   IndexArgs ia{indices, index_type, offsets, offset_type, num_indices};
   char* ws = static_cast<char*>(workspace);
   int final_buf = 0;
-  tbe_status st = launch_transpose(tables, ia, weighted ? 1 : 0, ws, L, cfg, -1, &final_buf,
+  tbe_status st = launch_transpose(tables, ia, weighted ? 1 : 0, ws, L, cfg, -1, 0, &final_buf,
                                    static_cast<hipStream_t>(stream));
   std::memset(view, 0, sizeof(*view));
   view->sorted_keys = reinterpret_cast<const uint32_t*>(ws + L.keys[final_buf]);

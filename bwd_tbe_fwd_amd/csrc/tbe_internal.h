@@ -41,6 +41,7 @@ constexpr int kRadixTile = kBlock * kRadixItems;      // 4096 keys
 
 struct Config {
   int threshold, chunk, hist_enable, fwd_unroll, bwd_unroll, sort_blocks, bag_windows, fused_long;
+  int pretransposed;
 };
 Config resolve_config(const tbe_config* c);
 
@@ -97,9 +98,11 @@ tbe_status launch_bounds_indices(const tbe_tables* tb, void* indices, int itype,
 
 // skip_table >= 0: that table's lookups are left out of the runs (its rows are
 // updated by the histogram backward)
+// invalid_as_row0: an id outside its table counts as row 0 (the value the bounds
+// repair writes) instead of being dropped
 tbe_status launch_transpose(const tbe_tables* tb, const IndexArgs& ia, int weighted,
                             char* ws, const BwdLayout& L, const Config& cfg, int skip_table,
-                            int* final_buf, hipStream_t s);
+                            int invalid_as_row0, int* final_buf, hipStream_t s);
 
 // histogram backward of the small table (counts x gradient on MFMA, then the optimizer)
 constexpr int kHistBwdBlocks = 512;  // max partials (workgroups) of the histogram backward

@@ -93,8 +93,9 @@ __device__ __forceinline__ uint64_t match_digit(uint32_t d, int bits, uint64_t v
 template <typename IT, typename OT, bool WEIGHTED>
 __global__ __launch_bounds__(kBlock) void linearize_kernel(
     const IT* __restrict__ indices, const OT* __restrict__ offsets, const int64_t* __restrict__ meta,
-    int32_t B, int64_t nbags, int32_t N, uint32_t sentinel, int skip_t, uint32_t* __restrict__ keys,
-    uint32_t* __restrict__ pay, uint32_t* __restrict__ bag_of, int32_t* __restrict__ n_eff) {
+    int32_t B, int64_t nbags, int32_t N, uint32_t sentinel, int skip_t, int invalid_as_row0,
+    uint32_t* __restrict__ keys, uint32_t* __restrict__ pay, uint32_t* __restrict__ bag_of,
+    int32_t* __restrict__ n_eff) {
   const int lane = lane_id();
   const int64_t wave = (static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x) >> 6;
   const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * kBlock) >> 6;
@@ -161,7 +162,8 @@ __global__ __launch_bounds__(kBlock) void linearize_kernel(
       if (valid && !((skip_mask >> k) & 1ull)) {
         const int64_t r = static_cast<int64_t>(indices[p]);
         const uint32_t key = (static_cast<uint64_t>(r) < static_cast<uint64_t>(Ek))
-                                 ? static_cast<uint32_t>(rbk + r) : sentinel;
+                                 ? static_cast<uint32_t>(rbk + r)
+                                 : (invalid_as_row0 ? static_cast<uint32_t>(rbk) : sentinel);
         const int32_t q = compact(p);
         keys[q] = key;
         const uint32_t b = static_cast<uint32_t>(g0 + k);
@@ -636,7 +638,8 @@ __global__ void fill_i32_kernel(int32_t* p, int32_t v, int64_t n) {
 
 template <typename IT, typename OT>
 tbe_status linearize_go(const tbe_tables* tb, const IndexArgs& ia, int weighted, uint32_t* keys,
-                        uint32_t* pay, uint32_t* bag_of, int skip_t, int32_t* n_eff, hipStream_t s) {
+                        uint32_t* pay, uint32_t* bag_of, int skip_t, int invalid_as_row0,
+                        int32_t* n_eff, hipStream_t s) {
   const int64_t nbags = static_cast<int64_t>(tb->T) * tb->B;
   const int64_t groups = (nbags + kWave - 1) / kWave;
   const int64_t cap = static_cast<int64_t>(device_cu_count()) * 8 * kWavesPerBlock;
@@ -646,13 +649,13 @@ tbe_status linearize_go(const tbe_tables* tb, const IndexArgs& ia, int weighted,
   if (weighted)
     hipLaunchKernelGGL((linearize_kernel<IT, OT, true>), dim3(grid), dim3(kBlock), 0, s,
                        static_cast<const IT*>(ia.indices), static_cast<const OT*>(ia.offsets), tb->meta,
-                       tb->B, nbags, static_cast<int32_t>(ia.N), sentinel, skip_t, keys, pay, bag_of,
-                       n_eff);
+                       tb->B, nbags, static_cast<int32_t>(ia.N), sentinel, skip_t, invalid_as_row0, keys, pay,
+                       bag_of, n_eff);
   else
     hipLaunchKernelGGL((linearize_kernel<IT, OT, false>), dim3(grid), dim3(kBlock), 0, s,
                        static_cast<const IT*>(ia.indices), static_cast<const OT*>(ia.offsets), tb->meta,
-                       tb->B, nbags, static_cast<int32_t>(ia.N), sentinel, skip_t, keys, pay, bag_of,
-                       n_eff);
+                       tb->B, nbags, static_cast<int32_t>(ia.N), sentinel, skip_t, invalid_as_row0, keys, pay,
+                       bag_of, n_eff);
   return check_launch("linearize");
 }
 
@@ -666,8 +669,8 @@ tbe_status launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s) {
 }
 
 tbe_status launch_transpose(const tbe_tables* tb, const IndexArgs& ia, int weighted, char* ws,
-                            const BwdLayout& L, const Config& cfg, int skip_table, int* final_buf,
-                            hipStream_t s) {
+                            const BwdLayout& L, const Config& cfg, int skip_table,
+                            int invalid_as_row0, int* final_buf, hipStream_t s) {
   int32_t* counters = reinterpret_cast<int32_t*>(ws + L.counters);
   if (tbe_status st = launch_fill_i32(counters, 0, kNumCounters, s)) return st;
   const int64_t N = L.N;
@@ -688,11 +691,11 @@ tbe_status launch_transpose(const tbe_tables* tb, const IndexArgs& ia, int weigh
   int32_t* n_eff = skip_table >= 0 ? counters + kNeff : nullptr;
   tbe_status st;
   if (ia.itype == TBE_I32)
-    st = ia.otype == TBE_I32 ? linearize_go<int32_t, int32_t>(tb, ia, weighted, keys[0], pay[0], bag_of, skip_table, n_eff, s)
-                             : linearize_go<int32_t, int64_t>(tb, ia, weighted, keys[0], pay[0], bag_of, skip_table, n_eff, s);
+    st = ia.otype == TBE_I32 ? linearize_go<int32_t, int32_t>(tb, ia, weighted, keys[0], pay[0], bag_of, skip_table, invalid_as_row0, n_eff, s)
+                             : linearize_go<int32_t, int64_t>(tb, ia, weighted, keys[0], pay[0], bag_of, skip_table, invalid_as_row0, n_eff, s);
   else
-    st = ia.otype == TBE_I32 ? linearize_go<int64_t, int32_t>(tb, ia, weighted, keys[0], pay[0], bag_of, skip_table, n_eff, s)
-                             : linearize_go<int64_t, int64_t>(tb, ia, weighted, keys[0], pay[0], bag_of, skip_table, n_eff, s);
+    st = ia.otype == TBE_I32 ? linearize_go<int64_t, int32_t>(tb, ia, weighted, keys[0], pay[0], bag_of, skip_table, invalid_as_row0, n_eff, s)
+                             : linearize_go<int64_t, int64_t>(tb, ia, weighted, keys[0], pay[0], bag_of, skip_table, invalid_as_row0, n_eff, s);
   if (st) return st;
   uint32_t* hist = reinterpret_cast<uint32_t*>(ws + L.sort_hist);
   uint32_t* tot = hist + static_cast<int64_t>(kRadixDigits) * L.nblocks;

@@ -111,6 +111,8 @@ typedef struct {
   int32_t fused_long;      /* 1: long runs in one launch - each chunk writes its partial, a device-scope
                               fence, then a per-run countdown; the last chunk applies the optimizer
                               (blog section 4, problem 5).  0: chunk kernel + apply kernel (default) */
+  int32_t pretransposed;   /* backward only: 1 = the workspace already holds this batch's transpose,
+                              written by tbe_forward_hoisted; the backward skips its own (default 0) */
 } tbe_config;
 
 /* Device-side view of the transpose, for inspection by tests (tbe_transpose). */
@@ -202,6 +204,32 @@ tbe_status tbe_forward_repair(const tbe_tables* tables, const void* weights, voi
                               int64_t num_indices, const float* per_sample_weights, float* out,
                               int64_t* error_counts, void* workspace, size_t workspace_bytes,
                               const tbe_config* config, tbe_stream_t stream);
+
+/*
+ * Forward with the backward's transpose hoisted into it (blog section 2,
+ * forward-state reuse and preprocessing; the tutorial's section on forward
+ * slower, total faster).  Computes out exactly as tbe_forward
+ * (error_counts == NULL) or tbe_forward_repair (error_counts != NULL, with
+ * bounds_workspace as there), and, on a second stream owned by the library,
+ * the backward's linearize / sort / run-length encoding / routing of the same
+ * batch into bwd_workspace (tbe_backward_workspace_bytes for the same tables,
+ * num_indices, per-sample-weights presence and config).  The second stream
+ * forks from `stream` after the offsets are final and joins it again before
+ * the call returns: work enqueued later on `stream` sees the output and the
+ * transpose.  A following tbe_backward_* with config->pretransposed = 1 and the
+ * same tables, indices, offsets, per-sample-weights presence, config and
+ * bwd_workspace skips its own transpose.  With repair, an out-of-range id
+ * counts in the transpose as row 0 of its table, the value the repair writes,
+ * whichever of the two reads the id first.  Calls that overlap on one device
+ * share the second stream and run their transposes in call order.
+ */
+tbe_status tbe_forward_hoisted(const tbe_tables* tables, const void* weights, void* indices,
+                               int32_t index_type, void* offsets, int32_t offset_type,
+                               int64_t num_indices, const float* per_sample_weights, float* out,
+                               int64_t* error_counts, void* bounds_workspace,
+                               size_t bounds_workspace_bytes, void* bwd_workspace,
+                               size_t bwd_workspace_bytes, const tbe_config* config,
+                               tbe_stream_t stream);
 
 /*
  * Bytes of workspace the backward (and tbe_transpose) needs for num_indices

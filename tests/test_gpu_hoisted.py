@@ -1,0 +1,133 @@
+"""Transpose hoisted into the forward: tbe_forward_hoisted runs the backward's linearize / sort /
+run-length encoding / routing on a second stream while the forward pools; the backward with
+pretransposed = 1 then skips its own transpose.  Everything must equal the plain two calls bit
+for bit, and the oracle on the (repaired) input within the usual bounds."""
+import numpy as np
+import pytest
+import torch
+
+import bwd_tbe_fwd_amd as tbe
+import oracle
+import tbe_inputs as ti
+from gpu_util import check_momentum, check_weights, flush_print, host_arrays, row_g_abs_sq, step_bound
+from test_gpu_forward import small_spec
+
+pytestmark = pytest.mark.gpu
+
+
+def _inject(bt, seed, bad_offsets):
+    """Out-of-range ids (5 %) and, optionally, broken offsets (1 %) on host copies."""
+    rng = np.random.default_rng(seed)
+    idx = bt.indices.numpy().astype(np.int64).copy()
+    off = bt.offsets.numpy().astype(np.int64).copy()
+    bad = rng.random(idx.size) < 0.05
+    idx[bad] = rng.choice([-1, -50, 10 ** 7], size=int(bad.sum()))
+    if bad_offsets:
+        ob = rng.random(off.size) < 0.01
+        off[ob] = rng.integers(-3, idx.size + 9, size=int(ob.sum()))
+        off[-1] = idx.size - 2
+    return idx, off
+
+
+def _step(bt, idx, off, hoisted, repair, cfg_kw=None):
+    """forward (+ repair) then backward, on device copies; returns everything observable."""
+    cfg_kw = cfg_kw or {}
+    spec = bt.spec
+    t = tbe.Tables(bt.E, bt.D, bt.B, bt.w_dtype, device="cuda", pooling_hint=spec.pooling_hint)
+    W = bt.weights.cuda()
+    d_idx = torch.as_tensor(idx).to(bt.indices.dtype).cuda()
+    d_off = torch.as_tensor(off).to(bt.offsets.dtype).cuda()
+    psw = None if bt.psw is None else bt.psw.cuda()
+    grad = bt.grad_out.cuda()
+    mom = bt.momentum.cuda() if bt.momentum is not None else None
+    out = torch.full((bt.B, sum(bt.D)), float("nan"), device="cuda")
+    counts = torch.full((2,), -1, dtype=torch.int64, device="cuda") if repair else None
+    bws = tbe.workspace(tbe.tbe_bounds_check_workspace_bytes(t)) if repair else None
+    cfg = tbe.make_config(**cfg_kw)
+    ws = tbe.workspace(tbe.tbe_backward_workspace_bytes(t, d_idx.numel(), psw is not None, cfg))
+    if hoisted:
+        tbe.tbe_forward_hoisted(t, W, d_idx, d_off, psw, out, counts, bws, ws, cfg)
+        bcfg = tbe.make_config(pretransposed=1, **cfg_kw)
+    else:
+        if repair:
+            tbe.tbe_forward_repair(t, W, d_idx, d_off, psw, out, counts, bws, cfg)
+        else:
+            tbe.tbe_forward(t, W, d_idx, d_off, psw, out, cfg)
+        bcfg = cfg
+    lr = oracle.f32_literal(spec.lr)
+    if spec.optimizer == "sgd":
+        tbe.tbe_backward_sgd(t, W, d_idx, d_off, psw, grad, lr, ws, bcfg)
+    else:
+        tbe.tbe_backward_rowwise_adagrad(t, W, mom, d_idx, d_off, psw, grad, lr,
+                                         oracle.f32_literal(spec.eps), ws, bcfg)
+    torch.cuda.synchronize()
+    return dict(out=out.cpu(), W=W.cpu(), mom=None if mom is None else mom.cpu(),
+                idx=d_idx.cpu(), off=d_off.cpu(), counts=None if counts is None else counts.cpu(),
+                hist=t.c.hist_table)
+
+
+def _assert_same(a, b):
+    assert torch.equal(a["out"].view(torch.int32), b["out"].view(torch.int32))
+    assert torch.equal(a["W"].view(torch.uint8), b["W"].view(torch.uint8))
+    if a["mom"] is not None:
+        assert torch.equal(a["mom"].view(torch.int32), b["mom"].view(torch.int32))
+    assert torch.equal(a["idx"], b["idx"]) and torch.equal(a["off"], b["off"])
+    if a["counts"] is not None:
+        assert torch.equal(a["counts"], b["counts"])
+
+
+@pytest.mark.parametrize("name", ["skewed", "mixed", "histogram", "uniform", "tiny"])
+@pytest.mark.parametrize("repair", [False, True])
+def test_hoisted_equals_plain(name, repair):
+    spec = small_spec(name)
+    flush_print(f"hoisted {name} repair={repair}")
+    bt = ti.make_batch(spec, 81)
+    idx, off = _inject(bt, 3, bad_offsets=repair)
+    cfg_kw = dict(long_threshold=32, chunk=16)
+    plain = _step(bt, idx, off, hoisted=False, repair=repair, cfg_kw=cfg_kw)
+    hoist = _step(bt, idx, off, hoisted=True, repair=repair, cfg_kw=cfg_kw)
+    _assert_same(plain, hoist)
+    if repair:
+        assert hoist["counts"][0] > 0 and hoist["counts"][1] > 0
+
+
+@pytest.mark.parametrize("name", ["skewed", "histogram"])
+def test_hoisted_repaired_matches_oracle(name):
+    """The hoisted step on faulty input equals the oracle's step on the repaired input: an
+    out-of-range id counts as row 0 of its table in the backward."""
+    spec = small_spec(name)
+    bt = ti.make_batch(spec, 83)
+    idx, off = _inject(bt, 5, bad_offsets=True)
+    got = _step(bt, idx, off, hoisted=True, repair=True)
+    exp_idx, exp_off, exp_cnt = oracle.bounds_check(bt.T, bt.B, bt.E, idx, off)
+    assert np.array_equal(got["idx"].numpy().astype(np.int64), exp_idx)
+    assert np.array_equal(got["off"].numpy().astype(np.int64), exp_off)
+    a = host_arrays(bt)
+    r = oracle.backward(a["T"], a["B"], a["E"], a["D"], oracle.F16, a["W"], exp_idx, exp_off, None,
+                        a["grad"], oracle.ROWWISE_ADAGRAD, oracle.f32_literal(spec.lr),
+                        oracle.f32_literal(spec.eps), a["mom"])
+    lr32, eps32 = oracle.f32_literal(spec.lr), oracle.f32_literal(spec.eps)
+    check_weights(got["W"], r, bt.w_dtype, step_bound(r, bt.E, bt.D, lr32, eps32, True), f"hoisted {name}")
+    gsq, Dr = row_g_abs_sq(r, bt.E, bt.D)
+    check_momentum(got["mom"], r, Dr, gsq, f"hoisted {name}")
+
+
+def test_hoisted_workspace_holds_latest_batch():
+    """Two hoisted forwards into one workspace: the backward uses the second batch's runs."""
+    spec = small_spec("skewed")
+    bt1, bt2 = ti.make_batch(spec, 85), ti.make_batch(spec, 86)
+    t = tbe.Tables(bt1.E, bt1.D, bt1.B, bt1.w_dtype, device="cuda")
+    n = max(bt1.num_indices, bt2.num_indices)
+    ws = tbe.workspace(tbe.tbe_backward_workspace_bytes(t, n, False))
+    out = torch.empty(bt1.B, sum(bt1.D), device="cuda")
+    tbe.tbe_forward_hoisted(t, bt1.weights.cuda(), bt1.indices.cuda(), bt1.offsets.cuda(), None, out,
+                            None, None, ws)
+    i2, o2 = bt2.indices.cuda(), bt2.offsets.cuda()
+    tbe.tbe_forward_hoisted(t, bt2.weights.cuda(), i2, o2, None, out, None, None, ws)
+    W, mom = bt2.weights.cuda(), bt2.momentum.cuda()
+    lr, eps = oracle.f32_literal(spec.lr), oracle.f32_literal(spec.eps)
+    tbe.tbe_backward_rowwise_adagrad(t, W, mom, i2, o2, None, bt2.grad_out.cuda(), lr, eps, ws,
+                                     tbe.make_config(pretransposed=1))
+    ref = _step(bt2, bt2.indices.numpy(), bt2.offsets.numpy(), hoisted=False, repair=False)
+    assert torch.equal(W.cpu().view(torch.int16), ref["W"].view(torch.int16))
+    assert torch.equal(mom.cpu(), ref["mom"])
