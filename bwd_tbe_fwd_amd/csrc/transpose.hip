@@ -212,14 +212,12 @@ __global__ __launch_bounds__(kBlock) void radix_upsweep(const uint32_t* __restri
         for (int q = 0; q < 4; ++q) k[4 * s + q] = i + q < hi ? keys[i + q] : 0u;
       }
     }
+    // counts are order-free: one LDS atomic add per key (equal digits serialize in
+    // the LDS unit, which is cheaper than matching lanes first)
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int64_t i = base + (j >> 2) * 4 * kWave + 4 * lane + (j & 3);
-      const bool valid = i < hi;
-      const uint32_t d = (k[j] >> shift) & mask;
-      const uint64_t peers = match_digit(d, bits, __ballot(valid));
-      if (valid && lane == __ffsll(static_cast<long long>(peers)) - 1) s_cnt[w][d] += __popcll(peers);
-      __builtin_amdgcn_wave_barrier();
+      if (i < hi) atomicAdd(&s_cnt[w][(k[j] >> shift) & mask], 1u);
     }
   }
   __syncthreads();

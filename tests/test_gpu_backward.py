@@ -273,3 +273,18 @@ def test_hist_backward_middle_table(B):
     bt = ti.make_batch(spec, 71)
     db, _, _, _ = run_and_check(bt, tbe.make_config(long_threshold=32, chunk=16), what=f"hist middle B={B}")
     assert db.tables.c.hist_table == 1
+
+
+@pytest.mark.parametrize("windows", [8, 32, 64])
+@pytest.mark.parametrize("name", ["skewed", "mixed"])
+def test_long_chunks_grouped_by_window(name, windows):
+    """Long-run chunks grouped by (table, bag window): same result as the ungrouped
+    order bit for bit (each chunk writes its own partial; the apply sums them in chunk order),
+    and the oracle's within the stated bounds."""
+    bt = ti.make_batch(small_spec(name), 47)
+    kw = dict(long_threshold=16, chunk=8)
+    _, W1, m1, _ = run_and_check(bt, tbe.make_config(bag_windows=windows, **kw), what=f"{name} windows={windows}")
+    _, W0, m0, _ = run_and_check(bt, tbe.make_config(bag_windows=1, **kw), what=f"{name} ungrouped")
+    assert torch.equal(W1.cpu().view(torch.uint8), W0.cpu().view(torch.uint8))
+    if m1 is not None:
+        assert torch.equal(m1.cpu(), m0.cpu())
