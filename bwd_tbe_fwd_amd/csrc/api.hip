@@ -357,7 +357,7 @@ tbe_status tbe_forward(const tbe_tables* tables, const void* weights, const void
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int hist = (cfg.hist_enable && !per_sample_weights && tables->hist_table >= 0) ? tables->hist_table : -1;
   if (hist >= 0)
-    if (tbe_status st = launch_forward_hist(tables, weights, ia, out, s)) return st;
+    if (tbe_status st = launch_forward_hist(tables, weights, ia, out, nullptr, s)) return st;
   return launch_forward_gather(tables, weights, ia, per_sample_weights, out, hist, cfg.fwd_unroll,
                                nullptr, s);
 }
@@ -368,16 +368,10 @@ static tbe_status forward_body(const tbe_tables* tables, const void* weights, co
                                const float* psw, float* out, int64_t* error_counts, const Config& cfg,
                                hipStream_t s) {
   const int hist = (cfg.hist_enable && !psw && tables->hist_table >= 0) ? tables->hist_table : -1;
-  if (hist >= 0) {
-    // the histogram kernel does not repair: standalone validation first
-    if (error_counts)
-      if (tbe_status st = launch_bounds_indices(tables, const_cast<void*>(ia.indices), ia.itype,
-                                                ia.offsets, ia.otype, ia.N, error_counts, s))
-        return st;
-    if (tbe_status st = launch_forward_hist(tables, weights, ia, out, s)) return st;
-    return launch_forward_gather(tables, weights, ia, psw, out, hist, cfg.fwd_unroll, nullptr, s);
-  }
-  return launch_forward_gather(tables, weights, ia, psw, out, -1, cfg.fwd_unroll, error_counts, s);
+  // both kernels repair the ids they read (the histogram table's, everyone else's)
+  if (hist >= 0)
+    if (tbe_status st = launch_forward_hist(tables, weights, ia, out, error_counts, s)) return st;
+  return launch_forward_gather(tables, weights, ia, psw, out, hist, cfg.fwd_unroll, error_counts, s);
 }
 
 static tbe_status check_bounds_ws(const tbe_tables* tables, const void* workspace, size_t bytes) {

@@ -193,42 +193,85 @@ constexpr int kHistRows = 64;   // K of the contraction (table rows, zero padded
 constexpr int kHistCols = 128;  // max D
 constexpr int kHistBags = 16;   // M of one MFMA tile
 constexpr int kHistHead = 256;  // ids per bag counted into the histogram
+constexpr int kHistLoads = 8;   // id loads in flight per lane while counting
 
-template <typename IT, typename OT>
+template <typename IT, typename OT, bool REPAIR>
 __global__ __launch_bounds__(kBlock) void fwd_hist_kernel(
-    const uint16_t* __restrict__ Wt, const IT* __restrict__ indices, const OT* __restrict__ offsets,
+    const uint16_t* __restrict__ Wt, IT* __restrict__ indices, const OT* __restrict__ offsets,
     float* __restrict__ out, int64_t bag0, int32_t B, int32_t E, int32_t D, int64_t col_base,
-    int32_t out_width, int64_t N) {
+    int32_t out_width, int64_t N, int64_t* __restrict__ counts) {
   __shared__ __align__(16) uint16_t s_wT[kHistCols * kHistRows];            // [col][row]
   __shared__ __align__(16) float s_tile[kWavesPerBlock][kHistBags * kHistCols];
+  __shared__ int32_t s_off[kWavesPerBlock][kHistBags + 1];
   const int lane = lane_id();
   const int w = threadIdx.x >> 6;
-  for (int i = threadIdx.x; i < kHistCols * kHistRows; i += kBlock) {
-    const int col = i / kHistRows, row = i % kHistRows;
-    s_wT[i] = (row < E && col < D) ? Wt[static_cast<int64_t>(row) * D + col] : 0;
+  // the table, read row-major (coalesced, 4 elements a lane) and stored transposed
+  for (int i = threadIdx.x; i < kHistRows * (kHistCols / 4); i += kBlock) {
+    const int row = i / (kHistCols / 4), col = 4 * (i % (kHistCols / 4));
+    u32x2 v = {0u, 0u};
+    if (row < E && col < D) v = *reinterpret_cast<const u32x2*>(Wt + static_cast<int64_t>(row) * D + col);
+    s_wT[(col + 0) * kHistRows + row] = static_cast<uint16_t>(v.x);
+    s_wT[(col + 1) * kHistRows + row] = static_cast<uint16_t>(v.x >> 16);
+    s_wT[(col + 2) * kHistRows + row] = static_cast<uint16_t>(v.y);
+    s_wT[(col + 3) * kHistRows + row] = static_cast<uint16_t>(v.y >> 16);
   }
   __syncthreads();
   uint32_t* cnt = reinterpret_cast<uint32_t*>(s_tile[w]);
   float* otile = s_tile[w];
+  int32_t* off = s_off[w];
+  int64_t fixed = 0;
   const int64_t tiles = (static_cast<int64_t>(B) + kHistBags - 1) / kHistBags;
   for (int64_t tile = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + w; tile < tiles;
        tile += static_cast<int64_t>(gridDim.x) * kWavesPerBlock) {
     const int64_t b0 = tile * kHistBags;
     const int nbag = static_cast<int>(min<int64_t>(kHistBags, B - b0));
-    for (int i = lane; i < kHistBags * kHistRows; i += kWave) cnt[i] = 0u;
-    int64_t o = 0;
-    if (lane <= nbag) {
-      o = static_cast<int64_t>(offsets[bag0 + b0 + lane]);
-      o = min(max(o, static_cast<int64_t>(0)), N);
+    // the 17 offsets of the tile, clamped to [0, N] and made monotone, so that the
+    // tile's ids are one contiguous range [o0, o0 + n)
+    int32_t o = 0;
+    if (lane <= kHistBags) {
+      const int64_t v = static_cast<int64_t>(offsets[bag0 + b0 + min(lane, nbag)]);
+      o = static_cast<int32_t>(min(max(v, static_cast<int64_t>(0)), N));
     }
+    for (int d = 1; d < 32; d <<= 1) {
+      const int32_t u = __shfl_up(o, d);
+      if (lane >= d) o = max(o, u);
+    }
+    const int32_t o0 = read_lane(o, 0);
+    const int32_t n = read_lane(o, kHistBags) - o0;
+    if (lane <= kHistBags) off[lane] = o - o0;
+    for (int i = lane; i < kHistBags * kHistRows; i += kWave) cnt[i] = 0u;
     __builtin_amdgcn_wave_barrier();
-    for (int i = 0; i < nbag; ++i) {
-      const int64_t s = read_lane64(o, i);
-      const int64_t e = max(read_lane64(o, i + 1), s);
-      const int64_t eh = min(e, s + kHistHead);
-      for (int64_t j = s + lane; j < eh; j += kWave) {
-        const int64_t r = static_cast<int64_t>(indices[j]);
-        if (static_cast<uint64_t>(r) < static_cast<uint64_t>(E)) atomicAdd(&cnt[i * kHistRows + r], 1u);
+    // each bag's first 256 ids, read as one coalesced range with kHistLoads loads in
+    // flight per lane; an id's bag comes from a 4-step search of the offsets
+    for (int32_t j0 = 0; j0 < n; j0 += kHistLoads * kWave) {
+      int64_t r[kHistLoads];
+#pragma unroll
+      for (int u = 0; u < kHistLoads; ++u) {
+        const int32_t j = j0 + u * kWave + lane;
+        r[u] = j < n ? static_cast<int64_t>(indices[o0 + j]) : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < kHistLoads; ++u) {
+        const int32_t j = j0 + u * kWave + lane;
+        if (j < n) {
+          int b = 0;
+#pragma unroll
+          for (int step = 8; step > 0; step >>= 1)
+            if (off[b + step] <= j) b += step;
+          if (j - off[b] < kHistHead) {
+            int64_t row = r[u];
+            if (static_cast<uint64_t>(row) >= static_cast<uint64_t>(E)) {
+              if constexpr (REPAIR) {  // repaired to row 0, in place, and counted
+                indices[o0 + j] = 0;
+                ++fixed;
+                row = 0;
+              } else {
+                row = -1;  // contributes nothing
+              }
+            }
+            if (row >= 0) atomicAdd(&cnt[b * kHistRows + static_cast<int>(row)], 1u);
+          }
+        }
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -241,27 +284,37 @@ __global__ __launch_bounds__(kBlock) void fwd_hist_kernel(
       for (int q = 0; q < 4; ++q) a[s][q] = static_cast<_Float16>(static_cast<float>(cnt[base + q]));
     }
     __builtin_amdgcn_wave_barrier();
-    for (int n = 0; n < D / 16; ++n) {
+    for (int nt = 0; nt < D / 16; ++nt) {
       float4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         // B operand: lane l holds column 16n + l%16, rows 16s + 4(l/16) + [0, 4)
         const half4_t bf = *reinterpret_cast<const half4_t*>(
-            &s_wT[(16 * n + (lane & 15)) * kHistRows + 16 * s + 4 * (lane >> 4)]);
+            &s_wT[(16 * nt + (lane & 15)) * kHistRows + 16 * s + 4 * (lane >> 4)]);
         acc = __builtin_amdgcn_mfma_f32_16x16x16f16(a[s], bf, acc, 0, 0, 0);
       }
       // result: lane l holds column 16n + l%16 of bags 4(l/16) + [0, 4)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) otile[(4 * (lane >> 4) + q) * kHistCols + 16 * n + (lane & 15)] = acc[q];
+      for (int q = 0; q < 4; ++q) otile[(4 * (lane >> 4) + q) * kHistCols + 16 * nt + (lane & 15)] = acc[q];
     }
     __builtin_amdgcn_wave_barrier();
     // ids past the first 256 of a bag: gathered from the LDS copy of the table
     for (int i = 0; i < nbag; ++i) {
-      const int64_t s = read_lane64(o, i);
-      const int64_t e = max(read_lane64(o, i + 1), s);
-      for (int64_t j = s + kHistHead; j < e; ++j) {
-        const int64_t r = static_cast<int64_t>(indices[j]);
-        if (static_cast<uint64_t>(r) >= static_cast<uint64_t>(E)) continue;
+      const int32_t s = o0 + off[i], e = o0 + off[i + 1];
+      for (int32_t j = s + kHistHead; j < e; ++j) {
+        int64_t r = static_cast<int64_t>(indices[j]);
+        if (static_cast<uint64_t>(r) >= static_cast<uint64_t>(E)) {
+          if constexpr (REPAIR) {
+            __builtin_amdgcn_wave_barrier();
+            if (lane == 0) {
+              indices[j] = 0;
+              ++fixed;
+            }
+            r = 0;
+          } else {
+            continue;
+          }
+        }
         for (int col = lane; col < D; col += kWave)
           otile[i * kHistCols + col] += static_cast<float>(
               __builtin_bit_cast(_Float16, s_wT[col * kHistRows + r]));
@@ -275,6 +328,11 @@ __global__ __launch_bounds__(kBlock) void fwd_hist_kernel(
       store_f4(out + (b0 + i) * out_width + col_base + 4 * c4, v);
     }
     __builtin_amdgcn_wave_barrier();
+  }
+  if constexpr (REPAIR) {  // one atomic per wave
+    for (int msk = 1; msk < kWave; msk <<= 1) fixed += __shfl_xor(fixed, msk);
+    if (lane == 0 && fixed)
+      atomicAdd(reinterpret_cast<unsigned long long*>(counts), static_cast<unsigned long long>(fixed));
   }
 }
 
@@ -340,15 +398,20 @@ tbe_status gather_dispatch_idx(const tbe_tables* tb, const void* W, const IndexA
 
 template <typename IT, typename OT>
 tbe_status hist_go(const tbe_tables* tb, const void* W, const IndexArgs& ia, float* out,
-                   hipStream_t s) {
+                   int64_t* repair_counts, hipStream_t s) {
   const int64_t tiles = (static_cast<int64_t>(tb->B) + kHistBags - 1) / kHistBags;
   const int grid = grid_for(tiles);
   ProfScope ps("fwd_hist", s);
-  hipLaunchKernelGGL((fwd_hist_kernel<IT, OT>), dim3(grid), dim3(kBlock), 0, s,
-                     static_cast<const uint16_t*>(W) + tb->hist_w_base,
-                     static_cast<const IT*>(ia.indices), static_cast<const OT*>(ia.offsets), out,
-                     static_cast<int64_t>(tb->hist_table) * tb->B, tb->B, tb->hist_E, tb->hist_D,
-                     static_cast<int64_t>(tb->hist_col), tb->out_width, ia.N);
+#define TBE_HIST_LAUNCH(R)                                                                         \
+  hipLaunchKernelGGL((fwd_hist_kernel<IT, OT, R>), dim3(grid), dim3(kBlock), 0, s,                 \
+                     static_cast<const uint16_t*>(W) + tb->hist_w_base,                           \
+                     const_cast<IT*>(static_cast<const IT*>(ia.indices)),                         \
+                     static_cast<const OT*>(ia.offsets), out,                                     \
+                     static_cast<int64_t>(tb->hist_table) * tb->B, tb->B, tb->hist_E, tb->hist_D,   \
+                     static_cast<int64_t>(tb->hist_col), tb->out_width, ia.N, repair_counts)
+  if (repair_counts) TBE_HIST_LAUNCH(true);
+  else TBE_HIST_LAUNCH(false);
+#undef TBE_HIST_LAUNCH
   return check_launch("fwd_hist");
 }
 
@@ -367,14 +430,14 @@ tbe_status launch_forward_gather(const tbe_tables* tb, const void* W, const Inde
 }
 
 tbe_status launch_forward_hist(const tbe_tables* tb, const void* W, const IndexArgs& ia,
-                               float* out, hipStream_t s) {
+                               float* out, int64_t* rc, hipStream_t s) {
   if (tb->B == 0 || tb->hist_table < 0) return TBE_OK;
   if (ia.itype == TBE_I32) {
-    if (ia.otype == TBE_I32) return hist_go<int32_t, int32_t>(tb, W, ia, out, s);
-    return hist_go<int32_t, int64_t>(tb, W, ia, out, s);
+    if (ia.otype == TBE_I32) return hist_go<int32_t, int32_t>(tb, W, ia, out, rc, s);
+    return hist_go<int32_t, int64_t>(tb, W, ia, out, rc, s);
   }
-  if (ia.otype == TBE_I32) return hist_go<int64_t, int32_t>(tb, W, ia, out, s);
-  return hist_go<int64_t, int64_t>(tb, W, ia, out, s);
+  if (ia.otype == TBE_I32) return hist_go<int64_t, int32_t>(tb, W, ia, out, rc, s);
+  return hist_go<int64_t, int64_t>(tb, W, ia, out, rc, s);
 }
 
 }  // namespace tbe

@@ -85,8 +85,9 @@ tbe_status launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
 tbe_status launch_forward_gather(const tbe_tables* tb, const void* W, const IndexArgs& ia,
                                  const float* psw, float* out, int skip_table, int unroll,
                                  int64_t* repair_counts, hipStream_t s);
+// repair_counts != NULL: ids outside the table are repaired to 0 in place and counted there
 tbe_status launch_forward_hist(const tbe_tables* tb, const void* W, const IndexArgs& ia,
-                               float* out, hipStream_t s);
+                               float* out, int64_t* repair_counts, hipStream_t s);
 
 tbe_status launch_bounds(const tbe_tables* tb, void* indices, int itype, void* offsets, int otype,
                          int64_t N, int64_t* counts, void* ws, hipStream_t s);

@@ -292,18 +292,27 @@ __global__ __launch_bounds__(kBlock) void radix_downsweep(
       p[s] = valid ? pin[i] : 0u;
     }
     __builtin_amdgcn_wave_barrier();
+    // Stable rank of each key among the wave's keys of its digit: the lowest lane of
+    // each group of equal digits adds the group size to the wave's digit counter
+    // with one LDS atomic that returns the count before it (a wave's LDS operations
+    // execute in order, so the 16 atomics need no wait in between), then every lane
+    // adds the returned base, read from its group's lowest lane, to its place in
+    // the group.  r packs the place (bits 0-7) and the lowest lane (bits 8-15).
+    uint32_t base[kRadixItems];
 #pragma unroll
     for (int s = 0; s < kRadixItems; ++s) {
       const bool valid = wbase + s * kWave + lane < hi;
       const uint32_t d = (k[s] >> shift) & mask;
       const uint64_t peers = match_digit(d, bits, __ballot(valid));
-      const uint32_t prior = valid ? s_wcnt[w][d] : 0u;
-      r[s] = prior + __popcll(peers & lanemask_lt());
-      __builtin_amdgcn_wave_barrier();
-      if (valid && lane == __ffsll(static_cast<long long>(peers)) - 1)
-        s_wcnt[w][d] = prior + __popcll(peers);
-      __builtin_amdgcn_wave_barrier();
+      const int lead = __ffsll(static_cast<long long>(peers)) - 1;
+      base[s] = 0u;
+      if (valid && lane == lead) base[s] = atomicAdd(&s_wcnt[w][d], static_cast<uint32_t>(__popcll(peers)));
+      r[s] = static_cast<uint32_t>(__popcll(peers & lanemask_lt())) | (static_cast<uint32_t>(lead & 63) << 8);
     }
+#pragma unroll
+    for (int s = 0; s < kRadixItems; ++s)
+      r[s] = (r[s] & 0xffu) + static_cast<uint32_t>(__shfl(static_cast<int>(base[s]), static_cast<int>(r[s] >> 8)));
+    __builtin_amdgcn_wave_barrier();
     __syncthreads();
     for (int d = threadIdx.x; d < ndig; d += kBlock) {
       const uint32_t c0 = s_wcnt[0][d], c1 = s_wcnt[1][d], c2 = s_wcnt[2][d], c3 = s_wcnt[3][d];

@@ -196,8 +196,9 @@ tbe_status tbe_forward(const tbe_tables* tables, const void* weights, const void
  * step).  Same results as tbe_bounds_check followed by tbe_forward: offsets
  * and indices repaired in place by the same rules, error_counts [device, 2 x
  * int64] overwritten with {indices repaired, offsets changed}, out as in
- * tbe_forward.  When the histogram path is used, its ids are validated by the
- * standalone step instead.  workspace: tbe_bounds_check_workspace_bytes().
+ * tbe_forward.  When the histogram path is used, its kernel repairs that
+ * table's ids the same way while it counts them.  workspace:
+ * tbe_bounds_check_workspace_bytes().
  */
 tbe_status tbe_forward_repair(const tbe_tables* tables, const void* weights, void* indices,
                               int32_t index_type, void* offsets, int32_t offset_type,
