@@ -32,7 +32,7 @@ METRIC = "TBE fwd+bwd lookups/s and achieved HBM GB/s vs peak, 1 MI355X"
 HBM_PEAK_GBS = 8000.0
 KERNELS = ["bounds_offsets", "bounds_indices", "fwd_gather", "fwd_hist", "linearize",
            "radix_upsweep", "radix_scan", "radix_downsweep", "rle", "classify", "short_run",
-           "grad_accum", "long_apply"]
+           "grad_accum", "long_apply", "hist_bwd_partial", "hist_bwd_apply"]
 
 
 # sources each timed kernel is built from: its counters in profiles/ are valid only while
@@ -47,6 +47,7 @@ KERNEL_SOURCES = {
     "radix_upsweep": ["transpose.hip", "tbe_device.h"],
     "radix_downsweep": ["transpose.hip", "tbe_device.h"],
     "bounds_indices": ["bounds.hip", "tbe_device.h"],
+    "hist_bwd_partial": ["hist_backward.hip", "tbe_device.h"],
 }
 
 
@@ -79,61 +80,70 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def batch_stats(bt: ti.Batch, threshold=256, chunk=256):
-    """Host-side statistics of the drawn batch (from the inputs only)."""
+def batch_stats(bt: ti.Batch, hist_table: int, threshold=256, chunk=256):
+    """Host-side statistics of the drawn batch (from the inputs only), per table.  hist_table
+    (or -1): the table whose backward goes through the histogram kernels, not the runs."""
     idx = bt.indices.cpu().numpy().astype(np.int64)
     off = bt.offsets.cpu().numpy().astype(np.int64)
     B = bt.B
-    U = 0
-    short_lookups = 0
-    short_runs = 0
-    long_lookups = 0
-    long_runs = 0
-    chunks = 0
-    hottest = 0
+    per = []
     for t in range(bt.T):
-        c = np.bincount(idx[off[t * B]:off[(t + 1) * B]], minlength=bt.E[t])
+        lk = idx[off[t * B]:off[(t + 1) * B]]
+        c = np.bincount(lk, minlength=bt.E[t])
         c = c[c > 0]
-        U += c.size
-        hottest = max(hottest, int(c.max()) if c.size else 0)
         lg = c >= threshold
-        long_runs += int(lg.sum())
-        long_lookups += int(c[lg].sum())
-        short_runs += int((~lg).sum())
-        short_lookups += int(c[~lg].sum())
-        chunks += int(((c[lg] + chunk - 1) // chunk).sum())
-    return dict(N=int(idx.size), TB=bt.T * B, U=U, hottest=hottest, short_runs=short_runs,
-                short_lookups=short_lookups, long_runs=long_runs, long_lookups=long_lookups,
-                chunks=chunks)
+        per.append(dict(D=bt.D[t], N=int(lk.size), U=int(c.size), hottest=int(c.max()) if c.size else 0,
+                        long_runs=int(lg.sum()), long_lookups=int(c[lg].sum()),
+                        short_runs=int((~lg).sum()), short_lookups=int(c[~lg].sum()),
+                        chunks=int(((c[lg] + chunk - 1) // chunk).sum()), hist=t == hist_table))
+    tot = lambda k, only_runs=False: sum(p[k] for p in per if not (only_runs and p["hist"]))
+    return dict(N=int(idx.size), TB=bt.T * B, U=tot("U"), hottest=max(p["hottest"] for p in per),
+                short_runs=tot("short_runs", True), short_lookups=tot("short_lookups", True),
+                long_runs=tot("long_runs", True), long_lookups=tot("long_lookups", True),
+                chunks=tot("chunks", True), per_table=per)
 
 
-def algorithmic_bytes(bt: ti.Batch, st: dict, passes: int):
-    """What each kernel must move per launch (no credit for cache reuse)."""
+def algorithmic_bytes(bt: ti.Batch, st: dict):
+    """What each kernel must move per launch (no credit for cache reuse), summed over tables
+    with their own D."""
     s_w = bt.weights.element_size()
     s_i = bt.indices.element_size()
     s_o = bt.offsets.element_size()
-    D = bt.D[0]
-    N, TB, U = st["N"], st["TB"], st["U"]
-    return {
-        # per lookup: index + row; per bag: offset + output row
-        "fwd_gather": N * (s_i + D * s_w) + TB * (s_o + D * 4),
+    s_p = 4 if bt.psw is not None else 0          # per-sample weight per lookup
+    B = bt.B
+    per = st["per_table"]
+    gen = [p for p in per if not p["hist"]]       # tables the generic kernels serve
+    hst = [p for p in per if p["hist"]]
+    runs_N = sum(p["N"] for p in gen)              # keys the sort covers
+    U = sum(p["U"] for p in gen)
+    by = {
+        # per lookup: index (+ weight) + row; per bag: offset + output row
+        "fwd_gather": sum(p["N"] * (s_i + s_p + p["D"] * s_w) + B * (s_o + p["D"] * 4) for p in gen),
         # per lookup: index read, key + payload written; per bag: offset
-        "linearize": N * (s_i + 8) + TB * s_o,
+        "linearize": st["N"] * s_i + runs_N * 8 + st["TB"] * s_o,
         # per pass: keys + payloads read and written
-        "radix_downsweep": N * 16,
-        "radix_upsweep": N * 4,
-        # per lookup of a short run: payload + fp32 gradient row; per short run: descriptor,
-        # weight row read + write, Adagrad state read + write
-        "short_run": st["short_lookups"] * (4 + D * 4) + st["short_runs"] * (16 + 2 * D * s_w + 8),
-        # per lookup of a long run: payload + gradient row; per chunk: partial row written
-        "grad_accum": st["long_lookups"] * (4 + D * 4) + st["chunks"] * (8 + D * 4),
+        "radix_downsweep": runs_N * 16,
+        "radix_upsweep": runs_N * 4,
+        # per lookup of a short run: payload (+ weight) + fp32 gradient row; per short run:
+        # descriptor, weight row read + write, Adagrad state read + write
+        "short_run": sum(p["short_lookups"] * (4 + s_p + p["D"] * 4)
+                         + p["short_runs"] * (16 + 2 * p["D"] * s_w + 8) for p in gen),
+        # per lookup of a long run: payload (+ weight) + gradient row; per chunk: partial row
+        "grad_accum": sum(p["long_lookups"] * (4 + s_p + p["D"] * 4) + p["chunks"] * (8 + p["D"] * 4)
+                          for p in gen),
         # per chunk: partial row read; per long run: descriptor, weight row r/w, state r/w
-        "long_apply": st["chunks"] * D * 4 + st["long_runs"] * (20 + 2 * D * s_w + 8),
-        "bounds_indices": N * s_i,
-        "bounds_offsets": 3 * (TB + 1) * s_o,
-        "rle": 3 * N * 4 + U * 8,
+        "long_apply": sum(p["chunks"] * p["D"] * 4 + p["long_runs"] * (20 + 2 * p["D"] * s_w + 8)
+                          for p in gen),
+        "bounds_indices": st["N"] * s_i,
+        "bounds_offsets": 3 * (st["TB"] + 1) * s_o,
+        "rle": 3 * runs_N * 4 + U * 8,
         "classify": U * 8 + U * 16,
     }
+    for p in hst:
+        # per lookup: index; per bag: offset + output (forward) or gradient (backward) row
+        by["fwd_hist"] = p["N"] * s_i + B * (s_o + p["D"] * 4) + 64 * p["D"] * s_w
+        by["hist_bwd_partial"] = p["N"] * s_i + B * (s_o + p["D"] * 4)
+    return by
 
 
 def calib_copy():
@@ -149,26 +159,35 @@ def calib_copy():
 
 
 def cpu_baseline(spec: ti.BatchSpec, seed: int):
-    """The CPU oracle, single-threaded, on a bounded sample of the same workload: 2 of the 32
-    tables with every bag (same B, L and Zipf recipe).  Returns lookups/s of forward+backward."""
+    """The CPU oracle, single-threaded, on a bounded sample of the same workload: 2 of its
+    tables with every bag (same B, L, id and weight recipe).  Returns lookups/s of
+    forward + backward."""
     import oracle
     sample = ti.scaled(spec, T=2, name_suffix=" (2-table sample)")
     bt = ti.make_batch(sample, seed, device="cuda")
     a = dict(E=np.array(bt.E), D=np.array(bt.D), W=bt.weights.double().cpu().numpy(),
              idx=bt.indices.long().cpu().numpy(), off=bt.offsets.long().cpu().numpy(),
-             grad=bt.grad_out.double().cpu().numpy(), mom=bt.momentum.double().cpu().numpy())
+             grad=bt.grad_out.double().cpu().numpy(),
+             psw=None if bt.psw is None else bt.psw.double().cpu().numpy(),
+             mom=None if bt.momentum is None else bt.momentum.double().cpu().numpy())
+    odt = {torch.float32: oracle.F32, torch.float16: oracle.F16, torch.bfloat16: oracle.BF16}[bt.w_dtype]
     del bt
     torch.cuda.empty_cache()
+    ada = spec.optimizer == "rowwise_adagrad"
     t0 = time.perf_counter()
-    oracle.forward(sample.T, sample.B, a["E"], a["D"], a["W"], a["idx"], a["off"])
-    oracle.backward(sample.T, sample.B, a["E"], a["D"], oracle.F16, a["W"], a["idx"], a["off"], None,
-                    a["grad"], oracle.ROWWISE_ADAGRAD, oracle.f32_literal(spec.lr),
-                    oracle.f32_literal(spec.eps), a["mom"])
+    oracle.forward(sample.T, sample.B, a["E"], a["D"], a["W"], a["idx"], a["off"], a["psw"])
+    if ada:
+        oracle.backward(sample.T, sample.B, a["E"], a["D"], odt, a["W"], a["idx"], a["off"], a["psw"],
+                        a["grad"], oracle.ROWWISE_ADAGRAD, oracle.f32_literal(spec.lr),
+                        oracle.f32_literal(spec.eps), a["mom"])
+    else:
+        oracle.backward(sample.T, sample.B, a["E"], a["D"], odt, a["W"], a["idx"], a["off"], a["psw"],
+                        a["grad"], oracle.SGD, oracle.f32_literal(spec.lr))
     dt = time.perf_counter() - t0
     n = int(a["idx"].size)
     return {"value": n / dt, "unit": "lookups/s", "cores": 1, "kind": "oracle",
-            "sample": f"2 of 32 tables, all {sample.B} bags: {n} lookups, forward + transpose + "
-                      f"row-wise Adagrad backward in fp64, single thread, {dt:.1f} s"}
+            "sample": f"2 of {spec.T} tables, all {sample.B} bags: {n} lookups, forward + transpose + "
+                      f"{spec.optimizer} backward in fp64, single thread, {dt:.1f} s"}
 
 
 def main():
@@ -204,9 +223,11 @@ def main():
     bt = ti.make_batch(spec, seed, device=dev)
     torch.cuda.synchronize()
     log(f"generated {spec.name}: {bt.num_indices} lookups in {time.perf_counter() - t0:.1f} s")
-    st = batch_stats(bt)
-    log(f"batch: {st}")
     tables = tbe.Tables(bt.E, bt.D, bt.B, bt.w_dtype, device=dev, pooling_hint=spec.pooling_hint)
+    # the histogram kernels take that table when there are no per-sample weights
+    hist_table = tables.c.hist_table if bt.psw is None else -1
+    st = batch_stats(bt, hist_table)
+    log("batch: " + ", ".join(f"{k} {v}" for k, v in st.items() if k != "per_table"))
     out = torch.empty(bt.B, sum(bt.D), dtype=torch.float32, device=dev)
     weighted = bt.psw is not None
     ws = tbe.workspace(tbe.tbe_backward_workspace_bytes(tables, bt.num_indices, weighted), dev)
@@ -240,13 +261,14 @@ def main():
     torch.cuda.synchronize()
     # which kernel dominates: one profiled step per kernel (outside the timed region), with the
     # transpose in the backward call so that no two kernels overlap and each time is its own
-    per_kernel = {}
+    per_kernel, launches_per_step = {}, {}
     for k in ([] if args.dominant else KERNELS):
         tbe.tbe_profile_select(k)
         step(hoist=False)
         n, ms = tbe.tbe_profile_read()
         if n:
             per_kernel[k] = ms
+            launches_per_step[k] = n
     tbe.tbe_profile_select(None)
     dominant = args.dominant or max(per_kernel, key=per_kernel.get)
     log("one step per kernel (ms): " + ", ".join(f"{k} {v:.3f}" for k, v in per_kernel.items()))
@@ -262,12 +284,12 @@ def main():
     tbe.tbe_profile_select(None)
     ms_per_step = elapsed * 1e3 / args.steps
     N = st["N"]
-    ab = algorithmic_bytes(bt, st, 3)
+    ab = algorithmic_bytes(bt, st)
     dom_avg_ms = dom_ms / max(launches, 1)
     dom_bytes = ab.get(dominant, 0)
     achieved = dom_bytes / (dom_avg_ms * 1e-3) / 1e9 if dom_avg_ms > 0 else 0.0
-    step_bytes = sum(ab[k] for k in ("fwd_gather", "linearize", "short_run", "grad_accum", "long_apply")) \
-        + 3 * ab["radix_downsweep"] + 3 * ab["radix_upsweep"]
+    # every kernel of the step, times its launches per step (radix: one per pass)
+    step_bytes = sum(ab.get(k, 0) * n for k, n in launches_per_step.items())
     res = {
         "metric": METRIC,
         "value": N / (ms_per_step * 1e-3),
@@ -294,7 +316,7 @@ def main():
                      "traffic": measured_traffic(dominant) if args.workload == "skewed" else None,
                      "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_ms": dom_avg_ms,
                      "launches_timed": launches},
-        "step_algorithmic_GBps": step_bytes / (ms_per_step * 1e-3) / 1e9,
+        "step_algorithmic_GBps": step_bytes / (ms_per_step * 1e-3) / 1e9 if step_bytes else None,
         # event-timed per kernel, one step each with nothing overlapping (transpose in the backward)
         "kernel_ms_one_step": per_kernel,
     }

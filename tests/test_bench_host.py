@@ -1,0 +1,42 @@
+"""Host logic of bench.py: batch statistics and algorithmic bytes on a small batch (CPU)."""
+import numpy as np
+import torch
+
+import bench
+import tbe_inputs as ti
+
+
+def _spec():
+    tables = (ti.TableSpec(64, 128, ("fixed", 100)),
+              ti.TableSpec(500, 32, ("poisson", 30.0, None, None), ("zipf", 1.2, None)))
+    return ti.BatchSpec("bench host", tables, B=300, w_dtype=torch.float16, w_range=0.05,
+                        pooling_hint=(100, 30))
+
+
+def test_batch_stats_partition_the_lookups():
+    bt = ti.make_batch(_spec(), 3, device="cpu")
+    st = bench.batch_stats(bt, hist_table=-1, threshold=20, chunk=8)
+    idx, off = bt.indices.numpy(), bt.offsets.numpy()
+    assert st["N"] == idx.size and st["TB"] == 2 * 300
+    assert st["short_lookups"] + st["long_lookups"] == idx.size
+    uniq = sum(np.unique(idx[off[t * 300]:off[(t + 1) * 300]]).size for t in range(2))
+    assert st["U"] == uniq == st["short_runs"] + st["long_runs"]
+    # table 0: 30000 lookups over 64 rows, every row long (>= 20)
+    p0 = st["per_table"][0]
+    assert p0["long_lookups"] == 30000 and p0["short_runs"] == 0
+    # with table 0 on the histogram kernels, the run statistics cover table 1 only
+    sh = bench.batch_stats(bt, hist_table=0, threshold=20, chunk=8)
+    p1 = sh["per_table"][1]
+    assert sh["short_lookups"] + sh["long_lookups"] == p1["N"]
+
+
+def test_algorithmic_bytes_by_hand():
+    bt = ti.make_batch(_spec(), 4, device="cpu")
+    st = bench.batch_stats(bt, hist_table=0)
+    ab = bench.algorithmic_bytes(bt, st)
+    p1 = st["per_table"][1]
+    # generic forward: table 1 only; 8-byte ids, 2-byte weights, fp32 output rows of 32
+    assert ab["fwd_gather"] == p1["N"] * (8 + 32 * 2) + 300 * (8 + 32 * 4)
+    # the histogram table: its ids, one offset and one 128-wide fp32 row per bag, the table once
+    assert ab["fwd_hist"] == 30000 * 8 + 300 * (8 + 128 * 4) + 64 * 128 * 2
+    assert ab["radix_downsweep"] == p1["N"] * 16
