@@ -108,6 +108,7 @@ Config resolve_config(const tbe_config* c) {
   r.bag_windows = c->bag_windows;
   r.fused_long = c->fused_long;
   r.pretransposed = c->pretransposed;
+  r.bags_per_wave = (c->bags_per_wave >= 1 && c->bags_per_wave <= 64) ? c->bags_per_wave : 0;
   return r;
 }
 
@@ -268,6 +269,7 @@ void tbe_config_default(tbe_config* cfg) {
   cfg->bag_windows = 1;
   cfg->fused_long = 0;
   cfg->pretransposed = 0;
+  cfg->bags_per_wave = 0;
 }
 
 int64_t tbe_meta_entries(int32_t T) { return T >= 0 ? static_cast<int64_t>(TBE_META_FIELDS) * (T + 1) : 0; }
@@ -359,7 +361,7 @@ tbe_status tbe_forward(const tbe_tables* tables, const void* weights, const void
   if (hist >= 0)
     if (tbe_status st = launch_forward_hist(tables, weights, ia, out, nullptr, s)) return st;
   return launch_forward_gather(tables, weights, ia, per_sample_weights, out, hist, cfg.fwd_unroll,
-                               nullptr, s);
+                               cfg.bags_per_wave, nullptr, s);
 }
 
 // Forward after the offsets are final: the histogram table (if used) and the
@@ -371,7 +373,8 @@ static tbe_status forward_body(const tbe_tables* tables, const void* weights, co
   // both kernels repair the ids they read (the histogram table's, everyone else's)
   if (hist >= 0)
     if (tbe_status st = launch_forward_hist(tables, weights, ia, out, error_counts, s)) return st;
-  return launch_forward_gather(tables, weights, ia, psw, out, hist, cfg.fwd_unroll, error_counts, s);
+  return launch_forward_gather(tables, weights, ia, psw, out, hist, cfg.fwd_unroll, cfg.bags_per_wave,
+                               error_counts, s);
 }
 
 static tbe_status check_bounds_ws(const tbe_tables* tables, const void* workspace, size_t bytes) {

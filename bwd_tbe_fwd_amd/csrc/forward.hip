@@ -87,7 +87,7 @@ __global__ __launch_bounds__(kBlock) void fwd_gather_kernel(
     const typename Fmt<DT>::S* __restrict__ W, IT* __restrict__ indices,
     const OT* __restrict__ offsets, const float* __restrict__ psw, float* __restrict__ out,
     const int64_t* __restrict__ meta, int32_t skip_t, int32_t n_tables, int32_t B,
-    int32_t out_width, int64_t N, int64_t* __restrict__ counts) {
+    int32_t out_width, int64_t N, int32_t group, int64_t* __restrict__ counts) {
   const int lane = lane_id();
   const int64_t wave = (static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x) >> 6;
   const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * kBlock) >> 6;
@@ -95,9 +95,9 @@ __global__ __launch_bounds__(kBlock) void fwd_gather_kernel(
   int cur_t = -1;
   TableMeta m{};
   int64_t fixed = 0;
-  for (int64_t base = wave * kWave; base < slots; base += nwaves * kWave) {
-    // one bag per lane: its table, batch row and clamped [start, end)
-    const int64_t slot = base + lane;
+  for (int64_t base = wave * group; base < slots; base += nwaves * group) {
+    // one bag per lane (group <= 64 of them): its table, batch row and clamped [start, end)
+    const int64_t slot = lane < group ? base + lane : slots;
     int64_t s = 0, e = 0;
     int32_t bt = 0, bb = 0;
     if (slot < slots) {
@@ -110,7 +110,7 @@ __global__ __launch_bounds__(kBlock) void fwd_gather_kernel(
       s = min(max(s, static_cast<int64_t>(0)), N);
       e = min(max(e, s), N);
     }
-    const int nb = static_cast<int>(min<int64_t>(kWave, slots - base));
+    const int nb = static_cast<int>(min<int64_t>(group, slots - base));
     // ids of the first bag; each later bag's first ids are fetched one bag ahead
     int64_t nxt_id = -1;
     float nxt_w = 0.f;
@@ -346,9 +346,9 @@ int grid_for(int64_t work_waves) {
 
 template <int DT, typename IT, typename OT, bool PSW, int VEC, typename ACC>
 tbe_status gather_go(const tbe_tables* tb, const void* W, const IndexArgs& ia, const float* psw,
-                     float* out, int skip, int nt, int unroll, int64_t* repair_counts, hipStream_t s) {
+                     float* out, int skip, int nt, int unroll, int group, int64_t* repair_counts, hipStream_t s) {
   const int64_t slots = static_cast<int64_t>(nt) * tb->B;
-  const int grid = grid_for((slots + kWave - 1) / kWave);
+  const int grid = grid_for((slots + group - 1) / group);
   using S = typename Fmt<DT>::S;
   ProfScope ps("fwd_gather", s);
 #define TBE_FWD_LAUNCH(U, R)                                                                     \
@@ -356,7 +356,7 @@ tbe_status gather_go(const tbe_tables* tb, const void* W, const IndexArgs& ia, c
                      0, s, static_cast<const S*>(W),                                                \
                      const_cast<IT*>(static_cast<const IT*>(ia.indices)),                           \
                      static_cast<const OT*>(ia.offsets), psw, out, tb->meta, skip, nt, tb->B,         \
-                     tb->out_width, ia.N, repair_counts)
+                     tb->out_width, ia.N, group, repair_counts)
   if (repair_counts) TBE_FWD_LAUNCH(8, true);
   else if (unroll <= 2) TBE_FWD_LAUNCH(2, false);
   else if (unroll <= 4) TBE_FWD_LAUNCH(4, false);
@@ -367,33 +367,33 @@ tbe_status gather_go(const tbe_tables* tb, const void* W, const IndexArgs& ia, c
 
 template <int DT, typename IT, typename OT>
 tbe_status gather_dispatch_psw(const tbe_tables* tb, const void* W, const IndexArgs& ia,
-                               const float* psw, float* out, int skip, int nt, int unroll,
+                               const float* psw, float* out, int skip, int nt, int unroll, int group,
                                int64_t* rc, hipStream_t s) {
   if constexpr (DT == 0) {
-    if (psw) return gather_go<DT, IT, OT, true, 4, double>(tb, W, ia, psw, out, skip, nt, unroll, rc, s);
-    return gather_go<DT, IT, OT, false, 4, double>(tb, W, ia, psw, out, skip, nt, unroll, rc, s);
+    if (psw) return gather_go<DT, IT, OT, true, 4, double>(tb, W, ia, psw, out, skip, nt, unroll, group, rc, s);
+    return gather_go<DT, IT, OT, false, 4, double>(tb, W, ia, psw, out, skip, nt, unroll, group, rc, s);
   } else {
     if (tb->all_D_mult8) {
-      if (psw) return gather_go<DT, IT, OT, true, 8, float>(tb, W, ia, psw, out, skip, nt, unroll, rc, s);
-      return gather_go<DT, IT, OT, false, 8, float>(tb, W, ia, psw, out, skip, nt, unroll, rc, s);
+      if (psw) return gather_go<DT, IT, OT, true, 8, float>(tb, W, ia, psw, out, skip, nt, unroll, group, rc, s);
+      return gather_go<DT, IT, OT, false, 8, float>(tb, W, ia, psw, out, skip, nt, unroll, group, rc, s);
     }
-    if (psw) return gather_go<DT, IT, OT, true, 4, float>(tb, W, ia, psw, out, skip, nt, unroll, rc, s);
-    return gather_go<DT, IT, OT, false, 4, float>(tb, W, ia, psw, out, skip, nt, unroll, rc, s);
+    if (psw) return gather_go<DT, IT, OT, true, 4, float>(tb, W, ia, psw, out, skip, nt, unroll, group, rc, s);
+    return gather_go<DT, IT, OT, false, 4, float>(tb, W, ia, psw, out, skip, nt, unroll, group, rc, s);
   }
 }
 
 template <int DT>
 tbe_status gather_dispatch_idx(const tbe_tables* tb, const void* W, const IndexArgs& ia,
-                               const float* psw, float* out, int skip, int nt, int unroll,
+                               const float* psw, float* out, int skip, int nt, int unroll, int group,
                                int64_t* rc, hipStream_t s) {
   if (ia.itype == TBE_I32) {
     if (ia.otype == TBE_I32)
-      return gather_dispatch_psw<DT, int32_t, int32_t>(tb, W, ia, psw, out, skip, nt, unroll, rc, s);
-    return gather_dispatch_psw<DT, int32_t, int64_t>(tb, W, ia, psw, out, skip, nt, unroll, rc, s);
+      return gather_dispatch_psw<DT, int32_t, int32_t>(tb, W, ia, psw, out, skip, nt, unroll, group, rc, s);
+    return gather_dispatch_psw<DT, int32_t, int64_t>(tb, W, ia, psw, out, skip, nt, unroll, group, rc, s);
   }
   if (ia.otype == TBE_I32)
-    return gather_dispatch_psw<DT, int64_t, int32_t>(tb, W, ia, psw, out, skip, nt, unroll, rc, s);
-  return gather_dispatch_psw<DT, int64_t, int64_t>(tb, W, ia, psw, out, skip, nt, unroll, rc, s);
+    return gather_dispatch_psw<DT, int64_t, int32_t>(tb, W, ia, psw, out, skip, nt, unroll, group, rc, s);
+  return gather_dispatch_psw<DT, int64_t, int64_t>(tb, W, ia, psw, out, skip, nt, unroll, group, rc, s);
 }
 
 template <typename IT, typename OT>
@@ -419,13 +419,21 @@ tbe_status hist_go(const tbe_tables* tb, const void* W, const IndexArgs& ia, flo
 
 tbe_status launch_forward_gather(const tbe_tables* tb, const void* W, const IndexArgs& ia,
                                  const float* psw, float* out, int skip_table,
-                                 int unroll, int64_t* rc, hipStream_t s) {
+                                 int unroll, int group, int64_t* rc, hipStream_t s) {
   const int n_tables = skip_table >= 0 ? tb->T - 1 : tb->T;
   if (n_tables <= 0 || tb->B == 0) return TBE_OK;
+  if (group < 1 || group > kWave) {
+    // automatic: about 8 steps per wave of a full grid, so that waves that drew heavy
+    // bags (wide tables, long bags) do not set the kernel's end
+    const int64_t slots = static_cast<int64_t>(n_tables) * tb->B;
+    const int64_t full = static_cast<int64_t>(device_cu_count()) * 8 * kWavesPerBlock;
+    group = 8;
+    while (group < kWave && slots >= static_cast<int64_t>(2 * group) * full * 8) group *= 2;
+  }
   switch (tb->w_dtype) {
-    case TBE_F32: return gather_dispatch_idx<0>(tb, W, ia, psw, out, skip_table, n_tables, unroll, rc, s);
-    case TBE_F16: return gather_dispatch_idx<1>(tb, W, ia, psw, out, skip_table, n_tables, unroll, rc, s);
-    default: return gather_dispatch_idx<2>(tb, W, ia, psw, out, skip_table, n_tables, unroll, rc, s);
+    case TBE_F32: return gather_dispatch_idx<0>(tb, W, ia, psw, out, skip_table, n_tables, unroll, group, rc, s);
+    case TBE_F16: return gather_dispatch_idx<1>(tb, W, ia, psw, out, skip_table, n_tables, unroll, group, rc, s);
+    default: return gather_dispatch_idx<2>(tb, W, ia, psw, out, skip_table, n_tables, unroll, group, rc, s);
   }
 }
 

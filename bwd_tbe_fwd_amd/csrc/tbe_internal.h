@@ -41,7 +41,7 @@ constexpr int kRadixTile = kBlock * kRadixItems;      // 4096 keys
 
 struct Config {
   int threshold, chunk, hist_enable, fwd_unroll, bwd_unroll, sort_blocks, bag_windows, fused_long;
-  int pretransposed;
+  int pretransposed, bags_per_wave;
 };
 Config resolve_config(const tbe_config* c);
 
@@ -84,7 +84,7 @@ tbe_status launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
 
 tbe_status launch_forward_gather(const tbe_tables* tb, const void* W, const IndexArgs& ia,
                                  const float* psw, float* out, int skip_table, int unroll,
-                                 int64_t* repair_counts, hipStream_t s);
+                                 int bags_per_wave, int64_t* repair_counts, hipStream_t s);
 // repair_counts != NULL: ids outside the table are repaired to 0 in place and counted there
 tbe_status launch_forward_hist(const tbe_tables* tb, const void* W, const IndexArgs& ia,
                                float* out, int64_t* repair_counts, hipStream_t s);

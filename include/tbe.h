@@ -113,6 +113,9 @@ typedef struct {
                               (blog section 4, problem 5).  0: chunk kernel + apply kernel (default) */
   int32_t pretransposed;   /* backward only: 1 = the workspace already holds this batch's transpose,
                               written by tbe_forward_hoisted; the backward skips its own (default 0) */
+  int32_t bags_per_wave;   /* forward: consecutive bags a wave takes per grid step, their offsets read
+                              in one load ("bags per program", blog section 2), 1..64; 0 (default):
+                              the power of two in [8, 64] that gives every wave about 8 steps */
 } tbe_config;
 
 /* Device-side view of the transpose, for inspection by tests (tbe_transpose). */

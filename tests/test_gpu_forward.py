@@ -95,6 +95,19 @@ def test_forward_unroll_knob_is_bitwise_neutral():
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[1], outs[2])
 
 
+@pytest.mark.parametrize("name", ["skewed", "mixed"])
+def test_forward_bags_per_wave_knob_is_bitwise_neutral(name):
+    """Each bag is pooled by one wave in the same order whatever the number of bags a wave
+    takes per step (ragged: B is not a multiple of any of them)."""
+    bt = ti.make_batch(small_spec(name), 10)
+    db = DevBatch(bt)
+    outs = [db.forward(tbe.make_config(bags_per_wave=g)).cpu() for g in (64, 1, 7, 16, 33)]
+    for o in outs[1:]:
+        assert torch.equal(outs[0], o)
+    ref, ref_abs = _oracle_forward(bt)
+    check_forward(outs[0].numpy(), ref, ref_abs, bt.w_dtype == torch.float32, name)
+
+
 def _integer_weights(bt, lo=-8, hi=8, seed=0):
     g = torch.Generator().manual_seed(seed)
     bt.weights = torch.randint(lo, hi + 1, bt.weights.shape, generator=g).to(bt.w_dtype)
