@@ -109,7 +109,14 @@ Config resolve_config(const tbe_config* c) {
   r.fused_long = c->fused_long;
   r.pretransposed = c->pretransposed;
   r.bags_per_wave = (c->bags_per_wave >= 1 && c->bags_per_wave <= 64) ? c->bags_per_wave : 0;
+  r.bwd_streams = c->bwd_streams == 2 ? 2 : 1;
   return r;
+}
+
+// The table the histogram kernels take in this call, or -1: the eligible table, when
+// the histogram paths are on and there are no per-sample weights.
+int histogram_table(const tbe_tables* tb, const Config& cfg, const float* psw) {
+  return (cfg.hist_enable && !psw && tb->hist_table >= 0) ? tb->hist_table : -1;
 }
 
 namespace {
@@ -175,7 +182,7 @@ BwdLayout bwd_layout(const tbe_tables* tb, int64_t N, int weighted, const Config
     L.chunk_order = c.take(L.cap_chunk * 4);
     L.unit_cnt = c.take(static_cast<size_t>(L.units) * 4);
   }
-  if (tb->hist_table >= 0 && !weighted) {
+  if (cfg.hist_enable && tb->hist_table >= 0 && !weighted) {
     L.hist_partial = c.take(static_cast<size_t>(kHistBwdBlocks) * 64 * 128 * 4);
     L.hist_count = c.take(static_cast<size_t>(kHistBwdBlocks) * 64 * 4);
   }
@@ -270,6 +277,7 @@ void tbe_config_default(tbe_config* cfg) {
   cfg->fused_long = 0;
   cfg->pretransposed = 0;
   cfg->bags_per_wave = 0;
+  cfg->bwd_streams = 1;
 }
 
 int64_t tbe_meta_entries(int32_t T) { return T >= 0 ? static_cast<int64_t>(TBE_META_FIELDS) * (T + 1) : 0; }
@@ -357,7 +365,7 @@ tbe_status tbe_forward(const tbe_tables* tables, const void* weights, const void
   const Config cfg = resolve_config(config);
   IndexArgs ia{indices, index_type, offsets, offset_type, num_indices};
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int hist = (cfg.hist_enable && !per_sample_weights && tables->hist_table >= 0) ? tables->hist_table : -1;
+  const int hist = histogram_table(tables, cfg, per_sample_weights);
   if (hist >= 0)
     if (tbe_status st = launch_forward_hist(tables, weights, ia, out, nullptr, s)) return st;
   return launch_forward_gather(tables, weights, ia, per_sample_weights, out, hist, cfg.fwd_unroll,
@@ -369,7 +377,7 @@ tbe_status tbe_forward(const tbe_tables* tables, const void* weights, const void
 static tbe_status forward_body(const tbe_tables* tables, const void* weights, const IndexArgs& ia,
                                const float* psw, float* out, int64_t* error_counts, const Config& cfg,
                                hipStream_t s) {
-  const int hist = (cfg.hist_enable && !psw && tables->hist_table >= 0) ? tables->hist_table : -1;
+  const int hist = histogram_table(tables, cfg, psw);
   // both kernels repair the ids they read (the histogram table's, everyone else's)
   if (hist >= 0)
     if (tbe_status st = launch_forward_hist(tables, weights, ia, out, error_counts, s)) return st;
@@ -411,7 +419,7 @@ tbe_status tbe_forward_repair(const tbe_tables* tables, const void* weights, voi
 }
 
 // ---------------------------------------------------------------------------
-// second stream for the hoisted transpose (one per device, made on first use)
+// second stream (hoisted transpose, concurrent long runs)
 // ---------------------------------------------------------------------------
 namespace {
 struct SideStream {
@@ -421,14 +429,16 @@ struct SideStream {
 constexpr int kMaxDevices = 64;
 std::mutex g_side_mu;
 SideStream g_side[kMaxDevices];
+}  // namespace
 
-// Returns the current device's side stream with g_side_mu held by the caller.
-tbe_status side_stream(SideStream** out) {
+Fork::Fork(hipStream_t s) : main_(s) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
     set_error("hipGetDevice failed or device id out of range");
-    return TBE_ERR_HIP;
+    st_ = TBE_ERR_HIP;
+    return;
   }
+  g_side_mu.lock();
   SideStream& ss = g_side[dev];
   if (!ss.stream) {
     // default priority; does not synchronize with the null stream
@@ -436,13 +446,37 @@ tbe_status side_stream(SideStream** out) {
         hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
         hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess) {
       set_error("could not create the side stream or its events");
-      return TBE_ERR_HIP;
+      st_ = TBE_ERR_HIP;
+      ss.stream = nullptr;
+      g_side_mu.unlock();
+      return;
     }
   }
-  *out = &ss;
-  return TBE_OK;
+  if (hipEventRecord(ss.fork, s) != hipSuccess || hipStreamWaitEvent(ss.stream, ss.fork, 0) != hipSuccess) {
+    set_error("fork to the side stream failed");
+    st_ = TBE_ERR_HIP;
+    g_side_mu.unlock();
+    return;
+  }
+  side_ = ss.stream;
+  done_ = ss.join;
+  joined_ = false;
 }
-}  // namespace
+
+tbe_status Fork::join() {
+  if (joined_) return st_;
+  joined_ = true;
+  const bool ok = hipEventRecord(static_cast<hipEvent_t>(done_), side_) == hipSuccess &&
+                  hipStreamWaitEvent(main_, static_cast<hipEvent_t>(done_), 0) == hipSuccess;
+  g_side_mu.unlock();
+  if (!ok) {
+    set_error("join of the side stream failed");
+    st_ = TBE_ERR_HIP;
+  }
+  return st_;
+}
+
+Fork::~Fork() { join(); }
 
 tbe_status tbe_forward_hoisted(const tbe_tables* tables, const void* weights, void* indices,
                                int32_t index_type, void* offsets, int32_t offset_type,
@@ -481,26 +515,17 @@ tbe_status tbe_forward_hoisted(const tbe_tables* tables, const void* weights, vo
                           : TBE_OK;
     return forward_body(tables, weights, ia, per_sample_weights, out, error_counts, cfg, s);
   }
-  const int hist = (cfg.hist_enable && !per_sample_weights && tables->hist_table >= 0) ? tables->hist_table : -1;
-  std::lock_guard<std::mutex> lk(g_side_mu);
-  SideStream* ss = nullptr;
-  if (tbe_status st = side_stream(&ss)) return st;
-  if (hipEventRecord(ss->fork, s) != hipSuccess || hipStreamWaitEvent(ss->stream, ss->fork, 0) != hipSuccess) {
-    set_error("fork to the side stream failed");
-    return TBE_ERR_HIP;
-  }
+  const int hist = histogram_table(tables, cfg, per_sample_weights);
+  Fork fork(s);
+  if (tbe_status st = fork.status()) return st;
   int final_buf = 0;
   const tbe_status st_t = launch_transpose(tables, ia, weighted, static_cast<char*>(bwd_workspace), L,
-                                           cfg, hist, error_counts ? 1 : 0, &final_buf, ss->stream);
-  // join even after a failed launch, so that the streams stay ordered
-  const bool rec_ok = hipEventRecord(ss->join, ss->stream) == hipSuccess;
+                                           cfg, hist, error_counts ? 1 : 0, &final_buf, fork.side());
   const tbe_status st_f = st_t ? TBE_OK
                                : forward_body(tables, weights, ia, per_sample_weights, out, error_counts, cfg, s);
-  if (!rec_ok || hipStreamWaitEvent(s, ss->join, 0) != hipSuccess) {
-    set_error("join of the side stream failed");
-    return TBE_ERR_HIP;
-  }
-  return st_t ? st_t : st_f;
+  // joined even after a failed launch, so that the streams stay ordered
+  const tbe_status st_j = fork.join();
+  return st_t ? st_t : (st_f ? st_f : st_j);
 }
 
 size_t tbe_backward_workspace_bytes(const tbe_tables* tables, int64_t num_indices, int32_t weighted,
@@ -531,7 +556,7 @@ static tbe_status backward_common(const tbe_tables* tables, void* weights, float
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   // the small table's rows are updated from per-bag counts x gradient (MFMA) instead of runs
-  const int hist = (cfg.hist_enable && !psw && tables->hist_table >= 0) ? tables->hist_table : -1;
+  const int hist = histogram_table(tables, cfg, psw);
   // pretransposed: tbe_forward_hoisted left the sorted runs in the workspace; the
   // radix passes alternate buffers starting from buffer 0
   int final_buf = L.passes & 1;
@@ -540,7 +565,16 @@ static tbe_status backward_common(const tbe_tables* tables, void* weights, float
   if (hist >= 0)
     if (tbe_status st = launch_hist_backward(tables, weights, momentum, opt, ia, grad_out, lr, eps, ws, L, s))
       return st;
-  return launch_backward_update(tables, weights, momentum, opt, psw, grad_out, lr, eps, ws, L, final_buf, cfg, s);
+  if (cfg.bwd_streams < 2 || L.cap_long == 0)
+    return launch_backward_update(tables, weights, momentum, opt, psw, grad_out, lr, eps, ws, L,
+                                  final_buf, cfg, s, s);
+  // long runs on a second stream, concurrent with the short runs (disjoint rows)
+  Fork fork(s);
+  if (tbe_status st = fork.status()) return st;
+  const tbe_status st = launch_backward_update(tables, weights, momentum, opt, psw, grad_out, lr, eps,
+                                               ws, L, final_buf, cfg, s, fork.side());
+  const tbe_status st_j = fork.join();
+  return st ? st : st_j;
 }
 
 tbe_status tbe_backward_sgd(const tbe_tables* tables, void* weights, const void* indices,

@@ -167,15 +167,15 @@ tbe_status launch_grad_accum(const tbe_tables* tb, const float* psw, const float
 tbe_status launch_backward_update(const tbe_tables* tb, void* W, float* momentum, int opt,
                                   const float* psw, const float* grad_out, float lr, float eps,
                                   char* ws, const BwdLayout& L, int final_buf, const Config& cfg,
-                                  hipStream_t s) {
+                                  hipStream_t s, hipStream_t s_long) {
   if (L.N == 0) return TBE_OK;
   switch (tb->w_dtype) {
     case TBE_F32:
-      return launch_short_and_apply<0>(tb, W, momentum, opt, psw, grad_out, lr, eps, ws, L, final_buf, cfg, s);
+      return launch_short_and_apply<0>(tb, W, momentum, opt, psw, grad_out, lr, eps, ws, L, final_buf, cfg, s, s_long);
     case TBE_F16:
-      return launch_short_and_apply<1>(tb, W, momentum, opt, psw, grad_out, lr, eps, ws, L, final_buf, cfg, s);
+      return launch_short_and_apply<1>(tb, W, momentum, opt, psw, grad_out, lr, eps, ws, L, final_buf, cfg, s, s_long);
     default:
-      return launch_short_and_apply<2>(tb, W, momentum, opt, psw, grad_out, lr, eps, ws, L, final_buf, cfg, s);
+      return launch_short_and_apply<2>(tb, W, momentum, opt, psw, grad_out, lr, eps, ws, L, final_buf, cfg, s, s_long);
   }
 }
 

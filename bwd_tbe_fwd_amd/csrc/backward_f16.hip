@@ -4,5 +4,5 @@
 namespace tbe {
 template tbe_status launch_short_and_apply<1>(const tbe_tables*, void*, float*, int, const float*,
                                               const float*, float, float, char*, const BwdLayout&,
-                                              int, const Config&, hipStream_t);
+                                              int, const Config&, hipStream_t, hipStream_t);
 }  // namespace tbe

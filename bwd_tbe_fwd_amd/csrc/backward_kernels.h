@@ -384,6 +384,6 @@ template <int DT>
 tbe_status launch_short_and_apply(const tbe_tables* tb, void* W, float* momentum, int opt,
                                   const float* psw, const float* grad_out, float lr, float eps,
                                   char* ws, const BwdLayout& L, int final_buf, const Config& cfg,
-                                  hipStream_t s);
+                                  hipStream_t s, hipStream_t s_long);
 
 }  // namespace tbe

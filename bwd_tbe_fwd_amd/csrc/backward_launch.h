@@ -92,7 +92,7 @@ template <int DT>
 tbe_status launch_short_and_apply(const tbe_tables* tb, void* W, float* momentum, int opt,
                                   const float* psw, const float* grad_out, float lr, float eps,
                                   char* ws, const BwdLayout& L, int final_buf, const Config& cfg,
-                                  hipStream_t s) {
+                                  hipStream_t s, hipStream_t s_long) {
   const int32_t* counters = reinterpret_cast<const int32_t*>(ws + L.counters);
   const uint32_t* pay = reinterpret_cast<const uint32_t*>(ws + L.pay[final_buf]);
   const uint32_t* bag_of = psw ? reinterpret_cast<const uint32_t*>(ws + L.bag_of) : nullptr;
@@ -110,6 +110,8 @@ tbe_status launch_short_and_apply(const tbe_tables* tb, void* W, float* momentum
     if (st) return st;
   }
   if (L.cap_long == 0) return TBE_OK;
+  // long runs touch other rows than short runs: s_long may be a second stream
+  s = s_long;
   if (cfg.fused_long) {
     const uint32_t* order = nullptr;
     if (tbe_status st = launch_chunk_order(tb, psw, ws, L, final_buf, cfg, &order, s)) return st;

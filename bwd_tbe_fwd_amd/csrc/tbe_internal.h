@@ -41,7 +41,7 @@ constexpr int kRadixTile = kBlock * kRadixItems;      // 4096 keys
 
 struct Config {
   int threshold, chunk, hist_enable, fwd_unroll, bwd_unroll, sort_blocks, bag_windows, fused_long;
-  int pretransposed, bags_per_wave;
+  int pretransposed, bags_per_wave, bwd_streams;
 };
 Config resolve_config(const tbe_config* c);
 
@@ -115,9 +115,29 @@ tbe_status launch_hist_backward(const tbe_tables* tb, void* W, float* momentum, 
 tbe_status launch_chunk_order(const tbe_tables* tb, const float* psw, char* ws, const BwdLayout& L,
                               int final_buf, const Config& cfg, const uint32_t** order, hipStream_t s);
 
+// short runs on s, long runs (chunks, apply) on s_long (s itself, or a fork of it)
 tbe_status launch_backward_update(const tbe_tables* tb, void* W, float* momentum, int opt,
                                   const float* psw, const float* grad_out, float lr, float eps,
                                   char* ws, const BwdLayout& L, int final_buf, const Config& cfg,
-                                  hipStream_t s);
+                                  hipStream_t s, hipStream_t s_long);
+
+// A second stream forked from s: work enqueued on side() starts after everything
+// enqueued on s before the fork, and join() makes later work on s wait for it.
+// One per device, made on first use, default priority; a Fork holds a lock until
+// it is joined, so forks of concurrent calls on one device take turns.
+class Fork {
+ public:
+  explicit Fork(hipStream_t s);
+  ~Fork();
+  tbe_status status() const { return st_; }
+  hipStream_t side() const { return side_; }
+  tbe_status join();
+
+ private:
+  hipStream_t main_, side_ = nullptr;
+  void* done_ = nullptr;  // hipEvent_t
+  tbe_status st_ = TBE_OK;
+  bool joined_ = true;
+};
 
 }  // namespace tbe

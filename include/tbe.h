@@ -116,6 +116,8 @@ typedef struct {
   int32_t bags_per_wave;   /* forward: consecutive bags a wave takes per grid step, their offsets read
                               in one load ("bags per program", blog section 2), 1..64; 0 (default):
                               the power of two in [8, 64] that gives every wave about 8 steps */
+  int32_t bwd_streams;     /* backward: 2 = long runs (chunks, apply) on the library's second stream,
+                              concurrent with the short runs; 1 = one stream (default 1) */
 } tbe_config;
 
 /* Device-side view of the transpose, for inspection by tests (tbe_transpose). */

@@ -288,3 +288,17 @@ def test_long_chunks_grouped_by_window(name, windows):
     assert torch.equal(W1.cpu().view(torch.uint8), W0.cpu().view(torch.uint8))
     if m1 is not None:
         assert torch.equal(m1.cpu(), m0.cpu())
+
+
+@pytest.mark.parametrize("name", ["skewed", "mixed", "histogram", "tiny"])
+@pytest.mark.parametrize("fused", [0, 1])
+def test_long_runs_on_second_stream_bitwise_same(name, fused):
+    """bwd_streams = 2 runs the long-run chunks and their apply on the library's second
+    stream, concurrent with the short runs: the same bits as one stream."""
+    bt = ti.make_batch(small_spec(name), 73)
+    kw = dict(long_threshold=16, chunk=8, fused_long=fused)
+    _, W2, m2, _ = run_and_check(bt, tbe.make_config(bwd_streams=2, **kw), what=f"{name} two streams")
+    _, W1, m1, _ = run_and_check(bt, tbe.make_config(bwd_streams=1, **kw), what=f"{name} one stream")
+    assert torch.equal(W2.cpu().view(torch.uint8), W1.cpu().view(torch.uint8))
+    if m2 is not None:
+        assert torch.equal(m2.cpu(), m1.cpu())
