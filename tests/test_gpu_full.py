@@ -1,4 +1,5 @@
-"""Parity at the full workload sizes, in the launch configuration the benchmark times.
+"""Parity at the full workload sizes, in the launch configuration the benchmark times (id
+repair fused into the pooling, the backward's transpose hoisted into the forward call).
 
 The oracle cannot redo an 84M-lookup batch in seconds, so at these sizes:
   * forward:   sampled bags (random, longest, empty, first/last) are recomputed one by one
@@ -58,7 +59,17 @@ def test_full_forward_sampled_bags(n):
     bt = db.bt
     out = torch.full((bt.B, sum(bt.D)), float("nan"), dtype=torch.float32, device="cuda")
     tbe.tbe_forward(db.tables, db.W, db.idx, db.off, db.psw, out)
+    # the benchmark's launch configuration: id repair fused into the pooling and the backward's
+    # transpose on the second stream; valid inputs, so nothing is repaired and out is the same
+    out_b = torch.full_like(out, float("nan"))
+    counts = torch.full((2,), -1, dtype=torch.int64, device="cuda")
+    bws = tbe.workspace(tbe.tbe_bounds_check_workspace_bytes(db.tables))
+    ws = db.workspace()
+    tbe.tbe_forward_hoisted(db.tables, db.W, db.idx, db.off, db.psw, out_b, counts, bws, ws)
     torch.cuda.synchronize()
+    assert counts.cpu().tolist() == [0, 0]
+    assert torch.equal(out.view(torch.int32), out_b.view(torch.int32))
+    del ws, bws, out_b
     rng = np.random.default_rng(len(n))
     off = h["off"]
     lens = np.diff(off)
@@ -167,13 +178,21 @@ def test_full_backward_sampled_rows(n):
     m0 = None if db.mom is None else db.mom.clone()
     ws = db.workspace()
     lr, eps = oracle.f32_literal(spec.lr), oracle.f32_literal(spec.eps)
+    # the benchmark's launch configuration: fused repair, transpose hoisted into the forward
+    # call (second stream), backward with pretransposed runs
+    out = torch.empty((bt.B, sum(bt.D)), dtype=torch.float32, device="cuda")
+    err_counts = torch.full((2,), -1, dtype=torch.int64, device="cuda")
+    bws = tbe.workspace(tbe.tbe_bounds_check_workspace_bytes(db.tables))
+    tbe.tbe_forward_hoisted(db.tables, db.W, db.idx, db.off, db.psw, out, err_counts, bws, ws)
+    cfg = tbe.make_config(pretransposed=1)
     if spec.optimizer == "sgd":
-        tbe.tbe_backward_sgd(db.tables, db.W, db.idx, db.off, db.psw, db.grad, lr, ws)
+        tbe.tbe_backward_sgd(db.tables, db.W, db.idx, db.off, db.psw, db.grad, lr, ws, cfg)
     else:
         tbe.tbe_backward_rowwise_adagrad(db.tables, db.W, db.mom, db.idx, db.off, db.psw, db.grad,
-                                         lr, eps, ws)
+                                         lr, eps, ws, cfg)
     torch.cuda.synchronize()
-    del ws
+    assert err_counts.cpu().tolist() == [0, 0]
+    del ws, bws, out
     # every untouched row of every table is bit-identical
     pos = 0
     for t in range(bt.T):
