@@ -20,7 +20,7 @@ import torch
 import bwd_tbe_fwd_amd as tbe
 import oracle
 import tbe_inputs as ti
-from gpu_util import ODT, DevBatch, check_forward, check_momentum, check_weights, flush_print
+from gpu_util import ODT, DevBatch, check_forward, check_momentum, check_weights, flush_print, step_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -223,3 +223,77 @@ def test_full_backward_sampled_rows(n):
             check_momentum(mg, res, np.array([D], float), np.array([(res["g_abs"] ** 2).sum()]),
                            f"{n} state ({t},{r})")
     flush_print(f"{n}: {len(samples)} sampled rows and all untouched rows match")
+
+
+def test_max_total_rows():
+    """The largest row space the 32-bit keys allow: 2^31 - 2 rows in all (a 17 GB fp16 table of
+    2^31 - 1002 rows next to a 1000-row one), ids spread over the whole range.  Keys up to
+    2^31 - 3, four radix passes, the sentinel 2^31 - 2; forward bags, every touched row and a
+    sample of untouched rows checked against the oracle."""
+    _cache.clear()
+    gc.collect()
+    torch.cuda.empty_cache()
+    E0 = 2 ** 31 - 2 - 1000
+    spec = ti.BatchSpec("max rows", (ti.TableSpec(E0, 4, ("poisson", 5.0, None, None)),
+                                     ti.TableSpec(1000, 8, ("fixed", 3))),
+                        B=2000, w_dtype=torch.float16, w_range=0.5, optimizer="rowwise_adagrad")
+    flush_print("drawing the max-rows batch (17 GB of weights)")
+    bt = ti.make_batch(spec, 91, device="cuda")
+    db = DevBatch.__new__(DevBatch)
+    db.bt, db.device = bt, "cuda"
+    db.tables = tbe.Tables(bt.E, bt.D, bt.B, bt.w_dtype, device="cuda")
+    assert db.tables.c.total_rows == 2 ** 31 - 2
+    db.W, db.idx, db.off, db.psw, db.grad, db.mom = (bt.weights, bt.indices, bt.offsets, None,
+                                                      bt.grad_out, bt.momentum)
+    idx, off = bt.indices.long().cpu().numpy(), bt.offsets.long().cpu().numpy()
+    assert idx[:off[bt.B]].max() > 2 ** 30   # high ids are exercised
+    # transpose: four passes, keys follow their lookups, (key, position) increasing
+    ws = db.workspace(None, True)
+    view = tbe.tbe_transpose(db.tables, db.idx, db.off, True, ws)
+    torch.cuda.synchronize()
+    assert view.radix_passes == 4
+    N = bt.num_indices
+    keys = tbe.device_view(view.sorted_keys, N, torch.int32, ws).cpu().numpy().view(np.uint32).astype(np.int64)
+    pos = tbe.device_view(view.sorted_payload, N, torch.int32, ws).cpu().numpy().view(np.uint32).astype(np.int64)
+    del ws
+    bag_of = np.repeat(np.arange(bt.T * bt.B, dtype=np.int64), np.diff(off))
+    rowbase = np.array([0, E0, E0 + 1000], dtype=np.int64)
+    assert np.array_equal(keys, (rowbase[bag_of // bt.B] + idx)[pos])
+    assert np.all(np.diff(keys) * (N + 1) + np.diff(pos) > 0)
+    # forward, every bag of both tables (few lookups): the oracle on the touched rows
+    out = torch.full((bt.B, 12), float("nan"), device="cuda")
+    tbe.tbe_forward(db.tables, db.W, db.idx, db.off, None, out)
+    torch.cuda.synchronize()
+    got = out.double().cpu().numpy()
+    cols = [0, 4, 12]
+    for t in range(2):
+        s, e = off[t * bt.B], off[(t + 1) * bt.B]
+        uniq, local = np.unique(idx[s:e], return_inverse=True)
+        Wsub = table_rows(db, t, uniq)
+        o = off[t * bt.B:(t + 1) * bt.B + 1] - s
+        ref, ref_abs = oracle.forward(1, bt.B, [uniq.size], [bt.D[t]], Wsub, local, o)
+        check_forward(got[:, cols[t]:cols[t + 1]], ref, ref_abs, False, f"max rows table {t}")
+    # backward: every touched row of table 0, against the oracle on its own lookups
+    s0, e0 = off[0], off[bt.B]
+    uniq, local = np.unique(idx[s0:e0], return_inverse=True)
+    W_before = table_rows(db, 0, uniq)
+    m_before = db.mom[torch.as_tensor(uniq, device="cuda")].double().cpu().numpy()
+    free = np.setdiff1d(np.random.default_rng(0).integers(0, E0, 64), uniq)
+    W_free = table_rows(db, 0, free)
+    ws = db.workspace()
+    lr, eps = oracle.f32_literal(spec.lr), oracle.f32_literal(spec.eps)
+    tbe.tbe_backward_rowwise_adagrad(db.tables, db.W, db.mom, db.idx, db.off, None, db.grad, lr, eps, ws)
+    torch.cuda.synchronize()
+    del ws
+    g0 = db.grad[:, 0:4].double().cpu().numpy()
+    bag0 = np.repeat(np.arange(bt.B), np.diff(off[:bt.B + 1]))
+    # one oracle call over table 0 restricted to its touched rows (renumbered 0..U-1)
+    r = oracle.backward(1, bt.B, [uniq.size], [4], oracle.F16, W_before, local,
+                        off[:bt.B + 1] - s0, None, g0, oracle.ROWWISE_ADAGRAD, lr, eps, m_before)
+    W_after = torch.from_numpy(table_rows(db, 0, uniq).ravel()).to(torch.float16)
+    check_weights(W_after, r, torch.float16, step_bound(r, [uniq.size], [4], lr, eps, True), "max rows")
+    assert np.array_equal(table_rows(db, 0, free), W_free)
+    assert bag0.size == e0 - s0
+    del bt, db
+    gc.collect()
+    torch.cuda.empty_cache()
