@@ -228,7 +228,8 @@ tbe_status check_index_args(const tbe_tables* tb, const void* indices, int itype
                             int otype, int64_t N) {
   if (itype != TBE_I32 && itype != TBE_I64) { set_error("bad index type %d", itype); return TBE_ERR_ARG; }
   if (otype != TBE_I32 && otype != TBE_I64) { set_error("bad offset type %d", otype); return TBE_ERR_ARG; }
-  if (N < 0 || N >= (1ll << 31)) { set_error("num_indices %lld outside [0, 2^31)", (long long)N); return TBE_ERR_UNSUPPORTED; }
+  // positions are 32-bit in the kernels, with room for a step of a few hundred past the end
+  if (N < 0 || N > TBE_MAX_LOOKUPS) { set_error("num_indices %lld outside [0, 2^31 - 4096]", (long long)N); return TBE_ERR_UNSUPPORTED; }
   if (N > 0 && !indices) { set_error("indices is NULL"); return TBE_ERR_ARG; }
   if (!offsets) { set_error("offsets is NULL"); return TBE_ERR_ARG; }
   if (itype == TBE_I32 && N > 0 && (reinterpret_cast<uintptr_t>(indices) & 3)) { set_error("indices misaligned"); return TBE_ERR_ARG; }

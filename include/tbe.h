@@ -32,7 +32,7 @@
  *    sum_{t'<t} D_t'.
  *  - Limits: 1 <= T; 0 <= B; 4 <= D_t <= 1024 with D_t % 4 == 0;
  *    sum_t E_t < 2^31 - 1 (linearized row ids are 32-bit); number of lookups
- *    < 2^31; T*B < 2^31.
+ *    <= TBE_MAX_LOOKUPS = 2^31 - 4096; T*B < 2^31.
  *  - Invalid input with bounds checking off: an index outside [0, E_t)
  *    contributes nothing to the forward and nothing to the backward, and no
  *    memory outside the weights is touched; the pages leave this case to an
@@ -64,6 +64,7 @@ typedef enum {
 } tbe_status;
 
 #define TBE_MAX_D 1024
+#define TBE_MAX_LOOKUPS 2147479552LL /* 2^31 - 4096 */
 #define TBE_NUM_BUCKETS 9   /* short-run buckets next_pow2(D) = 4, 8, ..., 1024 */
 #define TBE_META_FIELDS 4   /* per table: row base, weight base, column base, D */
 

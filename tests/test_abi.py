@@ -123,3 +123,19 @@ def test_workspace_histogram_table_partials():
     d = tbe.tbe_backward_workspace_bytes(hist, n, False) - tbe.tbe_backward_workspace_bytes(plain, n, False)
     assert extra <= d < extra + 1024
     assert tbe.tbe_backward_workspace_bytes(hist, n, True) == tbe.tbe_backward_workspace_bytes(plain, n, True)
+
+
+def test_lookup_count_limit():
+    """At most 2^31 - 4096 lookups (32-bit positions with room for a step past the end)."""
+    t = tbe.Tables([10], [8], 4, torch.float32, device=None)
+    t.c.meta = 256
+    L = tbe.lib()
+    top = 2 ** 31 - 4096
+    for n in (top + 1, 2 ** 31, -1):
+        st = L.tbe_forward(t.ref, None, ctypes.c_void_p(4096), 1, ctypes.c_void_p(4096), 1, n, None,
+                           None, None, None)
+        assert st == 2 and b"num_indices" in L.tbe_last_error(), n
+    # at the limit the same call gets past the count check (and stops at the missing weights)
+    st = L.tbe_forward(t.ref, None, ctypes.c_void_p(4096), 1, ctypes.c_void_p(4096), 1, top, None,
+                       None, None, None)
+    assert b"num_indices" not in L.tbe_last_error()

@@ -297,3 +297,59 @@ def test_max_total_rows():
     del bt, db
     gc.collect()
     torch.cuda.empty_cache()
+
+
+def test_max_lookups():
+    """The largest lookup count the ABI accepts, 2^31 - 4096 (one table of 2^20 rows, 524287
+    bags of 4096 int32 ids): sampled bags of the forward, run and chunk counts of the
+    transpose, and sampled rows of the summed gradient (SGD, lr = -1, zero fp32 weights)."""
+    _cache.clear()
+    gc.collect()
+    torch.cuda.empty_cache()
+    E, L, B = 2 ** 20, 4096, 2 ** 19 - 1
+    spec = ti.BatchSpec("max lookups", (ti.TableSpec(E, 4, ("fixed", L)),), B=B,
+                        w_dtype=torch.float32, w_range=0.5, itype=torch.int32, otype=torch.int64,
+                        optimizer="sgd")
+    flush_print("drawing the max-lookups batch (2^31 - 4096 int32 ids)")
+    bt = ti.make_batch(spec, 93, device="cuda")
+    N = bt.num_indices
+    assert N == 2 ** 31 - 4096
+    tables = tbe.Tables(bt.E, bt.D, bt.B, bt.w_dtype, device="cuda")
+    idx, off = bt.indices, bt.offsets
+    # forward: sampled bags against the oracle
+    out = torch.full((B, 4), float("nan"), device="cuda")
+    tbe.tbe_forward(tables, bt.weights, idx, off, None, out)
+    torch.cuda.synchronize()
+    W = bt.weights.view(E, 4)
+    rng = np.random.default_rng(7)
+    for b in [0, B - 1] + rng.integers(0, B, 20).tolist():
+        ids = idx[b * L:(b + 1) * L].long().cpu().numpy()
+        uniq, local = np.unique(ids, return_inverse=True)
+        ref, ref_abs = oracle.forward(1, 1, [uniq.size], [4], W[torch.as_tensor(uniq, device="cuda")].double().cpu().numpy(),
+                                      local, [0, L])
+        check_forward(out[b:b + 1].double().cpu().numpy(), ref, ref_abs, True, f"max lookups bag {b}")
+    del out
+    # transpose counters against a histogram of the ids
+    counts = torch.bincount(idx.long(), minlength=E)
+    ws = tbe.workspace(tbe.tbe_backward_workspace_bytes(tables, N, False))
+    view = tbe.tbe_transpose(tables, idx, off, False, ws)
+    torch.cuda.synchronize()
+    cnt = tbe.device_view(view.counters, 16, torch.int32, ws).cpu().numpy()
+    c = counts[counts > 0]
+    assert int(cnt[tbe.COUNTER_RUNS]) == c.numel()
+    assert int(cnt[tbe.COUNTER_LONG]) == int((c >= 256).sum())
+    assert int(cnt[tbe.COUNTER_CHUNKS]) == int(((c[c >= 256] + 255) // 256).sum())
+    # backward: sampled rows' summed gradient
+    bt.weights.zero_()
+    tbe.tbe_backward_sgd(tables, bt.weights, idx, off, None, bt.grad_out, -1.0, ws)
+    torch.cuda.synchronize()
+    del ws
+    for r in rng.integers(0, E, 12).tolist():
+        pos = (idx == r).nonzero().flatten()
+        g = bt.grad_out[pos // L].double().cpu().numpy()
+        res = oracle.backward(1, g.shape[0], [1], [4], oracle.F32, np.zeros(4), np.zeros(g.shape[0], np.int64),
+                              np.arange(g.shape[0] + 1), None, g, oracle.SGD, -1.0)
+        check_weights(bt.weights.view(E, 4)[r].cpu(), res, torch.float32, res["g_abs"], f"max lookups row {r}")
+    del bt, counts, tables
+    gc.collect()
+    torch.cuda.empty_cache()
