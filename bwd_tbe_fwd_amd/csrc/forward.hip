@@ -15,9 +15,11 @@
 // elements, fp32: 4) or 8-byte vector loads, so one wave instruction fetches
 // 64/(D/VEC) rows; UNROLL such instructions are issued before any is summed.
 // The bag's ids are loaded coalesced, one per lane, and handed to the row
-// groups with lane shuffles; the 64 bags a wave walks in a row have their
-// offsets fetched in one coalesced load.  Per-group partial sums are combined
-// with xor shuffles and one group writes the output row.
+// groups with lane shuffles; the consecutive bags a wave takes per grid step
+// (up to 64, the bags-per-wave knob) have their offsets fetched in one
+// coalesced load.  Per-group partial sums are combined with xor shuffles and
+// one group writes the output row.  With the fused bounds check (REPAIR), an
+// id outside its table is read as row 0, rewritten to 0 in place and counted.
 #include "tbe_device.h"
 #include "tbe_internal.h"
 
@@ -178,14 +180,16 @@ __global__ __launch_bounds__(kBlock) void fwd_gather_kernel(
 // ---------------------------------------------------------------------------
 // histogram + MFMA path for one small table (E <= 64, 64 <= D <= 128, fp16)
 // ---------------------------------------------------------------------------
-// One wave owns 16 consecutive bags (one 16-row MFMA tile).  The wave counts
-// each bag's first 256 ids into an LDS histogram (16 x 64), turns it into the
-// fp16 A operand (counts <= 256 are exact in fp16), and multiplies it by the
-// table held transposed in LDS as the B operand with v_mfma_f32_16x16x16_f16
-// (fp32 accumulation).  The products count * w are exact in fp32; only the
-// accumulation rounds.  Ids beyond the first 256 of a bag are gathered and
-// added to the tile; the finished 16 x D tile leaves through LDS as 16-byte
-// row-contiguous stores.
+// One wave owns 16 consecutive bags (one 16-row MFMA tile).  Their ids are one
+// contiguous range, read coalesced with several loads in flight; the wave
+// counts each bag's first 256 ids into an LDS histogram (16 x 64), turns it
+// into the fp16 A operand (counts <= 256 are exact in fp16), and multiplies it
+// by the table held transposed in LDS as the B operand with
+// v_mfma_f32_16x16x16_f16 (fp32 accumulation).  The products count * w are
+// exact in fp32; only the accumulation rounds.  Ids beyond the first 256 of a
+// bag are gathered and added to the tile; the finished 16 x D tile leaves
+// through LDS as 16-byte row-contiguous stores.  With REPAIR, ids outside the
+// table are repaired to 0 in place and counted, as in the gather.
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
