@@ -158,6 +158,32 @@ def calib_copy():
     print(json.dumps({"calib_copy_bytes_read": n, "calib_copy_bytes_written": n, "launches": 3}))
 
 
+def copy_peak_gbps(n: int = 1 << 30, reps: int = 5) -> float:
+    """What a plain streaming copy reaches on this GPU (the library's 16-byte-per-lane copy
+    of 1 GiB, read + write bytes over the event-timed average)."""
+    a = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    tbe.tbe_calibration_copy(a, b, n)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        tbe.tbe_calibration_copy(a, b, n)
+    e1.record()
+    torch.cuda.synchronize()
+    return 2 * n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+
+def host_cpu() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(spec: ti.BatchSpec, seed: int):
     """The CPU oracle, single-threaded, on a bounded sample of the same workload: 2 of its
     tables with every bag (same B, L, id and weight recipe).  Returns lookups/s of
@@ -187,7 +213,8 @@ def cpu_baseline(spec: ti.BatchSpec, seed: int):
     n = int(a["idx"].size)
     return {"value": n / dt, "unit": "lookups/s", "cores": 1, "kind": "oracle",
             "sample": f"2 of {spec.T} tables, all {sample.B} bags: {n} lookups, forward + transpose + "
-                      f"{spec.optimizer} backward in fp64, single thread, {dt:.1f} s"}
+                      f"{spec.optimizer} backward in fp64, single thread, {dt:.1f} s",
+            "host": f"{host_cpu()}, {os.cpu_count()} logical CPUs visible"}
 
 
 def main():
@@ -237,8 +264,10 @@ def main():
     if bt.momentum is None:
         bt.momentum = torch.zeros(sum(bt.E), dtype=torch.float32, device=dev)
 
-    def step(hoist=args.hoist == "on"):
+    def step(hoist=args.hoist == "on", events=None):
         bcfg = tbe.make_config(pretransposed=1) if hoist else None
+        if events:
+            events[0].record()
         if args.bounds == "standalone":
             tbe.tbe_bounds_check(tables, bt.indices, bt.offsets, counts, bws)
         repair = args.bounds == "fused"
@@ -249,12 +278,16 @@ def main():
             tbe.tbe_forward_repair(tables, bt.weights, bt.indices, bt.offsets, bt.psw, out, counts, bws)
         else:
             tbe.tbe_forward(tables, bt.weights, bt.indices, bt.offsets, bt.psw, out)
+        if events:
+            events[1].record()
         if spec.optimizer == "sgd":
             tbe.tbe_backward_sgd(tables, bt.weights, bt.indices, bt.offsets, bt.psw, bt.grad_out,
                                  lr, ws, bcfg)
         else:
             tbe.tbe_backward_rowwise_adagrad(tables, bt.weights, bt.momentum, bt.indices, bt.offsets,
                                              bt.psw, bt.grad_out, lr, eps, ws, bcfg)
+        if events:
+            events[2].record()
 
     for _ in range(args.warmup):
         step()
@@ -274,15 +307,20 @@ def main():
     log("one step per kernel (ms): " + ", ".join(f"{k} {v:.3f}" for k, v in per_kernel.items()))
     # timed region; the dominant kernel's launches are bracketed by HIP events on its stream
     tbe.tbe_profile_select(dominant)
+    # events on the calls' stream split each step into its forward and backward calls
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        step(events=ev[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     launches, dom_ms = tbe.tbe_profile_read()
     tbe.tbe_profile_select(None)
     ms_per_step = elapsed * 1e3 / args.steps
+    fwd_ms = float(np.median([a.elapsed_time(b) for a, b, _ in ev]))
+    bwd_ms = float(np.median([b.elapsed_time(c) for _, b, c in ev]))
     N = st["N"]
     ab = algorithmic_bytes(bt, st)
     dom_avg_ms = dom_ms / max(launches, 1)
@@ -317,6 +355,13 @@ def main():
                      "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_ms": dom_avg_ms,
                      "launches_timed": launches},
         "step_algorithmic_GBps": step_bytes / (ms_per_step * 1e-3) / 1e9 if step_bytes else None,
+        # the whole step's algorithmic bytes at the HBM peak, over the measured step time
+        "step_roofline_frac": step_bytes / (HBM_PEAK_GBS * 1e9) / (ms_per_step * 1e-3) if step_bytes else None,
+        # medians over the timed steps, HIP events around each call (the forward call holds the
+        # hoisted transpose)
+        "forward_call_ms": fwd_ms, "backward_call_ms": bwd_ms,
+        "forward_lookups_per_s": N / (fwd_ms * 1e-3), "backward_lookups_per_s": N / (bwd_ms * 1e-3),
+        "copy_peak_GBps": copy_peak_gbps(),
         # event-timed per kernel, one step each with nothing overlapping (transpose in the backward)
         "kernel_ms_one_step": per_kernel,
     }
