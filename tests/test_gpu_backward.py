@@ -302,3 +302,22 @@ def test_long_runs_on_second_stream_bitwise_same(name, fused):
     assert torch.equal(W2.cpu().view(torch.uint8), W1.cpu().view(torch.uint8))
     if m2 is not None:
         assert torch.equal(m2.cpu(), m1.cpu())
+
+
+def test_more_tables_than_the_lds_table_cache():
+    """2100 tables (past the 2048 the classifier keeps in LDS): forward, transpose and a
+    row-wise Adagrad step against the oracle, with widths 4 .. 64 and a few long runs."""
+    D = (4, 8, 12, 16, 32, 64)
+    tables = tuple(ti.TableSpec(40 + (t % 7), D[t % len(D)], ("poisson", 3.0, None, None),
+                                ("zipf", 1.3, None) if t % 50 == 0 else ("uniform",))
+                   for t in range(2100))
+    spec = ti.BatchSpec("2100 tables", tables, B=90, w_dtype=torch.float16, w_range=0.5,
+                        optimizer="rowwise_adagrad")
+    bt = ti.make_batch(spec, 97)
+    db = DevBatch(bt)
+    out = db.forward()
+    a = host_arrays(bt)
+    ref, ref_abs = oracle.forward(a["T"], a["B"], a["E"], a["D"], a["W"], a["idx"], a["off"])
+    from gpu_util import check_forward
+    check_forward(out.cpu().numpy(), ref, ref_abs, False, "2100 tables forward")
+    run_and_check(bt, tbe.make_config(long_threshold=32, chunk=16), what="2100 tables")
