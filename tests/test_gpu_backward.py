@@ -321,3 +321,22 @@ def test_more_tables_than_the_lds_table_cache():
     from gpu_util import check_forward
     check_forward(out.cpu().numpy(), ref, ref_abs, False, "2100 tables forward")
     run_and_check(bt, tbe.make_config(long_threshold=32, chunk=16), what="2100 tables")
+
+
+@pytest.mark.parametrize("optimizer", ["sgd", "rowwise_adagrad"])
+def test_every_lookup_on_one_row(optimizer):
+    """Degenerate batch: 200 000 lookups, all of row 3 of a one-row-hot table (and a one-row
+    table beside it): one run of 200 000 lookups split into 782 chunks, and a run per table."""
+    tables = (ti.TableSpec(10, 64, ("fixed", 200)), ti.TableSpec(1, 16, ("fixed", 2)))
+    spec = ti.BatchSpec("one hot row", tables, B=1000, w_dtype=torch.float16, w_range=0.5,
+                        optimizer=optimizer)
+    bt = ti.make_batch(spec, 99)
+    idx = bt.indices.clone()
+    idx[:200_000] = 3
+    bt.indices = idx
+    db, W, mom, r = run_and_check(bt, what=f"one row {optimizer}")
+    assert r["num_runs"] == 2
+    W0 = bt.weights.view(-1)[:640].view(10, 64)
+    got = W.cpu()[:640].view(10, 64)
+    untouched = [i for i in range(10) if i != 3]
+    assert torch.equal(got[untouched].view(torch.int16), W0[untouched].view(torch.int16))
