@@ -83,7 +83,8 @@ __global__ __launch_bounds__(kBlock) void hist_bwd_partial_kernel(
     // the 17 offsets of this wave's bags, clamped to [0, N] and made monotone (running max)
     int32_t o = 0;
     if (lane <= kHbWaveBags) {
-      const int64_t v = static_cast<int64_t>(offsets[bag0 + bw + min(lane, nbw)]);
+      // waves past the last bag (nbw = 0) read the table's end offset, not beyond it
+      const int64_t v = static_cast<int64_t>(offsets[bag0 + min(bw + min(lane, nbw), static_cast<int64_t>(B))]);
       o = static_cast<int32_t>(min(max(v, static_cast<int64_t>(0)), N));
     }
     for (int d = 1; d < 32; d <<= 1) {

@@ -340,3 +340,16 @@ def test_every_lookup_on_one_row(optimizer):
     got = W.cpu()[:640].view(10, 64)
     untouched = [i for i in range(10) if i != 3]
     assert torch.equal(got[untouched].view(torch.int16), W0[untouched].view(torch.int16))
+
+
+@pytest.mark.parametrize("B", [10, 70, 200])
+def test_hist_backward_table_last(B):
+    """The histogram table last among the tables, B not a multiple of the 64-bag workgroup
+    step: waves past the last bag stop at the table's end offset."""
+    tables = (ti.TableSpec(700, 32, ("poisson", 3.0, None, None)),
+              ti.TableSpec(64, 128, ("poisson", 90.0, None, None)))
+    spec = ti.BatchSpec(f"hist last B={B}", tables, B=B, w_dtype=torch.float16, w_range=0.05,
+                        optimizer="rowwise_adagrad", pooling_hint=(3, 90))
+    bt = ti.make_batch(spec, 101)
+    db, _, _, _ = run_and_check(bt, what=f"hist last B={B}")
+    assert db.tables.c.hist_table == 1
