@@ -109,7 +109,7 @@ Config resolve_config(const tbe_config* c) {
   r.fused_long = c->fused_long;
   r.pretransposed = c->pretransposed;
   r.bags_per_wave = (c->bags_per_wave >= 1 && c->bags_per_wave <= 64) ? c->bags_per_wave : 0;
-  r.bwd_streams = c->bwd_streams == 2 ? 2 : 1;
+  r.bwd_streams = (c->bwd_streams == 1 || c->bwd_streams == 2) ? c->bwd_streams : 0;
   return r;
 }
 
@@ -278,7 +278,7 @@ void tbe_config_default(tbe_config* cfg) {
   cfg->fused_long = 0;
   cfg->pretransposed = 0;
   cfg->bags_per_wave = 0;
-  cfg->bwd_streams = 1;
+  cfg->bwd_streams = 0;
 }
 
 int64_t tbe_meta_entries(int32_t T) { return T >= 0 ? static_cast<int64_t>(TBE_META_FIELDS) * (T + 1) : 0; }
@@ -566,7 +566,12 @@ static tbe_status backward_common(const tbe_tables* tables, void* weights, float
   if (hist >= 0)
     if (tbe_status st = launch_hist_backward(tables, weights, momentum, opt, ia, grad_out, lr, eps, ws, L, s))
       return st;
-  if (cfg.bwd_streams < 2 || L.cap_long == 0)
+  // automatic: short runs of several widths are several short launches, whose tails leave
+  // room for the long runs
+  int buckets = 0;
+  for (int b = 0; b < TBE_NUM_BUCKETS; ++b) buckets += L.cap_short[b] > 0;
+  const int streams = cfg.bwd_streams ? cfg.bwd_streams : (buckets >= 2 ? 2 : 1);
+  if (streams < 2 || L.cap_long == 0)
     return launch_backward_update(tables, weights, momentum, opt, psw, grad_out, lr, eps, ws, L,
                                   final_buf, cfg, s, s);
   // long runs on a second stream, concurrent with the short runs (disjoint rows)

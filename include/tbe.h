@@ -118,7 +118,8 @@ typedef struct {
                               in one load ("bags per program", blog section 2), 1..64; 0 (default):
                               the power of two in [8, 64] that gives every wave about 8 steps */
   int32_t bwd_streams;     /* backward: 2 = long runs (chunks, apply) on the library's second stream,
-                              concurrent with the short runs; 1 = one stream (default 1) */
+                              concurrent with the short runs; 1 = one stream; 0 (default): 2 when
+                              the tables' widths fall in two or more short-run buckets */
 } tbe_config;
 
 /* Device-side view of the transpose, for inspection by tests (tbe_transpose). */

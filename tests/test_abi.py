@@ -109,7 +109,7 @@ def test_config_defaults():
     assert (c.long_threshold, c.chunk, c.hist_enable) == (256, 256, 1)
     assert c.bag_windows <= 1 and c.fused_long == 0 and c.sort_blocks == 0
     assert c.pretransposed == 0 and c.bags_per_wave == 0  # 0: chosen from the batch shape
-    assert c.bwd_streams == 1
+    assert c.bwd_streams == 0  # 0: chosen from the tables' widths
 
 
 def test_workspace_histogram_table_partials():
