@@ -92,7 +92,9 @@ def batch_stats(bt: ti.Batch, hist_table: int, threshold=256, chunk=256):
         c = np.bincount(lk, minlength=bt.E[t])
         c = c[c > 0]
         lg = c >= threshold
+        lens = np.diff(off[t * B:(t + 1) * B + 1])
         per.append(dict(D=bt.D[t], N=int(lk.size), U=int(c.size), hottest=int(c.max()) if c.size else 0,
+                        tail=int(np.maximum(lens - 256, 0).sum()),   # lookups past a bag's first 256
                         long_runs=int(lg.sum()), long_lookups=int(c[lg].sum()),
                         short_runs=int((~lg).sum()), short_lookups=int(c[~lg].sum()),
                         chunks=int(((c[lg] + chunk - 1) // chunk).sum()), hist=t == hist_table))
@@ -103,9 +105,10 @@ def batch_stats(bt: ti.Batch, hist_table: int, threshold=256, chunk=256):
                 chunks=tot("chunks", True), per_table=per)
 
 
-def algorithmic_bytes(bt: ti.Batch, st: dict):
+def algorithmic_bytes(bt: ti.Batch, st: dict, hoist: bool):
     """What each kernel must move per launch (no credit for cache reuse), summed over tables
-    with their own D."""
+    with their own D.  hoist: the histogram forward keeps each bag's counts (64 u16) and the
+    histogram backward reads them and only the ids past a bag's first 256."""
     s_w = bt.weights.element_size()
     s_i = bt.indices.element_size()
     s_o = bt.offsets.element_size()
@@ -143,6 +146,9 @@ def algorithmic_bytes(bt: ti.Batch, st: dict):
         # per lookup: index; per bag: offset + output (forward) or gradient (backward) row
         by["fwd_hist"] = p["N"] * s_i + B * (s_o + p["D"] * 4) + 64 * p["D"] * s_w
         by["hist_bwd_partial"] = p["N"] * s_i + B * (s_o + p["D"] * 4)
+        if hoist:   # + the saved counts, written once and read once
+            by["fwd_hist"] += B * 64 * 2
+            by["hist_bwd_partial"] = p["tail"] * s_i + B * (s_o + 64 * 2 + p["D"] * 4)
     return by
 
 
@@ -322,7 +328,7 @@ def main():
     fwd_ms = float(np.median([a.elapsed_time(b) for a, b, _ in ev]))
     bwd_ms = float(np.median([b.elapsed_time(c) for _, b, c in ev]))
     N = st["N"]
-    ab = algorithmic_bytes(bt, st)
+    ab = algorithmic_bytes(bt, st, args.hoist == "on")
     dom_avg_ms = dom_ms / max(launches, 1)
     dom_bytes = ab.get(dominant, 0)
     achieved = dom_bytes / (dom_avg_ms * 1e-3) / 1e9 if dom_avg_ms > 0 else 0.0

@@ -185,6 +185,7 @@ BwdLayout bwd_layout(const tbe_tables* tb, int64_t N, int weighted, const Config
   if (cfg.hist_enable && tb->hist_table >= 0 && !weighted) {
     L.hist_partial = c.take(static_cast<size_t>(kHistBwdBlocks) * 64 * 128 * 4);
     L.hist_count = c.take(static_cast<size_t>(kHistBwdBlocks) * 64 * 4);
+    L.hist_saved = c.take(static_cast<size_t>((tb->B + 15) / 16 * 16) * 64 * 2);
   }
   L.counters = c.take(kNumCounters * 4);
   L.total = c.off;
@@ -368,7 +369,7 @@ tbe_status tbe_forward(const tbe_tables* tables, const void* weights, const void
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int hist = histogram_table(tables, cfg, per_sample_weights);
   if (hist >= 0)
-    if (tbe_status st = launch_forward_hist(tables, weights, ia, out, nullptr, s)) return st;
+    if (tbe_status st = launch_forward_hist(tables, weights, ia, out, nullptr, nullptr, s)) return st;
   return launch_forward_gather(tables, weights, ia, per_sample_weights, out, hist, cfg.fwd_unroll,
                                cfg.bags_per_wave, nullptr, s);
 }
@@ -377,11 +378,12 @@ tbe_status tbe_forward(const tbe_tables* tables, const void* weights, const void
 // gather; with error_counts, out-of-range ids are repaired on the way.
 static tbe_status forward_body(const tbe_tables* tables, const void* weights, const IndexArgs& ia,
                                const float* psw, float* out, int64_t* error_counts, const Config& cfg,
-                               hipStream_t s) {
+                               uint16_t* save_counts, hipStream_t s) {
   const int hist = histogram_table(tables, cfg, psw);
   // both kernels repair the ids they read (the histogram table's, everyone else's)
   if (hist >= 0)
-    if (tbe_status st = launch_forward_hist(tables, weights, ia, out, error_counts, s)) return st;
+    if (tbe_status st = launch_forward_hist(tables, weights, ia, out, error_counts, save_counts, s))
+      return st;
   return launch_forward_gather(tables, weights, ia, psw, out, hist, cfg.fwd_unroll, cfg.bags_per_wave,
                                error_counts, s);
 }
@@ -416,7 +418,7 @@ tbe_status tbe_forward_repair(const tbe_tables* tables, const void* weights, voi
                                                    num_indices, error_counts, s);
   const Config cfg = resolve_config(config);
   IndexArgs ia{indices, index_type, offsets, offset_type, num_indices};
-  return forward_body(tables, weights, ia, per_sample_weights, out, error_counts, cfg, s);
+  return forward_body(tables, weights, ia, per_sample_weights, out, error_counts, cfg, nullptr, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -514,16 +516,20 @@ tbe_status tbe_forward_hoisted(const tbe_tables* tables, const void* weights, vo
       return error_counts ? launch_bounds_indices(tables, indices, index_type, offsets, offset_type,
                                                   num_indices, error_counts, s)
                           : TBE_OK;
-    return forward_body(tables, weights, ia, per_sample_weights, out, error_counts, cfg, s);
+    return forward_body(tables, weights, ia, per_sample_weights, out, error_counts, cfg, nullptr, s);
   }
   const int hist = histogram_table(tables, cfg, per_sample_weights);
+  // forward-state reuse: the histogram forward keeps its counts for the backward
+  uint16_t* saved = hist >= 0 ? reinterpret_cast<uint16_t*>(static_cast<char*>(bwd_workspace) + L.hist_saved)
+                              : nullptr;
   Fork fork(s);
   if (tbe_status st = fork.status()) return st;
   int final_buf = 0;
   const tbe_status st_t = launch_transpose(tables, ia, weighted, static_cast<char*>(bwd_workspace), L,
                                            cfg, hist, error_counts ? 1 : 0, &final_buf, fork.side());
   const tbe_status st_f = st_t ? TBE_OK
-                               : forward_body(tables, weights, ia, per_sample_weights, out, error_counts, cfg, s);
+                               : forward_body(tables, weights, ia, per_sample_weights, out, error_counts,
+                                              cfg, saved, s);
   // joined even after a failed launch, so that the streams stay ordered
   const tbe_status st_j = fork.join();
   return st_t ? st_t : (st_f ? st_f : st_j);
@@ -563,9 +569,13 @@ static tbe_status backward_common(const tbe_tables* tables, void* weights, float
   int final_buf = L.passes & 1;
   if (!cfg.pretransposed)
     if (tbe_status st = launch_transpose(tables, ia, psw ? 1 : 0, ws, L, cfg, hist, 0, &final_buf, s)) return st;
-  if (hist >= 0)
-    if (tbe_status st = launch_hist_backward(tables, weights, momentum, opt, ia, grad_out, lr, eps, ws, L, s))
+  if (hist >= 0) {
+    // with the hoisted forward's state, its saved counts replace counting the first 256 ids
+    const uint16_t* saved = cfg.pretransposed ? reinterpret_cast<const uint16_t*>(ws + L.hist_saved) : nullptr;
+    if (tbe_status st = launch_hist_backward(tables, weights, momentum, opt, ia, grad_out, lr, eps, ws, L,
+                                             saved, s))
       return st;
+  }
   // automatic: short runs of several widths are several short launches, whose tails leave
   // room for the long runs
   int buckets = 0;

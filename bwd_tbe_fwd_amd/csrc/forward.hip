@@ -189,7 +189,9 @@ __global__ __launch_bounds__(kBlock) void fwd_gather_kernel(
 // exact in fp32; only the accumulation rounds.  Ids beyond the first 256 of a
 // bag are gathered and added to the tile; the finished 16 x D tile leaves
 // through LDS as 16-byte row-contiguous stores.  With REPAIR, ids outside the
-// table are repaired to 0 in place and counted, as in the gather.
+// table are repaired to 0 in place and counted, as in the gather.  With
+// save_counts, the tile's counts also go to HBM as u16 (bag-major, 64 rows a
+// bag), the forward state the histogram backward reuses.
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
@@ -203,7 +205,7 @@ template <typename IT, typename OT, bool REPAIR>
 __global__ __launch_bounds__(kBlock) void fwd_hist_kernel(
     const uint16_t* __restrict__ Wt, IT* __restrict__ indices, const OT* __restrict__ offsets,
     float* __restrict__ out, int64_t bag0, int32_t B, int32_t E, int32_t D, int64_t col_base,
-    int32_t out_width, int64_t N, int64_t* __restrict__ counts) {
+    int32_t out_width, int64_t N, int64_t* __restrict__ counts, uint16_t* __restrict__ save_counts) {
   __shared__ __align__(16) uint16_t s_wT[kHistCols * kHistRows];            // [col][row]
   __shared__ __align__(16) float s_tile[kWavesPerBlock][kHistBags * kHistCols];
   __shared__ int32_t s_off[kWavesPerBlock][kHistBags + 1];
@@ -279,6 +281,16 @@ __global__ __launch_bounds__(kBlock) void fwd_hist_kernel(
       }
     }
     __builtin_amdgcn_wave_barrier();
+    if (save_counts) {  // 16 bags x 64 rows as u16 (the padding bags of the last tile hold zeros)
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int e = 8 * (k * kWave + lane);
+        const u32x4 c0 = *reinterpret_cast<const u32x4*>(&cnt[e]);
+        const u32x4 c1 = *reinterpret_cast<const u32x4*>(&cnt[e + 4]);
+        const u32x4 v = {c0.x | (c0.y << 16), c0.z | (c0.w << 16), c1.x | (c1.y << 16), c1.z | (c1.w << 16)};
+        *reinterpret_cast<u32x4*>(save_counts + b0 * kHistRows + e) = v;
+      }
+    }
     // A operand: lane l holds bag l%16, rows 16s + 4(l/16) + [0, 4)
     half4_t a[4];
 #pragma unroll
@@ -402,7 +414,7 @@ tbe_status gather_dispatch_idx(const tbe_tables* tb, const void* W, const IndexA
 
 template <typename IT, typename OT>
 tbe_status hist_go(const tbe_tables* tb, const void* W, const IndexArgs& ia, float* out,
-                   int64_t* repair_counts, hipStream_t s) {
+                   int64_t* repair_counts, uint16_t* save_counts, hipStream_t s) {
   const int64_t tiles = (static_cast<int64_t>(tb->B) + kHistBags - 1) / kHistBags;
   const int grid = grid_for(tiles);
   ProfScope ps("fwd_hist", s);
@@ -412,7 +424,8 @@ tbe_status hist_go(const tbe_tables* tb, const void* W, const IndexArgs& ia, flo
                      const_cast<IT*>(static_cast<const IT*>(ia.indices)),                         \
                      static_cast<const OT*>(ia.offsets), out,                                     \
                      static_cast<int64_t>(tb->hist_table) * tb->B, tb->B, tb->hist_E, tb->hist_D,   \
-                     static_cast<int64_t>(tb->hist_col), tb->out_width, ia.N, repair_counts)
+                     static_cast<int64_t>(tb->hist_col), tb->out_width, ia.N, repair_counts,     \
+                     save_counts)
   if (repair_counts) TBE_HIST_LAUNCH(true);
   else TBE_HIST_LAUNCH(false);
 #undef TBE_HIST_LAUNCH
@@ -442,14 +455,14 @@ tbe_status launch_forward_gather(const tbe_tables* tb, const void* W, const Inde
 }
 
 tbe_status launch_forward_hist(const tbe_tables* tb, const void* W, const IndexArgs& ia,
-                               float* out, int64_t* rc, hipStream_t s) {
+                               float* out, int64_t* rc, uint16_t* sc, hipStream_t s) {
   if (tb->B == 0 || tb->hist_table < 0) return TBE_OK;
   if (ia.itype == TBE_I32) {
-    if (ia.otype == TBE_I32) return hist_go<int32_t, int32_t>(tb, W, ia, out, rc, s);
-    return hist_go<int32_t, int64_t>(tb, W, ia, out, rc, s);
+    if (ia.otype == TBE_I32) return hist_go<int32_t, int32_t>(tb, W, ia, out, rc, sc, s);
+    return hist_go<int32_t, int64_t>(tb, W, ia, out, rc, sc, s);
   }
-  if (ia.otype == TBE_I32) return hist_go<int64_t, int32_t>(tb, W, ia, out, rc, s);
-  return hist_go<int64_t, int64_t>(tb, W, ia, out, rc, s);
+  if (ia.otype == TBE_I32) return hist_go<int64_t, int32_t>(tb, W, ia, out, rc, sc, s);
+  return hist_go<int64_t, int64_t>(tb, W, ia, out, rc, sc, s);
 }
 
 }  // namespace tbe

@@ -26,6 +26,12 @@
 // is written once per workgroup as a partial.  The apply kernel sums a row's
 // partials in a fixed order and applies SGD or row-wise Adagrad to rows whose
 // count is nonzero, so results are bitwise repeatable.
+//
+// After the hoisted forward, the counts of each bag's first 256 lookups are the
+// ones the histogram forward already made (kept as u16 in the workspace): a wave
+// loads them into LDS and reads only the ids past a bag's first 256, so the
+// id stream of this table is read once per training step instead of twice.
+// The counts are the same integers either way, so the results are bitwise equal.
 #include "tbe_device.h"
 #include "tbe_internal.h"
 
@@ -40,6 +46,7 @@ constexpr int kHbCols = 128;    // max D; each wave owns 32 columns (2 MFMA N ti
 constexpr int kHbWaveBags = 16; // bags one wave counts per step
 constexpr int kHbBags = kHbWaveBags * kWavesPerBlock;  // bags per workgroup step: MFMA K, 16 steps of 4
 constexpr int kHbLoads = 8;     // id loads in flight per lane while counting
+constexpr int kHbHead = 256;    // ids per bag the histogram forward counts (its saved counts)
 
 __device__ __forceinline__ void wave_sync() { __builtin_amdgcn_wave_barrier(); }
 
@@ -50,8 +57,8 @@ template <typename IT, typename OT>
 __global__ __launch_bounds__(kBlock) void hist_bwd_partial_kernel(
     const IT* __restrict__ indices, const OT* __restrict__ offsets,
     const float* __restrict__ grad_out, int64_t bag0, int32_t B, int32_t E, int32_t D,
-    int64_t col_base, int32_t out_width, int64_t N, float* __restrict__ partial,
-    int32_t* __restrict__ pcount) {
+    int64_t col_base, int32_t out_width, int64_t N, const uint16_t* __restrict__ saved,
+    float* __restrict__ partial, int32_t* __restrict__ pcount) {
   __shared__ __align__(16) uint32_t s_cnt[kHbBags * kHbRows];
   __shared__ int32_t s_off[kWavesPerBlock][kHbWaveBags + 1];
   const int lane = lane_id();
@@ -95,27 +102,50 @@ __global__ __launch_bounds__(kBlock) void hist_bwd_partial_kernel(
     const int32_t n = read_lane(o, kHbWaveBags) - o0;
     __syncthreads();  // every wave is done reading the previous step's counts
     if (lane <= kHbWaveBags) off[lane] = o - o0;
+    if (saved) {
+      // the forward's counts of the 16 bags (the forward pads the last tile with zero counts;
+      // a wave past the last bag has none)
 #pragma unroll
-    for (int x = lane; x < kHbWaveBags * kHbRows / 4; x += kWave)
-      reinterpret_cast<u32x4*>(mycnt)[x] = u32x4{0u, 0u, 0u, 0u};
-    wave_sync();
-    // count every lookup of the wave's 16 bags; ids outside [0, E) are dropped
-    for (int32_t j0 = 0; j0 < n; j0 += kHbLoads * kWave) {
-      int64_t r[kHbLoads];
-#pragma unroll
-      for (int u = 0; u < kHbLoads; ++u) {
-        const int32_t j = j0 + u * kWave + lane;
-        r[u] = j < n ? static_cast<int64_t>(indices[o0 + j]) : -1;
+      for (int k = 0; k < 2; ++k) {
+        const int e = 8 * (k * kWave + lane);
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (nbw > 0) v = *reinterpret_cast<const u32x4*>(saved + bw * kHbRows + e);
+        reinterpret_cast<u32x4*>(mycnt + e)[0] = u32x4{v.x & 0xffffu, v.x >> 16, v.y & 0xffffu, v.y >> 16};
+        reinterpret_cast<u32x4*>(mycnt + e)[1] = u32x4{v.z & 0xffffu, v.z >> 16, v.w & 0xffffu, v.w >> 16};
       }
+      wave_sync();
+      // ids past each bag's first 256
+      for (int i = 0; i < nbw; ++i) {
+        const int32_t e = off[i + 1];
+        for (int32_t j = off[i] + kHbHead + lane; j < e; j += kWave) {
+          const int64_t r = static_cast<int64_t>(indices[o0 + j]);
+          if (static_cast<uint64_t>(r) < static_cast<uint64_t>(E))
+            atomicAdd(&mycnt[i * kHbRows + static_cast<int>(r)], 1u);
+        }
+      }
+    } else {
 #pragma unroll
-      for (int u = 0; u < kHbLoads; ++u) {
-        const int32_t j = j0 + u * kWave + lane;
-        if (static_cast<uint64_t>(r[u]) < static_cast<uint64_t>(E)) {
-          int b = 0;  // largest b in [0, 16) with off[b] <= j: the bag of lookup j
+      for (int x = lane; x < kHbWaveBags * kHbRows / 4; x += kWave)
+        reinterpret_cast<u32x4*>(mycnt)[x] = u32x4{0u, 0u, 0u, 0u};
+      wave_sync();
+      // count every lookup of the wave's 16 bags; ids outside [0, E) are dropped
+      for (int32_t j0 = 0; j0 < n; j0 += kHbLoads * kWave) {
+        int64_t r[kHbLoads];
 #pragma unroll
-          for (int step = 8; step > 0; step >>= 1)
-            if (off[b + step] <= j) b += step;
-          atomicAdd(&mycnt[b * kHbRows + static_cast<int>(r[u])], 1u);
+        for (int u = 0; u < kHbLoads; ++u) {
+          const int32_t j = j0 + u * kWave + lane;
+          r[u] = j < n ? static_cast<int64_t>(indices[o0 + j]) : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < kHbLoads; ++u) {
+          const int32_t j = j0 + u * kWave + lane;
+          if (static_cast<uint64_t>(r[u]) < static_cast<uint64_t>(E)) {
+            int b = 0;  // largest b in [0, 16) with off[b] <= j: the bag of lookup j
+#pragma unroll
+            for (int step = 8; step > 0; step >>= 1)
+              if (off[b + step] <= j) b += step;
+            atomicAdd(&mycnt[b * kHbRows + static_cast<int>(r[u])], 1u);
+          }
         }
       }
     }
@@ -226,12 +256,12 @@ __global__ __launch_bounds__(kBlock) void hist_bwd_apply_kernel(
 
 template <typename IT, typename OT>
 tbe_status hist_partial_go(const tbe_tables* tb, const IndexArgs& ia, const float* grad_out,
-                           int P, float* partial, int32_t* pcount, hipStream_t s) {
+                           const uint16_t* saved, int P, float* partial, int32_t* pcount, hipStream_t s) {
   ProfScope ps("hist_bwd_partial", s);
   hipLaunchKernelGGL((hist_bwd_partial_kernel<IT, OT>), dim3(P), dim3(kBlock), 0, s,
                      static_cast<const IT*>(ia.indices), static_cast<const OT*>(ia.offsets), grad_out,
                      static_cast<int64_t>(tb->hist_table) * tb->B, tb->B, tb->hist_E, tb->hist_D,
-                     static_cast<int64_t>(tb->hist_col), tb->out_width, ia.N, partial, pcount);
+                     static_cast<int64_t>(tb->hist_col), tb->out_width, ia.N, saved, partial, pcount);
   return check_launch("hist_bwd_partial");
 }
 
@@ -239,7 +269,7 @@ tbe_status hist_partial_go(const tbe_tables* tb, const IndexArgs& ia, const floa
 
 tbe_status launch_hist_backward(const tbe_tables* tb, void* W, float* momentum, int opt,
                                 const IndexArgs& ia, const float* grad_out, float lr, float eps,
-                                char* ws, const BwdLayout& L, hipStream_t s) {
+                                char* ws, const BwdLayout& L, const uint16_t* saved, hipStream_t s) {
   if (tb->B == 0 || tb->hist_table < 0) return TBE_OK;
   if (tb->hist_table >= tb->T || tb->hist_E < 1 || tb->hist_E > kHbRows || tb->hist_D > kHbCols || tb->hist_D % 16 || tb->w_dtype != TBE_F16) {
     set_error("histogram table outside E <= 64, D <= 128, D %% 16 == 0, fp16");
@@ -252,11 +282,11 @@ tbe_status launch_hist_backward(const tbe_tables* tb, void* W, float* momentum, 
   int32_t* pcount = reinterpret_cast<int32_t*>(ws + L.hist_count);
   tbe_status st;
   if (ia.itype == TBE_I32)
-    st = ia.otype == TBE_I32 ? hist_partial_go<int32_t, int32_t>(tb, ia, grad_out, P, partial, pcount, s)
-                             : hist_partial_go<int32_t, int64_t>(tb, ia, grad_out, P, partial, pcount, s);
+    st = ia.otype == TBE_I32 ? hist_partial_go<int32_t, int32_t>(tb, ia, grad_out, saved, P, partial, pcount, s)
+                             : hist_partial_go<int32_t, int64_t>(tb, ia, grad_out, saved, P, partial, pcount, s);
   else
-    st = ia.otype == TBE_I32 ? hist_partial_go<int64_t, int32_t>(tb, ia, grad_out, P, partial, pcount, s)
-                             : hist_partial_go<int64_t, int64_t>(tb, ia, grad_out, P, partial, pcount, s);
+    st = ia.otype == TBE_I32 ? hist_partial_go<int64_t, int32_t>(tb, ia, grad_out, saved, P, partial, pcount, s)
+                             : hist_partial_go<int64_t, int64_t>(tb, ia, grad_out, saved, P, partial, pcount, s);
   if (st) return st;
   uint16_t* Wt = static_cast<uint16_t*>(W) + tb->hist_w_base;
   ProfScope ps("hist_bwd_apply", s);

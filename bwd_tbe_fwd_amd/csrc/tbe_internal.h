@@ -53,6 +53,7 @@ struct BwdLayout {
   size_t sort_hist, seg_cnt, cls_cnt, counters, total;
   size_t chunk_unit, chunk_order, unit_cnt;  // long-run chunk ordering by (table, bag window)
   size_t hist_partial, hist_count;             // histogram backward: per-block partial sums
+  size_t hist_saved;                           // per-bag counts the histogram forward saves (u16)
   int nwin, win_size, units;
   int64_t cap_long, cap_chunk, cap_short[TBE_NUM_BUCKETS];
   int64_t seg;        // keys per sort / RLE block (multiple of kRadixTile)
@@ -85,9 +86,12 @@ tbe_status launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
 tbe_status launch_forward_gather(const tbe_tables* tb, const void* W, const IndexArgs& ia,
                                  const float* psw, float* out, int skip_table, int unroll,
                                  int bags_per_wave, int64_t* repair_counts, hipStream_t s);
-// repair_counts != NULL: ids outside the table are repaired to 0 in place and counted there
+// repair_counts != NULL: ids outside the table are repaired to 0 in place and counted there;
+// save_counts != NULL: each bag's counts (its first 256 ids, 64 u16 a bag) are kept for the
+// backward
 tbe_status launch_forward_hist(const tbe_tables* tb, const void* W, const IndexArgs& ia,
-                               float* out, int64_t* repair_counts, hipStream_t s);
+                               float* out, int64_t* repair_counts, uint16_t* save_counts,
+                               hipStream_t s);
 
 tbe_status launch_bounds(const tbe_tables* tb, void* indices, int itype, void* offsets, int otype,
                          int64_t N, int64_t* counts, void* ws, hipStream_t s);
@@ -107,9 +111,12 @@ tbe_status launch_transpose(const tbe_tables* tb, const IndexArgs& ia, int weigh
 
 // histogram backward of the small table (counts x gradient on MFMA, then the optimizer)
 constexpr int kHistBwdBlocks = 512;  // max partials (workgroups) of the histogram backward
+// saved_counts: the counts the histogram forward kept (then only ids past a bag's first 256
+// are read), or NULL to count every id
 tbe_status launch_hist_backward(const tbe_tables* tb, void* W, float* momentum, int opt,
                                 const IndexArgs& ia, const float* grad_out, float lr, float eps,
-                                char* ws, const BwdLayout& L, hipStream_t s);
+                                char* ws, const BwdLayout& L, const uint16_t* saved_counts,
+                                hipStream_t s);
 
 // groups long-run chunks by (table, bag window); *order = NULL when not grouped
 tbe_status launch_chunk_order(const tbe_tables* tb, const float* psw, char* ws, const BwdLayout& L,

@@ -226,7 +226,9 @@ tbe_status tbe_forward_repair(const tbe_tables* tables, const void* weights, voi
  * the call returns: work enqueued later on `stream` sees the output and the
  * transpose.  A following tbe_backward_* with config->pretransposed = 1 and the
  * same tables, indices, offsets, per-sample-weights presence, config and
- * bwd_workspace skips its own transpose.  With repair, an out-of-range id
+ * bwd_workspace skips its own transpose; with the histogram table, the forward
+ * also keeps each bag's lookup counts there and that backward reuses them
+ * instead of counting the table's ids again.  With repair, an out-of-range id
  * counts in the transpose as row 0 of its table, the value the repair writes,
  * whichever of the two reads the id first.  Calls that overlap on one device
  * share the second stream and run their transposes in call order.

@@ -114,12 +114,13 @@ def test_config_defaults():
 
 def test_workspace_histogram_table_partials():
     """A histogram-eligible table adds its per-workgroup partials (512 x 64 x 128 floats and
-    512 x 64 counts) to the unweighted workspace only."""
+    512 x 64 counts) and the forward's saved counts (B rounded up to 16, x 64 u16) to the
+    unweighted workspace only."""
     E, D, B, n = [64, 1000], [128, 64], 4096, 600_000
     plain = tbe.Tables(E, D, B, torch.float16, device=None)
     hist = tbe.Tables(E, D, B, torch.float16, device=None, pooling_hint=[128, 5])
     assert plain.c.hist_table == -1 and hist.c.hist_table == 0
-    extra = 512 * 64 * 128 * 4 + 512 * 64 * 4
+    extra = 512 * 64 * 128 * 4 + 512 * 64 * 4 + 4096 * 64 * 2
     d = tbe.tbe_backward_workspace_bytes(hist, n, False) - tbe.tbe_backward_workspace_bytes(plain, n, False)
     assert extra <= d < extra + 1024
     assert tbe.tbe_backward_workspace_bytes(hist, n, True) == tbe.tbe_backward_workspace_bytes(plain, n, True)

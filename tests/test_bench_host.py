@@ -33,10 +33,26 @@ def test_batch_stats_partition_the_lookups():
 def test_algorithmic_bytes_by_hand():
     bt = ti.make_batch(_spec(), 4, device="cpu")
     st = bench.batch_stats(bt, hist_table=0)
-    ab = bench.algorithmic_bytes(bt, st)
+    ab = bench.algorithmic_bytes(bt, st, hoist=False)
     p1 = st["per_table"][1]
     # generic forward: table 1 only; 8-byte ids, 2-byte weights, fp32 output rows of 32
     assert ab["fwd_gather"] == p1["N"] * (8 + 32 * 2) + 300 * (8 + 32 * 4)
     # the histogram table: its ids, one offset and one 128-wide fp32 row per bag, the table once
     assert ab["fwd_hist"] == 30000 * 8 + 300 * (8 + 128 * 4) + 64 * 128 * 2
     assert ab["radix_downsweep"] == p1["N"] * 16
+    # hoisted: the forward writes 64 u16 counts a bag, the backward reads them, the gradient
+    # rows and offsets, and no ids (no bag is longer than 256)
+    assert ab["hist_bwd_partial"] == 30000 * 8 + 300 * (8 + 128 * 4)
+    ah = bench.algorithmic_bytes(bt, st, hoist=True)
+    assert ah["fwd_hist"] == ab["fwd_hist"] + 300 * 128
+    assert ah["hist_bwd_partial"] == 300 * (8 + 128 + 128 * 4)
+
+
+def test_tail_lookups_past_256():
+    tables = (ti.TableSpec(64, 64, ("fixed", 300)), ti.TableSpec(50, 16, ("fixed", 2)))
+    bt = ti.make_batch(ti.BatchSpec("tails", tables, B=20, w_dtype=torch.float16, w_range=0.05,
+                                    pooling_hint=(300, 2)), 5, device="cpu")
+    st = bench.batch_stats(bt, hist_table=0)
+    assert st["per_table"][0]["tail"] == 20 * 44 and st["per_table"][1]["tail"] == 0
+    ah = bench.algorithmic_bytes(bt, st, hoist=True)
+    assert ah["hist_bwd_partial"] == 20 * 44 * 8 + 20 * (8 + 128 + 64 * 4)

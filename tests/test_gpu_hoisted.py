@@ -91,6 +91,33 @@ def test_hoisted_equals_plain(name, repair):
         assert hoist["counts"][0] > 0 and hoist["counts"][1] > 0
 
 
+@pytest.mark.parametrize("L,B,last", [(("poisson", 300.0, None, None), 130, False),
+                                      (("poisson", 300.0, None, None), 77, True),
+                                      (("fixed", 256), 33, False),
+                                      (("fixed", 257), 48, True),
+                                      (("poisson", 40.0, None, None), 1000, False)])
+@pytest.mark.parametrize("repair", [False, True])
+def test_hoisted_histogram_reuses_forward_counts(L, B, last, repair):
+    """After the hoisted forward the histogram backward takes each bag's counts of its first
+    256 ids from the forward and reads only the ids past them: bitwise equal to the plain two
+    calls (which count every id in the backward), with bags longer than 256, bags of exactly
+    256 and 257, a ragged last tile of 16 bags, the table first or last, and out-of-range ids
+    dropped (no repair) or repaired to row 0."""
+    hist = ti.TableSpec(64, 64, L)
+    comp = ti.TableSpec(900, 64, ("poisson", 6.0, None, None), ("zipf", 1.1, None))
+    tables, hint = ((comp, hist), (6, 128)) if last else ((hist, comp), (128, 6))
+    spec = ti.BatchSpec(f"hoisted hist L={L} B={B} last={last}", tables, B=B, w_dtype=torch.float16,
+                        w_range=0.05, optimizer="rowwise_adagrad", pooling_hint=hint)
+    flush_print(spec.name, f"repair={repair}")
+    bt = ti.make_batch(spec, 87)
+    idx, off = _inject(bt, 7, bad_offsets=False)
+    cfg_kw = dict(long_threshold=32, chunk=16)
+    plain = _step(bt, idx, off, hoisted=False, repair=repair, cfg_kw=cfg_kw)
+    hoist = _step(bt, idx, off, hoisted=True, repair=repair, cfg_kw=cfg_kw)
+    assert hoist["hist"] == (1 if last else 0)
+    _assert_same(plain, hoist)
+
+
 @pytest.mark.parametrize("name", ["skewed", "histogram"])
 def test_hoisted_repaired_matches_oracle(name):
     """The hoisted step on faulty input equals the oracle's step on the repaired input: an
