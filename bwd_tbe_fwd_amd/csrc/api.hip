@@ -91,6 +91,21 @@ int device_cu_count() {
   return cached[dev];
 }
 
+int blocks_per_cu(const void* kernel) {
+  static std::mutex mu;
+  static std::vector<std::pair<const void*, int>> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const auto& e : cache)
+    if (e.first == kernel) return e.second;
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kBlock, 0) != hipSuccess || n < 1) {
+    (void)hipGetLastError();  // not sticky; fall back to the usual 8 (32 waves)
+    n = 8;
+  }
+  cache.emplace_back(kernel, n);
+  return n;
+}
+
 // ---------------------------------------------------------------------------
 // config and workspace layout
 // ---------------------------------------------------------------------------

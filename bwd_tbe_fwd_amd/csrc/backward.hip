@@ -105,16 +105,15 @@ __global__ __launch_bounds__(kBlock) void chunk_scatter_kernel(const uint32_t* _
 template <bool WEIGHTED>
 tbe_status accum_go(const tbe_tables* tb, const float* psw, const float* grad_out, char* ws,
                     const BwdLayout& L, int final_buf, const Config& cfg, hipStream_t s) {
-  const int64_t maxb = static_cast<int64_t>(device_cu_count()) * 8;
-  const int grid = static_cast<int>(
-      hmax(1, hmin((L.cap_chunk + kWavesPerBlock - 1) / kWavesPerBlock, maxb)));
+  const int64_t work = (L.cap_chunk + kWavesPerBlock - 1) / kWavesPerBlock;
   const uint32_t* pay = reinterpret_cast<const uint32_t*>(ws + L.pay[final_buf]);
   const uint32_t* bag_of = WEIGHTED ? reinterpret_cast<const uint32_t*>(ws + L.bag_of) : nullptr;
   const uint32_t* order = nullptr;
   if (tbe_status st = launch_chunk_order(tb, psw, ws, L, final_buf, cfg, &order, s)) return st;
   ProfScope ps("grad_accum", s);
 #define TBE_ACC(U)                                                                                 \
-  hipLaunchKernelGGL((grad_accum_kernel<WEIGHTED, U>), dim3(grid), dim3(kBlock), 0, s, grad_out, pay, \
+  hipLaunchKernelGGL((grad_accum_kernel<WEIGHTED, U>), dim3(resident_grid(grad_accum_kernel<WEIGHTED, U>, work)), \
+                     dim3(kBlock), 0, s, grad_out, pay,                                             \
                      bag_of, psw, reinterpret_cast<const uint4*>(ws + L.long_list),               \
                      reinterpret_cast<const uint32_t*>(ws + L.long_table),                        \
                      reinterpret_cast<const uint2*>(ws + L.chunk_list),                           \

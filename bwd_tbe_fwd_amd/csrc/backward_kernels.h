@@ -27,7 +27,7 @@
 
 namespace tbe {
 
-template <int DT, int BD, int OPT, bool WEIGHTED, int UNROLL>
+template <int DT, int BD, int NP, int OPT, bool WEIGHTED, int UNROLL>
 __global__ __launch_bounds__(kBlock) void short_run_kernel(
     typename Fmt<DT>::S* __restrict__ W, float* __restrict__ momentum,
     const float* __restrict__ grad_out, const uint32_t* __restrict__ pay,
@@ -35,9 +35,9 @@ __global__ __launch_bounds__(kBlock) void short_run_kernel(
     const uint4* __restrict__ list, const int32_t* __restrict__ count_ptr,
     const int64_t* __restrict__ meta, int32_t B, int32_t out_width, float lr, float eps) {
   using S = typename Fmt<DT>::S;
-  constexpr int NP = BD > 256 ? BD / 256 : 1;   // column passes of 64 lanes x 4 floats
-  constexpr int LPR = BD >= 256 ? 64 : BD / 4;  // lanes per run
-  constexpr int RPW = kWave / LPR;              // runs per wave
+  constexpr int LPR = BD / (4 * NP);  // lanes per run; each lane owns NP float4 column chunks
+  constexpr int RPW = kWave / LPR;     // runs per wave
+  static_assert(LPR >= 1 && LPR <= kWave && (LPR & (LPR - 1)) == 0, "lanes per run");
   const int lane = lane_id();
   const int g = lane / LPR;
   const int c = lane % LPR;
@@ -56,7 +56,7 @@ __global__ __launch_bounds__(kBlock) void short_run_kernel(
     bool act[NP];
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
-      const int col = p * 256 + c * 4;
+      const int col = p * 4 * LPR + c * 4;
       act[p] = col < D;
       if (act[p]) {
         load_vec<DT, 4>(wrow + col, w[p]);
@@ -101,7 +101,7 @@ __global__ __launch_bounds__(kBlock) void short_run_kernel(
 #pragma unroll
           for (int p = 0; p < NP; ++p) {
             if (ok && act[p]) {
-              const f32x4 x = load_f4(grow + p * 256 + c * 4);
+              const f32x4 x = load_f4(grow + p * 4 * LPR + c * 4);
               v[u][p][0] = x.x; v[u][p][1] = x.y; v[u][p][2] = x.z; v[u][p][3] = x.w;
             } else {
 #pragma unroll
@@ -143,7 +143,7 @@ __global__ __launch_bounds__(kBlock) void short_run_kernel(
     }
 #pragma unroll
     for (int p = 0; p < NP; ++p)
-      if (act[p]) store_vec4<DT>(wrow + p * 256 + c * 4, w[p]);
+      if (act[p]) store_vec4<DT>(wrow + p * 4 * LPR + c * 4, w[p]);
   }
 }
 

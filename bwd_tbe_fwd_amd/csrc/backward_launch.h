@@ -8,6 +8,13 @@ namespace tbe {
 namespace detail {
 
 constexpr int kShortUnroll = 4;
+constexpr int kShortMinChunks = 1;  // float4 column chunks per lane at least (fewer lanes per run)
+
+constexpr int short_chunks(int BD) {
+  const int np = BD >= 256 ? BD / 256 : 1;
+  const int want = kShortMinChunks < BD / 4 ? kShortMinChunks : BD / 4;
+  return np > want ? np : want;
+}
 
 template <int DT, int BD, int OPT, bool WEIGHTED>
 tbe_status short_go(void* W, float* momentum, const float* psw, const float* grad_out,
@@ -15,13 +22,14 @@ tbe_status short_go(void* W, float* momentum, const float* psw, const float* gra
                     const int32_t* count, int64_t cap, const tbe_tables* tb, float lr, float eps,
                     hipStream_t s) {
   using S = typename Fmt<DT>::S;
-  constexpr int LPR = BD >= 256 ? 64 : BD / 4;
+  constexpr int NP = short_chunks(BD);
+  constexpr int LPR = BD / (4 * NP);
   constexpr int RPW = kWave / LPR;
   const int64_t waves = (cap + RPW - 1) / RPW;
-  const int64_t maxb = static_cast<int64_t>(device_cu_count()) * 8;
-  const int grid = static_cast<int>(hmax(1, hmin((waves + kWavesPerBlock - 1) / kWavesPerBlock, maxb)));
+  const auto kernel = short_run_kernel<DT, BD, NP, OPT, WEIGHTED, kShortUnroll>;
+  const int grid = resident_grid(kernel, (waves + kWavesPerBlock - 1) / kWavesPerBlock);
   ProfScope ps("short_run", s);
-  hipLaunchKernelGGL((short_run_kernel<DT, BD, OPT, WEIGHTED, kShortUnroll>), dim3(grid), dim3(kBlock), 0, s,
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kBlock), 0, s,
                      static_cast<S*>(W), momentum, grad_out, pay, bag_of, psw, list, count, tb->meta,
                      tb->B, tb->out_width, lr, eps);
   return check_launch("short_run");
@@ -52,10 +60,10 @@ tbe_status apply_go(void* W, float* momentum, const uint4* long_list, const uint
                     const int32_t* counters, int64_t cap, const tbe_tables* tb, int chunk,
                     const float* partial, float lr, float eps, hipStream_t s) {
   using S = typename Fmt<DT>::S;
-  const int64_t maxb = static_cast<int64_t>(device_cu_count()) * 8;
-  const int grid = static_cast<int>(hmax(1, hmin(cap, maxb)));
+  const auto kernel = long_apply_kernel<DT, OPT>;
+  const int grid = resident_grid(kernel, cap);
   ProfScope ps("long_apply", s);
-  hipLaunchKernelGGL((long_apply_kernel<DT, OPT>), dim3(grid), dim3(kBlock), 0, s, static_cast<S*>(W),
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kBlock), 0, s, static_cast<S*>(W),
                      momentum, long_list, long_table, counters, tb->meta, chunk, tb->max_D, partial, lr, eps);
   return check_launch("long_apply");
 }
@@ -65,11 +73,11 @@ tbe_status fused_go(void* W, float* momentum, const float* psw, const float* gra
                     const BwdLayout& L, int final_buf, const Config& cfg, const uint32_t* order,
                     const tbe_tables* tb, float lr, float eps, hipStream_t s) {
   using S = typename Fmt<DT>::S;
-  const int64_t maxb = static_cast<int64_t>(device_cu_count()) * 8;
   const int64_t batches = (L.cap_chunk + kFusedBatch - 1) / kFusedBatch;
-  const int grid = static_cast<int>(hmax(1, hmin((batches + kWavesPerBlock - 1) / kWavesPerBlock, maxb)));
+  const auto kernel = long_fused_kernel<DT, OPT, WEIGHTED>;
+  const int grid = resident_grid(kernel, (batches + kWavesPerBlock - 1) / kWavesPerBlock);
   ProfScope ps("long_fused", s);
-  hipLaunchKernelGGL((long_fused_kernel<DT, OPT, WEIGHTED>), dim3(grid), dim3(kBlock), 0, s,
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kBlock), 0, s,
                      static_cast<S*>(W), momentum, grad_out,
                      reinterpret_cast<const uint32_t*>(ws + L.pay[final_buf]),
                      WEIGHTED ? reinterpret_cast<const uint32_t*>(ws + L.bag_of) : nullptr, psw,

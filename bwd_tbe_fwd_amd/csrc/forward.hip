@@ -352,24 +352,18 @@ __global__ __launch_bounds__(kBlock) void fwd_hist_kernel(
   }
 }
 
-int grid_for(int64_t work_waves) {
-  const int64_t cap = static_cast<int64_t>(device_cu_count()) * 8;  // 8 workgroups (32 waves) per CU
-  int64_t blocks = (work_waves + kWavesPerBlock - 1) / kWavesPerBlock;
-  if (blocks > cap) blocks = cap;
-  if (blocks < 1) blocks = 1;
-  return static_cast<int>(blocks);
-}
 
 template <int DT, typename IT, typename OT, bool PSW, int VEC, typename ACC>
 tbe_status gather_go(const tbe_tables* tb, const void* W, const IndexArgs& ia, const float* psw,
                      float* out, int skip, int nt, int unroll, int group, int64_t* repair_counts, hipStream_t s) {
   const int64_t slots = static_cast<int64_t>(nt) * tb->B;
-  const int grid = grid_for((slots + group - 1) / group);
+  const int64_t work = ((slots + group - 1) / group + kWavesPerBlock - 1) / kWavesPerBlock;
   using S = typename Fmt<DT>::S;
   ProfScope ps("fwd_gather", s);
 #define TBE_FWD_LAUNCH(U, R)                                                                     \
-  hipLaunchKernelGGL((fwd_gather_kernel<DT, IT, OT, PSW, VEC, ACC, U, R>), dim3(grid), dim3(kBlock), \
-                     0, s, static_cast<const S*>(W),                                                \
+  hipLaunchKernelGGL((fwd_gather_kernel<DT, IT, OT, PSW, VEC, ACC, U, R>),                       \
+                     dim3(resident_grid(fwd_gather_kernel<DT, IT, OT, PSW, VEC, ACC, U, R>, work)), \
+                     dim3(kBlock), 0, s, static_cast<const S*>(W),                                  \
                      const_cast<IT*>(static_cast<const IT*>(ia.indices)),                           \
                      static_cast<const OT*>(ia.offsets), psw, out, tb->meta, skip, nt, tb->B,         \
                      tb->out_width, ia.N, group, repair_counts)
@@ -416,10 +410,11 @@ template <typename IT, typename OT>
 tbe_status hist_go(const tbe_tables* tb, const void* W, const IndexArgs& ia, float* out,
                    int64_t* repair_counts, uint16_t* save_counts, hipStream_t s) {
   const int64_t tiles = (static_cast<int64_t>(tb->B) + kHistBags - 1) / kHistBags;
-  const int grid = grid_for(tiles);
+  const int64_t work = (tiles + kWavesPerBlock - 1) / kWavesPerBlock;
   ProfScope ps("fwd_hist", s);
 #define TBE_HIST_LAUNCH(R)                                                                         \
-  hipLaunchKernelGGL((fwd_hist_kernel<IT, OT, R>), dim3(grid), dim3(kBlock), 0, s,                 \
+  hipLaunchKernelGGL((fwd_hist_kernel<IT, OT, R>), dim3(resident_grid(fwd_hist_kernel<IT, OT, R>, work)), \
+                     dim3(kBlock), 0, s,                                                          \
                      static_cast<const uint16_t*>(W) + tb->hist_w_base,                           \
                      const_cast<IT*>(static_cast<const IT*>(ia.indices)),                         \
                      static_cast<const OT*>(ia.offsets), out,                                     \

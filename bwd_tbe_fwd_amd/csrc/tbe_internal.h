@@ -32,6 +32,16 @@ constexpr int kWavesPerBlock = kBlock / 64;
 int device_cu_count();                 // compute units of the current device (cached)
 inline int64_t hmin(int64_t a, int64_t b) { return a < b ? a : b; }
 inline int64_t hmax(int64_t a, int64_t b) { return a > b ? a : b; }
+// Workgroups of kBlock threads of `kernel` one CU holds at once (its registers and
+// LDS decide), queried once per kernel.
+int blocks_per_cu(const void* kernel);
+// Grid of a grid-stride kernel: every workgroup resident at once (a workgroup that
+// has to wait for a free slot would start its whole share late), at most work_blocks.
+template <typename K>
+int resident_grid(K* kernel, int64_t work_blocks) {
+  const int64_t cap = static_cast<int64_t>(device_cu_count()) * blocks_per_cu(reinterpret_cast<const void*>(kernel));
+  return static_cast<int>(hmax(1, hmin(work_blocks, cap)));
+}
 
 // Radix sort geometry (least-significant digit first, up to 9 bits a pass)
 constexpr int kRadixMaxBits = 9;
