@@ -125,6 +125,7 @@ Config resolve_config(const tbe_config* c) {
   r.pretransposed = c->pretransposed;
   r.bags_per_wave = (c->bags_per_wave >= 1 && c->bags_per_wave <= 64) ? c->bags_per_wave : 0;
   r.bwd_streams = (c->bwd_streams == 1 || c->bwd_streams == 2) ? c->bwd_streams : 0;
+  r.tiny = c->tiny_runs > 0 ? static_cast<int>(hmin(c->tiny_runs, r.threshold - 1)) : 0;
   return r;
 }
 
@@ -295,6 +296,7 @@ void tbe_config_default(tbe_config* cfg) {
   cfg->pretransposed = 0;
   cfg->bags_per_wave = 0;
   cfg->bwd_streams = 0;
+  cfg->tiny_runs = 8;
 }
 
 int64_t tbe_meta_entries(int32_t T) { return T >= 0 ? static_cast<int64_t>(TBE_META_FIELDS) * (T + 1) : 0; }

@@ -17,7 +17,9 @@
 // BD/256 column passes) and a wave owns 64/(BD/4) short runs at once - no lane
 // is masked off for D = BD, and the per-run metadata (one 16-byte descriptor)
 // is amortized over the lanes of the run.  UNROLL gradient rows are in flight
-// per lane before they are summed.  The weight row and the Adagrad state are
+// per lane before they are summed.  A wave step whose runs are all tiny (a few
+// lookups each: their time goes to waiting on the descriptor, payload and row
+// loads, not to bandwidth) serves twice as many runs with half the lanes each.  The weight row and the Adagrad state are
 // loaded before the gradient loop so their latency overlaps it.  Accumulation
 // is fp32 throughout; no float atomics anywhere, so results are deterministic.
 #pragma once
@@ -27,123 +29,154 @@
 
 namespace tbe {
 
-template <int DT, int BD, int NP, int OPT, bool WEIGHTED, int UNROLL>
+// One short run, owned by a group of LPR lanes (c: this lane's place in the group); each
+// lane holds NP float4 column chunks of the row.
+template <int DT, int NP, int LPR, int OPT, bool WEIGHTED, int UNROLL>
+__device__ __forceinline__ void short_run_one(
+    typename Fmt<DT>::S* __restrict__ W, float* __restrict__ momentum,
+    const float* __restrict__ grad_out, const uint32_t* __restrict__ pay,
+    const uint32_t* __restrict__ bag_of, const float* __restrict__ psw, const uint4 dsc, int c,
+    const int64_t* __restrict__ meta, int32_t B, int32_t out_width, float lr, float eps) {
+  using S = typename Fmt<DT>::S;
+  const uint32_t key = dsc.x, start = dsc.y, len = dsc.z;
+  const int t = static_cast<int>(dsc.w);
+  const TableMeta m = load_meta(meta, t);
+  const int D = static_cast<int>(m.D);
+  S* wrow = W + m.w_base + (static_cast<int64_t>(key) - m.row_base) * D;
+  const int64_t bag_lo = static_cast<int64_t>(t) * B;
+  float w[NP][4];
+  bool act[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int col = p * 4 * LPR + c * 4;
+    act[p] = col < D;
+    if (act[p]) {
+      load_vec<DT, 4>(wrow + col, w[p]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) w[p][q] = 0.f;
+    }
+  }
+  float mom = 0.f;
+  if constexpr (OPT == kOptAdagrad) mom = momentum[key];
+  float acc[NP][4];
+#pragma unroll
+  for (int p = 0; p < NP; ++p)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[p][q] = 0.f;
+  for (uint32_t j0 = 0; j0 < len; j0 += LPR) {
+    const int nb = static_cast<int>(min<uint32_t>(LPR, len - j0));
+    int32_t myb = -1;
+    float myw = 1.f;
+    if (c < nb) {
+      const uint32_t pv = pay[start + j0 + c];
+      int64_t bag;
+      if constexpr (WEIGHTED) {
+        bag = bag_of[pv];
+        myw = psw[pv];
+      } else {
+        bag = pv;
+      }
+      const int64_t br = bag - bag_lo;
+      myb = (br >= 0 && br < B) ? static_cast<int32_t>(br) : -1;
+    }
+    for (int q0 = 0; q0 < nb; q0 += UNROLL) {
+      float v[UNROLL][NP][4];
+      float wq[UNROLL];
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        const int q = q0 + u;
+        const int b = __shfl(myb, q, LPR);
+        wq[u] = WEIGHTED ? __shfl(myw, q, LPR) : 1.f;
+        const bool ok = q < nb && b >= 0;
+        const float* grow = grad_out + static_cast<int64_t>(b) * out_width + m.col_base;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+          if (ok && act[p]) {
+            const f32x4 x = load_f4(grow + p * 4 * LPR + c * 4);
+            v[u][p][0] = x.x; v[u][p][1] = x.y; v[u][p][2] = x.z; v[u][p][3] = x.w;
+          } else {
+#pragma unroll
+            for (int q2 = 0; q2 < 4; ++q2) v[u][p][q2] = 0.f;
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+#pragma unroll
+          for (int q2 = 0; q2 < 4; ++q2) {
+            if constexpr (WEIGHTED) acc[p][q2] += wq[u] * v[u][p][q2];
+            else acc[p][q2] += v[u][p][q2];
+          }
+    }
+  }
+  if constexpr (OPT == kOptSGD) {
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) w[p][q] -= lr * acc[p][q];
+  } else {
+    float ss = 0.f;
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) ss += act[p] ? acc[p][q] * acc[p][q] : 0.f;
+#pragma unroll
+    for (int msk = 1; msk < LPR; msk <<= 1) ss += __shfl_xor(ss, msk);
+    const float mnew = mom + ss / static_cast<float>(D);
+    const float denom = sqrtf(mnew) + eps;
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) w[p][q] -= lr * acc[p][q] / denom;
+    if (c == 0) momentum[key] = mnew;
+  }
+#pragma unroll
+  for (int p = 0; p < NP; ++p)
+    if (act[p]) store_vec4<DT>(wrow + p * 4 * LPR + c * 4, w[p]);
+}
+
+// Short runs of one D bucket, list[0 .. n).  A wave step takes 2 x RPW_S consecutive runs.
+// When every run of the step has at most `tiny` lookups, each is served by LPR_T = LPR_S / 2
+// lanes holding NPT = 2 float4 chunks a lane, all of them at once (twice the runs in flight:
+// such runs wait on memory, not on bandwidth); otherwise the step runs as two halves of
+// RPW_S runs with LPR_S lanes each.  Rows wider than 256 columns or narrower than 64 have
+// one mode only (NPT == NPS).
+template <int DT, int BD, int NPS, int NPT, int OPT, bool WEIGHTED, int US, int UT>
 __global__ __launch_bounds__(kBlock) void short_run_kernel(
     typename Fmt<DT>::S* __restrict__ W, float* __restrict__ momentum,
     const float* __restrict__ grad_out, const uint32_t* __restrict__ pay,
     const uint32_t* __restrict__ bag_of, const float* __restrict__ psw,
-    const uint4* __restrict__ list, const int32_t* __restrict__ count_ptr,
+    const uint4* __restrict__ list, const int32_t* __restrict__ count_ptr, int64_t cap, int tiny,
     const int64_t* __restrict__ meta, int32_t B, int32_t out_width, float lr, float eps) {
-  using S = typename Fmt<DT>::S;
-  constexpr int LPR = BD / (4 * NP);  // lanes per run; each lane owns NP float4 column chunks
-  constexpr int RPW = kWave / LPR;     // runs per wave
-  static_assert(LPR >= 1 && LPR <= kWave && (LPR & (LPR - 1)) == 0, "lanes per run");
+  constexpr int LPR_S = BD / (4 * NPS), LPR_T = BD / (4 * NPT);  // lanes per run
+  constexpr int RPW_S = kWave / LPR_S;                            // runs per half step
+  static_assert(LPR_S >= 1 && LPR_S <= kWave && (LPR_S & (LPR_S - 1)) == 0, "lanes per run");
+  static_assert(NPT == NPS || LPR_T * 2 == LPR_S, "tiny steps halve the lanes per run");
   const int lane = lane_id();
-  const int g = lane / LPR;
-  const int c = lane % LPR;
-  const int64_t n = *count_ptr;
-  const int64_t sub = ((static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x) >> 6) * RPW + g;
-  const int64_t nsub = ((static_cast<int64_t>(gridDim.x) * kBlock) >> 6) * RPW;
-  for (int64_t i = sub; i < n; i += nsub) {
-    const uint4 dsc = list[i];
-    const uint32_t key = dsc.x, start = dsc.y, len = dsc.z;
-    const int t = static_cast<int>(dsc.w);
-    const TableMeta m = load_meta(meta, t);
-    const int D = static_cast<int>(m.D);
-    S* wrow = W + m.w_base + (static_cast<int64_t>(key) - m.row_base) * D;
-    const int64_t bag_lo = static_cast<int64_t>(t) * B;
-    float w[NP][4];
-    bool act[NP];
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      const int col = p * 4 * LPR + c * 4;
-      act[p] = col < D;
-      if (act[p]) {
-        load_vec<DT, 4>(wrow + col, w[p]);
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) w[p][q] = 0.f;
+  const int64_t n = min(static_cast<int64_t>(*count_ptr), cap);
+  const int64_t wave = (static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x) >> 6;
+  const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * kBlock) >> 6;
+  for (int64_t i0 = wave * 2 * RPW_S; i0 < n; i0 += nwaves * 2 * RPW_S) {
+    if constexpr (NPT != NPS) {
+      const int64_t it = i0 + lane / LPR_T;
+      const uint4 dsc = it < n ? list[it] : make_uint4(0u, 0u, 0u, 0u);
+      if (__ballot(it < n && dsc.z > static_cast<uint32_t>(tiny)) == 0) {
+        if (it < n)
+          short_run_one<DT, NPT, LPR_T, OPT, WEIGHTED, UT>(W, momentum, grad_out, pay, bag_of, psw, dsc,
+                                                           lane % LPR_T, meta, B, out_width, lr, eps);
+        continue;
       }
     }
-    float mom = 0.f;
-    if constexpr (OPT == kOptAdagrad) mom = momentum[key];
-    float acc[NP][4];
-#pragma unroll
-    for (int p = 0; p < NP; ++p)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) acc[p][q] = 0.f;
-    for (uint32_t j0 = 0; j0 < len; j0 += LPR) {
-      const int nb = static_cast<int>(min<uint32_t>(LPR, len - j0));
-      int32_t myb = -1;
-      float myw = 1.f;
-      if (c < nb) {
-        const uint32_t pv = pay[start + j0 + c];
-        int64_t bag;
-        if constexpr (WEIGHTED) {
-          bag = bag_of[pv];
-          myw = psw[pv];
-        } else {
-          bag = pv;
-        }
-        const int64_t br = bag - bag_lo;
-        myb = (br >= 0 && br < B) ? static_cast<int32_t>(br) : -1;
-      }
-      for (int q0 = 0; q0 < nb; q0 += UNROLL) {
-        float v[UNROLL][NP][4];
-        float wq[UNROLL];
-#pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-          const int q = q0 + u;
-          const int b = __shfl(myb, q, LPR);
-          wq[u] = WEIGHTED ? __shfl(myw, q, LPR) : 1.f;
-          const bool ok = q < nb && b >= 0;
-          const float* grow = grad_out + static_cast<int64_t>(b) * out_width + m.col_base;
-#pragma unroll
-          for (int p = 0; p < NP; ++p) {
-            if (ok && act[p]) {
-              const f32x4 x = load_f4(grow + p * 4 * LPR + c * 4);
-              v[u][p][0] = x.x; v[u][p][1] = x.y; v[u][p][2] = x.z; v[u][p][3] = x.w;
-            } else {
-#pragma unroll
-              for (int q2 = 0; q2 < 4; ++q2) v[u][p][q2] = 0.f;
-            }
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < UNROLL; ++u)
-#pragma unroll
-          for (int p = 0; p < NP; ++p)
-#pragma unroll
-            for (int q2 = 0; q2 < 4; ++q2) {
-              if constexpr (WEIGHTED) acc[p][q2] += wq[u] * v[u][p][q2];
-              else acc[p][q2] += v[u][p][q2];
-            }
-      }
+#pragma unroll 1
+    for (int h = 0; h < 2; ++h) {
+      const int64_t i = i0 + h * RPW_S + lane / LPR_S;
+      if (i < n)
+        short_run_one<DT, NPS, LPR_S, OPT, WEIGHTED, US>(W, momentum, grad_out, pay, bag_of, psw, list[i],
+                                                         lane % LPR_S, meta, B, out_width, lr, eps);
     }
-    if constexpr (OPT == kOptSGD) {
-#pragma unroll
-      for (int p = 0; p < NP; ++p)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) w[p][q] -= lr * acc[p][q];
-    } else {
-      float ss = 0.f;
-#pragma unroll
-      for (int p = 0; p < NP; ++p)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) ss += act[p] ? acc[p][q] * acc[p][q] : 0.f;
-#pragma unroll
-      for (int msk = 1; msk < LPR; msk <<= 1) ss += __shfl_xor(ss, msk);
-      const float mnew = mom + ss / static_cast<float>(D);
-      const float denom = sqrtf(mnew) + eps;
-#pragma unroll
-      for (int p = 0; p < NP; ++p)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) w[p][q] -= lr * acc[p][q] / denom;
-      if (c == 0) momentum[key] = mnew;
-    }
-#pragma unroll
-    for (int p = 0; p < NP; ++p)
-      if (act[p]) store_vec4<DT>(wrow + p * 4 * LPR + c * 4, w[p]);
   }
 }
 

@@ -8,39 +8,41 @@ namespace tbe {
 namespace detail {
 
 constexpr int kShortUnroll = 4;
-constexpr int kShortMinChunks = 1;  // float4 column chunks per lane at least (fewer lanes per run)
+constexpr int kTinyUnroll = 2;
 
-constexpr int short_chunks(int BD) {
+// float4 column chunks per lane: one (BD / 4 lanes per run) up to 256 columns, then all 64
+// lanes with BD / 256 chunks.  Steps of tiny runs of rows 64 .. 256 wide take two chunks
+// (half the lanes per run); narrower rows already put 8 or more runs in a wave step, wider
+// rows hold 8 or 16 floats a lane, and more would cost waves
+constexpr int short_chunks(int BD, bool tiny) {
   const int np = BD >= 256 ? BD / 256 : 1;
-  const int want = kShortMinChunks < BD / 4 ? kShortMinChunks : BD / 4;
-  return np > want ? np : want;
+  return (tiny && BD >= 64 && BD <= 256) ? 2 : np;
 }
 
 template <int DT, int BD, int OPT, bool WEIGHTED>
 tbe_status short_go(void* W, float* momentum, const float* psw, const float* grad_out,
                     const uint32_t* pay, const uint32_t* bag_of, const uint4* list,
-                    const int32_t* count, int64_t cap, const tbe_tables* tb, float lr, float eps,
-                    hipStream_t s) {
+                    const int32_t* count, int tiny, int64_t cap, const tbe_tables* tb,
+                    float lr, float eps, hipStream_t s) {
   using S = typename Fmt<DT>::S;
-  constexpr int NP = short_chunks(BD);
-  constexpr int LPR = BD / (4 * NP);
-  constexpr int RPW = kWave / LPR;
+  constexpr int NPS = short_chunks(BD, false), NPT = short_chunks(BD, true);
+  constexpr int RPW = 2 * kWave / (BD / (4 * NPS));  // runs per wave step
   const int64_t waves = (cap + RPW - 1) / RPW;
-  const auto kernel = short_run_kernel<DT, BD, NP, OPT, WEIGHTED, kShortUnroll>;
+  const auto kernel = short_run_kernel<DT, BD, NPS, NPT, OPT, WEIGHTED, kShortUnroll, kTinyUnroll>;
   const int grid = resident_grid(kernel, (waves + kWavesPerBlock - 1) / kWavesPerBlock);
   ProfScope ps("short_run", s);
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(kBlock), 0, s,
-                     static_cast<S*>(W), momentum, grad_out, pay, bag_of, psw, list, count, tb->meta,
-                     tb->B, tb->out_width, lr, eps);
+                     static_cast<S*>(W), momentum, grad_out, pay, bag_of, psw, list, count, cap, tiny,
+                     tb->meta, tb->B, tb->out_width, lr, eps);
   return check_launch("short_run");
 }
 
 template <int DT, int OPT, bool WEIGHTED>
 tbe_status short_bucket(int b, void* W, float* momentum, const float* psw, const float* grad_out,
                         const uint32_t* pay, const uint32_t* bag_of, const uint4* list,
-                        const int32_t* count, int64_t cap, const tbe_tables* tb, float lr, float eps,
-                        hipStream_t s) {
-#define TBE_SB(BD) short_go<DT, BD, OPT, WEIGHTED>(W, momentum, psw, grad_out, pay, bag_of, list, count, cap, tb, lr, eps, s)
+                        const int32_t* count, int tiny, int64_t cap,
+                        const tbe_tables* tb, float lr, float eps, hipStream_t s) {
+#define TBE_SB(BD) short_go<DT, BD, OPT, WEIGHTED>(W, momentum, psw, grad_out, pay, bag_of, list, count, tiny, cap, tb, lr, eps, s)
   switch (b) {
     case 0: return TBE_SB(4);
     case 1: return TBE_SB(8);
@@ -107,14 +109,13 @@ tbe_status launch_short_and_apply(const tbe_tables* tb, void* W, float* momentum
   for (int b = 0; b < TBE_NUM_BUCKETS; ++b) {
     if (!L.cap_short[b]) continue;
     const uint4* list = reinterpret_cast<const uint4*>(ws + L.short_list[b]);
+    const int64_t cap = L.cap_short[b];
     const int32_t* cnt = counters + kShort0 + b;
-    tbe_status st;
-    if (opt == kOptSGD)
-      st = psw ? detail::short_bucket<DT, kOptSGD, true>(b, W, momentum, psw, grad_out, pay, bag_of, list, cnt, L.cap_short[b], tb, lr, eps, s)
-               : detail::short_bucket<DT, kOptSGD, false>(b, W, momentum, psw, grad_out, pay, bag_of, list, cnt, L.cap_short[b], tb, lr, eps, s);
-    else
-      st = psw ? detail::short_bucket<DT, kOptAdagrad, true>(b, W, momentum, psw, grad_out, pay, bag_of, list, cnt, L.cap_short[b], tb, lr, eps, s)
-               : detail::short_bucket<DT, kOptAdagrad, false>(b, W, momentum, psw, grad_out, pay, bag_of, list, cnt, L.cap_short[b], tb, lr, eps, s);
+#define TBE_SHORT(OPT, WTD) \
+  detail::short_bucket<DT, OPT, WTD>(b, W, momentum, psw, grad_out, pay, bag_of, list, cnt, cfg.tiny, cap, tb, lr, eps, s)
+    const tbe_status st = opt == kOptSGD ? (psw ? TBE_SHORT(kOptSGD, true) : TBE_SHORT(kOptSGD, false))
+                                         : (psw ? TBE_SHORT(kOptAdagrad, true) : TBE_SHORT(kOptAdagrad, false));
+#undef TBE_SHORT
     if (st) return st;
   }
   if (L.cap_long == 0) return TBE_OK;

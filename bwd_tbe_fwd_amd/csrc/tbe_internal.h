@@ -52,6 +52,7 @@ constexpr int kRadixTile = kBlock * kRadixItems;      // 4096 keys
 struct Config {
   int threshold, chunk, hist_enable, fwd_unroll, bwd_unroll, sort_blocks, bag_windows, fused_long;
   int pretransposed, bags_per_wave, bwd_streams;
+  int tiny;  // wave steps of short runs of at most this many lookups: half the lanes per run
 };
 Config resolve_config(const tbe_config* c);
 

@@ -120,6 +120,9 @@ typedef struct {
   int32_t bwd_streams;     /* backward: 2 = long runs (chunks, apply) on the library's second stream,
                               concurrent with the short runs; 1 = one stream; 0 (default): 2 when
                               the tables' widths fall in two or more short-run buckets */
+  int32_t tiny_runs;       /* backward: a wave step whose short runs all have at most this many
+                              lookups serves twice as many runs with half the lanes each (rows of
+                              64 .. 256 columns); default 8, 0: off */
 } tbe_config;
 
 /* Device-side view of the transpose, for inspection by tests (tbe_transpose). */
@@ -129,7 +132,7 @@ typedef struct {
   const uint32_t* run_key;         /* [N] key of run r (first num_runs used) */
   const uint32_t* run_start;       /* [N+1] first sorted position of run r; run_start[num_runs] = N */
   const int32_t* counters;         /* [16]: 0 runs, 1 long runs, 2 chunks, 3..11 short runs per
-                                      bucket (next_pow2(D) = 4 .. 1024) */
+                                      bucket (next_pow2(D) = 4 .. 1024), 12 keys the sort covers */
   const uint32_t* long_list;       /* [cap][4] {key, start, len, first chunk} per long run */
   const uint32_t* long_table;      /* [cap] table of each long run */
   const uint32_t* chunk_list;      /* [cap][2] {long-run slot, chunk number} per chunk */

@@ -110,6 +110,7 @@ def test_config_defaults():
     assert c.bag_windows <= 1 and c.fused_long == 0 and c.sort_blocks == 0
     assert c.pretransposed == 0 and c.bags_per_wave == 0  # 0: chosen from the batch shape
     assert c.bwd_streams == 0  # 0: chosen from the tables' widths
+    assert c.tiny_runs == 8    # short runs of <= 8 lookups: half the lanes per run
 
 
 def test_workspace_histogram_table_partials():

@@ -353,3 +353,22 @@ def test_hist_backward_table_last(B):
     bt = ti.make_batch(spec, 101)
     db, _, _, _ = run_and_check(bt, what=f"hist last B={B}")
     assert db.tables.c.hist_table == 1
+
+
+@pytest.mark.parametrize("n", ["uniform", "mixed", "skewed"])
+@pytest.mark.parametrize("tiny", [0, 1, 8, 64])
+def test_tiny_run_steps(n, tiny):
+    """Wave steps whose short runs all have at most tiny_runs lookups serve twice the runs
+    with half the lanes each: the oracle's step either way, and with SGD (no cross-lane
+    reduction) the same bits as with those steps off."""
+    spec = small_spec(n)
+    flush_print(f"tiny runs {n} tiny={tiny}")
+    bt = ti.make_batch(spec, 61)
+    cfg = tbe.make_config(tiny_runs=tiny, long_threshold=32, chunk=16)
+    run_and_check(bt, cfg, what=f"tiny {n} {tiny}")
+    W = {}
+    for t in (0, tiny):
+        db = DevBatch(bt)
+        W[t], _ = db.backward(tbe.make_config(tiny_runs=t, long_threshold=32, chunk=16), optimizer="sgd")
+        torch.cuda.synchronize()
+    assert torch.equal(W[0].cpu().view(torch.uint8), W[tiny].cpu().view(torch.uint8))
