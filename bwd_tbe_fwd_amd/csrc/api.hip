@@ -288,7 +288,7 @@ void tbe_config_default(tbe_config* cfg) {
   cfg->long_threshold = 256;
   cfg->chunk = 256;
   cfg->hist_enable = 1;
-  cfg->fwd_unroll = 8;
+  cfg->fwd_unroll = 4;
   cfg->bwd_unroll = 2;
   cfg->sort_blocks = 0;
   cfg->bag_windows = 1;

@@ -367,10 +367,16 @@ tbe_status gather_go(const tbe_tables* tb, const void* W, const IndexArgs& ia, c
                      const_cast<IT*>(static_cast<const IT*>(ia.indices)),                           \
                      static_cast<const OT*>(ia.offsets), psw, out, tb->meta, skip, nt, tb->B,         \
                      tb->out_width, ia.N, group, repair_counts)
-  if (repair_counts) TBE_FWD_LAUNCH(8, true);
-  else if (unroll <= 2) TBE_FWD_LAUNCH(2, false);
-  else if (unroll <= 4) TBE_FWD_LAUNCH(4, false);
-  else TBE_FWD_LAUNCH(8, false);
+  if (repair_counts) {
+    if (unroll <= 4) TBE_FWD_LAUNCH(4, true);
+    else TBE_FWD_LAUNCH(8, true);
+  } else if (unroll <= 2) {
+    TBE_FWD_LAUNCH(2, false);
+  } else if (unroll <= 4) {
+    TBE_FWD_LAUNCH(4, false);
+  } else {
+    TBE_FWD_LAUNCH(8, false);
+  }
 #undef TBE_FWD_LAUNCH
   return check_launch("fwd_gather");
 }

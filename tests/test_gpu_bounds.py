@@ -116,3 +116,31 @@ def test_fused_bounds_forward_equals_check_then_forward(weighted, hist, itype):
     ref, ref_abs = oracle.forward(spec.T, spec.B, bt.E, bt.D, bt.weights.double().numpy(), exp_idx,
                                   exp_off, None if bt.psw is None else bt.psw.double().numpy())
     check_forward(out.cpu().numpy(), ref, ref_abs, False, "fused bounds forward")
+
+
+@pytest.mark.parametrize("weighted", [False, True])
+def test_fused_bounds_forward_unroll_is_bitwise_neutral(weighted):
+    """The fused id check pools with 4 or 8 row loads in flight per lane group: the same
+    output bits, repaired arrays and counts either way."""
+    tables = (ti.TableSpec(500, 32, ("poisson", 5.0, None, None), ("zipf", 1.1, None)),
+              ti.TableSpec(3000, 128, ("poisson", 40.0, None, None)),
+              ti.TableSpec(200, 256, ("poisson", 3.0, None, None)))
+    spec = ti.BatchSpec("fused unroll", tables, B=777, w_dtype=torch.bfloat16, w_range=0.05,
+                        weighted=weighted)
+    bt, idx, off = _faulty_batch(spec, 5)
+    t = tbe.Tables(bt.E, bt.D, bt.B, bt.w_dtype, device="cuda")
+    res = []
+    for u in (4, 8):
+        d_idx, d_off = torch.as_tensor(idx).cuda(), torch.as_tensor(off).cuda()
+        out = torch.full((bt.B, sum(bt.D)), float("nan"), device="cuda")
+        counts = torch.full((2,), -1, dtype=torch.int64, device="cuda")
+        ws = tbe.workspace(tbe.tbe_bounds_check_workspace_bytes(t))
+        psw = None if bt.psw is None else bt.psw.cuda()
+        tbe.tbe_forward_repair(t, bt.weights.cuda(), d_idx, d_off, psw, out, counts, ws,
+                               tbe.make_config(fwd_unroll=u))
+        torch.cuda.synchronize()
+        res.append((out.cpu(), d_idx.cpu(), d_off.cpu(), counts.cpu()))
+    assert torch.equal(res[0][0].view(torch.int32), res[1][0].view(torch.int32))
+    for a, b in zip(res[0][1:], res[1][1:]):
+        assert torch.equal(a, b)
+    assert res[0][3][0] > 0
