@@ -146,6 +146,7 @@ struct Carver {
   }
 };
 constexpr int kDefaultSortBlocks = 4096;
+constexpr int kClsBlocks = 4096;  // classification workgroups at most (the scan takes up to 4096)
 constexpr int kMaxSortBlocks = 4096;
 }  // namespace
 
@@ -182,7 +183,7 @@ BwdLayout bwd_layout(const tbe_tables* tb, int64_t N, int weighted, const Config
   L.nblocks = static_cast<int>((n1 + L.seg - 1) / L.seg);
   L.sort_hist = c.take((static_cast<size_t>(kRadixDigits) * L.nblocks + kRadixDigits) * 4);
   L.seg_cnt = c.take(static_cast<size_t>(L.nblocks) * 4);
-  L.cls_blocks = static_cast<int>(hmax(1, hmin(1024, (n1 + kBlock - 1) / kBlock)));
+  L.cls_blocks = static_cast<int>(hmax(1, hmin(kClsBlocks, (n1 + kBlock - 1) / kBlock)));
   L.cls_cnt = c.take(static_cast<size_t>(TBE_NUM_BUCKETS + 2) * L.cls_blocks * 4);
   // long-run chunks grouped by (table, window of bags); at most 4096 groups
   L.nwin = 1;

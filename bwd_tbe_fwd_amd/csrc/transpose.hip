@@ -472,18 +472,26 @@ constexpr int kCats = 1 + TBE_NUM_BUCKETS;  // 0: long, 1 + b: short bucket b
 constexpr int kClsRows = kCats + 1;         // + chunks of long runs
 constexpr int kLdsTables = 2048;
 
+// row bases and widths of the tables in dynamic LDS (sized for T at launch: a few hundred
+// bytes for tens of tables, so LDS does not limit the workgroups a CU holds)
 struct TableLds {
-  int64_t rb[kLdsTables + 1];
-  int32_t D[kLdsTables];
+  int64_t* rb;  // [T + 1]
+  int32_t* D;   // [T]
 };
+inline size_t table_lds_bytes(int T) {
+  return T <= kLdsTables ? static_cast<size_t>(T + 1) * 8 + static_cast<size_t>(T) * 4 : 0;
+}
 
-__device__ __forceinline__ void load_tables(TableLds& s, const int64_t* __restrict__ meta, int T) {
+__device__ __forceinline__ TableLds load_tables(const int64_t* __restrict__ meta, int T) {
+  extern __shared__ __align__(8) char s_dyn[];
+  TableLds s{reinterpret_cast<int64_t*>(s_dyn), reinterpret_cast<int32_t*>(s_dyn + static_cast<size_t>(T + 1) * 8)};
   if (T <= kLdsTables)
     for (int t = threadIdx.x; t <= T; t += kBlock) {
       s.rb[t] = meta[4 * t];
       if (t < T) s.D[t] = static_cast<int32_t>(meta[4 * t + 3]);
     }
   __syncthreads();
+  return s;
 }
 
 __device__ __forceinline__ int lds_table_of_key(const TableLds& s, const int64_t* __restrict__ meta, int T,
@@ -529,10 +537,9 @@ __global__ __launch_bounds__(kBlock) void classify_count(
     const uint32_t* __restrict__ run_key, const uint32_t* __restrict__ run_start,
     const int32_t* __restrict__ counters, const int64_t* __restrict__ meta, int T,
     uint32_t total_rows, int threshold, int chunk, uint32_t* __restrict__ cls_cnt) {
-  __shared__ TableLds s_tab;
   __shared__ uint32_t s_cnt[kClsRows];
   if (threadIdx.x < kClsRows) s_cnt[threadIdx.x] = 0;
-  load_tables(s_tab, meta, T);
+  const TableLds s_tab = load_tables(meta, T);
   int64_t lo, hi;
   block_segment(counters[kRuns], lo, hi);
   for (int64_t r = lo + threadIdx.x; r < hi; r += kBlock) {
@@ -582,13 +589,12 @@ __global__ __launch_bounds__(kBlock) void classify_write(
     uint32_t total_rows, int threshold, int chunk, const uint32_t* __restrict__ cls_cnt,
     uint4* __restrict__ long_list, uint32_t* __restrict__ long_table, uint32_t* __restrict__ long_count,
     uint2* __restrict__ chunk_list, int64_t cap_long, int64_t cap_chunk, ShortLists lists) {
-  __shared__ TableLds s_tab;
   __shared__ uint32_t s_base[kClsRows];
   __shared__ uint32_t s_wcnt[kWavesPerBlock][kCats];
   __shared__ uint32_t s_tmp[kWavesPerBlock];
   const int lane = lane_id(), w = threadIdx.x >> 6;
   if (threadIdx.x < kClsRows) s_base[threadIdx.x] = cls_cnt[threadIdx.x * gridDim.x + blockIdx.x];
-  load_tables(s_tab, meta, T);
+  const TableLds s_tab = load_tables(meta, T);
   int64_t lo, hi;
   block_segment(counters[kRuns], lo, hi);
   for (int64_t tile = lo; tile < hi; tile += kBlock) {
@@ -750,10 +756,11 @@ tbe_status launch_transpose(const tbe_tables* tb, const IndexArgs& ia, int weigh
     uint32_t* cls_cnt = reinterpret_cast<uint32_t*>(ws + L.cls_cnt);
     const uint32_t total_rows = static_cast<uint32_t>(tb->total_rows);
     ProfScope ps("classify", s);
-    hipLaunchKernelGGL(classify_count, dim3(L.cls_blocks), dim3(kBlock), 0, s, run_key, run_start,
+    const size_t lds = table_lds_bytes(tb->T);
+    hipLaunchKernelGGL(classify_count, dim3(L.cls_blocks), dim3(kBlock), lds, s, run_key, run_start,
                        counters, tb->meta, tb->T, total_rows, cfg.threshold, cfg.chunk, cls_cnt);
     hipLaunchKernelGGL(classify_scan, dim3(kClsRows), dim3(kBlock), 0, s, cls_cnt, L.cls_blocks, counters);
-    hipLaunchKernelGGL(classify_write, dim3(L.cls_blocks), dim3(kBlock), 0, s, run_key, run_start,
+    hipLaunchKernelGGL(classify_write, dim3(L.cls_blocks), dim3(kBlock), lds, s, run_key, run_start,
                        counters, tb->meta, tb->T, total_rows, cfg.threshold, cfg.chunk, cls_cnt,
                        reinterpret_cast<uint4*>(ws + L.long_list), reinterpret_cast<uint32_t*>(ws + L.long_table),
                        reinterpret_cast<uint32_t*>(ws + L.long_count),
