@@ -32,7 +32,8 @@ METRIC = "TBE fwd+bwd lookups/s and achieved HBM GB/s vs peak, 1 MI355X"
 HBM_PEAK_GBS = 8000.0
 KERNELS = ["bounds_offsets", "bounds_indices", "fwd_gather", "fwd_hist", "linearize",
            "radix_upsweep", "radix_scan", "radix_downsweep", "rle", "classify", "short_run",
-           "grad_accum", "long_apply", "hist_bwd_partial", "hist_bwd_apply"]
+           "grad_accum", "long_apply", "hist_bwd_partial", "hist_bwd_apply", "dense_select",
+           "dense_partial", "dense_apply"]
 
 
 # sources each timed kernel is built from: its counters in profiles/ are valid only while
@@ -42,6 +43,7 @@ KERNEL_SOURCES = {
     "fwd_hist": ["forward.hip", "tbe_device.h"],
     "short_run": ["backward_kernels.h", "backward_launch.h", "tbe_device.h"],
     "grad_accum": ["backward.hip", "backward_kernels.h", "tbe_device.h"],
+    "dense_partial": ["dense_backward.hip", "tbe_device.h"],
     "long_apply": ["backward_kernels.h", "backward_launch.h", "tbe_device.h"],
     "linearize": ["transpose.hip", "tbe_device.h"],
     "radix_upsweep": ["transpose.hip", "tbe_device.h"],
@@ -80,12 +82,17 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def batch_stats(bt: ti.Batch, hist_table: int, threshold=256, chunk=256):
+def batch_stats(bt: ti.Batch, hist_table: int, threshold=256, chunk=256, dense_min=2048,
+                dense_rows=128):
     """Host-side statistics of the drawn batch (from the inputs only), per table.  hist_table
-    (or -1): the table whose backward goes through the histogram kernels, not the runs."""
+    (or -1): the table whose backward goes through the histogram kernels, not the runs.  The
+    dense hot rows are picked as the library does: per eligible table (no per-sample weights,
+    16 <= D <= 128, D % 16 == 0, not the histogram table), its long runs of at least dense_min
+    lookups in key order, at most dense_rows of them (dense_min 0: none)."""
     idx = bt.indices.cpu().numpy().astype(np.int64)
     off = bt.offsets.cpu().numpy().astype(np.int64)
     B = bt.B
+    dmin = max(dense_min, threshold) if dense_min > 0 else 0
     per = []
     for t in range(bt.T):
         lk = idx[off[t * B]:off[(t + 1) * B]]
@@ -93,11 +100,21 @@ def batch_stats(bt: ti.Batch, hist_table: int, threshold=256, chunk=256):
         c = c[c > 0]
         lg = c >= threshold
         lens = np.diff(off[t * B:(t + 1) * B + 1])
-        per.append(dict(D=bt.D[t], N=int(lk.size), U=int(c.size), hottest=int(c.max()) if c.size else 0,
+        D = bt.D[t]
+        ok = (dmin > 0 and bt.psw is None and 16 <= D <= 128 and D % 16 == 0 and t != hist_table)
+        dl = c[lg][c[lg] >= dmin][:dense_rows] if ok else c[:0]   # c is in key order
+        dn = np.zeros(c.size, dtype=bool)
+        if dl.size:
+            dn[np.flatnonzero(lg)[np.flatnonzero(c[lg] >= dmin)[:dense_rows]]] = True
+        gl = lg & ~dn                                                # long runs left to the chunks
+        per.append(dict(D=D, N=int(lk.size), U=int(c.size), hottest=int(c.max()) if c.size else 0,
                         tail=int(np.maximum(lens - 256, 0).sum()),   # lookups past a bag's first 256
                         long_runs=int(lg.sum()), long_lookups=int(c[lg].sum()),
                         short_runs=int((~lg).sum()), short_lookups=int(c[~lg].sum()),
-                        chunks=int(((c[lg] + chunk - 1) // chunk).sum()), hist=t == hist_table))
+                        chunks=int(((c[lg] + chunk - 1) // chunk).sum()),
+                        dense_rows=int(dl.size), dense_lookups=int(dl.sum()),
+                        gen_long_runs=int(gl.sum()), gen_long_lookups=int(c[gl].sum()),
+                        gen_chunks=int(((c[gl] + chunk - 1) // chunk).sum()), hist=t == hist_table))
     tot = lambda k, only_runs=False: sum(p[k] for p in per if not (only_runs and p["hist"]))
     return dict(N=int(idx.size), TB=bt.T * B, U=tot("U"), hottest=max(p["hottest"] for p in per),
                 short_runs=tot("short_runs", True), short_lookups=tot("short_lookups", True),
@@ -105,10 +122,11 @@ def batch_stats(bt: ti.Batch, hist_table: int, threshold=256, chunk=256):
                 chunks=tot("chunks", True), per_table=per)
 
 
-def algorithmic_bytes(bt: ti.Batch, st: dict, hoist: bool):
+def algorithmic_bytes(bt: ti.Batch, st: dict, hoist: bool, dense_P: int = 24):
     """What each kernel must move per launch (no credit for cache reuse), summed over tables
     with their own D.  hoist: the histogram forward keeps each bag's counts (64 u16) and the
-    histogram backward reads them and only the ids past a bag's first 256."""
+    histogram backward reads them and only the ids past a bag's first 256.  dense_P: the dense
+    path's partials per table."""
     s_w = bt.weights.element_size()
     s_i = bt.indices.element_size()
     s_o = bt.offsets.element_size()
@@ -132,11 +150,18 @@ def algorithmic_bytes(bt: ti.Batch, st: dict, hoist: bool):
         "short_run": sum(p["short_lookups"] * (4 + s_p + p["D"] * 4)
                          + p["short_runs"] * (16 + 2 * p["D"] * s_w + 8) for p in gen),
         # per lookup of a long run: payload (+ weight) + gradient row; per chunk: partial row
-        "grad_accum": sum(p["long_lookups"] * (4 + s_p + p["D"] * 4) + p["chunks"] * (8 + p["D"] * 4)
+        # (the long runs the dense path takes are skipped)
+        "grad_accum": sum(p["gen_long_lookups"] * (4 + s_p + p["D"] * 4) + p["gen_chunks"] * (8 + p["D"] * 4)
                           for p in gen),
         # per chunk: partial row read; per long run: descriptor, weight row r/w, state r/w
-        "long_apply": sum(p["chunks"] * p["D"] * 4 + p["long_runs"] * (20 + 2 * p["D"] * s_w + 8)
+        "long_apply": sum(p["gen_chunks"] * p["D"] * 4 + p["gen_long_runs"] * (20 + 2 * p["D"] * s_w + 8)
                           for p in gen),
+        # per table with dense rows: its ids, offsets and B x D gradient slice, and its
+        # partials (P per table, one row of D floats per dense row each)
+        "dense_partial": sum(p["N"] * s_i + B * (s_o + p["D"] * 4) + dense_P * p["dense_rows"] * p["D"] * 4
+                             for p in gen if p["dense_rows"]),
+        # per dense row: its P partial rows, weight row r/w, state r/w
+        "dense_apply": sum(p["dense_rows"] * (dense_P * p["D"] * 4 + 2 * p["D"] * s_w + 8) for p in gen),
         "bounds_indices": st["N"] * s_i,
         "bounds_offsets": 3 * (st["TB"] + 1) * s_o,
         "rle": 3 * runs_N * 4 + U * 8,
@@ -328,7 +353,11 @@ def main():
     fwd_ms = float(np.median([a.elapsed_time(b) for a, b, _ in ev]))
     bwd_ms = float(np.median([b.elapsed_time(c) for _, b, c in ev]))
     N = st["N"]
-    ab = algorithmic_bytes(bt, st, args.hoist == "on")
+    # the dense path writes one partial per workgroup; its kernel holds 3 workgroups per CU and
+    # launches one round of them over the tables
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    dense_P = max(1, min(64, 2048 // bt.T, (bt.B + 63) // 64, cus * 3 // bt.T))
+    ab = algorithmic_bytes(bt, st, args.hoist == "on", dense_P)
     dom_avg_ms = dom_ms / max(launches, 1)
     dom_bytes = ab.get(dominant, 0)
     achieved = dom_bytes / (dom_avg_ms * 1e-3) / 1e9 if dom_avg_ms > 0 else 0.0

@@ -47,7 +47,8 @@ class tbe_config(ctypes.Structure):
                 ("bwd_unroll", ctypes.c_int32), ("sort_blocks", ctypes.c_int32),
                 ("bag_windows", ctypes.c_int32), ("fused_long", ctypes.c_int32),
                 ("pretransposed", ctypes.c_int32), ("bags_per_wave", ctypes.c_int32),
-                ("bwd_streams", ctypes.c_int32), ("tiny_runs", ctypes.c_int32)]
+                ("bwd_streams", ctypes.c_int32), ("tiny_runs", ctypes.c_int32),
+                ("dense_min", ctypes.c_int32)]
 
 
 class tbe_runs_view(ctypes.Structure):

@@ -126,6 +126,8 @@ Config resolve_config(const tbe_config* c) {
   r.bags_per_wave = (c->bags_per_wave >= 1 && c->bags_per_wave <= 64) ? c->bags_per_wave : 0;
   r.bwd_streams = (c->bwd_streams == 1 || c->bwd_streams == 2) ? c->bwd_streams : 0;
   r.tiny = c->tiny_runs > 0 ? static_cast<int>(hmin(c->tiny_runs, r.threshold - 1)) : 0;
+  // a dense row is a long run
+  r.dense_min = c->dense_min > 0 ? static_cast<int>(hmax(c->dense_min, r.threshold)) : 0;
   return r;
 }
 
@@ -203,6 +205,17 @@ BwdLayout bwd_layout(const tbe_tables* tb, int64_t N, int weighted, const Config
     L.hist_partial = c.take(static_cast<size_t>(kHistBwdBlocks) * 64 * 128 * 4);
     L.hist_count = c.take(static_cast<size_t>(kHistBwdBlocks) * 64 * 4);
     L.hist_saved = c.take(static_cast<size_t>((tb->B + 15) / 16 * 16) * 64 * 2);
+  }
+  if (cfg.dense_min > 0 && !weighted && !cfg.fused_long && tb->B > 0) {
+    // partials per table: about 2048 workgroups in all, at most 64 a table, at most one per
+    // 64-bag step
+    const int64_t steps = (static_cast<int64_t>(tb->B) + 63) / 64;
+    L.dense_on = 1;
+    L.dense_P = static_cast<int>(hmax(1, hmin(hmin(64, 2048 / tb->T), steps)));
+    L.dense_rows = c.take(static_cast<size_t>(tb->T) * kDenseRows * 4);
+    L.dense_cnt = c.take(static_cast<size_t>(tb->T) * 4);
+    L.long_flag = c.take(static_cast<size_t>(L.cap_long) * 4);
+    L.dense_partial = c.take(static_cast<size_t>(tb->T) * L.dense_P * kDenseRows * 128 * 4);
   }
   L.counters = c.take(kNumCounters * 4);
   L.total = c.off;
@@ -298,6 +311,7 @@ void tbe_config_default(tbe_config* cfg) {
   cfg->bags_per_wave = 0;
   cfg->bwd_streams = 0;
   cfg->tiny_runs = 8;
+  cfg->dense_min = 2048;
 }
 
 int64_t tbe_meta_entries(int32_t T) { return T >= 0 ? static_cast<int64_t>(TBE_META_FIELDS) * (T + 1) : 0; }
@@ -594,19 +608,30 @@ static tbe_status backward_common(const tbe_tables* tables, void* weights, float
                                              saved, s))
       return st;
   }
+  // the hottest long runs of each table go to the dense path (flags read by the chunk and
+  // apply kernels)
+  if (L.dense_on)
+    if (tbe_status st = launch_dense_select(tables, ws, L, hist, cfg, s)) return st;
   // automatic: short runs of several widths are several short launches, whose tails leave
   // room for the long runs
   int buckets = 0;
   for (int b = 0; b < TBE_NUM_BUCKETS; ++b) buckets += L.cap_short[b] > 0;
   const int streams = cfg.bwd_streams ? cfg.bwd_streams : (buckets >= 2 ? 2 : 1);
-  if (streams < 2 || L.cap_long == 0)
-    return launch_backward_update(tables, weights, momentum, opt, psw, grad_out, lr, eps, ws, L,
-                                  final_buf, cfg, s, s);
-  // long runs on a second stream, concurrent with the short runs (disjoint rows)
+  if (streams < 2 || L.cap_long == 0) {
+    if (tbe_status st = launch_backward_update(tables, weights, momentum, opt, psw, grad_out, lr, eps, ws,
+                                               L, final_buf, cfg, s, s))
+      return st;
+    return L.dense_on ? launch_dense_backward(tables, weights, momentum, opt, ia, grad_out, lr, eps, ws, L, s)
+                      : TBE_OK;
+  }
+  // long runs (and the dense rows) on a second stream, concurrent with the short runs
+  // (disjoint rows)
   Fork fork(s);
   if (tbe_status st = fork.status()) return st;
-  const tbe_status st = launch_backward_update(tables, weights, momentum, opt, psw, grad_out, lr, eps,
-                                               ws, L, final_buf, cfg, s, fork.side());
+  tbe_status st = launch_backward_update(tables, weights, momentum, opt, psw, grad_out, lr, eps, ws, L,
+                                         final_buf, cfg, s, fork.side());
+  if (!st && L.dense_on)
+    st = launch_dense_backward(tables, weights, momentum, opt, ia, grad_out, lr, eps, ws, L, fork.side());
   const tbe_status st_j = fork.join();
   return st ? st : st_j;
 }

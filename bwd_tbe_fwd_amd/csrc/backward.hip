@@ -21,13 +21,15 @@ __global__ __launch_bounds__(kBlock) void grad_accum_kernel(
     const uint4* __restrict__ long_list, const uint32_t* __restrict__ long_table,
     const uint2* __restrict__ chunk_list, const int32_t* __restrict__ counters,
     const int64_t* __restrict__ meta, int32_t B, int32_t out_width, int chunk, int max_D,
-    const uint32_t* __restrict__ order, float* __restrict__ partial) {
+    const uint32_t* __restrict__ order, const uint32_t* __restrict__ long_flag,
+    float* __restrict__ partial) {
   const int64_t wave = (static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x) >> 6;
   const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * kBlock) >> 6;
   const int64_t n = counters[kChunks];
   for (int64_t i = wave; i < n; i += nwaves) {
     const int64_t cix = order ? order[i] : i;
     const uint2 ch = chunk_list[cix];
+    if (long_flag && long_flag[ch.x]) continue;  // a dense row: updated by the dense path
     const uint4 L = long_list[ch.x];
     const int t = static_cast<int>(long_table[ch.x]);
     const TableMeta m = load_meta(meta, t);
@@ -119,6 +121,7 @@ tbe_status accum_go(const tbe_tables* tb, const float* psw, const float* grad_ou
                      reinterpret_cast<const uint2*>(ws + L.chunk_list),                           \
                      reinterpret_cast<const int32_t*>(ws + L.counters), tb->meta, tb->B,           \
                      tb->out_width, cfg.chunk, tb->max_D, order,                                  \
+                     L.dense_on ? reinterpret_cast<const uint32_t*>(ws + L.long_flag) : nullptr,  \
                      reinterpret_cast<float*>(ws + L.partial))
   if (cfg.bwd_unroll <= 2) TBE_ACC(2);
   else if (cfg.bwd_unroll <= 4) TBE_ACC(4);

@@ -361,13 +361,14 @@ __global__ __launch_bounds__(kBlock) void long_apply_kernel(
     typename Fmt<DT>::S* __restrict__ W, float* __restrict__ momentum,
     const uint4* __restrict__ long_list, const uint32_t* __restrict__ long_table,
     const int32_t* __restrict__ counters, const int64_t* __restrict__ meta, int chunk, int max_D,
-    const float* __restrict__ partial, float lr, float eps) {
+    const float* __restrict__ partial, const uint32_t* __restrict__ long_flag, float lr, float eps) {
   using S = typename Fmt<DT>::S;
   __shared__ __align__(16) float s_red[kWavesPerBlock][TBE_MAX_D];
   __shared__ float s_tmp[kWavesPerBlock];
   const int lane = lane_id(), w = threadIdx.x >> 6;
   const int64_t n = counters[kLong];
   for (int64_t li = blockIdx.x; li < n; li += gridDim.x) {
+    if (long_flag && long_flag[li]) continue;  // a dense row: updated by the dense path
     const uint4 L = long_list[li];
     const int t = static_cast<int>(long_table[li]);
     const TableMeta m = load_meta(meta, t);

@@ -60,13 +60,14 @@ tbe_status short_bucket(int b, void* W, float* momentum, const float* psw, const
 template <int DT, int OPT>
 tbe_status apply_go(void* W, float* momentum, const uint4* long_list, const uint32_t* long_table,
                     const int32_t* counters, int64_t cap, const tbe_tables* tb, int chunk,
-                    const float* partial, float lr, float eps, hipStream_t s) {
+                    const float* partial, const uint32_t* long_flag, float lr, float eps, hipStream_t s) {
   using S = typename Fmt<DT>::S;
   const auto kernel = long_apply_kernel<DT, OPT>;
   const int grid = resident_grid(kernel, cap);
   ProfScope ps("long_apply", s);
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(kBlock), 0, s, static_cast<S*>(W),
-                     momentum, long_list, long_table, counters, tb->meta, chunk, tb->max_D, partial, lr, eps);
+                     momentum, long_list, long_table, counters, tb->meta, chunk, tb->max_D, partial, long_flag,
+                     lr, eps);
   return check_launch("long_apply");
 }
 
@@ -134,9 +135,10 @@ tbe_status launch_short_and_apply(const tbe_tables* tb, void* W, float* momentum
   const uint4* long_list = reinterpret_cast<const uint4*>(ws + L.long_list);
   const uint32_t* long_table = reinterpret_cast<const uint32_t*>(ws + L.long_table);
   const float* partial = reinterpret_cast<const float*>(ws + L.partial);
+  const uint32_t* long_flag = L.dense_on ? reinterpret_cast<const uint32_t*>(ws + L.long_flag) : nullptr;
   if (opt == kOptSGD)
-    return detail::apply_go<DT, kOptSGD>(W, momentum, long_list, long_table, counters, L.cap_long, tb, cfg.chunk, partial, lr, eps, s);
-  return detail::apply_go<DT, kOptAdagrad>(W, momentum, long_list, long_table, counters, L.cap_long, tb, cfg.chunk, partial, lr, eps, s);
+    return detail::apply_go<DT, kOptSGD>(W, momentum, long_list, long_table, counters, L.cap_long, tb, cfg.chunk, partial, long_flag, lr, eps, s);
+  return detail::apply_go<DT, kOptAdagrad>(W, momentum, long_list, long_table, counters, L.cap_long, tb, cfg.chunk, partial, long_flag, lr, eps, s);
 }
 
 }  // namespace tbe

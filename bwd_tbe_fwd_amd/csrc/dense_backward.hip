@@ -1,0 +1,439 @@
+// Backward of the hottest rows of large tables as a dense product.
+//
+// PyTorch blog "Modernizing Table Batched Embeddings with FBTriton", section 2
+// ("forward-state reuse and preprocessing") computes the gradient of the small
+// histogram table as per-bag row counts times grad_out on tensor cores instead
+// of a per-lookup gather.  The same identity holds for any set of rows R of any
+// table t: for r in R,
+//     g[r, :] = sum_b count_b[r] * grad_out[b, col_t : col_t + D],
+// which is the sum over every lookup of r of its bag's gradient row.  On the
+// sorted-run path a row with n lookups reads n gradient rows (n * 4D bytes);
+// here the table's B x D gradient slice is read once for all rows of R
+// together, plus the table's ids.  For rows looked up thousands of times
+// (the head of a skewed id distribution) that replaces most of the long-run
+// gradient traffic.
+//
+// gfx950 mapping.  dense_select (one wave per table) takes the table's long
+// runs of at least dense_min lookups, in key order, up to kDenseRows of them,
+// records their row ids (sorted, as the long list is in key order) and flags
+// their long-list slots so that the chunk and apply kernels skip them.
+// dense_partial: workgroup (t, p) takes the table's 64-bag steps p, p + P, ...;
+// each of its four waves counts the lookups of 16 of the step's bags that hit
+// a selected row (a bit filter in LDS, then a 7-step search of the sorted row
+// ids) into the shared count[128 rows][64 bags]; then wave w multiplies the
+// counts by gradient columns 32 w .. 32 w + 31 of the 64 bags on
+// v_mfma_f32_16x16x32_bf16.  The pages' compensated high/low product, made
+// exact: the fp32 gradient is split into three bf16 parts whose sum is exactly
+// its value, counts are exact in bf16 (byte by byte above 255), so every
+// product is exact and only the fp32 accumulation rounds.  (fp32 MFMA would
+// be 16x slower per flop: 128 rows x 64 bags x D per step is 137 GFLOP over
+// the large skewed batch.)  The 128 x 32 accumulator (8 x 2 tiles) stays in
+// registers across the steps and is written once as the workgroup's partial.
+// dense_apply sums a row's P partials in a fixed order and applies SGD or
+// row-wise Adagrad: results are bitwise repeatable.
+#include "backward_launch.h"
+
+namespace tbe {
+namespace {
+
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kDnCols = 128;     // max D; each wave owns 32 columns (2 MFMA N tiles)
+constexpr int kDnWaveBags = 16;  // bags one wave counts per step
+constexpr int kDnBags = kDnWaveBags * kWavesPerBlock;  // bags per step: MFMA K, 16 steps of 4
+constexpr int kDnLoads = 8;      // id loads in flight per lane while counting
+
+__device__ __forceinline__ bool dense_table_ok(int D, int t, int hist_t) {
+  return t != hist_t && D >= 16 && D <= kDnCols && D % 16 == 0;
+}
+
+// one wave per table: its long runs are long-list slots [lo, hi) (the list is in key order)
+__global__ __launch_bounds__(kBlock) void dense_select_kernel(
+    const uint4* __restrict__ long_list, const uint32_t* __restrict__ long_table,
+    const int32_t* __restrict__ counters, int64_t cap_long, const int64_t* __restrict__ meta, int T,
+    int hist_t, uint32_t dense_min, int32_t* __restrict__ dense_rows, int32_t* __restrict__ dense_cnt,
+    uint32_t* __restrict__ long_flag) {
+  const int lane = lane_id();
+  const int t = static_cast<int>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int64_t n = min(static_cast<int64_t>(counters[kLong]), cap_long);
+  // first slot of table t and of table t + 1
+  auto lower = [&](uint32_t v) {
+    int64_t lo = 0, hi = n;
+    while (lo < hi) {
+      const int64_t mid = (lo + hi) >> 1;
+      if (long_table[mid] < v) lo = mid + 1; else hi = mid;
+    }
+    return lo;
+  };
+  const int64_t s0 = lower(static_cast<uint32_t>(t)), s1 = lower(static_cast<uint32_t>(t) + 1);
+  const TableMeta m = load_meta(meta, t);
+  const bool ok = dense_table_ok(static_cast<int>(m.D), t, hist_t);
+  int taken = 0;
+  for (int64_t s = s0 + lane; s - lane < s1; s += kWave) {
+    const bool in = s < s1;
+    uint4 L = make_uint4(0u, 0u, 0u, 0u);
+    if (in) L = long_list[s];
+    const bool want = in && ok && L.z >= dense_min;
+    const uint64_t wm = __ballot(want);
+    const int rank = taken + __popcll(wm & lanemask_lt());
+    const bool take = want && rank < kDenseRows;
+    if (take) dense_rows[static_cast<int64_t>(t) * kDenseRows + rank] = static_cast<int32_t>(L.x - m.row_base);
+    if (in) long_flag[s] = take ? 1u : 0u;
+    taken = min(kDenseRows, taken + __popcll(wm));
+  }
+  if (lane == 0) dense_cnt[t] = taken;
+}
+
+// bf16 bits of a float whose low 16 bits are zero (exact)
+__device__ __forceinline__ short bf16_bits(float x) {
+  return static_cast<short>(__builtin_bit_cast(uint32_t, x) >> 16);
+}
+// x = hi + mid + lo exactly: each part keeps the top 8 significand bits of what is left
+// (truncation, so every subtraction is exact in fp32)
+__device__ __forceinline__ void split3(float x, short& hi, short& mid, short& lo) {
+  const float h = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, x) & 0xffff0000u);
+  const float r = x - h;
+  const float m = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, r) & 0xffff0000u);
+  const float l = r - m;  // at most 8 significant bits left
+  hi = bf16_bits(h);
+  mid = bf16_bits(m);
+  lo = static_cast<short>(__builtin_bit_cast(uint32_t, l) >> 16);
+}
+
+// The 17 offsets of a wave's 16 bags (lanes 0..16; waves past the last bag read the
+// table's end offset), clamped to [0, N].
+template <typename OT>
+__device__ __forceinline__ int32_t wave_offsets(const OT* __restrict__ offsets, int64_t bag0, int64_t bw,
+                                                int nbw, int32_t B, int64_t N) {
+  const int lane = lane_id();
+  int32_t o = 0;
+  if (lane <= kDnWaveBags) {
+    const int64_t v = static_cast<int64_t>(offsets[bag0 + min(bw + min(lane, nbw), static_cast<int64_t>(B))]);
+    o = static_cast<int32_t>(min(max(v, static_cast<int64_t>(0)), N));
+  }
+  return o;
+}
+
+// Workgroup (t, p) = blockIdx.x: table t's 64-bag steps p, p + P, ...
+// The product runs on v_mfma_f32_16x16x32_bf16 with every operand exact in bf16: the gradient
+// as three bf16 parts (hi + mid + lo = its fp32 value), a count below 256 as itself, larger
+// counts byte by byte (each byte times its power of 256).  Every product is therefore exact,
+// and only the fp32 accumulation rounds, as in the fp32 sums of the chunk path.  A step's
+// gradient rows and ids are requested together, and the next step's offsets before this
+// step's counting, so a step waits on memory about once.
+template <typename IT, typename OT>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void dense_partial_kernel(
+    const IT* __restrict__ indices, const OT* __restrict__ offsets, const float* __restrict__ grad_out,
+    const int64_t* __restrict__ meta, int32_t B, int32_t out_width, int64_t N, int P,
+    const int32_t* __restrict__ dense_rows, const int32_t* __restrict__ dense_cnt,
+    float* __restrict__ partial) {
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+  constexpr int kStride = kDnBags + 4;   // counts [row][bag]; rows padded against bank conflicts
+  constexpr int kBloomWords = 1024;      // 32768-bit filter of the selected rows (id mod 32768)
+  __shared__ __align__(16) uint32_t s_cnt[kDenseRows * kStride];
+  __shared__ uint32_t s_bloom[kBloomWords];
+  __shared__ int32_t s_rows[kDenseRows];
+  __shared__ int32_t s_off[kWavesPerBlock][kDnWaveBags + 1];
+  __shared__ uint32_t s_big;
+  const int t = static_cast<int>(blockIdx.x) / P, p = static_cast<int>(blockIdx.x) % P;
+  const int nd = dense_cnt[t];
+  if (nd == 0) return;  // uniform over the workgroup
+  const int ntiles = (nd + 15) / 16;
+  const TableMeta m = load_meta(meta, t);
+  const int D = static_cast<int>(m.D);
+  const int64_t E = m.E;
+  const int lane = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int cw = 32 * w;                // this wave's first column
+  const int c2 = cw + 2 * (lane & 15);  // result columns c2 (tile 0) and c2 + 1 (tile 1)
+  // the selected rows, ascending (the unused tail padded with a value no id matches), and
+  // the filter that lets most ids skip the search
+  for (int i = threadIdx.x; i < kBloomWords; i += kBlock) s_bloom[i] = 0u;
+  for (int i = threadIdx.x; i < kDenseRows; i += kBlock)
+    s_rows[i] = i < nd ? dense_rows[static_cast<int64_t>(t) * kDenseRows + i] : 0x7fffffff;
+  __syncthreads();
+  for (int i = threadIdx.x; i < nd; i += kBlock) {
+    const uint32_t h = static_cast<uint32_t>(s_rows[i]) & (32 * kBloomWords - 1);
+    atomicOr(&s_bloom[h >> 5], 1u << (h & 31));
+  }
+  float4_t acc[kDenseRows / 16][2];
+#pragma unroll
+  for (int mt = 0; mt < kDenseRows / 16; ++mt) acc[mt][0] = acc[mt][1] = float4_t{0.f, 0.f, 0.f, 0.f};
+  int32_t* off = s_off[w];
+  const int64_t bag0 = static_cast<int64_t>(t) * B;
+  const int64_t steps = (static_cast<int64_t>(B) + kDnBags - 1) / kDnBags;
+  auto wave_bags = [&](int64_t st, int64_t& bw, int& nbw) {
+    const int nb = static_cast<int>(min<int64_t>(kDnBags, static_cast<int64_t>(B) - st * kDnBags));
+    bw = st * kDnBags + kDnWaveBags * w;
+    nbw = max(0, min(kDnWaveBags, nb - kDnWaveBags * w));
+  };
+  int32_t o_next = 0;
+  if (p < steps) {
+    int64_t bw;
+    int nbw;
+    wave_bags(p, bw, nbw);
+    o_next = wave_offsets(offsets, bag0, bw, nbw, B, N);
+  }
+  for (int64_t st = p; st < steps; st += P) {
+    const int64_t b0 = st * kDnBags;
+    const int nb = static_cast<int>(min<int64_t>(kDnBags, static_cast<int64_t>(B) - b0));
+    // gradient values: gv[8 kk + j] = bag 32 kk + 8 (l / 16) + j, columns c2, c2 + 1
+    f32x2 gv[16];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int i = 32 * kk + 8 * (lane >> 4) + j;
+        gv[8 * kk + j] = f32x2{0.f, 0.f};
+        if (i < nb && c2 < D)
+          gv[8 * kk + j] = *reinterpret_cast<const f32x2*>(grad_out + (b0 + i) * out_width + m.col_base + c2);
+      }
+    }
+    // this wave's bag range from the offsets fetched one step ahead (monotone running max)
+    int32_t o = o_next;
+    for (int d = 1; d < 32; d <<= 1) {
+      const int32_t u = __shfl_up(o, d);
+      if (lane >= d) o = max(o, u);
+    }
+    const int32_t o0 = read_lane(o, 0);
+    const int32_t n = read_lane(o, kDnWaveBags) - o0;
+    if (st + P < steps) {
+      int64_t bw;
+      int nbw;
+      wave_bags(st + P, bw, nbw);
+      o_next = wave_offsets(offsets, bag0, bw, nbw, B, N);
+    }
+    __syncthreads();  // every wave is done with the previous step's counts (and the filter is set)
+    if (threadIdx.x == 0) s_big = 0u;
+    if (lane <= kDnWaveBags) off[lane] = o - o0;
+    // this wave's 16 bag columns of every row
+#pragma unroll
+    for (int x = lane; x < kDenseRows * (kDnWaveBags / 4); x += kWave)
+      *reinterpret_cast<u32x4*>(&s_cnt[(x >> 2) * kStride + kDnWaveBags * w + 4 * (x & 3)]) = u32x4{0u, 0u, 0u, 0u};
+    __builtin_amdgcn_wave_barrier();
+    // every lookup of the wave's 16 bags that hits a selected row
+    bool big = false;
+    for (int32_t j0 = 0; j0 < n; j0 += kDnLoads * kWave) {
+      int64_t r[kDnLoads];
+#pragma unroll
+      for (int u = 0; u < kDnLoads; ++u) {
+        const int32_t j = j0 + u * kWave + lane;
+        r[u] = j < n ? static_cast<int64_t>(indices[o0 + j]) : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < kDnLoads; ++u) {
+        const int32_t j = j0 + u * kWave + lane;
+        if (static_cast<uint64_t>(r[u]) < static_cast<uint64_t>(E)) {
+          const int32_t id = static_cast<int32_t>(r[u]);
+          const uint32_t h = static_cast<uint32_t>(id) & (32 * kBloomWords - 1);
+          if ((s_bloom[h >> 5] >> (h & 31)) & 1u) {
+            int k = 0;  // largest k with s_rows[k] <= id (or 0)
+#pragma unroll
+            for (int step = kDenseRows / 2; step > 0; step >>= 1)
+              if (s_rows[k + step] <= id) k += step;
+            if (s_rows[k] == id) {
+              int b = 0;  // the bag of lookup j
+#pragma unroll
+              for (int step = 8; step > 0; step >>= 1)
+                if (off[b + step] <= j) b += step;
+              big |= atomicAdd(&s_cnt[k * kStride + kDnWaveBags * w + b], 1u) >= 255u;
+            }
+          }
+        }
+      }
+    }
+    if (__ballot(big)) s_big = 1u;
+    __syncthreads();  // all 64 bags counted
+    const int levels = s_big != 0u ? 4 : 1;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      s16x8 bh[2], bm[2], bl[2];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          short h, mi, lo;
+          split3(q ? gv[8 * kk + j].y : gv[8 * kk + j].x, h, mi, lo);
+          bh[q][j] = h;
+          bm[q][j] = mi;
+          bl[q][j] = lo;
+        }
+      }
+#pragma unroll
+      for (int mt = 0; mt < kDenseRows / 16; ++mt) {
+        if (mt < ntiles) {
+          const uint32_t* src = &s_cnt[(16 * mt + (lane & 15)) * kStride + 32 * kk + 8 * (lane >> 4)];
+          const u32x4 c0 = *reinterpret_cast<const u32x4*>(src);
+          const u32x4 c1 = *reinterpret_cast<const u32x4*>(src + 4);
+          const uint32_t cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+          for (int lv = 0; lv < levels; ++lv) {
+            // counts byte lv, times 256^lv: at most 8 significant bits, exact in bf16
+            const uint32_t sh = 8 * lv;
+            s16x8 a;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) a[j] = bf16_bits(static_cast<float>(((cv[j] >> sh) & 255u) << sh));
+            const bf16x8 ab = __builtin_bit_cast(bf16x8, a);
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              acc[mt][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab, __builtin_bit_cast(bf16x8, bh[q]), acc[mt][q], 0, 0, 0);
+              acc[mt][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab, __builtin_bit_cast(bf16x8, bm[q]), acc[mt][q], 0, 0, 0);
+              acc[mt][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab, __builtin_bit_cast(bf16x8, bl[q]), acc[mt][q], 0, 0, 0);
+            }
+          }
+        }
+      }
+    }
+  }
+  // every workgroup of the table writes its partial (zeros when it had no step)
+  float* dst = partial + static_cast<int64_t>(blockIdx.x) * kDenseRows * kDnCols;
+  if (c2 < D) {
+#pragma unroll
+    for (int mt = 0; mt < kDenseRows / 16; ++mt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * mt + 4 * (lane >> 4) + i;
+        if (row < nd) *reinterpret_cast<f32x2*>(dst + row * kDnCols + c2) = f32x2{acc[mt][0][i], acc[mt][1][i]};
+      }
+    }
+  }
+}
+
+// Workgroup (t, k) = blockIdx.x: selected row k of table t.  Thread (g, q) sums partials
+// g, g + 8, ... of column quad q in increasing order, the eight sums are added in g order,
+// then the row's optimizer step.
+template <int DT, int OPT>
+__global__ __launch_bounds__(kBlock) void dense_apply_kernel(
+    typename Fmt<DT>::S* __restrict__ W, float* __restrict__ momentum, const int64_t* __restrict__ meta,
+    int P, const int32_t* __restrict__ dense_rows, const int32_t* __restrict__ dense_cnt,
+    const float* __restrict__ partial, float lr, float eps) {
+  using S = typename Fmt<DT>::S;
+  constexpr int kGroups = kBlock / (kDnCols / 4);  // 8
+  __shared__ __align__(16) float s_part[kGroups][kDnCols];
+  const int t = static_cast<int>(blockIdx.x) / kDenseRows, k = static_cast<int>(blockIdx.x) % kDenseRows;
+  if (k >= dense_cnt[t]) return;
+  const TableMeta m = load_meta(meta, t);
+  const int D = static_cast<int>(m.D);
+  const int q = threadIdx.x & (kDnCols / 4 - 1), g = threadIdx.x / (kDnCols / 4);
+  const int col = 4 * q;
+  if (col < D) {
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+    const float* src = partial + (static_cast<int64_t>(t) * P * kDenseRows + k) * kDnCols + col;
+    const int64_t pstride = static_cast<int64_t>(kDenseRows) * kDnCols;
+    int pp = g;
+    for (; pp + 3 * kGroups < P; pp += 4 * kGroups) {
+      const f32x4 x0 = load_f4(src + pp * pstride);
+      const f32x4 x1 = load_f4(src + (pp + kGroups) * pstride);
+      const f32x4 x2 = load_f4(src + (pp + 2 * kGroups) * pstride);
+      const f32x4 x3 = load_f4(src + (pp + 3 * kGroups) * pstride);
+      a += x0; a += x1; a += x2; a += x3;
+    }
+    for (; pp < P; pp += kGroups) a += load_f4(src + pp * pstride);
+    *reinterpret_cast<f32x4*>(&s_part[g][col]) = a;
+  }
+  __syncthreads();
+  if (threadIdx.x >= kWave) return;
+  // wave 0 finishes: lane l owns columns 4 l .. 4 l + 3
+  const int lane = threadIdx.x;
+  const int c = 4 * lane;
+  const bool act = lane < kDnCols / 4 && c < D;
+  const int64_t row = dense_rows[static_cast<int64_t>(t) * kDenseRows + k];
+  S* wrow = W + m.w_base + row * D;
+  float gv[4] = {0.f, 0.f, 0.f, 0.f};
+  float wv[4] = {0.f, 0.f, 0.f, 0.f};
+  if (act) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float s = s_part[0][c + e];
+#pragma unroll
+      for (int gg = 1; gg < kGroups; ++gg) s += s_part[gg][c + e];
+      gv[e] = s;
+    }
+    load_vec<DT, 4>(wrow + c, wv);
+  }
+  if constexpr (OPT == kOptSGD) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) wv[e] -= lr * gv[e];
+  } else {
+    float ss = gv[0] * gv[0] + gv[1] * gv[1] + gv[2] * gv[2] + gv[3] * gv[3];
+    for (int msk = 1; msk < kWave; msk <<= 1) ss += __shfl_xor(ss, msk);
+    const int64_t key = m.row_base + row;
+    const float mnew = momentum[key] + ss / static_cast<float>(D);
+    const float denom = sqrtf(mnew) + eps;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) wv[e] -= lr * gv[e] / denom;
+    if (lane == 0) momentum[key] = mnew;
+  }
+  if (act) store_vec4<DT>(wrow + c, wv);
+}
+
+template <typename IT, typename OT>
+tbe_status partial_go(const tbe_tables* tb, const IndexArgs& ia, const float* grad_out, char* ws,
+                      const BwdLayout& L, int P, hipStream_t s) {
+  ProfScope ps("dense_partial", s);
+  hipLaunchKernelGGL((dense_partial_kernel<IT, OT>), dim3(tb->T * P), dim3(kBlock), 0, s,
+                     static_cast<const IT*>(ia.indices), static_cast<const OT*>(ia.offsets), grad_out,
+                     tb->meta, tb->B, tb->out_width, ia.N, P,
+                     reinterpret_cast<const int32_t*>(ws + L.dense_rows),
+                     reinterpret_cast<const int32_t*>(ws + L.dense_cnt),
+                     reinterpret_cast<float*>(ws + L.dense_partial));
+  return check_launch("dense_partial");
+}
+
+template <int DT, int OPT>
+tbe_status apply_dense_go(const tbe_tables* tb, void* W, float* momentum, char* ws, const BwdLayout& L,
+                          int P, float lr, float eps, hipStream_t s) {
+  using S = typename Fmt<DT>::S;
+  ProfScope ps("dense_apply", s);
+  hipLaunchKernelGGL((dense_apply_kernel<DT, OPT>), dim3(tb->T * kDenseRows), dim3(kBlock), 0, s,
+                     static_cast<S*>(W), momentum, tb->meta, P,
+                     reinterpret_cast<const int32_t*>(ws + L.dense_rows),
+                     reinterpret_cast<const int32_t*>(ws + L.dense_cnt),
+                     reinterpret_cast<const float*>(ws + L.dense_partial), lr, eps);
+  return check_launch("dense_apply");
+}
+
+}  // namespace
+
+tbe_status launch_dense_select(const tbe_tables* tb, char* ws, const BwdLayout& L, int hist_t,
+                               const Config& cfg, hipStream_t s) {
+  ProfScope ps("dense_select", s);
+  hipLaunchKernelGGL(dense_select_kernel, dim3((tb->T + kWavesPerBlock - 1) / kWavesPerBlock), dim3(kBlock), 0, s,
+                     reinterpret_cast<const uint4*>(ws + L.long_list),
+                     reinterpret_cast<const uint32_t*>(ws + L.long_table),
+                     reinterpret_cast<const int32_t*>(ws + L.counters), L.cap_long, tb->meta, tb->T, hist_t,
+                     static_cast<uint32_t>(cfg.dense_min), reinterpret_cast<int32_t*>(ws + L.dense_rows),
+                     reinterpret_cast<int32_t*>(ws + L.dense_cnt), reinterpret_cast<uint32_t*>(ws + L.long_flag));
+  return check_launch("dense_select");
+}
+
+tbe_status launch_dense_backward(const tbe_tables* tb, void* W, float* momentum, int opt,
+                                 const IndexArgs& ia, const float* grad_out, float lr, float eps,
+                                 char* ws, const BwdLayout& L, hipStream_t s) {
+  // partials per table: as many workgroups as the GPU holds at once over all tables (one
+  // round, no tail), at most the workspace's dense_P
+  const int64_t resident = static_cast<int64_t>(device_cu_count()) *
+                           blocks_per_cu(reinterpret_cast<const void*>(dense_partial_kernel<int64_t, int64_t>));
+  const int P = static_cast<int>(hmax(1, hmin(L.dense_P, resident / tb->T)));
+  tbe_status st;
+  if (ia.itype == TBE_I32)
+    st = ia.otype == TBE_I32 ? partial_go<int32_t, int32_t>(tb, ia, grad_out, ws, L, P, s)
+                             : partial_go<int32_t, int64_t>(tb, ia, grad_out, ws, L, P, s);
+  else
+    st = ia.otype == TBE_I32 ? partial_go<int64_t, int32_t>(tb, ia, grad_out, ws, L, P, s)
+                             : partial_go<int64_t, int64_t>(tb, ia, grad_out, ws, L, P, s);
+  if (st) return st;
+#define TBE_DA(DT) \
+  (opt == kOptSGD ? apply_dense_go<DT, kOptSGD>(tb, W, momentum, ws, L, P, lr, eps, s) \
+                  : apply_dense_go<DT, kOptAdagrad>(tb, W, momentum, ws, L, P, lr, eps, s))
+  switch (tb->w_dtype) {
+    case TBE_F32: return TBE_DA(0);
+    case TBE_F16: return TBE_DA(1);
+    default: return TBE_DA(2);
+  }
+#undef TBE_DA
+}
+
+}  // namespace tbe

@@ -53,6 +53,7 @@ struct Config {
   int threshold, chunk, hist_enable, fwd_unroll, bwd_unroll, sort_blocks, bag_windows, fused_long;
   int pretransposed, bags_per_wave, bwd_streams;
   int tiny;  // wave steps of short runs of at most this many lookups: half the lanes per run
+  int dense_min;  // long runs of at least this many lookups take the dense path (0: off)
 };
 Config resolve_config(const tbe_config* c);
 
@@ -65,6 +66,10 @@ struct BwdLayout {
   size_t chunk_unit, chunk_order, unit_cnt;  // long-run chunk ordering by (table, bag window)
   size_t hist_partial, hist_count;             // histogram backward: per-block partial sums
   size_t hist_saved;                           // per-bag counts the histogram forward saves (u16)
+  // dense hot rows: per table kDenseRows selected row ids and their count, a flag per long
+  // run (1: taken by the dense path), dense_P partials of kDenseRows x 128 floats per table
+  size_t dense_rows, dense_cnt, long_flag, dense_partial;
+  int dense_P, dense_on;
   int nwin, win_size, units;
   int64_t cap_long, cap_chunk, cap_short[TBE_NUM_BUCKETS];
   int64_t seg;        // keys per sort / RLE block (multiple of kRadixTile)
@@ -122,6 +127,15 @@ tbe_status launch_transpose(const tbe_tables* tb, const IndexArgs& ia, int weigh
 
 // histogram backward of the small table (counts x gradient on MFMA, then the optimizer)
 constexpr int kHistBwdBlocks = 512;  // max partials (workgroups) of the histogram backward
+// dense hot rows of large tables (counts x gradient on MFMA): the selection flags the long runs
+// it takes (before the chunk and apply kernels run); the backward updates those rows
+constexpr int kDenseRows = 128;  // rows per table at most
+tbe_status launch_dense_select(const tbe_tables* tb, char* ws, const BwdLayout& L, int hist_t,
+                               const Config& cfg, hipStream_t s);
+tbe_status launch_dense_backward(const tbe_tables* tb, void* W, float* momentum, int opt,
+                                 const IndexArgs& ia, const float* grad_out, float lr, float eps,
+                                 char* ws, const BwdLayout& L, hipStream_t s);
+
 // saved_counts: the counts the histogram forward kept (then only ids past a bag's first 256
 // are read), or NULL to count every id
 tbe_status launch_hist_backward(const tbe_tables* tb, void* W, float* momentum, int opt,

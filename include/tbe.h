@@ -124,6 +124,12 @@ typedef struct {
   int32_t tiny_runs;       /* backward: a wave step whose short runs all have at most this many
                               lookups serves twice as many runs with half the lanes each (rows of
                               64 .. 256 columns); default 8, 0: off */
+  int32_t dense_min;       /* backward without per-sample weights: per table (16 <= D <= 128,
+                              D % 16 == 0, not the histogram table), up to 128 long runs of at
+                              least this many lookups, in key order, are updated from per-bag
+                              counts x grad_out on MFMA instead of their chunks (default 2048;
+                              values below long_threshold act as long_threshold; 0: off; off
+                              with fused_long) */
 } tbe_config;
 
 /* Device-side view of the transpose, for inspection by tests (tbe_transpose). */

@@ -111,6 +111,7 @@ def test_config_defaults():
     assert c.pretransposed == 0 and c.bags_per_wave == 0  # 0: chosen from the batch shape
     assert c.bwd_streams == 0  # 0: chosen from the tables' widths
     assert c.tiny_runs == 8    # short runs of <= 8 lookups: half the lanes per run
+    assert c.dense_min == 2048  # long runs of >= 2048 lookups: dense counts x gradient
 
 
 def test_workspace_histogram_table_partials():

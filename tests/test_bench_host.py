@@ -56,3 +56,26 @@ def test_tail_lookups_past_256():
     assert st["per_table"][0]["tail"] == 20 * 44 and st["per_table"][1]["tail"] == 0
     ah = bench.algorithmic_bytes(bt, st, hoist=True)
     assert ah["hist_bwd_partial"] == 20 * 44 * 8 + 20 * (8 + 128 + 64 * 4)
+
+
+def test_dense_rows_statistics():
+    """The dense hot rows: per eligible table, long runs of >= dense_min lookups in key order,
+    at most 128; their lookups leave the chunk and apply bytes for the dense kernels'."""
+    tables = (ti.TableSpec(300, 128, ("fixed", 40)),      # 300 rows x ~133 lookups: all long
+              ti.TableSpec(50, 200, ("fixed", 40)),       # D = 200: not eligible
+              ti.TableSpec(64, 64, ("fixed", 40)))
+    bt = ti.make_batch(ti.BatchSpec("dense stats", tables, B=1000, w_dtype=torch.float16,
+                                    w_range=0.05), 6, device="cpu")
+    st = bench.batch_stats(bt, hist_table=-1, threshold=64, chunk=64, dense_min=100)
+    p0, p1, p2 = st["per_table"]
+    idx, off = bt.indices.numpy().astype(np.int64), bt.offsets.numpy().astype(np.int64)
+    c0 = np.bincount(idx[off[0]:off[1000]], minlength=300)
+    want = np.flatnonzero(c0 >= 100)[:128]
+    assert p0["dense_rows"] == want.size == 128 and p0["dense_lookups"] == int(c0[want].sum())
+    assert p0["gen_long_lookups"] + p0["dense_lookups"] == p0["long_lookups"]
+    assert p1["dense_rows"] == 0 and p1["gen_long_lookups"] == p1["long_lookups"]
+    assert p2["dense_rows"] == 64                 # every row of the 64-row table
+    ab = bench.algorithmic_bytes(bt, st, hoist=False, dense_P=4)
+    assert ab["dense_partial"] == sum(p["N"] * 8 + 1000 * (8 + p["D"] * 4) + 4 * p["dense_rows"] * p["D"] * 4
+                                      for p in (p0, p2))
+    assert ab["dense_apply"] == sum(p["dense_rows"] * (4 * p["D"] * 4 + 2 * p["D"] * 2 + 8) for p in (p0, p2))

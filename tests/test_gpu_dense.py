@@ -1,0 +1,168 @@
+"""Dense hot rows: per table, the long runs of at least dense_min lookups (up to 128, in key
+order) are updated from per-bag counts x grad_out on MFMA instead of their chunks.  The step
+equals the oracle's within the usual bounds, is bitwise repeatable, and is exact with integer
+gradients."""
+import numpy as np
+import pytest
+import torch
+
+import bwd_tbe_fwd_amd as tbe
+import oracle
+import tbe_inputs as ti
+from gpu_util import DevBatch, check_weights, flush_print, host_arrays, oracle_backward, step_bound
+from test_gpu_backward import run_and_check
+
+pytestmark = pytest.mark.gpu
+
+
+def _spec(D=(128, 64, 32, 200), E=(300, 1000, 400, 250), B=777, L=(60.0, 40.0, 30.0, 20.0),
+          zipf=1.1, w_dtype=torch.float16, optimizer="rowwise_adagrad", itype=torch.int64,
+          otype=torch.int64, weighted=False, hint=None):
+    """Skewed tables: eligible widths (128, 64, 32) and one that is not (200)."""
+    tables = tuple(ti.TableSpec(e, d, ("poisson", l, None, None), ("zipf", zipf, None))
+                   for e, d, l in zip(E, D, L))
+    return ti.BatchSpec(f"dense D={D} B={B}", tables, B=B, w_dtype=w_dtype, w_range=0.05,
+                        optimizer=optimizer, itype=itype, otype=otype, weighted=weighted,
+                        pooling_hint=hint)
+
+
+def _cfg(dense_min, **kw):
+    return tbe.make_config(long_threshold=16, chunk=8, dense_min=dense_min, **kw)
+
+
+def _long_lens(bt, threshold):
+    """Per table: lengths of its runs of >= threshold lookups, in key order."""
+    idx, off, B = bt.indices.numpy().astype(np.int64), bt.offsets.numpy().astype(np.int64), bt.B
+    out = []
+    for t in range(bt.T):
+        lk = idx[off[t * B]:off[(t + 1) * B]]
+        lk = lk[(lk >= 0) & (lk < bt.E[t])]
+        c = np.bincount(lk, minlength=bt.E[t])
+        out.append(c[c >= threshold])
+    return out
+
+
+@pytest.mark.parametrize("w_dtype", [torch.float32, torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("optimizer", ["sgd", "rowwise_adagrad"])
+def test_dense_rows_match_oracle(w_dtype, optimizer):
+    spec = _spec(w_dtype=w_dtype, optimizer=optimizer)
+    bt = ti.make_batch(spec, 71)
+    lens = _long_lens(bt, 48)
+    assert sum(int((l >= 48).sum()) for l in lens[:3]) > 20   # the dense path has rows to take
+    flush_print(f"dense {w_dtype} {optimizer}")
+    run_and_check(bt, _cfg(48), what=f"dense {w_dtype} {optimizer}")
+
+
+@pytest.mark.parametrize("itype,otype", [(torch.int32, torch.int32), (torch.int64, torch.int32),
+                                         (torch.int32, torch.int64)])
+def test_dense_rows_index_types(itype, otype):
+    bt = ti.make_batch(_spec(itype=itype, otype=otype, B=300), 73)
+    run_and_check(bt, _cfg(32), what=f"dense {itype} {otype}")
+
+
+def test_dense_rows_change_the_summation_and_repeat():
+    """fp32 weights, Adagrad: the dense path sums the hot rows' gradients in another order than
+    the chunks (other low bits, so it did run), and the same bits on every call."""
+    bt = ti.make_batch(_spec(w_dtype=torch.float32), 75)
+    outs = {}
+    for dm in (0, 48, 48):
+        db = DevBatch(bt)
+        W, mom = db.backward(_cfg(dm))
+        torch.cuda.synchronize()
+        outs.setdefault(dm, []).append((W.cpu(), mom.cpu()))
+    (Wa, ma), (Wb, mb) = outs[48]
+    assert torch.equal(Wa.view(torch.int32), Wb.view(torch.int32)) and torch.equal(ma, mb)
+    W0, _ = outs[0][0]
+    assert not torch.equal(W0.view(torch.int32), Wa.view(torch.int32))
+
+
+@pytest.mark.parametrize("dense_min", [16, 48])
+def test_dense_rows_exact_with_integer_gradients(dense_min):
+    """Gradients in {-1, 0, 1}, zero weights, SGD with lr = -1: every sum is an exact integer
+    in fp32, so the dense path, the chunk path and the oracle agree bit for bit."""
+    spec = _spec(w_dtype=torch.float32, optimizer="sgd", B=500)
+    bt = ti.make_batch(spec, 77)
+    g = torch.Generator().manual_seed(7)
+    bt.grad_out = torch.randint(-1, 2, bt.grad_out.shape, generator=g).float()
+    bt.weights = torch.zeros_like(bt.weights)
+    outs = []
+    for dm in (dense_min, 0):
+        db = DevBatch(bt)
+        W, _ = db.backward(_cfg(dm), lr=-1.0)
+        torch.cuda.synchronize()
+        outs.append(W.cpu())
+    assert torch.equal(outs[0].view(torch.int32), outs[1].view(torch.int32))
+    r = oracle_backward(bt, lr=-1.0)
+    assert np.array_equal(outs[0].double().numpy(), r["g"])
+    assert np.abs(r["g"]).max() > 20
+
+
+def test_dense_rows_more_than_128_per_table():
+    """Every row of a 600-row table is hit about 120 times: the first 128 qualifying rows in key
+    order take the dense path, the rest their chunks."""
+    tables = (ti.TableSpec(600, 128, ("fixed", 100)), ti.TableSpec(3000, 64, ("poisson", 5.0, None, None)))
+    spec = ti.BatchSpec("dense cap", tables, B=720, w_dtype=torch.float32, w_range=0.05,
+                        optimizer="rowwise_adagrad")
+    bt = ti.make_batch(spec, 79)
+    assert int((_long_lens(bt, 64)[0] >= 64).sum()) > 300
+    run_and_check(bt, _cfg(64), what="dense cap")
+
+
+def test_dense_rows_with_histogram_table_and_bad_ids():
+    """A histogram-eligible small table (its own MFMA path), dense rows in the others, and ids
+    outside their tables (dropped by both paths)."""
+    tables = (ti.TableSpec(64, 128, ("fixed", 100)),
+              ti.TableSpec(400, 128, ("poisson", 50.0, None, None), ("zipf", 1.2, None)),
+              ti.TableSpec(900, 64, ("poisson", 20.0, None, None), ("zipf", 1.1, None)))
+    spec = ti.BatchSpec("dense + hist", tables, B=600, w_dtype=torch.float16, w_range=0.05,
+                        optimizer="sgd", pooling_hint=(100, 50, 20))
+    bt = ti.make_batch(spec, 81)
+    idx = bt.indices.clone()
+    bad = torch.zeros(idx.numel(), dtype=torch.bool)
+    bad[3::11] = True
+    idx[bad] = torch.where(torch.arange(idx.numel())[bad] % 2 == 0, torch.tensor(-1),
+                           torch.tensor(10 ** 6)).to(idx.dtype)
+    bt.indices = idx
+    db = DevBatch(bt)
+    assert db.tables.c.hist_table == 0
+    W, _ = db.backward(_cfg(32))
+    torch.cuda.synchronize()
+    a = host_arrays(bt)
+    keep = (~bad).double().numpy()
+    ids = np.where(bad.numpy(), 0, a["idx"])
+    lr32 = oracle.f32_literal(spec.lr)
+    r = oracle.backward(a["T"], a["B"], a["E"], a["D"], oracle.F16, a["W"], ids, a["off"], keep,
+                        a["grad"], oracle.SGD, lr32)
+    check_weights(W, r, torch.float16, step_bound(r, bt.E, bt.D, lr32, 0.0, False), "dense + hist")
+
+
+@pytest.mark.parametrize("B", [1, 63, 64, 65, 4100])
+def test_dense_rows_bag_counts(B):
+    """Bag counts around the 64-bag step and the partial count."""
+    spec = _spec(B=B, L=(90.0, 60.0, 30.0, 10.0))
+    bt = ti.make_batch(spec, 83)
+    run_and_check(bt, _cfg(16), what=f"dense B={B}")
+
+
+def test_dense_rows_off_with_per_sample_weights():
+    bt = ti.make_batch(_spec(weighted=True, B=400), 85)
+    run_and_check(bt, _cfg(16), what="dense weighted (off)")
+
+
+@pytest.mark.parametrize("L", [300, 70000])
+def test_dense_rows_counts_above_255(L):
+    """Bags with hundreds (and tens of thousands) of lookups of one row: the counts go through
+    the bf16 product byte by byte and stay exact (integer gradients, so bit for bit)."""
+    tables = (ti.TableSpec(2, 64, ("fixed", L)), ti.TableSpec(500, 128, ("poisson", 8.0, None, None)))
+    spec = ti.BatchSpec(f"dense big counts L={L}", tables, B=70 if L < 1000 else 3,
+                        w_dtype=torch.float32, w_range=0.05, optimizer="sgd")
+    bt = ti.make_batch(spec, 87)
+    g = torch.Generator().manual_seed(9)
+    bt.grad_out = torch.randint(-1, 2, bt.grad_out.shape, generator=g).float()
+    bt.weights = torch.zeros_like(bt.weights)
+    db = DevBatch(bt)
+    W, _ = db.backward(_cfg(16), lr=-1.0)
+    torch.cuda.synchronize()
+    r = oracle_backward(bt, lr=-1.0)
+    assert np.array_equal(W.cpu().double().numpy(), r["g"])
+    assert np.abs(r["g"][:128]).max() > 255
