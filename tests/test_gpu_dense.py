@@ -166,3 +166,17 @@ def test_dense_rows_counts_above_255(L):
     r = oracle_backward(bt, lr=-1.0)
     assert np.array_equal(W.cpu().double().numpy(), r["g"])
     assert np.abs(r["g"][:128]).max() > 255
+
+
+def test_dense_rows_on_the_second_stream():
+    """The dense rows, chunks and applies on the library's second stream, concurrent with the
+    short runs: the same bits as on one stream."""
+    bt = ti.make_batch(_spec(w_dtype=torch.float32), 89)
+    outs = []
+    for streams in (1, 2):
+        db = DevBatch(bt)
+        W, mom = db.backward(_cfg(48, bwd_streams=streams))
+        torch.cuda.synchronize()
+        outs.append((W.cpu(), mom.cpu()))
+    assert torch.equal(outs[0][0].view(torch.int32), outs[1][0].view(torch.int32))
+    assert torch.equal(outs[0][1], outs[1][1])
