@@ -102,6 +102,21 @@ __device__ __forceinline__ void split3(float x, short& hi, short& mid, short& lo
   lo = static_cast<short>(__builtin_bit_cast(uint32_t, l) >> 16);
 }
 
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// acc[q] += A (16 rows x 32 bags, bf16) x the gradient's three bf16 parts (32 bags x 16 columns,
+// column tile q)
+__device__ __forceinline__ void dense_mfma(float4_t (&acc)[2], bf16x8 a, const s16x8 (&bh)[2],
+                                           const s16x8 (&bm)[2], const s16x8 (&bl)[2]) {
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, bh[q]), acc[q], 0, 0, 0);
+    acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, bm[q]), acc[q], 0, 0, 0);
+    acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, bl[q]), acc[q], 0, 0, 0);
+  }
+}
+
 // The 17 offsets of a wave's 16 bags (lanes 0..16; waves past the last bag read the
 // table's end offset), clamped to [0, N].
 template <typename OT>
@@ -129,11 +144,11 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     const int64_t* __restrict__ meta, int32_t B, int32_t out_width, int64_t N, int P,
     const int32_t* __restrict__ dense_rows, const int32_t* __restrict__ dense_cnt,
     float* __restrict__ partial) {
-  typedef short s16x8 __attribute__((ext_vector_type(8)));
-  typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
   constexpr int kStride = kDnBags + 4;   // counts [row][bag]; rows padded against bank conflicts
   constexpr int kBloomWords = 1024;      // 32768-bit filter of the selected rows (id mod 32768)
-  __shared__ __align__(16) uint32_t s_cnt[kDenseRows * kStride];
+  // counts as fp32 (exact integers below 2^24): a count below 256 is then its own bf16 value
+  // in the high half of its bits
+  __shared__ __align__(16) float s_cnt[kDenseRows * kStride];
   __shared__ uint32_t s_bloom[kBloomWords];
   __shared__ int32_t s_rows[kDenseRows];
   __shared__ int32_t s_off[kWavesPerBlock][kDnWaveBags + 1];
@@ -212,7 +227,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     // this wave's 16 bag columns of every row
 #pragma unroll
     for (int x = lane; x < kDenseRows * (kDnWaveBags / 4); x += kWave)
-      *reinterpret_cast<u32x4*>(&s_cnt[(x >> 2) * kStride + kDnWaveBags * w + 4 * (x & 3)]) = u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<f32x4*>(&s_cnt[(x >> 2) * kStride + kDnWaveBags * w + 4 * (x & 3)]) = f32x4{0.f, 0.f, 0.f, 0.f};
     __builtin_amdgcn_wave_barrier();
     // every lookup of the wave's 16 bags that hits a selected row
     bool big = false;
@@ -225,6 +240,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
       }
 #pragma unroll
       for (int u = 0; u < kDnLoads; ++u) {
+        if (j0 + u * kWave >= n) break;  // uniform: no lane has an id left
         const int32_t j = j0 + u * kWave + lane;
         if (static_cast<uint64_t>(r[u]) < static_cast<uint64_t>(E)) {
           const int32_t id = static_cast<int32_t>(r[u]);
@@ -239,7 +255,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
 #pragma unroll
               for (int step = 8; step > 0; step >>= 1)
                 if (off[b + step] <= j) b += step;
-              big |= atomicAdd(&s_cnt[k * kStride + kDnWaveBags * w + b], 1u) >= 255u;
+              big |= atomicAdd(&s_cnt[k * kStride + kDnWaveBags * w + b], 1.f) >= 255.f;
             }
           }
         }
@@ -247,7 +263,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     }
     if (__ballot(big)) s_big = 1u;
     __syncthreads();  // all 64 bags counted
-    const int levels = s_big != 0u ? 4 : 1;
+    const bool any_big = __builtin_amdgcn_readfirstlane(s_big) != 0u;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       s16x8 bh[2], bm[2], bl[2];
@@ -265,22 +281,32 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
 #pragma unroll
       for (int mt = 0; mt < kDenseRows / 16; ++mt) {
         if (mt < ntiles) {
-          const uint32_t* src = &s_cnt[(16 * mt + (lane & 15)) * kStride + 32 * kk + 8 * (lane >> 4)];
+          const float* src = &s_cnt[(16 * mt + (lane & 15)) * kStride + 32 * kk + 8 * (lane >> 4)];
           const u32x4 c0 = *reinterpret_cast<const u32x4*>(src);
           const u32x4 c1 = *reinterpret_cast<const u32x4*>(src + 4);
-          const uint32_t cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-          for (int lv = 0; lv < levels; ++lv) {
-            // counts byte lv, times 256^lv: at most 8 significant bits, exact in bf16
-            const uint32_t sh = 8 * lv;
-            s16x8 a;
+          if (!any_big) {
+            // every count is below 256: the high halves of the fp32 counts are their bf16 values
+            const u32x4 pk = {__builtin_amdgcn_perm(c0.y, c0.x, 0x07060302u),
+                              __builtin_amdgcn_perm(c0.w, c0.z, 0x07060302u),
+                              __builtin_amdgcn_perm(c1.y, c1.x, 0x07060302u),
+                              __builtin_amdgcn_perm(c1.w, c1.z, 0x07060302u)};
+            dense_mfma(acc[mt], __builtin_bit_cast(bf16x8, pk), bh, bm, bl);
+          } else {
+            // byte by byte: byte lv of a count times 256^lv has at most 8 significant bits
+            const uint32_t cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll 1
+            for (int lv = 0; lv < 4; ++lv) {
+              u32x4 pk;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) a[j] = bf16_bits(static_cast<float>(((cv[j] >> sh) & 255u) << sh));
-            const bf16x8 ab = __builtin_bit_cast(bf16x8, a);
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-              acc[mt][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab, __builtin_bit_cast(bf16x8, bh[q]), acc[mt][q], 0, 0, 0);
-              acc[mt][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab, __builtin_bit_cast(bf16x8, bm[q]), acc[mt][q], 0, 0, 0);
-              acc[mt][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab, __builtin_bit_cast(bf16x8, bl[q]), acc[mt][q], 0, 0, 0);
+              for (int j = 0; j < 4; ++j) {
+                const uint32_t a = static_cast<uint32_t>(__builtin_bit_cast(float, cv[2 * j]));
+                const uint32_t b = static_cast<uint32_t>(__builtin_bit_cast(float, cv[2 * j + 1]));
+                const float lo = static_cast<float>(((a >> (8 * lv)) & 255u) << (8 * lv));
+                const float hi = static_cast<float>(((b >> (8 * lv)) & 255u) << (8 * lv));
+                pk[j] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, hi), __builtin_bit_cast(uint32_t, lo),
+                                              0x07060302u);
+              }
+              dense_mfma(acc[mt], __builtin_bit_cast(bf16x8, pk), bh, bm, bl);
             }
           }
         }
