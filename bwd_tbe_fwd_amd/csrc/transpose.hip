@@ -212,12 +212,27 @@ __global__ __launch_bounds__(kBlock) void radix_upsweep(const uint32_t* __restri
         for (int q = 0; q < 4; ++q) k[4 * s + q] = i + q < hi ? keys[i + q] : 0u;
       }
     }
-    // counts are order-free: one LDS atomic add per key (equal digits serialize in
-    // the LDS unit, which is cheaper than matching lanes first)
+    // counts are order-free: one LDS atomic add per key, except where keys repeat.  After the
+    // first pass a hot row's lookups lie side by side, so whole groups of four (and whole
+    // waves of groups) carry one digit, and adding them one by one would serialize on one
+    // LDS address: such a group adds 4 at once, such a wave 256 from one lane.
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int64_t i = base + (j >> 2) * 4 * kWave + 4 * lane + (j & 3);
-      if (i < hi) atomicAdd(&s_cnt[w][(k[j] >> shift) & mask], 1u);
+    for (int s = 0; s < 4; ++s) {
+      const int64_t i0 = base + s * 4 * kWave + 4 * lane;
+      uint32_t d[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) d[q] = (k[4 * s + q] >> shift) & mask;
+      const bool same4 = i0 + 3 < hi && d[1] == d[0] && d[2] == d[0] && d[3] == d[0];
+      const uint32_t dw = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(d[0])));
+      if (__ballot(!(same4 && d[0] == dw)) == 0) {
+        if (lane == 0) atomicAdd(&s_cnt[w][dw], 4u * kWave);
+      } else if (same4) {
+        atomicAdd(&s_cnt[w][d[0]], 4u);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (i0 + q < hi) atomicAdd(&s_cnt[w][d[q]], 1u);
+      }
     }
   }
   __syncthreads();
