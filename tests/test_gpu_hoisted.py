@@ -91,6 +91,21 @@ def test_hoisted_equals_plain(name, repair):
         assert hoist["counts"][0] > 0 and hoist["counts"][1] > 0
 
 
+@pytest.mark.parametrize("repair", [False, True])
+def test_hoisted_with_dense_rows(repair):
+    """The dense hot rows after the hoisted forward (fused repair or not): bitwise the plain
+    two calls, and the dense path really runs (fp32 weights: other low bits than the chunks)."""
+    spec = small_spec("skewed").replace(w_dtype=torch.float32)
+    bt = ti.make_batch(spec, 91)
+    idx, off = _inject(bt, 11, bad_offsets=repair)
+    kw = dict(long_threshold=32, chunk=16, dense_min=64)
+    plain = _step(bt, idx, off, hoisted=False, repair=repair, cfg_kw=kw)
+    hoist = _step(bt, idx, off, hoisted=True, repair=repair, cfg_kw=kw)
+    _assert_same(plain, hoist)
+    chunks = _step(bt, idx, off, hoisted=True, repair=repair, cfg_kw=dict(kw, dense_min=0))
+    assert not torch.equal(chunks["W"].view(torch.int32), hoist["W"].view(torch.int32))
+
+
 @pytest.mark.parametrize("L,B,last", [(("poisson", 300.0, None, None), 130, False),
                                       (("poisson", 300.0, None, None), 77, True),
                                       (("fixed", 256), 33, False),
