@@ -613,11 +613,10 @@ static tbe_status backward_common(const tbe_tables* tables, void* weights, float
   if (L.dense_on)
     if (tbe_status st = launch_dense_select(tables, ws, L, hist, cfg, s)) return st;
   // automatic: short runs of several widths are several short launches, whose tails leave
-  // room for the long runs; the dense rows' MFMA and latency-bound work also overlaps the
-  // bandwidth-bound short runs
+  // room for the long runs
   int buckets = 0;
   for (int b = 0; b < TBE_NUM_BUCKETS; ++b) buckets += L.cap_short[b] > 0;
-  const int streams = cfg.bwd_streams ? cfg.bwd_streams : ((buckets >= 2 || L.dense_on) ? 2 : 1);
+  const int streams = cfg.bwd_streams ? cfg.bwd_streams : (buckets >= 2 ? 2 : 1);
   if (streams < 2 || L.cap_long == 0) {
     if (tbe_status st = launch_backward_update(tables, weights, momentum, opt, psw, grad_out, lr, eps, ws,
                                                L, final_buf, cfg, s, s))
