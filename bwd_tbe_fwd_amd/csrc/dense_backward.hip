@@ -20,7 +20,8 @@
 // dense_partial: workgroup (t, p) takes the table's 64-bag steps p, p + P, ...;
 // each of its four waves counts the lookups of 16 of the step's bags that hit
 // a selected row (a bit filter in LDS, then a 7-step search of the sorted row
-// ids) into the shared count[128 rows][64 bags]; then wave w multiplies the
+// ids) into the shared count[128 rows][64 bags] (fp32, so that a count below
+// 256 is its own bf16 value); then wave w multiplies the
 // counts by gradient columns 32 w .. 32 w + 31 of the 64 bags on
 // v_mfma_f32_16x16x32_bf16.  The pages' compensated high/low product, made
 // exact: the fp32 gradient is split into three bf16 parts whose sum is exactly
@@ -41,7 +42,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kDnCols = 128;     // max D; each wave owns 32 columns (2 MFMA N tiles)
 constexpr int kDnWaveBags = 16;  // bags one wave counts per step
-constexpr int kDnBags = kDnWaveBags * kWavesPerBlock;  // bags per step: MFMA K, 16 steps of 4
+constexpr int kDnBags = kDnWaveBags * kWavesPerBlock;  // bags per step: the MFMA K, two blocks of 32
 constexpr int kDnLoads = 8;      // id loads in flight per lane while counting
 
 __device__ __forceinline__ bool dense_table_ok(int D, int t, int hist_t) {
