@@ -30,6 +30,8 @@ import tbe_inputs as ti  # noqa: E402
 
 METRIC = "TBE fwd+bwd lookups/s and achieved HBM GB/s vs peak, 1 MI355X"
 HBM_PEAK_GBS = 8000.0
+# MI355X dense matrix-core peaks (no sparsity), TFLOP/s
+MFMA_PEAK_TFLOPS = {"fp16": 2500.0, "bf16": 2500.0, "fp32": 157.3}
 KERNELS = ["bounds_offsets", "bounds_indices", "fwd_gather", "fwd_hist", "linearize",
            "radix_upsweep", "radix_scan", "radix_downsweep", "rle", "classify", "short_run",
            "grad_accum", "long_apply", "hist_bwd_partial", "hist_bwd_apply", "dense_select",
@@ -199,6 +201,28 @@ def algorithmic_bytes(bt: ti.Batch, st: dict, hoist: bool, dense_P: int = 24):
             by["fwd_hist"] += B * 64 * 2
             by["hist_bwd_partial"] = p["tail"] * s_i + B * (s_o + 64 * 2 + p["D"] * 4)
     return by
+
+
+def mfma_flops(bt: ti.Batch, st: dict):
+    """Matrix-core work per launch of the kernels that use it, as issued (rows and columns of
+    every MFMA tile, zero padding included): {kernel: (flops, dtype)}."""
+    B = bt.B
+    out = {}
+    for p in st["per_table"]:
+        if p["hist"]:
+            D = p["D"]
+            # forward: per 16-bag tile, counts (16 x 64) x table (64 x D) on 16x16x16 fp16
+            out["fwd_hist"] = (((B + 15) // 16) * 16 * 64 * D * 2, "fp16")
+            # backward: per 64-bag step, counts^T (64 rows x 64 bags) x grad (64 bags x 128 columns)
+            # on 16x16x4 fp32 (every wave multiplies its 32 columns, padded past D)
+            out["hist_bwd_partial"] = (((B + 63) // 64) * 64 * 64 * 128 * 2, "fp32")
+    dense = [p for p in st["per_table"] if p["dense_rows"]]
+    if dense:
+        # per table and 64-bag step: ceil(rows / 16) row tiles x 64 bags x 128 columns, three
+        # bf16 parts of the gradient
+        out["dense_partial"] = (sum(((B + 63) // 64) * ((p["dense_rows"] + 15) // 16) * 16 * 64 * 128 * 2 * 3
+                                    for p in dense), "bf16")
+    return out
 
 
 def calib_copy():
@@ -427,6 +451,14 @@ def main():
         "copy_peak_GBps": copy_peak_gbps(),
         # event-timed per kernel, one step each with nothing overlapping (transpose in the backward)
         "kernel_ms_one_step": per_kernel,
+        # matrix-core kernels: work as issued over their average launch time (one-step scan),
+        # against the dense MFMA peak of their operand type
+        "mfma_utilisation": {
+            k: {"dtype": dt, "flops_per_launch": fl,
+                "achieved_TFLOPs": fl / (per_kernel[k] / launches_per_step[k] * 1e-3) / 1e12,
+                "peak_TFLOPs": MFMA_PEAK_TFLOPS[dt],
+                "frac": fl / (per_kernel[k] / launches_per_step[k] * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[dt]}
+            for k, (fl, dt) in mfma_flops(bt, st).items() if per_kernel.get(k)},
     }
     if not args.no_cpu_baseline:
         del ws, out

@@ -79,3 +79,16 @@ def test_dense_rows_statistics():
     assert ab["dense_partial"] == sum(p["N"] * 8 + 1000 * (8 + p["D"] * 4) + 4 * p["dense_rows"] * p["D"] * 4
                                       for p in (p0, p2))
     assert ab["dense_apply"] == sum(p["dense_rows"] * (4 * p["D"] * 4 + 2 * p["D"] * 2 + 8) for p in (p0, p2))
+
+
+def test_mfma_flops():
+    bt = ti.make_batch(_spec(), 4, device="cpu")
+    st = bench.batch_stats(bt, hist_table=0)
+    fl = bench.mfma_flops(bt, st)
+    # 300 bags: 19 tiles of 16 bags, counts 16 x 64 times the 64 x 128 table; 5 steps of 64 bags
+    assert fl["fwd_hist"] == (19 * 16 * 64 * 128 * 2, "fp16")
+    assert fl["hist_bwd_partial"] == (5 * 64 * 64 * 128 * 2, "fp32")
+    # the Zipf table's hottest rows take the dense path: per 64-bag step, 16-row tiles x 64 bags
+    # x 128 columns, three bf16 parts
+    nd = st["per_table"][1]["dense_rows"]
+    assert nd >= 1 and fl["dense_partial"] == (5 * ((nd + 15) // 16) * 16 * 64 * 128 * 2 * 3, "bf16")
