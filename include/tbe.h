@@ -270,7 +270,11 @@ size_t tbe_backward_workspace_bytes(const tbe_tables* tables, int64_t num_indice
  * set, there are no per-sample weights and tables->hist_table >= 0, that
  * table's rows take their gradient from per-bag lookup counts times grad_out
  * on MFMA (blog section 2, forward-state reuse) and its lookups stay out of the
- * sort; the other tables go through the sorted runs.
+ * sort; the other tables go through the sorted runs.  With dense_min > 0 and no
+ * per-sample weights, each eligible table's hottest long runs (config
+ * dense_min) take the same counts x grad_out route on bf16 MFMA with an exact
+ * three-part split of the gradient; the step is the same up to the order of
+ * the fp32 sums.
  */
 tbe_status tbe_backward_sgd(const tbe_tables* tables, void* weights, const void* indices,
                             int32_t index_type, const void* offsets, int32_t offset_type,
