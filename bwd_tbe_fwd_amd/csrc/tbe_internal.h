@@ -84,8 +84,9 @@ BwdLayout bwd_layout(const tbe_tables* tb, int64_t N, int weighted, const Config
 constexpr int kOptSGD = 0;
 constexpr int kOptAdagrad = 1;
 
-// kNeff: keys the sort covers when a table is left out of the runs
-enum Counter { kRuns = 0, kLong = 1, kChunks = 2, kShort0 = 3, kNeff = 12, kNumCounters = 16 };
+// kNeff: keys the sort covers when a table is left out of the runs; kSorted: keys kept by the
+// first radix pass (sentinel keys left out), the length of the sorted arrays
+enum Counter { kRuns = 0, kLong = 1, kChunks = 2, kShort0 = 3, kNeff = 12, kSorted = 13, kNumCounters = 16 };
 static_assert(kShort0 + TBE_NUM_BUCKETS <= kNeff, "counter slots overlap");
 
 // ---------------------------------------------------------------------------

@@ -186,9 +186,11 @@ __global__ __launch_bounds__(kBlock) void linearize_kernel(
 // ---------------------------------------------------------------------------
 // radix sort
 // ---------------------------------------------------------------------------
+// drop: a key equal to it is not counted (the first pass leaves out the sentinel keys;
+// later passes pass a value no key has)
 __global__ __launch_bounds__(kBlock) void radix_upsweep(const uint32_t* __restrict__ keys, int64_t N,
                                                         const int32_t* __restrict__ n_eff,
-                                                        int64_t seg, int shift, int bits,
+                                                        int64_t seg, int shift, int bits, uint32_t drop,
                                                         uint32_t* __restrict__ hist, int nblk) {
   if (n_eff) N = min(N, static_cast<int64_t>(*n_eff));
   __shared__ uint32_t s_cnt[kWavesPerBlock][kRadixDigits];
@@ -220,9 +222,13 @@ __global__ __launch_bounds__(kBlock) void radix_upsweep(const uint32_t* __restri
     for (int s = 0; s < 4; ++s) {
       const int64_t i0 = base + s * 4 * kWave + 4 * lane;
       uint32_t d[4];
+      bool ok[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) d[q] = (k[4 * s + q] >> shift) & mask;
-      const bool same4 = i0 + 3 < hi && d[1] == d[0] && d[2] == d[0] && d[3] == d[0];
+      for (int q = 0; q < 4; ++q) {
+        d[q] = (k[4 * s + q] >> shift) & mask;
+        ok[q] = i0 + q < hi && k[4 * s + q] != drop;
+      }
+      const bool same4 = ok[0] && ok[1] && ok[2] && ok[3] && d[1] == d[0] && d[2] == d[0] && d[3] == d[0];
       const uint32_t dw = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(d[0])));
       if (__ballot(!(same4 && d[0] == dw)) == 0) {
         if (lane == 0) atomicAdd(&s_cnt[w][dw], 4u * kWave);
@@ -231,7 +237,7 @@ __global__ __launch_bounds__(kBlock) void radix_upsweep(const uint32_t* __restri
       } else {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          if (i0 + q < hi) atomicAdd(&s_cnt[w][d[q]], 1u);
+          if (ok[q]) atomicAdd(&s_cnt[w][d[q]], 1u);
       }
     }
   }
@@ -271,8 +277,10 @@ __global__ __launch_bounds__(kBlock) void radix_scan(uint32_t* __restrict__ hist
 __global__ __launch_bounds__(kBlock) void radix_downsweep(
     const uint32_t* __restrict__ kin, const uint32_t* __restrict__ pin, uint32_t* __restrict__ kout,
     uint32_t* __restrict__ pout, int64_t N, const int32_t* __restrict__ n_eff, int64_t seg,
-    int shift, int bits, const uint32_t* __restrict__ hist, const uint32_t* __restrict__ tot,
-    int nblk) {
+    int shift, int bits, uint32_t drop, const uint32_t* __restrict__ hist, const uint32_t* __restrict__ tot,
+    int nblk, int32_t* __restrict__ n_kept) {
+  // drop: keys equal to it are left out (not ranked, not written); the keys kept, over all
+  // blocks, go to *n_kept (block 0), the count every later kernel reads
   if (n_eff) N = min(N, static_cast<int64_t>(*n_eff));
   __shared__ uint32_t s_base[kRadixDigits];
   __shared__ uint32_t s_wcnt[kWavesPerBlock][kRadixDigits];
@@ -281,6 +289,7 @@ __global__ __launch_bounds__(kBlock) void radix_downsweep(
   __shared__ uint32_t s_key[kRadixTile];
   __shared__ uint32_t s_pay[kRadixTile];
   __shared__ uint32_t s_tmp[kWavesPerBlock];
+  __shared__ uint32_t s_kept;  // keys of the current tile that are kept
   const int lane = lane_id(), w = threadIdx.x >> 6;
   const int ndig = 1 << bits;
   const uint32_t mask = static_cast<uint32_t>(ndig - 1);
@@ -288,14 +297,15 @@ __global__ __launch_bounds__(kBlock) void radix_downsweep(
   {
     const int d0 = 2 * threadIdx.x, d1 = d0 + 1;
     const uint32_t a = d0 < ndig ? tot[d0] : 0u, b = d1 < ndig ? tot[d1] : 0u;
-    const uint32_t ex = block_exclusive_sum(a + b, s_tmp, nullptr);
+    uint32_t all;
+    const uint32_t ex = block_exclusive_sum(a + b, s_tmp, &all);
     if (d0 < ndig) s_base[d0] = ex + hist[static_cast<int64_t>(d0) * nblk + blockIdx.x];
     if (d1 < ndig) s_base[d1] = ex + a + hist[static_cast<int64_t>(d1) * nblk + blockIdx.x];
+    if (n_kept && blockIdx.x == 0 && threadIdx.x == 0) *n_kept = static_cast<int32_t>(all);
   }
   __syncthreads();
   const int64_t lo = blockIdx.x * seg, hi = min(lo + seg, N);
   for (int64_t tile = lo; tile < hi; tile += kRadixTile) {
-    const int tn = static_cast<int>(min<int64_t>(kRadixTile, hi - tile));
     for (int i = lane; i < ndig; i += kWave) s_wcnt[w][i] = 0;
     uint32_t k[kRadixItems], p[kRadixItems], r[kRadixItems];
     const int64_t wbase = tile + w * (kRadixItems * kWave);
@@ -316,7 +326,7 @@ __global__ __launch_bounds__(kBlock) void radix_downsweep(
     uint32_t base[kRadixItems];
 #pragma unroll
     for (int s = 0; s < kRadixItems; ++s) {
-      const bool valid = wbase + s * kWave + lane < hi;
+      const bool valid = wbase + s * kWave + lane < hi && k[s] != drop;
       const uint32_t d = (k[s] >> shift) & mask;
       const uint64_t peers = match_digit(d, bits, __ballot(valid));
       const int lead = __ffsll(static_cast<long long>(peers)) - 1;
@@ -341,14 +351,16 @@ __global__ __launch_bounds__(kBlock) void radix_downsweep(
     {
       const int d0 = 2 * threadIdx.x, d1 = d0 + 1;
       const uint32_t a = d0 < ndig ? s_tcnt[d0] : 0u, b = d1 < ndig ? s_tcnt[d1] : 0u;
-      const uint32_t ex = block_exclusive_sum(a + b, s_tmp, nullptr);
+      uint32_t kept;
+      const uint32_t ex = block_exclusive_sum(a + b, s_tmp, &kept);
       if (d0 < ndig) s_toff[d0] = ex;
       if (d1 < ndig) s_toff[d1] = ex + a;
+      if (threadIdx.x == 0) s_kept = kept;
     }
     __syncthreads();
 #pragma unroll
     for (int s = 0; s < kRadixItems; ++s) {
-      if (wbase + s * kWave + lane < hi) {
+      if (wbase + s * kWave + lane < hi && k[s] != drop) {
         const uint32_t d = (k[s] >> shift) & mask;
         const uint32_t pos = s_toff[d] + s_wcnt[w][d] + r[s];
         s_key[pos] = k[s];
@@ -356,7 +368,8 @@ __global__ __launch_bounds__(kBlock) void radix_downsweep(
       }
     }
     __syncthreads();
-    for (int j = threadIdx.x; j < tn; j += kBlock) {
+    const int kn = static_cast<int>(s_kept);  // the tile's keys, less those dropped
+    for (int j = threadIdx.x; j < kn; j += kBlock) {
       const uint32_t key = s_key[j];
       const uint32_t d = (key >> shift) & mask;
       const uint32_t g = s_base[d] + (static_cast<uint32_t>(j) - s_toff[d]);
@@ -727,13 +740,19 @@ tbe_status launch_transpose(const tbe_tables* tb, const IndexArgs& ia, int weigh
   if (st) return st;
   uint32_t* hist = reinterpret_cast<uint32_t*>(ws + L.sort_hist);
   uint32_t* tot = hist + static_cast<int64_t>(kRadixDigits) * L.nblocks;
+  // the first pass leaves out the sentinel keys (ids outside their table, lookups the dense
+  // rows take, positions no bag covers): later kernels see only the kept keys
+  const uint32_t sentinel = static_cast<uint32_t>(tb->total_rows);
+  int32_t* n_sorted = counters + kSorted;
   int cur = 0;
   for (int pass = 0; pass < L.passes; ++pass) {
     const int ndig = 1 << L.bits[pass];
+    const int32_t* n_in = pass == 0 ? n_eff : n_sorted;
+    const uint32_t drop = pass == 0 ? sentinel : ~0u;
     {
       ProfScope ps("radix_upsweep", s);
-      hipLaunchKernelGGL(radix_upsweep, dim3(L.nblocks), dim3(kBlock), 0, s, keys[cur], N, n_eff, L.seg,
-                         L.shift[pass], L.bits[pass], hist, L.nblocks);
+      hipLaunchKernelGGL(radix_upsweep, dim3(L.nblocks), dim3(kBlock), 0, s, keys[cur], N, n_in, L.seg,
+                         L.shift[pass], L.bits[pass], drop, hist, L.nblocks);
     }
     if ((st = check_launch("radix_upsweep"))) return st;
     {
@@ -744,8 +763,8 @@ tbe_status launch_transpose(const tbe_tables* tb, const IndexArgs& ia, int weigh
     {
       ProfScope ps("radix_downsweep", s);
       hipLaunchKernelGGL(radix_downsweep, dim3(L.nblocks), dim3(kBlock), 0, s, keys[cur], pay[cur],
-                         keys[cur ^ 1], pay[cur ^ 1], N, n_eff, L.seg, L.shift[pass], L.bits[pass], hist,
-                         tot, L.nblocks);
+                         keys[cur ^ 1], pay[cur ^ 1], N, n_in, L.seg, L.shift[pass], L.bits[pass], drop, hist,
+                         tot, L.nblocks, pass == 0 ? n_sorted : nullptr);
     }
     if ((st = check_launch("radix_downsweep"))) return st;
     cur ^= 1;
@@ -756,9 +775,9 @@ tbe_status launch_transpose(const tbe_tables* tb, const IndexArgs& ia, int weigh
   uint32_t* seg_cnt = reinterpret_cast<uint32_t*>(ws + L.seg_cnt);
   {
     ProfScope ps("rle", s);
-    hipLaunchKernelGGL(rle_count, dim3(L.nblocks), dim3(kBlock), 0, s, keys[cur], N, n_eff, L.seg, seg_cnt);
-    hipLaunchKernelGGL(rle_scan, dim3(1), dim3(kBlock), 0, s, seg_cnt, L.nblocks, counters, run_start, N, n_eff);
-    hipLaunchKernelGGL(rle_write, dim3(L.nblocks), dim3(kBlock), 0, s, keys[cur], N, n_eff, L.seg, seg_cnt,
+    hipLaunchKernelGGL(rle_count, dim3(L.nblocks), dim3(kBlock), 0, s, keys[cur], N, n_sorted, L.seg, seg_cnt);
+    hipLaunchKernelGGL(rle_scan, dim3(1), dim3(kBlock), 0, s, seg_cnt, L.nblocks, counters, run_start, N, n_sorted);
+    hipLaunchKernelGGL(rle_write, dim3(L.nblocks), dim3(kBlock), 0, s, keys[cur], N, n_sorted, L.seg, seg_cnt,
                        run_key, run_start);
   }
   if ((st = check_launch("rle"))) return st;

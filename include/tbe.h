@@ -135,12 +135,15 @@ typedef struct {
 
 /* Device-side view of the transpose, for inspection by tests (tbe_transpose). */
 typedef struct {
-  const uint32_t* sorted_keys;     /* [N] linearized row id, ascending */
-  const uint32_t* sorted_payload;  /* [N] bag id t*B+b, or lookup position when weighted */
+  const uint32_t* sorted_keys;     /* [counters[13]] linearized row id, ascending (lookups of ids
+                                      outside their table are left out) */
+  const uint32_t* sorted_payload;  /* [counters[13]] bag id t*B+b, or lookup position when weighted */
   const uint32_t* run_key;         /* [N] key of run r (first num_runs used) */
-  const uint32_t* run_start;       /* [N+1] first sorted position of run r; run_start[num_runs] = N */
+  const uint32_t* run_start;       /* [N+1] first sorted position of run r; run_start[num_runs] =
+                                      counters[13] */
   const int32_t* counters;         /* [16]: 0 runs, 1 long runs, 2 chunks, 3..11 short runs per
-                                      bucket (next_pow2(D) = 4 .. 1024), 12 keys the sort covers */
+                                      bucket (next_pow2(D) = 4 .. 1024), 12 keys the sort covers
+                                      when a table is left out, 13 keys sorted */
   const uint32_t* long_list;       /* [cap][4] {key, start, len, first chunk} per long run */
   const uint32_t* long_table;      /* [cap] table of each long run */
   const uint32_t* chunk_list;      /* [cap][2] {long-run slot, chunk number} per chunk */
