@@ -34,7 +34,7 @@ HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"fp16": 2500.0, "bf16": 2500.0, "fp32": 157.3}
 KERNELS = ["bounds_offsets", "bounds_indices", "fwd_gather", "fwd_hist", "linearize",
            "radix_upsweep", "radix_scan", "radix_downsweep", "rle", "classify", "short_run",
-           "grad_accum", "long_apply", "hist_bwd_partial", "hist_bwd_apply", "dense_select",
+           "grad_accum", "long_apply", "hist_bwd_partial", "hist_bwd_apply", "dense_sample", "dense_select",
            "dense_partial", "dense_apply"]
 
 

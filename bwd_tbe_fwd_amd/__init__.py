@@ -48,7 +48,7 @@ class tbe_config(ctypes.Structure):
                 ("bag_windows", ctypes.c_int32), ("fused_long", ctypes.c_int32),
                 ("pretransposed", ctypes.c_int32), ("bags_per_wave", ctypes.c_int32),
                 ("bwd_streams", ctypes.c_int32), ("tiny_runs", ctypes.c_int32),
-                ("dense_min", ctypes.c_int32)]
+                ("dense_min", ctypes.c_int32), ("dense_presort", ctypes.c_int32)]
 
 
 class tbe_runs_view(ctypes.Structure):

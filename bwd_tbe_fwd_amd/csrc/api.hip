@@ -91,18 +91,23 @@ int device_cu_count() {
   return cached[dev];
 }
 
-int blocks_per_cu(const void* kernel) {
+int blocks_per_cu(const void* kernel, size_t dyn_lds) {
+  struct Entry {
+    const void* kernel;
+    size_t lds;
+    int n;
+  };
   static std::mutex mu;
-  static std::vector<std::pair<const void*, int>> cache;
+  static std::vector<Entry> cache;
   std::lock_guard<std::mutex> lock(mu);
   for (const auto& e : cache)
-    if (e.first == kernel) return e.second;
+    if (e.kernel == kernel && e.lds == dyn_lds) return e.n;
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kBlock, 0) != hipSuccess || n < 1) {
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kBlock, dyn_lds) != hipSuccess || n < 1) {
     (void)hipGetLastError();  // not sticky; fall back to the usual 8 (32 waves)
     n = 8;
   }
-  cache.emplace_back(kernel, n);
+  cache.push_back(Entry{kernel, dyn_lds, n});
   return n;
 }
 
@@ -128,6 +133,7 @@ Config resolve_config(const tbe_config* c) {
   r.tiny = c->tiny_runs > 0 ? static_cast<int>(hmin(c->tiny_runs, r.threshold - 1)) : 0;
   // a dense row is a long run
   r.dense_min = c->dense_min > 0 ? static_cast<int>(hmax(c->dense_min, r.threshold)) : 0;
+  r.dense_presort = c->dense_presort > 0 ? 1 : (c->dense_presort < 0 ? -1 : 0);
   return r;
 }
 
@@ -151,6 +157,19 @@ constexpr int kDefaultSortBlocks = 4096;
 constexpr int kClsBlocks = 4096;  // classification workgroups at most (the scan takes up to 4096)
 constexpr int kMaxSortBlocks = 4096;
 }  // namespace
+
+// sort / RLE block segments and classification blocks for n keys
+static void sort_geometry(int64_t n, const Config& cfg, int64_t* seg, int* nblocks, int* cls_blocks) {
+  const int64_t n1 = n > 0 ? n : 1;
+  const int64_t tiles = (n1 + kRadixTile - 1) / kRadixTile;
+  int64_t want = cfg.sort_blocks > 0 ? cfg.sort_blocks : kDefaultSortBlocks;
+  if (want > kMaxSortBlocks) want = kMaxSortBlocks;
+  if (want > tiles) want = tiles;
+  const int64_t per = (tiles + want - 1) / want;  // tiles per block
+  *seg = per * kRadixTile;
+  *nblocks = static_cast<int>((n1 + *seg - 1) / *seg);
+  *cls_blocks = static_cast<int>(hmax(1, hmin(kClsBlocks, (n1 + kBlock - 1) / kBlock)));
+}
 
 BwdLayout bwd_layout(const tbe_tables* tb, int64_t N, int weighted, const Config& cfg) {
   BwdLayout L;
@@ -176,16 +195,9 @@ BwdLayout bwd_layout(const tbe_tables* tb, int64_t N, int weighted, const Config
     L.cap_short[b] = tb->bucket_rows[b] > 0 ? (tb->bucket_rows[b] < N ? tb->bucket_rows[b] : N) : 0;
     L.short_list[b] = L.cap_short[b] ? c.take(L.cap_short[b] * 16) : 0;
   }
-  const int64_t tiles = (n1 + kRadixTile - 1) / kRadixTile;
-  int64_t want = cfg.sort_blocks > 0 ? cfg.sort_blocks : kDefaultSortBlocks;
-  if (want > kMaxSortBlocks) want = kMaxSortBlocks;
-  if (want > tiles) want = tiles;
-  const int64_t per = (tiles + want - 1) / want;  // tiles per block
-  L.seg = per * kRadixTile;
-  L.nblocks = static_cast<int>((n1 + L.seg - 1) / L.seg);
+  sort_geometry(N, cfg, &L.seg, &L.nblocks, &L.cls_blocks);
   L.sort_hist = c.take((static_cast<size_t>(kRadixDigits) * L.nblocks + kRadixDigits) * 4);
   L.seg_cnt = c.take(static_cast<size_t>(L.nblocks) * 4);
-  L.cls_blocks = static_cast<int>(hmax(1, hmin(kClsBlocks, (n1 + kBlock - 1) / kBlock)));
   L.cls_cnt = c.take(static_cast<size_t>(TBE_NUM_BUCKETS + 2) * L.cls_blocks * 4);
   // long-run chunks grouped by (table, window of bags); at most 4096 groups
   L.nwin = 1;
@@ -214,8 +226,44 @@ BwdLayout bwd_layout(const tbe_tables* tb, int64_t N, int weighted, const Config
     L.dense_P = static_cast<int>(hmax(1, hmin(hmin(64, 2048 / tb->T), steps)));
     L.dense_rows = c.take(static_cast<size_t>(tb->T) * kDenseRows * 4);
     L.dense_cnt = c.take(static_cast<size_t>(tb->T) * 4);
-    L.long_flag = c.take(static_cast<size_t>(L.cap_long) * 4);
     L.dense_partial = c.take(static_cast<size_t>(tb->T) * L.dense_P * kDenseRows * 128 * 4);
+    // automatic: the rows are picked before the sort from 2^26 lookups on, where the sort
+    // work they take away outweighs the sample's fixed cost (about twenty short launches)
+    L.dense_presort = cfg.dense_presort > 0 || (cfg.dense_presort == 0 && N >= (int64_t{1} << 26));
+  }
+  if (L.dense_on && !L.dense_presort) L.long_flag = c.take(L.cap_long * 4);
+  if (L.dense_on && L.dense_presort) {
+    // the sample: 64 positions in every hot_stride, at most 2^20 keys (every lookup of
+    // batches up to 2^20 lookups); a row is taken when its sampled lookups reach dense_min
+    // scaled to the sample
+    L.hot_stride = 64;
+    while (64 * ((N + L.hot_stride - 1) / L.hot_stride) > (int64_t{1} << 20)) L.hot_stride *= 2;
+    L.hot_thr = static_cast<int>(hmax(1, (static_cast<int64_t>(cfg.dense_min) * 64 + L.hot_stride - 1) / L.hot_stride));
+    SortPlan& P = L.sample;
+    P.N = 64 * ((N + L.hot_stride - 1) / L.hot_stride);
+    const int64_t m1 = P.N > 0 ? P.N : 1;
+    for (int i = 0; i < 2; ++i) {
+      P.keys[i] = c.take(m1 * 4);
+      P.pay[i] = c.take(m1 * 4);
+    }
+    P.run_key = c.take(m1 * 4);
+    P.run_start = c.take((m1 + 1) * 4);
+    P.cap_long = P.N / L.hot_thr + 1;
+    P.cap_chunk = 0;
+    P.long_list = c.take(P.cap_long * 16);
+    P.long_table = c.take(P.cap_long * 4);
+    P.long_count = c.take(P.cap_long * 4);
+    P.chunk_list = 0;
+    sort_geometry(P.N, cfg, &P.seg, &P.nblocks, &P.cls_blocks);
+    P.sort_hist = c.take((static_cast<size_t>(kRadixDigits) * P.nblocks + kRadixDigits) * 4);
+    P.seg_cnt = c.take(static_cast<size_t>(P.nblocks) * 4);
+    P.cls_cnt = c.take(static_cast<size_t>(TBE_NUM_BUCKETS + 2) * P.cls_blocks * 4);
+    P.counters = c.take(kNumCounters * 4);
+    int64_t hs = 1024;  // at most a quarter full
+    while (hs < 4 * static_cast<int64_t>(kDenseRows) * tb->T) hs <<= 1;
+    L.hot_set_size = hs;
+    L.hot_set = c.take(static_cast<size_t>(hs) * 4);
+    L.hot_bloom = c.take(static_cast<size_t>(kHotBloomWords) * 4);
   }
   L.counters = c.take(kNumCounters * 4);
   L.total = c.off;
@@ -312,6 +360,7 @@ void tbe_config_default(tbe_config* cfg) {
   cfg->bwd_streams = 0;
   cfg->tiny_runs = 8;
   cfg->dense_min = 2048;
+  cfg->dense_presort = 0;
 }
 
 int64_t tbe_meta_entries(int32_t T) { return T >= 0 ? static_cast<int64_t>(TBE_META_FIELDS) * (T + 1) : 0; }
@@ -558,7 +607,7 @@ tbe_status tbe_forward_hoisted(const tbe_tables* tables, const void* weights, vo
   if (tbe_status st = fork.status()) return st;
   int final_buf = 0;
   const tbe_status st_t = launch_transpose(tables, ia, weighted, static_cast<char*>(bwd_workspace), L,
-                                           cfg, hist, error_counts ? 1 : 0, &final_buf, fork.side());
+                                           cfg, hist, error_counts ? 1 : 0, 1, &final_buf, fork.side());
   const tbe_status st_f = st_t ? TBE_OK
                                : forward_body(tables, weights, ia, per_sample_weights, out, error_counts,
                                               cfg, saved, s);
@@ -600,7 +649,11 @@ static tbe_status backward_common(const tbe_tables* tables, void* weights, float
   // radix passes alternate buffers starting from buffer 0
   int final_buf = L.passes & 1;
   if (!cfg.pretransposed)
-    if (tbe_status st = launch_transpose(tables, ia, psw ? 1 : 0, ws, L, cfg, hist, 0, &final_buf, s)) return st;
+    if (tbe_status st = launch_transpose(tables, ia, psw ? 1 : 0, ws, L, cfg, hist, 0, 1, &final_buf, s)) return st;
+  // without dense_presort the dense rows come from the long runs (flags read by the chunk and
+  // apply kernels)
+  if (L.dense_on && !L.dense_presort)
+    if (tbe_status st = launch_dense_select_runs(tables, ws, L, hist, cfg, s)) return st;
   if (hist >= 0) {
     // with the hoisted forward's state, its saved counts replace counting the first 256 ids
     const uint16_t* saved = cfg.pretransposed ? reinterpret_cast<const uint16_t*>(ws + L.hist_saved) : nullptr;
@@ -608,10 +661,6 @@ static tbe_status backward_common(const tbe_tables* tables, void* weights, float
                                              saved, s))
       return st;
   }
-  // the hottest long runs of each table go to the dense path (flags read by the chunk and
-  // apply kernels)
-  if (L.dense_on)
-    if (tbe_status st = launch_dense_select(tables, ws, L, hist, cfg, s)) return st;
   // automatic: short runs of several widths are several short launches, whose tails leave
   // room for the long runs
   int buckets = 0;
@@ -674,7 +723,7 @@ tbe_status tbe_transpose(const tbe_tables* tables, const void* indices, int32_t 
   IndexArgs ia{indices, index_type, offsets, offset_type, num_indices};
   char* ws = static_cast<char*>(workspace);
   int final_buf = 0;
-  tbe_status st = launch_transpose(tables, ia, weighted ? 1 : 0, ws, L, cfg, -1, 0, &final_buf,
+  tbe_status st = launch_transpose(tables, ia, weighted ? 1 : 0, ws, L, cfg, -1, 0, 0, &final_buf,
                                    static_cast<hipStream_t>(stream));
   std::memset(view, 0, sizeof(*view));
   view->sorted_keys = reinterpret_cast<const uint32_t*>(ws + L.keys[final_buf]);

@@ -112,6 +112,9 @@ tbe_status accum_go(const tbe_tables* tb, const float* psw, const float* grad_ou
   const uint32_t* bag_of = WEIGHTED ? reinterpret_cast<const uint32_t*>(ws + L.bag_of) : nullptr;
   const uint32_t* order = nullptr;
   if (tbe_status st = launch_chunk_order(tb, psw, ws, L, final_buf, cfg, &order, s)) return st;
+  // dense rows picked from the long runs: their chunks are skipped
+  const uint32_t* long_flag =
+      L.dense_on && !L.dense_presort ? reinterpret_cast<const uint32_t*>(ws + L.long_flag) : nullptr;
   ProfScope ps("grad_accum", s);
 #define TBE_ACC(U)                                                                                 \
   hipLaunchKernelGGL((grad_accum_kernel<WEIGHTED, U>), dim3(resident_grid(grad_accum_kernel<WEIGHTED, U>, work)), \
@@ -120,8 +123,7 @@ tbe_status accum_go(const tbe_tables* tb, const float* psw, const float* grad_ou
                      reinterpret_cast<const uint32_t*>(ws + L.long_table),                        \
                      reinterpret_cast<const uint2*>(ws + L.chunk_list),                           \
                      reinterpret_cast<const int32_t*>(ws + L.counters), tb->meta, tb->B,           \
-                     tb->out_width, cfg.chunk, tb->max_D, order,                                  \
-                     L.dense_on ? reinterpret_cast<const uint32_t*>(ws + L.long_flag) : nullptr,  \
+                     tb->out_width, cfg.chunk, tb->max_D, order, long_flag,                       \
                      reinterpret_cast<float*>(ws + L.partial))
   if (cfg.bwd_unroll <= 2) TBE_ACC(2);
   else if (cfg.bwd_unroll <= 4) TBE_ACC(4);

@@ -135,7 +135,9 @@ tbe_status launch_short_and_apply(const tbe_tables* tb, void* W, float* momentum
   const uint4* long_list = reinterpret_cast<const uint4*>(ws + L.long_list);
   const uint32_t* long_table = reinterpret_cast<const uint32_t*>(ws + L.long_table);
   const float* partial = reinterpret_cast<const float*>(ws + L.partial);
-  const uint32_t* long_flag = L.dense_on ? reinterpret_cast<const uint32_t*>(ws + L.long_flag) : nullptr;
+  // dense rows picked from the long runs: their slots are skipped
+  const uint32_t* long_flag =
+      L.dense_on && !L.dense_presort ? reinterpret_cast<const uint32_t*>(ws + L.long_flag) : nullptr;
   if (opt == kOptSGD)
     return detail::apply_go<DT, kOptSGD>(W, momentum, long_list, long_table, counters, L.cap_long, tb, cfg.chunk, partial, long_flag, lr, eps, s);
   return detail::apply_go<DT, kOptAdagrad>(W, momentum, long_list, long_table, counters, L.cap_long, tb, cfg.chunk, partial, long_flag, lr, eps, s);

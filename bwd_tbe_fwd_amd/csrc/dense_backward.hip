@@ -13,10 +13,18 @@
 // (the head of a skewed id distribution) that replaces most of the long-run
 // gradient traffic.
 //
-// gfx950 mapping.  dense_select (one wave per table) takes the table's long
-// runs of at least dense_min lookups, in key order, up to kDenseRows of them,
-// records their row ids (sorted, as the long list is in key order) and flags
-// their long-list slots so that the chunk and apply kernels skip them.
+// gfx950 mapping.  dense_select (one wave per table) takes a table's long runs
+// in key order, up to kDenseRows of them, and records their row ids
+// (ascending).  In large batches the rows are picked before the sort, from a
+// sample of the lookups: dense_sample writes the keys of 64 positions out of
+// every hot_stride, which are sorted and run-length encoded on their own, the
+// runs that reach dense_min scaled to the sample are taken, and their keys go
+// into a hashed key set that linearize consults: their lookups get the
+// sentinel key, so the sort, the run-length encoding and the run kernels never
+// see them.  Otherwise (the sample's twenty-odd launches would cost more than
+// they save) the rows come from the batch's own long runs of at least
+// dense_min lookups after the sort, and their long-list slots are flagged so
+// that the chunk and apply kernels skip them.
 // dense_partial: workgroup (t, p) takes the table's 64-bag steps p, p + P, ...;
 // each of its four waves counts the lookups of 16 of the step's bags that hit
 // a selected row (a bit filter in LDS, then a 7-step search of the sorted row
@@ -49,12 +57,56 @@ __device__ __forceinline__ bool dense_table_ok(int D, int t, int hist_t) {
   return t != hist_t && D >= 16 && D <= kDnCols && D % 16 == 0;
 }
 
-// one wave per table: its long runs are long-list slots [lo, hi) (the list is in key order)
+// The sample: wave j takes positions stride * j + [0, 64).  A position's table is the last
+// table whose first offset is at or below it; lookups of tables the dense path does not take,
+// positions no table covers and ids outside their table (unless invalid_as_row0, when they
+// count as row 0) get the sentinel key, which the sort leaves out.
+template <typename IT, typename OT>
+__global__ __launch_bounds__(kBlock) void dense_sample_kernel(
+    const IT* __restrict__ indices, const OT* __restrict__ offsets, const int64_t* __restrict__ meta, int T,
+    int32_t B, int64_t N, int64_t stride, int64_t nsamp, int hist_t, int invalid_as_row0, uint32_t sentinel,
+    uint32_t* __restrict__ keys, uint32_t* __restrict__ pay) {
+  const int lane = lane_id();
+  const int64_t wave = (static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x) >> 6;
+  const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * kBlock) >> 6;
+  auto first = [&](int t) {  // table t's first lookup, clamped to [0, N]
+    const int64_t v = static_cast<int64_t>(offsets[static_cast<int64_t>(t) * B]);
+    return min(max(v, static_cast<int64_t>(0)), N);
+  };
+  const int64_t lo0 = first(0), hiT = first(T);
+  for (int64_t j = wave; j < nsamp; j += nwaves) {
+    const int64_t p = j * stride + lane;
+    uint32_t key = sentinel;
+    if (p >= lo0 && p < hiT) {
+      int lo = 0, hi = T - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (first(mid) <= p) lo = mid; else hi = mid - 1;
+      }
+      const TableMeta m = load_meta(meta, lo);
+      if (dense_table_ok(static_cast<int>(m.D), lo, hist_t)) {
+        const int64_t r = static_cast<int64_t>(indices[p]);
+        if (static_cast<uint64_t>(r) < static_cast<uint64_t>(m.E)) key = static_cast<uint32_t>(m.row_base + r);
+        else if (invalid_as_row0) key = static_cast<uint32_t>(m.row_base);
+      }
+    }
+    keys[j * kWave + lane] = key;
+    pay[j * kWave + lane] = 0u;
+  }
+}
+
+// One wave per table: the table's long runs (long-list slots [lo, hi), in key order) of at
+// least min_len lookups become its dense rows, at most kDenseRows, in ascending order.
+// Picked from the sorted sample (hot_set != NULL): their keys go into the key set (linear
+// probing; the most slot groups a lookup reads into *probe_max) and its filter.  Picked from
+// the batch's own runs (long_flag != NULL): each slot's flag says whether the chunk and apply
+// kernels leave it to the dense path.
 __global__ __launch_bounds__(kBlock) void dense_select_kernel(
     const uint4* __restrict__ long_list, const uint32_t* __restrict__ long_table,
     const int32_t* __restrict__ counters, int64_t cap_long, const int64_t* __restrict__ meta, int T,
-    int hist_t, uint32_t dense_min, int32_t* __restrict__ dense_rows, int32_t* __restrict__ dense_cnt,
-    uint32_t* __restrict__ long_flag) {
+    int hist_t, uint32_t min_len, int32_t* __restrict__ dense_rows, int32_t* __restrict__ dense_cnt,
+    uint32_t* __restrict__ long_flag, uint32_t* __restrict__ hot_set, uint32_t hot_mask,
+    uint32_t* __restrict__ hot_filter, int32_t* __restrict__ probe_max) {
   const int lane = lane_id();
   const int t = static_cast<int>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -76,12 +128,25 @@ __global__ __launch_bounds__(kBlock) void dense_select_kernel(
     const bool in = s < s1;
     uint4 L = make_uint4(0u, 0u, 0u, 0u);
     if (in) L = long_list[s];
-    const bool want = in && ok && L.z >= dense_min;
+    const bool want = in && ok && L.z >= min_len;
     const uint64_t wm = __ballot(want);
     const int rank = taken + __popcll(wm & lanemask_lt());
     const bool take = want && rank < kDenseRows;
     if (take) dense_rows[static_cast<int64_t>(t) * kDenseRows + rank] = static_cast<int32_t>(L.x - m.row_base);
-    if (in) long_flag[s] = take ? 1u : 0u;
+    if (long_flag && in) long_flag[s] = take ? 1u : 0u;
+    if (hot_set && take) {
+      const uint32_t key = L.x;
+      const uint32_t h = hot_slot(key, hot_mask);
+      int i = 0;  // the set holds 4 slots per possible key: a free slot is always found
+      while (true) {
+        const uint32_t prev = atomicCAS(&hot_set[(h + i) & hot_mask], kHotEmpty, key);
+        if (prev == kHotEmpty || prev == key) break;
+        ++i;
+      }
+      atomicMax(probe_max, (i >> 2) + 1);  // groups of four a lookup reads at most
+      const uint32_t f = hot_filter_bit(key);
+      atomicOr(&hot_filter[f >> 5], 1u << (f & 31));
+    }
     taken = min(kDenseRows, taken + __popcll(wm));
   }
   if (lane == 0) dense_cnt[t] = taken;
@@ -422,17 +487,56 @@ tbe_status apply_dense_go(const tbe_tables* tb, void* W, float* momentum, char* 
   return check_launch("dense_apply");
 }
 
+template <typename IT, typename OT>
+tbe_status sample_go(const tbe_tables* tb, const IndexArgs& ia, int hist_t, int invalid_as_row0, char* ws,
+                     const BwdLayout& L, hipStream_t s) {
+  const SortPlan& P = L.sample;
+  const int64_t nsamp = P.N / kWave;
+  const auto kernel = dense_sample_kernel<IT, OT>;
+  const int grid = resident_grid(kernel, (nsamp + kWavesPerBlock - 1) / kWavesPerBlock);
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kBlock), 0, s, static_cast<const IT*>(ia.indices),
+                     static_cast<const OT*>(ia.offsets), tb->meta, tb->T, tb->B, ia.N,
+                     static_cast<int64_t>(L.hot_stride), nsamp, hist_t, invalid_as_row0,
+                     static_cast<uint32_t>(tb->total_rows), reinterpret_cast<uint32_t*>(ws + P.keys[0]),
+                     reinterpret_cast<uint32_t*>(ws + P.pay[0]));
+  return check_launch("dense_sample");
+}
+
 }  // namespace
 
+tbe_status launch_dense_sample(const tbe_tables* tb, const IndexArgs& ia, int hist_t, int invalid_as_row0,
+                               char* ws, const BwdLayout& L, hipStream_t s) {
+  if (ia.itype == TBE_I32)
+    return ia.otype == TBE_I32 ? sample_go<int32_t, int32_t>(tb, ia, hist_t, invalid_as_row0, ws, L, s)
+                               : sample_go<int32_t, int64_t>(tb, ia, hist_t, invalid_as_row0, ws, L, s);
+  return ia.otype == TBE_I32 ? sample_go<int64_t, int32_t>(tb, ia, hist_t, invalid_as_row0, ws, L, s)
+                             : sample_go<int64_t, int64_t>(tb, ia, hist_t, invalid_as_row0, ws, L, s);
+}
+
 tbe_status launch_dense_select(const tbe_tables* tb, char* ws, const BwdLayout& L, int hist_t,
-                               const Config& cfg, hipStream_t s) {
+                               hipStream_t s) {
+  const SortPlan& P = L.sample;
+  hipLaunchKernelGGL(dense_select_kernel, dim3((tb->T + kWavesPerBlock - 1) / kWavesPerBlock), dim3(kBlock), 0, s,
+                     reinterpret_cast<const uint4*>(ws + P.long_list),
+                     reinterpret_cast<const uint32_t*>(ws + P.long_table),
+                     reinterpret_cast<const int32_t*>(ws + P.counters), P.cap_long, tb->meta, tb->T, hist_t, 0u,
+                     reinterpret_cast<int32_t*>(ws + L.dense_rows), reinterpret_cast<int32_t*>(ws + L.dense_cnt),
+                     nullptr, reinterpret_cast<uint32_t*>(ws + L.hot_set), static_cast<uint32_t>(L.hot_set_size - 1),
+                     reinterpret_cast<uint32_t*>(ws + L.hot_bloom),
+                     reinterpret_cast<int32_t*>(ws + L.counters) + kHotProbe);
+  return check_launch("dense_select");
+}
+
+tbe_status launch_dense_select_runs(const tbe_tables* tb, char* ws, const BwdLayout& L, int hist_t,
+                                    const Config& cfg, hipStream_t s) {
   ProfScope ps("dense_select", s);
   hipLaunchKernelGGL(dense_select_kernel, dim3((tb->T + kWavesPerBlock - 1) / kWavesPerBlock), dim3(kBlock), 0, s,
                      reinterpret_cast<const uint4*>(ws + L.long_list),
                      reinterpret_cast<const uint32_t*>(ws + L.long_table),
                      reinterpret_cast<const int32_t*>(ws + L.counters), L.cap_long, tb->meta, tb->T, hist_t,
                      static_cast<uint32_t>(cfg.dense_min), reinterpret_cast<int32_t*>(ws + L.dense_rows),
-                     reinterpret_cast<int32_t*>(ws + L.dense_cnt), reinterpret_cast<uint32_t*>(ws + L.long_flag));
+                     reinterpret_cast<int32_t*>(ws + L.dense_cnt), reinterpret_cast<uint32_t*>(ws + L.long_flag),
+                     nullptr, 0u, nullptr, nullptr);
   return check_launch("dense_select");
 }
 

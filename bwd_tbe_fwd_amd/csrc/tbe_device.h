@@ -200,6 +200,18 @@ __device__ __forceinline__ int table_of_key(const int64_t* __restrict__ meta, in
   return lo;
 }
 
+// The key set of the dense rows: open addressing with linear probing over a power-of-two
+// array of keys (kHotEmpty marks a free slot) that starts at a 16-byte group of four
+// slots, so that a lookup reads whole groups (one, nearly always) and stops at the first
+// group with a free slot; and a 65536-bit filter that most other keys fail.  Both hashes
+// are multiplicative (Knuth's golden-ratio constant and a second odd multiplier).
+constexpr uint32_t kHotEmpty = 0xffffffffu;
+__device__ __forceinline__ uint32_t hot_slot(uint32_t key, uint32_t mask) {
+  const uint32_t h = key * 0x9e3779b1u;
+  return ((h ^ (h >> 15)) << 2) & mask;  // first slot of a group
+}
+__device__ __forceinline__ uint32_t hot_filter_bit(uint32_t key) { return (key * 0x85ebca6bu) >> 16; }
+
 // short-run bucket of width D: log2(next_pow2(D)) - 2, for 4 <= D <= 1024
 __host__ __device__ __forceinline__ int bucket_of_D(int D) {
   int b = 0, p = 4;

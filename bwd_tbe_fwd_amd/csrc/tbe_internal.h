@@ -33,13 +33,14 @@ int device_cu_count();                 // compute units of the current device (c
 inline int64_t hmin(int64_t a, int64_t b) { return a < b ? a : b; }
 inline int64_t hmax(int64_t a, int64_t b) { return a > b ? a : b; }
 // Workgroups of kBlock threads of `kernel` one CU holds at once (its registers and
-// LDS decide), queried once per kernel.
-int blocks_per_cu(const void* kernel);
+// LDS, with dyn_lds bytes of dynamic LDS, decide), queried once per kernel and size.
+int blocks_per_cu(const void* kernel, size_t dyn_lds = 0);
 // Grid of a grid-stride kernel: every workgroup resident at once (a workgroup that
 // has to wait for a free slot would start its whole share late), at most work_blocks.
 template <typename K>
-int resident_grid(K* kernel, int64_t work_blocks) {
-  const int64_t cap = static_cast<int64_t>(device_cu_count()) * blocks_per_cu(reinterpret_cast<const void*>(kernel));
+int resident_grid(K* kernel, int64_t work_blocks, size_t dyn_lds = 0) {
+  const int64_t cap = static_cast<int64_t>(device_cu_count()) *
+                      blocks_per_cu(reinterpret_cast<const void*>(kernel), dyn_lds);
   return static_cast<int>(hmax(1, hmin(work_blocks, cap)));
 }
 
@@ -54,8 +55,20 @@ struct Config {
   int pretransposed, bags_per_wave, bwd_streams;
   int tiny;  // wave steps of short runs of at most this many lookups: half the lanes per run
   int dense_min;  // long runs of at least this many lookups take the dense path (0: off)
+  int dense_presort;  // dense rows picked before the sort: 1 always, -1 never, 0 large batches
 };
 Config resolve_config(const tbe_config* c);
+
+// Buffers of one sort + run-length encoding + classification (byte offsets into the workspace)
+struct SortPlan {
+  int64_t N;                                   // keys at most
+  size_t keys[2], pay[2], run_key, run_start, sort_hist, seg_cnt, cls_cnt, counters;
+  size_t long_list, long_table, long_count, chunk_list;
+  int64_t cap_long, cap_chunk;
+  int64_t seg;        // keys per sort / RLE block (multiple of kRadixTile)
+  int nblocks;        // sort / RLE blocks
+  int cls_blocks;     // classification blocks
+};
 
 // Workspace carve-up of the backward / transpose (byte offsets, 256-aligned)
 struct BwdLayout {
@@ -66,10 +79,18 @@ struct BwdLayout {
   size_t chunk_unit, chunk_order, unit_cnt;  // long-run chunk ordering by (table, bag window)
   size_t hist_partial, hist_count;             // histogram backward: per-block partial sums
   size_t hist_saved;                           // per-bag counts the histogram forward saves (u16)
-  // dense hot rows: per table kDenseRows selected row ids and their count, a flag per long
-  // run (1: taken by the dense path), dense_P partials of kDenseRows x 128 floats per table
-  size_t dense_rows, dense_cnt, long_flag, dense_partial;
-  int dense_P, dense_on;
+  // dense hot rows: per table kDenseRows selected row ids and their count, dense_P partials of
+  // kDenseRows x 128 floats per table.  With dense_presort the rows are chosen before the sort
+  // from a sample of the lookups (64 positions every hot_stride, sorted and run-length encoded
+  // on their own: runs of at least hot_thr sampled lookups), and their keys go into an
+  // open-addressing set (hot_set, hot_set_size entries, at most a quarter of them used) with a
+  // 65536-bit filter, which linearize consults; otherwise they come from the batch's long runs
+  // after the sort, with a flag per long-list slot (long_flag) that the chunk and apply
+  // kernels read
+  size_t dense_rows, dense_cnt, dense_partial, hot_set, hot_bloom, long_flag;
+  int dense_P, dense_on, dense_presort, hot_stride, hot_thr;
+  int64_t hot_set_size;
+  SortPlan sample;
   int nwin, win_size, units;
   int64_t cap_long, cap_chunk, cap_short[TBE_NUM_BUCKETS];
   int64_t seg;        // keys per sort / RLE block (multiple of kRadixTile)
@@ -85,8 +106,10 @@ constexpr int kOptSGD = 0;
 constexpr int kOptAdagrad = 1;
 
 // kNeff: keys the sort covers when a table is left out of the runs; kSorted: keys kept by the
-// first radix pass (sentinel keys left out), the length of the sorted arrays
-enum Counter { kRuns = 0, kLong = 1, kChunks = 2, kShort0 = 3, kNeff = 12, kSorted = 13, kNumCounters = 16 };
+// first radix pass (sentinel keys left out), the length of the sorted arrays; kHotProbe: the
+// longest probe sequence of the dense-row key set
+enum Counter { kRuns = 0, kLong = 1, kChunks = 2, kShort0 = 3, kNeff = 12, kSorted = 13, kHotProbe = 14,
+               kNumCounters = 16 };
 static_assert(kShort0 + TBE_NUM_BUCKETS <= kNeff, "counter slots overlap");
 
 // ---------------------------------------------------------------------------
@@ -122,17 +145,29 @@ tbe_status launch_bounds_indices(const tbe_tables* tb, void* indices, int itype,
 // updated by the histogram backward)
 // invalid_as_row0: an id outside its table counts as row 0 (the value the bounds
 // repair writes) instead of being dropped
+// dense (with L.dense_on and L.dense_presort): the dense rows are picked first and their
+// lookups are left out of the runs (the backward's transpose; tbe_transpose keeps every
+// lookup)
 tbe_status launch_transpose(const tbe_tables* tb, const IndexArgs& ia, int weighted,
                             char* ws, const BwdLayout& L, const Config& cfg, int skip_table,
-                            int invalid_as_row0, int* final_buf, hipStream_t s);
+                            int invalid_as_row0, int dense, int* final_buf, hipStream_t s);
 
 // histogram backward of the small table (counts x gradient on MFMA, then the optimizer)
 constexpr int kHistBwdBlocks = 512;  // max partials (workgroups) of the histogram backward
-// dense hot rows of large tables (counts x gradient on MFMA): the selection flags the long runs
-// it takes (before the chunk and apply kernels run); the backward updates those rows
+// dense hot rows of large tables (counts x gradient on MFMA).  With dense_presort, before the
+// sort: the sampled keys (into L.sample's first key buffer), then, from the sample's sorted
+// runs, the rows of each table and the key set linearize consults.  The backward updates
+// those rows.
 constexpr int kDenseRows = 128;  // rows per table at most
+constexpr int kHotBloomWords = 2048;  // 65536-bit filter of the dense-row keys
+tbe_status launch_dense_sample(const tbe_tables* tb, const IndexArgs& ia, int hist_t, int invalid_as_row0,
+                               char* ws, const BwdLayout& L, hipStream_t s);
 tbe_status launch_dense_select(const tbe_tables* tb, char* ws, const BwdLayout& L, int hist_t,
-                               const Config& cfg, hipStream_t s);
+                               hipStream_t s);
+// the rows from the batch's sorted long runs instead (without dense_presort), flagging their
+// long-list slots
+tbe_status launch_dense_select_runs(const tbe_tables* tb, char* ws, const BwdLayout& L, int hist_t,
+                                    const Config& cfg, hipStream_t s);
 tbe_status launch_dense_backward(const tbe_tables* tb, void* W, float* momentum, int opt,
                                  const IndexArgs& ia, const float* grad_out, float lr, float eps,
                                  char* ws, const BwdLayout& L, hipStream_t s);

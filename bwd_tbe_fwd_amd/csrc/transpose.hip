@@ -90,12 +90,26 @@ __device__ __forceinline__ uint64_t match_digit(uint32_t d, int bits, uint64_t v
 // N - (lookups of skip_t) keys; that count goes to *n_eff.  Positions that no
 // bag covers (possible only with offsets that break the documented contract)
 // get the sentinel key, so every key and payload the sort reads is defined.
+// hot_set != NULL: keys in the dense-row key set (hot_mask + 1 slots; the most slot groups
+// a lookup reads in *hot_probes) get the sentinel key too: those lookups are the
+// dense path's.  The set's filter goes into LDS; keys that pass it probe the set (a
+// whole copy in LDS measured slower: it cost occupancy, and most probes are hits anyway).
+constexpr int kLinU = 8;  // positions per lane per step
 template <typename IT, typename OT, bool WEIGHTED>
 __global__ __launch_bounds__(kBlock) void linearize_kernel(
     const IT* __restrict__ indices, const OT* __restrict__ offsets, const int64_t* __restrict__ meta,
     int32_t B, int64_t nbags, int32_t N, uint32_t sentinel, int skip_t, int invalid_as_row0,
-    uint32_t* __restrict__ keys, uint32_t* __restrict__ pay, uint32_t* __restrict__ bag_of,
-    int32_t* __restrict__ n_eff) {
+    const uint32_t* __restrict__ hot_filter, const uint32_t* __restrict__ hot_set, uint32_t hot_mask,
+    const int32_t* __restrict__ hot_probes, uint32_t* __restrict__ keys, uint32_t* __restrict__ pay,
+    uint32_t* __restrict__ bag_of, int32_t* __restrict__ n_eff) {
+  __shared__ __align__(16) uint32_t s_filter[kHotBloomWords];
+  int hot_max = 0;
+  if (hot_set) {
+    for (int i = 4 * threadIdx.x; i < kHotBloomWords; i += 4 * kBlock)
+      *reinterpret_cast<u32x4*>(s_filter + i) = *reinterpret_cast<const u32x4*>(hot_filter + i);
+    hot_max = *hot_probes;
+    __syncthreads();
+  }
   const int lane = lane_id();
   const int64_t wave = (static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x) >> 6;
   const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * kBlock) >> 6;
@@ -145,31 +159,78 @@ __global__ __launch_bounds__(kBlock) void linearize_kernel(
     }
     const int32_t Eend = __shfl(e, kWave - 1);
     const uint64_t skip_mask = __ballot(skip);
-    for (int32_t base = S; base < Eend; base += kWave) {
-      const int32_t p = base + lane;
-      const bool valid = p < Eend;
-      // first lane l with e_l > p
-      int lo = 0, hi = kWave - 1;
+    // kLinU positions a lane per step: their ids (and then their key-set probes) are
+    // requested together
+    for (int32_t base = S; base < Eend; base += kLinU * kWave) {
+      int32_t p[kLinU];
+      int k[kLinU];
+      bool act[kLinU];
+      uint32_t key[kLinU];
 #pragma unroll
-      for (int step = 0; step < 6; ++step) {
-        const int mid = (lo + hi) >> 1;
-        const int32_t em = __shfl(e, mid);
-        if (em > p) hi = mid; else lo = mid + 1;
+      for (int u = 0; u < kLinU; ++u) {
+        p[u] = base + u * kWave + lane;
+        // first lane l with e_l > p
+        int lo = 0, hi = kWave - 1;
+#pragma unroll
+        for (int step = 0; step < 6; ++step) {
+          const int mid = (lo + hi) >> 1;
+          const int32_t em = __shfl(e, mid);
+          if (em > p[u]) hi = mid; else lo = mid + 1;
+        }
+        k[u] = lo;
+        act[u] = p[u] < Eend && !((skip_mask >> lo) & 1ull);
       }
-      const int k = lo;
-      const int64_t rbk = __shfl(rb, k);
-      const int64_t Ek = __shfl(E, k);
-      if (valid && !((skip_mask >> k) & 1ull)) {
-        const int64_t r = static_cast<int64_t>(indices[p]);
-        const uint32_t key = (static_cast<uint64_t>(r) < static_cast<uint64_t>(Ek))
-                                 ? static_cast<uint32_t>(rbk + r)
-                                 : (invalid_as_row0 ? static_cast<uint32_t>(rbk) : sentinel);
-        const int32_t q = compact(p);
-        keys[q] = key;
-        const uint32_t b = static_cast<uint32_t>(g0 + k);
+      int64_t r[kLinU];
+#pragma unroll
+      for (int u = 0; u < kLinU; ++u) r[u] = act[u] ? static_cast<int64_t>(indices[p[u]]) : 0;
+#pragma unroll
+      for (int u = 0; u < kLinU; ++u) {
+        const int64_t rbk = __shfl(rb, k[u]);
+        const int64_t Ek = __shfl(E, k[u]);
+        key[u] = (static_cast<uint64_t>(r[u]) < static_cast<uint64_t>(Ek))
+                     ? static_cast<uint32_t>(rbk + r[u])
+                     : (invalid_as_row0 ? static_cast<uint32_t>(rbk) : sentinel);
+      }
+      if (hot_set) {
+        // the filter, then every candidate's first group of four slots at once; the rare
+        // full group without the key sends its lanes to the next groups, all together
+        bool pend[kLinU];
+        uint32_t h[kLinU];
+        u32x4 v[kLinU];
+#pragma unroll
+        for (int u = 0; u < kLinU; ++u) {
+          const uint32_t f = hot_filter_bit(key[u]);
+          pend[u] = act[u] && key[u] != sentinel && ((s_filter[f >> 5] >> (f & 31)) & 1u);
+          h[u] = hot_slot(key[u], hot_mask);
+        }
+        for (int g = 0; g < hot_max; ++g) {
+#pragma unroll
+          for (int u = 0; u < kLinU; ++u)
+            if (pend[u]) v[u] = *reinterpret_cast<const u32x4*>(hot_set + ((h[u] + 4 * g) & hot_mask));
+          bool more = false;
+#pragma unroll
+          for (int u = 0; u < kLinU; ++u) {
+            if (!pend[u]) continue;
+            const uint32_t k = key[u];
+            const bool hit = v[u].x == k || v[u].y == k || v[u].z == k || v[u].w == k;
+            const bool gap = v[u].x == kHotEmpty || v[u].y == kHotEmpty || v[u].z == kHotEmpty ||
+                              v[u].w == kHotEmpty;
+            if (hit) key[u] = sentinel;
+            pend[u] = !hit && !gap;
+            more |= pend[u];
+          }
+          if (!__ballot(more)) break;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kLinU; ++u) {
+        if (!act[u]) continue;
+        const int32_t q = compact(p[u]);
+        keys[q] = key[u];
+        const uint32_t b = static_cast<uint32_t>(g0 + k[u]);
         if constexpr (WEIGHTED) {
-          pay[q] = static_cast<uint32_t>(p);
-          bag_of[p] = b;
+          pay[q] = static_cast<uint32_t>(p[u]);
+          bag_of[p[u]] = b;
         } else {
           pay[q] = b;
         }
@@ -677,27 +738,113 @@ __global__ void fill_i32_kernel(int32_t* p, int32_t v, int64_t n) {
   if (i < n) p[i] = v;
 }
 
+// the dense-row key set linearize consults (NULL set: none)
+struct HotSet {
+  const uint32_t* filter;
+  const uint32_t* set;
+  uint32_t mask;
+  const int32_t* probes;
+};
+
 template <typename IT, typename OT>
 tbe_status linearize_go(const tbe_tables* tb, const IndexArgs& ia, int weighted, uint32_t* keys,
                         uint32_t* pay, uint32_t* bag_of, int skip_t, int invalid_as_row0,
-                        int32_t* n_eff, hipStream_t s) {
+                        const HotSet& hot, int32_t* n_eff, hipStream_t s) {
   const int64_t nbags = static_cast<int64_t>(tb->T) * tb->B;
   const int64_t groups = (nbags + kWave - 1) / kWave;
-  const int64_t cap = static_cast<int64_t>(device_cu_count()) * 8 * kWavesPerBlock;
-  const int grid = static_cast<int>(hmax(1, (hmin(groups, cap) + kWavesPerBlock - 1) / kWavesPerBlock));
+  const int64_t work = (groups + kWavesPerBlock - 1) / kWavesPerBlock;
   const uint32_t sentinel = static_cast<uint32_t>(tb->total_rows);
   ProfScope ps("linearize", s);
   if (weighted)
-    hipLaunchKernelGGL((linearize_kernel<IT, OT, true>), dim3(grid), dim3(kBlock), 0, s,
+    hipLaunchKernelGGL((linearize_kernel<IT, OT, true>), dim3(resident_grid(linearize_kernel<IT, OT, true>, work)),
+                       dim3(kBlock), 0, s,
                        static_cast<const IT*>(ia.indices), static_cast<const OT*>(ia.offsets), tb->meta,
-                       tb->B, nbags, static_cast<int32_t>(ia.N), sentinel, skip_t, invalid_as_row0, keys, pay,
-                       bag_of, n_eff);
+                       tb->B, nbags, static_cast<int32_t>(ia.N), sentinel, skip_t, invalid_as_row0, hot.filter,
+                       hot.set, hot.mask, hot.probes, keys, pay, bag_of, n_eff);
   else
-    hipLaunchKernelGGL((linearize_kernel<IT, OT, false>), dim3(grid), dim3(kBlock), 0, s,
+    hipLaunchKernelGGL((linearize_kernel<IT, OT, false>), dim3(resident_grid(linearize_kernel<IT, OT, false>, work)),
+                       dim3(kBlock), 0, s,
                        static_cast<const IT*>(ia.indices), static_cast<const OT*>(ia.offsets), tb->meta,
-                       tb->B, nbags, static_cast<int32_t>(ia.N), sentinel, skip_t, invalid_as_row0, keys, pay,
-                       bag_of, n_eff);
+                       tb->B, nbags, static_cast<int32_t>(ia.N), sentinel, skip_t, invalid_as_row0, hot.filter,
+                       hot.set, hot.mask, hot.probes, keys, pay, bag_of, n_eff);
   return check_launch("linearize");
+}
+
+// Radix sort of the plan's keys[0] (with payloads) over `passes` passes, run-length encoding
+// and classification.  Keys equal to `drop` (the sentinel) are left out by the first pass;
+// n_in != NULL bounds the keys read (the count linearize leaves).  A run of at least
+// `threshold` lookups is long; short runs go to `lists` (capacity 0: not written).
+// names: the profiling names of the five phases.
+struct RouteNames {
+  const char *up, *scan, *down, *rle, *cls;
+};
+constexpr RouteNames kMainNames = {"radix_upsweep", "radix_scan", "radix_downsweep", "rle", "classify"};
+constexpr RouteNames kQuietNames = {"-", "-", "-", "-", "-"};
+
+tbe_status sort_route(const tbe_tables* tb, char* ws, const SortPlan& P, const BwdLayout& L,
+                      const int32_t* n_in, uint32_t drop, int threshold, int chunk, const ShortLists& lists,
+                      const RouteNames& nm, int* final_buf, hipStream_t s) {
+  const int64_t N = P.N;
+  int32_t* counters = reinterpret_cast<int32_t*>(ws + P.counters);
+  uint32_t* keys[2] = {reinterpret_cast<uint32_t*>(ws + P.keys[0]), reinterpret_cast<uint32_t*>(ws + P.keys[1])};
+  uint32_t* pay[2] = {reinterpret_cast<uint32_t*>(ws + P.pay[0]), reinterpret_cast<uint32_t*>(ws + P.pay[1])};
+  uint32_t* hist = reinterpret_cast<uint32_t*>(ws + P.sort_hist);
+  uint32_t* tot = hist + static_cast<int64_t>(kRadixDigits) * P.nblocks;
+  int32_t* n_sorted = counters + kSorted;
+  tbe_status st;
+  int cur = 0;
+  for (int pass = 0; pass < L.passes; ++pass) {
+    const int ndig = 1 << L.bits[pass];
+    const int32_t* n_p = pass == 0 ? n_in : n_sorted;
+    const uint32_t d = pass == 0 ? drop : ~0u;
+    {
+      ProfScope ps(nm.up, s);
+      hipLaunchKernelGGL(radix_upsweep, dim3(P.nblocks), dim3(kBlock), 0, s, keys[cur], N, n_p, P.seg,
+                         L.shift[pass], L.bits[pass], d, hist, P.nblocks);
+    }
+    if ((st = check_launch("radix_upsweep"))) return st;
+    {
+      ProfScope ps(nm.scan, s);
+      hipLaunchKernelGGL(radix_scan, dim3(ndig), dim3(kBlock), 0, s, hist, P.nblocks, tot);
+    }
+    if ((st = check_launch("radix_scan"))) return st;
+    {
+      ProfScope ps(nm.down, s);
+      hipLaunchKernelGGL(radix_downsweep, dim3(P.nblocks), dim3(kBlock), 0, s, keys[cur], pay[cur],
+                         keys[cur ^ 1], pay[cur ^ 1], N, n_p, P.seg, L.shift[pass], L.bits[pass], d, hist,
+                         tot, P.nblocks, pass == 0 ? n_sorted : nullptr);
+    }
+    if ((st = check_launch("radix_downsweep"))) return st;
+    cur ^= 1;
+  }
+  *final_buf = cur;
+  uint32_t* run_key = reinterpret_cast<uint32_t*>(ws + P.run_key);
+  uint32_t* run_start = reinterpret_cast<uint32_t*>(ws + P.run_start);
+  uint32_t* seg_cnt = reinterpret_cast<uint32_t*>(ws + P.seg_cnt);
+  {
+    ProfScope ps(nm.rle, s);
+    hipLaunchKernelGGL(rle_count, dim3(P.nblocks), dim3(kBlock), 0, s, keys[cur], N, n_sorted, P.seg, seg_cnt);
+    hipLaunchKernelGGL(rle_scan, dim3(1), dim3(kBlock), 0, s, seg_cnt, P.nblocks, counters, run_start, N, n_sorted);
+    hipLaunchKernelGGL(rle_write, dim3(P.nblocks), dim3(kBlock), 0, s, keys[cur], N, n_sorted, P.seg, seg_cnt,
+                       run_key, run_start);
+  }
+  if ((st = check_launch("rle"))) return st;
+  {
+    uint32_t* cls_cnt = reinterpret_cast<uint32_t*>(ws + P.cls_cnt);
+    const uint32_t total_rows = static_cast<uint32_t>(tb->total_rows);
+    ProfScope ps(nm.cls, s);
+    const size_t lds = table_lds_bytes(tb->T);
+    hipLaunchKernelGGL(classify_count, dim3(P.cls_blocks), dim3(kBlock), lds, s, run_key, run_start,
+                       counters, tb->meta, tb->T, total_rows, threshold, chunk, cls_cnt);
+    hipLaunchKernelGGL(classify_scan, dim3(kClsRows), dim3(kBlock), 0, s, cls_cnt, P.cls_blocks, counters);
+    hipLaunchKernelGGL(classify_write, dim3(P.cls_blocks), dim3(kBlock), lds, s, run_key, run_start,
+                       counters, tb->meta, tb->T, total_rows, threshold, chunk, cls_cnt,
+                       reinterpret_cast<uint4*>(ws + P.long_list), reinterpret_cast<uint32_t*>(ws + P.long_table),
+                       reinterpret_cast<uint32_t*>(ws + P.long_count),
+                       P.cap_chunk ? reinterpret_cast<uint2*>(ws + P.chunk_list) : nullptr, P.cap_long,
+                       P.cap_chunk, lists);
+  }
+  return check_launch("classify");
 }
 
 }  // namespace
@@ -711,96 +858,89 @@ tbe_status launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s) {
 
 tbe_status launch_transpose(const tbe_tables* tb, const IndexArgs& ia, int weighted, char* ws,
                             const BwdLayout& L, const Config& cfg, int skip_table,
-                            int invalid_as_row0, int* final_buf, hipStream_t s) {
+                            int invalid_as_row0, int dense, int* final_buf, hipStream_t s) {
   int32_t* counters = reinterpret_cast<int32_t*>(ws + L.counters);
   if (tbe_status st = launch_fill_i32(counters, 0, kNumCounters, s)) return st;
   const int64_t N = L.N;
   *final_buf = 0;
+  // without the dense rows (or with no lookups) no table has any: a backward that takes these
+  // runs as they are leaves every row to them
+  if (L.dense_on && L.dense_presort && (!dense || N == 0))
+    if (tbe_status st = launch_fill_i32(reinterpret_cast<int32_t*>(ws + L.dense_cnt), 0, tb->T, s)) return st;
+  dense = dense && L.dense_on && L.dense_presort;
   if (N == 0) {
     uint32_t* rs = reinterpret_cast<uint32_t*>(ws + L.run_start);
     return launch_fill_i32(reinterpret_cast<int32_t*>(rs), 0, 1, s);
   }
-  uint32_t* keys[2] = {reinterpret_cast<uint32_t*>(ws + L.keys[0]), reinterpret_cast<uint32_t*>(ws + L.keys[1])};
-  uint32_t* pay[2] = {reinterpret_cast<uint32_t*>(ws + L.pay[0]), reinterpret_cast<uint32_t*>(ws + L.pay[1])};
-  uint32_t* bag_of = weighted ? reinterpret_cast<uint32_t*>(ws + L.bag_of) : nullptr;
   // with a skipped table the sort covers only the other tables' lookups, a count
   // known on the device once linearize has run
   if (skip_table >= 0 && weighted) {
     set_error("a table can be left out of the runs only without per-sample weights");
     return TBE_ERR_ARG;
   }
-  int32_t* n_eff = skip_table >= 0 ? counters + kNeff : nullptr;
+  const uint32_t sentinel = static_cast<uint32_t>(tb->total_rows);
   tbe_status st;
+  // the dense rows, picked from a sample of the lookups before the sort
+  HotSet hot{nullptr, nullptr, 0u, nullptr};
+  if (dense) {
+    ProfScope ps("dense_sample", s);
+    const SortPlan& P = L.sample;
+    if ((st = launch_fill_i32(reinterpret_cast<int32_t*>(ws + P.counters), 0, kNumCounters, s))) return st;
+    if ((st = launch_fill_i32(reinterpret_cast<int32_t*>(ws + L.hot_set), -1, L.hot_set_size, s))) return st;
+    if ((st = launch_fill_i32(reinterpret_cast<int32_t*>(ws + L.hot_bloom), 0, kHotBloomWords, s))) return st;
+    if ((st = launch_dense_sample(tb, ia, skip_table, invalid_as_row0, ws, L, s))) return st;
+    ShortLists none;
+    for (int b = 0; b < TBE_NUM_BUCKETS; ++b) {
+      none.p[b] = nullptr;
+      none.cap[b] = 0;
+    }
+    int fb;
+    if ((st = sort_route(tb, ws, P, L, nullptr, sentinel, L.hot_thr, 1 << 30, none, kQuietNames, &fb, s))) return st;
+    if ((st = launch_dense_select(tb, ws, L, skip_table, s))) return st;
+    hot = HotSet{reinterpret_cast<const uint32_t*>(ws + L.hot_bloom),
+                 reinterpret_cast<const uint32_t*>(ws + L.hot_set), static_cast<uint32_t>(L.hot_set_size - 1),
+                 counters + kHotProbe};
+  }
+  uint32_t* keys0 = reinterpret_cast<uint32_t*>(ws + L.keys[0]);
+  uint32_t* pay0 = reinterpret_cast<uint32_t*>(ws + L.pay[0]);
+  uint32_t* bag_of = weighted ? reinterpret_cast<uint32_t*>(ws + L.bag_of) : nullptr;
+  int32_t* n_eff = skip_table >= 0 ? counters + kNeff : nullptr;
   if (ia.itype == TBE_I32)
-    st = ia.otype == TBE_I32 ? linearize_go<int32_t, int32_t>(tb, ia, weighted, keys[0], pay[0], bag_of, skip_table, invalid_as_row0, n_eff, s)
-                             : linearize_go<int32_t, int64_t>(tb, ia, weighted, keys[0], pay[0], bag_of, skip_table, invalid_as_row0, n_eff, s);
+    st = ia.otype == TBE_I32 ? linearize_go<int32_t, int32_t>(tb, ia, weighted, keys0, pay0, bag_of, skip_table, invalid_as_row0, hot, n_eff, s)
+                             : linearize_go<int32_t, int64_t>(tb, ia, weighted, keys0, pay0, bag_of, skip_table, invalid_as_row0, hot, n_eff, s);
   else
-    st = ia.otype == TBE_I32 ? linearize_go<int64_t, int32_t>(tb, ia, weighted, keys[0], pay[0], bag_of, skip_table, invalid_as_row0, n_eff, s)
-                             : linearize_go<int64_t, int64_t>(tb, ia, weighted, keys[0], pay[0], bag_of, skip_table, invalid_as_row0, n_eff, s);
+    st = ia.otype == TBE_I32 ? linearize_go<int64_t, int32_t>(tb, ia, weighted, keys0, pay0, bag_of, skip_table, invalid_as_row0, hot, n_eff, s)
+                             : linearize_go<int64_t, int64_t>(tb, ia, weighted, keys0, pay0, bag_of, skip_table, invalid_as_row0, hot, n_eff, s);
   if (st) return st;
-  uint32_t* hist = reinterpret_cast<uint32_t*>(ws + L.sort_hist);
-  uint32_t* tot = hist + static_cast<int64_t>(kRadixDigits) * L.nblocks;
   // the first pass leaves out the sentinel keys (ids outside their table, lookups the dense
   // rows take, positions no bag covers): later kernels see only the kept keys
-  const uint32_t sentinel = static_cast<uint32_t>(tb->total_rows);
-  int32_t* n_sorted = counters + kSorted;
-  int cur = 0;
-  for (int pass = 0; pass < L.passes; ++pass) {
-    const int ndig = 1 << L.bits[pass];
-    const int32_t* n_in = pass == 0 ? n_eff : n_sorted;
-    const uint32_t drop = pass == 0 ? sentinel : ~0u;
-    {
-      ProfScope ps("radix_upsweep", s);
-      hipLaunchKernelGGL(radix_upsweep, dim3(L.nblocks), dim3(kBlock), 0, s, keys[cur], N, n_in, L.seg,
-                         L.shift[pass], L.bits[pass], drop, hist, L.nblocks);
-    }
-    if ((st = check_launch("radix_upsweep"))) return st;
-    {
-      ProfScope ps("radix_scan", s);
-      hipLaunchKernelGGL(radix_scan, dim3(ndig), dim3(kBlock), 0, s, hist, L.nblocks, tot);
-    }
-    if ((st = check_launch("radix_scan"))) return st;
-    {
-      ProfScope ps("radix_downsweep", s);
-      hipLaunchKernelGGL(radix_downsweep, dim3(L.nblocks), dim3(kBlock), 0, s, keys[cur], pay[cur],
-                         keys[cur ^ 1], pay[cur ^ 1], N, n_in, L.seg, L.shift[pass], L.bits[pass], drop, hist,
-                         tot, L.nblocks, pass == 0 ? n_sorted : nullptr);
-    }
-    if ((st = check_launch("radix_downsweep"))) return st;
-    cur ^= 1;
+  SortPlan M;
+  M.N = N;
+  for (int i = 0; i < 2; ++i) {
+    M.keys[i] = L.keys[i];
+    M.pay[i] = L.pay[i];
   }
-  *final_buf = cur;
-  uint32_t* run_key = reinterpret_cast<uint32_t*>(ws + L.run_key);
-  uint32_t* run_start = reinterpret_cast<uint32_t*>(ws + L.run_start);
-  uint32_t* seg_cnt = reinterpret_cast<uint32_t*>(ws + L.seg_cnt);
-  {
-    ProfScope ps("rle", s);
-    hipLaunchKernelGGL(rle_count, dim3(L.nblocks), dim3(kBlock), 0, s, keys[cur], N, n_sorted, L.seg, seg_cnt);
-    hipLaunchKernelGGL(rle_scan, dim3(1), dim3(kBlock), 0, s, seg_cnt, L.nblocks, counters, run_start, N, n_sorted);
-    hipLaunchKernelGGL(rle_write, dim3(L.nblocks), dim3(kBlock), 0, s, keys[cur], N, n_sorted, L.seg, seg_cnt,
-                       run_key, run_start);
-  }
-  if ((st = check_launch("rle"))) return st;
+  M.run_key = L.run_key;
+  M.run_start = L.run_start;
+  M.sort_hist = L.sort_hist;
+  M.seg_cnt = L.seg_cnt;
+  M.cls_cnt = L.cls_cnt;
+  M.counters = L.counters;
+  M.long_list = L.long_list;
+  M.long_table = L.long_table;
+  M.long_count = L.long_count;
+  M.chunk_list = L.chunk_list;
+  M.cap_long = L.cap_long;
+  M.cap_chunk = L.cap_chunk;
+  M.seg = L.seg;
+  M.nblocks = L.nblocks;
+  M.cls_blocks = L.cls_blocks;
   ShortLists lists;
   for (int b = 0; b < TBE_NUM_BUCKETS; ++b) {
     lists.p[b] = L.cap_short[b] ? reinterpret_cast<uint4*>(ws + L.short_list[b]) : nullptr;
     lists.cap[b] = L.cap_short[b];
   }
-  {
-    uint32_t* cls_cnt = reinterpret_cast<uint32_t*>(ws + L.cls_cnt);
-    const uint32_t total_rows = static_cast<uint32_t>(tb->total_rows);
-    ProfScope ps("classify", s);
-    const size_t lds = table_lds_bytes(tb->T);
-    hipLaunchKernelGGL(classify_count, dim3(L.cls_blocks), dim3(kBlock), lds, s, run_key, run_start,
-                       counters, tb->meta, tb->T, total_rows, cfg.threshold, cfg.chunk, cls_cnt);
-    hipLaunchKernelGGL(classify_scan, dim3(kClsRows), dim3(kBlock), 0, s, cls_cnt, L.cls_blocks, counters);
-    hipLaunchKernelGGL(classify_write, dim3(L.cls_blocks), dim3(kBlock), lds, s, run_key, run_start,
-                       counters, tb->meta, tb->T, total_rows, cfg.threshold, cfg.chunk, cls_cnt,
-                       reinterpret_cast<uint4*>(ws + L.long_list), reinterpret_cast<uint32_t*>(ws + L.long_table),
-                       reinterpret_cast<uint32_t*>(ws + L.long_count),
-                       reinterpret_cast<uint2*>(ws + L.chunk_list), L.cap_long, L.cap_chunk, lists);
-  }
-  return check_launch("classify");
+  return sort_route(tb, ws, M, L, n_eff, sentinel, cfg.threshold, cfg.chunk, lists, kMainNames, final_buf, s);
 }
 
 }  // namespace tbe

@@ -126,11 +126,18 @@ typedef struct {
                               lookups serves twice as many runs with half the lanes each (rows of
                               64 .. 256 columns); default 8, 0: off */
   int32_t dense_min;       /* backward without per-sample weights: per table (16 <= D <= 128,
-                              D % 16 == 0, not the histogram table), up to 128 long runs of at
-                              least this many lookups, in key order, are updated from per-bag
-                              counts x grad_out on MFMA instead of their chunks (default 2048;
+                              D % 16 == 0, not the histogram table), up to 128 rows of at least
+                              this many lookups, in key order, are updated from per-bag counts x
+                              grad_out on MFMA instead of through the sorted runs (default 2048;
                               values below long_threshold act as long_threshold; 0: off; off
                               with fused_long) */
+  int32_t dense_presort;   /* backward with dense_min: 1 = the dense rows are picked before the
+                              sort, from the lookups at 64 positions in every S (S the smallest
+                              power of two >= 64 that leaves at most 2^20 of them; every lookup
+                              up to 2^20 lookups) with dense_min scaled by 64 / S, so that rows
+                              near it may fall either way, and their lookups stay out of the
+                              sort; -1 = they are the long runs of >= dense_min lookups after
+                              the sort; 0 (default): 1 from 2^26 lookups on, else -1 */
 } tbe_config;
 
 /* Device-side view of the transpose, for inspection by tests (tbe_transpose). */
@@ -143,7 +150,8 @@ typedef struct {
                                       counters[13] */
   const int32_t* counters;         /* [16]: 0 runs, 1 long runs, 2 chunks, 3..11 short runs per
                                       bucket (next_pow2(D) = 4 .. 1024), 12 keys the sort covers
-                                      when a table is left out, 13 keys sorted */
+                                      when a table is left out, 13 keys sorted, 14 used by the
+                                      backward's dense rows (0 here) */
   const uint32_t* long_list;       /* [cap][4] {key, start, len, first chunk} per long run */
   const uint32_t* long_table;      /* [cap] table of each long run */
   const uint32_t* chunk_list;      /* [cap][2] {long-run slot, chunk number} per chunk */
@@ -274,10 +282,10 @@ size_t tbe_backward_workspace_bytes(const tbe_tables* tables, int64_t num_indice
  * table's rows take their gradient from per-bag lookup counts times grad_out
  * on MFMA (blog section 2, forward-state reuse) and its lookups stay out of the
  * sort; the other tables go through the sorted runs.  With dense_min > 0 and no
- * per-sample weights, each eligible table's hottest long runs (config
- * dense_min) take the same counts x grad_out route on bf16 MFMA with an exact
- * three-part split of the gradient; the step is the same up to the order of
- * the fp32 sums.
+ * per-sample weights, each eligible table's rows of at least dense_min lookups
+ * (up to 128 a table; see dense_presort for how they are counted) take the same
+ * counts x grad_out route on bf16 MFMA with an exact three-part split of the
+ * gradient; the step is the same up to the order of the fp32 sums.
  */
 tbe_status tbe_backward_sgd(const tbe_tables* tables, void* weights, const void* indices,
                             int32_t index_type, const void* offsets, int32_t offset_type,

@@ -112,6 +112,7 @@ def test_config_defaults():
     assert c.bwd_streams == 0  # 0: chosen from the tables' widths
     assert c.tiny_runs == 8    # short runs of <= 8 lookups: half the lanes per run
     assert c.dense_min == 2048  # long runs of >= 2048 lookups: dense counts x gradient
+    assert c.dense_presort == 0  # 0: picked before the sort from 2^26 lookups on
 
 
 def test_workspace_histogram_table_partials():

@@ -1,7 +1,8 @@
-"""Dense hot rows: per table, the long runs of at least dense_min lookups (up to 128, in key
-order) are updated from per-bag counts x grad_out on MFMA instead of their chunks.  The step
-equals the oracle's within the usual bounds, is bitwise repeatable, and is exact with integer
-gradients."""
+"""Dense hot rows: per table, the rows of at least dense_min lookups (up to 128, in key order)
+are updated from per-bag counts x grad_out on MFMA.  Picked before the sort (dense_presort = 1:
+counted on a sample, every lookup up to 2^20 lookups, and left out of the sorted runs) or from
+the long runs after it (-1: their chunks skipped).  The step equals the oracle's within the
+usual bounds, is bitwise repeatable, and is exact with integer gradients."""
 import numpy as np
 import pytest
 import torch
@@ -26,8 +27,11 @@ def _spec(D=(128, 64, 32, 200), E=(300, 1000, 400, 250), B=777, L=(60.0, 40.0, 3
                         pooling_hint=hint)
 
 
-def _cfg(dense_min, **kw):
-    return tbe.make_config(long_threshold=16, chunk=8, dense_min=dense_min, **kw)
+PRESORT = [1, -1]
+
+
+def _cfg(dense_min, presort=1, **kw):
+    return tbe.make_config(long_threshold=16, chunk=8, dense_min=dense_min, dense_presort=presort, **kw)
 
 
 def _long_lens(bt, threshold):
@@ -44,13 +48,14 @@ def _long_lens(bt, threshold):
 
 @pytest.mark.parametrize("w_dtype", [torch.float32, torch.float16, torch.bfloat16])
 @pytest.mark.parametrize("optimizer", ["sgd", "rowwise_adagrad"])
-def test_dense_rows_match_oracle(w_dtype, optimizer):
+@pytest.mark.parametrize("presort", PRESORT)
+def test_dense_rows_match_oracle(w_dtype, optimizer, presort):
     spec = _spec(w_dtype=w_dtype, optimizer=optimizer)
     bt = ti.make_batch(spec, 71)
     lens = _long_lens(bt, 48)
     assert sum(int((l >= 48).sum()) for l in lens[:3]) > 20   # the dense path has rows to take
-    flush_print(f"dense {w_dtype} {optimizer}")
-    run_and_check(bt, _cfg(48), what=f"dense {w_dtype} {optimizer}")
+    flush_print(f"dense {w_dtype} {optimizer} presort={presort}")
+    run_and_check(bt, _cfg(48, presort), what=f"dense {w_dtype} {optimizer} presort={presort}")
 
 
 @pytest.mark.parametrize("itype,otype", [(torch.int32, torch.int32), (torch.int64, torch.int32),
@@ -60,14 +65,15 @@ def test_dense_rows_index_types(itype, otype):
     run_and_check(bt, _cfg(32), what=f"dense {itype} {otype}")
 
 
-def test_dense_rows_change_the_summation_and_repeat():
+@pytest.mark.parametrize("presort", PRESORT)
+def test_dense_rows_change_the_summation_and_repeat(presort):
     """fp32 weights, Adagrad: the dense path sums the hot rows' gradients in another order than
     the chunks (other low bits, so it did run), and the same bits on every call."""
     bt = ti.make_batch(_spec(w_dtype=torch.float32), 75)
     outs = {}
     for dm in (0, 48, 48):
         db = DevBatch(bt)
-        W, mom = db.backward(_cfg(dm))
+        W, mom = db.backward(_cfg(dm, presort))
         torch.cuda.synchronize()
         outs.setdefault(dm, []).append((W.cpu(), mom.cpu()))
     (Wa, ma), (Wb, mb) = outs[48]
@@ -77,7 +83,8 @@ def test_dense_rows_change_the_summation_and_repeat():
 
 
 @pytest.mark.parametrize("dense_min", [16, 48])
-def test_dense_rows_exact_with_integer_gradients(dense_min):
+@pytest.mark.parametrize("presort", PRESORT)
+def test_dense_rows_exact_with_integer_gradients(dense_min, presort):
     """Gradients in {-1, 0, 1}, zero weights, SGD with lr = -1: every sum is an exact integer
     in fp32, so the dense path, the chunk path and the oracle agree bit for bit."""
     spec = _spec(w_dtype=torch.float32, optimizer="sgd", B=500)
@@ -88,7 +95,7 @@ def test_dense_rows_exact_with_integer_gradients(dense_min):
     outs = []
     for dm in (dense_min, 0):
         db = DevBatch(bt)
-        W, _ = db.backward(_cfg(dm), lr=-1.0)
+        W, _ = db.backward(_cfg(dm, presort), lr=-1.0)
         torch.cuda.synchronize()
         outs.append(W.cpu())
     assert torch.equal(outs[0].view(torch.int32), outs[1].view(torch.int32))
@@ -97,7 +104,8 @@ def test_dense_rows_exact_with_integer_gradients(dense_min):
     assert np.abs(r["g"]).max() > 20
 
 
-def test_dense_rows_more_than_128_per_table():
+@pytest.mark.parametrize("presort", PRESORT)
+def test_dense_rows_more_than_128_per_table(presort):
     """Every row of a 600-row table is hit about 120 times: the first 128 qualifying rows in key
     order take the dense path, the rest their chunks."""
     tables = (ti.TableSpec(600, 128, ("fixed", 100)), ti.TableSpec(3000, 64, ("poisson", 5.0, None, None)))
@@ -105,10 +113,11 @@ def test_dense_rows_more_than_128_per_table():
                         optimizer="rowwise_adagrad")
     bt = ti.make_batch(spec, 79)
     assert int((_long_lens(bt, 64)[0] >= 64).sum()) > 300
-    run_and_check(bt, _cfg(64), what="dense cap")
+    run_and_check(bt, _cfg(64, presort), what=f"dense cap presort={presort}")
 
 
-def test_dense_rows_with_histogram_table_and_bad_ids():
+@pytest.mark.parametrize("presort", PRESORT)
+def test_dense_rows_with_histogram_table_and_bad_ids(presort):
     """A histogram-eligible small table (its own MFMA path), dense rows in the others, and ids
     outside their tables (dropped by both paths)."""
     tables = (ti.TableSpec(64, 128, ("fixed", 100)),
@@ -125,7 +134,7 @@ def test_dense_rows_with_histogram_table_and_bad_ids():
     bt.indices = idx
     db = DevBatch(bt)
     assert db.tables.c.hist_table == 0
-    W, _ = db.backward(_cfg(32))
+    W, _ = db.backward(_cfg(32, presort))
     torch.cuda.synchronize()
     a = host_arrays(bt)
     keep = (~bad).double().numpy()
@@ -150,7 +159,8 @@ def test_dense_rows_off_with_per_sample_weights():
 
 
 @pytest.mark.parametrize("L", [300, 70000])
-def test_dense_rows_counts_above_255(L):
+@pytest.mark.parametrize("presort", PRESORT)
+def test_dense_rows_counts_above_255(L, presort):
     """Bags with hundreds (and tens of thousands) of lookups of one row: the counts go through
     the bf16 product byte by byte and stay exact (integer gradients, so bit for bit)."""
     tables = (ti.TableSpec(2, 64, ("fixed", L)), ti.TableSpec(500, 128, ("poisson", 8.0, None, None)))
@@ -161,22 +171,60 @@ def test_dense_rows_counts_above_255(L):
     bt.grad_out = torch.randint(-1, 2, bt.grad_out.shape, generator=g).float()
     bt.weights = torch.zeros_like(bt.weights)
     db = DevBatch(bt)
-    W, _ = db.backward(_cfg(16), lr=-1.0)
+    W, _ = db.backward(_cfg(16, presort), lr=-1.0)
     torch.cuda.synchronize()
     r = oracle_backward(bt, lr=-1.0)
     assert np.array_equal(W.cpu().double().numpy(), r["g"])
     assert np.abs(r["g"][:128]).max() > 255
 
 
-def test_dense_rows_on_the_second_stream():
+@pytest.mark.parametrize("presort", PRESORT)
+def test_dense_rows_on_the_second_stream(presort):
     """The dense rows, chunks and applies on the library's second stream, concurrent with the
     short runs: the same bits as on one stream."""
     bt = ti.make_batch(_spec(w_dtype=torch.float32), 89)
     outs = []
     for streams in (1, 2):
         db = DevBatch(bt)
-        W, mom = db.backward(_cfg(48, bwd_streams=streams))
+        W, mom = db.backward(_cfg(48, presort, bwd_streams=streams))
         torch.cuda.synchronize()
         outs.append((W.cpu(), mom.cpu()))
     assert torch.equal(outs[0][0].view(torch.int32), outs[1][0].view(torch.int32))
     assert torch.equal(outs[0][1], outs[1][1])
+
+
+def test_dense_rows_from_a_strided_sample():
+    """Over 2^20 lookups the rows are picked from 64 positions in every 128 (rows of about
+    dense_min lookups may fall either way): still the oracle's step, the same bits on every
+    call, and other low bits than without the dense path (so it did run)."""
+    tables = (ti.TableSpec(2000, 128, ("poisson", 40.0, None, None), ("zipf", 1.1, None)),
+              ti.TableSpec(5000, 64, ("poisson", 30.0, None, None), ("zipf", 1.05, None)),
+              ti.TableSpec(3000, 32, ("poisson", 20.0, None, None)))
+    spec = ti.BatchSpec("dense sampled", tables, B=16384, w_dtype=torch.float32, w_range=0.05,
+                        optimizer="rowwise_adagrad")
+    bt = ti.make_batch(spec, 93)
+    assert 2 ** 20 < bt.indices.numel() <= 2 ** 21
+    assert int((_long_lens(bt, 512)[0] >= 512).sum()) > 20
+    flush_print("dense sampled")
+    _, Wa, ma, _ = run_and_check(bt, _cfg(256), what="dense sampled")
+    db = DevBatch(bt)
+    Wb, mb = db.backward(_cfg(256))
+    db0 = DevBatch(bt)
+    W0, _ = db0.backward(_cfg(0))
+    torch.cuda.synchronize()
+    assert torch.equal(Wa.cpu().view(torch.int32), Wb.cpu().view(torch.int32))
+    assert torch.equal(ma.cpu(), mb.cpu())
+    assert not torch.equal(W0.cpu().view(torch.int32), Wa.cpu().view(torch.int32))
+
+
+def test_dense_rows_many_tables():
+    """40 tables: the dense-row key set (2 x 128 slots a table, rounded up to a power of two)
+    outgrows LDS, so linearize filters keys in LDS and probes the set in global memory."""
+    tables = tuple(ti.TableSpec(300 + 10 * t, (32, 64, 128)[t % 3], ("poisson", 20.0, None, None),
+                                ("zipf", 1.1, None)) for t in range(40))
+    spec = ti.BatchSpec("dense 40 tables", tables, B=300, w_dtype=torch.float16, w_range=0.05,
+                        optimizer="sgd")
+    bt = ti.make_batch(spec, 95)
+    assert sum(int((l >= 32).sum()) for l in _long_lens(bt, 32)) > 200
+    flush_print("dense 40 tables")
+    run_and_check(bt, _cfg(32), what="dense 40 tables")

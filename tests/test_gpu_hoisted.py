@@ -92,13 +92,15 @@ def test_hoisted_equals_plain(name, repair):
 
 
 @pytest.mark.parametrize("repair", [False, True])
-def test_hoisted_with_dense_rows(repair):
-    """The dense hot rows after the hoisted forward (fused repair or not): bitwise the plain
-    two calls, and the dense path really runs (fp32 weights: other low bits than the chunks)."""
+@pytest.mark.parametrize("presort", [1, -1])
+def test_hoisted_with_dense_rows(repair, presort):
+    """The dense hot rows after the hoisted forward (fused repair or not; picked before the
+    sort or from the long runs): bitwise the plain two calls, and the dense path really runs
+    (fp32 weights: other low bits than the chunks)."""
     spec = small_spec("skewed").replace(w_dtype=torch.float32)
     bt = ti.make_batch(spec, 91)
     idx, off = _inject(bt, 11, bad_offsets=repair)
-    kw = dict(long_threshold=32, chunk=16, dense_min=64)
+    kw = dict(long_threshold=32, chunk=16, dense_min=64, dense_presort=presort)
     plain = _step(bt, idx, off, hoisted=False, repair=repair, cfg_kw=kw)
     hoist = _step(bt, idx, off, hoisted=True, repair=repair, cfg_kw=kw)
     _assert_same(plain, hoist)
