@@ -112,9 +112,10 @@ def batch_stats(bt: ti.Batch, hist_table: int, threshold=256, chunk=256, dense_m
                 dense_rows=128):
     """Host-side statistics of the drawn batch (from the inputs only), per table.  hist_table
     (or -1): the table whose backward goes through the histogram kernels, not the runs.  The
-    dense hot rows are picked as the library does: per eligible table (no per-sample weights,
-    16 <= D <= 128, D % 16 == 0, not the histogram table), its long runs of at least dense_min
-    lookups in key order, at most dense_rows of them (dense_min 0: none)."""
+    dense hot rows are picked as the library does after the sort: per eligible table (no
+    per-sample weights, 16 <= D <= 128, D % 16 == 0, not the histogram table), its long runs of
+    at least dense_min lookups in key order, at most dense_rows of them (dense_min 0: none).
+    The library's pre-sort pick counts a sample instead, so rows near dense_min may differ."""
     idx = bt.indices.cpu().numpy().astype(np.int64)
     off = bt.offsets.cpu().numpy().astype(np.int64)
     B = bt.B
@@ -148,11 +149,31 @@ def batch_stats(bt: ti.Batch, hist_table: int, threshold=256, chunk=256, dense_m
                 chunks=tot("chunks", True), per_table=per)
 
 
-def algorithmic_bytes(bt: ti.Batch, st: dict, hoist: bool, dense_P: int = 24):
+def presort_sample(N: int):
+    """The pre-sort pick of the dense rows (the library's automatic choice, from 2^26 lookups on):
+    (on, sampled keys).  The sample is 64 positions in every S, S the smallest power of two >= 64
+    that leaves at most 2^20 of them."""
+    if N < 2 ** 26:
+        return False, 0
+    S = 64
+    while 64 * -(-N // S) > 2 ** 20:
+        S *= 2
+    return True, 64 * -(-N // S)
+
+
+def radix_passes(total_rows: int):
+    """Radix passes over keys in [0, total_rows] at up to 9 bits a pass."""
+    return -(-max(1, int(total_rows).bit_length()) // 9)
+
+
+def algorithmic_bytes(bt: ti.Batch, st: dict, hoist: bool, dense_P: int = 24, presort: bool = False,
+                      sample_keys: int = 0):
     """What each kernel must move per launch (no credit for cache reuse), summed over tables
     with their own D.  hoist: the histogram forward keeps each bag's counts (64 u16) and the
     histogram backward reads them and only the ids past a bag's first 256.  dense_P: the dense
-    path's partials per table."""
+    path's partials per table.  presort: the dense rows are picked before the sort from
+    sample_keys sampled lookups, and their lookups leave the sort after its first pass (radix
+    figures are then averages over the passes)."""
     s_w = bt.weights.element_size()
     s_i = bt.indices.element_size()
     s_o = bt.offsets.element_size()
@@ -163,14 +184,20 @@ def algorithmic_bytes(bt: ti.Batch, st: dict, hoist: bool, dense_P: int = 24):
     hst = [p for p in per if p["hist"]]
     runs_N = sum(p["N"] for p in gen)              # keys the sort covers
     U = sum(p["U"] for p in gen)
+    passes = radix_passes(sum(bt.E))
+    kept, U_kept = runs_N, U                       # keys and runs past the first radix pass
+    if presort:
+        kept -= sum(p["dense_lookups"] for p in gen)
+        U_kept -= sum(p["dense_rows"] for p in gen)
     by = {
         # per lookup: index (+ weight) + row; per bag: offset + output row
         "fwd_gather": sum(p["N"] * (s_i + s_p + p["D"] * s_w) + B * (s_o + p["D"] * 4) for p in gen),
         # per lookup: index read, key + payload written; per bag: offset
         "linearize": st["N"] * s_i + runs_N * 8 + st["TB"] * s_o,
-        # per pass: keys + payloads read and written
-        "radix_downsweep": runs_N * 16,
-        "radix_upsweep": runs_N * 4,
+        # per pass: keys + payloads read and written (the first pass writes only the kept keys,
+        # later passes see only those)
+        "radix_downsweep": (runs_N * 8 + kept * 8 + (passes - 1) * kept * 16) / passes,
+        "radix_upsweep": (runs_N + (passes - 1) * kept) * 4 / passes,
         # per lookup of a short run: payload (+ weight) + fp32 gradient row; per short run:
         # descriptor, weight row read + write, Adagrad state read + write
         "short_run": sum(p["short_lookups"] * (4 + s_p + p["D"] * 4)
@@ -190,9 +217,18 @@ def algorithmic_bytes(bt: ti.Batch, st: dict, hoist: bool, dense_P: int = 24):
         "dense_apply": sum(p["dense_rows"] * (dense_P * p["D"] * 4 + 2 * p["D"] * s_w + 8) for p in gen),
         "bounds_indices": st["N"] * s_i,
         "bounds_offsets": 3 * (st["TB"] + 1) * s_o,
-        "rle": 3 * runs_N * 4 + U * 8,
-        "classify": U * 8 + U * 16,
+        "rle": 3 * kept * 4 + U_kept * 8,
+        "classify": U_kept * 8 + U_kept * 16,
     }
+    if presort:
+        # ids read and keys + payloads written at the sampled positions, the sample's own sort
+        # (keys + payloads read and written per pass, keys counted) and run-length encoding,
+        # the dense rows' key set (4 x 128 slots a table, a power of two) and 8 KB filter filled
+        slots = 1024
+        while slots < 4 * 128 * bt.T:
+            slots *= 2
+        by["dense_sample"] = sample_keys * (s_i + 8) + passes * sample_keys * 20 + 3 * sample_keys * 4 \
+            + slots * 4 + 8192
     for p in hst:
         # per lookup: index; per bag: offset + output (forward) or gradient (backward) row
         by["fwd_hist"] = p["N"] * s_i + B * (s_o + p["D"] * 4) + 64 * p["D"] * s_w
@@ -405,7 +441,8 @@ def main():
     # launches one round of them over the tables
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     dense_P = max(1, min(64, 2048 // bt.T, (bt.B + 63) // 64, cus * 3 // bt.T))
-    ab = algorithmic_bytes(bt, st, args.hoist == "on", dense_P)
+    presort, sample_keys = presort_sample(N) if bt.psw is None else (False, 0)
+    ab = algorithmic_bytes(bt, st, args.hoist == "on", dense_P, presort, sample_keys)
     dom_avg_ms = dom_ms / max(launches, 1)
     dom_bytes = ab.get(dominant, 0)
     achieved = dom_bytes / (dom_avg_ms * 1e-3) / 1e9 if dom_avg_ms > 0 else 0.0

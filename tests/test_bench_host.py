@@ -92,3 +92,25 @@ def test_mfma_flops():
     # x 128 columns, three bf16 parts
     nd = st["per_table"][1]["dense_rows"]
     assert nd >= 1 and fl["dense_partial"] == (5 * ((nd + 15) // 16) * 16 * 64 * 128 * 2 * 3, "bf16")
+
+
+def test_presort_sample_and_bytes():
+    """The pre-sort pick: from 2^26 lookups on, at most 2^20 sampled keys (64 in every power of
+    two S); the dense rows' lookups leave the radix passes after the first, and the runs."""
+    assert bench.presort_sample(2 ** 26 - 1) == (False, 0)
+    on, k = bench.presort_sample(83_897_668)
+    assert on and k == 64 * -(-83_897_668 // 8192) and k <= 2 ** 20
+    assert bench.radix_passes(64_000_000) == 3 and bench.radix_passes(511) == 1
+    tables = (ti.TableSpec(300, 128, ("fixed", 40)), ti.TableSpec(64, 64, ("fixed", 40)))
+    bt = ti.make_batch(ti.BatchSpec("presort bytes", tables, B=1000, w_dtype=torch.float16,
+                                    w_range=0.05), 7, device="cpu")
+    st = bench.batch_stats(bt, hist_table=-1, threshold=64, chunk=64, dense_min=100)
+    plain = bench.algorithmic_bytes(bt, st, hoist=False)
+    pre = bench.algorithmic_bytes(bt, st, hoist=False, presort=True, sample_keys=4096)
+    N = st["N"]
+    dl = sum(p["dense_lookups"] for p in st["per_table"])
+    kept = N - dl
+    assert dl > 0 and plain["radix_downsweep"] == N * 16     # 364 rows: one pass
+    assert pre["radix_downsweep"] == N * 8 + kept * 8 and pre["radix_upsweep"] == N * 4
+    assert pre["rle"] == 3 * kept * 4 + (st["U"] - 128 - 64) * 8
+    assert pre["linearize"] == plain["linearize"] and "dense_sample" in pre
