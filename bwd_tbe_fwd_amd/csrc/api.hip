@@ -263,6 +263,8 @@ BwdLayout bwd_layout(const tbe_tables* tb, int64_t N, int weighted, const Config
     while (hs < 4 * static_cast<int64_t>(kDenseRows) * tb->T) hs <<= 1;
     L.hot_set_size = hs;
     L.hot_set = c.take(static_cast<size_t>(hs) * 4);
+    L.hot_rank = c.take(static_cast<size_t>(hs));
+    L.dense_slot = c.take(static_cast<size_t>(n1));
     L.hot_bloom = c.take(static_cast<size_t>(kHotBloomWords) * 4);
   }
   L.counters = c.take(kNumCounters * 4);

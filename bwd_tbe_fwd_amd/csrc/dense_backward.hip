@@ -97,16 +97,16 @@ __global__ __launch_bounds__(kBlock) void dense_sample_kernel(
 
 // One wave per table: the table's long runs (long-list slots [lo, hi), in key order) of at
 // least min_len lookups become its dense rows, at most kDenseRows, in ascending order.
-// Picked from the sorted sample (hot_set != NULL): their keys go into the key set (linear
-// probing; the most slot groups a lookup reads into *probe_max) and its filter.  Picked from
+// Picked from the sorted sample (hot_set != NULL): their keys and ranks go into the key set
+// (linear probing; the most slot groups a lookup reads into *probe_max) and its filter.  Picked from
 // the batch's own runs (long_flag != NULL): each slot's flag says whether the chunk and apply
 // kernels leave it to the dense path.
 __global__ __launch_bounds__(kBlock) void dense_select_kernel(
     const uint4* __restrict__ long_list, const uint32_t* __restrict__ long_table,
     const int32_t* __restrict__ counters, int64_t cap_long, const int64_t* __restrict__ meta, int T,
     int hist_t, uint32_t min_len, int32_t* __restrict__ dense_rows, int32_t* __restrict__ dense_cnt,
-    uint32_t* __restrict__ long_flag, uint32_t* __restrict__ hot_set, uint32_t hot_mask,
-    uint32_t* __restrict__ hot_filter, int32_t* __restrict__ probe_max) {
+    uint32_t* __restrict__ long_flag, uint32_t* __restrict__ hot_set, uint8_t* __restrict__ hot_rank,
+    uint32_t hot_mask, uint32_t* __restrict__ hot_filter, int32_t* __restrict__ probe_max) {
   const int lane = lane_id();
   const int t = static_cast<int>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -139,7 +139,9 @@ __global__ __launch_bounds__(kBlock) void dense_select_kernel(
       const uint32_t h = hot_slot(key, hot_mask);
       int i = 0;  // the set holds 4 slots per possible key: a free slot is always found
       while (true) {
-        const uint32_t prev = atomicCAS(&hot_set[(h + i) & hot_mask], kHotEmpty, key);
+        const uint32_t e = (h + i) & hot_mask;
+        const uint32_t prev = atomicCAS(&hot_set[e], kHotEmpty, key);
+        if (prev == kHotEmpty) hot_rank[e] = static_cast<uint8_t>(rank);
         if (prev == kHotEmpty || prev == key) break;
         ++i;
       }
@@ -204,12 +206,14 @@ __device__ __forceinline__ int32_t wave_offsets(const OT* __restrict__ offsets, 
 // and only the fp32 accumulation rounds, as in the fp32 sums of the chunk path.  A step's
 // gradient rows and ids are requested together, and the next step's offsets before this
 // step's counting, so a step waits on memory about once.
-template <typename IT, typename OT>
+// SLOTS: each lookup's row rank comes from dense_slot (one byte a position, written by
+// linearize with the pre-sort pick) instead of its id, the filter and the search.
+template <typename IT, typename OT, bool SLOTS>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void dense_partial_kernel(
     const IT* __restrict__ indices, const OT* __restrict__ offsets, const float* __restrict__ grad_out,
     const int64_t* __restrict__ meta, int32_t B, int32_t out_width, int64_t N, int P,
     const int32_t* __restrict__ dense_rows, const int32_t* __restrict__ dense_cnt,
-    float* __restrict__ partial) {
+    const uint8_t* __restrict__ dense_slot, float* __restrict__ partial) {
   constexpr int kStride = kDnBags + 4;   // counts [row][bag]; rows padded against bank conflicts
   constexpr int kBloomWords = 1024;      // 32768-bit filter of the selected rows (id mod 32768)
   // counts as fp32 (exact integers below 2^24): a count below 256 is then its own bf16 value
@@ -297,7 +301,29 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     __builtin_amdgcn_wave_barrier();
     // every lookup of the wave's 16 bags that hits a selected row
     bool big = false;
-    for (int32_t j0 = 0; j0 < n; j0 += kDnLoads * kWave) {
+    if constexpr (SLOTS) {
+      for (int32_t j0 = 0; j0 < n; j0 += kDnLoads * kWave) {
+        uint32_t sl[kDnLoads];
+#pragma unroll
+        for (int u = 0; u < kDnLoads; ++u) {
+          const int32_t j = j0 + u * kWave + lane;
+          sl[u] = j < n ? dense_slot[o0 + j] : kNoDenseSlot;
+        }
+#pragma unroll
+        for (int u = 0; u < kDnLoads; ++u) {
+          if (j0 + u * kWave >= n) break;  // uniform: no lane has a lookup left
+          const int32_t j = j0 + u * kWave + lane;
+          if (sl[u] < static_cast<uint32_t>(nd)) {
+            int b = 0;  // the bag of lookup j
+#pragma unroll
+            for (int step = 8; step > 0; step >>= 1)
+              if (off[b + step] <= j) b += step;
+            big |= atomicAdd(&s_cnt[sl[u] * kStride + kDnWaveBags * w + b], 1.f) >= 255.f;
+          }
+        }
+      }
+    }
+    for (int32_t j0 = 0; !SLOTS && j0 < n; j0 += kDnLoads * kWave) {
       int64_t r[kDnLoads];
 #pragma unroll
       for (int u = 0; u < kDnLoads; ++u) {
@@ -465,12 +491,21 @@ template <typename IT, typename OT>
 tbe_status partial_go(const tbe_tables* tb, const IndexArgs& ia, const float* grad_out, char* ws,
                       const BwdLayout& L, int P, hipStream_t s) {
   ProfScope ps("dense_partial", s);
-  hipLaunchKernelGGL((dense_partial_kernel<IT, OT>), dim3(tb->T * P), dim3(kBlock), 0, s,
-                     static_cast<const IT*>(ia.indices), static_cast<const OT*>(ia.offsets), grad_out,
-                     tb->meta, tb->B, tb->out_width, ia.N, P,
-                     reinterpret_cast<const int32_t*>(ws + L.dense_rows),
-                     reinterpret_cast<const int32_t*>(ws + L.dense_cnt),
-                     reinterpret_cast<float*>(ws + L.dense_partial));
+  const uint8_t* slot = L.dense_presort ? reinterpret_cast<const uint8_t*>(ws + L.dense_slot) : nullptr;
+  if (slot)
+    hipLaunchKernelGGL((dense_partial_kernel<IT, OT, true>), dim3(tb->T * P), dim3(kBlock), 0, s,
+                       static_cast<const IT*>(ia.indices), static_cast<const OT*>(ia.offsets), grad_out,
+                       tb->meta, tb->B, tb->out_width, ia.N, P,
+                       reinterpret_cast<const int32_t*>(ws + L.dense_rows),
+                       reinterpret_cast<const int32_t*>(ws + L.dense_cnt), slot,
+                       reinterpret_cast<float*>(ws + L.dense_partial));
+  else
+    hipLaunchKernelGGL((dense_partial_kernel<IT, OT, false>), dim3(tb->T * P), dim3(kBlock), 0, s,
+                       static_cast<const IT*>(ia.indices), static_cast<const OT*>(ia.offsets), grad_out,
+                       tb->meta, tb->B, tb->out_width, ia.N, P,
+                       reinterpret_cast<const int32_t*>(ws + L.dense_rows),
+                       reinterpret_cast<const int32_t*>(ws + L.dense_cnt), nullptr,
+                       reinterpret_cast<float*>(ws + L.dense_partial));
   return check_launch("dense_partial");
 }
 
@@ -521,7 +556,8 @@ tbe_status launch_dense_select(const tbe_tables* tb, char* ws, const BwdLayout& 
                      reinterpret_cast<const uint32_t*>(ws + P.long_table),
                      reinterpret_cast<const int32_t*>(ws + P.counters), P.cap_long, tb->meta, tb->T, hist_t, 0u,
                      reinterpret_cast<int32_t*>(ws + L.dense_rows), reinterpret_cast<int32_t*>(ws + L.dense_cnt),
-                     nullptr, reinterpret_cast<uint32_t*>(ws + L.hot_set), static_cast<uint32_t>(L.hot_set_size - 1),
+                     nullptr, reinterpret_cast<uint32_t*>(ws + L.hot_set), reinterpret_cast<uint8_t*>(ws + L.hot_rank),
+                     static_cast<uint32_t>(L.hot_set_size - 1),
                      reinterpret_cast<uint32_t*>(ws + L.hot_bloom),
                      reinterpret_cast<int32_t*>(ws + L.counters) + kHotProbe);
   return check_launch("dense_select");
@@ -536,7 +572,7 @@ tbe_status launch_dense_select_runs(const tbe_tables* tb, char* ws, const BwdLay
                      reinterpret_cast<const int32_t*>(ws + L.counters), L.cap_long, tb->meta, tb->T, hist_t,
                      static_cast<uint32_t>(cfg.dense_min), reinterpret_cast<int32_t*>(ws + L.dense_rows),
                      reinterpret_cast<int32_t*>(ws + L.dense_cnt), reinterpret_cast<uint32_t*>(ws + L.long_flag),
-                     nullptr, 0u, nullptr, nullptr);
+                     nullptr, nullptr, 0u, nullptr, nullptr);
   return check_launch("dense_select");
 }
 
@@ -546,7 +582,7 @@ tbe_status launch_dense_backward(const tbe_tables* tb, void* W, float* momentum,
   // partials per table: as many workgroups as the GPU holds at once over all tables (one
   // round, no tail), at most the workspace's dense_P
   const int64_t resident = static_cast<int64_t>(device_cu_count()) *
-                           blocks_per_cu(reinterpret_cast<const void*>(dense_partial_kernel<int64_t, int64_t>));
+                           blocks_per_cu(reinterpret_cast<const void*>(dense_partial_kernel<int64_t, int64_t, false>));
   const int P = static_cast<int>(hmax(1, hmin(L.dense_P, resident / tb->T)));
   tbe_status st;
   if (ia.itype == TBE_I32)

@@ -201,11 +201,14 @@ __device__ __forceinline__ int table_of_key(const int64_t* __restrict__ meta, in
 }
 
 // The key set of the dense rows: open addressing with linear probing over a power-of-two
-// array of keys (kHotEmpty marks a free slot) that starts at a 16-byte group of four
-// slots, so that a lookup reads whole groups (one, nearly always) and stops at the first
-// group with a free slot; and a 65536-bit filter that most other keys fail.  Both hashes
-// are multiplicative (Knuth's golden-ratio constant and a second odd multiplier).
+// array of keys (kHotEmpty marks a free slot), with a byte array beside it holding each
+// key's rank among its table's dense rows.  Probing starts at a 16-byte group of four
+// slots (and the matching 4 bytes of ranks), so that a lookup reads whole groups (one,
+// nearly always) and stops at the first group with a free slot; a 65536-bit filter turns
+// most other keys away first.  Both hashes are
+// multiplicative (Knuth's golden-ratio constant and a second odd multiplier).
 constexpr uint32_t kHotEmpty = 0xffffffffu;
+constexpr uint8_t kNoDenseSlot = 0xff;  // a lookup that no dense row takes
 __device__ __forceinline__ uint32_t hot_slot(uint32_t key, uint32_t mask) {
   const uint32_t h = key * 0x9e3779b1u;
   return ((h ^ (h >> 15)) << 2) & mask;  // first slot of a group
