@@ -108,14 +108,15 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def batch_stats(bt: ti.Batch, hist_table: int, threshold=256, chunk=256, dense_min=2048,
+def batch_stats(bt: ti.Batch, hist_table: int, threshold=256, chunk=256, dense_min=1024,
                 dense_rows=128):
     """Host-side statistics of the drawn batch (from the inputs only), per table.  hist_table
     (or -1): the table whose backward goes through the histogram kernels, not the runs.  The
     dense hot rows are picked as the library does after the sort: per eligible table (no
     per-sample weights, 16 <= D <= 128, D % 16 == 0, not the histogram table), its long runs of
-    at least dense_min lookups in key order, at most dense_rows of them (dense_min 0: none).
-    The library's pre-sort pick counts a sample instead, so rows near dense_min may differ."""
+    at least dense_min lookups, the dense_rows longest when more qualify (among equal lengths
+    the smaller keys; dense_min 0: none).  The library's pre-sort pick counts a sample
+    instead, so rows near the cut may differ."""
     idx = bt.indices.cpu().numpy().astype(np.int64)
     off = bt.offsets.cpu().numpy().astype(np.int64)
     B = bt.B
@@ -129,10 +130,12 @@ def batch_stats(bt: ti.Batch, hist_table: int, threshold=256, chunk=256, dense_m
         lens = np.diff(off[t * B:(t + 1) * B + 1])
         D = bt.D[t]
         ok = (dmin > 0 and bt.psw is None and 16 <= D <= 128 and D % 16 == 0 and t != hist_table)
-        dl = c[lg][c[lg] >= dmin][:dense_rows] if ok else c[:0]   # c is in key order
+        cand = np.flatnonzero(lg & (c >= dmin)) if ok else np.zeros(0, dtype=np.int64)  # key order
+        if cand.size > dense_rows:   # the longest; among equal lengths the smaller keys
+            cand = np.sort(cand[np.lexsort((cand, -c[cand]))[:dense_rows]])
+        dl = c[cand]
         dn = np.zeros(c.size, dtype=bool)
-        if dl.size:
-            dn[np.flatnonzero(lg)[np.flatnonzero(c[lg] >= dmin)[:dense_rows]]] = True
+        dn[cand] = True
         gl = lg & ~dn                                                # long runs left to the chunks
         per.append(dict(D=D, N=int(lk.size), U=int(c.size), hottest=int(c.max()) if c.size else 0,
                         tail=int(np.maximum(lens - 256, 0).sum()),   # lookups past a bag's first 256

@@ -361,7 +361,7 @@ void tbe_config_default(tbe_config* cfg) {
   cfg->bags_per_wave = 0;
   cfg->bwd_streams = 0;
   cfg->tiny_runs = 8;
-  cfg->dense_min = 2048;
+  cfg->dense_min = 1024;
   cfg->dense_presort = 0;
 }
 

@@ -14,8 +14,8 @@
 // gradient traffic.
 //
 // gfx950 mapping.  dense_select (one wave per table) takes a table's long runs
-// in key order, up to kDenseRows of them, and records their row ids
-// (ascending).  In large batches the rows are picked before the sort, from a
+// of at least dense_min lookups (the kDenseRows longest when more qualify) and
+// records their row ids (ascending).  In large batches the rows are picked before the sort, from a
 // sample of the lookups: dense_sample writes the keys of 64 positions out of
 // every hot_stride, which are sorted and run-length encoded on their own, the
 // runs that reach dense_min scaled to the sample are taken, and their keys go
@@ -96,7 +96,8 @@ __global__ __launch_bounds__(kBlock) void dense_sample_kernel(
 }
 
 // One wave per table: the table's long runs (long-list slots [lo, hi), in key order) of at
-// least min_len lookups become its dense rows, at most kDenseRows, in ascending order.
+// least min_len lookups become its dense rows, in ascending order; when more than kDenseRows
+// qualify, the kDenseRows longest (among equal lengths, the smaller keys).
 // Picked from the sorted sample (hot_set != NULL): their keys and ranks go into the key set
 // (linear probing; the most slot groups a lookup reads into *probe_max) and its filter.  Picked from
 // the batch's own runs (long_flag != NULL): each slot's flag says whether the chunk and apply
@@ -123,12 +124,47 @@ __global__ __launch_bounds__(kBlock) void dense_select_kernel(
   const int64_t s0 = lower(static_cast<uint32_t>(t)), s1 = lower(static_cast<uint32_t>(t) + 1);
   const TableMeta m = load_meta(meta, t);
   const bool ok = dense_table_ok(static_cast<int>(m.D), t, hist_t);
+  const uint32_t* len_of = reinterpret_cast<const uint32_t*>(long_list) + 2;  // len_of[4 s]
+  // runs of at least v lookups (and the longest run)
+  auto count_ge = [&](uint32_t v, uint32_t* longest) {
+    int64_t c = 0;
+    uint32_t mx = 0;
+    for (int64_t s = s0 + lane; s - lane < s1; s += kWave) {
+      const uint32_t len = s < s1 ? len_of[4 * s] : 0u;
+      c += __popcll(__ballot(len >= v && len > 0));
+      mx = max(mx, len);
+    }
+    if (longest) {
+      for (int d = 1; d < kWave; d <<= 1) mx = max(mx, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mx), d)));
+      *longest = mx;
+    }
+    return c;
+  };
+  // kept: every run longer than tau, and the first `quota` runs of exactly tau lookups
+  uint32_t tau = max(min_len, 1u);
+  int64_t quota = int64_t{1} << 40;
+  if (ok) {
+    uint32_t hi;
+    if (count_ge(tau, &hi) > kDenseRows) {
+      uint32_t lo = tau;  // the largest v with at least kDenseRows runs of >= v lookups
+      while (lo < hi) {
+        const uint32_t mid = lo + (hi - lo + 1) / 2;
+        if (count_ge(mid, nullptr) >= kDenseRows) lo = mid; else hi = mid - 1;
+      }
+      tau = lo;
+      quota = kDenseRows - count_ge(tau + 1, nullptr);
+    }
+  }
   int taken = 0;
+  int64_t eq_seen = 0;  // runs of exactly tau lookups before this step
   for (int64_t s = s0 + lane; s - lane < s1; s += kWave) {
     const bool in = s < s1;
     uint4 L = make_uint4(0u, 0u, 0u, 0u);
     if (in) L = long_list[s];
-    const bool want = in && ok && L.z >= min_len;
+    const bool eq = in && L.z == tau;
+    const uint64_t em = __ballot(eq);
+    const bool want = in && ok && (L.z > tau || (eq && eq_seen + __popcll(em & lanemask_lt()) < quota));
+    eq_seen += __popcll(em);
     const uint64_t wm = __ballot(want);
     const int rank = taken + __popcll(wm & lanemask_lt());
     const bool take = want && rank < kDenseRows;

@@ -126,17 +126,18 @@ typedef struct {
                               lookups serves twice as many runs with half the lanes each (rows of
                               64 .. 256 columns); default 8, 0: off */
   int32_t dense_min;       /* backward without per-sample weights: per table (16 <= D <= 128,
-                              D % 16 == 0, not the histogram table), up to 128 rows of at least
-                              this many lookups, in key order, are updated from per-bag counts x
-                              grad_out on MFMA instead of through the sorted runs (default 2048;
+                              D % 16 == 0, not the histogram table), its rows of at least this
+                              many lookups (the 128 with the most when more qualify; among equal
+                              counts the smaller row ids) are updated from per-bag counts x
+                              grad_out on MFMA instead of through the sorted runs (default 1024;
                               values below long_threshold act as long_threshold; 0: off; off
                               with fused_long) */
   int32_t dense_presort;   /* backward with dense_min: 1 = the dense rows are picked before the
                               sort, from the lookups at 64 positions in every S (S the smallest
                               power of two >= 64 that leaves at most 2^20 of them; every lookup
                               up to 2^20 lookups) with dense_min scaled by 64 / S, so that rows
-                              near it may fall either way, and their lookups stay out of the
-                              sort; -1 = they are the long runs of >= dense_min lookups after
+                              near the cut may fall either way, and their lookups stay out of
+                              the sort; -1 = they are the long runs of >= dense_min lookups after
                               the sort; 0 (default): 1 from 2^26 lookups on, else -1 */
 } tbe_config;
 

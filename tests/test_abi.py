@@ -111,7 +111,7 @@ def test_config_defaults():
     assert c.pretransposed == 0 and c.bags_per_wave == 0  # 0: chosen from the batch shape
     assert c.bwd_streams == 0  # 0: chosen from the tables' widths
     assert c.tiny_runs == 8    # short runs of <= 8 lookups: half the lanes per run
-    assert c.dense_min == 2048  # long runs of >= 2048 lookups: dense counts x gradient
+    assert c.dense_min == 1024  # rows of >= 1024 lookups (the 128 longest): dense counts x gradient
     assert c.dense_presort == 0  # 0: picked before the sort from 2^26 lookups on
 
 

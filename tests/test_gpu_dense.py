@@ -106,8 +106,8 @@ def test_dense_rows_exact_with_integer_gradients(dense_min, presort):
 
 @pytest.mark.parametrize("presort", PRESORT)
 def test_dense_rows_more_than_128_per_table(presort):
-    """Every row of a 600-row table is hit about 120 times: the first 128 qualifying rows in key
-    order take the dense path, the rest their chunks."""
+    """Every row of a 600-row table is hit about 120 times: the 128 with the most lookups take
+    the dense path, the rest their chunks."""
     tables = (ti.TableSpec(600, 128, ("fixed", 100)), ti.TableSpec(3000, 64, ("poisson", 5.0, None, None)))
     spec = ti.BatchSpec("dense cap", tables, B=720, w_dtype=torch.float32, w_range=0.05,
                         optimizer="rowwise_adagrad")
@@ -228,3 +228,27 @@ def test_dense_rows_many_tables():
     assert sum(int((l >= 32).sum()) for l in _long_lens(bt, 32)) > 200
     flush_print("dense 40 tables")
     run_and_check(bt, _cfg(32), what="dense 40 tables")
+
+
+@pytest.mark.parametrize("presort", PRESORT)
+def test_dense_rows_are_the_longest_128(presort):
+    """More than 128 rows qualify: the dense path takes the 128 with the most lookups (among
+    equal counts the smaller row ids).  fp32 weights: a row the dense path updates ends with
+    other low bits than on the chunk path (almost always), so the rows whose bits differ must
+    lie in that set, and most of it must show."""
+    tables = (ti.TableSpec(600, 64, ("fixed", 100)),)
+    spec = ti.BatchSpec("dense top 128", tables, B=720, w_dtype=torch.float32, w_range=0.05,
+                        optimizer="sgd")
+    bt = ti.make_batch(spec, 97)
+    c = np.bincount(bt.indices.numpy().astype(np.int64), minlength=600)
+    q = np.flatnonzero(c >= 64)
+    assert q.size > 200
+    top = set(sorted(q.tolist(), key=lambda r: (-int(c[r]), r))[:128])
+    outs = []
+    for dm in (64, 0):
+        db = DevBatch(bt)
+        W, _ = db.backward(_cfg(dm, presort))
+        torch.cuda.synchronize()
+        outs.append(W.cpu().view(600, 64).view(torch.int32))
+    differ = set(torch.nonzero((outs[0] != outs[1]).any(dim=1)).flatten().tolist())
+    assert differ <= top and len(differ) >= 100, (len(differ), sorted(differ - top)[:5])
