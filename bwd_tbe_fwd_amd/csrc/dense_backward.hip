@@ -258,7 +258,6 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   __shared__ uint32_t s_bloom[kBloomWords];
   __shared__ int32_t s_rows[kDenseRows];
   __shared__ int32_t s_off[kWavesPerBlock][kDnWaveBags + 1];
-  __shared__ uint32_t s_big;
   const int t = static_cast<int>(blockIdx.x) / P, p = static_cast<int>(blockIdx.x) % P;
   const int nd = dense_cnt[t];
   if (nd == 0) return;  // uniform over the workgroup
@@ -328,7 +327,6 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
       o_next = wave_offsets(offsets, bag0, bw, nbw, B, N);
     }
     __syncthreads();  // every wave is done with the previous step's counts (and the filter is set)
-    if (threadIdx.x == 0) s_big = 0u;
     if (lane <= kDnWaveBags) off[lane] = o - o0;
     // this wave's 16 bag columns of every row
 #pragma unroll
@@ -336,7 +334,6 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
       *reinterpret_cast<f32x4*>(&s_cnt[(x >> 2) * kStride + kDnWaveBags * w + 4 * (x & 3)]) = f32x4{0.f, 0.f, 0.f, 0.f};
     __builtin_amdgcn_wave_barrier();
     // every lookup of the wave's 16 bags that hits a selected row
-    bool big = false;
     if constexpr (SLOTS) {
       for (int32_t j0 = 0; j0 < n; j0 += kDnLoads * kWave) {
         uint32_t sl[kDnLoads];
@@ -354,7 +351,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
 #pragma unroll
             for (int step = 8; step > 0; step >>= 1)
               if (off[b + step] <= j) b += step;
-            big |= atomicAdd(&s_cnt[sl[u] * kStride + kDnWaveBags * w + b], 1.f) >= 255.f;
+            atomicAdd(&s_cnt[sl[u] * kStride + kDnWaveBags * w + b], 1.f);
           }
         }
       }
@@ -383,15 +380,17 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
 #pragma unroll
               for (int step = 8; step > 0; step >>= 1)
                 if (off[b + step] <= j) b += step;
-              big |= atomicAdd(&s_cnt[k * kStride + kDnWaveBags * w + b], 1.f) >= 255.f;
+              atomicAdd(&s_cnt[k * kStride + kDnWaveBags * w + b], 1.f);
             }
           }
         }
       }
     }
-    if (__ballot(big)) s_big = 1u;
     __syncthreads();  // all 64 bags counted
-    const bool any_big = __builtin_amdgcn_readfirstlane(s_big) != 0u;
+    // a count can reach 256 only in a bag of at least 256 lookups: lane l checks bag l % 16
+    // of wave l / 16 (bags past the last have no lookups)
+    const bool any_big =
+        __ballot(s_off[lane >> 4][(lane & 15) + 1] - s_off[lane >> 4][lane & 15] >= 256) != 0;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       s16x8 bh[2], bm[2], bl[2];
