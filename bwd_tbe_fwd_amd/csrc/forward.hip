@@ -84,8 +84,15 @@ __device__ __forceinline__ void pool_bag(const typename Fmt<DT>::S* __restrict__
   }
 }
 
+// fp16 / bf16 tables without per-sample weights, up to 4 rows in flight, are held to at
+// least 6 waves per SIMD (80 registers): the kernel is bound by its row-load latency, and the
+// fused id check's instantiation otherwise takes 82 registers and 5 waves (skewed batch:
+// 2.66 -> 2.49 ms).  With per-sample weights, fp32 tables (fp64 sums) or 8 rows in flight
+// the bound would spill.
 template <int DT, typename IT, typename OT, bool PSW, int VEC, typename ACC, int UNROLL, bool REPAIR>
-__global__ __launch_bounds__(kBlock) void fwd_gather_kernel(
+__global__ __launch_bounds__(kBlock)
+__attribute__((amdgpu_waves_per_eu((PSW || DT == 0 || UNROLL > 4) ? 1 : 6)))
+void fwd_gather_kernel(
     const typename Fmt<DT>::S* __restrict__ W, IT* __restrict__ indices,
     const OT* __restrict__ offsets, const float* __restrict__ psw, float* __restrict__ out,
     const int64_t* __restrict__ meta, int32_t skip_t, int32_t n_tables, int32_t B,
