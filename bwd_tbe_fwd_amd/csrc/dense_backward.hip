@@ -300,6 +300,24 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   for (int64_t st = p; st < steps; st += P) {
     const int64_t b0 = st * kDnBags;
     const int nb = static_cast<int>(min<int64_t>(kDnBags, static_cast<int64_t>(B) - b0));
+    // this wave's bag range from the offsets fetched one step ahead (monotone running max)
+    int32_t o = o_next;
+    for (int d = 1; d < 32; d <<= 1) {
+      const int32_t u = __shfl_up(o, d);
+      if (lane >= d) o = max(o, u);
+    }
+    const int32_t o0 = read_lane(o, 0);
+    const int32_t n = read_lane(o, kDnWaveBags) - o0;
+    // SLOTS: the first slot bytes are requested before the gradient, so that counting (which
+    // waits only for them) overlaps the gradient's arrival
+    uint32_t sl0[kDnLoads];
+    if constexpr (SLOTS) {
+#pragma unroll
+      for (int u = 0; u < kDnLoads; ++u) {
+        const int32_t j = u * kWave + lane;
+        sl0[u] = j < n ? dense_slot[o0 + j] : kNoDenseSlot;
+      }
+    }
     // gradient values: gv[8 kk + j] = bag 32 kk + 8 (l / 16) + j, columns c2, c2 + 1
     f32x2 gv[16];
 #pragma unroll
@@ -312,14 +330,6 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
           gv[8 * kk + j] = *reinterpret_cast<const f32x2*>(grad_out + (b0 + i) * out_width + m.col_base + c2);
       }
     }
-    // this wave's bag range from the offsets fetched one step ahead (monotone running max)
-    int32_t o = o_next;
-    for (int d = 1; d < 32; d <<= 1) {
-      const int32_t u = __shfl_up(o, d);
-      if (lane >= d) o = max(o, u);
-    }
-    const int32_t o0 = read_lane(o, 0);
-    const int32_t n = read_lane(o, kDnWaveBags) - o0;
     if (st + P < steps) {
       int64_t bw;
       int nbw;
@@ -340,7 +350,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
 #pragma unroll
         for (int u = 0; u < kDnLoads; ++u) {
           const int32_t j = j0 + u * kWave + lane;
-          sl[u] = j < n ? dense_slot[o0 + j] : kNoDenseSlot;
+          sl[u] = j0 == 0 ? sl0[u] : (j < n ? dense_slot[o0 + j] : kNoDenseSlot);
         }
 #pragma unroll
         for (int u = 0; u < kDnLoads; ++u) {
