@@ -252,3 +252,32 @@ def test_dense_rows_are_the_longest_128(presort):
         outs.append(W.cpu().view(600, 64).view(torch.int32))
     differ = set(torch.nonzero((outs[0] != outs[1]).any(dim=1)).flatten().tolist())
     assert differ <= top and len(differ) >= 100, (len(differ), sorted(differ - top)[:5])
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_dense_rows_random_shapes(seed):
+    """Seeded random shapes through both picks: table sizes from 2 rows up, widths in and out
+    of the dense path's range, every weight and index type, thresholds and chunk sizes, one
+    or two streams; every step checked against the oracle."""
+    rng = np.random.default_rng(seed)
+    for it in range(30):
+        T = int(rng.integers(1, 6))
+        tables = tuple(ti.TableSpec(int(rng.choice([2, 17, 64, 300, 1000, 5000])),
+                                    int(rng.choice([8, 16, 48, 64, 96, 128, 200])),
+                                    ("poisson", float(rng.choice([3, 10, 30, 80])), None, None),
+                                    ("zipf", float(rng.choice([0.9, 1.1, 1.3])), None)
+                                    if rng.random() < 0.8 else ("uniform",))
+                       for _ in range(T))
+        spec = ti.BatchSpec(f"dense random {seed}.{it}", tables,
+                            B=int(rng.choice([1, 7, 63, 64, 65, 200, 700, 3000])),
+                            w_dtype=[torch.float32, torch.float16, torch.bfloat16][int(rng.integers(0, 3))],
+                            w_range=0.05, optimizer=["sgd", "rowwise_adagrad"][int(rng.integers(0, 2))],
+                            itype=[torch.int32, torch.int64][int(rng.integers(0, 2))],
+                            otype=[torch.int32, torch.int64][int(rng.integers(0, 2))])
+        bt = ti.make_batch(spec, 1000 * seed + it)
+        cfg = tbe.make_config(long_threshold=int(rng.choice([16, 32, 256])),
+                              chunk=int(rng.choice([8, 16, 256])),
+                              dense_min=int(rng.choice([16, 24, 40, 100])),
+                              dense_presort=int(rng.choice([1, -1])),
+                              bwd_streams=int(rng.choice([0, 1, 2])))
+        run_and_check(bt, cfg, what=f"{spec.name}: {bt.indices.numel()} lookups")
