@@ -195,9 +195,9 @@ def algorithmic_bytes(bt: ti.Batch, st: dict, hoist: bool, dense_P: int = 24, pr
     by = {
         # per lookup: index (+ weight) + row; per bag: offset + output row
         "fwd_gather": sum(p["N"] * (s_i + s_p + p["D"] * s_w) + B * (s_o + p["D"] * 4) for p in gen),
-        # per lookup: index read, key + payload written (with the pre-sort pick also its dense
-        # slot byte); per bag: offset
-        "linearize": st["N"] * s_i + runs_N * (8 + (1 if presort else 0)) + st["TB"] * s_o,
+        # per lookup: index read, key + payload written (with the pre-sort pick also its two
+        # dense-slot bytes); per bag: offset
+        "linearize": st["N"] * s_i + runs_N * (8 + (2 if presort else 0)) + st["TB"] * s_o,
         # per pass: keys + payloads read and written (the first pass writes only the kept keys,
         # later passes see only those)
         "radix_downsweep": (runs_N * 8 + kept * 8 + (passes - 1) * kept * 16) / passes,
@@ -213,10 +213,10 @@ def algorithmic_bytes(bt: ti.Batch, st: dict, hoist: bool, dense_P: int = 24, pr
         # per chunk: partial row read; per long run: descriptor, weight row r/w, state r/w
         "long_apply": sum(p["gen_chunks"] * p["D"] * 4 + p["gen_long_runs"] * (20 + 2 * p["D"] * s_w + 8)
                           for p in gen),
-        # per table with dense rows: its ids (with the pre-sort pick the dense slot bytes
+        # per table with dense rows: its ids (with the pre-sort pick the two dense-slot bytes
         # instead), offsets and B x D gradient slice, and its partials (P per table, one row of
         # D floats per dense row each)
-        "dense_partial": sum(p["N"] * (1 if presort else s_i) + B * (s_o + p["D"] * 4)
+        "dense_partial": sum(p["N"] * (2 if presort else s_i) + B * (s_o + p["D"] * 4)
                              + dense_P * p["dense_rows"] * p["D"] * 4 for p in gen if p["dense_rows"]),
         # per dense row: its P partial rows, weight row r/w, state r/w
         "dense_apply": sum(p["dense_rows"] * (dense_P * p["D"] * 4 + 2 * p["D"] * s_w + 8) for p in gen),

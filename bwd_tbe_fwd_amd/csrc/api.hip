@@ -264,7 +264,7 @@ BwdLayout bwd_layout(const tbe_tables* tb, int64_t N, int weighted, const Config
     L.hot_set_size = hs;
     L.hot_set = c.take(static_cast<size_t>(hs) * 4);
     L.hot_rank = c.take(static_cast<size_t>(hs));
-    L.dense_slot = c.take(static_cast<size_t>(n1));
+    L.dense_slot = c.take(static_cast<size_t>(n1) * 2);
     L.hot_bloom = c.take(static_cast<size_t>(kHotBloomWords) * 4);
   }
   L.counters = c.take(kNumCounters * 4);

@@ -242,14 +242,15 @@ __device__ __forceinline__ int32_t wave_offsets(const OT* __restrict__ offsets, 
 // and only the fp32 accumulation rounds, as in the fp32 sums of the chunk path.  A step's
 // gradient rows and ids are requested together, and the next step's offsets before this
 // step's counting, so a step waits on memory about once.
-// SLOTS: each lookup's row rank comes from dense_slot (one byte a position, written by
-// linearize with the pre-sort pick) instead of its id, the filter and the search.
+// SLOTS: each lookup's row rank and bag come from dense_slot (two bytes a position, written
+// by linearize with the pre-sort pick) instead of its id, the filter, the search of the row
+// list and the search of the bag offsets.
 template <typename IT, typename OT, bool SLOTS>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void dense_partial_kernel(
     const IT* __restrict__ indices, const OT* __restrict__ offsets, const float* __restrict__ grad_out,
     const int64_t* __restrict__ meta, int32_t B, int32_t out_width, int64_t N, int P,
     const int32_t* __restrict__ dense_rows, const int32_t* __restrict__ dense_cnt,
-    const uint8_t* __restrict__ dense_slot, float* __restrict__ partial) {
+    const uint16_t* __restrict__ dense_slot, float* __restrict__ partial) {
   constexpr int kStride = kDnBags + 4;   // counts [row][bag]; rows padded against bank conflicts
   constexpr int kBloomWords = 1024;      // 32768-bit filter of the selected rows (id mod 32768)
   // counts as fp32 (exact integers below 2^24): a count below 256 is then its own bf16 value
@@ -355,14 +356,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
 #pragma unroll
         for (int u = 0; u < kDnLoads; ++u) {
           if (j0 + u * kWave >= n) break;  // uniform: no lane has a lookup left
-          const int32_t j = j0 + u * kWave + lane;
-          if (sl[u] < static_cast<uint32_t>(nd)) {
-            int b = 0;  // the bag of lookup j
-#pragma unroll
-            for (int step = 8; step > 0; step >>= 1)
-              if (off[b + step] <= j) b += step;
-            atomicAdd(&s_cnt[sl[u] * kStride + kDnWaveBags * w + b], 1.f);
-          }
+          const uint32_t rank = sl[u] & 0xffu;
+          if (rank < static_cast<uint32_t>(nd))  // the wave's bags start at a multiple of 16
+            atomicAdd(&s_cnt[rank * kStride + kDnWaveBags * w + ((sl[u] >> 8) & 15u)], 1.f);
         }
       }
     }
@@ -536,7 +532,7 @@ template <typename IT, typename OT>
 tbe_status partial_go(const tbe_tables* tb, const IndexArgs& ia, const float* grad_out, char* ws,
                       const BwdLayout& L, int P, hipStream_t s) {
   ProfScope ps("dense_partial", s);
-  const uint8_t* slot = L.dense_presort ? reinterpret_cast<const uint8_t*>(ws + L.dense_slot) : nullptr;
+  const uint16_t* slot = L.dense_presort ? reinterpret_cast<const uint16_t*>(ws + L.dense_slot) : nullptr;
   if (slot)
     hipLaunchKernelGGL((dense_partial_kernel<IT, OT, true>), dim3(tb->T * P), dim3(kBlock), 0, s,
                        static_cast<const IT*>(ia.indices), static_cast<const OT*>(ia.offsets), grad_out,

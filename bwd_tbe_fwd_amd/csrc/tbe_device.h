@@ -208,7 +208,9 @@ __device__ __forceinline__ int table_of_key(const int64_t* __restrict__ meta, in
 // most other keys away first.  Both hashes are
 // multiplicative (Knuth's golden-ratio constant and a second odd multiplier).
 constexpr uint32_t kHotEmpty = 0xffffffffu;
-constexpr uint8_t kNoDenseSlot = 0xff;  // a lookup that no dense row takes
+// A lookup's dense slot: bits 0-7 the rank of its row among its table's dense rows (0xff:
+// none), bits 8-11 its bag's index within the table modulo 16
+constexpr uint16_t kNoDenseSlot = 0x00ff;
 __device__ __forceinline__ uint32_t hot_slot(uint32_t key, uint32_t mask) {
   const uint32_t h = key * 0x9e3779b1u;
   return ((h ^ (h >> 15)) << 2) & mask;  // first slot of a group

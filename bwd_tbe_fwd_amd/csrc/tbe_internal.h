@@ -88,8 +88,8 @@ struct BwdLayout {
   // after the sort, with a flag per long-list slot (long_flag) that the chunk and apply
   // kernels read
   // (hot_rank: the rank of each key-set slot's row among its table's dense rows; dense_slot:
-  // one byte per lookup position, its row's rank or none, written by linearize and read by
-  // the dense partial kernel instead of the ids)
+  // two bytes per lookup position, its row's rank or none and its bag modulo 16, written by
+  // linearize and read by the dense partial kernel instead of the ids)
   size_t dense_rows, dense_cnt, dense_partial, hot_set, hot_rank, hot_bloom, long_flag, dense_slot;
   int dense_P, dense_on, dense_presort, hot_stride, hot_thr;
   int64_t hot_set_size;

@@ -92,9 +92,9 @@ __device__ __forceinline__ uint64_t match_digit(uint32_t d, int bits, uint64_t v
 // get the sentinel key, so every key and payload the sort reads is defined.
 // hot_set != NULL: keys in the dense-row key set (hot_mask + 1 slots; the most slot groups
 // a lookup reads in *hot_probes) get the sentinel key too, and every position of a bag (and
-// every position no bag covers) gets its byte in dense_slot: the rank of its row among its
-// table's dense rows, or kNoDenseSlot (positions of the table left out, skip_t, are not
-// written): those lookups are the
+// every position no bag covers) gets its dense slot: the rank of its row among its table's
+// dense rows and its bag modulo 16, or kNoDenseSlot (positions of the table left out,
+// skip_t, are not written): those lookups are the
 // dense path's.  The set's filter goes into LDS; keys that pass it probe the set (a
 // whole copy in LDS measured slower: it cost occupancy, and most probes are hits anyway).
 constexpr int kLinU = 8;  // positions per lane per step
@@ -104,7 +104,7 @@ __global__ __launch_bounds__(kBlock) void linearize_kernel(
     int32_t B, int64_t nbags, int32_t N, uint32_t sentinel, int skip_t, int invalid_as_row0,
     const uint32_t* __restrict__ hot_filter, const uint32_t* __restrict__ hot_set,
     const uint8_t* __restrict__ hot_rank, uint32_t hot_mask, const int32_t* __restrict__ hot_probes,
-    uint8_t* __restrict__ dense_slot, uint32_t* __restrict__ keys,
+    uint16_t* __restrict__ dense_slot, uint32_t* __restrict__ keys,
     uint32_t* __restrict__ pay, uint32_t* __restrict__ bag_of, int32_t* __restrict__ n_eff) {
   __shared__ __align__(16) uint32_t s_filter[kHotBloomWords];
   int hot_max = 0;
@@ -149,12 +149,14 @@ __global__ __launch_bounds__(kBlock) void linearize_kernel(
     const int32_t S = clampN(static_cast<int64_t>(offsets[g0]), 0);
     int32_t e = S;
     int64_t rb = 0, E = 0;
+    int32_t b16 = 0;  // the lane's bag within its table, modulo 16
     bool skip = false;
     if (bag < nbags) {
       e = clampN(static_cast<int64_t>(offsets[bag + 1]), S);
       const int t = static_cast<int>(bag / B);
       rb = meta[4 * t];
       E = meta[4 * (t + 1)] - rb;
+      b16 = static_cast<int32_t>((bag - static_cast<int64_t>(t) * B) & 15);
       skip = t == skip_t;
     }
     // monotone end offsets across the 64 lanes (inclusive running max)
@@ -230,7 +232,7 @@ __global__ __launch_bounds__(kBlock) void linearize_kernel(
                              v[u].w == kHotEmpty;
             if (hit) {
               const int j = v[u].x == kk ? 0 : (v[u].y == kk ? 1 : (v[u].z == kk ? 2 : 3));
-              slot[u] = (rk[u] >> (8 * j)) & 0xffu;
+              slot[u] = (rk[u] >> (8 * j)) & 0xffu;  // the bag's part is added below
               key[u] = sentinel;
             }
             pend[u] = !hit && !gap;
@@ -241,7 +243,11 @@ __global__ __launch_bounds__(kBlock) void linearize_kernel(
       }
 #pragma unroll
       for (int u = 0; u < kLinU; ++u) {
-        if (hot_set && p[u] < Eend) dense_slot[p[u]] = static_cast<uint8_t>(slot[u]);
+        if (hot_set) {
+          const uint32_t bb = static_cast<uint32_t>(__shfl(b16, k[u]));  // every lane takes part
+          if (p[u] < Eend)
+            dense_slot[p[u]] = static_cast<uint16_t>(slot[u] == kNoDenseSlot ? slot[u] : (slot[u] | (bb << 8)));
+        }
         if (!act[u]) continue;
         const int32_t q = compact(p[u]);
         keys[q] = key[u];
@@ -763,7 +769,7 @@ struct HotSet {
   const uint8_t* rank;
   uint32_t mask;
   const int32_t* probes;
-  uint8_t* slot;  // per position: rank among the table's dense rows, or kNoDenseSlot
+  uint16_t* slot;  // per position: its dense slot (rank and bag modulo 16), or kNoDenseSlot
 };
 
 template <typename IT, typename OT>
@@ -920,7 +926,7 @@ tbe_status launch_transpose(const tbe_tables* tb, const IndexArgs& ia, int weigh
     hot = HotSet{reinterpret_cast<const uint32_t*>(ws + L.hot_bloom),
                  reinterpret_cast<const uint32_t*>(ws + L.hot_set), reinterpret_cast<const uint8_t*>(ws + L.hot_rank),
                  static_cast<uint32_t>(L.hot_set_size - 1), counters + kHotProbe,
-                 reinterpret_cast<uint8_t*>(ws + L.dense_slot)};
+                 reinterpret_cast<uint16_t*>(ws + L.dense_slot)};
   }
   uint32_t* keys0 = reinterpret_cast<uint32_t*>(ws + L.keys[0]);
   uint32_t* pay0 = reinterpret_cast<uint32_t*>(ws + L.pay[0]);

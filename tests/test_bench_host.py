@@ -118,6 +118,6 @@ def test_presort_sample_and_bytes():
     assert dl > 0 and plain["radix_downsweep"] == N * 16     # 364 rows: one pass
     assert pre["radix_downsweep"] == N * 8 + kept * 8 and pre["radix_upsweep"] == N * 4
     assert pre["rle"] == 3 * kept * 4 + (st["U"] - 128 - 64) * 8
-    assert pre["linearize"] == plain["linearize"] + N and "dense_sample" in pre
-    # the dense kernel reads one slot byte a lookup instead of its 8-byte id
-    assert plain["dense_partial"] - pre["dense_partial"] == N * 7
+    assert pre["linearize"] == plain["linearize"] + 2 * N and "dense_sample" in pre
+    # the dense kernel reads two slot bytes a lookup instead of its 8-byte id
+    assert plain["dense_partial"] - pre["dense_partial"] == N * 6
