@@ -149,16 +149,15 @@ __global__ __launch_bounds__(kBlock) void linearize_kernel(
     const int32_t S = clampN(static_cast<int64_t>(offsets[g0]), 0);
     int32_t e = S;
     int64_t rb = 0, E = 0;
-    int32_t b16 = 0;  // the lane's bag within its table, modulo 16
     bool skip = false;
     if (bag < nbags) {
       e = clampN(static_cast<int64_t>(offsets[bag + 1]), S);
       const int t = static_cast<int>(bag / B);
       rb = meta[4 * t];
       E = meta[4 * (t + 1)] - rb;
-      b16 = static_cast<int32_t>((bag - static_cast<int64_t>(t) * B) & 15);
       skip = t == skip_t;
     }
+    const int64_t tb0 = (g0 / B) * B;  // first bag of the group's first table
     // monotone end offsets across the 64 lanes (inclusive running max)
     for (int d = 1; d < kWave; d <<= 1) {
       const int32_t u = __shfl_up(e, d);
@@ -243,10 +242,13 @@ __global__ __launch_bounds__(kBlock) void linearize_kernel(
       }
 #pragma unroll
       for (int u = 0; u < kLinU; ++u) {
-        if (hot_set) {
-          const uint32_t bb = static_cast<uint32_t>(__shfl(b16, k[u]));  // every lane takes part
-          if (p[u] < Eend)
-            dense_slot[p[u]] = static_cast<uint16_t>(slot[u] == kNoDenseSlot ? slot[u] : (slot[u] | (bb << 8)));
+        if (hot_set && p[u] < Eend) {
+          // the bag's index within its table, modulo 16 (the group's 64 bags start in table
+          // g0 / B: one step past a table's end per table crossed)
+          int32_t local = static_cast<int32_t>(g0 + k[u] - tb0);
+          while (local >= B) local -= B;
+          const uint32_t bb = static_cast<uint32_t>(local & 15);
+          dense_slot[p[u]] = static_cast<uint16_t>(slot[u] == kNoDenseSlot ? slot[u] : (slot[u] | (bb << 8)));
         }
         if (!act[u]) continue;
         const int32_t q = compact(p[u]);
