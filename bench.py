@@ -493,6 +493,8 @@ def main():
         "copy_peak_GBps": copy_peak_gbps(),
         # event-timed per kernel, one step each with nothing overlapping (transpose in the backward)
         "kernel_ms_one_step": per_kernel,
+        # what each of those kernels must move per launch (no credit for cache reuse), GB
+        "algorithmic_GB_per_launch": {k: ab[k] / 1e9 for k in per_kernel if k in ab},
         # matrix-core kernels: work as issued over their average launch time (one-step scan),
         # against the dense MFMA peak of their operand type
         "mfma_utilisation": {
