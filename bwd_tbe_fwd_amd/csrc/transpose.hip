@@ -648,23 +648,44 @@ __device__ __forceinline__ int run_category(const TableLds& s, const int64_t* __
   return 1 + bucket_of_D(D);
 }
 
+// one_bucket >= 0: every table's short runs fall in that bucket, so a run's category follows
+// from its key's validity and its length alone (no table search).  Each wave adds its
+// counts with one LDS atomic per category (a lane per run would serialize on one address).
 __global__ __launch_bounds__(kBlock) void classify_count(
     const uint32_t* __restrict__ run_key, const uint32_t* __restrict__ run_start,
     const int32_t* __restrict__ counters, const int64_t* __restrict__ meta, int T,
-    uint32_t total_rows, int threshold, int chunk, uint32_t* __restrict__ cls_cnt) {
+    uint32_t total_rows, int threshold, int chunk, int one_bucket, uint32_t* __restrict__ cls_cnt) {
   __shared__ uint32_t s_cnt[kClsRows];
   if (threadIdx.x < kClsRows) s_cnt[threadIdx.x] = 0;
   const TableLds s_tab = load_tables(meta, T);
+  const int lane = lane_id();
   int64_t lo, hi;
   block_segment(counters[kRuns], lo, hi);
-  for (int64_t r = lo + threadIdx.x; r < hi; r += kBlock) {
-    const uint32_t key = run_key[r];
-    const uint32_t len = run_start[r + 1] - run_start[r];
-    int t;
-    uint32_t nch;
-    const int cat = run_category(s_tab, meta, T, total_rows, threshold, chunk, key, len, t, nch);
-    if (cat >= 0) atomicAdd(&s_cnt[cat], 1u);
-    if (nch) atomicAdd(&s_cnt[kCats], nch);
+  for (int64_t tile = lo; tile < hi; tile += kBlock) {  // uniform trip count (ballots below)
+    const int64_t r = tile + threadIdx.x;
+    int cat = -1;
+    uint32_t nch = 0;
+    if (r < hi) {
+      const uint32_t key = run_key[r];
+      const uint32_t len = run_start[r + 1] - run_start[r];
+      if (one_bucket >= 0) {
+        if (key < total_rows) {
+          const bool lng = len >= static_cast<uint32_t>(threshold);
+          cat = lng ? 0 : 1 + one_bucket;
+          nch = lng ? (len + chunk - 1) / chunk : 0u;
+        }
+      } else {
+        int t;
+        cat = run_category(s_tab, meta, T, total_rows, threshold, chunk, key, len, t, nch);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < kCats; ++c) {
+      const uint64_t m = __ballot(cat == c);
+      if (lane == 0 && m) atomicAdd(&s_cnt[c], static_cast<uint32_t>(__popcll(m)));
+    }
+    for (int d = 1; d < kWave; d <<= 1) nch += __shfl_xor(nch, d);
+    if (lane == 0 && nch) atomicAdd(&s_cnt[kCats], nch);
   }
   __syncthreads();
   if (threadIdx.x < kClsRows) cls_cnt[threadIdx.x * gridDim.x + blockIdx.x] = s_cnt[threadIdx.x];
@@ -862,8 +883,12 @@ tbe_status sort_route(const tbe_tables* tb, char* ws, const SortPlan& P, const B
     const uint32_t total_rows = static_cast<uint32_t>(tb->total_rows);
     ProfScope ps(nm.cls, s);
     const size_t lds = table_lds_bytes(tb->T);
+    int one_bucket = -1;  // the only short-run bucket any table falls in, if there is one
+    for (int b = 0; b < TBE_NUM_BUCKETS; ++b)
+      if (tb->bucket_rows[b] > 0) one_bucket = one_bucket == -1 ? b : -2;
     hipLaunchKernelGGL(classify_count, dim3(P.cls_blocks), dim3(kBlock), lds, s, run_key, run_start,
-                       counters, tb->meta, tb->T, total_rows, threshold, chunk, cls_cnt);
+                       counters, tb->meta, tb->T, total_rows, threshold, chunk, one_bucket < 0 ? -1 : one_bucket,
+                       cls_cnt);
     hipLaunchKernelGGL(classify_scan, dim3(kClsRows), dim3(kBlock), 0, s, cls_cnt, P.cls_blocks, counters);
     hipLaunchKernelGGL(classify_write, dim3(P.cls_blocks), dim3(kBlock), lds, s, run_key, run_start,
                        counters, tb->meta, tb->T, total_rows, threshold, chunk, cls_cnt,
