@@ -9,37 +9,39 @@
 // which is the sum over every lookup of r of its bag's gradient row.  On the
 // sorted-run path a row with n lookups reads n gradient rows (n * 4D bytes);
 // here the table's B x D gradient slice is read once for all rows of R
-// together, plus the table's ids.  For rows looked up thousands of times
-// (the head of a skewed id distribution) that replaces most of the long-run
-// gradient traffic.
+// together, plus the table's ids (or one two-byte slot per lookup).  For rows
+// looked up thousands of times (the head of a skewed id distribution) that
+// replaces most of the long-run gradient traffic.
 //
 // gfx950 mapping.  dense_select (one wave per table) takes a table's long runs
 // of at least dense_min lookups (the kDenseRows longest when more qualify) and
-// records their row ids (ascending).  In large batches the rows are picked before the sort, from a
-// sample of the lookups: dense_sample writes the keys of 64 positions out of
-// every hot_stride, which are sorted and run-length encoded on their own, the
-// runs that reach dense_min scaled to the sample are taken, and their keys go
-// into a hashed key set that linearize consults: their lookups get the
-// sentinel key, so the sort, the run-length encoding and the run kernels never
-// see them.  Otherwise (the sample's twenty-odd launches would cost more than
-// they save) the rows come from the batch's own long runs of at least
-// dense_min lookups after the sort, and their long-list slots are flagged so
-// that the chunk and apply kernels skip them.
+// records their row ids (ascending).  In large batches the rows are picked
+// before the sort, from a sample of the lookups: dense_sample writes the keys
+// of 64 positions out of every hot_stride, which are sorted and run-length
+// encoded on their own, the runs that reach dense_min scaled to the sample are
+// taken, and their keys go into a hashed key set that linearize consults:
+// their lookups get the sentinel key, so the sort, the run-length encoding and
+// the run kernels never see them, and every position gets a dense slot (its
+// row's rank among the table's dense rows, and its bag modulo 16).  Otherwise
+// (the sample's twenty-odd launches would cost more than they save) the rows
+// come from the batch's own long runs after the sort, and their long-list
+// slots are flagged so that the chunk and apply kernels skip them.
 // dense_partial: workgroup (t, p) takes the table's 64-bag steps p, p + P, ...;
 // each of its four waves counts the lookups of 16 of the step's bags that hit
-// a selected row (a bit filter in LDS, then a 7-step search of the sorted row
-// ids) into the shared count[128 rows][64 bags] (fp32, so that a count below
-// 256 is its own bf16 value); then wave w multiplies the
-// counts by gradient columns 32 w .. 32 w + 31 of the 64 bags on
-// v_mfma_f32_16x16x32_bf16.  The pages' compensated high/low product, made
-// exact: the fp32 gradient is split into three bf16 parts whose sum is exactly
-// its value, counts are exact in bf16 (byte by byte above 255), so every
-// product is exact and only the fp32 accumulation rounds.  (fp32 MFMA would
-// be 16x slower per flop: 128 rows x 64 bags x D per step is 137 GFLOP over
-// the large skewed batch.)  The 128 x 32 accumulator (8 x 2 tiles) stays in
-// registers across the steps and is written once as the workgroup's partial.
-// dense_apply sums a row's P partials in a fixed order and applies SGD or
-// row-wise Adagrad: results are bitwise repeatable.
+// a selected row (from the dense slots, or else through a bit filter in LDS, a
+// 7-step search of the sorted row ids and a 4-step search of the bag offsets)
+// into the shared count[128 rows][64 bags] (fp32, so that a count below 256 is
+// its own bf16 value); then wave w multiplies the counts by gradient columns
+// 32 w .. 32 w + 31 of the 64 bags on v_mfma_f32_16x16x32_bf16.  The blog's
+// compensated high/low product, made exact: the fp32 gradient is split into
+// three bf16 parts whose sum is exactly its value, counts are exact in bf16
+// (byte by byte above 255), so every product is exact and only the fp32
+// accumulation rounds.  (fp32 MFMA would be 16x slower per flop: 128 rows x 64
+// bags x D per step is 137 GFLOP over the large skewed batch.)  The 128 x 32
+// accumulator (8 x 2 tiles) stays in registers across the steps and is
+// written once as the workgroup's partial.  dense_apply sums a row's P
+// partials in a fixed order and applies SGD or row-wise Adagrad: results are
+// bitwise repeatable.
 #include "backward_launch.h"
 
 namespace tbe {

@@ -54,7 +54,7 @@ struct Config {
   int threshold, chunk, hist_enable, fwd_unroll, bwd_unroll, sort_blocks, bag_windows, fused_long;
   int pretransposed, bags_per_wave, bwd_streams;
   int tiny;  // wave steps of short runs of at most this many lookups: half the lanes per run
-  int dense_min;  // long runs of at least this many lookups take the dense path (0: off)
+  int dense_min;  // rows of at least this many lookups (the 128 longest a table) take the dense path (0: off)
   int dense_presort;  // dense rows picked before the sort: 1 always, -1 never, 0 large batches
 };
 Config resolve_config(const tbe_config* c);

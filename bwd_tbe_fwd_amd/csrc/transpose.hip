@@ -14,10 +14,16 @@
 //
 // gfx950 design:
 //  - linearize: a wave takes 64 consecutive bags (their offsets in one load),
-//    and its lanes walk the contiguous lookups of those bags, each lane finding
-//    its bag by a 6-step binary search over the 64 end offsets (lane shuffles).
+//    and its lanes walk the contiguous lookups of those bags, 8 positions a
+//    lane per step, each lane finding its bag by a 6-step binary search over
+//    the 64 end offsets (lane shuffles).  With the dense rows picked before the
+//    sort, their lookups get the sentinel key (a filter in LDS, then a probe of
+//    the hashed key set) and every position gets its dense slot.
 //  - sort: reduce-then-scan LSD radix, up to 9 bits a pass (26-bit keys take 3
-//    passes).  A fixed number of blocks each own a contiguous segment; per pass:
+//    passes); the first pass leaves the sentinel keys out, and the later
+//    kernels read the kept count from the device.  The dense-row pick sorts
+//    its sample with the same kernels (sort_route).  A fixed number of blocks
+//    each own a contiguous segment; per pass:
 //    upsweep (digit counts per block), a per-digit scan across blocks, and a
 //    downsweep that ranks each 4096-key tile stably in LDS (wave ballots find
 //    the lanes holding the same digit; the lowest lane adds the count), sorts
