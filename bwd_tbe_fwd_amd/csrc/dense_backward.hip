@@ -31,8 +31,9 @@
 // a selected row (from the dense slots, or else through a bit filter in LDS, a
 // 7-step search of the sorted row ids and a 4-step search of the bag offsets)
 // into the shared count[128 rows][64 bags] (fp32, so that a count below 256 is
-// its own bf16 value); then wave w multiplies the counts by gradient columns
-// 32 w .. 32 w + 31 of the 64 bags on v_mfma_f32_16x16x32_bf16.  The blog's
+// its own bf16 value; uint32 for a wave whose bags hold 2^24 lookups or more);
+// then wave w multiplies the counts by gradient columns 32 w .. 32 w + 31 of
+// the 64 bags on v_mfma_f32_16x16x32_bf16.  The blog's
 // compensated high/low product, made exact: the fp32 gradient is split into
 // three bf16 parts whose sum is exactly its value, counts are exact in bf16
 // (byte by byte above 255), so every product is exact and only the fp32
@@ -256,11 +257,13 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   constexpr int kStride = kDnBags + 4;   // counts [row][bag]; rows padded against bank conflicts
   constexpr int kBloomWords = 1024;      // 32768-bit filter of the selected rows (id mod 32768)
   // counts as fp32 (exact integers below 2^24): a count below 256 is then its own bf16 value
-  // in the high half of its bits
+  // in the high half of its bits; a wave whose 16 bags hold 2^24 lookups or more counts in
+  // uint32 instead (s_intc)
   __shared__ __align__(16) float s_cnt[kDenseRows * kStride];
   __shared__ uint32_t s_bloom[kBloomWords];
   __shared__ int32_t s_rows[kDenseRows];
   __shared__ int32_t s_off[kWavesPerBlock][kDnWaveBags + 1];
+  __shared__ int32_t s_intc[kWavesPerBlock];  // 1: the wave's counts of this step are uint32
   const int t = static_cast<int>(blockIdx.x) / P, p = static_cast<int>(blockIdx.x) % P;
   const int nd = dense_cnt[t];
   if (nd == 0) return;  // uniform over the workgroup
@@ -311,6 +314,11 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     }
     const int32_t o0 = read_lane(o, 0);
     const int32_t n = read_lane(o, kDnWaveBags) - o0;
+    // an fp32 count stops growing at 2^24, which only a wave whose bags hold 2^24 lookups or
+    // more can reach: such a wave counts with integer adds on the same slots (its columns are
+    // then read as uint32 below; its step always takes the byte-by-byte path, since one of its
+    // 16 bags has at least 2^20 lookups)
+    const bool intc = n >= (1 << 24);
     // SLOTS: the first slot bytes are requested before the gradient, so that counting (which
     // waits only for them) overlaps the gradient's arrival
     uint32_t sl0[kDnLoads];
@@ -341,6 +349,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     }
     __syncthreads();  // every wave is done with the previous step's counts (and the filter is set)
     if (lane <= kDnWaveBags) off[lane] = o - o0;
+    if (lane == 0) s_intc[w] = intc ? 1 : 0;
     // this wave's 16 bag columns of every row
 #pragma unroll
     for (int x = lane; x < kDenseRows * (kDnWaveBags / 4); x += kWave)
@@ -359,8 +368,11 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
         for (int u = 0; u < kDnLoads; ++u) {
           if (j0 + u * kWave >= n) break;  // uniform: no lane has a lookup left
           const uint32_t rank = sl[u] & 0xffu;
-          if (rank < static_cast<uint32_t>(nd))  // the wave's bags start at a multiple of 16
-            atomicAdd(&s_cnt[rank * kStride + kDnWaveBags * w + ((sl[u] >> 8) & 15u)], 1.f);
+          if (rank < static_cast<uint32_t>(nd)) {  // the wave's bags start at a multiple of 16
+            float* c = &s_cnt[rank * kStride + kDnWaveBags * w + ((sl[u] >> 8) & 15u)];
+            if (intc) atomicAdd(reinterpret_cast<uint32_t*>(c), 1u);
+            else atomicAdd(c, 1.f);
+          }
         }
       }
     }
@@ -388,7 +400,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
 #pragma unroll
               for (int step = 8; step > 0; step >>= 1)
                 if (off[b + step] <= j) b += step;
-              atomicAdd(&s_cnt[k * kStride + kDnWaveBags * w + b], 1.f);
+              float* c = &s_cnt[k * kStride + kDnWaveBags * w + b];
+              if (intc) atomicAdd(reinterpret_cast<uint32_t*>(c), 1u);
+              else atomicAdd(c, 1.f);
             }
           }
         }
@@ -427,15 +441,18 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
                               __builtin_amdgcn_perm(c1.w, c1.z, 0x07060302u)};
             dense_mfma(acc[mt], __builtin_bit_cast(bf16x8, pk), bh, bm, bl);
           } else {
-            // byte by byte: byte lv of a count times 256^lv has at most 8 significant bits
+            // byte by byte: byte lv of a count times 256^lv has at most 8 significant bits.
+            // The lane's 8 bag columns belong to wave 2 kk + lane / 32, whose counts are fp32
+            // or (intc) uint32
             const uint32_t cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+            const bool ic = s_intc[2 * kk + (lane >> 5)] != 0;
 #pragma unroll 1
             for (int lv = 0; lv < 4; ++lv) {
               u32x4 pk;
 #pragma unroll
               for (int j = 0; j < 4; ++j) {
-                const uint32_t a = static_cast<uint32_t>(__builtin_bit_cast(float, cv[2 * j]));
-                const uint32_t b = static_cast<uint32_t>(__builtin_bit_cast(float, cv[2 * j + 1]));
+                const uint32_t a = ic ? cv[2 * j] : static_cast<uint32_t>(__builtin_bit_cast(float, cv[2 * j]));
+                const uint32_t b = ic ? cv[2 * j + 1] : static_cast<uint32_t>(__builtin_bit_cast(float, cv[2 * j + 1]));
                 const float lo = static_cast<float>(((a >> (8 * lv)) & 255u) << (8 * lv));
                 const float hi = static_cast<float>(((b >> (8 * lv)) & 255u) << (8 * lv));
                 pk[j] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, hi), __builtin_bit_cast(uint32_t, lo),

@@ -179,6 +179,30 @@ def test_dense_rows_counts_above_255(L, presort):
 
 
 @pytest.mark.parametrize("presort", PRESORT)
+def test_dense_rows_count_above_2_pow_24(presort):
+    """One bag with 3 * 2^23 lookups of one row: an fp32 count would stop at 2^24 (a third
+    short); the wave that counts that bag counts in uint32, so the step stays exact (integer
+    gradients, zero weights, SGD with lr = -1, so the weights are the oracle's sums bit for
+    bit)."""
+    L = 3 * 2 ** 23
+    tables = (ti.TableSpec(1, 64, ("fixed", L)), ti.TableSpec(500, 128, ("poisson", 8.0, None, None)))
+    spec = ti.BatchSpec("dense count 3*2^23", tables, B=1, w_dtype=torch.float32, w_range=0.05,
+                        optimizer="sgd", itype=torch.int32, otype=torch.int64)
+    bt = ti.make_batch(spec, 88)
+    g = torch.Generator().manual_seed(10)
+    bt.grad_out = torch.randint(-1, 2, bt.grad_out.shape, generator=g).float()
+    bt.grad_out[0, :64] = torch.tensor([1.0, -1.0] * 32)
+    bt.weights = torch.zeros_like(bt.weights)
+    flush_print(f"dense count above 2^24 presort={presort}: {bt.indices.numel()} lookups")
+    db = DevBatch(bt)
+    W, _ = db.backward(_cfg(16, presort), lr=-1.0)
+    torch.cuda.synchronize()
+    r = oracle_backward(bt, lr=-1.0)
+    assert np.abs(r["g"][:64]).max() == L
+    assert np.array_equal(W.cpu().double().numpy(), r["g"])
+
+
+@pytest.mark.parametrize("presort", PRESORT)
 def test_dense_rows_on_the_second_stream(presort):
     """The dense rows, chunks and applies on the library's second stream, concurrent with the
     short runs: the same bits as on one stream."""
