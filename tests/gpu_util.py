@@ -6,7 +6,12 @@ well under 160 stays below 1e-5 of the sum of |terms|; fp64 accumulation ends in
 rounding to fp32):
   * fp16/bf16 tables, fp32 accumulation:  |gpu - oracle| <= 1e-5 * sum|terms|
   * fp32 tables, fp64 accumulation:       |gpu - oracle| <= 1e-12 * sum|terms| + 0.5 ulp_fp32
-  * updated fp16/bf16 weights:            within 1 ulp of the oracle's rounded value
+  * updated fp16/bf16 weights:            within 1 ulp of the oracle's rounded value; only
+                                          where the gradient's own bound carried through the
+                                          step, 1e-5 * sum|step terms|, exceeds one ulp of the
+                                          exact result (a step that cancels the weight), the
+                                          weight may instead lie within that bound + 1 ulp of
+                                          the exact result
   * updated fp32 weights:                 |gpu - oracle| <= 1e-5 * (|w| + |step terms|)
   * row-wise Adagrad state:               |gpu - oracle| <= 1e-5 * (m + sum_d g_abs_d^2 / D)
 """
@@ -136,8 +141,16 @@ def bf_or_h_ulp(x: np.ndarray, dtype: torch.dtype) -> np.ndarray:
     return 2.0 ** (e - 7)
 
 
+# fp16/bf16 weights checked so far in this process: how many, how many lay beyond 1 ulp of the
+# oracle's rounded value (each of those passed only under the composed bound), and the largest
+# distance in ulp
+ULP_STATS = {"weights": 0, "beyond_1ulp": 0, "max_ulp": 0}
+
+
 def check_weights(W_gpu: torch.Tensor, r: dict, dtype: torch.dtype, step_abs=None, what=""):
-    """fp16/bf16: within 1 ulp of the oracle's rounded value; fp32: 1e-5 * (|w| + |step terms|)."""
+    """fp16/bf16: within 1 ulp of the oracle's rounded value, except under the one condition in
+    the module docstring; fp32: 1e-5 * (|w| + |step terms|).  Prints, for fp16/bf16, how many
+    weights lay beyond 1 ulp and the largest distance."""
     bits = weight_bits(W_gpu)
     if dtype == torch.float32:
         got = W_gpu.double().cpu().numpy()
@@ -148,13 +161,24 @@ def check_weights(W_gpu: torch.Tensor, r: dict, dtype: torch.dtype, step_abs=Non
     else:
         d = np.abs(ordered16(bits) - ordered16(r["w_bits"]))
         bad = d > 1
-        if bad.any() and step_abs is not None:
-            # where the step cancels the weight, the fp32 error of the step (1e-5 of its |terms|)
-            # can exceed one ulp of the tiny result: allow that error plus one ulp
+        beyond = int(bad.sum())
+        if beyond and step_abs is not None:
+            # the composed bound: the gradient may be off by 1e-5 of its |terms| (fp32
+            # accumulation), which the step carries into the weight as 1e-5 * step_abs; where
+            # that exceeds one ulp of the exact result, a correctly rounded fp32 step can land
+            # more than 1 ulp from the oracle's rounded value
             got = W_gpu.double().cpu().numpy()
             exp = r["w_new"]
             one_ulp = np.abs(bf_or_h_ulp(exp, dtype))
-            bad &= ~(np.abs(got - exp) <= one_ulp + 1e-5 * step_abs)
+            sa = np.broadcast_to(np.asarray(step_abs, dtype=np.float64), exp.shape)
+            composed = 1e-5 * sa > one_ulp
+            bad &= ~(composed & (np.abs(got - exp) <= one_ulp + 1e-5 * sa))
+        mx = int(d.max()) if d.size else 0
+        ULP_STATS["weights"] += int(d.size)
+        ULP_STATS["beyond_1ulp"] += beyond
+        ULP_STATS["max_ulp"] = max(ULP_STATS["max_ulp"], mx)
+        flush_print(f"{what}: {d.size} {'fp16' if dtype == torch.float16 else 'bf16'} weights, "
+                    f"{beyond} beyond 1 ulp (max {mx} ulp)")
     if bad.any():
         i = int(np.argwhere(bad)[0][0])
         raise AssertionError(f"{what}: {int(bad.sum())} weights off; first at {i}: gpu bits "
