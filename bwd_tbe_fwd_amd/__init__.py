@@ -59,10 +59,11 @@ class tbe_runs_view(ctypes.Structure):
                 ("short_list", ctypes.c_void_p * NUM_BUCKETS),
                 ("long_capacity", ctypes.c_int64), ("chunk_capacity", ctypes.c_int64),
                 ("short_capacity", ctypes.c_int64 * NUM_BUCKETS),
-                ("payload_is_position", ctypes.c_int32), ("radix_passes", ctypes.c_int32)]
+                ("payload_is_position", ctypes.c_int32), ("radix_passes", ctypes.c_int32),
+                ("dense_rows", ctypes.c_void_p), ("dense_count", ctypes.c_void_p)]
 
 
-# every symbol the header declares, with its ctypes signature
+# every symbol the headers in include/ declare, with its ctypes signature
 _P = ctypes.c_void_p
 _SIGS = {
     "tbe_status_string": ([ctypes.c_int], ctypes.c_char_p),
@@ -88,6 +89,7 @@ _SIGS = {
                                       ctypes.c_size_t, _P, _P], ctypes.c_int),
     "tbe_transpose": ([_P, _P, ctypes.c_int32, _P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
                        _P, ctypes.c_size_t, _P, _P, _P], ctypes.c_int),
+    # measurement hooks (include/tbe_measure.h)
     "tbe_profile_select": ([ctypes.c_char_p], ctypes.c_int),
     "tbe_profile_read": ([_P, _P], ctypes.c_int),
     "tbe_calibration_copy": ([_P, _P, ctypes.c_int64, _P], ctypes.c_int),

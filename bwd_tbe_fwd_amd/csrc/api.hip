@@ -724,9 +724,13 @@ tbe_status tbe_transpose(const tbe_tables* tables, const void* indices, int32_t 
   }
   IndexArgs ia{indices, index_type, offsets, offset_type, num_indices};
   char* ws = static_cast<char*>(workspace);
-  int final_buf = 0;
-  tbe_status st = launch_transpose(tables, ia, weighted ? 1 : 0, ws, L, cfg, -1, 0, 0, &final_buf,
-                                   static_cast<hipStream_t>(stream));
+  // pretransposed: describe what tbe_forward_hoisted left in the workspace, whose radix
+  // passes alternate buffers starting from buffer 0
+  int final_buf = L.passes & 1;
+  tbe_status st = TBE_OK;
+  if (!cfg.pretransposed)
+    st = launch_transpose(tables, ia, weighted ? 1 : 0, ws, L, cfg, -1, 0, 0, &final_buf,
+                          static_cast<hipStream_t>(stream));
   std::memset(view, 0, sizeof(*view));
   view->sorted_keys = reinterpret_cast<const uint32_t*>(ws + L.keys[final_buf]);
   view->sorted_payload = reinterpret_cast<const uint32_t*>(ws + L.pay[final_buf]);
@@ -744,6 +748,10 @@ tbe_status tbe_transpose(const tbe_tables* tables, const void* indices, int32_t 
   view->chunk_capacity = L.cap_chunk;
   view->payload_is_position = weighted ? 1 : 0;
   view->radix_passes = L.passes;
+  if (L.dense_on && L.dense_presort) {
+    view->dense_rows = reinterpret_cast<const int32_t*>(ws + L.dense_rows);
+    view->dense_count = reinterpret_cast<const int32_t*>(ws + L.dense_cnt);
+  }
   return st;
 }
 

@@ -1,13 +1,13 @@
 // Long-run gradient accumulation (split into fixed-size chunks) and the
 // backward's update orchestration.
 //
-// PyTorch blog "Modernizing Table Batched Embeddings with FBTriton", section 4,
-// problem 1: a run at or above the threshold becomes fixed 256-lookup chunks,
-// split-K style, so one hot row's work spreads over the whole machine; the
-// chunk partials land in a workspace and a second kernel applies the optimizer
-// (section 3, grad_accum + apply).  Here every chunk writes its own partial
-// row (no atomics), and the apply kernel adds a run's partials in a fixed
-// order, so the result does not depend on scheduling.
+// After PyTorch blog "Modernizing Table Batched Embeddings with FBTriton",
+// section 4 (problem 1) and section 3 (grad_accum, then an apply kernel): a
+// run at or above the threshold is cut into 256-lookup chunks, so that one hot
+// row's lookups are summed by many waves at once, like a split reduction.
+// Here every chunk writes its own fp32 partial row into the workspace (no
+// atomics), and the apply kernel adds a run's partials in a fixed order and
+// steps the optimizer, so the result does not depend on scheduling.
 #include "backward_kernels.h"
 
 namespace tbe {

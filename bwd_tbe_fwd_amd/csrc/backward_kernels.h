@@ -1,14 +1,17 @@
 // Backward gradient reduction and optimizer kernels (templates; instantiated
 // per weight format in backward_f32.hip / backward_f16.hip / backward_bf16.hip).
 //
-// PyTorch blog "Modernizing Table Batched Embeddings with FBTriton", section 3:
-// a short run (SL < 256) is owned start to finish by one program (gather,
-// accumulate in registers, optimizer, plain store, no atomics); a long run is
-// cut into 256-lookup chunks whose partial sums land in a workspace, and a
-// second kernel applies the optimizer.  Weighted tables scale each gradient
-// row by its per-sample weight before accumulating.  Section 4, problem 3:
-// short runs are launched per next_pow2(D) bucket so each bucket uses its own
-// lane count.  The optimizer is the backward's epilogue: SGD (w - lr*g) or
+// Routing after PyTorch blog "Modernizing Table Batched Embeddings with
+// FBTriton", sections 3 and 4 (problem 3).  Here, a run of fewer than 256
+// lookups goes to short_run_kernel, where one lane group reads every gradient
+// row of the run, sums them in registers, runs the optimizer and stores the
+// row: nothing else writes that row, so no atomics are needed.  A run of 256
+// or more is split into 256-lookup chunks: grad_accum_kernel writes one fp32
+// partial row per chunk into the workspace and long_apply_kernel adds a run's
+// partials and steps the optimizer.  With per-sample weights, the kernels
+// multiply a lookup's gradient row by its weight as they add it.  Short runs
+// are launched once per width bucket next_pow2(D), and the bucket fixes how
+// many lanes serve one run.  The optimizer is the backward's epilogue: SGD (w - lr*g) or
 // exact row-wise Adagrad ("Table-Batched Embeddings in Triton", section 5:
 // m += mean_d g_d^2, w -= lr*g/(sqrt(m)+eps) with the new m).
 //

@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "../../include/tbe.h"
+#include "../../include/tbe_measure.h"
 
 namespace tbe {
 

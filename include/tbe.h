@@ -33,6 +33,13 @@
  *  - Limits: 1 <= T; 0 <= B; 4 <= D_t <= 1024 with D_t % 4 == 0;
  *    sum_t E_t < 2^31 - 1 (linearized row ids are 32-bit); number of lookups
  *    <= TBE_MAX_LOOKUPS = 2^31 - 4096; T*B < 2^31.
+ *  - Concurrency: calls on different streams may be made from several host
+ *    threads.  The calls that use the library's second stream
+ *    (tbe_forward_hoisted, and a backward with bwd_streams = 2 or its automatic
+ *    choice) hold one process-wide lock from their fork to their join, that is
+ *    while they enqueue their launches (never while the GPU runs them), so
+ *    such calls from different threads are enqueued one after another; their
+ *    second-stream work then runs in that order.
  *  - Invalid input with bounds checking off: an index outside [0, E_t)
  *    contributes nothing to the forward and nothing to the backward, and no
  *    memory outside the weights is touched; the pages leave this case to an
@@ -94,7 +101,8 @@ typedef struct {
 } tbe_tables;
 
 /*
- * Knobs ("every fix is a config value": blog section 5).  tbe_config_default
+ * Knobs (blog section 5 keeps each tuning choice as a config value rather
+ * than a code path).  tbe_config_default
  * gives the pages' defaults; a NULL config pointer means the defaults.
  */
 typedef struct {
@@ -113,8 +121,9 @@ typedef struct {
   int32_t fused_long;      /* 1: long runs in one launch - each chunk writes its partial, a device-scope
                               fence, then a per-run countdown; the last chunk applies the optimizer
                               (blog section 4, problem 5).  0: chunk kernel + apply kernel (default) */
-  int32_t pretransposed;   /* backward only: 1 = the workspace already holds this batch's transpose,
-                              written by tbe_forward_hoisted; the backward skips its own (default 0) */
+  int32_t pretransposed;   /* backward and tbe_transpose: 1 = the workspace already holds this batch's
+                              transpose, written by tbe_forward_hoisted; the backward skips its own,
+                              tbe_transpose only describes it (default 0) */
   int32_t bags_per_wave;   /* forward: consecutive bags a wave takes per grid step, their offsets read
                               in one load ("bags per program", blog section 2), 1..64; 0 (default):
                               the power of two in [8, 64] that gives every wave about 8 steps */
@@ -161,6 +170,13 @@ typedef struct {
   int64_t short_capacity[TBE_NUM_BUCKETS];
   int32_t payload_is_position;     /* 1 for weighted calls */
   int32_t radix_passes;
+  const int32_t* dense_rows;       /* [T][128] per table its dense rows (local row ids, ascending),
+                                      the first dense_count[t] used, when they are picked before the
+                                      sort (dense_min > 0, unweighted, and dense_presort = 1, or 0
+                                      from 2^26 lookups on); their lookups are in no run.  NULL
+                                      otherwise (no dense rows, or rows picked from the long runs
+                                      by the backward, which stay in long_list) */
+  const int32_t* dense_count;      /* [T], or NULL with dense_rows */
 } tbe_runs_view;
 
 /* Static description of a status code. */
@@ -266,9 +282,9 @@ tbe_status tbe_forward_hoisted(const tbe_tables* tables, const void* weights, vo
 
 /*
  * Bytes of workspace the backward (and tbe_transpose) needs for num_indices
- * lookups; weighted = 1 when per-sample weights will be passed.  Bounded by
- * the index count alone (blog section 4: workspace preallocated to a bound
- * computed from the index count), so no device count is read back.
+ * lookups; weighted = 1 when per-sample weights will be passed.  The size
+ * follows from the lookup count and the table geometry alone (blog section 4:
+ * the run counts stay on the device), so no device count is read back.
  */
 size_t tbe_backward_workspace_bytes(const tbe_tables* tables, int64_t num_indices,
                                     int32_t weighted, const tbe_config* config);
@@ -314,29 +330,17 @@ tbe_status tbe_backward_rowwise_adagrad(const tbe_tables* tables, void* weights,
  * stable radix sort, run-length encoding, long/short routing with D buckets
  * and chunk plan.  Fills *view [host] with device pointers into workspace;
  * nothing is read back.  weighted selects the payload (see tbe_runs_view).
+ * Every table's lookups take part and no dense rows are picked (dense_rows
+ * then lists none).  With config->pretransposed = 1 nothing is launched: the
+ * view describes the transpose that tbe_forward_hoisted left in `workspace`
+ * for the same tables, num_indices, weighted flag and config (the histogram
+ * table's lookups, the dense rows picked before the sort, and, with repair,
+ * an out-of-range id counted as row 0 of its table, as that call leaves them).
  */
 tbe_status tbe_transpose(const tbe_tables* tables, const void* indices, int32_t index_type,
                          const void* offsets, int32_t offset_type, int64_t num_indices,
                          int32_t weighted, void* workspace, size_t workspace_bytes,
                          const tbe_config* config, tbe_runs_view* view, tbe_stream_t stream);
-
-/*
- * Kernel timing for measurement.  tbe_profile_select(name) makes the library
- * record a pair of HIP events on the launch stream around every later launch
- * of the kernel called `name` (NULL stops recording);
- * tbe_profile_read waits for the recorded events and returns the number of
- * timed launches and their total milliseconds, then forgets them.
- */
-tbe_status tbe_profile_select(const char* kernel_name);
-tbe_status tbe_profile_read(int64_t* launches, double* total_ms);
-
-/*
- * Measurement support: copies `bytes` (a multiple of 16, buffers 16-byte aligned)
- * from src to dst with one 16-byte load and store per lane, like the library's
- * kernels.  Its hardware byte counters, for a copy of known size, calibrate the
- * counters read for the other kernels.
- */
-tbe_status tbe_calibration_copy(const void* src, void* dst, int64_t bytes, tbe_stream_t stream);
 
 #ifdef __cplusplus
 }

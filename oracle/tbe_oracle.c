@@ -17,8 +17,9 @@
  *    uses a stable sort of the linearized row id, which fixes the order of
  *    lookups inside a run;
  *  - backward: same blog, section 3 (sum the upstream gradient rows of every
- *    lookup of a run, then exactly one optimizer step per touched row;
- *    weighted tables scale each gradient row by its per-sample weight first);
+ *    lookup of a run, then exactly one optimizer step per touched row; with
+ *    per-sample weights a lookup's gradient row is multiplied by its weight
+ *    before it is added);
  *    SGD as in the blog's backward-pass goal (w - lr*grad); row-wise Adagrad
  *    as in the tutorial's section 5 (one fp32 state per row, state += mean of
  *    g^2 over the row, w -= lr*g/(sqrt(state)+eps), using the new state);

@@ -1,5 +1,7 @@
-"""The C-ABI library loads, exports every symbol include/tbe.h declares, its structs have the
-layout the binding assumes, and host-side validation works - no GPU needed (no kernel runs)."""
+"""The C-ABI library loads, exports every symbol the headers in include/ declare (tbe.h, the
+computation; tbe_measure.h, the measurement hooks), its structs have the layout the binding
+assumes, and host-side validation works - no GPU needed (no kernel runs)."""
+import glob
 import ctypes
 import os
 import re
@@ -12,12 +14,15 @@ import bwd_tbe_fwd_amd as tbe
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "tbe.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
-def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(tbe_[a-z_0-9]+)\s*\(", text)))
+def declared_functions(headers=None):
+    names = set()
+    for h in headers or HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(tbe_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_symbol():
@@ -27,6 +32,16 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(tbe._SIGS), set(names) ^ set(tbe._SIGS)
+    # the product header holds the computation, the measurement hooks live apart
+    measure = set(declared_functions([os.path.join(ROOT, "include", "tbe_measure.h")]))
+    assert measure == {"tbe_profile_select", "tbe_profile_read", "tbe_calibration_copy"}
+    assert not measure & set(declared_functions([HEADER]))
+
+
+def test_headers_compile_as_c(tmp_path):
+    src = tmp_path / "inc.c"
+    src.write_text("".join(f'#include "{h}"\n' for h in HEADERS) + "int main(void) { return 0; }\n")
+    subprocess.check_call(["gcc", "-std=c11", "-Wall", "-Werror", "-o", str(tmp_path / "inc"), str(src)])
 
 
 def test_struct_layout_matches_header(tmp_path):
@@ -36,9 +51,10 @@ def test_struct_layout_matches_header(tmp_path):
 #include <stddef.h>
 #include "{HEADER}"
 int main(void) {{
-  printf("%zu %zu %zu %zu %zu %zu %zu\\n", sizeof(tbe_tables), offsetof(tbe_tables, hist_w_base),
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(tbe_tables), offsetof(tbe_tables, hist_w_base),
          offsetof(tbe_tables, bucket_rows), offsetof(tbe_tables, meta), sizeof(tbe_config),
-         sizeof(tbe_runs_view), offsetof(tbe_runs_view, short_capacity));
+         sizeof(tbe_runs_view), offsetof(tbe_runs_view, short_capacity),
+         offsetof(tbe_runs_view, dense_count));
   return 0;
 }}
 """)
@@ -47,7 +63,8 @@ int main(void) {{
     got = [int(x) for x in subprocess.check_output([str(exe)]).split()]
     exp = [ctypes.sizeof(tbe.tbe_tables), tbe.tbe_tables.hist_w_base.offset,
            tbe.tbe_tables.bucket_rows.offset, tbe.tbe_tables.meta.offset, ctypes.sizeof(tbe.tbe_config),
-           ctypes.sizeof(tbe.tbe_runs_view), tbe.tbe_runs_view.short_capacity.offset]
+           ctypes.sizeof(tbe.tbe_runs_view), tbe.tbe_runs_view.short_capacity.offset,
+           tbe.tbe_runs_view.dense_count.offset]
     assert got == exp
 
 

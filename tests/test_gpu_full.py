@@ -1,6 +1,11 @@
 """Parity at the full workload sizes, in the launch configuration the benchmark times (id
 repair fused into the pooling, the backward's transpose hoisted into the forward call).
 
+Whole tables (test_full_whole_tables): for at least two tables of every workload, including the
+one holding the hottest row, everything is compared against the oracle run on that table's own
+lookups - tables are independent, so this is the oracle's result for the whole batch
+restricted to those tables.
+
 The oracle cannot redo an 84M-lookup batch in seconds, so at these sizes:
   * forward:   sampled bags (random, longest, empty, first/last) are recomputed one by one
                by the oracle from host copies of exactly the rows they touch;
@@ -20,7 +25,8 @@ import torch
 import bwd_tbe_fwd_amd as tbe
 import oracle
 import tbe_inputs as ti
-from gpu_util import ODT, DevBatch, check_forward, check_momentum, check_weights, flush_print, step_bound
+from gpu_util import (ODT, DevBatch, check_forward, check_momentum, check_weights, flush_print,
+                      row_g_abs_sq, step_bound)
 
 pytestmark = pytest.mark.gpu
 
@@ -223,6 +229,161 @@ def test_full_backward_sampled_rows(n):
             check_momentum(mg, res, np.array([D], float), np.array([(res["g_abs"] ** 2).sum()]),
                            f"{n} state ({t},{r})")
     flush_print(f"{n}: {len(samples)} sampled rows and all untouched rows match")
+
+
+# tables compared whole at full size: the one holding the batch's hottest row plus fixed picks
+# (both tables of the histogram workload; one of each width of the mixed workload)
+WHOLE_TABLES = {"uniform": [0, 25], "histogram": [0, 1], "mixed": [0, 5, 10, 15], "skewed": [0, 31]}
+
+
+def _host(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().numpy()
+
+
+def _u32(ptr, n, ws):
+    return tbe.device_view(ptr, n, torch.int32, ws).cpu().numpy().view(np.uint32).astype(np.int64)
+
+
+@pytest.mark.parametrize("n", ["uniform", "histogram", "mixed", "skewed"])
+def test_full_whole_tables(n):
+    """Whole tables at the full workload size, in the benchmark's launch configuration (offsets
+    repair and id check fused into the pooling, the transpose hoisted into the forward call on
+    the second stream with the dense rows picked as the benchmark picks them, the backward
+    reusing it).  For every checked table, against the oracle run on that table's own lookups
+    (tables are independent): every output column of every bag; every touched row's weights
+    and Adagrad state; every untouched row bit for bit; the complete short and long lists (key,
+    length, width bucket) and chunk plan as sets, and each run's payloads in the sorted arrays in
+    the oracle's stable order."""
+    db, h = full_batch(n)
+    bt = db.bt
+    spec = bt.spec
+    T, B, N = bt.T, bt.B, bt.num_indices
+    off, idx = h["off"], h["idx"]
+    weighted = db.psw is not None
+    counts = [np.bincount(idx[off[t * B]:off[(t + 1) * B]], minlength=bt.E[t]) for t in range(T)]
+    hot_t = int(np.argmax([c.max() for c in counts]))
+    chk = sorted(set(WHOLE_TABLES[n]) | {hot_t})
+    rowbase = np.concatenate([[0], np.cumsum(bt.E)]).astype(np.int64)
+    wbase = np.concatenate([[0], np.cumsum(np.array(bt.E, np.int64) * np.array(bt.D, np.int64))])
+    cols = np.concatenate([[0], np.cumsum(bt.D)])
+    W0 = db.W.clone()
+    m0 = None if db.mom is None else db.mom.clone()
+    lr, eps = oracle.f32_literal(spec.lr), oracle.f32_literal(spec.eps)
+    out = torch.full((B, sum(bt.D)), float("nan"), dtype=torch.float32, device="cuda")
+    err_counts = torch.full((2,), -1, dtype=torch.int64, device="cuda")
+    bws = tbe.workspace(tbe.tbe_bounds_check_workspace_bytes(db.tables))
+    ws = db.workspace()
+    tbe.tbe_forward_hoisted(db.tables, db.W, db.idx, db.off, db.psw, out, err_counts, bws, ws)
+    torch.cuda.synchronize()
+    assert err_counts.cpu().tolist() == [0, 0]
+    # the routing the hoisted forward left in the workspace, copied out before the backward
+    view = tbe.tbe_transpose(db.tables, db.idx, db.off, weighted, ws, tbe.make_config(pretransposed=1))
+    cnt = tbe.device_view(view.counters, 16, torch.int32, ws).cpu().numpy()
+    kept = int(cnt[13])
+    keys = _u32(view.sorted_keys, kept, ws)
+    pay = _u32(view.sorted_payload, kept, ws)
+    n_long, n_chunk = int(cnt[tbe.COUNTER_LONG]), int(cnt[tbe.COUNTER_CHUNKS])
+    long_list = _u32(view.long_list, 4 * n_long, ws).reshape(-1, 4)
+    long_table = _u32(view.long_table, n_long, ws)
+    chunk_list = _u32(view.chunk_list, 2 * n_chunk, ws).reshape(-1, 2)
+    shorts = {b: _u32(view.short_list[b], 4 * int(cnt[tbe.COUNTER_SHORT0 + b]), ws).reshape(-1, 4)
+              for b in range(tbe.NUM_BUCKETS) if view.short_list[b]}
+    dense_rows = {}
+    if view.dense_rows:
+        dcnt = tbe.device_view(view.dense_count, T, torch.int32, ws).cpu().numpy()
+        drows = tbe.device_view(view.dense_rows, T * 128, torch.int32, ws).cpu().numpy().reshape(T, 128)
+        dense_rows = {t: drows[t, :dcnt[t]].astype(np.int64) for t in range(T)}
+    cfg = tbe.make_config(pretransposed=1)
+    if spec.optimizer == "sgd":
+        tbe.tbe_backward_sgd(db.tables, db.W, db.idx, db.off, db.psw, db.grad, lr, ws, cfg)
+    else:
+        tbe.tbe_backward_rowwise_adagrad(db.tables, db.W, db.mom, db.idx, db.off, db.psw, db.grad,
+                                         lr, eps, ws, cfg)
+    torch.cuda.synchronize()
+    del ws, bws
+    hist_t = db.tables.c.hist_table if not weighted else -1
+    ada = spec.optimizer == "rowwise_adagrad"
+    opt = oracle.ROWWISE_ADAGRAD if ada else oracle.SGD
+    for t in chk:
+        s, e = int(off[t * B]), int(off[(t + 1) * B])
+        E, D = bt.E[t], bt.D[t]
+        ids = idx[s:e]
+        uniq, local = np.unique(ids, return_inverse=True)
+        U = uniq.size
+        o_t = off[t * B:(t + 1) * B + 1] - s
+        psw = None if h["psw"] is None else h["psw"][s:e]
+        rows_dev = torch.as_tensor(uniq, device="cuda")
+        Wt0 = W0[wbase[t]:wbase[t + 1]].view(E, D)
+        Wt1 = db.W[wbase[t]:wbase[t + 1]].view(E, D)
+        W_sub = Wt0[rows_dev].double().cpu().numpy()
+        # forward: every bag, every column of the table's slice
+        ref, ref_abs = oracle.forward(1, B, [U], [D], W_sub, local, o_t, psw)
+        check_forward(out[:, cols[t]:cols[t + 1]].double().cpu().numpy(), ref, ref_abs,
+                      bt.w_dtype == torch.float32, f"{n} table {t} forward")
+        # backward: every touched row, one oracle step from the table's own lookups
+        g_t = db.grad[:, cols[t]:cols[t + 1]].double().cpu().numpy()
+        m_in = None if m0 is None else m0[rowbase[t]:rowbase[t + 1]][rows_dev].double().cpu().numpy()
+        r = oracle.backward(1, B, [U], [D], ODT[bt.w_dtype], W_sub, local, o_t, psw, g_t, opt, lr, eps, m_in)
+        check_weights(Wt1[rows_dev].reshape(-1).cpu(), r, bt.w_dtype, step_bound(r, [U], [D], lr, eps, ada),
+                      f"{n} table {t} weights")
+        if ada:
+            gsq, Dr = row_g_abs_sq(r, [U], [D])
+            check_momentum(db.mom[rowbase[t]:rowbase[t + 1]][rows_dev], r, Dr, gsq, f"{n} table {t} state")
+        free = torch.from_numpy(counts[t] == 0).cuda()
+        bits = (lambda x: x.view(torch.int32) if x.dtype == torch.float32 else x.view(torch.int16))
+        assert torch.equal(bits(Wt1[free]), bits(Wt0[free])), f"{n} table {t}: untouched rows changed"
+        if m0 is not None:
+            assert torch.equal(db.mom[rowbase[t]:rowbase[t + 1]][free], m0[rowbase[t]:rowbase[t + 1]][free])
+        # routing: the oracle's runs of this table against the GPU lists
+        tr = oracle.transpose(1, B, [U], local, o_t)
+        rk = uniq[tr["run_key"]]                # row id of each run
+        rl = tr["run_len"]
+        lens_all = rl
+        if t == hist_t:
+            # the histogram table's lookups stay out of the sort: no run of it anywhere
+            assert not (long_table == t).any()
+            for lst in shorts.values():
+                assert not (lst[:, 3] == t).any()
+            got_runs = 0
+        else:
+            dn = dense_rows.get(t, np.zeros(0, np.int64))
+            assert np.all(np.isin(dn, rk)), f"{n} table {t}: a dense row with no lookup"
+            keep = ~np.isin(rk, dn)
+            exp_long = {(int(k), int(l)) for k, l in zip(rk[keep], rl[keep]) if l >= 256}
+            exp_short = {(int(k), int(l)) for k, l in zip(rk[keep], rl[keep]) if l < 256}
+            sl_t = long_list[long_table == t]
+            got_long = {(int(k) - int(rowbase[t]), int(l)) for k, l in zip(sl_t[:, 0], sl_t[:, 2])}
+            assert got_long == exp_long, f"{n} table {t}: long runs differ"
+            bucket = tbe.BUCKET_D.index(max(4, 1 << (D - 1).bit_length()))
+            got_short = set()
+            for b, lst in shorts.items():
+                mine = lst[lst[:, 3] == t]
+                assert b == bucket or mine.shape[0] == 0, f"{n} table {t}: short run in bucket {b}"
+                got_short |= {(int(k) - int(rowbase[t]), int(l)) for k, l in zip(mine[:, 0], mine[:, 2])}
+            assert got_short == exp_short, f"{n} table {t}: short runs differ"
+            # chunk plan of every long run
+            for slot in np.flatnonzero(long_table == t):
+                k, st0, ln, cb = (int(x) for x in long_list[slot])
+                nch = (ln + 255) // 256
+                assert np.array_equal(chunk_list[cb:cb + nch], np.stack([np.full(nch, slot), np.arange(nch)], 1))
+            # every run's keys and payloads in the sorted arrays: the oracle's stable order
+            runs = [long_list[long_table == t][:, :3]] + [lst[lst[:, 3] == t][:, :3] for lst in shorts.values()]
+            runs = np.concatenate(runs) if runs else np.zeros((0, 3), np.int64)
+            assert np.array_equal(tr["run_key"], np.arange(U))   # one oracle run per touched row
+            q = np.searchsorted(uniq, runs[:, 0] - rowbase[t])    # the oracle's run of each GPU run
+            ln = runs[:, 2]
+            within = np.arange(int(ln.sum())) - np.repeat(np.cumsum(ln) - ln, ln)
+            gpu_at = np.repeat(runs[:, 1], ln) + within
+            ora_at = np.repeat(tr["run_start"][q], ln) + within
+            assert np.array_equal(keys[gpu_at], np.repeat(runs[:, 0], ln)), f"{n} table {t}: keys"
+            want = (tr["sorted_pos"] + s) if weighted else (tr["sorted_bag"] + t * B)
+            assert np.array_equal(pay[gpu_at], want[ora_at]), f"{n} table {t}: payload order"
+            got_runs = runs.shape[0]
+        long_share = float(lens_all[lens_all >= 256].sum()) / max(1, ids.size)
+        flush_print(f"{n} table {t}: N={ids.size} U={U} max SL={int(lens_all.max()) if U else 0} "
+                    f"long-run share={long_share:.3f} runs in lists={got_runs} "
+                    f"dense rows={dense_rows.get(t, np.zeros(0)).size}")
+    del W0, m0, out
 
 
 def test_max_total_rows():
