@@ -79,6 +79,8 @@ _SIGS = {
                     ctypes.c_int),
     "tbe_forward_repair": ([_P, _P, _P, ctypes.c_int32, _P, ctypes.c_int32, ctypes.c_int64, _P, _P,
                             _P, _P, ctypes.c_size_t, _P, _P], ctypes.c_int),
+    "tbe_forward_repair_noalloc": ([_P, _P, _P, ctypes.c_int32, _P, ctypes.c_int32, ctypes.c_int64,
+                                    _P, _P, _P, _P, _P], ctypes.c_int),
     "tbe_forward_hoisted": ([_P, _P, _P, ctypes.c_int32, _P, ctypes.c_int32, ctypes.c_int64, _P, _P,
                              _P, _P, ctypes.c_size_t, _P, ctypes.c_size_t, _P, _P], ctypes.c_int),
     "tbe_backward_workspace_bytes": ([_P, ctypes.c_int64, ctypes.c_int32, _P], ctypes.c_size_t),
@@ -204,6 +206,19 @@ def tbe_forward_repair(tables: Tables, weights: torch.Tensor, indices: torch.Ten
                                   _ptr(workspace), workspace.numel() * workspace.element_size(),
                                   None if config is None else ctypes.byref(config), _stream(stream))
     _check(st, "tbe_forward_repair")
+
+
+def tbe_forward_repair_noalloc(tables: Tables, weights: torch.Tensor, indices: torch.Tensor,
+                               offsets: torch.Tensor, per_sample_weights: Optional[torch.Tensor],
+                               out: torch.Tensor, error_counts: torch.Tensor,
+                               config: Optional[tbe_config] = None, stream=None):
+    st = lib().tbe_forward_repair_noalloc(tables.ref, _ptr(weights), _ptr(indices),
+                                          _I_DTYPE[indices.dtype], _ptr(offsets),
+                                          _I_DTYPE[offsets.dtype], indices.numel(),
+                                          _ptr(per_sample_weights), _ptr(out), _ptr(error_counts),
+                                          None if config is None else ctypes.byref(config),
+                                          _stream(stream))
+    _check(st, "tbe_forward_repair_noalloc")
 
 
 def tbe_forward_hoisted(tables: Tables, weights: torch.Tensor, indices: torch.Tensor,

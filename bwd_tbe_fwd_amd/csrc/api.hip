@@ -479,20 +479,26 @@ static tbe_status check_bounds_ws(const tbe_tables* tables, const void* workspac
   return TBE_OK;
 }
 
-tbe_status tbe_forward_repair(const tbe_tables* tables, const void* weights, void* indices,
-                              int32_t index_type, void* offsets, int32_t offset_type, int64_t num_indices,
-                              const float* per_sample_weights, float* out, int64_t* error_counts,
-                              void* workspace, size_t workspace_bytes, const tbe_config* config,
-                              tbe_stream_t stream) {
-  g_error[0] = 0;
+static tbe_status check_repair_args(const tbe_tables* tables, const void* weights, void* indices,
+                                    int32_t index_type, void* offsets, int32_t offset_type,
+                                    int64_t num_indices, const float* out, const int64_t* error_counts) {
   if (tbe_status st = check_tables(tables)) return st;
   if (tbe_status st = check_index_args(tables, indices, index_type, offsets, offset_type, num_indices)) return st;
   if (!error_counts) { set_error("error_counts is NULL"); return TBE_ERR_ARG; }
-  if (tbe_status st = check_bounds_ws(tables, workspace, workspace_bytes)) return st;
   if (tables->B > 0) {
     if (tbe_status st = check_rows(weights, "weights", weight_align(tables))) return st;
     if (tbe_status st = check_rows(out, "out", 16)) return st;
   }
+  return TBE_OK;
+}
+
+// tbe_forward_repair once its arguments are checked; workspace holds the offsets repair's
+// block partials (bounds_workspace bytes)
+static tbe_status forward_repair_body(const tbe_tables* tables, const void* weights, void* indices,
+                                      int32_t index_type, void* offsets, int32_t offset_type,
+                                      int64_t num_indices, const float* per_sample_weights, float* out,
+                                      int64_t* error_counts, void* workspace, const tbe_config* config,
+                                      tbe_stream_t stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (tbe_status st = launch_bounds_offsets(tables, offsets, offset_type, num_indices, error_counts,
                                             workspace, s))
@@ -502,6 +508,74 @@ tbe_status tbe_forward_repair(const tbe_tables* tables, const void* weights, voi
   const Config cfg = resolve_config(config);
   IndexArgs ia{indices, index_type, offsets, offset_type, num_indices};
   return forward_body(tables, weights, ia, per_sample_weights, out, error_counts, cfg, nullptr, s);
+}
+
+tbe_status tbe_forward_repair(const tbe_tables* tables, const void* weights, void* indices,
+                              int32_t index_type, void* offsets, int32_t offset_type, int64_t num_indices,
+                              const float* per_sample_weights, float* out, int64_t* error_counts,
+                              void* workspace, size_t workspace_bytes, const tbe_config* config,
+                              tbe_stream_t stream) {
+  g_error[0] = 0;
+  if (tbe_status st = check_repair_args(tables, weights, indices, index_type, offsets, offset_type,
+                                        num_indices, out, error_counts))
+    return st;
+  if (tbe_status st = check_bounds_ws(tables, workspace, workspace_bytes)) return st;
+  return forward_repair_body(tables, weights, indices, index_type, offsets, offset_type, num_indices,
+                             per_sample_weights, out, error_counts, workspace, config, stream);
+}
+
+// ---------------------------------------------------------------------------
+// The entry point that allocates nothing.  The offsets repair's block partials live in a
+// static device array, one copy per GPU, held until the process ends.  In host code the name
+// `scratch` is a host-side stand-in, not device memory: kernels get the address that
+// hipGetSymbolAddress returns for the current device, looked up once per device (its first
+// call there, with that device current) and kept.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) int64_t scratch[TBE_NOALLOC_SCRATCH_BYTES / sizeof(int64_t)];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices] = {};
+}  // namespace
+
+static tbe_status scratch_of_current_device(void** ptr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) {
+    set_error("hipGetDevice failed or device id out of range");
+    return TBE_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      set_error("hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+      return TBE_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return TBE_OK;
+}
+
+tbe_status tbe_forward_repair_noalloc(const tbe_tables* tables, const void* weights, void* indices,
+                                      int32_t index_type, void* offsets, int32_t offset_type,
+                                      int64_t num_indices, const float* per_sample_weights, float* out,
+                                      int64_t* error_counts, const tbe_config* config, tbe_stream_t stream) {
+  g_error[0] = 0;
+  if (tbe_status st = check_repair_args(tables, weights, indices, index_type, offsets, offset_type,
+                                        num_indices, out, error_counts))
+    return st;
+  if (bounds_workspace(tables) > sizeof(scratch)) {
+    set_error("the offsets repair needs %zu bytes of scratch, more than the %zu bytes the library holds",
+              bounds_workspace(tables), sizeof(scratch));
+    return TBE_ERR_WORKSPACE;
+  }
+  void* ws = nullptr;
+  if (tbe_status st = scratch_of_current_device(&ws)) return st;
+  return forward_repair_body(tables, weights, indices, index_type, offsets, offset_type, num_indices,
+                             per_sample_weights, out, error_counts, ws, config, stream);
 }
 
 // ---------------------------------------------------------------------------

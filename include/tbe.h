@@ -253,6 +253,26 @@ tbe_status tbe_forward_repair(const tbe_tables* tables, const void* weights, voi
                               const tbe_config* config, tbe_stream_t stream);
 
 /*
+ * tbe_forward_repair without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments and results as
+ * tbe_forward_repair minus workspace / workspace_bytes: the offsets repair's
+ * block partials live in a static device array of the library,
+ * TBE_NOALLOC_SCRATCH_BYTES (16 KiB) on each GPU, held until the process
+ * ends; a call that would need more returns TBE_ERR_WORKSPACE.  Nothing is
+ * allocated: no hipMalloc, hipFree or allocating library routine.  Every call
+ * on one GPU shares that GPU's array, so calls that overlap on one GPU (on
+ * different streams, or from different threads) race on it and must be
+ * ordered by the caller; calls on different GPUs do not share anything.
+ */
+#define TBE_NOALLOC_SCRATCH_BYTES 16384
+tbe_status tbe_forward_repair_noalloc(const tbe_tables* tables, const void* weights, void* indices,
+                                      int32_t index_type, void* offsets, int32_t offset_type,
+                                      int64_t num_indices, const float* per_sample_weights,
+                                      float* out, int64_t* error_counts, const tbe_config* config,
+                                      tbe_stream_t stream);
+
+/*
  * Forward with the backward's transpose hoisted into it (blog section 2,
  * forward-state reuse and preprocessing; the tutorial's section on forward
  * slower, total faster).  Computes out exactly as tbe_forward
