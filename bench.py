@@ -51,7 +51,15 @@ KERNEL_SOURCES = {
     "radix_upsweep": ["transpose.hip", "tbe_device.h"],
     "radix_downsweep": ["transpose.hip", "tbe_device.h"],
     "bounds_indices": ["bounds.hip", "tbe_device.h"],
+    "bounds_offsets": ["bounds.hip", "tbe_device.h"],
     "hist_bwd_partial": ["hist_backward.hip", "tbe_device.h"],
+    "hist_bwd_apply": ["hist_backward.hip", "tbe_device.h"],
+    "radix_scan": ["transpose.hip", "tbe_device.h"],
+    "rle": ["transpose.hip", "tbe_device.h"],
+    "classify": ["transpose.hip", "tbe_device.h"],
+    "dense_sample": ["dense_backward.hip", "tbe_device.h"],
+    "dense_select": ["dense_backward.hip", "tbe_device.h"],
+    "dense_apply": ["dense_backward.hip", "tbe_device.h"],
 }
 
 
@@ -76,32 +84,211 @@ def all_sources_hash() -> str:
     return h.hexdigest()
 
 
-def measured_step_traffic():
-    """Bytes beyond L2 of one whole step (every kernel, every launch) from the committed
-    counters, scaled by the copy calibration; None if any library source changed since."""
-    path = os.path.join(ROOT, "profiles", "skewed_large_traffic.json")
-    try:
-        with open(path) as f:
-            st = json.load(f)["step"]
-    except (OSError, KeyError, ValueError):
-        return None
-    return st["traffic_bytes"] if st.get("sources_sha256") == all_sources_hash() else None
+# profile summaries in profiles/ are named for the workload they cover
+PROFILE_TAG = {"skewed": "skewed_large", "histogram": "histogram", "mixed": "mixed_width",
+               "uniform": "uniform", "tiny": "tiny"}
 
 
-def measured_traffic(kernel: str):
-    """Bytes beyond L2 per launch from the committed rocprofv3 counters, scaled by the copy
-    calibration; None if there are none or the kernel's sources changed since."""
-    path = os.path.join(ROOT, "profiles", "skewed_large_traffic.json")
+def _traffic_file(workload: str):
+    path = os.path.join(ROOT, "profiles", f"{PROFILE_TAG[workload]}_traffic.json")
     try:
         with open(path) as f:
-            prof = json.load(f)
-        k = prof["kernels"][kernel]
-    except (OSError, KeyError, ValueError):
+            return json.load(f)
+    except (OSError, ValueError):
         return None
+
+
+def measured_step_traffic(workload: str):
+    """Bytes leaving L2 over one whole step (every kernel, every launch) from the committed
+    counters, {"copy_calibrated": FETCH_SIZE / WRITE_SIZE scaled by the copy factors,
+    "by_request_size": read and write requests weighted by their sizes}; None if any library
+    source changed since they were taken."""
+    prof = _traffic_file(workload)
+    if not prof or prof.get("sources_sha256") != all_sources_hash():
+        return None
+    return prof["step"]
+
+
+def measured_traffic(workload: str, kernel: str, launches_per_step: int):
+    """The same per launch of one kernel (its counters summed over a step, divided by its
+    launches per step), plus its L2 hit rate; None if the kernel's sources changed since."""
+    prof = _traffic_file(workload)
+    if not prof or kernel not in prof.get("kernels", {}):
+        return None
+    k = prof["kernels"][kernel]
     if k.get("sources_sha256") != kernel_sources_hash(kernel):
         return None
-    c = prof["calibration"]
-    return (k["fetch_kib"] * c["fetch_factor"] + k["write_kib"] * c["write_factor"]) * 1024
+    n = max(1, launches_per_step)
+    return {"copy_calibrated": k["copy_calibrated_bytes_per_step"] / n,
+            "by_request_size": k["sized_bytes_per_step"] / n,
+            "read_by_request_size": k["sized_read_bytes_per_step"] / n,
+            "write_by_request_size": k["sized_write_bytes_per_step"] / n,
+            "l2_hit_rate": k.get("l2_hit_rate")}
+
+
+# kernel names in rocprofv3 output -> the names bench.py times them under
+def kernel_group(name: str) -> str:
+    n = name.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+    n = n.split("<")[0].split("::")[-1]
+    n = n[:-len("_kernel")] if n.endswith("_kernel") else n
+    for prefix, group in (("rle_", "rle"), ("classify_", "classify"), ("bounds_offsets_", "bounds_offsets")):
+        if n.startswith(prefix):
+            return group
+    return n
+
+
+def _csv_rows(d: str, suffix: str):
+    import csv
+    import glob
+    for f in sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)):
+        with open(f) as fh:
+            yield from csv.DictReader(fh)
+
+
+def _counter_totals(d: str):
+    """{(group, counter): [dispatches, total]} over every dispatch in a --pmc output directory."""
+    tot = {}
+    for row in _csv_rows(d, "counter_collection.csv"):
+        k = (kernel_group(row.get("Kernel_Name", "?")), row["Counter_Name"])
+        a = tot.setdefault(k, [0, 0.0])
+        a[0] += 1
+        a[1] += float(row["Counter_Value"])
+    return tot
+
+
+PROFILE_RUNS = {
+    # name -> rocprofv3 options; every run profiles `python3 bench.py ...` (the workload's flags
+    # appended) with the transpose in the backward call, so that no two kernels overlap
+    "trace": "--kernel-trace --stats",
+    "fetch": "--pmc FETCH_SIZE",
+    "write": "--pmc WRITE_SIZE",
+    "rd": "--pmc TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_32B_sum TCC_EA0_RDREQ_64B_sum TCC_EA0_RDREQ_128B_sum",
+    "wr": "--pmc TCC_EA0_WRREQ_sum TCC_EA0_WRREQ_64B_sum TCC_HIT_sum TCC_MISS_sum",
+}
+PROFILE_STEPS = 3   # counter runs: --steps 2 --warmup 1 --dominant short_run (no per-kernel scan)
+
+
+def profile_commands(workload: str):
+    bench_args = {"trace": f"--workload {workload} --steps 10 --warmup 2 --no-cpu-baseline --hoist off"}
+    cmds = {}
+    for name, opt in PROFILE_RUNS.items():
+        args = bench_args.get(name, f"--workload {workload} --steps 2 --warmup 1 --no-cpu-baseline "
+                                    f"--hoist off --dominant short_run")
+        filt = "" if name == "trace" else " --kernel-include-regex tbe::"
+        cmds[name] = (f"rocprofv3 {opt}{filt} --output-format csv -d gpurun_out/prof/{workload}_{name} "
+                      f"-o run -- python3 bench.py {args}")
+        if name != "trace":
+            cmds["calib_" + name] = (f"rocprofv3 {opt} --kernel-include-regex calibration --output-format csv "
+                                     f"-d gpurun_out/prof/calib_{name} -o run -- python3 bench.py --calib-copy")
+    return cmds
+
+
+def summarize_profiles(root: str, workload: str, out_dir: str = None):
+    """Writes <tag>_kernel_trace.md, <tag>_hbm_counters.md and <tag>_traffic.json (into
+    profiles/ by default) from the rocprofv3 output directories that profile_commands(workload)
+    names, under root."""
+    tag = PROFILE_TAG[workload]
+    out_dir = out_dir or os.path.join(ROOT, "profiles")
+    cmds = profile_commands(workload)
+    d = lambda name: os.path.join(root, f"{workload}_{name}") if not name.startswith("calib") \
+        else os.path.join(root, name)
+    # durations
+    trace = [r for r in _csv_rows(d("trace"), "kernel_stats.csv") if "tbe::" in r["Name"]]
+    # the copy of known size: 1 GiB read and written per launch, 3 launches
+    n_copy = 3
+    copy_b = float(1 << 30)
+    cal = {}
+    for name in ("fetch", "write", "rd", "wr"):
+        for (g, c), (n, v) in _counter_totals(d("calib_" + name)).items():
+            if g == "calibration_copy":
+                cal[c] = v / n
+    fetch_factor = copy_b / (cal["FETCH_SIZE"] * 1024)
+    write_factor = copy_b / (cal["WRITE_SIZE"] * 1024)
+    sized_rd = lambda c: 32 * c["TCC_EA0_RDREQ_32B_sum"] + 64 * c["TCC_EA0_RDREQ_64B_sum"] + 128 * c["TCC_EA0_RDREQ_128B_sum"]
+    sized_wr = lambda c: 32 * (c["TCC_EA0_WRREQ_sum"] - c["TCC_EA0_WRREQ_64B_sum"]) + 64 * c["TCC_EA0_WRREQ_64B_sum"]
+    cal_sized = (sized_rd(cal) / copy_b, sized_wr(cal) / copy_b)
+    per = {}
+    for name in ("fetch", "write", "rd", "wr"):
+        for (g, c), (n, v) in _counter_totals(d(name)).items():
+            per.setdefault(g, {})[c] = v / PROFILE_STEPS        # per step
+            per[g]["dispatches_per_step"] = n / PROFILE_STEPS
+    kernels = {}
+    for g, c in per.items():
+        if not all(k in c for k in ("FETCH_SIZE", "WRITE_SIZE", "TCC_EA0_RDREQ_32B_sum", "TCC_EA0_WRREQ_sum")):
+            continue
+        hit, miss = c.get("TCC_HIT_sum", 0.0), c.get("TCC_MISS_sum", 0.0)
+        kernels[g] = {
+            "dispatches_per_step": c["dispatches_per_step"],
+            "fetch_kib_per_step": c["FETCH_SIZE"], "write_kib_per_step": c["WRITE_SIZE"],
+            "copy_calibrated_bytes_per_step": (c["FETCH_SIZE"] * fetch_factor + c["WRITE_SIZE"] * write_factor) * 1024,
+            "sized_read_bytes_per_step": sized_rd(c), "sized_write_bytes_per_step": sized_wr(c),
+            "sized_bytes_per_step": sized_rd(c) + sized_wr(c),
+            "read_requests_per_step": {"32B": c["TCC_EA0_RDREQ_32B_sum"], "64B": c["TCC_EA0_RDREQ_64B_sum"],
+                                       "128B": c["TCC_EA0_RDREQ_128B_sum"], "all": c["TCC_EA0_RDREQ_sum"]},
+            "l2_hit_rate": hit / (hit + miss) if hit + miss > 0 else None,
+            "sources_sha256": kernel_sources_hash(g) if g in KERNEL_SOURCES else None,
+        }
+    # the benchmark's own copy (its streaming-peak figure) is not part of the step
+    in_step = [k for g, k in kernels.items() if g != "calibration_copy"]
+    step = {"copy_calibrated": sum(k["copy_calibrated_bytes_per_step"] for k in in_step),
+            "by_request_size": sum(k["sized_bytes_per_step"] for k in in_step)}
+    out = {"workload": ti.WORKLOADS[workload].name, "commands": cmds, "steps_counted": PROFILE_STEPS,
+           "calibration": {"copy_bytes": copy_b, "fetch_factor": fetch_factor, "write_factor": write_factor,
+                           "sized_read_over_copy": cal_sized[0], "sized_write_over_copy": cal_sized[1],
+                           "copy_read_requests": {k: cal.get(k) for k in ("TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum",
+                                                                           "TCC_EA0_RDREQ_64B_sum", "TCC_EA0_RDREQ_128B_sum")}},
+           "kernels": kernels, "step": step, "sources_sha256": all_sources_hash()}
+    os.makedirs(out_dir, exist_ok=True)
+    with open(os.path.join(out_dir, f"{tag}_traffic.json"), "w") as f:
+        json.dump(out, f, indent=1)
+    with open(os.path.join(out_dir, f"{tag}_kernel_trace.md"), "w") as f:
+        f.write(f"# Kernel durations, {ti.WORKLOADS[workload].name}\n\n")
+        f.write("Command (from the repository root, with `TMPDIR=/tmp` exported):\n\n    "
+                + cmds["trace"] + "\n\n")
+        f.write(f"{2 + len(KERNELS) + 10} steps traced: 2 warm-up, one per timed kernel name, 10 timed; "
+                "the transpose runs in the backward call (`--hoist off`), so no two kernels overlap. "
+                "Library kernels only, from `run_kernel_stats.csv`.\n\n")
+        f.write("| kernel | calls | average us | total ms | share of GPU time % |\n|---|---|---|---|---|\n")
+        for r in trace:
+            nm = r["Name"].replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+            nm = nm.replace("tbe::", "")
+            f.write(f"| `{nm}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                    f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.2f} |\n")
+    with open(os.path.join(out_dir, f"{tag}_hbm_counters.md"), "w") as f:
+        f.write(f"# Bytes leaving L2, {ti.WORKLOADS[workload].name}\n\n")
+        f.write("Commands (from the repository root, with `TMPDIR=/tmp` exported):\n\n")
+        for k, c in cmds.items():
+            if k != "trace":
+                f.write(f"    {c}\n")
+        f.write(f"\n{PROFILE_STEPS} steps counted (`--steps 2 --warmup 1 --dominant short_run`: no per-kernel "
+                "scan), transpose in the backward call.  Figures are per step, summed over a kernel's "
+                "dispatches (radix passes and the three rle / classify kernels under one name; the pre-sort "
+                "sample's own small sort counts under the radix names).\n\n")
+        f.write("Two byte counts:\n\n"
+                "* copy-calibrated: FETCH_SIZE and WRITE_SIZE scaled by what they read for the library's "
+                f"1 GiB copy (`tbe_calibration_copy`): factors x{fetch_factor:.3f} (fetch) and "
+                f"x{write_factor:.3f} (write).  FETCH_SIZE prices every non-32-byte read request at 64 "
+                "bytes, and the copy issues 128-byte requests, hence the factor;\n"
+                "* by request size: 32 x TCC_EA0_RDREQ_32B + 64 x TCC_EA0_RDREQ_64B + 128 x "
+                "TCC_EA0_RDREQ_128B read, 32 x (TCC_EA0_WRREQ - TCC_EA0_WRREQ_64B) + 64 x "
+                "TCC_EA0_WRREQ_64B written: no fitted factor (on the copy it reads "
+                f"{cal_sized[0]:.3f} x the bytes read and {cal_sized[1]:.3f} x the bytes written).\n\n"
+                "Both count requests leaving L2 towards memory, so reads the 256 MB Infinity Cache "
+                "(MALL) serves are included: they bound HBM traffic from above.  L2 hit rate = "
+                "TCC_HIT / (TCC_HIT + TCC_MISS).\n\n")
+        f.write("| kernel | dispatches / step | FETCH_SIZE KiB | WRITE_SIZE KiB | copy-calibrated GB | "
+                "read by size GB | write by size GB | 32B / 64B / 128B read requests (M) | L2 hit rate |\n"
+                "|---|---|---|---|---|---|---|---|---|\n")
+        for g, k in sorted(kernels.items(), key=lambda kv: -kv[1]["sized_bytes_per_step"]):
+            rq = k["read_requests_per_step"]
+            hr = "" if k["l2_hit_rate"] is None else f"{k['l2_hit_rate']:.3f}"
+            f.write(f"| `{g}` | {k['dispatches_per_step']:.0f} | {k['fetch_kib_per_step']:.0f} | "
+                    f"{k['write_kib_per_step']:.0f} | {k['copy_calibrated_bytes_per_step'] / 1e9:.3f} | "
+                    f"{k['sized_read_bytes_per_step'] / 1e9:.3f} | {k['sized_write_bytes_per_step'] / 1e9:.3f} | "
+                    f"{rq['32B'] / 1e6:.2f} / {rq['64B'] / 1e6:.2f} / {rq['128B'] / 1e6:.2f} | {hr} |\n")
+        f.write(f"| step | | | | {step['copy_calibrated'] / 1e9:.3f} | | | | |\n")
+        f.write(f"\nStep by request size: {step['by_request_size'] / 1e9:.3f} GB.\n")
+    print(f"wrote {out_dir}/{tag}_*: {len(kernels)} kernels, step {step['by_request_size'] / 1e9:.2f} GB by size")
 
 
 def log(*a):
@@ -129,6 +316,9 @@ def batch_stats(bt: ti.Batch, hist_table: int, threshold=256, chunk=256, dense_m
         lg = c >= threshold
         lens = np.diff(off[t * B:(t + 1) * B + 1])
         D = bt.D[t]
+        # bags whose gradient slice a short run / a chunked long run reads at least once
+        cnt_row = np.bincount(lk, minlength=bt.E[t])
+        bag = np.repeat(np.arange(B, dtype=np.int64), lens)
         ok = (dmin > 0 and bt.psw is None and 16 <= D <= 128 and D % 16 == 0 and t != hist_table)
         cand = np.flatnonzero(lg & (c >= dmin)) if ok else np.zeros(0, dtype=np.int64)  # key order
         if cand.size > dense_rows:   # the longest; among equal lengths the smaller keys
@@ -137,7 +327,15 @@ def batch_stats(bt: ti.Batch, hist_table: int, threshold=256, chunk=256, dense_m
         dn = np.zeros(c.size, dtype=bool)
         dn[cand] = True
         gl = lg & ~dn                                                # long runs left to the chunks
+        row_ids = np.flatnonzero(cnt_row)                            # touched rows, as c is ordered
+        row_class = np.zeros(bt.E[t], dtype=np.int8)                 # 1 short, 2 chunked long
+        row_class[row_ids[~lg]] = 1
+        row_class[row_ids[gl]] = 2
+        cls = row_class[lk]
+        short_bags = int(np.unique(bag[cls == 1]).size)
+        long_bags = int(np.unique(bag[cls == 2]).size)
         per.append(dict(D=D, N=int(lk.size), U=int(c.size), hottest=int(c.max()) if c.size else 0,
+                        short_bags=short_bags, long_bags=long_bags,
                         tail=int(np.maximum(lens - 256, 0).sum()),   # lookups past a bag's first 256
                         long_runs=int(lg.sum()), long_lookups=int(c[lg].sum()),
                         short_runs=int((~lg).sum()), short_lookups=int(c[~lg].sum()),
@@ -242,6 +440,56 @@ def algorithmic_bytes(bt: ti.Batch, st: dict, hoist: bool, dense_P: int = 24, pr
             by["fwd_hist"] += B * 64 * 2
             by["hist_bwd_partial"] = p["tail"] * s_i + B * (s_o + 64 * 2 + p["D"] * 4)
     return by
+
+
+def compulsory_bytes(bt: ti.Batch, st: dict, ab: dict, presort: bool = False):
+    """The bytes each kernel, and the whole step, cannot avoid moving: every input byte read once
+    and every output byte written once, with perfect on-chip reuse of anything read twice (a hot
+    weight row, a bag's gradient slice read by several of its runs).  Kernels that read nothing
+    twice (the transpose, the dense and histogram products, the applies) keep their algorithmic
+    bytes `ab`.  Returns (per kernel, step).
+
+    fwd_gather: ids (+ per-sample weights) and offsets once, each touched row once, the output
+    once.  short_run: payloads (+ weights) and descriptors once, the gradient slice of every bag
+    that one of its runs reads, each short-run row read and written once, its state.  grad_accum:
+    payloads once, the gradient slices its chunks read, one partial row written per chunk.
+    Step: ids, offsets and per-sample weights once; the output written once and the upstream
+    gradient read once; every touched row read by the forward and read and written by the
+    backward (separate calls: the rows leave the GPU's caches in between), its state read and
+    written; plus the transpose's and the long runs' own traffic as modelled per kernel."""
+    s_w = bt.weights.element_size()
+    s_i = bt.indices.element_size()
+    s_o = bt.offsets.element_size()
+    s_p = 4 if bt.psw is not None else 0
+    B = bt.B
+    per = st["per_table"]
+    gen = [p for p in per if not p["hist"]]
+    out = dict(ab)
+    out["fwd_gather"] = sum(p["N"] * (s_i + s_p) + p["U"] * p["D"] * s_w + B * (s_o + p["D"] * 4) for p in gen)
+    out["short_run"] = sum(p["short_lookups"] * (4 + s_p) + p["short_runs"] * (16 + 2 * p["D"] * s_w + 8)
+                           + p["short_bags"] * p["D"] * 4 for p in gen)
+    out["grad_accum"] = sum(p["gen_long_lookups"] * (4 + s_p) + p["long_bags"] * p["D"] * 4
+                            + p["gen_chunks"] * (8 + p["D"] * 4) for p in gen)
+    width = sum(bt.D)
+    mom = 8 if bt.spec.optimizer == "rowwise_adagrad" else 0
+    step = (st["N"] * (s_i + s_p) + (st["TB"] + 1) * s_o + 2 * B * width * 4
+            + sum(p["U"] * (3 * p["D"] * s_w + mom) for p in per))
+    # the transpose (linearize's key and payload writes, the radix passes, run-length encoding,
+    # classification, the pre-sort sample) and the long runs' partials (written, then read)
+    passes = radix_passes(sum(bt.E))
+    step += (ab.get("linearize", 0) - st["N"] * s_i - st["TB"] * s_o
+             + passes * (ab.get("radix_downsweep", 0) + ab.get("radix_upsweep", 0))
+             + ab.get("rle", 0) + ab.get("classify", 0) + ab.get("dense_sample", 0)
+             + sum(2 * p["gen_chunks"] * p["D"] * 4 for p in gen))
+    if ab.get("dense_partial"):
+        # the dense path's partials, written and read (its ids or slots and gradient slices are
+        # counted above: the slice once for the step)
+        dp = ab["dense_apply"] - sum(p["dense_rows"] * (2 * p["D"] * s_w + 8) for p in gen)
+        step += 2 * dp + sum(p["N"] * (2 if presort else 0) for p in gen if p["dense_rows"])
+    for p in per:
+        if p["hist"]:   # the small table's saved counts (hoisted forward), written and read
+            step += 2 * B * 64 * 2
+    return out, step
 
 
 def mfma_flops(bt: ti.Batch, st: dict):
@@ -354,7 +602,19 @@ def main():
     ap.add_argument("--calib-copy", action="store_true")
     ap.add_argument("--dominant", default=None,
                     help="kernel to time inside the timed region (skips the one-step-per-kernel scan)")
+    ap.add_argument("--summarize-profiles", metavar="DIR", default=None,
+                    help="write profiles/ summaries of --workload from the rocprofv3 output "
+                         "directories under DIR (see profile_commands) and exit; no GPU needed")
+    ap.add_argument("--profile-commands", action="store_true",
+                    help="print the rocprofv3 commands whose output --summarize-profiles reads")
     args = ap.parse_args()
+    if args.profile_commands:
+        for c in profile_commands(args.workload).values():
+            print(c)
+        return
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles, args.workload)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -449,11 +709,22 @@ def main():
     presort, sample_keys = presort_sample(N) if bt.psw is None else (False, 0)
     ab = algorithmic_bytes(bt, st, args.hoist == "on", dense_P, presort, sample_keys)
     dom_avg_ms = dom_ms / max(launches, 1)
-    dom_bytes = ab.get(dominant, 0)
+    # the byte models give a radix pass's bytes per launch (the passes' average) and every other
+    # kernel's bytes per step (a kernel launched per width bucket covers every table once)
+    per_launch_model = ("radix_downsweep", "radix_upsweep")
+    nl = lambda k: max(1, launches_per_step.get(k, 1))
+    per_launch = lambda m, k: m.get(k, 0) if k in per_launch_model else m.get(k, 0) / nl(k)
+    per_step = lambda m, k: m.get(k, 0) * nl(k) if k in per_launch_model else m.get(k, 0)
+    dom_bytes = per_launch(ab, dominant)
     achieved = dom_bytes / (dom_avg_ms * 1e-3) / 1e9 if dom_avg_ms > 0 else 0.0
-    # every kernel of the step, times its launches per step (radix: one per pass)
-    step_bytes = sum(ab.get(k, 0) * n for k, n in launches_per_step.items())
-    step_traffic = measured_step_traffic() if args.workload == "skewed" else None
+    # every kernel of the step
+    step_bytes = sum(per_step(ab, k) for k in launches_per_step)
+    comp, step_comp = compulsory_bytes(bt, st, ab, presort)
+    dom_comp = per_launch(comp, dominant)
+    traffic = measured_traffic(args.workload, dominant, launches_per_step.get(dominant, 1))
+    step_traffic = measured_step_traffic(args.workload)
+    dom_s = dom_avg_ms * 1e-3
+    step_s = ms_per_step * 1e-3
     res = {
         "metric": METRIC,
         "value": N / (ms_per_step * 1e-3),
@@ -475,17 +746,36 @@ def main():
                             "off": "forward + backward"}[args.bounds]
                    + ("; transpose hoisted into the forward call, concurrent with the pooling on a "
                       "second stream" if args.hoist == "on" else "")},
+        # achieved = the kernel's algorithmic bytes (every lookup's row counted, no credit for
+        # cache reuse) over its event-timed average launch; a model, not HBM throughput
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(dominant) if args.workload == "skewed" else None,
+                     # FETCH_SIZE + WRITE_SIZE per launch, copy-calibrated (profiles/)
+                     "traffic": traffic["copy_calibrated"] if traffic else None,
                      "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_ms": dom_avg_ms,
-                     "launches_timed": launches},
-        "step_algorithmic_GBps": step_bytes / (ms_per_step * 1e-3) / 1e9 if step_bytes else None,
-        # bytes beyond L2 of the whole step (rocprofv3 counters in profiles/, every kernel) over
-        # the step time: the achieved rate the counters see (Infinity-Cache hits included)
-        "step_traffic_GBps": step_traffic / (ms_per_step * 1e-3) / 1e9 if step_traffic else None,
+                     "launches_timed": launches,
+                     # what the kernel cannot avoid moving (each input byte read once, each output
+                     # byte written once), over the same launch time: the bound with headroom
+                     "compulsory_bytes_per_launch": dom_comp,
+                     "compulsory_frac": dom_comp / dom_s / (HBM_PEAK_GBS * 1e9) if dom_s > 0 else None,
+                     # bytes leaving L2 by request size (32/64/128-byte read requests, 32/64-byte
+                     # writes), Infinity-Cache hits included, and the kernel's L2 hit rate
+                     "traffic_by_request_size": traffic["by_request_size"] if traffic else None,
+                     "traffic_frac": traffic["by_request_size"] / dom_s / (HBM_PEAK_GBS * 1e9)
+                     if traffic and dom_s > 0 else None,
+                     "l2_hit_rate": traffic["l2_hit_rate"] if traffic else None,
+                     "traffic_note": "bytes leaving L2 towards memory: reads served by the Infinity "
+                                     "Cache are included, so they bound HBM bytes from above"},
+        "step_algorithmic_GBps": step_bytes / step_s / 1e9 if step_bytes else None,
+        # bytes leaving L2 over the whole step (rocprofv3 counters in profiles/, every kernel)
+        # over the step time, by request size; Infinity-Cache hits included
+        "step_traffic_GBps": step_traffic["by_request_size"] / step_s / 1e9 if step_traffic else None,
         # the whole step's algorithmic bytes at the HBM peak, over the measured step time
-        "step_roofline_frac": step_bytes / (HBM_PEAK_GBS * 1e9) / (ms_per_step * 1e-3) if step_bytes else None,
+        "step_roofline_frac": step_bytes / (HBM_PEAK_GBS * 1e9) / step_s if step_bytes else None,
+        # the step's compulsory bytes (ids, offsets, output and gradient once; touched rows read
+        # by the forward, read and written by the backward; the sort's own passes) at the peak
+        "step_compulsory_GB": step_comp / 1e9,
+        "step_compulsory_frac": step_comp / (HBM_PEAK_GBS * 1e9) / step_s,
         # medians over the timed steps, HIP events around each call (the forward call holds the
         # hoisted transpose)
         "forward_call_ms": fwd_ms, "backward_call_ms": bwd_ms,
@@ -494,7 +784,9 @@ def main():
         # event-timed per kernel, one step each with nothing overlapping (transpose in the backward)
         "kernel_ms_one_step": per_kernel,
         # what each of those kernels must move per launch (no credit for cache reuse), GB
-        "algorithmic_GB_per_launch": {k: ab[k] / 1e9 for k in per_kernel if k in ab},
+        "algorithmic_GB_per_launch": {k: per_launch(ab, k) / 1e9 for k in per_kernel if k in ab},
+        # what each cannot avoid moving per step (perfect on-chip reuse), GB
+        "compulsory_GB_per_step": {k: per_step(comp, k) / 1e9 for k in per_kernel if k in comp},
         # matrix-core kernels: work as issued over their average launch time (one-step scan),
         # against the dense MFMA peak of their operand type
         "mfma_utilisation": {

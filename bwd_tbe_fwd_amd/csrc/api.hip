@@ -91,23 +91,23 @@ int device_cu_count() {
   return cached[dev];
 }
 
-int blocks_per_cu(const void* kernel, size_t dyn_lds) {
+int blocks_per_cu(const void* kernel, size_t dyn_lds, int threads) {
   struct Entry {
     const void* kernel;
     size_t lds;
-    int n;
+    int threads, n;
   };
   static std::mutex mu;
   static std::vector<Entry> cache;
   std::lock_guard<std::mutex> lock(mu);
   for (const auto& e : cache)
-    if (e.kernel == kernel && e.lds == dyn_lds) return e.n;
+    if (e.kernel == kernel && e.lds == dyn_lds && e.threads == threads) return e.n;
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kBlock, dyn_lds) != hipSuccess || n < 1) {
-    (void)hipGetLastError();  // not sticky; fall back to the usual 8 (32 waves)
-    n = 8;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, dyn_lds) != hipSuccess || n < 1) {
+    (void)hipGetLastError();  // not sticky; fall back to 32 waves
+    n = 32 * kWave / threads;
   }
-  cache.push_back(Entry{kernel, dyn_lds, n});
+  cache.push_back(Entry{kernel, dyn_lds, threads, n});
   return n;
 }
 
@@ -282,6 +282,8 @@ BwdLayout bwd_layout(const tbe_tables* tb, int64_t N, int weighted, const Config
     L.bits[p] = bits;
     shift += bits;
   }
+  // the radix passes alternate buffers from buffer 0
+  L.final_buf = L.passes & 1;
   return L;
 }
 
@@ -721,9 +723,9 @@ static tbe_status backward_common(const tbe_tables* tables, void* weights, float
   char* ws = static_cast<char*>(workspace);
   // the small table's rows are updated from per-bag counts x gradient (MFMA) instead of runs
   const int hist = histogram_table(tables, cfg, psw);
-  // pretransposed: tbe_forward_hoisted left the sorted runs in the workspace; the
-  // radix passes alternate buffers starting from buffer 0
-  int final_buf = L.passes & 1;
+  // pretransposed: tbe_forward_hoisted left the sorted runs in the workspace, the sorted
+  // payloads in buffer L.final_buf
+  int final_buf = L.final_buf;
   if (!cfg.pretransposed)
     if (tbe_status st = launch_transpose(tables, ia, psw ? 1 : 0, ws, L, cfg, hist, 0, 1, &final_buf, s)) return st;
   // without dense_presort the dense rows come from the long runs (flags read by the chunk and
@@ -798,9 +800,9 @@ tbe_status tbe_transpose(const tbe_tables* tables, const void* indices, int32_t 
   }
   IndexArgs ia{indices, index_type, offsets, offset_type, num_indices};
   char* ws = static_cast<char*>(workspace);
-  // pretransposed: describe what tbe_forward_hoisted left in the workspace, whose radix
-  // passes alternate buffers starting from buffer 0
-  int final_buf = L.passes & 1;
+  // pretransposed: describe what tbe_forward_hoisted left in the workspace (sorted keys and
+  // payloads in buffer L.final_buf)
+  int final_buf = L.final_buf;
   tbe_status st = TBE_OK;
   if (!cfg.pretransposed)
     st = launch_transpose(tables, ia, weighted ? 1 : 0, ws, L, cfg, -1, 0, 0, &final_buf,

@@ -35,13 +35,13 @@ inline int64_t hmin(int64_t a, int64_t b) { return a < b ? a : b; }
 inline int64_t hmax(int64_t a, int64_t b) { return a > b ? a : b; }
 // Workgroups of kBlock threads of `kernel` one CU holds at once (its registers and
 // LDS, with dyn_lds bytes of dynamic LDS, decide), queried once per kernel and size.
-int blocks_per_cu(const void* kernel, size_t dyn_lds = 0);
+int blocks_per_cu(const void* kernel, size_t dyn_lds = 0, int threads = kBlock);
 // Grid of a grid-stride kernel: every workgroup resident at once (a workgroup that
 // has to wait for a free slot would start its whole share late), at most work_blocks.
 template <typename K>
-int resident_grid(K* kernel, int64_t work_blocks, size_t dyn_lds = 0) {
+int resident_grid(K* kernel, int64_t work_blocks, size_t dyn_lds = 0, int threads = kBlock) {
   const int64_t cap = static_cast<int64_t>(device_cu_count()) *
-                      blocks_per_cu(reinterpret_cast<const void*>(kernel), dyn_lds);
+                      blocks_per_cu(reinterpret_cast<const void*>(kernel), dyn_lds, threads);
   return static_cast<int>(hmax(1, hmin(work_blocks, cap)));
 }
 
@@ -103,6 +103,7 @@ struct BwdLayout {
   int passes;         // radix passes
   int shift[4], bits[4];
   int key_bits;
+  int final_buf;      // key / payload buffer holding the sorted result
 };
 BwdLayout bwd_layout(const tbe_tables* tb, int64_t N, int weighted, const Config& cfg);
 

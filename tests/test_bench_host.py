@@ -1,4 +1,9 @@
-"""Host logic of bench.py: batch statistics and algorithmic bytes on a small batch (CPU)."""
+"""Host logic of bench.py: batch statistics, algorithmic and compulsory bytes on a small batch,
+and the profile summaries from rocprofv3-shaped CSV files (CPU)."""
+import csv
+import json
+import os
+
 import numpy as np
 import torch
 
@@ -121,3 +126,88 @@ def test_presort_sample_and_bytes():
     assert pre["linearize"] == plain["linearize"] + 2 * N and "dense_sample" in pre
     # the dense kernel reads two slot bytes a lookup instead of its 8-byte id
     assert plain["dense_partial"] - pre["dense_partial"] == N * 6
+
+
+def test_compulsory_bytes_by_hand():
+    """Each touched row once, each bag's gradient slice once per kernel, ids and offsets once."""
+    bt = ti.make_batch(_spec(), 8, device="cpu")
+    st = bench.batch_stats(bt, hist_table=0, threshold=20, chunk=8, dense_min=0)
+    ab = bench.algorithmic_bytes(bt, st, hoist=False)
+    comp, step = bench.compulsory_bytes(bt, st, ab)
+    p1 = st["per_table"][1]
+    idx, off = bt.indices.numpy().astype(np.int64), bt.offsets.numpy().astype(np.int64)
+    lk = idx[off[300]:off[600]]
+    bag = np.repeat(np.arange(300), np.diff(off[300:601]))
+    c = np.bincount(lk, minlength=500)
+    short = (c[lk] < 20)
+    assert p1["short_bags"] == np.unique(bag[short]).size and p1["long_bags"] == np.unique(bag[~short]).size
+    assert comp["fwd_gather"] == p1["N"] * 8 + p1["U"] * 32 * 2 + 300 * (8 + 32 * 4)
+    assert comp["short_run"] == (p1["short_lookups"] * 4 + p1["short_runs"] * (16 + 2 * 32 * 2 + 8)
+                                 + p1["short_bags"] * 32 * 4)
+    assert comp["grad_accum"] == p1["gen_long_lookups"] * 4 + p1["long_bags"] * 32 * 4 + p1["gen_chunks"] * (8 + 32 * 4)
+    assert comp["short_run"] < ab["short_run"] and comp["fwd_gather"] < ab["fwd_gather"]
+    assert comp["linearize"] == ab["linearize"] and comp["rle"] == ab["rle"]
+    # the step: ids, offsets, output and gradient once, rows three times (+ state: SGD has none)
+    base = st["N"] * 8 + 601 * 8 + 2 * 300 * 160 * 4 + sum(p["U"] * 3 * p["D"] * 2 for p in st["per_table"])
+    assert step > base and step < base + 10 * st["N"] * 20
+
+
+def test_kernel_groups():
+    g = bench.kernel_group
+    assert g("void tbe::(anonymous namespace)::short_run_kernel<1, 128, 1, 2, 1, false, 4, 2>(float*)") == "short_run"
+    assert g("tbe::(anonymous namespace)::rle_write(unsigned int const*)") == "rle"
+    assert g("void tbe::classify_count(int)") == "classify"
+    assert g("tbe::(anonymous namespace)::bounds_offsets_reduce<long>(long const*)") == "bounds_offsets"
+    assert g("tbe::(anonymous namespace)::radix_downsweep(int)") == "radix_downsweep"
+    assert g("tbe::(anonymous namespace)::calibration_copy_kernel(float4 const*)") == "calibration_copy"
+
+
+def _write_csv(path, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=list(rows[0]))
+        w.writeheader()
+        w.writerows(rows)
+
+
+def test_profile_summaries_from_counter_files(tmp_path):
+    """Counter files shaped like rocprofv3's: bytes by request size need no factor (the copy's
+    1 GiB of 128-byte reads reads back as 1 GiB), FETCH_SIZE is scaled by the copy's factor,
+    per-step figures sum a kernel's dispatches over the counted steps."""
+    root = tmp_path / "prof"
+    K = "void tbe::(anonymous namespace)::short_run_kernel<1, 128>(float*)"
+    C = "tbe::(anonymous namespace)::calibration_copy_kernel(float4 const*)"
+    GiB = 1 << 30
+    def ctr(kernel, values, n):
+        return [{"Kernel_Name": kernel, "Counter_Name": c, "Counter_Value": v}
+                for _ in range(n) for c, v in values.items()]
+    copy = {"fetch": {"FETCH_SIZE": GiB / 2 / 1024}, "write": {"WRITE_SIZE": GiB / 1024},
+            "rd": {"TCC_EA0_RDREQ_sum": GiB / 128, "TCC_EA0_RDREQ_32B_sum": 0, "TCC_EA0_RDREQ_64B_sum": 0,
+                   "TCC_EA0_RDREQ_128B_sum": GiB / 128},
+            "wr": {"TCC_EA0_WRREQ_sum": GiB / 64, "TCC_EA0_WRREQ_64B_sum": GiB / 64, "TCC_HIT_sum": 0,
+                   "TCC_MISS_sum": GiB / 128}}
+    kern = {"fetch": {"FETCH_SIZE": 1000.0}, "write": {"WRITE_SIZE": 100.0},
+            "rd": {"TCC_EA0_RDREQ_sum": 30.0, "TCC_EA0_RDREQ_32B_sum": 10.0, "TCC_EA0_RDREQ_64B_sum": 10.0,
+                   "TCC_EA0_RDREQ_128B_sum": 10.0},
+            "wr": {"TCC_EA0_WRREQ_sum": 8.0, "TCC_EA0_WRREQ_64B_sum": 6.0, "TCC_HIT_sum": 75.0,
+                   "TCC_MISS_sum": 25.0}}
+    for name in ("fetch", "write", "rd", "wr"):
+        _write_csv(str(root / f"calib_{name}" / "host" / "1" / "run_counter_collection.csv"), ctr(C, copy[name], 3))
+        _write_csv(str(root / f"skewed_{name}" / "host" / "2" / "run_counter_collection.csv"),
+                   ctr(K, kern[name], 2 * bench.PROFILE_STEPS))
+    _write_csv(str(root / "skewed_trace" / "host" / "3" / "run_kernel_stats.csv"),
+               [{"Name": K, "Calls": 30, "TotalDurationNs": 9e7, "AverageNs": 3e6, "Percentage": 35.0}])
+    out = tmp_path / "out"
+    bench.summarize_profiles(str(root), "skewed", str(out))
+    j = json.load(open(out / "skewed_large_traffic.json"))
+    cal = j["calibration"]
+    assert abs(cal["fetch_factor"] - 2.0) < 1e-12 and abs(cal["write_factor"] - 1.0) < 1e-12
+    assert abs(cal["sized_read_over_copy"] - 1.0) < 1e-12 and abs(cal["sized_write_over_copy"] - 1.0) < 1e-12
+    k = j["kernels"]["short_run"]
+    assert k["dispatches_per_step"] == 2
+    assert k["sized_read_bytes_per_step"] == 2 * (32 * 10 + 64 * 10 + 128 * 10)
+    assert k["sized_write_bytes_per_step"] == 2 * (32 * 2 + 64 * 6)
+    assert k["copy_calibrated_bytes_per_step"] == 2 * (1000 * 2 + 100) * 1024
+    assert k["l2_hit_rate"] == 0.75
+    assert "short_run" in open(out / "skewed_large_kernel_trace.md").read()
+    assert "| `short_run` |" in open(out / "skewed_large_hbm_counters.md").read()

@@ -52,3 +52,4 @@ def test_random_shapes_every_path(seed):
         idx, off = _inject(bt, it, bad_offsets=repair)
         _assert_same(_step(bt, idx, off, hoisted=False, repair=repair, cfg_kw=kw),
                      _step(bt, idx, off, hoisted=True, repair=repair, cfg_kw=kw))
+
