@@ -194,11 +194,14 @@ void fwd_gather_kernel(
 // by the table held transposed in LDS as the B operand with
 // v_mfma_f32_16x16x16_f16 (fp32 accumulation).  The products count * w are
 // exact in fp32; only the accumulation rounds.  Ids beyond the first 256 of a
-// bag are gathered and added to the tile; the finished 16 x D tile leaves
-// through LDS as 16-byte row-contiguous stores.  With REPAIR, ids outside the
-// table are repaired to 0 in place and counted, as in the gather.  With
-// save_counts, the tile's counts also go to HBM as u16 (bag-major, 64 rows a
-// bag), the forward state the histogram backward reuses.
+// bag are gathered and added to the tile; the finished tile leaves through LDS,
+// 64 columns at a time, as 16-byte row-contiguous stores.  The count area and
+// the output stage share one 16 x 68-word LDS area per wave (the counts are in
+// registers by the time the products are staged), and eight waves share the
+// table, so a CU holds 24 waves.  With REPAIR, ids outside the table are
+// repaired to 0 in place and counted, as in the gather.  With save_counts, the
+// tile's counts also go to HBM as u16 (bag-major, 64 rows a bag), the forward
+// state the histogram backward reuses.
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
@@ -207,35 +210,46 @@ constexpr int kHistCols = 128;  // max D
 constexpr int kHistBags = 16;   // M of one MFMA tile
 constexpr int kHistHead = 256;  // ids per bag counted into the histogram
 constexpr int kHistLoads = 8;   // id loads in flight per lane while counting
+constexpr int kHistWaves = 8;   // waves per workgroup, sharing one copy of the table
+constexpr int kHistThreads = kHistWaves * kWave;
+constexpr int kHistHalf = 64;   // output columns staged at a time
+// LDS strides padded against bank conflicts (32 banks of 4 bytes): a table column holds its
+// 64 rows in 68 halves, so the 16 columns of an MFMA B operand start in 16 different bank
+// pairs; a bag's counts (and a staged output row of 64 columns) take 68 words, so the 16 bags
+// of the A operand spread over the banks and the four row groups of an MFMA result land in
+// two bank halves
+constexpr int kHistWStride = kHistRows + 4;
+constexpr int kHistStride = kHistRows + 4;
 
 template <typename IT, typename OT, bool REPAIR>
-__global__ __launch_bounds__(kBlock) void fwd_hist_kernel(
+__global__ __launch_bounds__(kHistThreads) void fwd_hist_kernel(
     const uint16_t* __restrict__ Wt, IT* __restrict__ indices, const OT* __restrict__ offsets,
     float* __restrict__ out, int64_t bag0, int32_t B, int32_t E, int32_t D, int64_t col_base,
     int32_t out_width, int64_t N, int64_t* __restrict__ counts, uint16_t* __restrict__ save_counts) {
-  __shared__ __align__(16) uint16_t s_wT[kHistCols * kHistRows];            // [col][row]
-  __shared__ __align__(16) float s_tile[kWavesPerBlock][kHistBags * kHistCols];
-  __shared__ int32_t s_off[kWavesPerBlock][kHistBags + 1];
+  __shared__ __align__(16) uint16_t s_wT[kHistCols * kHistWStride];           // [col][row]
+  __shared__ __align__(16) uint32_t s_tile[kHistWaves][kHistBags * kHistStride];
+  __shared__ int32_t s_off[kHistWaves][kHistBags + 1];
   const int lane = lane_id();
   const int w = threadIdx.x >> 6;
-  // the table, read row-major (coalesced, 4 elements a lane) and stored transposed
-  for (int i = threadIdx.x; i < kHistRows * (kHistCols / 4); i += kBlock) {
-    const int row = i / (kHistCols / 4), col = 4 * (i % (kHistCols / 4));
+  // the table (16 KB, once per workgroup), stored transposed: lane l of a wave takes row l,
+  // so neighbouring lanes write neighbouring halves of a column
+  for (int i = threadIdx.x; i < kHistRows * (kHistCols / 4); i += kHistThreads) {
+    const int row = i % kHistRows, col = 4 * (i / kHistRows);
     u32x2 v = {0u, 0u};
     if (row < E && col < D) v = *reinterpret_cast<const u32x2*>(Wt + static_cast<int64_t>(row) * D + col);
-    s_wT[(col + 0) * kHistRows + row] = static_cast<uint16_t>(v.x);
-    s_wT[(col + 1) * kHistRows + row] = static_cast<uint16_t>(v.x >> 16);
-    s_wT[(col + 2) * kHistRows + row] = static_cast<uint16_t>(v.y);
-    s_wT[(col + 3) * kHistRows + row] = static_cast<uint16_t>(v.y >> 16);
+    s_wT[(col + 0) * kHistWStride + row] = static_cast<uint16_t>(v.x);
+    s_wT[(col + 1) * kHistWStride + row] = static_cast<uint16_t>(v.x >> 16);
+    s_wT[(col + 2) * kHistWStride + row] = static_cast<uint16_t>(v.y);
+    s_wT[(col + 3) * kHistWStride + row] = static_cast<uint16_t>(v.y >> 16);
   }
   __syncthreads();
-  uint32_t* cnt = reinterpret_cast<uint32_t*>(s_tile[w]);
-  float* otile = s_tile[w];
+  uint32_t* cnt = s_tile[w];                          // counts [bag][row], then ...
+  float* otile = reinterpret_cast<float*>(s_tile[w]);  // ... the staged output [bag][column - c0]
   int32_t* off = s_off[w];
   int64_t fixed = 0;
   const int64_t tiles = (static_cast<int64_t>(B) + kHistBags - 1) / kHistBags;
-  for (int64_t tile = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + w; tile < tiles;
-       tile += static_cast<int64_t>(gridDim.x) * kWavesPerBlock) {
+  for (int64_t tile = static_cast<int64_t>(blockIdx.x) * kHistWaves + w; tile < tiles;
+       tile += static_cast<int64_t>(gridDim.x) * kHistWaves) {
     const int64_t b0 = tile * kHistBags;
     const int nbag = static_cast<int>(min<int64_t>(kHistBags, B - b0));
     // the 17 offsets of the tile, clamped to [0, N] and made monotone, so that the
@@ -252,10 +266,12 @@ __global__ __launch_bounds__(kBlock) void fwd_hist_kernel(
     const int32_t o0 = read_lane(o, 0);
     const int32_t n = read_lane(o, kHistBags) - o0;
     if (lane <= kHistBags) off[lane] = o - o0;
-    for (int i = lane; i < kHistBags * kHistRows; i += kWave) cnt[i] = 0u;
+    for (int i = lane; i < kHistBags * kHistStride; i += kWave) cnt[i] = 0u;
     __builtin_amdgcn_wave_barrier();
     // each bag's first 256 ids, read as one coalesced range with kHistLoads loads in
-    // flight per lane; an id's bag comes from a 4-step search of the offsets
+    // flight per lane; positions only grow, so a lane's bag search continues from its last
+    // bag (off[16] = n ends it)
+    int bcur = 0;
     for (int32_t j0 = 0; j0 < n; j0 += kHistLoads * kWave) {
       int64_t r[kHistLoads];
 #pragma unroll
@@ -267,10 +283,8 @@ __global__ __launch_bounds__(kBlock) void fwd_hist_kernel(
       for (int u = 0; u < kHistLoads; ++u) {
         const int32_t j = j0 + u * kWave + lane;
         if (j < n) {
-          int b = 0;
-#pragma unroll
-          for (int step = 8; step > 0; step >>= 1)
-            if (off[b + step] <= j) b += step;
+          while (off[bcur + 1] <= j) ++bcur;
+          const int b = bcur;
           if (j - off[b] < kHistHead) {
             int64_t row = r[u];
             if (static_cast<uint64_t>(row) >= static_cast<uint64_t>(E)) {
@@ -282,7 +296,7 @@ __global__ __launch_bounds__(kBlock) void fwd_hist_kernel(
                 row = -1;  // contributes nothing
               }
             }
-            if (row >= 0) atomicAdd(&cnt[b * kHistRows + static_cast<int>(row)], 1u);
+            if (row >= 0) atomicAdd(&cnt[b * kHistStride + static_cast<int>(row)], 1u);
           }
         }
       }
@@ -291,66 +305,73 @@ __global__ __launch_bounds__(kBlock) void fwd_hist_kernel(
     if (save_counts) {  // 16 bags x 64 rows as u16 (the padding bags of the last tile hold zeros)
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
-        const int e = 8 * (k * kWave + lane);
-        const u32x4 c0 = *reinterpret_cast<const u32x4*>(&cnt[e]);
-        const u32x4 c1 = *reinterpret_cast<const u32x4*>(&cnt[e + 4]);
+        const int e = 8 * (k * kWave + lane);  // bag e / 64, rows e % 64 + [0, 8)
+        const int c = (e / kHistRows) * kHistStride + e % kHistRows;
+        const u32x4 c0 = *reinterpret_cast<const u32x4*>(&cnt[c]);
+        const u32x4 c1 = *reinterpret_cast<const u32x4*>(&cnt[c + 4]);
         const u32x4 v = {c0.x | (c0.y << 16), c0.z | (c0.w << 16), c1.x | (c1.y << 16), c1.z | (c1.w << 16)};
         *reinterpret_cast<u32x4*>(save_counts + b0 * kHistRows + e) = v;
       }
     }
-    // A operand: lane l holds bag l%16, rows 16s + 4(l/16) + [0, 4)
+    // A operand: lane l holds bag l%16, rows 16s + 4(l/16) + [0, 4), read 16 bytes at a time
     half4_t a[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const int base = (lane & 15) * kHistRows + 16 * s + 4 * (lane >> 4);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) a[s][q] = static_cast<_Float16>(static_cast<float>(cnt[base + q]));
+      const u32x4 c = *reinterpret_cast<const u32x4*>(&cnt[(lane & 15) * kHistStride + 16 * s + 4 * (lane >> 4)]);
+      a[s][0] = static_cast<_Float16>(static_cast<float>(c.x));
+      a[s][1] = static_cast<_Float16>(static_cast<float>(c.y));
+      a[s][2] = static_cast<_Float16>(static_cast<float>(c.z));
+      a[s][3] = static_cast<_Float16>(static_cast<float>(c.w));
     }
-    __builtin_amdgcn_wave_barrier();
-    for (int nt = 0; nt < D / 16; ++nt) {
-      float4_t acc = {0.f, 0.f, 0.f, 0.f};
+    __builtin_amdgcn_wave_barrier();  // the counts are in registers: the area takes the output
+    for (int c0 = 0; c0 < D; c0 += kHistHalf) {
+      const int nc = min(kHistHalf, D - c0);
+      for (int nt = 0; nt < nc / 16; ++nt) {
+        float4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        // B operand: lane l holds column 16n + l%16, rows 16s + 4(l/16) + [0, 4)
-        const half4_t bf = *reinterpret_cast<const half4_t*>(
-            &s_wT[(16 * nt + (lane & 15)) * kHistRows + 16 * s + 4 * (lane >> 4)]);
-        acc = __builtin_amdgcn_mfma_f32_16x16x16f16(a[s], bf, acc, 0, 0, 0);
-      }
-      // result: lane l holds column 16n + l%16 of bags 4(l/16) + [0, 4)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) otile[(4 * (lane >> 4) + q) * kHistCols + 16 * nt + (lane & 15)] = acc[q];
-    }
-    __builtin_amdgcn_wave_barrier();
-    // ids past the first 256 of a bag: gathered from the LDS copy of the table
-    for (int i = 0; i < nbag; ++i) {
-      const int32_t s = o0 + off[i], e = o0 + off[i + 1];
-      for (int32_t j = s + kHistHead; j < e; ++j) {
-        int64_t r = static_cast<int64_t>(indices[j]);
-        if (static_cast<uint64_t>(r) >= static_cast<uint64_t>(E)) {
-          if constexpr (REPAIR) {
-            __builtin_amdgcn_wave_barrier();
-            if (lane == 0) {
-              indices[j] = 0;
-              ++fixed;
-            }
-            r = 0;
-          } else {
-            continue;
-          }
+        for (int s = 0; s < 4; ++s) {
+          // B operand: lane l holds column c0 + 16n + l%16, rows 16s + 4(l/16) + [0, 4)
+          const half4_t bf = *reinterpret_cast<const half4_t*>(
+              &s_wT[(c0 + 16 * nt + (lane & 15)) * kHistWStride + 16 * s + 4 * (lane >> 4)]);
+          acc = __builtin_amdgcn_mfma_f32_16x16x16f16(a[s], bf, acc, 0, 0, 0);
         }
-        for (int col = lane; col < D; col += kWave)
-          otile[i * kHistCols + col] += static_cast<float>(
-              __builtin_bit_cast(_Float16, s_wT[col * kHistRows + r]));
+        // result: lane l holds column c0 + 16n + l%16 of bags 4(l/16) + [0, 4)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) otile[(4 * (lane >> 4) + q) * kHistStride + 16 * nt + (lane & 15)] = acc[q];
       }
+      __builtin_amdgcn_wave_barrier();
+      // ids past the first 256 of a bag: gathered from the LDS copy of the table (the
+      // repair, and its count, happen on the first column block)
+      for (int i = 0; i < nbag; ++i) {
+        const int32_t s = o0 + off[i], e = o0 + off[i + 1];
+        for (int32_t j = s + kHistHead; j < e; ++j) {
+          int64_t r = static_cast<int64_t>(indices[j]);
+          if (static_cast<uint64_t>(r) >= static_cast<uint64_t>(E)) {
+            if constexpr (REPAIR) {
+              __builtin_amdgcn_wave_barrier();
+              if (lane == 0 && c0 == 0) {
+                indices[j] = 0;
+                ++fixed;
+              }
+              r = 0;
+            } else {
+              continue;
+            }
+          }
+          for (int col = lane; col < nc; col += kWave)
+            otile[i * kHistStride + col] += static_cast<float>(
+                __builtin_bit_cast(_Float16, s_wT[(c0 + col) * kHistWStride + r]));
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      const int c4n = nc / 4;
+      for (int x = lane; x < nbag * c4n; x += kWave) {
+        const int i = x / c4n, c4 = x - i * c4n;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(&otile[i * kHistStride + 4 * c4]);
+        store_f4(out + (b0 + i) * out_width + col_base + c0 + 4 * c4, v);
+      }
+      __builtin_amdgcn_wave_barrier();
     }
-    __builtin_amdgcn_wave_barrier();
-    const int c4n = D / 4;
-    for (int x = lane; x < nbag * c4n; x += kWave) {
-      const int i = x / c4n, c4 = x - i * c4n;
-      const f32x4 v = *reinterpret_cast<const f32x4*>(&otile[i * kHistCols + 4 * c4]);
-      store_f4(out + (b0 + i) * out_width + col_base + 4 * c4, v);
-    }
-    __builtin_amdgcn_wave_barrier();
   }
   if constexpr (REPAIR) {  // one atomic per wave
     for (int msk = 1; msk < kWave; msk <<= 1) fixed += __shfl_xor(fixed, msk);
@@ -423,11 +444,12 @@ template <typename IT, typename OT>
 tbe_status hist_go(const tbe_tables* tb, const void* W, const IndexArgs& ia, float* out,
                    int64_t* repair_counts, uint16_t* save_counts, hipStream_t s) {
   const int64_t tiles = (static_cast<int64_t>(tb->B) + kHistBags - 1) / kHistBags;
-  const int64_t work = (tiles + kWavesPerBlock - 1) / kWavesPerBlock;
+  const int64_t work = (tiles + kHistWaves - 1) / kHistWaves;
   ProfScope ps("fwd_hist", s);
 #define TBE_HIST_LAUNCH(R)                                                                         \
-  hipLaunchKernelGGL((fwd_hist_kernel<IT, OT, R>), dim3(resident_grid(fwd_hist_kernel<IT, OT, R>, work)), \
-                     dim3(kBlock), 0, s,                                                          \
+  hipLaunchKernelGGL((fwd_hist_kernel<IT, OT, R>),                                               \
+                     dim3(resident_grid(fwd_hist_kernel<IT, OT, R>, work, 0, kHistThreads)),      \
+                     dim3(kHistThreads), 0, s,                                                    \
                      static_cast<const uint16_t*>(W) + tb->hist_w_base,                           \
                      const_cast<IT*>(static_cast<const IT*>(ia.indices)),                         \
                      static_cast<const OT*>(ia.offsets), out,                                     \
