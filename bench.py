@@ -32,6 +32,7 @@ METRIC = "TBE fwd+bwd lookups/s and achieved HBM GB/s vs peak, 1 MI355X"
 HBM_PEAK_GBS = 8000.0
 # MI355X dense matrix-core peaks (no sparsity), TFLOP/s
 MFMA_PEAK_TFLOPS = {"fp16": 2500.0, "bf16": 2500.0, "fp32": 157.3}
+MFMA_KERNELS = ("fwd_hist", "hist_bwd_partial", "dense_partial")  # the kernels mfma_flops prices
 KERNELS = ["bounds_offsets", "bounds_indices", "fwd_gather", "fwd_hist", "linearize",
            "radix_upsweep", "radix_scan", "radix_downsweep", "rle", "classify", "short_run",
            "grad_accum", "long_apply", "hist_bwd_partial", "hist_bwd_apply", "dense_sample", "dense_select",
@@ -183,6 +184,29 @@ def profile_commands(workload: str):
     return cmds
 
 
+def mfma_rows(workload: str, trace: list, batch=None):
+    """Matrix-core utilisation of the traced kernels that use MFMA: the workload's batch drawn on
+    the CPU (same seed as on the GPU), its issued flops per launch over the trace's average
+    duration.  {kernel: {dtype, flops_per_launch, average_us, achieved_TFLOPs, peak_TFLOPs, frac}}"""
+    if not any(kernel_group(r["Name"]) in MFMA_KERNELS for r in trace):
+        return {}
+    spec = ti.WORKLOADS[workload]
+    bt = batch if batch is not None else ti.make_batch(spec, device="cpu")
+    tables = tbe.Tables(bt.E, bt.D, bt.B, bt.w_dtype, device="cpu", pooling_hint=spec.pooling_hint)
+    hist_table = tables.c.hist_table if bt.psw is None else -1
+    flops = mfma_flops(bt, batch_stats(bt, hist_table))
+    out = {}
+    for r in trace:
+        g = kernel_group(r["Name"])
+        if g in flops:
+            fl, dt = flops[g]
+            us = float(r["AverageNs"]) / 1e3
+            ach = fl / (us * 1e-6) / 1e12
+            out[g] = {"dtype": dt, "flops_per_launch": fl, "average_us": us, "achieved_TFLOPs": ach,
+                      "peak_TFLOPs": MFMA_PEAK_TFLOPS[dt], "frac": ach / MFMA_PEAK_TFLOPS[dt]}
+    return out
+
+
 def summarize_profiles(root: str, workload: str, out_dir: str = None):
     """Writes <tag>_kernel_trace.md, <tag>_hbm_counters.md and <tag>_traffic.json (into
     profiles/ by default) from the rocprofv3 output directories that profile_commands(workload)
@@ -239,8 +263,6 @@ def summarize_profiles(root: str, workload: str, out_dir: str = None):
                                                                            "TCC_EA0_RDREQ_64B_sum", "TCC_EA0_RDREQ_128B_sum")}},
            "kernels": kernels, "step": step, "sources_sha256": all_sources_hash()}
     os.makedirs(out_dir, exist_ok=True)
-    with open(os.path.join(out_dir, f"{tag}_traffic.json"), "w") as f:
-        json.dump(out, f, indent=1)
     with open(os.path.join(out_dir, f"{tag}_kernel_trace.md"), "w") as f:
         f.write(f"# Kernel durations, {ti.WORKLOADS[workload].name}\n\n")
         f.write("Command (from the repository root, with `TMPDIR=/tmp` exported):\n\n    "
@@ -254,6 +276,18 @@ def summarize_profiles(root: str, workload: str, out_dir: str = None):
             nm = nm.replace("tbe::", "")
             f.write(f"| `{nm}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                     f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.2f} |\n")
+        mf = mfma_rows(workload, trace)
+        if mf:
+            f.write("\nMatrix-core kernels: work as issued (every MFMA tile, zero padding included) over the "
+                    "average duration above, against the dense MFMA peak of the operand type.\n\n")
+            f.write("| kernel | operands | GFLOP per launch | average us | achieved TFLOP/s | peak TFLOP/s | "
+                    "fraction of peak |\n|---|---|---|---|---|---|---|\n")
+            for k, v in mf.items():
+                f.write(f"| `{k}` | {v['dtype']} | {v['flops_per_launch'] / 1e9:.2f} | {v['average_us']:.1f} | "
+                        f"{v['achieved_TFLOPs']:.1f} | {v['peak_TFLOPs']:.1f} | {v['frac']:.4f} |\n")
+    out["mfma_utilisation"] = mf
+    with open(os.path.join(out_dir, f"{tag}_traffic.json"), "w") as f:
+        json.dump(out, f, indent=1)
     with open(os.path.join(out_dir, f"{tag}_hbm_counters.md"), "w") as f:
         f.write(f"# Bytes leaving L2, {ti.WORKLOADS[workload].name}\n\n")
         f.write("Commands (from the repository root, with `TMPDIR=/tmp` exported):\n\n")

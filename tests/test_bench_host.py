@@ -211,3 +211,19 @@ def test_profile_summaries_from_counter_files(tmp_path):
     assert k["l2_hit_rate"] == 0.75
     assert "short_run" in open(out / "skewed_large_kernel_trace.md").read()
     assert "| `short_run` |" in open(out / "skewed_large_hbm_counters.md").read()
+
+
+def test_mfma_rows_histogram():
+    """Matrix-core utilisation from a trace row: the histogram forward issues one 16x16x16 fp16
+    tile product per 16 bags and 16 columns, counts (16 x 64) by table (64 x 128), so
+    131072 bags x 64 x 128 x 2 = 2^31 flops; at 50 us that is 42.9 TFLOP/s of 2500."""
+    K = "void tbe::(anonymous namespace)::fwd_hist_kernel<long, long, true>(unsigned short const*)"
+    rows = [{"Name": K, "Calls": 31, "TotalDurationNs": 31 * 5e4, "AverageNs": 5e4, "Percentage": 9.0},
+            {"Name": "void tbe::(anonymous namespace)::short_run_kernel<1>(float*)", "Calls": 31,
+             "TotalDurationNs": 31 * 1e5, "AverageNs": 1e5, "Percentage": 12.0}]
+    mf = bench.mfma_rows("histogram", rows)
+    assert set(mf) == {"fwd_hist"}
+    assert mf["fwd_hist"]["flops_per_launch"] == 2 ** 31 and mf["fwd_hist"]["dtype"] == "fp16"
+    assert abs(mf["fwd_hist"]["achieved_TFLOPs"] - 2 ** 31 / 5e-5 / 1e12) < 1e-9
+    assert abs(mf["fwd_hist"]["frac"] - 2 ** 31 / 5e-5 / 1e12 / 2500.0) < 1e-12
+    assert bench.mfma_rows("histogram", rows[1:]) == {}
