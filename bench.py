@@ -396,9 +396,23 @@ def presort_sample(N: int):
     return True, 64 * -(-N // S)
 
 
-def radix_passes(total_rows: int):
-    """Radix passes over keys in [0, total_rows] at up to 9 bits a pass."""
-    return -(-max(1, int(total_rows).bit_length()) // 9)
+def radix_passes(total_rows: int, E=None, n_keys: int = 0):
+    """Radix passes over keys in [0, total_rows] at up to 9 bits a pass.  With the tables' rows E
+    and the keys sorted, the library's automatic choice: each table sorted on its own on the bits
+    of its largest local row id when that takes fewer bits, there are at least 2 tables and at
+    most half as many tables as sort blocks (one per 4096-key tile, at most 4096)."""
+    kb = max(1, int(total_rows).bit_length())
+    passes = -(-kb // 9)
+    if E is None or len(E) < 2:
+        return passes
+    lb = max(1, int(max(E) - 1).bit_length())
+    tiles = max(1, -(-int(n_keys) // 4096))
+    want = min(4096, tiles)
+    per = -(-tiles // want)
+    nblk = -(-max(1, int(n_keys)) // (per * 4096))
+    if 2 * len(E) <= nblk and lb < kb and -(-lb // 9) <= passes:
+        return -(-lb // 9)
+    return passes
 
 
 def algorithmic_bytes(bt: ti.Batch, st: dict, hoist: bool, dense_P: int = 24, presort: bool = False,
@@ -419,7 +433,7 @@ def algorithmic_bytes(bt: ti.Batch, st: dict, hoist: bool, dense_P: int = 24, pr
     hst = [p for p in per if p["hist"]]
     runs_N = sum(p["N"] for p in gen)              # keys the sort covers
     U = sum(p["U"] for p in gen)
-    passes = radix_passes(sum(bt.E))
+    passes = radix_passes(sum(bt.E), bt.E, bt.num_indices)
     kept, U_kept = runs_N, U                       # keys and runs past the first radix pass
     if presort:
         kept -= sum(p["dense_lookups"] for p in gen)
@@ -510,7 +524,7 @@ def compulsory_bytes(bt: ti.Batch, st: dict, ab: dict, presort: bool = False):
             + sum(p["U"] * (3 * p["D"] * s_w + mom) for p in per))
     # the transpose (linearize's key and payload writes, the radix passes, run-length encoding,
     # classification, the pre-sort sample) and the long runs' partials (written, then read)
-    passes = radix_passes(sum(bt.E))
+    passes = radix_passes(sum(bt.E), bt.E, bt.num_indices)
     step += (ab.get("linearize", 0) - st["N"] * s_i - st["TB"] * s_o
              + passes * (ab.get("radix_downsweep", 0) + ab.get("radix_upsweep", 0))
              + ab.get("rle", 0) + ab.get("classify", 0) + ab.get("dense_sample", 0)

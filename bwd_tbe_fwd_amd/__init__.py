@@ -36,7 +36,7 @@ class tbe_tables(ctypes.Structure):
                 ("max_D", ctypes.c_int32), ("out_width", ctypes.c_int32),
                 ("all_D_mult8", ctypes.c_int32), ("hist_table", ctypes.c_int32),
                 ("hist_E", ctypes.c_int32), ("hist_D", ctypes.c_int32), ("hist_col", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("hist_w_base", ctypes.c_int64),
+                ("row_bits", ctypes.c_int32), ("hist_w_base", ctypes.c_int64),
                 ("total_rows", ctypes.c_int64), ("total_elems", ctypes.c_int64),
                 ("bucket_rows", ctypes.c_int64 * NUM_BUCKETS), ("meta", ctypes.c_void_p)]
 
@@ -48,7 +48,8 @@ class tbe_config(ctypes.Structure):
                 ("bag_windows", ctypes.c_int32), ("fused_long", ctypes.c_int32),
                 ("pretransposed", ctypes.c_int32), ("bags_per_wave", ctypes.c_int32),
                 ("bwd_streams", ctypes.c_int32), ("tiny_runs", ctypes.c_int32),
-                ("dense_min", ctypes.c_int32), ("dense_presort", ctypes.c_int32)]
+                ("dense_min", ctypes.c_int32), ("dense_presort", ctypes.c_int32),
+                ("sort_by_table", ctypes.c_int32)]
 
 
 class tbe_runs_view(ctypes.Structure):
@@ -60,7 +61,8 @@ class tbe_runs_view(ctypes.Structure):
                 ("long_capacity", ctypes.c_int64), ("chunk_capacity", ctypes.c_int64),
                 ("short_capacity", ctypes.c_int64 * NUM_BUCKETS),
                 ("payload_is_position", ctypes.c_int32), ("radix_passes", ctypes.c_int32),
-                ("dense_rows", ctypes.c_void_p), ("dense_count", ctypes.c_void_p)]
+                ("dense_rows", ctypes.c_void_p), ("dense_count", ctypes.c_void_p),
+                ("sorted_by_table", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 # every symbol the headers in include/ declare, with its ctypes signature

@@ -134,6 +134,7 @@ Config resolve_config(const tbe_config* c) {
   // a dense row is a long run
   r.dense_min = c->dense_min > 0 ? static_cast<int>(hmax(c->dense_min, r.threshold)) : 0;
   r.dense_presort = c->dense_presort > 0 ? 1 : (c->dense_presort < 0 ? -1 : 0);
+  r.sort_by_table = c->sort_by_table > 0 ? 1 : (c->sort_by_table < 0 ? -1 : 0);
   return r;
 }
 
@@ -267,23 +268,37 @@ BwdLayout bwd_layout(const tbe_tables* tb, int64_t N, int weighted, const Config
     L.dense_slot = c.take(static_cast<size_t>(n1) * 2);
     L.hot_bloom = c.take(static_cast<size_t>(kHotBloomWords) * 4);
   }
-  L.counters = c.take(kNumCounters * 4);
-  L.total = c.off;
   // keys are in [0, total_rows]; total_rows itself marks an id outside its table
   uint32_t maxkey = static_cast<uint32_t>(tb->total_rows);
   int kb = 1;
   while (kb < 32 && (maxkey >> kb) != 0) ++kb;
   L.key_bits = kb;
-  L.passes = (kb + kRadixMaxBits - 1) / kRadixMaxBits;
-  int shift = 0;
-  for (int p = 0; p < L.passes; ++p) {
-    const int bits = kb / L.passes + (p < kb % L.passes ? 1 : 0);
-    L.shift[p] = shift;
-    L.bits[p] = bits;
-    shift += bits;
+  auto plan = [](int bits_total, int by_table, RadixPlan& R) {
+    R.passes = (bits_total + kRadixMaxBits - 1) / kRadixMaxBits;
+    int shift = 0;
+    for (int p = 0; p < R.passes; ++p) {
+      const int bits = bits_total / R.passes + (p < bits_total % R.passes ? 1 : 0);
+      R.shift[p] = shift;
+      R.bits[p] = bits;
+      shift += bits;
+    }
+    R.by_table = by_table;
+  };
+  plan(kb, 0, L.sample_radix);
+  L.radix = L.sample_radix;
+  // by table: the local row ids of the largest table in no more passes, at least one sort block
+  // per table and most blocks dealt by keys (at most half as many tables as blocks)
+  const int lb = tb->row_bits > 0 ? tb->row_bits : 1;
+  const bool can_by_table = tb->T >= 2 && 2 * static_cast<int64_t>(tb->T) <= L.nblocks &&
+                            (lb + kRadixMaxBits - 1) / kRadixMaxBits <= L.sample_radix.passes;
+  if (cfg.sort_by_table > 0 ? can_by_table : (cfg.sort_by_table == 0 && can_by_table && lb < kb)) {
+    plan(lb, 1, L.radix);
+    L.tstart = c.take(static_cast<size_t>(2) * (tb->T + 1) * 4);
   }
+  L.counters = c.take(kNumCounters * 4);
+  L.total = c.off;
   // the radix passes alternate buffers from buffer 0
-  L.final_buf = L.passes & 1;
+  L.final_buf = L.radix.passes & 1;
   return L;
 }
 
@@ -365,6 +380,7 @@ void tbe_config_default(tbe_config* cfg) {
   cfg->tiny_runs = 8;
   cfg->dense_min = 1024;
   cfg->dense_presort = 0;
+  cfg->sort_by_table = 0;
 }
 
 int64_t tbe_meta_entries(int32_t T) { return T >= 0 ? static_cast<int64_t>(TBE_META_FIELDS) * (T + 1) : 0; }
@@ -384,10 +400,12 @@ tbe_status tbe_tables_derive(int32_t T, int32_t B, int32_t w_dtype, const int64_
   out->all_D_mult8 = 1;
   int64_t rows = 0, elems = 0, cols = 0;
   int maxD = 0;
+  out->row_bits = 1;
   for (int t = 0; t < T; ++t) {
     const int64_t E = E_host[t];
     const int32_t D = D_host[t];
     if (E < 1) { set_error("table %d has %lld rows", t, (long long)E); return TBE_ERR_ARG; }
+    while (out->row_bits < 32 && ((E - 1) >> out->row_bits) != 0) ++out->row_bits;
     if (D < 4 || D > TBE_MAX_D || D % 4) { set_error("table %d: D=%d not in [4, %d] or not a multiple of 4", t, D, TBE_MAX_D); return TBE_ERR_UNSUPPORTED; }
     meta_host[4 * t + 0] = rows;
     meta_host[4 * t + 1] = elems;
@@ -823,7 +841,8 @@ tbe_status tbe_transpose(const tbe_tables* tables, const void* indices, int32_t 
   view->long_capacity = L.cap_long;
   view->chunk_capacity = L.cap_chunk;
   view->payload_is_position = weighted ? 1 : 0;
-  view->radix_passes = L.passes;
+  view->radix_passes = L.radix.passes;
+  view->sorted_by_table = L.radix.by_table;
   if (L.dense_on && L.dense_presort) {
     view->dense_rows = reinterpret_cast<const int32_t*>(ws + L.dense_rows);
     view->dense_count = reinterpret_cast<const int32_t*>(ws + L.dense_cnt);

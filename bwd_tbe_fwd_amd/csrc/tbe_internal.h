@@ -57,6 +57,7 @@ struct Config {
   int tiny;  // wave steps of short runs of at most this many lookups: half the lanes per run
   int dense_min;  // rows of at least this many lookups (the 128 longest a table) take the dense path (0: off)
   int dense_presort;  // dense rows picked before the sort: 1 always, -1 never, 0 large batches
+  int sort_by_table;  // each table's lookups sorted on their own: 1 when possible, -1 never, 0 auto
 };
 Config resolve_config(const tbe_config* c);
 
@@ -69,6 +70,16 @@ struct SortPlan {
   int64_t seg;        // keys per sort / RLE block (multiple of kRadixTile)
   int nblocks;        // sort / RLE blocks
   int cls_blocks;     // classification blocks
+};
+
+// Radix passes (least-significant digit first): each pass's digit position and width.
+// by_table: each table's keys are sorted on their own, on the bits of the local row id (key -
+// the table's row base); the batch keeps a table's lookups together, so the result is the
+// order of the linearized ids.
+struct RadixPlan {
+  int passes;
+  int shift[4], bits[4];
+  int by_table;
 };
 
 // Workspace carve-up of the backward / transpose (byte offsets, 256-aligned)
@@ -100,8 +111,9 @@ struct BwdLayout {
   int64_t seg;        // keys per sort / RLE block (multiple of kRadixTile)
   int nblocks;        // sort / RLE blocks
   int cls_blocks;     // classification blocks
-  int passes;         // radix passes
-  int shift[4], bits[4];
+  RadixPlan radix;    // the sort of the batch's keys
+  RadixPlan sample_radix;  // the sort of the dense-row sample (always on the linearized ids)
+  size_t tstart;      // by-table sort: 2 x (T + 1) int32, each table's start in a pass's input / output
   int key_bits;
   int final_buf;      // key / payload buffer holding the sorted result
 };

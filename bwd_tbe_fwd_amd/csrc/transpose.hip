@@ -21,9 +21,11 @@
 //    the hashed key set) and every position gets its dense slot.
 //  - sort: reduce-then-scan LSD radix, up to 9 bits a pass (26-bit keys take 3
 //    passes); the first pass leaves the sentinel keys out, and the later
-//    kernels read the kept count from the device.  The dense-row pick sorts
-//    its sample with the same kernels (sort_route).  A fixed number of blocks
-//    each own a contiguous segment; per pass:
+//    kernels read the kept count from the device.  When the largest table needs
+//    fewer bits than the linearized ids, each table's keys are sorted on their
+//    own on local row bits (same order, smaller digits; see the radix section).
+//    The dense-row pick sorts its sample with the same kernels (sort_route).  A
+//    fixed number of blocks each own a contiguous segment; per pass:
 //    upsweep (digit counts per block), a per-digit scan across blocks, and a
 //    downsweep that ranks each 4096-key tile stably in LDS (wave ballots find
 //    the lanes holding the same digit; the lowest lane adds the count), sorts
@@ -232,32 +234,158 @@ __global__ __launch_bounds__(kBlock) void linearize_kernel(
 // ---------------------------------------------------------------------------
 // radix sort
 // ---------------------------------------------------------------------------
+// Two plans share the kernels below.  Global: the keys are sorted on their whole value, and
+// block b owns [b seg, (b + 1) seg) of a pass's input.  BY_TABLE: linearize leaves each table's
+// lookups together, in the batch's table order, and a key of table t is its row base plus the
+// local row, so sorting each table's range on its own, on the bits of the local row, gives the
+// order of the global sort — with fewer bits a pass when the largest table is much smaller
+// than all tables together (2M-row tables of a 64M-row batch: three 7-bit passes instead of
+// three 9-bit ones, so a 4096-key tile holds about 32 keys of a digit instead of 8, written out
+// as longer contiguous pieces).  A pass's blocks are dealt to the tables: table t takes blocks
+// [f(t), f(t + 1)) with f(t) = t + (nblk - T) start_t / n (at least one each, the rest in
+// proportion to the keys), which split the table's range evenly.  The per-digit scan over
+// blocks is the global one; a block of table t derives its digit bases from it, and each
+// table's first block records where the table starts in the pass's output (the next pass's
+// start_t).  start_t must be non-decreasing, start_0 = 0 and start_T = n, the pass's keys.
+
+// f(t): the first block of table t (f(T) = nblk)
+__device__ __forceinline__ int table_first_block(const int32_t* __restrict__ start, int T, int nblk, int t) {
+  if (t >= T) return nblk;
+  const int64_t n = start[T];
+  return t + static_cast<int>(n > 0 ? static_cast<int64_t>(nblk - T) * start[t] / n : 0);
+}
+
+struct TableRange {
+  int t, first, last;  // the block's table and that table's blocks [first, last)
+  int32_t lo, hi;      // the block's keys
+};
+
+__device__ TableRange table_range(const int32_t* __restrict__ start, int T, int nblk, int b) {
+  int lo = 0, hi = T;  // f(lo) <= b < f(hi)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (table_first_block(start, T, nblk, mid) <= b) lo = mid;
+    else hi = mid;
+  }
+  TableRange r;
+  r.t = lo;
+  r.first = table_first_block(start, T, nblk, lo);
+  r.last = table_first_block(start, T, nblk, lo + 1);
+  const int64_t s0 = start[lo], s1 = max(start[lo + 1], start[lo]);
+  const int64_t per = (s1 - s0 + (r.last - r.first) - 1) / (r.last - r.first);
+  const int64_t a = min(s0 + static_cast<int64_t>(b - r.first) * per, s1);
+  r.lo = static_cast<int32_t>(a);
+  r.hi = static_cast<int32_t>(min(a + per, s1));
+  return r;
+}
+
+// BY_TABLE plan, before the first pass: where each table's keys start in linearize's output (the
+// batch's table order, the left-out table's lookups closed up), clamped into [0, n] and made
+// non-decreasing; start[T] = n = N - (the left-out table's lookups), the keys linearize wrote.
+// One workgroup.
+template <typename OT>
+__global__ __launch_bounds__(kBlock) void table_starts_kernel(const OT* __restrict__ offsets, int T, int32_t B,
+                                                             int32_t N, int skip_t, int32_t* __restrict__ start) {
+  __shared__ int32_t s_tmp[kWavesPerBlock];
+  auto at = [&](int64_t i) {
+    return static_cast<int32_t>(min(max(static_cast<int64_t>(offsets[i]), int64_t{0}), static_cast<int64_t>(N)));
+  };
+  int32_t skip_lo = 0, skip_len = 0;
+  if (skip_t >= 0) {
+    skip_lo = at(static_cast<int64_t>(skip_t) * B);
+    skip_len = max(at(static_cast<int64_t>(skip_t + 1) * B), skip_lo) - skip_lo;
+  }
+  const int32_t n = N - skip_len;
+  const int ipt = (T + 1 + kBlock - 1) / kBlock;
+  const int i0 = threadIdx.x * ipt;
+  int32_t run = 0;  // running maximum over this thread's entries
+  for (int q = 0; q < ipt; ++q) {
+    const int t = i0 + q;
+    if (t > T) break;
+    int32_t v = n;
+    if (t == 0) {
+      v = 0;
+    } else if (t < T) {
+      const int32_t p = at(static_cast<int64_t>(t) * B);
+      v = p - min(max(p - skip_lo, 0), skip_len);
+    }
+    run = max(run, v);
+  }
+  // exclusive maximum over the threads before this one (all values are >= 0)
+  const int lane = lane_id(), w = threadIdx.x >> 6;
+  int32_t inc = run;
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int32_t u = __shfl_up(inc, d);
+    if (lane >= d) inc = max(inc, u);
+  }
+  if (lane == kWave - 1) s_tmp[w] = inc;
+  __syncthreads();
+  int32_t pre = __shfl_up(inc, 1);
+  if (lane == 0) pre = 0;
+  for (int k = 0; k < w; ++k) pre = max(pre, s_tmp[k]);
+  run = pre;
+  for (int q = 0; q < ipt; ++q) {
+    const int t = i0 + q;
+    if (t > T) break;
+    int32_t v = n;
+    if (t == 0) {
+      v = 0;
+    } else if (t < T) {
+      const int32_t p = at(static_cast<int64_t>(t) * B);
+      v = p - min(max(p - skip_lo, 0), skip_len);
+    }
+    run = max(run, v);
+    start[t] = t == T ? n : run;
+  }
+}
+
 // drop: a key equal to it is not counted (the first pass leaves out the sentinel keys;
 // later passes pass a value no key has)
+template <bool BY_TABLE>
 __global__ __launch_bounds__(kBlock) void radix_upsweep(const uint32_t* __restrict__ keys, int64_t N,
                                                         const int32_t* __restrict__ n_eff,
                                                         int64_t seg, int shift, int bits, uint32_t drop,
-                                                        uint32_t* __restrict__ hist, int nblk) {
-  if (n_eff) N = min(N, static_cast<int64_t>(*n_eff));
+                                                        uint32_t* __restrict__ hist, int nblk,
+                                                        const int32_t* __restrict__ tstart,
+                                                        const int64_t* __restrict__ meta, int T) {
   __shared__ uint32_t s_cnt[kWavesPerBlock][kRadixDigits];
+  __shared__ int32_t s_rng[3];
   const int lane = lane_id(), w = threadIdx.x >> 6;
   const int ndig = 1 << bits;
   const uint32_t mask = static_cast<uint32_t>(ndig - 1);
   for (int i = lane; i < ndig; i += kWave) s_cnt[w][i] = 0;
-  __builtin_amdgcn_wave_barrier();
-  const int64_t lo = blockIdx.x * seg, hi = min(lo + seg, N);
-  // each wave reads 4 x 256 consecutive keys per step, 16 bytes per lane per load
-  for (int64_t base = lo + w * 16 * kWave; base < hi; base += 16 * kBlock) {
+  int64_t lo, hi;
+  uint32_t rb = 0;  // the row base subtracted before the digit is taken
+  if constexpr (BY_TABLE) {
+    if (threadIdx.x == 0) {
+      const TableRange r = table_range(tstart, T, nblk, blockIdx.x);
+      s_rng[0] = r.t;
+      s_rng[1] = r.lo;
+      s_rng[2] = r.hi;
+    }
+    __syncthreads();
+    rb = static_cast<uint32_t>(meta[4 * s_rng[0]]);
+    lo = s_rng[1];
+    hi = s_rng[2];
+  } else {
+    if (n_eff) N = min(N, static_cast<int64_t>(*n_eff));
+    lo = blockIdx.x * seg;
+    hi = min(lo + seg, N);
+    __builtin_amdgcn_wave_barrier();
+  }
+  // each wave reads 4 x 256 consecutive keys per step, 16 bytes per lane per load, from the
+  // 16-byte boundary at or below lo
+  for (int64_t base = (lo & ~int64_t{3}) + w * 16 * kWave; base < hi; base += 16 * kBlock) {
     uint32_t k[16];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int64_t i = base + s * 4 * kWave + 4 * lane;
-      if (i + 3 < hi) {
+      if (i >= lo && i + 3 < hi) {
         const u32x4 v = *reinterpret_cast<const u32x4*>(keys + i);
         k[4 * s] = v.x; k[4 * s + 1] = v.y; k[4 * s + 2] = v.z; k[4 * s + 3] = v.w;
       } else {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) k[4 * s + q] = i + q < hi ? keys[i + q] : 0u;
+        for (int q = 0; q < 4; ++q) k[4 * s + q] = (i + q >= lo && i + q < hi) ? keys[i + q] : 0u;
       }
     }
     // counts are order-free: one LDS atomic add per key, except where keys repeat.  After the
@@ -271,8 +399,8 @@ __global__ __launch_bounds__(kBlock) void radix_upsweep(const uint32_t* __restri
       bool ok[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        d[q] = (k[4 * s + q] >> shift) & mask;
-        ok[q] = i0 + q < hi && k[4 * s + q] != drop;
+        d[q] = ((k[4 * s + q] - rb) >> shift) & mask;
+        ok[q] = i0 + q >= lo && i0 + q < hi && k[4 * s + q] != drop;
       }
       const bool same4 = ok[0] && ok[1] && ok[2] && ok[3] && d[1] == d[0] && d[2] == d[0] && d[3] == d[0];
       const uint32_t dw = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(d[0])));
@@ -320,14 +448,15 @@ __global__ __launch_bounds__(kBlock) void radix_scan(uint32_t* __restrict__ hist
   if (threadIdx.x == 0) tot[blockIdx.x] = total;
 }
 
+template <bool BY_TABLE>
 __global__ __launch_bounds__(kBlock) void radix_downsweep(
     const uint32_t* __restrict__ kin, const uint32_t* __restrict__ pin, uint32_t* __restrict__ kout,
     uint32_t* __restrict__ pout, int64_t N, const int32_t* __restrict__ n_eff, int64_t seg,
     int shift, int bits, uint32_t drop, const uint32_t* __restrict__ hist, const uint32_t* __restrict__ tot,
-    int nblk, int32_t* __restrict__ n_kept) {
+    int nblk, int32_t* __restrict__ n_kept, const int32_t* __restrict__ tstart,
+    int32_t* __restrict__ tstart_next, const int64_t* __restrict__ meta, int T) {
   // drop: keys equal to it are left out (not ranked, not written); the keys kept, over all
   // blocks, go to *n_kept (block 0), the count every later kernel reads
-  if (n_eff) N = min(N, static_cast<int64_t>(*n_eff));
   __shared__ uint32_t s_base[kRadixDigits];
   __shared__ uint32_t s_wcnt[kWavesPerBlock][kRadixDigits];
   __shared__ uint32_t s_toff[kRadixDigits];
@@ -336,21 +465,63 @@ __global__ __launch_bounds__(kBlock) void radix_downsweep(
   __shared__ uint32_t s_pay[kRadixTile];
   __shared__ uint32_t s_tmp[kWavesPerBlock];
   __shared__ uint32_t s_kept;  // keys of the current tile that are kept
+  __shared__ int32_t s_rng[5];
   const int lane = lane_id(), w = threadIdx.x >> 6;
   const int ndig = 1 << bits;
   const uint32_t mask = static_cast<uint32_t>(ndig - 1);
-  // global base of each digit for this block: digits below + earlier blocks
-  {
-    const int d0 = 2 * threadIdx.x, d1 = d0 + 1;
+  int64_t lo, hi;
+  uint32_t rb = 0;  // the row base subtracted before the digit is taken
+  const int d0 = 2 * threadIdx.x, d1 = d0 + 1;
+  if constexpr (BY_TABLE) {
+    if (threadIdx.x == 0) {
+      const TableRange r = table_range(tstart, T, nblk, blockIdx.x);
+      s_rng[0] = r.t;
+      s_rng[1] = r.first;
+      s_rng[2] = r.last;
+      s_rng[3] = r.lo;
+      s_rng[4] = r.hi;
+    }
+    __syncthreads();
+    const int t = s_rng[0], first = s_rng[1], last = s_rng[2];
+    rb = static_cast<uint32_t>(meta[4 * t]);
+    lo = s_rng[3];
+    hi = s_rng[4];
+    // hist[d][b] holds the keys of digit d in the blocks before b (all tables), tot[d] all of
+    // them.  The table's keys start after the earlier tables' keys, the sum over digits of the
+    // prefix at its first block; its digit d after its keys of smaller digits; this block's
+    // after the table's earlier blocks' keys of digit d.
+    auto col = [&](int d, int b) -> uint32_t {
+      return d < ndig ? (b < nblk ? hist[static_cast<int64_t>(d) * nblk + b] : tot[d]) : 0u;
+    };
+    const uint32_t a0 = col(d0, first), a1 = col(d1, first);
+    const uint32_t c0 = col(d0, last) - a0, c1 = col(d1, last) - a1;  // the table's keys per digit
+    const uint32_t o0 = col(d0, blockIdx.x) - a0, o1 = col(d1, blockIdx.x) - a1;
+    const uint32_t t0 = d0 < ndig ? tot[d0] : 0u, t1 = d1 < ndig ? tot[d1] : 0u;
+    const uint32_t start_out = block_sum(a0 + a1, s_tmp);
+    const uint32_t all = block_sum(t0 + t1, s_tmp);
+    const uint32_t ex = block_exclusive_sum(c0 + c1, s_tmp, nullptr);
+    if (d0 < ndig) s_base[d0] = start_out + ex + o0;
+    if (d1 < ndig) s_base[d1] = start_out + ex + c0 + o1;
+    if (threadIdx.x == 0) {
+      if (static_cast<int>(blockIdx.x) == first) tstart_next[t] = static_cast<int32_t>(start_out);
+      if (blockIdx.x == 0) {
+        tstart_next[T] = static_cast<int32_t>(all);
+        if (n_kept) *n_kept = static_cast<int32_t>(all);
+      }
+    }
+  } else {
+    if (n_eff) N = min(N, static_cast<int64_t>(*n_eff));
+    // global base of each digit for this block: digits below + earlier blocks
     const uint32_t a = d0 < ndig ? tot[d0] : 0u, b = d1 < ndig ? tot[d1] : 0u;
     uint32_t all;
     const uint32_t ex = block_exclusive_sum(a + b, s_tmp, &all);
     if (d0 < ndig) s_base[d0] = ex + hist[static_cast<int64_t>(d0) * nblk + blockIdx.x];
     if (d1 < ndig) s_base[d1] = ex + a + hist[static_cast<int64_t>(d1) * nblk + blockIdx.x];
     if (n_kept && blockIdx.x == 0 && threadIdx.x == 0) *n_kept = static_cast<int32_t>(all);
+    lo = blockIdx.x * seg;
+    hi = min(lo + seg, N);
   }
   __syncthreads();
-  const int64_t lo = blockIdx.x * seg, hi = min(lo + seg, N);
   for (int64_t tile = lo; tile < hi; tile += kRadixTile) {
     for (int i = lane; i < ndig; i += kWave) s_wcnt[w][i] = 0;
     uint32_t k[kRadixItems], p[kRadixItems], r[kRadixItems];
@@ -373,7 +544,7 @@ __global__ __launch_bounds__(kBlock) void radix_downsweep(
 #pragma unroll
     for (int s = 0; s < kRadixItems; ++s) {
       const bool valid = wbase + s * kWave + lane < hi && k[s] != drop;
-      const uint32_t d = (k[s] >> shift) & mask;
+      const uint32_t d = ((k[s] - rb) >> shift) & mask;
       const uint64_t peers = match_digit(d, bits, __ballot(valid));
       const int lead = __ffsll(static_cast<long long>(peers)) - 1;
       base[s] = 0u;
@@ -407,7 +578,7 @@ __global__ __launch_bounds__(kBlock) void radix_downsweep(
 #pragma unroll
     for (int s = 0; s < kRadixItems; ++s) {
       if (wbase + s * kWave + lane < hi && k[s] != drop) {
-        const uint32_t d = (k[s] >> shift) & mask;
+        const uint32_t d = ((k[s] - rb) >> shift) & mask;
         const uint32_t pos = s_toff[d] + s_wcnt[w][d] + r[s];
         s_key[pos] = k[s];
         s_pay[pos] = p[s];
@@ -417,7 +588,7 @@ __global__ __launch_bounds__(kBlock) void radix_downsweep(
     const int kn = static_cast<int>(s_kept);  // the tile's keys, less those dropped
     for (int j = threadIdx.x; j < kn; j += kBlock) {
       const uint32_t key = s_key[j];
-      const uint32_t d = (key >> shift) & mask;
+      const uint32_t d = ((key - rb) >> shift) & mask;
       const uint32_t g = s_base[d] + (static_cast<uint32_t>(j) - s_toff[d]);
       kout[g] = key;
       pout[g] = s_pay[j];
@@ -782,7 +953,9 @@ struct RouteNames {
 constexpr RouteNames kMainNames = {"radix_upsweep", "radix_scan", "radix_downsweep", "rle", "classify"};
 constexpr RouteNames kQuietNames = {"-", "-", "-", "-", "-"};
 
-tbe_status sort_route(const tbe_tables* tb, char* ws, const SortPlan& P, const BwdLayout& L,
+// R.by_table: tstart holds the first pass's table starts (table_starts_kernel) and room for
+// the next pass's
+tbe_status sort_route(const tbe_tables* tb, char* ws, const SortPlan& P, const RadixPlan& R, int32_t* tstart,
                       const int32_t* n_in, uint32_t drop, int threshold, int chunk, const ShortLists& lists,
                       const RouteNames& nm, int* final_buf, hipStream_t s) {
   const int64_t N = P.N;
@@ -794,14 +967,22 @@ tbe_status sort_route(const tbe_tables* tb, char* ws, const SortPlan& P, const B
   int32_t* n_sorted = counters + kSorted;
   tbe_status st;
   int cur = 0;
-  for (int pass = 0; pass < L.passes; ++pass) {
-    const int ndig = 1 << L.bits[pass];
+  const int T = tb->T;
+  for (int pass = 0; pass < R.passes; ++pass) {
+    const int ndig = 1 << R.bits[pass];
     const int32_t* n_p = pass == 0 ? n_in : n_sorted;
     const uint32_t d = pass == 0 ? drop : ~0u;
+    // by table: this pass's table starts, and where the next pass's go
+    const int32_t* ts_in = R.by_table ? tstart + (pass & 1) * (T + 1) : nullptr;
+    int32_t* ts_out = R.by_table ? tstart + ((pass + 1) & 1) * (T + 1) : nullptr;
     {
       ProfScope ps(nm.up, s);
-      hipLaunchKernelGGL(radix_upsweep, dim3(P.nblocks), dim3(kBlock), 0, s, keys[cur], N, n_p, P.seg,
-                         L.shift[pass], L.bits[pass], d, hist, P.nblocks);
+      if (R.by_table)
+        hipLaunchKernelGGL(radix_upsweep<true>, dim3(P.nblocks), dim3(kBlock), 0, s, keys[cur], N, n_p, P.seg,
+                           R.shift[pass], R.bits[pass], d, hist, P.nblocks, ts_in, tb->meta, T);
+      else
+        hipLaunchKernelGGL(radix_upsweep<false>, dim3(P.nblocks), dim3(kBlock), 0, s, keys[cur], N, n_p, P.seg,
+                           R.shift[pass], R.bits[pass], d, hist, P.nblocks, ts_in, tb->meta, T);
     }
     if ((st = check_launch("radix_upsweep"))) return st;
     {
@@ -811,9 +992,14 @@ tbe_status sort_route(const tbe_tables* tb, char* ws, const SortPlan& P, const B
     if ((st = check_launch("radix_scan"))) return st;
     {
       ProfScope ps(nm.down, s);
-      hipLaunchKernelGGL(radix_downsweep, dim3(P.nblocks), dim3(kBlock), 0, s, keys[cur], pay[cur],
-                         keys[cur ^ 1], pay[cur ^ 1], N, n_p, P.seg, L.shift[pass], L.bits[pass], d, hist,
-                         tot, P.nblocks, pass == 0 ? n_sorted : nullptr);
+      if (R.by_table)
+        hipLaunchKernelGGL(radix_downsweep<true>, dim3(P.nblocks), dim3(kBlock), 0, s, keys[cur], pay[cur],
+                           keys[cur ^ 1], pay[cur ^ 1], N, n_p, P.seg, R.shift[pass], R.bits[pass], d, hist,
+                           tot, P.nblocks, pass == 0 ? n_sorted : nullptr, ts_in, ts_out, tb->meta, T);
+      else
+        hipLaunchKernelGGL(radix_downsweep<false>, dim3(P.nblocks), dim3(kBlock), 0, s, keys[cur], pay[cur],
+                           keys[cur ^ 1], pay[cur ^ 1], N, n_p, P.seg, R.shift[pass], R.bits[pass], d, hist,
+                           tot, P.nblocks, pass == 0 ? n_sorted : nullptr, ts_in, ts_out, tb->meta, T);
     }
     if ((st = check_launch("radix_downsweep"))) return st;
     cur ^= 1;
@@ -900,7 +1086,9 @@ tbe_status launch_transpose(const tbe_tables* tb, const IndexArgs& ia, int weigh
       none.cap[b] = 0;
     }
     int fb;
-    if ((st = sort_route(tb, ws, P, L, nullptr, sentinel, L.hot_thr, 1 << 30, none, kQuietNames, &fb, s))) return st;
+    if ((st = sort_route(tb, ws, P, L.sample_radix, nullptr, nullptr, sentinel, L.hot_thr, 1 << 30, none,
+                         kQuietNames, &fb, s)))
+      return st;
     if ((st = launch_dense_select(tb, ws, L, skip_table, s))) return st;
     hot = HotSet{reinterpret_cast<const uint32_t*>(ws + L.hot_bloom),
                  reinterpret_cast<const uint32_t*>(ws + L.hot_set), reinterpret_cast<const uint8_t*>(ws + L.hot_rank),
@@ -946,7 +1134,23 @@ tbe_status launch_transpose(const tbe_tables* tb, const IndexArgs& ia, int weigh
     lists.p[b] = L.cap_short[b] ? reinterpret_cast<uint4*>(ws + L.short_list[b]) : nullptr;
     lists.cap[b] = L.cap_short[b];
   }
-  return sort_route(tb, ws, M, L, n_eff, sentinel, cfg.threshold, cfg.chunk, lists, kMainNames, final_buf, s);
+  int32_t* tstart = nullptr;
+  if (L.radix.by_table) {
+    // each table's first key in linearize's output
+    tstart = reinterpret_cast<int32_t*>(ws + L.tstart);
+    ProfScope ps("table_starts", s);
+    if (ia.otype == TBE_I32)
+      hipLaunchKernelGGL(table_starts_kernel<int32_t>, dim3(1), dim3(kBlock), 0, s,
+                         static_cast<const int32_t*>(ia.offsets), tb->T, tb->B, static_cast<int32_t>(N),
+                         skip_table, tstart);
+    else
+      hipLaunchKernelGGL(table_starts_kernel<int64_t>, dim3(1), dim3(kBlock), 0, s,
+                         static_cast<const int64_t*>(ia.offsets), tb->T, tb->B, static_cast<int32_t>(N),
+                         skip_table, tstart);
+    if ((st = check_launch("table_starts"))) return st;
+  }
+  return sort_route(tb, ws, M, L.radix, tstart, n_eff, sentinel, cfg.threshold, cfg.chunk, lists, kMainNames,
+                    final_buf, s);
 }
 
 }  // namespace tbe

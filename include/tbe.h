@@ -91,7 +91,7 @@ typedef struct {
   int32_t hist_E;            /* rows of that table */
   int32_t hist_D;            /* width of that table */
   int32_t hist_col;          /* its first output column */
-  int32_t reserved;
+  int32_t row_bits;          /* bits of the largest local row id, max_t E_t - 1 (at least 1) */
   int64_t hist_w_base;       /* its first element in the weight buffer */
   int64_t total_rows;        /* sum_t E_t: linearized row ids are [0, total_rows) */
   int64_t total_elems;       /* sum_t E_t * D_t: elements of the weight buffer */
@@ -148,6 +148,12 @@ typedef struct {
                               near the cut may fall either way, and their lookups stay out of
                               the sort; -1 = they are the long runs of >= dense_min lookups after
                               the sort; 0 (default): 1 from 2^26 lookups on, else -1 */
+  int32_t sort_by_table;   /* backward transpose: 1 = each table's lookups are sorted on their own,
+                              on the bits of the local row id (the batch keeps a table's lookups
+                              together, so the order is the same as sorting the linearized ids);
+                              -1 = one sort of the linearized ids; 0 (default): by table when the
+                              largest table needs fewer bits than the linearized ids, there are at
+                              least 2 tables and at most half as many tables as sort blocks */
 } tbe_config;
 
 /* Device-side view of the transpose, for inspection by tests (tbe_transpose). */
@@ -177,6 +183,10 @@ typedef struct {
                                       otherwise (no dense rows, or rows picked from the long runs
                                       by the backward, which stay in long_list) */
   const int32_t* dense_count;      /* [T], or NULL with dense_rows */
+  int32_t sorted_by_table;         /* 1: each table's lookups were sorted on their own, on the bits
+                                      of the local row id (tbe_config.sort_by_table); the result is
+                                      the same order */
+  int32_t reserved;
 } tbe_runs_view;
 
 /* Static description of a status code. */

@@ -51,10 +51,11 @@ def test_struct_layout_matches_header(tmp_path):
 #include <stddef.h>
 #include "{HEADER}"
 int main(void) {{
-  printf("%zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(tbe_tables), offsetof(tbe_tables, hist_w_base),
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(tbe_tables), offsetof(tbe_tables, hist_w_base),
          offsetof(tbe_tables, bucket_rows), offsetof(tbe_tables, meta), sizeof(tbe_config),
          sizeof(tbe_runs_view), offsetof(tbe_runs_view, short_capacity),
-         offsetof(tbe_runs_view, dense_count));
+         offsetof(tbe_runs_view, dense_count), offsetof(tbe_runs_view, sorted_by_table),
+         offsetof(tbe_config, sort_by_table), offsetof(tbe_tables, row_bits));
   return 0;
 }}
 """)
@@ -64,7 +65,8 @@ int main(void) {{
     exp = [ctypes.sizeof(tbe.tbe_tables), tbe.tbe_tables.hist_w_base.offset,
            tbe.tbe_tables.bucket_rows.offset, tbe.tbe_tables.meta.offset, ctypes.sizeof(tbe.tbe_config),
            ctypes.sizeof(tbe.tbe_runs_view), tbe.tbe_runs_view.short_capacity.offset,
-           tbe.tbe_runs_view.dense_count.offset]
+           tbe.tbe_runs_view.dense_count.offset, tbe.tbe_runs_view.sorted_by_table.offset,
+           tbe.tbe_config.sort_by_table.offset, tbe.tbe_tables.row_bits.offset]
     assert got == exp
 
 
@@ -73,6 +75,7 @@ def test_tables_derive_host_logic():
                    pooling_hint=[10, 128, 30, 100])
     c = t.c
     assert (c.T, c.B, c.max_D, c.out_width) == (4, 512, 1024, 32 + 128 + 256 + 1024)
+    assert c.row_bits == 22  # the largest local row id, 3999999, takes 22 bits
     assert c.total_rows == 100 + 64 + 4_000_000 + 7
     assert c.total_elems == 100 * 32 + 64 * 128 + 4_000_000 * 256 + 7 * 1024
     assert c.hist_table == 1 and c.hist_E == 64 and c.hist_D == 128 and c.hist_col == 32

@@ -111,6 +111,11 @@ def test_presort_sample_and_bytes():
     on, k = bench.presort_sample(83_897_668)
     assert on and k == 64 * -(-83_897_668 // 8192) and k <= 2 ** 20
     assert bench.radix_passes(64_000_000) == 3 and bench.radix_passes(511) == 1
+    # by table: 32 tables of 2M rows (21 bits, three passes either way); 32 tables of 2^17 rows
+    # take two passes instead of three once there are 64 sort blocks
+    assert bench.radix_passes(64_000_000, [2_000_000] * 32, 84_000_000) == 3
+    assert bench.radix_passes(32 << 17, [1 << 17] * 32, 64 * 4096) == 2
+    assert bench.radix_passes(32 << 17, [1 << 17] * 32, 63 * 4096) == 3
     tables = (ti.TableSpec(300, 128, ("fixed", 40)), ti.TableSpec(64, 64, ("fixed", 40)))
     bt = ti.make_batch(ti.BatchSpec("presort bytes", tables, B=1000, w_dtype=torch.float16,
                                     w_range=0.05), 7, device="cpu")

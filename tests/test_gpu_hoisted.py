@@ -175,3 +175,23 @@ def test_hoisted_workspace_holds_latest_batch():
     ref = _step(bt2, bt2.indices.numpy(), bt2.offsets.numpy(), hoisted=False, repair=False)
     assert torch.equal(W.cpu().view(torch.int16), ref["W"].view(torch.int16))
     assert torch.equal(mom.cpu(), ref["mom"])
+
+
+@pytest.mark.parametrize("name,kw", [("histogram", dict(B=20000)),
+                                     ("skewed", dict(B=3000, E_div=400, T=8)),
+                                     ("mixed", dict(B=1500, E_div=50))])
+@pytest.mark.parametrize("repair", [False, True])
+def test_by_table_sort_same_step(name, kw, repair):
+    """A whole step whose sort takes each table on its own (sort_by_table = 1) equals the step
+    with one sort of the linearized ids bit for bit, hoisted and plain, with out-of-range ids
+    (dropped from the sort, or repaired to row 0 with broken offsets repaired too), the
+    histogram table left out of the sort, and dense rows picked before the sort."""
+    spec = ti.scaled(ti.WORKLOADS[name], **kw)
+    bt = ti.make_batch(spec, 93)
+    flush_print(f"by-table step {name} {kw} repair={repair} N={bt.num_indices}")
+    idx, off = _inject(bt, 13, bad_offsets=repair)
+    base = dict(long_threshold=32, chunk=16, dense_min=64, dense_presort=1)
+    one = _step(bt, idx, off, hoisted=False, repair=repair, cfg_kw=dict(base, sort_by_table=-1))
+    for hoisted in (False, True):
+        by = _step(bt, idx, off, hoisted=hoisted, repair=repair, cfg_kw=dict(base, sort_by_table=1))
+        _assert_same(one, by)

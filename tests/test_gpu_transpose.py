@@ -131,3 +131,47 @@ def test_transpose_tutorial_batch_statistics():
         assert int(cnt[tbe.COUNTER_SHORT0:tbe.COUNTER_SHORT0 + tbe.NUM_BUCKETS].sum()) == row["short"]
         assert int(cnt[tbe.COUNTER_CHUNKS]) == row["chunks"]
         assert int(cnt[tbe.COUNTER_RUNS]) == gold["unique_rows"]
+
+
+BY_TABLE_CASES = [("skewed", dict(B=3000, E_div=400, T=8), False),
+                  ("skewed", dict(B=3000, E_div=400, T=8), True),
+                  ("uniform", dict(B=2000, E_div=100, T=6), False),
+                  ("mixed", dict(B=1500, E_div=50), True)]
+
+
+@pytest.mark.parametrize("name,kw,weighted", BY_TABLE_CASES)
+def test_transpose_by_table(name, kw, weighted):
+    """Each table's lookups sorted on their own, on the bits of the local row id
+    (sort_by_table = 1): the oracle's transpose bit for bit with the automatic, 64 and the
+    maximum number of sort blocks (table boundaries inside blocks' ranges, tables of very
+    different sizes), and the same as one sort of the linearized ids."""
+    bt = ti.make_batch(ti.scaled(ti.WORKLOADS[name], **kw), 21)
+    flush_print(f"by table {name} {kw} weighted={weighted} N={bt.num_indices}")
+    for blocks in (0, 64, 4096):
+        cfg = tbe.make_config(sort_by_table=1, sort_blocks=blocks)
+        g, _ = check_transpose(bt, weighted, cfg, what=f"{name} by table, {blocks} blocks")
+        assert g["view"].sorted_by_table == 1
+    g, _ = check_transpose(bt, weighted, tbe.make_config(sort_by_table=-1), what=f"{name} one sort")
+    assert g["view"].sorted_by_table == 0
+
+
+def test_transpose_by_table_edges():
+    """By table with an empty table first and one in the middle, a one-row table and the
+    largest table setting the passes (2^21 rows: three 7-bit passes against 22 bits of
+    linearized ids).  Out-of-range ids, whose lookups leave the sort, are covered by the whole
+    steps in test_gpu_hoisted."""
+    tables = (ti.TableSpec(5000, 64, ("fixed", 0)),
+              ti.TableSpec(1, 64, ("poisson", 3.0, None, None)),
+              ti.TableSpec(1 << 21, 128, ("poisson", 12.0, None, None), ("zipf", 1.05, 20000)),
+              ti.TableSpec(700, 64, ("fixed", 0)),
+              ti.TableSpec(300_000, 32, ("poisson", 6.0, None, None)),
+              ti.TableSpec(9000, 64, ("poisson", 20.0, 1, 60)))
+    spec = ti.BatchSpec("by-table edges", tables, B=4000, w_dtype=torch.float16, w_range=0.05,
+                        optimizer="sgd", seed=77)
+    bt = ti.make_batch(spec)
+    flush_print(f"by table edges N={bt.num_indices}")
+    for w in (False, True):
+        g, _ = check_transpose(bt, w, tbe.make_config(sort_by_table=1), what=f"edges weighted={w}")
+        assert g["view"].sorted_by_table == 1 and g["view"].radix_passes == 3
+    g, _ = check_transpose(bt, False, tbe.make_config(), what="edges automatic")
+    assert g["view"].sorted_by_table == 1
