@@ -175,3 +175,24 @@ def test_transpose_by_table_edges():
         assert g["view"].sorted_by_table == 1 and g["view"].radix_passes == 3
     g, _ = check_transpose(bt, False, tbe.make_config(), what="edges automatic")
     assert g["view"].sorted_by_table == 1
+
+
+def test_transpose_by_table_many_tables():
+    """By table over 600 tables of 300 .. 30000 rows (the table starts of the first pass scanned
+    three to a thread, a block's table found among hundreds), with empty tables among them, in
+    two passes where the linearized ids need three: the oracle's transpose bit for bit."""
+    rng = np.random.default_rng(3)
+    tables = []
+    for t in range(600):
+        E = int(rng.integers(300, 30000))
+        L = ("fixed", 0) if t % 97 == 5 else ("poisson", float(rng.integers(4, 30)), None, None)
+        idx = ("zipf", 1.05, min(E, 500)) if t % 3 == 0 else ("uniform",)
+        tables.append(ti.TableSpec(E, 32, L, idx))
+    spec = ti.BatchSpec("600 tables", tuple(tables), B=700, w_dtype=torch.float16, w_range=0.05,
+                        optimizer="sgd", seed=41)
+    bt = ti.make_batch(spec)
+    flush_print(f"600 tables N={bt.num_indices}")
+    assert bt.num_indices >= 2 * 600 * 4096
+    g, _ = check_transpose(bt, False, tbe.make_config(), what="600 tables")
+    # automatic: 15 bits of the largest local row id take 2 passes, 24 bits of linearized ids 3
+    assert g["view"].sorted_by_table == 1 and g["view"].radix_passes == 2
