@@ -692,8 +692,9 @@ def main():
     if bt.momentum is None:
         bt.momentum = torch.zeros(sum(bt.E), dtype=torch.float32, device=dev)
 
-    def step(hoist=args.hoist == "on", events=None):
-        bcfg = tbe.make_config(pretransposed=1) if hoist else None
+    def step(hoist=args.hoist == "on", events=None, one_stream=False):
+        # one_stream: the backward on one stream (bwd_streams = 1), so that no kernel shares the GPU
+        bcfg = tbe.make_config(pretransposed=1 if hoist else 0, bwd_streams=1 if one_stream else 0)
         if events:
             events[0].record()
         if args.bounds == "standalone":
@@ -721,11 +722,12 @@ def main():
         step()
     torch.cuda.synchronize()
     # which kernel dominates: one profiled step per kernel (outside the timed region), with the
-    # transpose in the backward call so that no two kernels overlap and each time is its own
+    # transpose in the backward call and the backward on one stream, so that no two kernels
+    # overlap and each time is its own
     per_kernel, launches_per_step = {}, {}
     for k in ([] if args.dominant else KERNELS):
         tbe.tbe_profile_select(k)
-        step(hoist=False)
+        step(hoist=False, one_stream=True)
         n, ms = tbe.tbe_profile_read()
         if n:
             per_kernel[k] = ms
@@ -751,10 +753,14 @@ def main():
     bwd_ms = float(np.median([b.elapsed_time(c) for _, b, c in ev]))
     N = st["N"]
     # the dense path writes one partial per workgroup; its kernel holds 3 workgroups per CU and
-    # launches one round of them over the tables
+    # launches one round of them over the tables, or one workgroup per CU when it runs beside the
+    # short runs (the library's automatic backward when the dense rows are picked before the
+    # sort and every table's width falls in one short-run bucket)
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
-    dense_P = max(1, min(64, 2048 // bt.T, (bt.B + 63) // 64, cus * 3 // bt.T))
     presort, sample_keys = presort_sample(N) if bt.psw is None else (False, 0)
+    buckets = len({max(4, 1 << max(0, int(d) - 1).bit_length()) for d in bt.D})
+    beside = presort and buckets == 1 and any(p["dense_rows"] for p in st["per_table"])
+    dense_P = max(1, min(64, 2048 // bt.T, (bt.B + 63) // 64, cus * (1 if beside else 3) // bt.T))
     ab = algorithmic_bytes(bt, st, args.hoist == "on", dense_P, presort, sample_keys)
     dom_avg_ms = dom_ms / max(launches, 1)
     # the byte models give a radix pass's bytes per launch (the passes' average) and every other
@@ -812,6 +818,13 @@ def main():
                      "traffic_frac": traffic["by_request_size"] / dom_s / (HBM_PEAK_GBS * 1e9)
                      if traffic and dom_s > 0 else None,
                      "l2_hit_rate": traffic["l2_hit_rate"] if traffic else None,
+                     # the dense rows' kernel on the second stream during the short runs (one
+                     # workgroup per CU): its bytes and the two kernels' bytes over this launch time
+                     "beside": ({"kernel": "dense_partial",
+                                 "algorithmic_bytes_per_launch": per_launch(ab, "dense_partial"),
+                                 "combined_frac": (dom_bytes + per_launch(ab, "dense_partial")) / dom_s
+                                 / (HBM_PEAK_GBS * 1e9)}
+                                if beside and dominant == "short_run" and dom_s > 0 else None),
                      "traffic_note": "bytes leaving L2 towards memory: reads served by the Infinity "
                                      "Cache are included, so they bound HBM bytes from above"},
         "step_algorithmic_GBps": step_bytes / step_s / 1e9 if step_bytes else None,
@@ -829,7 +842,8 @@ def main():
         "forward_call_ms": fwd_ms, "backward_call_ms": bwd_ms,
         "forward_lookups_per_s": N / (fwd_ms * 1e-3), "backward_lookups_per_s": N / (bwd_ms * 1e-3),
         "copy_peak_GBps": copy_peak_gbps(),
-        # event-timed per kernel, one step each with nothing overlapping (transpose in the backward)
+        # event-timed per kernel, one step each with nothing overlapping (transpose in the backward,
+        # backward on one stream)
         "kernel_ms_one_step": per_kernel,
         # what each of those kernels must move per launch (no credit for cache reuse), GB
         "algorithmic_GB_per_launch": {k: per_launch(ab, k) / 1e9 for k in per_kernel if k in ab},

@@ -91,6 +91,24 @@ int device_cu_count() {
   return cached[dev];
 }
 
+int kernel_vgprs(const void* kernel) {
+  struct Entry {
+    const void* kernel;
+    int n;
+  };
+  static std::mutex mu;
+  static std::vector<Entry> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const auto& e : cache)
+    if (e.kernel == kernel) return e.n;
+  hipFuncAttributes a;
+  int n = 0;
+  if (hipFuncGetAttributes(&a, kernel) == hipSuccess && a.numRegs > 0) n = a.numRegs;
+  else (void)hipGetLastError();  // not sticky; unknown: 0
+  cache.push_back(Entry{kernel, n});
+  return n;
+}
+
 int blocks_per_cu(const void* kernel, size_t dyn_lds, int threads) {
   struct Entry {
     const void* kernel;
@@ -135,6 +153,7 @@ Config resolve_config(const tbe_config* c) {
   r.dense_min = c->dense_min > 0 ? static_cast<int>(hmax(c->dense_min, r.threshold)) : 0;
   r.dense_presort = c->dense_presort > 0 ? 1 : (c->dense_presort < 0 ? -1 : 0);
   r.sort_by_table = c->sort_by_table > 0 ? 1 : (c->sort_by_table < 0 ? -1 : 0);
+  r.short_reserve = 0;
   return r;
 }
 
@@ -762,6 +781,23 @@ static tbe_status backward_common(const tbe_tables* tables, void* weights, float
   int buckets = 0;
   for (int b = 0; b < TBE_NUM_BUCKETS; ++b) buckets += L.cap_short[b] > 0;
   const int streams = cfg.bwd_streams ? cfg.bwd_streams : (buckets >= 2 ? 2 : 1);
+  if (cfg.bwd_streams == 0 && streams < 2 && L.dense_on && L.dense_presort) {
+    // the dense rows' kernels (matrix cores and LDS counting) on the second stream, launched
+    // first with one workgroup per CU, beside the short runs (bound by gradient-row reads),
+    // whose grid leaves that workgroup's registers free; the long runs follow the short runs
+    // (disjoint rows throughout)
+    Fork fork(s);
+    if (tbe_status st = fork.status()) return st;
+    tbe_status st = launch_dense_backward(tables, weights, momentum, opt, ia, grad_out, lr, eps, ws, L,
+                                          fork.side(), 1);
+    Config c2 = cfg;
+    c2.short_reserve = (dense_partial_vgprs() + 7) / 8 * 8;
+    if (!st)
+      st = launch_backward_update(tables, weights, momentum, opt, psw, grad_out, lr, eps, ws, L, final_buf, c2,
+                                  s, s);
+    const tbe_status st_j = fork.join();
+    return st ? st : st_j;
+  }
   if (streams < 2 || L.cap_long == 0) {
     if (tbe_status st = launch_backward_update(tables, weights, momentum, opt, psw, grad_out, lr, eps, ws,
                                                L, final_buf, cfg, s, s))

@@ -19,17 +19,24 @@ constexpr int short_chunks(int BD, bool tiny) {
   return (tiny && BD >= 64 && BD <= 256) ? 2 : np;
 }
 
+// reserve > 0: the grid leaves that many vector registers of every SIMD lane free (for a kernel
+// on another stream); a workgroup is one wave on each of a CU's four SIMDs
 template <int DT, int BD, int OPT, bool WEIGHTED>
 tbe_status short_go(void* W, float* momentum, const float* psw, const float* grad_out,
                     const uint32_t* pay, const uint32_t* bag_of, const uint4* list,
                     const int32_t* count, int tiny, int64_t cap, const tbe_tables* tb,
-                    float lr, float eps, hipStream_t s) {
+                    float lr, float eps, int reserve, hipStream_t s) {
   using S = typename Fmt<DT>::S;
   constexpr int NPS = short_chunks(BD, false), NPT = short_chunks(BD, true);
   constexpr int RPW = 2 * kWave / (BD / (4 * NPS));  // runs per wave step
   const int64_t waves = (cap + RPW - 1) / RPW;
   const auto kernel = short_run_kernel<DT, BD, NPS, NPT, OPT, WEIGHTED, kShortUnroll, kTinyUnroll>;
-  const int grid = resident_grid(kernel, (waves + kWavesPerBlock - 1) / kWavesPerBlock);
+  int grid = resident_grid(kernel, (waves + kWavesPerBlock - 1) / kWavesPerBlock);
+  const int regs = (kernel_vgprs(reinterpret_cast<const void*>(kernel)) + 7) / 8 * 8;
+  if (reserve > 0 && regs > 0) {
+    const int fit = hmax(1, (512 - reserve) / regs);
+    grid = static_cast<int>(hmin(grid, static_cast<int64_t>(device_cu_count()) * fit));
+  }
   ProfScope ps("short_run", s);
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(kBlock), 0, s,
                      static_cast<S*>(W), momentum, grad_out, pay, bag_of, psw, list, count, cap, tiny,
@@ -41,8 +48,8 @@ template <int DT, int OPT, bool WEIGHTED>
 tbe_status short_bucket(int b, void* W, float* momentum, const float* psw, const float* grad_out,
                         const uint32_t* pay, const uint32_t* bag_of, const uint4* list,
                         const int32_t* count, int tiny, int64_t cap,
-                        const tbe_tables* tb, float lr, float eps, hipStream_t s) {
-#define TBE_SB(BD) short_go<DT, BD, OPT, WEIGHTED>(W, momentum, psw, grad_out, pay, bag_of, list, count, tiny, cap, tb, lr, eps, s)
+                        const tbe_tables* tb, float lr, float eps, int reserve, hipStream_t s) {
+#define TBE_SB(BD) short_go<DT, BD, OPT, WEIGHTED>(W, momentum, psw, grad_out, pay, bag_of, list, count, tiny, cap, tb, lr, eps, reserve, s)
   switch (b) {
     case 0: return TBE_SB(4);
     case 1: return TBE_SB(8);
@@ -113,7 +120,8 @@ tbe_status launch_short_and_apply(const tbe_tables* tb, void* W, float* momentum
     const int64_t cap = L.cap_short[b];
     const int32_t* cnt = counters + kShort0 + b;
 #define TBE_SHORT(OPT, WTD) \
-  detail::short_bucket<DT, OPT, WTD>(b, W, momentum, psw, grad_out, pay, bag_of, list, cnt, cfg.tiny, cap, tb, lr, eps, s)
+  detail::short_bucket<DT, OPT, WTD>(b, W, momentum, psw, grad_out, pay, bag_of, list, cnt, cfg.tiny, cap, tb, lr, eps, \
+                                     cfg.short_reserve, s)
     const tbe_status st = opt == kOptSGD ? (psw ? TBE_SHORT(kOptSGD, true) : TBE_SHORT(kOptSGD, false))
                                          : (psw ? TBE_SHORT(kOptAdagrad, true) : TBE_SHORT(kOptAdagrad, false));
 #undef TBE_SHORT

@@ -636,13 +636,19 @@ tbe_status launch_dense_select_runs(const tbe_tables* tb, char* ws, const BwdLay
   return check_launch("dense_select");
 }
 
+int dense_partial_vgprs() {
+  return kernel_vgprs(reinterpret_cast<const void*>(dense_partial_kernel<int64_t, int64_t, true>));
+}
+
 tbe_status launch_dense_backward(const tbe_tables* tb, void* W, float* momentum, int opt,
                                  const IndexArgs& ia, const float* grad_out, float lr, float eps,
-                                 char* ws, const BwdLayout& L, hipStream_t s) {
+                                 char* ws, const BwdLayout& L, hipStream_t s, int wgs_per_cu) {
   // partials per table: as many workgroups as the GPU holds at once over all tables (one
-  // round, no tail), at most the workspace's dense_P
-  const int64_t resident = static_cast<int64_t>(device_cu_count()) *
-                           blocks_per_cu(reinterpret_cast<const void*>(dense_partial_kernel<int64_t, int64_t, false>));
+  // round, no tail), or wgs_per_cu a CU, at most the workspace's dense_P
+  const int64_t resident =
+      static_cast<int64_t>(device_cu_count()) *
+      (wgs_per_cu > 0 ? wgs_per_cu
+                      : blocks_per_cu(reinterpret_cast<const void*>(dense_partial_kernel<int64_t, int64_t, false>)));
   const int P = static_cast<int>(hmax(1, hmin(L.dense_P, resident / tb->T)));
   tbe_status st;
   if (ia.itype == TBE_I32)

@@ -58,6 +58,8 @@ struct Config {
   int dense_min;  // rows of at least this many lookups (the 128 longest a table) take the dense path (0: off)
   int dense_presort;  // dense rows picked before the sort: 1 always, -1 never, 0 large batches
   int sort_by_table;  // each table's lookups sorted on their own: 1 when possible, -1 never, 0 auto
+  int short_reserve;  // set by the backward: vector registers per SIMD lane the short-run grid leaves free
+                     // for a kernel on another stream (0: it takes every slot)
 };
 Config resolve_config(const tbe_config* c);
 
@@ -185,9 +187,14 @@ tbe_status launch_dense_select(const tbe_tables* tb, char* ws, const BwdLayout& 
 // long-list slots
 tbe_status launch_dense_select_runs(const tbe_tables* tb, char* ws, const BwdLayout& L, int hist_t,
                                     const Config& cfg, hipStream_t s);
+// wgs_per_cu > 0: the partial kernel's grid is that many workgroups per CU (else as many as fit)
 tbe_status launch_dense_backward(const tbe_tables* tb, void* W, float* momentum, int opt,
                                  const IndexArgs& ia, const float* grad_out, float lr, float eps,
-                                 char* ws, const BwdLayout& L, hipStream_t s);
+                                 char* ws, const BwdLayout& L, hipStream_t s, int wgs_per_cu = 0);
+// vector registers a lane of the kernel holds (cached)
+int kernel_vgprs(const void* kernel);
+// registers of the dense partial kernel (the instantiation the skewed batches use)
+int dense_partial_vgprs();
 
 // saved_counts: the counts the histogram forward kept (then only ids past a bag's first 256
 // are read), or NULL to count every id
