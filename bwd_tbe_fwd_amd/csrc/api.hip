@@ -91,24 +91,6 @@ int device_cu_count() {
   return cached[dev];
 }
 
-int kernel_vgprs(const void* kernel) {
-  struct Entry {
-    const void* kernel;
-    int n;
-  };
-  static std::mutex mu;
-  static std::vector<Entry> cache;
-  std::lock_guard<std::mutex> lock(mu);
-  for (const auto& e : cache)
-    if (e.kernel == kernel) return e.n;
-  hipFuncAttributes a;
-  int n = 0;
-  if (hipFuncGetAttributes(&a, kernel) == hipSuccess && a.numRegs > 0) n = a.numRegs;
-  else (void)hipGetLastError();  // not sticky; unknown: 0
-  cache.push_back(Entry{kernel, n});
-  return n;
-}
-
 int blocks_per_cu(const void* kernel, size_t dyn_lds, int threads) {
   struct Entry {
     const void* kernel;
@@ -769,32 +751,46 @@ static tbe_status backward_common(const tbe_tables* tables, void* weights, float
   // apply kernels)
   if (L.dense_on && !L.dense_presort)
     if (tbe_status st = launch_dense_select_runs(tables, ws, L, hist, cfg, s)) return st;
-  if (hist >= 0) {
+  // automatic: short runs of several widths are several short launches, whose tails leave
+  // room for the long runs
+  int buckets = 0;
+  for (int b = 0; b < TBE_NUM_BUCKETS; ++b) buckets += L.cap_short[b] > 0;
+  const int streams = cfg.bwd_streams ? cfg.bwd_streams : (buckets >= 2 ? 2 : 1);
+  const bool beside = cfg.bwd_streams == 0 && streams < 2 && ((L.dense_on && L.dense_presort) || hist >= 0);
+  if (hist >= 0 && !beside) {
     // with the hoisted forward's state, its saved counts replace counting the first 256 ids
     const uint16_t* saved = cfg.pretransposed ? reinterpret_cast<const uint16_t*>(ws + L.hist_saved) : nullptr;
     if (tbe_status st = launch_hist_backward(tables, weights, momentum, opt, ia, grad_out, lr, eps, ws, L,
                                              saved, s))
       return st;
   }
-  // automatic: short runs of several widths are several short launches, whose tails leave
-  // room for the long runs
-  int buckets = 0;
-  for (int b = 0; b < TBE_NUM_BUCKETS; ++b) buckets += L.cap_short[b] > 0;
-  const int streams = cfg.bwd_streams ? cfg.bwd_streams : (buckets >= 2 ? 2 : 1);
-  if (cfg.bwd_streams == 0 && streams < 2 && L.dense_on && L.dense_presort) {
-    // the dense rows' kernels (matrix cores and LDS counting) on the second stream, launched
-    // first with one workgroup per CU, beside the short runs (bound by gradient-row reads),
-    // whose grid leaves that workgroup's registers free; the long runs follow the short runs
-    // (disjoint rows throughout)
+  const bool side_dense = L.dense_on && L.dense_presort;
+  if (beside) {
+    // the histogram table's backward and the dense rows' kernels (matrix cores and LDS
+    // counting) on the second stream, launched first with one workgroup per CU, beside the
+    // short runs (bound by gradient-row reads), whose grid leaves that workgroup's share of
+    // every SIMD free; the long runs follow the short runs (disjoint rows throughout)
     Fork fork(s);
     if (tbe_status st = fork.status()) return st;
-    tbe_status st = launch_dense_backward(tables, weights, momentum, opt, ia, grad_out, lr, eps, ws, L,
-                                          fork.side(), 1);
+    tbe_status st = TBE_OK;
+    int reserve = 0;  // the side kernels' share of a SIMD's registers, in 1/512
+    if (hist >= 0) {
+      const uint16_t* saved = cfg.pretransposed ? reinterpret_cast<const uint16_t*>(ws + L.hist_saved) : nullptr;
+      st = launch_hist_backward(tables, weights, momentum, opt, ia, grad_out, lr, eps, ws, L, saved, fork.side(), 1);
+      reserve = hmax(reserve, (512 + hist_partial_blocks_per_cu() - 1) / hist_partial_blocks_per_cu());
+    }
+    if (!st && side_dense) {
+      st = launch_dense_backward(tables, weights, momentum, opt, ia, grad_out, lr, eps, ws, L, fork.side(), 1);
+      reserve = hmax(reserve, (512 + dense_partial_blocks_per_cu() - 1) / dense_partial_blocks_per_cu());
+    }
     Config c2 = cfg;
-    c2.short_reserve = (dense_partial_vgprs() + 7) / 8 * 8;
+    c2.short_reserve = reserve;
     if (!st)
       st = launch_backward_update(tables, weights, momentum, opt, psw, grad_out, lr, eps, ws, L, final_buf, c2,
                                   s, s);
+    // dense rows picked from the long runs after the sort: after the chunk kernels on s
+    if (!st && L.dense_on && !L.dense_presort)
+      st = launch_dense_backward(tables, weights, momentum, opt, ia, grad_out, lr, eps, ws, L, s);
     const tbe_status st_j = fork.join();
     return st ? st : st_j;
   }

@@ -19,8 +19,9 @@ constexpr int short_chunks(int BD, bool tiny) {
   return (tiny && BD >= 64 && BD <= 256) ? 2 : np;
 }
 
-// reserve > 0: the grid leaves that many vector registers of every SIMD lane free (for a kernel
-// on another stream); a workgroup is one wave on each of a CU's four SIMDs
+// reserve > 0: the grid leaves that share (in 1/512) of every SIMD free for a kernel on another
+// stream: of the workgroups a CU holds (a workgroup is one wave on each of its four SIMDs), the
+// grid takes the share 1 - reserve / 512, at least one
 template <int DT, int BD, int OPT, bool WEIGHTED>
 tbe_status short_go(void* W, float* momentum, const float* psw, const float* grad_out,
                     const uint32_t* pay, const uint32_t* bag_of, const uint4* list,
@@ -32,9 +33,8 @@ tbe_status short_go(void* W, float* momentum, const float* psw, const float* gra
   const int64_t waves = (cap + RPW - 1) / RPW;
   const auto kernel = short_run_kernel<DT, BD, NPS, NPT, OPT, WEIGHTED, kShortUnroll, kTinyUnroll>;
   int grid = resident_grid(kernel, (waves + kWavesPerBlock - 1) / kWavesPerBlock);
-  const int regs = (kernel_vgprs(reinterpret_cast<const void*>(kernel)) + 7) / 8 * 8;
-  if (reserve > 0 && regs > 0) {
-    const int fit = hmax(1, (512 - reserve) / regs);
+  if (reserve > 0) {
+    const int fit = hmax(1, blocks_per_cu(reinterpret_cast<const void*>(kernel)) * (512 - reserve) / 512);
     grid = static_cast<int>(hmin(grid, static_cast<int64_t>(device_cu_count()) * fit));
   }
   ProfScope ps("short_run", s);

@@ -636,8 +636,8 @@ tbe_status launch_dense_select_runs(const tbe_tables* tb, char* ws, const BwdLay
   return check_launch("dense_select");
 }
 
-int dense_partial_vgprs() {
-  return kernel_vgprs(reinterpret_cast<const void*>(dense_partial_kernel<int64_t, int64_t, true>));
+int dense_partial_blocks_per_cu() {
+  return blocks_per_cu(reinterpret_cast<const void*>(dense_partial_kernel<int64_t, int64_t, true>));
 }
 
 tbe_status launch_dense_backward(const tbe_tables* tb, void* W, float* momentum, int opt,

@@ -267,9 +267,14 @@ tbe_status hist_partial_go(const tbe_tables* tb, const IndexArgs& ia, const floa
 
 }  // namespace
 
+int hist_partial_blocks_per_cu() {
+  return blocks_per_cu(reinterpret_cast<const void*>(hist_bwd_partial_kernel<int64_t, int64_t>));
+}
+
 tbe_status launch_hist_backward(const tbe_tables* tb, void* W, float* momentum, int opt,
                                 const IndexArgs& ia, const float* grad_out, float lr, float eps,
-                                char* ws, const BwdLayout& L, const uint16_t* saved, hipStream_t s) {
+                                char* ws, const BwdLayout& L, const uint16_t* saved, hipStream_t s,
+                                int wgs_per_cu) {
   if (tb->B == 0 || tb->hist_table < 0) return TBE_OK;
   if (tb->hist_table >= tb->T || tb->hist_E < 1 || tb->hist_E > kHbRows || tb->hist_D > kHbCols || tb->hist_D % 16 || tb->w_dtype != TBE_F16) {
     set_error("histogram table outside E <= 64, D <= 128, D %% 16 == 0, fp16");
@@ -277,7 +282,9 @@ tbe_status launch_hist_backward(const tbe_tables* tb, void* W, float* momentum, 
   }
   // one partial per workgroup; each workgroup step covers 64 bags
   const int64_t steps = (static_cast<int64_t>(tb->B) + kHbBags - 1) / kHbBags;
-  const int P = static_cast<int>(hmax(1, hmin(kHistBwdBlocks, steps)));
+  int64_t P64 = hmin(kHistBwdBlocks, steps);
+  if (wgs_per_cu > 0) P64 = hmin(P64, static_cast<int64_t>(device_cu_count()) * wgs_per_cu);
+  const int P = static_cast<int>(hmax(1, P64));
   float* partial = reinterpret_cast<float*>(ws + L.hist_partial);
   int32_t* pcount = reinterpret_cast<int32_t*>(ws + L.hist_count);
   tbe_status st;

@@ -58,8 +58,8 @@ struct Config {
   int dense_min;  // rows of at least this many lookups (the 128 longest a table) take the dense path (0: off)
   int dense_presort;  // dense rows picked before the sort: 1 always, -1 never, 0 large batches
   int sort_by_table;  // each table's lookups sorted on their own: 1 when possible, -1 never, 0 auto
-  int short_reserve;  // set by the backward: vector registers per SIMD lane the short-run grid leaves free
-                     // for a kernel on another stream (0: it takes every slot)
+  int short_reserve;  // set by the backward: the share (in 1/512) of every SIMD's registers the
+                     // short-run grid leaves free for a kernel on another stream (0: none)
 };
 Config resolve_config(const tbe_config* c);
 
@@ -191,17 +191,18 @@ tbe_status launch_dense_select_runs(const tbe_tables* tb, char* ws, const BwdLay
 tbe_status launch_dense_backward(const tbe_tables* tb, void* W, float* momentum, int opt,
                                  const IndexArgs& ia, const float* grad_out, float lr, float eps,
                                  char* ws, const BwdLayout& L, hipStream_t s, int wgs_per_cu = 0);
-// vector registers a lane of the kernel holds (cached)
-int kernel_vgprs(const void* kernel);
-// registers of the dense partial kernel (the instantiation the skewed batches use)
-int dense_partial_vgprs();
+// workgroups per CU the dense partial kernel holds at once
+int dense_partial_blocks_per_cu();
 
 // saved_counts: the counts the histogram forward kept (then only ids past a bag's first 256
 // are read), or NULL to count every id
+// wgs_per_cu > 0: the partial kernel's grid is at most that many workgroups per CU
 tbe_status launch_hist_backward(const tbe_tables* tb, void* W, float* momentum, int opt,
                                 const IndexArgs& ia, const float* grad_out, float lr, float eps,
                                 char* ws, const BwdLayout& L, const uint16_t* saved_counts,
-                                hipStream_t s);
+                                hipStream_t s, int wgs_per_cu = 0);
+// workgroups per CU the histogram partial kernel holds at once
+int hist_partial_blocks_per_cu();
 
 // groups long-run chunks by (table, bag window); *order = NULL when not grouped
 tbe_status launch_chunk_order(const tbe_tables* tb, const float* psw, char* ws, const BwdLayout& L,

@@ -130,9 +130,10 @@ typedef struct {
   int32_t bwd_streams;     /* backward: 2 = long runs (chunks, apply, dense rows) on the library's
                               second stream, concurrent with the short runs; 1 = one stream;
                               0 (default): 2 when the tables' widths fall in two or more short-run
-                              buckets; otherwise, when the dense rows are picked before the sort,
-                              the dense rows on the second stream (one workgroup per CU) beside
-                              the short runs, whose grid leaves room for them */
+                              buckets; otherwise, when the dense rows are picked before the sort
+                              or the histogram table is in use, those rows' kernels on the second
+                              stream (one workgroup per CU) beside the short runs, whose grid
+                              leaves room for them */
   int32_t tiny_runs;       /* backward: a wave step whose short runs all have at most this many
                               lookups serves twice as many runs with half the lanes each (rows of
                               64 .. 256 columns); default 8, 0: off */
