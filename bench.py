@@ -770,6 +770,7 @@ def main():
     per_launch = lambda m, k: m.get(k, 0) if k in per_launch_model else m.get(k, 0) / nl(k)
     per_step = lambda m, k: m.get(k, 0) * nl(k) if k in per_launch_model else m.get(k, 0)
     dom_bytes = per_launch(ab, dominant)
+    side_kernels = ("dense_partial", "dense_apply", "grad_accum", "long_apply")
     achieved = dom_bytes / (dom_avg_ms * 1e-3) / 1e9 if dom_avg_ms > 0 else 0.0
     # every kernel of the step
     step_bytes = sum(per_step(ab, k) for k in launches_per_step)
@@ -818,12 +819,15 @@ def main():
                      "traffic_frac": traffic["by_request_size"] / dom_s / (HBM_PEAK_GBS * 1e9)
                      if traffic and dom_s > 0 else None,
                      "l2_hit_rate": traffic["l2_hit_rate"] if traffic else None,
-                     # the dense rows' kernel on the second stream during the short runs (one
-                     # workgroup per CU): its bytes and the two kernels' bytes over this launch time
-                     "beside": ({"kernel": "dense_partial",
-                                 "algorithmic_bytes_per_launch": per_launch(ab, "dense_partial"),
-                                 "combined_frac": (dom_bytes + per_launch(ab, "dense_partial")) / dom_s
-                                 / (HBM_PEAK_GBS * 1e9)}
+                     # what runs on the second stream while the short runs' first grid runs: the
+                     # dense rows (one workgroup per CU), then the long runs, then a second
+                     # short-run grid taking the runs the first has not reached from a shared
+                     # counter; their bytes and every byte of the span over this launch time
+                     "beside": ({"kernels": ["dense_partial", "dense_apply", "grad_accum", "long_apply",
+                                             "short_run (second grid)"],
+                                 "algorithmic_bytes_per_launch": sum(per_step(ab, k) for k in side_kernels),
+                                 "combined_frac": (dom_bytes + sum(per_step(ab, k) for k in side_kernels))
+                                 / dom_s / (HBM_PEAK_GBS * 1e9)}
                                 if beside and dominant == "short_run" and dom_s > 0 else None),
                      "traffic_note": "bytes leaving L2 towards memory: reads served by the Infinity "
                                      "Cache are included, so they bound HBM bytes from above"},

@@ -136,6 +136,7 @@ Config resolve_config(const tbe_config* c) {
   r.dense_presort = c->dense_presort > 0 ? 1 : (c->dense_presort < 0 ? -1 : 0);
   r.sort_by_table = c->sort_by_table > 0 ? 1 : (c->sort_by_table < 0 ? -1 : 0);
   r.short_reserve = 0;
+  r.short_work = nullptr;
   return r;
 }
 
@@ -770,6 +771,12 @@ static tbe_status backward_common(const tbe_tables* tables, void* weights, float
     // counting) on the second stream, launched first with one workgroup per CU, beside the
     // short runs (bound by gradient-row reads), whose grid leaves that workgroup's share of
     // every SIMD free (disjoint rows throughout)
+    // with the long runs on the second stream, the short runs take their work from a counter
+    // (cleared before the fork, so the second stream's work starts after it): a second
+    // short-run grid follows the long runs there and takes what the first has not reached
+    int32_t* work = side_dense ? reinterpret_cast<int32_t*>(ws + L.counters) + kShortWork : nullptr;
+    if (work)
+      if (tbe_status st = launch_fill_i32(work, 0, 1, s)) return st;
     Fork fork(s);
     if (tbe_status st = fork.status()) return st;
     tbe_status st = TBE_OK;
@@ -785,6 +792,7 @@ static tbe_status backward_common(const tbe_tables* tables, void* weights, float
     }
     Config c2 = cfg;
     c2.short_reserve = reserve;
+    c2.short_work = work;
     // with the dense rows picked before the sort, the long runs follow the dense kernels on the
     // second stream: their chunks start in the slots the dense kernel leaves while the short
     // runs go on (skewed batch 9.72 -> 9.64 ms)

@@ -141,6 +141,8 @@ __device__ __forceinline__ void short_run_one(
     if (act[p]) store_vec4<DT>(wrow + p * 4 * LPR + c * 4, w[p]);
 }
 
+constexpr int kShortGrab = 16;  // wave steps a short-run wave takes from the shared counter at once
+
 // Short runs of one D bucket, list[0 .. n).  A wave step takes 2 x RPW_S consecutive runs.
 // When every run of the step has at most `tiny` lookups, each is served by LPR_T = LPR_S / 2
 // lanes holding NPT = 2 float4 chunks a lane, all of them at once (twice the runs in flight:
@@ -153,16 +155,16 @@ __global__ __launch_bounds__(kBlock) void short_run_kernel(
     const float* __restrict__ grad_out, const uint32_t* __restrict__ pay,
     const uint32_t* __restrict__ bag_of, const float* __restrict__ psw,
     const uint4* __restrict__ list, const int32_t* __restrict__ count_ptr, int64_t cap, int tiny,
-    const int64_t* __restrict__ meta, int32_t B, int32_t out_width, float lr, float eps) {
+    const int64_t* __restrict__ meta, int32_t B, int32_t out_width, float lr, float eps,
+    int32_t* __restrict__ work) {
   constexpr int LPR_S = BD / (4 * NPS), LPR_T = BD / (4 * NPT);  // lanes per run
   constexpr int RPW_S = kWave / LPR_S;                            // runs per half step
   static_assert(LPR_S >= 1 && LPR_S <= kWave && (LPR_S & (LPR_S - 1)) == 0, "lanes per run");
   static_assert(NPT == NPS || LPR_T * 2 == LPR_S, "tiny steps halve the lanes per run");
   const int lane = lane_id();
   const int64_t n = min(static_cast<int64_t>(*count_ptr), cap);
-  const int64_t wave = (static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x) >> 6;
-  const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * kBlock) >> 6;
-  for (int64_t i0 = wave * 2 * RPW_S; i0 < n; i0 += nwaves * 2 * RPW_S) {
+  // one wave step: runs [i0, i0 + 2 RPW_S)
+  auto step = [&](int64_t i0) {
     if constexpr (NPT != NPS) {
       const int64_t it = i0 + lane / LPR_T;
       const uint4 dsc = it < n ? list[it] : make_uint4(0u, 0u, 0u, 0u);
@@ -170,7 +172,7 @@ __global__ __launch_bounds__(kBlock) void short_run_kernel(
         if (it < n)
           short_run_one<DT, NPT, LPR_T, OPT, WEIGHTED, UT>(W, momentum, grad_out, pay, bag_of, psw, dsc,
                                                            lane % LPR_T, meta, B, out_width, lr, eps);
-        continue;
+        return;
       }
     }
 #pragma unroll 1
@@ -180,7 +182,25 @@ __global__ __launch_bounds__(kBlock) void short_run_kernel(
         short_run_one<DT, NPS, LPR_S, OPT, WEIGHTED, US>(W, momentum, grad_out, pay, bag_of, psw, list[i],
                                                          lane % LPR_S, meta, B, out_width, lr, eps);
     }
+  };
+  if (work) {
+    // steps taken from the shared counter, kShortGrab at a time, until every step is taken (by
+    // this grid or by another launch that shares the counter); each run is still served by
+    // exactly one wave, in the same way, so the result does not depend on which
+    const int64_t nsteps = (n + 2 * RPW_S - 1) / (2 * RPW_S);
+    for (;;) {
+      int32_t g0 = 0;
+      if (lane == 0) g0 = atomicAdd(work, kShortGrab);
+      g0 = __shfl(g0, 0);
+      if (g0 >= nsteps) break;
+      const int64_t g1 = min(static_cast<int64_t>(g0) + kShortGrab, nsteps);
+      for (int64_t g = g0; g < g1; ++g) step(g * 2 * RPW_S);
+    }
+    return;
   }
+  const int64_t wave = (static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x) >> 6;
+  const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * kBlock) >> 6;
+  for (int64_t i0 = wave * 2 * RPW_S; i0 < n; i0 += nwaves * 2 * RPW_S) step(i0);
 }
 
 // Sums the gradient rows of lookups [lo, hi) of one long run (table t) into

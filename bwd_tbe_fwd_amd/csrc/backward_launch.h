@@ -26,21 +26,23 @@ template <int DT, int BD, int OPT, bool WEIGHTED>
 tbe_status short_go(void* W, float* momentum, const float* psw, const float* grad_out,
                     const uint32_t* pay, const uint32_t* bag_of, const uint4* list,
                     const int32_t* count, int tiny, int64_t cap, const tbe_tables* tb,
-                    float lr, float eps, int reserve, hipStream_t s) {
+                    float lr, float eps, int reserve, int32_t* work, hipStream_t s) {
   using S = typename Fmt<DT>::S;
   constexpr int NPS = short_chunks(BD, false), NPT = short_chunks(BD, true);
   constexpr int RPW = 2 * kWave / (BD / (4 * NPS));  // runs per wave step
   const int64_t waves = (cap + RPW - 1) / RPW;
   const auto kernel = short_run_kernel<DT, BD, NPS, NPT, OPT, WEIGHTED, kShortUnroll, kTinyUnroll>;
   int grid = resident_grid(kernel, (waves + kWavesPerBlock - 1) / kWavesPerBlock);
+  // the second grid on a shared counter is timed under its own name, so that the first one's
+  // time is the short runs' span
   if (reserve > 0) {
     const int fit = hmax(1, blocks_per_cu(reinterpret_cast<const void*>(kernel)) * (512 - reserve) / 512);
     grid = static_cast<int>(hmin(grid, static_cast<int64_t>(device_cu_count()) * fit));
   }
-  ProfScope ps("short_run", s);
+  ProfScope ps(work && reserve == 0 ? "short_run_more" : "short_run", s);
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(kBlock), 0, s,
                      static_cast<S*>(W), momentum, grad_out, pay, bag_of, psw, list, count, cap, tiny,
-                     tb->meta, tb->B, tb->out_width, lr, eps);
+                     tb->meta, tb->B, tb->out_width, lr, eps, work);
   return check_launch("short_run");
 }
 
@@ -48,8 +50,9 @@ template <int DT, int OPT, bool WEIGHTED>
 tbe_status short_bucket(int b, void* W, float* momentum, const float* psw, const float* grad_out,
                         const uint32_t* pay, const uint32_t* bag_of, const uint4* list,
                         const int32_t* count, int tiny, int64_t cap,
-                        const tbe_tables* tb, float lr, float eps, int reserve, hipStream_t s) {
-#define TBE_SB(BD) short_go<DT, BD, OPT, WEIGHTED>(W, momentum, psw, grad_out, pay, bag_of, list, count, tiny, cap, tb, lr, eps, reserve, s)
+                        const tbe_tables* tb, float lr, float eps, int reserve, int32_t* work,
+                        hipStream_t s) {
+#define TBE_SB(BD) short_go<DT, BD, OPT, WEIGHTED>(W, momentum, psw, grad_out, pay, bag_of, list, count, tiny, cap, tb, lr, eps, reserve, work, s)
   switch (b) {
     case 0: return TBE_SB(4);
     case 1: return TBE_SB(8);
@@ -106,6 +109,13 @@ tbe_status launch_grad_accum(const tbe_tables* tb, const float* psw, const float
                              char* ws, const BwdLayout& L, int final_buf, const Config& cfg,
                              hipStream_t s);
 
+// the long runs' chunks and their apply on s
+template <int DT>
+tbe_status long_runs_and_apply(const tbe_tables* tb, void* W, float* momentum, int opt,
+                               const float* psw, const float* grad_out, float lr, float eps,
+                               char* ws, const BwdLayout& L, int final_buf, const Config& cfg,
+                               hipStream_t s);
+
 template <int DT>
 tbe_status launch_short_and_apply(const tbe_tables* tb, void* W, float* momentum, int opt,
                                   const float* psw, const float* grad_out, float lr, float eps,
@@ -114,22 +124,41 @@ tbe_status launch_short_and_apply(const tbe_tables* tb, void* W, float* momentum
   const int32_t* counters = reinterpret_cast<const int32_t*>(ws + L.counters);
   const uint32_t* pay = reinterpret_cast<const uint32_t*>(ws + L.pay[final_buf]);
   const uint32_t* bag_of = psw ? reinterpret_cast<const uint32_t*>(ws + L.bag_of) : nullptr;
-  for (int b = 0; b < TBE_NUM_BUCKETS; ++b) {
-    if (!L.cap_short[b]) continue;
-    const uint4* list = reinterpret_cast<const uint4*>(ws + L.short_list[b]);
-    const int64_t cap = L.cap_short[b];
-    const int32_t* cnt = counters + kShort0 + b;
+  // the short runs of every bucket on stream ss, the grid leaving `reserve` free
+  auto short_runs = [&](hipStream_t ss, int reserve) -> tbe_status {
+    for (int b = 0; b < TBE_NUM_BUCKETS; ++b) {
+      if (!L.cap_short[b]) continue;
+      const uint4* list = reinterpret_cast<const uint4*>(ws + L.short_list[b]);
+      const int64_t cap = L.cap_short[b];
+      const int32_t* cnt = counters + kShort0 + b;
 #define TBE_SHORT(OPT, WTD) \
   detail::short_bucket<DT, OPT, WTD>(b, W, momentum, psw, grad_out, pay, bag_of, list, cnt, cfg.tiny, cap, tb, lr, eps, \
-                                     cfg.short_reserve, s)
-    const tbe_status st = opt == kOptSGD ? (psw ? TBE_SHORT(kOptSGD, true) : TBE_SHORT(kOptSGD, false))
-                                         : (psw ? TBE_SHORT(kOptAdagrad, true) : TBE_SHORT(kOptAdagrad, false));
+                                     reserve, cfg.short_work, ss)
+      const tbe_status st = opt == kOptSGD ? (psw ? TBE_SHORT(kOptSGD, true) : TBE_SHORT(kOptSGD, false))
+                                           : (psw ? TBE_SHORT(kOptAdagrad, true) : TBE_SHORT(kOptAdagrad, false));
 #undef TBE_SHORT
-    if (st) return st;
-  }
-  if (L.cap_long == 0) return TBE_OK;
+      if (st) return st;
+    }
+    return TBE_OK;
+  };
+  if (tbe_status st = short_runs(s, cfg.short_reserve)) return st;
   // long runs touch other rows than short runs: s_long may be a second stream
-  s = s_long;
+  if (tbe_status st = long_runs_and_apply<DT>(tb, W, momentum, opt, psw, grad_out, lr, eps, ws, L, final_buf,
+                                          cfg, s_long))
+    return st;
+  // with a shared work counter, a second short-run grid on the long runs' stream, after them,
+  // takes the short runs the first grid has not reached (one wave step at a time)
+  if (cfg.short_work && s_long != s) return short_runs(s_long, 0);
+  return TBE_OK;
+}
+
+template <int DT>
+tbe_status long_runs_and_apply(const tbe_tables* tb, void* W, float* momentum, int opt,
+                               const float* psw, const float* grad_out, float lr, float eps,
+                               char* ws, const BwdLayout& L, int final_buf, const Config& cfg,
+                               hipStream_t s) {
+  const int32_t* counters = reinterpret_cast<const int32_t*>(ws + L.counters);
+  if (L.cap_long == 0) return TBE_OK;
   if (cfg.fused_long) {
     const uint32_t* order = nullptr;
     if (tbe_status st = launch_chunk_order(tb, psw, ws, L, final_buf, cfg, &order, s)) return st;

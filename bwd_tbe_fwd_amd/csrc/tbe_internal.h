@@ -60,6 +60,9 @@ struct Config {
   int sort_by_table;  // each table's lookups sorted on their own: 1 when possible, -1 never, 0 auto
   int short_reserve;  // set by the backward: the share (in 1/512) of every SIMD's registers the
                      // short-run grid leaves free for a kernel on another stream (0: none)
+  int32_t* short_work;  // set by the backward: a zeroed device counter from which the short-run
+                        // waves take their work (NULL: each wave takes fixed steps); with the
+                        // long runs on a second stream a second short-run grid follows them there
 };
 Config resolve_config(const tbe_config* c);
 
@@ -128,7 +131,7 @@ constexpr int kOptAdagrad = 1;
 // first radix pass (sentinel keys left out), the length of the sorted arrays; kHotProbe: the
 // longest probe sequence of the dense-row key set
 enum Counter { kRuns = 0, kLong = 1, kChunks = 2, kShort0 = 3, kNeff = 12, kSorted = 13, kHotProbe = 14,
-               kNumCounters = 16 };
+               kShortWork = 15, kNumCounters = 16 };
 static_assert(kShort0 + TBE_NUM_BUCKETS <= kNeff, "counter slots overlap");
 
 // ---------------------------------------------------------------------------
