@@ -149,7 +149,9 @@ constexpr int kShortGrab = 16;  // wave steps a short-run wave takes from the sh
 // such runs wait on memory, not on bandwidth); otherwise the step runs as two halves of
 // RPW_S runs with LPR_S lanes each.  Rows wider than 256 columns or narrower than 64 have
 // one mode only (NPT == NPS).
-template <int DT, int BD, int NPS, int NPT, int OPT, bool WEIGHTED, int US, int UT>
+// SHARED: the wave steps come from the counter `work` (kShortGrab at a time), which other
+// launches may share; otherwise wave w takes steps w, w + waves, ...
+template <int DT, int BD, int NPS, int NPT, int OPT, bool WEIGHTED, int US, int UT, bool SHARED>
 __global__ __launch_bounds__(kBlock) void short_run_kernel(
     typename Fmt<DT>::S* __restrict__ W, float* __restrict__ momentum,
     const float* __restrict__ grad_out, const uint32_t* __restrict__ pay,
@@ -183,7 +185,7 @@ __global__ __launch_bounds__(kBlock) void short_run_kernel(
                                                          lane % LPR_S, meta, B, out_width, lr, eps);
     }
   };
-  if (work) {
+  if constexpr (SHARED) {
     // steps taken from the shared counter, kShortGrab at a time, until every step is taken (by
     // this grid or by another launch that shares the counter); each run is still served by
     // exactly one wave, in the same way, so the result does not depend on which
@@ -196,11 +198,11 @@ __global__ __launch_bounds__(kBlock) void short_run_kernel(
       const int64_t g1 = min(static_cast<int64_t>(g0) + kShortGrab, nsteps);
       for (int64_t g = g0; g < g1; ++g) step(g * 2 * RPW_S);
     }
-    return;
+  } else {
+    const int64_t wave = (static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x) >> 6;
+    const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * kBlock) >> 6;
+    for (int64_t i0 = wave * 2 * RPW_S; i0 < n; i0 += nwaves * 2 * RPW_S) step(i0);
   }
-  const int64_t wave = (static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x) >> 6;
-  const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * kBlock) >> 6;
-  for (int64_t i0 = wave * 2 * RPW_S; i0 < n; i0 += nwaves * 2 * RPW_S) step(i0);
 }
 
 // Sums the gradient rows of lookups [lo, hi) of one long run (table t) into

@@ -8,6 +8,10 @@ namespace tbe {
 namespace detail {
 
 constexpr int kShortUnroll = 4;
+// gradient rows in flight per run for the short-run grids on a shared counter (held to part of
+// every CU beside the dense rows): fewer waves, so more rows each (skewed batch 9.40 -> 9.25 ms;
+// at full occupancy 8 rows cost the uniform batch's tiny runs 7 %)
+constexpr int kShortUnrollShared = 8;
 constexpr int kTinyUnroll = 2;
 
 // float4 column chunks per lane: one (BD / 4 lanes per run) up to 256 columns, then all 64
@@ -31,7 +35,11 @@ tbe_status short_go(void* W, float* momentum, const float* psw, const float* gra
   constexpr int NPS = short_chunks(BD, false), NPT = short_chunks(BD, true);
   constexpr int RPW = 2 * kWave / (BD / (4 * NPS));  // runs per wave step
   const int64_t waves = (cap + RPW - 1) / RPW;
-  const auto kernel = short_run_kernel<DT, BD, NPS, NPT, OPT, WEIGHTED, kShortUnroll, kTinyUnroll>;
+  // the shared-counter grids (unweighted only: they serve batches with dense rows) take more
+  // rows in flight
+  const auto kernel = work ? short_run_kernel<DT, BD, NPS, NPT, OPT, WEIGHTED,
+                                              WEIGHTED ? kShortUnroll : kShortUnrollShared, kTinyUnroll, true>
+                           : short_run_kernel<DT, BD, NPS, NPT, OPT, WEIGHTED, kShortUnroll, kTinyUnroll, false>;
   int grid = resident_grid(kernel, (waves + kWavesPerBlock - 1) / kWavesPerBlock);
   // the second grid on a shared counter is timed under its own name, so that the first one's
   // time is the short runs' span
