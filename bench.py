@@ -267,9 +267,12 @@ def summarize_profiles(root: str, workload: str, out_dir: str = None):
         f.write(f"# Kernel durations, {ti.WORKLOADS[workload].name}\n\n")
         f.write("Command (from the repository root, with `TMPDIR=/tmp` exported):\n\n    "
                 + cmds["trace"] + "\n\n")
-        f.write(f"{2 + len(KERNELS) + 10} steps traced: 2 warm-up, one per timed kernel name, 10 timed; "
-                "the transpose runs in the backward call (`--hoist off`), so no two kernels overlap. "
-                "Library kernels only, from `run_kernel_stats.csv`.\n\n")
+        f.write(f"{2 + len(KERNELS) + 10} steps traced: 2 warm-up, one per timed kernel name (backward on one "
+                "stream), 10 timed; the transpose runs in the backward call (`--hoist off`).  In the timed "
+                "steps the library's automatic backward may run kernels side by side on two streams (with "
+                "the dense rows picked before the sort: the dense rows, the long runs and a second "
+                "short-run grid beside the first one, both grids taking their work from a shared counter), "
+                "so those durations overlap.  Library kernels only, from `run_kernel_stats.csv`.\n\n")
         f.write("| kernel | calls | average us | total ms | share of GPU time % |\n|---|---|---|---|---|\n")
         for r in trace:
             nm = r["Name"].replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
