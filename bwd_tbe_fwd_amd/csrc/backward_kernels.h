@@ -149,9 +149,10 @@ constexpr int kShortGrab = 16;  // wave steps a short-run wave takes from the sh
 // such runs wait on memory, not on bandwidth); otherwise the step runs as two halves of
 // RPW_S runs with LPR_S lanes each.  Rows wider than 256 columns or narrower than 64 have
 // one mode only (NPT == NPS).
-// SHARED: the wave steps come from the counter `work` (kShortGrab at a time), which other
-// launches may share; otherwise wave w takes steps w, w + waves, ...
-template <int DT, int BD, int NPS, int NPT, int OPT, bool WEIGHTED, int US, int UT, bool SHARED>
+// SHARED > 0: the wave steps come from the counter `work` (kShortGrab at a time), which other
+// launches share (1: the first grid, 2: a second one, the same code under its own name, so that
+// profiles time the two apart); 0: wave w takes steps w, w + waves, ...
+template <int DT, int BD, int NPS, int NPT, int OPT, bool WEIGHTED, int US, int UT, int SHARED>
 __global__ __launch_bounds__(kBlock) void short_run_kernel(
     typename Fmt<DT>::S* __restrict__ W, float* __restrict__ momentum,
     const float* __restrict__ grad_out, const uint32_t* __restrict__ pay,
@@ -185,7 +186,7 @@ __global__ __launch_bounds__(kBlock) void short_run_kernel(
                                                          lane % LPR_S, meta, B, out_width, lr, eps);
     }
   };
-  if constexpr (SHARED) {
+  if constexpr (SHARED > 0) {
     // steps taken from the shared counter, kShortGrab at a time, until every step is taken (by
     // this grid or by another launch that shares the counter); each run is still served by
     // exactly one wave, in the same way, so the result does not depend on which

@@ -36,10 +36,21 @@ tbe_status short_go(void* W, float* momentum, const float* psw, const float* gra
   constexpr int RPW = 2 * kWave / (BD / (4 * NPS));  // runs per wave step
   const int64_t waves = (cap + RPW - 1) / RPW;
   // the shared-counter grids (unweighted only: they serve batches with dense rows) take more
-  // rows in flight
-  const auto kernel = work ? short_run_kernel<DT, BD, NPS, NPT, OPT, WEIGHTED,
-                                              WEIGHTED ? kShortUnroll : kShortUnrollShared, kTinyUnroll, true>
-                           : short_run_kernel<DT, BD, NPS, NPT, OPT, WEIGHTED, kShortUnroll, kTinyUnroll, false>;
+  // rows in flight; the first (beside other kernels, reserve > 0) and the second grid are
+  // separate instantiations of the same code
+  auto kernel = short_run_kernel<DT, BD, NPS, NPT, OPT, WEIGHTED, kShortUnroll, kTinyUnroll, 0>;
+  if constexpr (WEIGHTED) {
+    // the shared counter comes with the dense rows, which per-sample weights rule out; a grid
+    // that ignored it would serve every run a second time
+    if (work) {
+      set_error("shared short-run grids serve batches without per-sample weights only");
+      return TBE_ERR_ARG;
+    }
+  } else {
+    if (work)
+      kernel = reserve > 0 ? short_run_kernel<DT, BD, NPS, NPT, OPT, WEIGHTED, kShortUnrollShared, kTinyUnroll, 1>
+                           : short_run_kernel<DT, BD, NPS, NPT, OPT, WEIGHTED, kShortUnrollShared, kTinyUnroll, 2>;
+  }
   int grid = resident_grid(kernel, (waves + kWavesPerBlock - 1) / kWavesPerBlock);
   // the second grid on a shared counter is timed under its own name, so that the first one's
   // time is the short runs' span
