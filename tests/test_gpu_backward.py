@@ -73,9 +73,13 @@ def test_gradient_extraction(weighted):
     assert np.all(err <= 1e-5 * r["g_abs"]), float((err - 1e-5 * r["g_abs"]).max())
 
 
-def test_backward_deterministic():
+@pytest.mark.parametrize("cfg_kw", [{}, dict(dense_min=64, dense_presort=1)])
+def test_backward_deterministic(cfg_kw):
+    """Bitwise the same on every run: also when the dense rows are picked before the sort, so
+    that two short-run grids on two streams take their runs from a shared counter in whatever
+    order they get there."""
     bt = ti.make_batch(small_spec("skewed"), 31)
-    cfg = tbe.make_config(long_threshold=16, chunk=16)
+    cfg = tbe.make_config(long_threshold=16, chunk=16, **cfg_kw)
     outs = []
     for _ in range(2):
         db = DevBatch(bt)

@@ -16,7 +16,8 @@ pytestmark = pytest.mark.gpu
 class Step:
     """Device buffers of one batch and the calls of one step on them."""
 
-    def __init__(self, bt, weights, momentum):
+    def __init__(self, bt, weights, momentum, cfg_kw=None):
+        cfg_kw = cfg_kw or {}
         self.bt = bt
         self.t = tbe.Tables(bt.E, bt.D, bt.B, bt.w_dtype, device="cuda", pooling_hint=bt.spec.pooling_hint)
         self.W, self.mom = weights, momentum
@@ -26,8 +27,8 @@ class Step:
         self.out = torch.zeros(bt.B, sum(bt.D), device="cuda")
         self.counts = torch.zeros(2, dtype=torch.int64, device="cuda")
         self.bws = tbe.workspace(tbe.tbe_bounds_check_workspace_bytes(self.t))
-        self.cfg = tbe.make_config(long_threshold=16, chunk=8)
-        self.bcfg = tbe.make_config(long_threshold=16, chunk=8, pretransposed=1)
+        self.cfg = tbe.make_config(long_threshold=16, chunk=8, **cfg_kw)
+        self.bcfg = tbe.make_config(long_threshold=16, chunk=8, pretransposed=1, **cfg_kw)
         self.ws = tbe.workspace(tbe.tbe_backward_workspace_bytes(self.t, self.idx.numel(),
                                                                  self.psw is not None, self.cfg))
 
@@ -45,12 +46,18 @@ class Step:
                                              self.bcfg)
 
 
-@pytest.mark.parametrize("name", ["skewed", "mixed", "histogram"])
-def test_step_graph_replays_match_eager(name):
+# dense rows picked before the sort: the backward runs them, the long runs and a second short-run
+# grid on the second stream beside the first, both grids taking work from a shared counter
+PRESORT = dict(dense_min=64, dense_presort=1)
+
+
+@pytest.mark.parametrize("name,cfg_kw", [("skewed", None), ("mixed", None), ("histogram", None),
+                                         ("skewed", PRESORT)])
+def test_step_graph_replays_match_eager(name, cfg_kw):
     bt = ti.make_batch(small_spec(name), 95)
     mom0 = (bt.momentum if bt.momentum is not None else torch.zeros(sum(bt.E))).cuda()
-    eager = Step(bt, bt.weights.cuda(), mom0.clone())
-    graphed = Step(bt, bt.weights.cuda(), mom0.clone())
+    eager = Step(bt, bt.weights.cuda(), mom0.clone(), cfg_kw)
+    graphed = Step(bt, bt.weights.cuda(), mom0.clone(), cfg_kw)
     # warm-up outside the capture (makes the library's second stream), then reset the state
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
