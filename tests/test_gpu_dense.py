@@ -305,3 +305,51 @@ def test_dense_rows_random_shapes(seed):
                               dense_presort=int(rng.choice([1, -1])),
                               bwd_streams=int(rng.choice([0, 1, 2])))
         run_and_check(bt, cfg, what=f"{spec.name}: {bt.indices.numel()} lookups")
+
+
+@pytest.mark.parametrize("seed", [3, 4])
+def test_dense_rows_beside_the_short_runs_random_shapes(seed):
+    """Seeded random shapes through the automatic backward's side-by-side mode: with the dense
+    rows picked before the sort and every table in one short-run bucket, the dense rows (and
+    the histogram table, when there is one) run on the second stream beside the short runs,
+    whose two grids take their work from one shared counter, the long runs between them on the
+    second stream.  Every step is checked against the oracle, the second short-run grid must
+    have run, and every third step also goes through the hoisted forward, bit for bit equal to
+    the plain calls."""
+    from test_gpu_hoisted import _assert_same, _step
+    rng = np.random.default_rng(seed)
+    for it in range(12):
+        bucket = int(rng.choice([64, 128]))
+        widths = [d for d in range(16, 129, 16) if bucket // 2 < d <= bucket]
+        T = int(rng.integers(1, 5))
+        lam = [float(rng.choice([10, 30, 80])) for _ in range(T)]
+        tables = [ti.TableSpec(int(rng.choice([40, 300, 1000, 5000])), int(rng.choice(widths)),
+                               ("poisson", l, None, None), ("zipf", float(rng.choice([1.05, 1.2, 1.4])), None))
+                  for l in lam]
+        hint = [max(1, int(l)) for l in lam]
+        if bucket == 128 and rng.random() < 0.5:   # a histogram table (at most 64 rows), same bucket
+            at = int(rng.integers(0, T + 1))
+            L = int(rng.choice([64, 100, 300]))
+            tables.insert(at, ti.TableSpec(int(rng.choice([17, 64])), 128, ("fixed", L)))
+            hint.insert(at, L)
+        spec = ti.BatchSpec(f"beside {seed}.{it}", tuple(tables), B=int(rng.choice([63, 200, 700, 3000])),
+                            w_dtype=[torch.float32, torch.float16, torch.bfloat16][int(rng.integers(0, 3))],
+                            w_range=0.05, optimizer=["sgd", "rowwise_adagrad"][int(rng.integers(0, 2))],
+                            itype=[torch.int32, torch.int64][int(rng.integers(0, 2))],
+                            otype=[torch.int32, torch.int64][int(rng.integers(0, 2))],
+                            pooling_hint=tuple(hint))
+        bt = ti.make_batch(spec, 2000 * seed + it)
+        kw = dict(long_threshold=int(rng.choice([16, 32, 256])), chunk=int(rng.choice([8, 16, 256])),
+                  dense_min=int(rng.choice([16, 40, 100])), dense_presort=1)
+        what = f"{spec.name}: D={bt.D} B={bt.B} {bt.indices.numel()} lookups {kw}"
+        flush_print(what)
+        tbe.tbe_profile_select("short_run_more")
+        db, _, _, _ = run_and_check(bt, tbe.make_config(**kw), what=what)
+        n_more, _ = tbe.tbe_profile_read()
+        tbe.tbe_profile_select(None)
+        assert n_more >= 1, what
+        if it % 3 == 0:
+            idx, off = bt.indices.numpy(), bt.offsets.numpy()
+            repair = bool(rng.integers(0, 2))
+            _assert_same(_step(bt, idx, off, hoisted=False, repair=repair, cfg_kw=kw),
+                         _step(bt, idx, off, hoisted=True, repair=repair, cfg_kw=kw))
