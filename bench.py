@@ -477,12 +477,12 @@ def algorithmic_bytes(bt: ti.Batch, st: dict, hoist: bool, dense_P: int = 24, pr
     if presort:
         # ids read and keys + payloads written at the sampled positions, the sample's own sort
         # (keys + payloads read and written per pass, keys counted) and run-length encoding,
-        # the dense rows' key set (4 x 128 slots a table, a power of two) and 8 KB filter filled
-        slots = 1024
-        while slots < 4 * 128 * bt.T:
-            slots *= 2
+        # the dense rows' key set (8 x 128 words a table, a power of two) and 8 KB filter filled
+        words = 1024
+        while words < 8 * 128 * bt.T:
+            words *= 2
         by["dense_sample"] = sample_keys * (s_i + 8) + passes * sample_keys * 20 + 3 * sample_keys * 4 \
-            + slots * 4 + 8192
+            + words * 4 + 8192
     for p in hst:
         # per lookup: index; per bag: offset + output (forward) or gradient (backward) row
         by["fwd_hist"] = p["N"] * s_i + B * (s_o + p["D"] * 4) + 64 * p["D"] * s_w

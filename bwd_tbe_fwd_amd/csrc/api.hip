@@ -262,11 +262,11 @@ BwdLayout bwd_layout(const tbe_tables* tb, int64_t N, int weighted, const Config
     P.seg_cnt = c.take(static_cast<size_t>(P.nblocks) * 4);
     P.cls_cnt = c.take(static_cast<size_t>(TBE_NUM_BUCKETS + 2) * P.cls_blocks * 4);
     P.counters = c.take(kNumCounters * 4);
-    int64_t hs = 1024;  // at most a quarter full
-    while (hs < 4 * static_cast<int64_t>(kDenseRows) * tb->T) hs <<= 1;
+    // words of 16-byte records, three key slots each: at most a sixth of the slots used
+    int64_t hs = 1024;
+    while (hs < 8 * static_cast<int64_t>(kDenseRows) * tb->T) hs <<= 1;
     L.hot_set_size = hs;
     L.hot_set = c.take(static_cast<size_t>(hs) * 4);
-    L.hot_rank = c.take(static_cast<size_t>(hs));
     L.dense_slot = c.take(static_cast<size_t>(n1) * 2);
     L.hot_bloom = c.take(static_cast<size_t>(kHotBloomWords) * 4);
   }

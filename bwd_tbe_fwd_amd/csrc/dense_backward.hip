@@ -109,7 +109,7 @@ __global__ __launch_bounds__(kBlock) void dense_select_kernel(
     const uint4* __restrict__ long_list, const uint32_t* __restrict__ long_table,
     const int32_t* __restrict__ counters, int64_t cap_long, const int64_t* __restrict__ meta, int T,
     int hist_t, uint32_t min_len, int32_t* __restrict__ dense_rows, int32_t* __restrict__ dense_cnt,
-    uint32_t* __restrict__ long_flag, uint32_t* __restrict__ hot_set, uint8_t* __restrict__ hot_rank,
+    uint32_t* __restrict__ long_flag, uint32_t* __restrict__ hot_set,
     uint32_t hot_mask, uint32_t* __restrict__ hot_filter, int32_t* __restrict__ probe_max) {
   const int lane = lane_id();
   const int t = static_cast<int>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
@@ -176,15 +176,18 @@ __global__ __launch_bounds__(kBlock) void dense_select_kernel(
     if (hot_set && take) {
       const uint32_t key = L.x;
       const uint32_t h = hot_slot(key, hot_mask);
-      int i = 0;  // the set holds 4 slots per possible key: a free slot is always found
-      while (true) {
-        const uint32_t e = (h + i) & hot_mask;
-        const uint32_t prev = atomicCAS(&hot_set[e], kHotEmpty, key);
-        if (prev == kHotEmpty) hot_rank[e] = static_cast<uint8_t>(rank);
-        if (prev == kHotEmpty || prev == key) break;
-        ++i;
+      // the set holds at least 6 slots per possible key: a free slot is always found
+      int g = 0;
+      for (bool placed = false; !placed; ++g) {
+        const uint32_t rec = (h + 4 * g) & hot_mask;
+        for (int j = 0; j < kHotSlotsPerRecord && !placed; ++j) {
+          const uint32_t prev = atomicCAS(&hot_set[rec + j], kHotEmpty, key);
+          if (prev == kHotEmpty)  // its rank into byte j of the record's rank word
+            reinterpret_cast<uint8_t*>(hot_set + rec + kHotSlotsPerRecord)[j] = static_cast<uint8_t>(rank);
+          placed = prev == kHotEmpty || prev == key;
+        }
       }
-      atomicMax(probe_max, (i >> 2) + 1);  // groups of four a lookup reads at most
+      atomicMax(probe_max, g);  // records a lookup reads at most
       const uint32_t f = hot_filter_bit(key);
       atomicOr(&hot_filter[f >> 5], 1u << (f & 31));
     }
@@ -616,7 +619,7 @@ tbe_status launch_dense_select(const tbe_tables* tb, char* ws, const BwdLayout& 
                      reinterpret_cast<const uint32_t*>(ws + P.long_table),
                      reinterpret_cast<const int32_t*>(ws + P.counters), P.cap_long, tb->meta, tb->T, hist_t, 0u,
                      reinterpret_cast<int32_t*>(ws + L.dense_rows), reinterpret_cast<int32_t*>(ws + L.dense_cnt),
-                     nullptr, reinterpret_cast<uint32_t*>(ws + L.hot_set), reinterpret_cast<uint8_t*>(ws + L.hot_rank),
+                     nullptr, reinterpret_cast<uint32_t*>(ws + L.hot_set),
                      static_cast<uint32_t>(L.hot_set_size - 1),
                      reinterpret_cast<uint32_t*>(ws + L.hot_bloom),
                      reinterpret_cast<int32_t*>(ws + L.counters) + kHotProbe);
@@ -632,7 +635,7 @@ tbe_status launch_dense_select_runs(const tbe_tables* tb, char* ws, const BwdLay
                      reinterpret_cast<const int32_t*>(ws + L.counters), L.cap_long, tb->meta, tb->T, hist_t,
                      static_cast<uint32_t>(cfg.dense_min), reinterpret_cast<int32_t*>(ws + L.dense_rows),
                      reinterpret_cast<int32_t*>(ws + L.dense_cnt), reinterpret_cast<uint32_t*>(ws + L.long_flag),
-                     nullptr, nullptr, 0u, nullptr, nullptr);
+                     nullptr, 0u, nullptr, nullptr);
   return check_launch("dense_select");
 }
 

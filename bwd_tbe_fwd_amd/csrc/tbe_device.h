@@ -201,19 +201,19 @@ __device__ __forceinline__ int table_of_key(const int64_t* __restrict__ meta, in
 }
 
 // The key set of the dense rows: open addressing with linear probing over a power-of-two
-// array of keys (kHotEmpty marks a free slot), with a byte array beside it holding each
-// key's rank among its table's dense rows.  Probing starts at a 16-byte group of four
-// slots (and the matching 4 bytes of ranks), so that a lookup reads whole groups (one,
-// nearly always) and stops at the first group with a free slot; a 65536-bit filter turns
-// most other keys away first.  Both hashes are
-// multiplicative (Knuth's golden-ratio constant and a second odd multiplier).
+// array of 16-byte records, each three key slots (kHotEmpty marks a free one) and a word
+// holding their keys' ranks among their tables' dense rows (byte j for slot j), so that one
+// load answers a probe: a lookup reads whole records (one, nearly always) and stops at the
+// first record with a free slot; a 65536-bit filter turns most other keys away first.  Both
+// hashes are multiplicative (Knuth's golden-ratio constant and a second odd multiplier).
 constexpr uint32_t kHotEmpty = 0xffffffffu;
+constexpr int kHotSlotsPerRecord = 3;
 // A lookup's dense slot: bits 0-7 the rank of its row among its table's dense rows (0xff:
 // none), bits 8-11 its bag's index within the table modulo 16
 constexpr uint16_t kNoDenseSlot = 0x00ff;
 __device__ __forceinline__ uint32_t hot_slot(uint32_t key, uint32_t mask) {
   const uint32_t h = key * 0x9e3779b1u;
-  return ((h ^ (h >> 15)) << 2) & mask;  // first slot of a group
+  return ((h ^ (h >> 15)) << 2) & mask;  // first word of a record
 }
 __device__ __forceinline__ uint32_t hot_filter_bit(uint32_t key) { return (key * 0x85ebca6bu) >> 16; }
 

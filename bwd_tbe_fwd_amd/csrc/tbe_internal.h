@@ -100,14 +100,14 @@ struct BwdLayout {
   // kDenseRows x 128 floats per table.  With dense_presort the rows are chosen before the sort
   // from a sample of the lookups (64 positions every hot_stride, sorted and run-length encoded
   // on their own: runs of at least hot_thr sampled lookups), and their keys go into an
-  // open-addressing set (hot_set, hot_set_size entries, at most a quarter of them used) with a
+  // open-addressing set (hot_set: hot_set_size words, 16-byte records of three key slots and
+  // their ranks, at most a sixth of the slots used) with a
   // 65536-bit filter, which linearize consults; otherwise they come from the batch's long runs
   // after the sort, with a flag per long-list slot (long_flag) that the chunk and apply
   // kernels read
-  // (hot_rank: the rank of each key-set slot's row among its table's dense rows; dense_slot:
-  // two bytes per lookup position, its row's rank or none and its bag modulo 16, written by
-  // linearize and read by the dense partial kernel instead of the ids)
-  size_t dense_rows, dense_cnt, dense_partial, hot_set, hot_rank, hot_bloom, long_flag, dense_slot;
+  // (dense_slot: two bytes per lookup position, its row's rank or none and its bag modulo 16,
+  // written by linearize and read by the dense partial kernel instead of the ids)
+  size_t dense_rows, dense_cnt, dense_partial, hot_set, hot_bloom, long_flag, dense_slot;
   int dense_P, dense_on, dense_presort, hot_stride, hot_thr;
   int64_t hot_set_size;
   SortPlan sample;

@@ -51,8 +51,8 @@ namespace {
 // N - (lookups of skip_t) keys; that count goes to *n_eff.  Positions that no
 // bag covers (possible only with offsets that break the documented contract)
 // get the sentinel key, so every key and payload the sort reads is defined.
-// hot_set != NULL: keys in the dense-row key set (hot_mask + 1 slots; the most slot groups
-// a lookup reads in *hot_probes) get the sentinel key too, and every position of a bag (and
+// hot_set != NULL: keys in the dense-row key set (hot_mask + 1 words of records; the most
+// records a lookup reads in *hot_probes) get the sentinel key too, and every position of a bag (and
 // every position no bag covers) gets its dense slot: the rank of its row among its table's
 // dense rows and its bag modulo 16, or kNoDenseSlot (positions of the table left out,
 // skip_t, are not written): those lookups are the
@@ -64,7 +64,7 @@ __global__ __launch_bounds__(kBlock) void linearize_kernel(
     const IT* __restrict__ indices, const OT* __restrict__ offsets, const int64_t* __restrict__ meta,
     int32_t B, int64_t nbags, int32_t N, uint32_t sentinel, int skip_t, int invalid_as_row0,
     const uint32_t* __restrict__ hot_filter, const uint32_t* __restrict__ hot_set,
-    const uint8_t* __restrict__ hot_rank, uint32_t hot_mask, const int32_t* __restrict__ hot_probes,
+    uint32_t hot_mask, const int32_t* __restrict__ hot_probes,
     uint16_t* __restrict__ dense_slot, uint32_t* __restrict__ keys,
     uint32_t* __restrict__ pay, uint32_t* __restrict__ bag_of, int32_t* __restrict__ n_eff) {
   __shared__ __align__(16) uint32_t s_filter[kHotBloomWords];
@@ -162,11 +162,11 @@ __global__ __launch_bounds__(kBlock) void linearize_kernel(
 #pragma unroll
       for (int u = 0; u < kLinU; ++u) slot[u] = kNoDenseSlot;
       if (hot_set) {
-        // the filter, then every candidate's first group of four slots (16 bytes of keys and
-        // the 4 bytes of their ranks) at once; the rare full group without the key sends its
-        // lanes to the next groups, all together
+        // the filter, then every candidate's first record (three keys and their ranks, one
+        // 16-byte load) at once; the rare full record without the key sends its lanes to the
+        // next records, all together
         bool pend[kLinU];
-        uint32_t h[kLinU], rk[kLinU];
+        uint32_t h[kLinU];
         u32x4 v[kLinU];
 #pragma unroll
         for (int u = 0; u < kLinU; ++u) {
@@ -180,19 +180,17 @@ __global__ __launch_bounds__(kBlock) void linearize_kernel(
             if (!pend[u]) continue;
             const uint32_t e = (h[u] + 4 * g) & hot_mask;
             v[u] = *reinterpret_cast<const u32x4*>(hot_set + e);
-            rk[u] = *reinterpret_cast<const uint32_t*>(hot_rank + e);
           }
           bool more = false;
 #pragma unroll
           for (int u = 0; u < kLinU; ++u) {
             if (!pend[u]) continue;
             const uint32_t kk = key[u];
-            const bool hit = v[u].x == kk || v[u].y == kk || v[u].z == kk || v[u].w == kk;
-            const bool gap = v[u].x == kHotEmpty || v[u].y == kHotEmpty || v[u].z == kHotEmpty ||
-                             v[u].w == kHotEmpty;
+            const bool hit = v[u].x == kk || v[u].y == kk || v[u].z == kk;
+            const bool gap = v[u].x == kHotEmpty || v[u].y == kHotEmpty || v[u].z == kHotEmpty;
             if (hit) {
-              const int j = v[u].x == kk ? 0 : (v[u].y == kk ? 1 : (v[u].z == kk ? 2 : 3));
-              slot[u] = (rk[u] >> (8 * j)) & 0xffu;  // the bag's part is added below
+              const int j = v[u].x == kk ? 0 : (v[u].y == kk ? 1 : 2);
+              slot[u] = (v[u].w >> (8 * j)) & 0xffu;  // the bag's part is added below
               key[u] = sentinel;
             }
             pend[u] = !hit && !gap;
@@ -922,7 +920,6 @@ __global__ void fill_i32_kernel(int32_t* p, int32_t v, int64_t n) {
 struct HotSet {
   const uint32_t* filter;
   const uint32_t* set;
-  const uint8_t* rank;
   uint32_t mask;
   const int32_t* probes;
   uint16_t* slot;  // per position: its dense slot (rank and bag modulo 16), or kNoDenseSlot
@@ -942,13 +939,13 @@ tbe_status linearize_go(const tbe_tables* tb, const IndexArgs& ia, int weighted,
                        dim3(kBlock), 0, s,
                        static_cast<const IT*>(ia.indices), static_cast<const OT*>(ia.offsets), tb->meta,
                        tb->B, nbags, static_cast<int32_t>(ia.N), sentinel, skip_t, invalid_as_row0, hot.filter,
-                       hot.set, hot.rank, hot.mask, hot.probes, hot.slot, keys, pay, bag_of, n_eff);
+                       hot.set, hot.mask, hot.probes, hot.slot, keys, pay, bag_of, n_eff);
   else
     hipLaunchKernelGGL((linearize_kernel<IT, OT, false>), dim3(resident_grid(linearize_kernel<IT, OT, false>, work)),
                        dim3(kBlock), 0, s,
                        static_cast<const IT*>(ia.indices), static_cast<const OT*>(ia.offsets), tb->meta,
                        tb->B, nbags, static_cast<int32_t>(ia.N), sentinel, skip_t, invalid_as_row0, hot.filter,
-                       hot.set, hot.rank, hot.mask, hot.probes, hot.slot, keys, pay, bag_of, n_eff);
+                       hot.set, hot.mask, hot.probes, hot.slot, keys, pay, bag_of, n_eff);
   return check_launch("linearize");
 }
 
@@ -1086,7 +1083,7 @@ tbe_status launch_transpose(const tbe_tables* tb, const IndexArgs& ia, int weigh
   const uint32_t sentinel = static_cast<uint32_t>(tb->total_rows);
   tbe_status st;
   // the dense rows, picked from a sample of the lookups before the sort
-  HotSet hot{nullptr, nullptr, nullptr, 0u, nullptr, nullptr};
+  HotSet hot{nullptr, nullptr, 0u, nullptr, nullptr};
   if (dense) {
     ProfScope ps("dense_sample", s);
     const SortPlan& P = L.sample;
@@ -1105,7 +1102,7 @@ tbe_status launch_transpose(const tbe_tables* tb, const IndexArgs& ia, int weigh
       return st;
     if ((st = launch_dense_select(tb, ws, L, skip_table, s))) return st;
     hot = HotSet{reinterpret_cast<const uint32_t*>(ws + L.hot_bloom),
-                 reinterpret_cast<const uint32_t*>(ws + L.hot_set), reinterpret_cast<const uint8_t*>(ws + L.hot_rank),
+                 reinterpret_cast<const uint32_t*>(ws + L.hot_set),
                  static_cast<uint32_t>(L.hot_set_size - 1), counters + kHotProbe,
                  reinterpret_cast<uint16_t*>(ws + L.dense_slot)};
   }
