@@ -102,7 +102,7 @@ __global__ __launch_bounds__(kBlock) void dense_sample_kernel(
 // least min_len lookups become its dense rows, in ascending order; when more than kDenseRows
 // qualify, the kDenseRows longest (among equal lengths, the smaller keys).
 // Picked from the sorted sample (hot_set != NULL): their keys and ranks go into the key set
-// (linear probing; the most slot groups a lookup reads into *probe_max) and its filter.  Picked from
+// (linear probing over records; the most records a lookup reads into *probe_max) and its filter.  Picked from
 // the batch's own runs (long_flag != NULL): each slot's flag says whether the chunk and apply
 // kernels leave it to the dense path.
 __global__ __launch_bounds__(kBlock) void dense_select_kernel(
