@@ -381,6 +381,10 @@ __global__ __launch_bounds__(kHistThreads) void fwd_hist_kernel(
 }
 
 
+// One workgroup per kWavesPerBlock groups of bags, not a grid sized to what the CUs hold: the
+// dispatcher gives each slot that frees up the next workgroup, so CUs and waves that drew heavy
+// bags or slow rows do not set the kernel's end, while the workgroups still start in bag order
+// (skewed batch 2.50 -> 2.41 ms, uniform 1.56 -> 1.40 ms with the bag groups below).
 template <int DT, typename IT, typename OT, bool PSW, int VEC, typename ACC>
 tbe_status gather_go(const tbe_tables* tb, const void* W, const IndexArgs& ia, const float* psw,
                      float* out, int skip, int nt, int unroll, int group, int64_t* repair_counts, hipStream_t s) {
@@ -390,7 +394,7 @@ tbe_status gather_go(const tbe_tables* tb, const void* W, const IndexArgs& ia, c
   ProfScope ps("fwd_gather", s);
 #define TBE_FWD_LAUNCH(U, R)                                                                     \
   hipLaunchKernelGGL((fwd_gather_kernel<DT, IT, OT, PSW, VEC, ACC, U, R>),                       \
-                     dim3(resident_grid(fwd_gather_kernel<DT, IT, OT, PSW, VEC, ACC, U, R>, work)), \
+                     dim3(static_cast<int>(hmin(work, int64_t{1} << 30))),                         \
                      dim3(kBlock), 0, s, static_cast<const S*>(W),                                  \
                      const_cast<IT*>(static_cast<const IT*>(ia.indices)),                           \
                      static_cast<const OT*>(ia.offsets), psw, out, tb->meta, skip, nt, tb->B,         \
@@ -470,12 +474,11 @@ tbe_status launch_forward_gather(const tbe_tables* tb, const void* W, const Inde
   const int n_tables = skip_table >= 0 ? tb->T - 1 : tb->T;
   if (n_tables <= 0 || tb->B == 0) return TBE_OK;
   if (group < 1 || group > kWave) {
-    // automatic: about 8 steps per wave of a full grid, so that waves that drew heavy
-    // bags (wide tables, long bags) do not set the kernel's end
+    // automatic: the smallest power of two from 8 that keeps the launch within 65536
+    // workgroups (one group of bags a wave)
     const int64_t slots = static_cast<int64_t>(n_tables) * tb->B;
-    const int64_t full = static_cast<int64_t>(device_cu_count()) * 8 * kWavesPerBlock;
     group = 8;
-    while (group < kWave && slots >= static_cast<int64_t>(2 * group) * full * 8) group *= 2;
+    while (group < kWave && slots > static_cast<int64_t>(group) * kWavesPerBlock * 65536) group *= 2;
   }
   switch (tb->w_dtype) {
     case TBE_F32: return gather_dispatch_idx<0>(tb, W, ia, psw, out, skip_table, n_tables, unroll, group, rc, s);

@@ -124,9 +124,10 @@ typedef struct {
   int32_t pretransposed;   /* backward and tbe_transpose: 1 = the workspace already holds this batch's
                               transpose, written by tbe_forward_hoisted; the backward skips its own,
                               tbe_transpose only describes it (default 0) */
-  int32_t bags_per_wave;   /* forward: consecutive bags a wave takes per grid step, their offsets read
-                              in one load ("bags per program", blog section 2), 1..64; 0 (default):
-                              the power of two in [8, 64] that gives every wave about 8 steps */
+  int32_t bags_per_wave;   /* forward: consecutive bags one wave pools, their offsets read in one
+                              load ("bags per program", blog section 2), 1..64; 0 (default): the
+                              smallest power of two from 8 that keeps the launch within 65536
+                              workgroups */
   int32_t bwd_streams;     /* backward: 2 = long runs (chunks, apply, dense rows) on the library's
                               second stream, concurrent with the short runs; 1 = one stream;
                               0 (default): 2 when the tables' widths fall in two or more short-run
