@@ -45,6 +45,9 @@ int resident_grid(K* kernel, int64_t work_blocks, size_t dyn_lds = 0, int thread
   return static_cast<int>(hmax(1, hmin(work_blocks, cap)));
 }
 
+// MI355X's Infinity Cache (the last level before HBM)
+constexpr int64_t kInfinityCacheBytes = int64_t{256} << 20;
+
 // Radix sort geometry (least-significant digit first, up to 9 bits a pass)
 constexpr int kRadixMaxBits = 9;
 constexpr int kRadixDigits = 1 << kRadixMaxBits;
