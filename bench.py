@@ -399,11 +399,13 @@ def presort_sample(N: int):
     return True, 64 * -(-N // S)
 
 
-def radix_passes(total_rows: int, E=None, n_keys: int = 0):
+def radix_passes(total_rows: int, E=None, n_keys: int = 0, all_keys: bool = True):
     """Radix passes over keys in [0, total_rows] at up to 9 bits a pass.  With the tables' rows E
     and the keys sorted, the library's automatic choice: each table sorted on its own on the bits
     of its largest local row id when that takes fewer bits, there are at least 2 tables and at
-    most half as many tables as sort blocks (one per 4096-key tile, at most 4096)."""
+    most half as many tables as sort blocks (segments of whole 4096-key tiles, at most 4096
+    blocks, at least two tiles a block when that still leaves 1024 blocks and twice as many
+    blocks as tables, if the sort covers all n_keys: all_keys, no histogram table left out)."""
     kb = max(1, int(total_rows).bit_length())
     passes = -(-kb // 9)
     if E is None or len(E) < 2:
@@ -411,6 +413,9 @@ def radix_passes(total_rows: int, E=None, n_keys: int = 0):
     lb = max(1, int(max(E) - 1).bit_length())
     tiles = max(1, -(-int(n_keys) // 4096))
     want = min(4096, tiles)
+    two = (tiles + 1) // 2
+    if all_keys and want > two and two >= max(1024, 2 * len(E)):
+        want = two
     per = -(-tiles // want)
     nblk = -(-max(1, int(n_keys)) // (per * 4096))
     if 2 * len(E) <= nblk and lb < kb and -(-lb // 9) <= passes:
@@ -436,7 +441,7 @@ def algorithmic_bytes(bt: ti.Batch, st: dict, hoist: bool, dense_P: int = 24, pr
     hst = [p for p in per if p["hist"]]
     runs_N = sum(p["N"] for p in gen)              # keys the sort covers
     U = sum(p["U"] for p in gen)
-    passes = radix_passes(sum(bt.E), bt.E, bt.num_indices)
+    passes = radix_passes(sum(bt.E), bt.E, bt.num_indices, not any(p["hist"] for p in per))
     kept, U_kept = runs_N, U                       # keys and runs past the first radix pass
     if presort:
         kept -= sum(p["dense_lookups"] for p in gen)
@@ -527,7 +532,7 @@ def compulsory_bytes(bt: ti.Batch, st: dict, ab: dict, presort: bool = False):
             + sum(p["U"] * (3 * p["D"] * s_w + mom) for p in per))
     # the transpose (linearize's key and payload writes, the radix passes, run-length encoding,
     # classification, the pre-sort sample) and the long runs' partials (written, then read)
-    passes = radix_passes(sum(bt.E), bt.E, bt.num_indices)
+    passes = radix_passes(sum(bt.E), bt.E, bt.num_indices, not any(p["hist"] for p in per))
     step += (ab.get("linearize", 0) - st["N"] * s_i - st["TB"] * s_o
              + passes * (ab.get("radix_downsweep", 0) + ab.get("radix_upsweep", 0))
              + ab.get("rle", 0) + ab.get("classify", 0) + ab.get("dense_sample", 0)
