@@ -382,7 +382,7 @@ void tbe_config_default(tbe_config* cfg) {
   cfg->chunk = 256;
   cfg->hist_enable = 1;
   cfg->fwd_unroll = 4;
-  cfg->bwd_unroll = 2;
+  cfg->bwd_unroll = 8;
   cfg->sort_blocks = 0;
   cfg->bag_windows = 1;
   cfg->fused_long = 0;

@@ -112,7 +112,7 @@ typedef struct {
                               on MFMA forward, counts^T x grad_out on MFMA backward (default 1) */
   int32_t fwd_unroll;      /* forward row loads in flight per lane group: 2, 4 or 8 (default 4; the
                               fused id check takes 4 or 8) */
-  int32_t bwd_unroll;      /* long-run chunk gradient rows in flight per lane group: 2, 4 or 8 (default 2) */
+  int32_t bwd_unroll;      /* long-run chunk gradient rows in flight per lane group: 2, 4 or 8 (default 8) */
   int32_t sort_blocks;     /* workgroups of each radix pass (default 0 = automatic) */
   int32_t bag_windows;     /* long-run chunks are processed grouped by (table, bag window of their
                               first lookup), B / bag_windows bags per window, so that chunks that
