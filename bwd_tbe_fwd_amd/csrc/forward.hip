@@ -394,7 +394,7 @@ tbe_status gather_go(const tbe_tables* tb, const void* W, const IndexArgs& ia, c
   ProfScope ps("fwd_gather", s);
 #define TBE_FWD_LAUNCH(U, R)                                                                     \
   hipLaunchKernelGGL((fwd_gather_kernel<DT, IT, OT, PSW, VEC, ACC, U, R>),                       \
-                     dim3(static_cast<int>(hmin(work, int64_t{1} << 30))),                         \
+                     dim3(static_cast<int>(hmax(1, hmin(work, int64_t{1} << 30)))),                \
                      dim3(kBlock), 0, s, static_cast<const S*>(W),                                  \
                      const_cast<IT*>(static_cast<const IT*>(ia.indices)),                           \
                      static_cast<const OT*>(ia.offsets), psw, out, tb->meta, skip, nt, tb->B,         \

@@ -938,13 +938,13 @@ tbe_status linearize_go(const tbe_tables* tb, const IndexArgs& ia, int weighted,
   // share the CUs as they come (skewed 0.52 -> 0.50 ms; hoisted step 9.25 -> 9.22 ms)
   ProfScope ps("linearize", s);
   if (weighted)
-    hipLaunchKernelGGL((linearize_kernel<IT, OT, true>), dim3(static_cast<int>(hmin(work, int64_t{1} << 30))),
+    hipLaunchKernelGGL((linearize_kernel<IT, OT, true>), dim3(static_cast<int>(hmax(1, hmin(work, int64_t{1} << 30)))),
                        dim3(kBlock), 0, s,
                        static_cast<const IT*>(ia.indices), static_cast<const OT*>(ia.offsets), tb->meta,
                        tb->B, nbags, static_cast<int32_t>(ia.N), sentinel, skip_t, invalid_as_row0, hot.filter,
                        hot.set, hot.mask, hot.probes, hot.slot, keys, pay, bag_of, n_eff);
   else
-    hipLaunchKernelGGL((linearize_kernel<IT, OT, false>), dim3(static_cast<int>(hmin(work, int64_t{1} << 30))),
+    hipLaunchKernelGGL((linearize_kernel<IT, OT, false>), dim3(static_cast<int>(hmax(1, hmin(work, int64_t{1} << 30)))),
                        dim3(kBlock), 0, s,
                        static_cast<const IT*>(ia.indices), static_cast<const OT*>(ia.offsets), tb->meta,
                        tb->B, nbags, static_cast<int32_t>(ia.N), sentinel, skip_t, invalid_as_row0, hot.filter,

@@ -196,3 +196,18 @@ def test_transpose_by_table_many_tables():
     g, _ = check_transpose(bt, False, tbe.make_config(), what="600 tables")
     # automatic: 15 bits of the largest local row id take 2 passes, 24 bits of linearized ids 3
     assert g["view"].sorted_by_table == 1 and g["view"].radix_passes == 2
+
+
+@pytest.mark.parametrize("weighted", [False, True])
+def test_transpose_without_bags(weighted):
+    """B = 0 with lookups present: no bag covers any position, so nothing is sorted and no run
+    is found (the linearize launch still has its one workgroup)."""
+    t = tbe.Tables([50, 70], [16, 32], 0, torch.float16, device="cuda")
+    idx = torch.tensor([3, 1, 4, 1, 5], dtype=torch.int64, device="cuda")
+    off = torch.zeros(1, dtype=torch.int64, device="cuda")
+    ws = tbe.workspace(tbe.tbe_backward_workspace_bytes(t, idx.numel(), weighted))
+    view = tbe.tbe_transpose(t, idx, off, weighted, ws)
+    torch.cuda.synchronize()
+    cnt = tbe.device_view(view.counters, 16, torch.int32, ws).cpu().numpy()
+    assert cnt[tbe.COUNTER_RUNS] == 0 and cnt[tbe.COUNTER_LONG] == 0 and cnt[tbe.COUNTER_CHUNKS] == 0
+    assert all(cnt[tbe.COUNTER_SHORT0 + b] == 0 for b in range(tbe.NUM_BUCKETS))
