@@ -336,8 +336,8 @@ def batch_stats(bt: ti.Batch, hist_table: int, threshold=256, chunk=256, dense_m
                 dense_rows=128):
     """Host-side statistics of the drawn batch (from the inputs only), per table.  hist_table
     (or -1): the table whose backward goes through the histogram kernels, not the runs.  The
-    dense hot rows are picked as the library does after the sort: per eligible table (no
-    per-sample weights, 16 <= D <= 128, D % 16 == 0, not the histogram table), its long runs of
+    dense hot rows are picked as the library does after the sort: per eligible table (16 <= D
+    <= 128, D % 16 == 0, not the histogram table), its long runs of
     at least dense_min lookups, the dense_rows longest when more qualify (among equal lengths
     the smaller keys; dense_min 0: none).  The library's pre-sort pick counts a sample
     instead, so rows near the cut may differ."""
@@ -356,7 +356,7 @@ def batch_stats(bt: ti.Batch, hist_table: int, threshold=256, chunk=256, dense_m
         # bags whose gradient slice a short run / a chunked long run reads at least once
         cnt_row = np.bincount(lk, minlength=bt.E[t])
         bag = np.repeat(np.arange(B, dtype=np.int64), lens)
-        ok = (dmin > 0 and bt.psw is None and 16 <= D <= 128 and D % 16 == 0 and t != hist_table)
+        ok = (dmin > 0 and 16 <= D <= 128 and D % 16 == 0 and t != hist_table)
         cand = np.flatnonzero(lg & (c >= dmin)) if ok else np.zeros(0, dtype=np.int64)  # key order
         if cand.size > dense_rows:   # the longest; among equal lengths the smaller keys
             cand = np.sort(cand[np.lexsort((cand, -c[cand]))[:dense_rows]])
@@ -468,9 +468,9 @@ def algorithmic_bytes(bt: ti.Batch, st: dict, hoist: bool, dense_P: int = 24, pr
         "long_apply": sum(p["gen_chunks"] * p["D"] * 4 + p["gen_long_runs"] * (20 + 2 * p["D"] * s_w + 8)
                           for p in gen),
         # per table with dense rows: its ids (with the pre-sort pick the two dense-slot bytes
-        # instead), offsets and B x D gradient slice, and its partials (P per table, one row of
-        # D floats per dense row each)
-        "dense_partial": sum(p["N"] * (2 if presort else s_i) + B * (s_o + p["D"] * 4)
+        # instead; with per-sample weights also the weights), offsets and B x D gradient slice,
+        # and its partials (P per table, one row of D floats per dense row each)
+        "dense_partial": sum(p["N"] * ((2 if presort else s_i) + s_p) + B * (s_o + p["D"] * 4)
                              + dense_P * p["dense_rows"] * p["D"] * 4 for p in gen if p["dense_rows"]),
         # per dense row: its P partial rows, weight row r/w, state r/w
         "dense_apply": sum(p["dense_rows"] * (dense_P * p["D"] * 4 + 2 * p["D"] * s_w + 8) for p in gen),
@@ -564,8 +564,9 @@ def mfma_flops(bt: ti.Batch, st: dict):
     dense = [p for p in st["per_table"] if p["dense_rows"]]
     if dense:
         # per table and 64-bag step: ceil(rows / 16) row tiles x 64 bags x 128 columns, three
-        # bf16 parts of the gradient
-        out["dense_partial"] = (sum(((B + 63) // 64) * ((p["dense_rows"] + 15) // 16) * 16 * 64 * 128 * 2 * 3
+        # bf16 parts of the gradient (with per-sample weights times three parts of the weight sums)
+        parts = 9 if bt.psw is not None else 3
+        out["dense_partial"] = (sum(((B + 63) // 64) * ((p["dense_rows"] + 15) // 16) * 16 * 64 * 128 * 2 * parts
                                     for p in dense), "bf16")
     return out
 

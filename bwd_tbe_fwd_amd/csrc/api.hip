@@ -231,7 +231,7 @@ BwdLayout bwd_layout(const tbe_tables* tb, int64_t N, int weighted, const Config
     L.hist_count = c.take(static_cast<size_t>(kHistBwdBlocks) * 64 * 4);
     L.hist_saved = c.take(static_cast<size_t>((tb->B + 15) / 16 * 16) * 64 * 2);
   }
-  if (cfg.dense_min > 0 && !weighted && !cfg.fused_long && tb->B > 0) {
+  if (cfg.dense_min > 0 && !cfg.fused_long && tb->B > 0) {
     // partials per table: about 2048 workgroups in all, at most 64 a table, at most one per
     // 64-bag step
     const int64_t steps = (static_cast<int64_t>(tb->B) + 63) / 64;
@@ -767,7 +767,10 @@ static tbe_status backward_common(const tbe_tables* tables, void* weights, float
   int buckets = 0;
   for (int b = 0; b < TBE_NUM_BUCKETS; ++b) buckets += L.cap_short[b] > 0;
   const int streams = cfg.bwd_streams ? cfg.bwd_streams : (buckets >= 2 ? 2 : 1);
-  const bool beside = cfg.bwd_streams == 0 && streams < 2 && ((L.dense_on && L.dense_presort) || hist >= 0);
+  // (with per-sample weights the dense rows run on the short runs' stream or after the long runs:
+  // the shared-counter short-run grids serve unweighted batches only)
+  const bool beside =
+      cfg.bwd_streams == 0 && streams < 2 && ((L.dense_on && L.dense_presort && !psw) || hist >= 0);
   if (hist >= 0 && !beside) {
     // with the hoisted forward's state, its saved counts replace counting the first 256 ids
     const uint16_t* saved = cfg.pretransposed ? reinterpret_cast<const uint16_t*>(ws + L.hist_saved) : nullptr;
@@ -775,7 +778,7 @@ static tbe_status backward_common(const tbe_tables* tables, void* weights, float
                                              saved, s))
       return st;
   }
-  const bool side_dense = L.dense_on && L.dense_presort;
+  const bool side_dense = L.dense_on && L.dense_presort && !psw;
   if (beside) {
     // the histogram table's backward and the dense rows' kernels (matrix cores and LDS
     // counting) on the second stream, launched first with one workgroup per CU, beside the
@@ -797,7 +800,7 @@ static tbe_status backward_common(const tbe_tables* tables, void* weights, float
       reserve = hmax(reserve, (512 + hist_partial_blocks_per_cu() - 1) / hist_partial_blocks_per_cu());
     }
     if (!st && side_dense) {
-      st = launch_dense_backward(tables, weights, momentum, opt, ia, grad_out, lr, eps, ws, L, fork.side(), 1);
+      st = launch_dense_backward(tables, weights, momentum, opt, ia, psw, grad_out, lr, eps, ws, L, fork.side(), 1);
       reserve = hmax(reserve, (512 + dense_partial_blocks_per_cu() - 1) / dense_partial_blocks_per_cu());
     }
     Config c2 = cfg;
@@ -811,7 +814,7 @@ static tbe_status backward_common(const tbe_tables* tables, void* weights, float
                                   s, side_dense ? fork.side() : s);
     // dense rows picked from the long runs after the sort: after the chunk kernels on s
     if (!st && L.dense_on && !L.dense_presort)
-      st = launch_dense_backward(tables, weights, momentum, opt, ia, grad_out, lr, eps, ws, L, s);
+      st = launch_dense_backward(tables, weights, momentum, opt, ia, psw, grad_out, lr, eps, ws, L, s);
     const tbe_status st_j = fork.join();
     return st ? st : st_j;
   }
@@ -819,7 +822,7 @@ static tbe_status backward_common(const tbe_tables* tables, void* weights, float
     if (tbe_status st = launch_backward_update(tables, weights, momentum, opt, psw, grad_out, lr, eps, ws,
                                                L, final_buf, cfg, s, s))
       return st;
-    return L.dense_on ? launch_dense_backward(tables, weights, momentum, opt, ia, grad_out, lr, eps, ws, L, s)
+    return L.dense_on ? launch_dense_backward(tables, weights, momentum, opt, ia, psw, grad_out, lr, eps, ws, L, s)
                       : TBE_OK;
   }
   // long runs (and the dense rows) on a second stream, concurrent with the short runs
@@ -829,7 +832,7 @@ static tbe_status backward_common(const tbe_tables* tables, void* weights, float
   tbe_status st = launch_backward_update(tables, weights, momentum, opt, psw, grad_out, lr, eps, ws, L,
                                          final_buf, cfg, s, fork.side());
   if (!st && L.dense_on)
-    st = launch_dense_backward(tables, weights, momentum, opt, ia, grad_out, lr, eps, ws, L, fork.side());
+    st = launch_dense_backward(tables, weights, momentum, opt, ia, psw, grad_out, lr, eps, ws, L, fork.side());
   const tbe_status st_j = fork.join();
   return st ? st : st_j;
 }

@@ -42,7 +42,9 @@
 // accumulator (8 x 2 tiles) stays in registers across the steps and is
 // written once as the workgroup's partial.  dense_apply sums a row's P
 // partials in a fixed order and applies SGD or row-wise Adagrad: results are
-// bitwise repeatable.
+// bitwise repeatable.  With per-sample weights the counts become per-bag sums
+// of the weights (see dense_partial_kernel), the same identity with each
+// lookup's gradient row scaled by its weight.
 #include "backward_launch.h"
 
 namespace tbe {
@@ -251,12 +253,19 @@ __device__ __forceinline__ int32_t wave_offsets(const OT* __restrict__ offsets, 
 // SLOTS: each lookup's row rank and bag come from dense_slot (two bytes a position, written
 // by linearize with the pre-sort pick) instead of its id, the filter, the search of the row
 // list and the search of the bag offsets.
-template <typename IT, typename OT, bool SLOTS>
+// WEIGHTED: a (row, bag) entry is the sum of the per-sample weights of the bag's lookups of the
+// row instead of their count, so that entry x gradient row is the sum of the weighted gradient
+// rows.  The lanes resolve their lookups' rows in parallel and stage (rank, weight) in LDS by
+// position; then one lane per bag adds its bag's staged weights in position order (no atomics:
+// every sum is formed in one fixed order).  The sums, fp32 values, are split into three bf16
+// parts as the gradient is: each of the nine part products is exact, and only the fp32 sums
+// round.
+template <typename IT, typename OT, bool SLOTS, bool WEIGHTED>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void dense_partial_kernel(
     const IT* __restrict__ indices, const OT* __restrict__ offsets, const float* __restrict__ grad_out,
     const int64_t* __restrict__ meta, int32_t B, int32_t out_width, int64_t N, int P,
     const int32_t* __restrict__ dense_rows, const int32_t* __restrict__ dense_cnt,
-    const uint16_t* __restrict__ dense_slot, float* __restrict__ partial) {
+    const uint16_t* __restrict__ dense_slot, const float* __restrict__ psw, float* __restrict__ partial) {
   constexpr int kStride = kDnBags + 4;   // counts [row][bag]; rows padded against bank conflicts
   constexpr int kBloomWords = 1024;      // 32768-bit filter of the selected rows (id mod 32768)
   // counts as fp32 (exact integers below 2^24): a count below 256 is then its own bf16 value
@@ -325,7 +334,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     // SLOTS: the first slot bytes are requested before the gradient, so that counting (which
     // waits only for them) overlaps the gradient's arrival
     uint32_t sl0[kDnLoads];
-    if constexpr (SLOTS) {
+    if constexpr (SLOTS && !WEIGHTED) {
 #pragma unroll
       for (int u = 0; u < kDnLoads; ++u) {
         const int32_t j = u * kWave + lane;
@@ -359,7 +368,54 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
       *reinterpret_cast<f32x4*>(&s_cnt[(x >> 2) * kStride + kDnWaveBags * w + 4 * (x & 3)]) = f32x4{0.f, 0.f, 0.f, 0.f};
     __builtin_amdgcn_wave_barrier();
     // every lookup of the wave's 16 bags that hits a selected row
-    if constexpr (SLOTS) {
+    if constexpr (WEIGHTED) {
+      // rounds of kDnLoads x 64 lookups: every lane resolves its lookups' rows and stages
+      // (row, weight) in LDS by position; then lane l < 16 adds bag l's staged weights in
+      // position order, from LDS
+      __shared__ uint2 s_stage[kWavesPerBlock][kDnLoads * kWave];
+      uint2* stage = s_stage[w];
+      for (int32_t j0 = 0; j0 < n; j0 += kDnLoads * kWave) {
+        int64_t r[kDnLoads];
+        float pw[kDnLoads];
+#pragma unroll
+        for (int u = 0; u < kDnLoads; ++u) {
+          const int32_t j = j0 + u * kWave + lane;
+          if constexpr (SLOTS) r[u] = j < n ? static_cast<int64_t>(dense_slot[o0 + j]) : kNoDenseSlot;
+          else r[u] = j < n ? static_cast<int64_t>(indices[o0 + j]) : -1;
+          pw[u] = j < n ? psw[o0 + j] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < kDnLoads; ++u) {
+          uint32_t k = 0xffffffffu;  // the row's rank, or none
+          if constexpr (SLOTS) {
+            const uint32_t rank = static_cast<uint32_t>(r[u]) & 0xffu;
+            if (rank < static_cast<uint32_t>(nd)) k = rank;
+          } else if (static_cast<uint64_t>(r[u]) < static_cast<uint64_t>(E)) {
+            const int32_t id = static_cast<int32_t>(r[u]);
+            const uint32_t h = static_cast<uint32_t>(id) & (32 * kBloomWords - 1);
+            if ((s_bloom[h >> 5] >> (h & 31)) & 1u) {
+              int kk = 0;  // largest kk with s_rows[kk] <= id (or 0)
+#pragma unroll
+              for (int step = kDenseRows / 2; step > 0; step >>= 1)
+                if (s_rows[kk + step] <= id) kk += step;
+              if (s_rows[kk] == id) k = static_cast<uint32_t>(kk);
+            }
+          }
+          stage[u * kWave + lane] = make_uint2(k, __builtin_bit_cast(uint32_t, pw[u]));
+        }
+        __builtin_amdgcn_wave_barrier();
+        if (lane < kDnWaveBags) {
+          float* col = &s_cnt[kDnWaveBags * w + lane];  // row k of this bag's column at k * kStride
+          const int32_t hi = min(off[lane + 1], j0 + kDnLoads * kWave);
+          for (int32_t j = max(off[lane], j0); j < hi; ++j) {
+            const uint2 e = stage[j - j0];
+            if (e.x < static_cast<uint32_t>(nd)) col[e.x * kStride] += __builtin_bit_cast(float, e.y);
+          }
+        }
+        __builtin_amdgcn_wave_barrier();  // the stage is read before the next round overwrites it
+      }
+    }
+    if constexpr (SLOTS && !WEIGHTED) {
       for (int32_t j0 = 0; j0 < n; j0 += kDnLoads * kWave) {
         uint32_t sl[kDnLoads];
 #pragma unroll
@@ -379,7 +435,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
         }
       }
     }
-    for (int32_t j0 = 0; !SLOTS && j0 < n; j0 += kDnLoads * kWave) {
+    for (int32_t j0 = 0; !SLOTS && !WEIGHTED && j0 < n; j0 += kDnLoads * kWave) {
       int64_t r[kDnLoads];
 #pragma unroll
       for (int u = 0; u < kDnLoads; ++u) {
@@ -436,7 +492,22 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
           const float* src = &s_cnt[(16 * mt + (lane & 15)) * kStride + 32 * kk + 8 * (lane >> 4)];
           const u32x4 c0 = *reinterpret_cast<const u32x4*>(src);
           const u32x4 c1 = *reinterpret_cast<const u32x4*>(src + 4);
-          if (!any_big) {
+          if constexpr (WEIGHTED) {
+            // the weight sums as three bf16 parts each, against the gradient's three parts
+            const uint32_t cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+            s16x8 ah, am, al;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              short h, mi, lo;
+              split3(__builtin_bit_cast(float, cv[j]), h, mi, lo);
+              ah[j] = h;
+              am[j] = mi;
+              al[j] = lo;
+            }
+            dense_mfma(acc[mt], __builtin_bit_cast(bf16x8, ah), bh, bm, bl);
+            dense_mfma(acc[mt], __builtin_bit_cast(bf16x8, am), bh, bm, bl);
+            dense_mfma(acc[mt], __builtin_bit_cast(bf16x8, al), bh, bm, bl);
+          } else if (!any_big) {
             // every count is below 256: the high halves of the fp32 counts are their bf16 values
             const u32x4 pk = {__builtin_amdgcn_perm(c0.y, c0.x, 0x07060302u),
                               __builtin_amdgcn_perm(c0.w, c0.z, 0x07060302u),
@@ -550,25 +621,29 @@ __global__ __launch_bounds__(kBlock) void dense_apply_kernel(
   if (act) store_vec4<DT>(wrow + c, wv);
 }
 
+template <typename IT, typename OT, bool SLOTS, bool WEIGHTED>
+void partial_launch(const tbe_tables* tb, const IndexArgs& ia, const float* grad_out, const float* psw,
+                    char* ws, const BwdLayout& L, int P, const uint16_t* slot, hipStream_t s) {
+  hipLaunchKernelGGL((dense_partial_kernel<IT, OT, SLOTS, WEIGHTED>), dim3(tb->T * P), dim3(kBlock), 0, s,
+                     static_cast<const IT*>(ia.indices), static_cast<const OT*>(ia.offsets), grad_out,
+                     tb->meta, tb->B, tb->out_width, ia.N, P,
+                     reinterpret_cast<const int32_t*>(ws + L.dense_rows),
+                     reinterpret_cast<const int32_t*>(ws + L.dense_cnt), slot, psw,
+                     reinterpret_cast<float*>(ws + L.dense_partial));
+}
+
 template <typename IT, typename OT>
-tbe_status partial_go(const tbe_tables* tb, const IndexArgs& ia, const float* grad_out, char* ws,
-                      const BwdLayout& L, int P, hipStream_t s) {
+tbe_status partial_go(const tbe_tables* tb, const IndexArgs& ia, const float* grad_out, const float* psw,
+                      char* ws, const BwdLayout& L, int P, hipStream_t s) {
   ProfScope ps("dense_partial", s);
   const uint16_t* slot = L.dense_presort ? reinterpret_cast<const uint16_t*>(ws + L.dense_slot) : nullptr;
-  if (slot)
-    hipLaunchKernelGGL((dense_partial_kernel<IT, OT, true>), dim3(tb->T * P), dim3(kBlock), 0, s,
-                       static_cast<const IT*>(ia.indices), static_cast<const OT*>(ia.offsets), grad_out,
-                       tb->meta, tb->B, tb->out_width, ia.N, P,
-                       reinterpret_cast<const int32_t*>(ws + L.dense_rows),
-                       reinterpret_cast<const int32_t*>(ws + L.dense_cnt), slot,
-                       reinterpret_cast<float*>(ws + L.dense_partial));
-  else
-    hipLaunchKernelGGL((dense_partial_kernel<IT, OT, false>), dim3(tb->T * P), dim3(kBlock), 0, s,
-                       static_cast<const IT*>(ia.indices), static_cast<const OT*>(ia.offsets), grad_out,
-                       tb->meta, tb->B, tb->out_width, ia.N, P,
-                       reinterpret_cast<const int32_t*>(ws + L.dense_rows),
-                       reinterpret_cast<const int32_t*>(ws + L.dense_cnt), nullptr,
-                       reinterpret_cast<float*>(ws + L.dense_partial));
+  if (slot) {
+    if (psw) partial_launch<IT, OT, true, true>(tb, ia, grad_out, psw, ws, L, P, slot, s);
+    else partial_launch<IT, OT, true, false>(tb, ia, grad_out, psw, ws, L, P, slot, s);
+  } else {
+    if (psw) partial_launch<IT, OT, false, true>(tb, ia, grad_out, psw, ws, L, P, slot, s);
+    else partial_launch<IT, OT, false, false>(tb, ia, grad_out, psw, ws, L, P, slot, s);
+  }
   return check_launch("dense_partial");
 }
 
@@ -640,26 +715,26 @@ tbe_status launch_dense_select_runs(const tbe_tables* tb, char* ws, const BwdLay
 }
 
 int dense_partial_blocks_per_cu() {
-  return blocks_per_cu(reinterpret_cast<const void*>(dense_partial_kernel<int64_t, int64_t, true>));
+  return blocks_per_cu(reinterpret_cast<const void*>(dense_partial_kernel<int64_t, int64_t, true, false>));
 }
 
 tbe_status launch_dense_backward(const tbe_tables* tb, void* W, float* momentum, int opt,
-                                 const IndexArgs& ia, const float* grad_out, float lr, float eps,
-                                 char* ws, const BwdLayout& L, hipStream_t s, int wgs_per_cu) {
+                                 const IndexArgs& ia, const float* psw, const float* grad_out, float lr,
+                                 float eps, char* ws, const BwdLayout& L, hipStream_t s, int wgs_per_cu) {
   // partials per table: as many workgroups as the GPU holds at once over all tables (one
   // round, no tail), or wgs_per_cu a CU, at most the workspace's dense_P
-  const int64_t resident =
-      static_cast<int64_t>(device_cu_count()) *
-      (wgs_per_cu > 0 ? wgs_per_cu
-                      : blocks_per_cu(reinterpret_cast<const void*>(dense_partial_kernel<int64_t, int64_t, false>)));
+  // (the weighted instance holds fewer workgroups a CU: registers and its LDS stage)
+  const void* k = psw ? reinterpret_cast<const void*>(dense_partial_kernel<int64_t, int64_t, false, true>)
+                      : reinterpret_cast<const void*>(dense_partial_kernel<int64_t, int64_t, false, false>);
+  const int64_t resident = static_cast<int64_t>(device_cu_count()) * (wgs_per_cu > 0 ? wgs_per_cu : blocks_per_cu(k));
   const int P = static_cast<int>(hmax(1, hmin(L.dense_P, resident / tb->T)));
   tbe_status st;
   if (ia.itype == TBE_I32)
-    st = ia.otype == TBE_I32 ? partial_go<int32_t, int32_t>(tb, ia, grad_out, ws, L, P, s)
-                             : partial_go<int32_t, int64_t>(tb, ia, grad_out, ws, L, P, s);
+    st = ia.otype == TBE_I32 ? partial_go<int32_t, int32_t>(tb, ia, grad_out, psw, ws, L, P, s)
+                             : partial_go<int32_t, int64_t>(tb, ia, grad_out, psw, ws, L, P, s);
   else
-    st = ia.otype == TBE_I32 ? partial_go<int64_t, int32_t>(tb, ia, grad_out, ws, L, P, s)
-                             : partial_go<int64_t, int64_t>(tb, ia, grad_out, ws, L, P, s);
+    st = ia.otype == TBE_I32 ? partial_go<int64_t, int32_t>(tb, ia, grad_out, psw, ws, L, P, s)
+                             : partial_go<int64_t, int64_t>(tb, ia, grad_out, psw, ws, L, P, s);
   if (st) return st;
 #define TBE_DA(DT) \
   (opt == kOptSGD ? apply_dense_go<DT, kOptSGD>(tb, W, momentum, ws, L, P, lr, eps, s) \

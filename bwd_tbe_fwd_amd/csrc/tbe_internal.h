@@ -193,10 +193,11 @@ tbe_status launch_dense_select(const tbe_tables* tb, char* ws, const BwdLayout& 
 // long-list slots
 tbe_status launch_dense_select_runs(const tbe_tables* tb, char* ws, const BwdLayout& L, int hist_t,
                                     const Config& cfg, hipStream_t s);
-// wgs_per_cu > 0: the partial kernel's grid is that many workgroups per CU (else as many as fit)
+// wgs_per_cu > 0: the partial kernel's grid is that many workgroups per CU (else as many as fit);
+// psw != NULL: the per-sample weights of the lookups
 tbe_status launch_dense_backward(const tbe_tables* tb, void* W, float* momentum, int opt,
-                                 const IndexArgs& ia, const float* grad_out, float lr, float eps,
-                                 char* ws, const BwdLayout& L, hipStream_t s, int wgs_per_cu = 0);
+                                 const IndexArgs& ia, const float* psw, const float* grad_out, float lr,
+                                 float eps, char* ws, const BwdLayout& L, hipStream_t s, int wgs_per_cu = 0);
 // workgroups per CU the dense partial kernel holds at once
 int dense_partial_blocks_per_cu();
 

@@ -138,11 +138,12 @@ typedef struct {
   int32_t tiny_runs;       /* backward: a wave step whose short runs all have at most this many
                               lookups serves twice as many runs with half the lanes each (rows of
                               64 .. 256 columns); default 8, 0: off */
-  int32_t dense_min;       /* backward without per-sample weights: per table (16 <= D <= 128,
-                              D % 16 == 0, not the histogram table), its rows of at least this
-                              many lookups (the 128 with the most when more qualify; among equal
-                              counts the smaller row ids) are updated from per-bag counts x
-                              grad_out on MFMA instead of through the sorted runs (default 1024;
+  int32_t dense_min;       /* backward: per table (16 <= D <= 128, D % 16 == 0, not the
+                              histogram table), its rows of at least this many lookups (the 128
+                              with the most when more qualify; among equal counts the smaller row
+                              ids) are updated from per-bag counts (with per-sample weights: per-bag
+                              sums of the weights) x grad_out on MFMA instead of through the
+                              sorted runs (default 1024;
                               values below long_threshold act as long_threshold; 0: off; off
                               with fused_long) */
   int32_t dense_presort;   /* backward with dense_min: 1 = the dense rows are picked before the
@@ -332,11 +333,12 @@ size_t tbe_backward_workspace_bytes(const tbe_tables* tables, int64_t num_indice
  * set, there are no per-sample weights and tables->hist_table >= 0, that
  * table's rows take their gradient from per-bag lookup counts times grad_out
  * on MFMA (blog section 2, forward-state reuse) and its lookups stay out of the
- * sort; the other tables go through the sorted runs.  With dense_min > 0 and no
- * per-sample weights, each eligible table's rows of at least dense_min lookups
- * (up to 128 a table; see dense_presort for how they are counted) take the same
- * counts x grad_out route on bf16 MFMA with an exact three-part split of the
- * gradient; the step is the same up to the order of the fp32 sums.
+ * sort; the other tables go through the sorted runs.  With dense_min > 0, each
+ * eligible table's rows of at least dense_min lookups (up to 128 a table; see
+ * dense_presort for how they are counted) take the same counts x grad_out route
+ * on bf16 MFMA with an exact three-part split of the gradient (with per-sample
+ * weights, per-bag sums of the weights, also split in three parts, in place of
+ * the counts); the step is the same up to the order of the fp32 sums.
  */
 tbe_status tbe_backward_sgd(const tbe_tables* tables, void* weights, const void* indices,
                             int32_t index_type, const void* offsets, int32_t offset_type,

@@ -153,9 +153,30 @@ def test_dense_rows_bag_counts(B):
     run_and_check(bt, _cfg(16), what=f"dense B={B}")
 
 
-def test_dense_rows_off_with_per_sample_weights():
-    bt = ti.make_batch(_spec(weighted=True, B=400), 85)
-    run_and_check(bt, _cfg(16), what="dense weighted (off)")
+@pytest.mark.parametrize("w_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("optimizer", ["sgd", "rowwise_adagrad"])
+@pytest.mark.parametrize("presort", PRESORT)
+def test_dense_rows_with_per_sample_weights(w_dtype, optimizer, presort):
+    """Per-sample weights: a dense row takes, per bag, the sum of the weights of the bag's
+    lookups of it in place of their count (one lane a bag, in position order), in three exact
+    bf16 parts against the gradient's three.  The step matches the oracle and repeats bit for
+    bit; with fp32 weights it also differs in its low bits from the chunk path, so the dense
+    path ran."""
+    bt = ti.make_batch(_spec(w_dtype=w_dtype, optimizer=optimizer, weighted=True, B=400), 85)
+    what = f"dense weighted {w_dtype} {optimizer} presort={presort}"
+    flush_print(what)
+    run_and_check(bt, _cfg(16, presort), what=what)
+    outs = []
+    for dm in (16, 16, 0):
+        db = DevBatch(bt)
+        W, mom = db.backward(_cfg(dm, presort))
+        torch.cuda.synchronize()
+        outs.append((W.cpu(), None if mom is None else mom.cpu()))
+    assert torch.equal(outs[0][0].view(torch.uint8), outs[1][0].view(torch.uint8)), what
+    if outs[0][1] is not None:
+        assert torch.equal(outs[0][1], outs[1][1]), what
+    if w_dtype == torch.float32:
+        assert not torch.equal(outs[0][0].view(torch.int32), outs[2][0].view(torch.int32)), what
 
 
 @pytest.mark.parametrize("L", [300, 70000])
@@ -281,8 +302,9 @@ def test_dense_rows_are_the_longest_128(presort):
 @pytest.mark.parametrize("seed", [1, 2])
 def test_dense_rows_random_shapes(seed):
     """Seeded random shapes through both picks: table sizes from 2 rows up, widths in and out
-    of the dense path's range, every weight and index type, thresholds and chunk sizes, one
-    or two streams; every step checked against the oracle."""
+    of the dense path's range, every weight and index type, with and without per-sample
+    weights, thresholds and chunk sizes, one or two streams; every step checked against the
+    oracle."""
     rng = np.random.default_rng(seed)
     for it in range(30):
         T = int(rng.integers(1, 6))
@@ -298,13 +320,14 @@ def test_dense_rows_random_shapes(seed):
                             w_range=0.05, optimizer=["sgd", "rowwise_adagrad"][int(rng.integers(0, 2))],
                             itype=[torch.int32, torch.int64][int(rng.integers(0, 2))],
                             otype=[torch.int32, torch.int64][int(rng.integers(0, 2))])
-        bt = ti.make_batch(spec, 1000 * seed + it)
         cfg = tbe.make_config(long_threshold=int(rng.choice([16, 32, 256])),
                               chunk=int(rng.choice([8, 16, 256])),
                               dense_min=int(rng.choice([16, 24, 40, 100])),
                               dense_presort=int(rng.choice([1, -1])),
                               bwd_streams=int(rng.choice([0, 1, 2])))
-        run_and_check(bt, cfg, what=f"{spec.name}: {bt.indices.numel()} lookups")
+        spec = spec.replace(weighted=bool(rng.random() < 0.4))
+        bt = ti.make_batch(spec, 1000 * seed + it)
+        run_and_check(bt, cfg, what=f"{spec.name} weighted={spec.weighted}: {bt.indices.numel()} lookups")
 
 
 @pytest.mark.parametrize("seed", [3, 4])
