@@ -261,7 +261,7 @@ __device__ __forceinline__ int32_t wave_offsets(const OT* __restrict__ offsets, 
 // parts as the gradient is: each of the nine part products is exact, and only the fp32 sums
 // round.
 template <typename IT, typename OT, bool SLOTS, bool WEIGHTED>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void dense_partial_kernel(
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(WEIGHTED ? 2 : 3))) void dense_partial_kernel(
     const IT* __restrict__ indices, const OT* __restrict__ offsets, const float* __restrict__ grad_out,
     const int64_t* __restrict__ meta, int32_t B, int32_t out_width, int64_t N, int P,
     const int32_t* __restrict__ dense_rows, const int32_t* __restrict__ dense_cnt,
