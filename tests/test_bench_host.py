@@ -104,6 +104,22 @@ def test_mfma_flops():
     assert nd >= 1 and fl["dense_partial"] == (5 * ((nd + 15) // 16) * 16 * 64 * 128 * 2 * 3, "bf16")
 
 
+def test_weighted_batches_take_dense_rows():
+    """With per-sample weights the dense rows are picked as without (per-bag sums of the weights
+    replace the counts): the same rows, the weights read besides the ids, and nine bf16 part
+    products per tile instead of three (no histogram table: it does not take weighted calls)."""
+    plain = ti.make_batch(_spec(), 4, device="cpu")
+    wtd = ti.make_batch(_spec().replace(weighted=True), 4, device="cpu")
+    sp, sw = bench.batch_stats(plain, hist_table=-1), bench.batch_stats(wtd, hist_table=-1)
+    assert [p["dense_rows"] for p in sw["per_table"]] == [p["dense_rows"] for p in sp["per_table"]]
+    assert sum(p["dense_rows"] for p in sw["per_table"]) > 0
+    fp, fw = bench.mfma_flops(plain, sp), bench.mfma_flops(wtd, sw)
+    assert fw["dense_partial"][0] == 3 * fp["dense_partial"][0]
+    ap = bench.algorithmic_bytes(plain, sp, hoist=False, dense_P=4)
+    aw = bench.algorithmic_bytes(wtd, sw, hoist=False, dense_P=4)
+    assert aw["dense_partial"] - ap["dense_partial"] == 4 * sum(p["N"] for p in sw["per_table"] if p["dense_rows"])
+
+
 def test_presort_sample_and_bytes():
     """The pre-sort pick: from 2^26 lookups on, at most 2^20 sampled keys (64 in every power of
     two S); the dense rows' lookups leave the radix passes after the first, and the runs."""
