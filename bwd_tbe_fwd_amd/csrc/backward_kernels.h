@@ -54,14 +54,14 @@ __device__ __forceinline__ void short_run_one(
     const int col = p * 4 * LPR + c * 4;
     act[p] = col < D;
     if (act[p]) {
-      load_vec<DT, 4>(wrow + col, w[p]);
+      load_vec<DT, 4, true>(wrow + col, w[p]);  // read once, written back below
     } else {
 #pragma unroll
       for (int q = 0; q < 4; ++q) w[p][q] = 0.f;
     }
   }
   float mom = 0.f;
-  if constexpr (OPT == kOptAdagrad) mom = momentum[key];
+  if constexpr (OPT == kOptAdagrad) mom = __builtin_nontemporal_load(momentum + key);
   float acc[NP][4];
 #pragma unroll
   for (int p = 0; p < NP; ++p)
@@ -134,11 +134,11 @@ __device__ __forceinline__ void short_run_one(
     for (int p = 0; p < NP; ++p)
 #pragma unroll
       for (int q = 0; q < 4; ++q) w[p][q] -= lr * acc[p][q] / denom;
-    if (c == 0) momentum[key] = mnew;
+    if (c == 0) store_pol<true>(momentum + key, mnew);  // written once, not read back here
   }
 #pragma unroll
   for (int p = 0; p < NP; ++p)
-    if (act[p]) store_vec4<DT>(wrow + p * 4 * LPR + c * 4, w[p]);
+    if (act[p]) store_vec4<DT, true>(wrow + p * 4 * LPR + c * 4, w[p]);
 }
 
 constexpr int kShortGrab = 16;  // wave steps a short-run wave takes from the shared counter at once

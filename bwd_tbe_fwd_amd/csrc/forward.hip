@@ -171,7 +171,7 @@ void fwd_gather_kernel(
           for (int i = 0; i < VEC; i += 4) {
             f32x4 o = {static_cast<float>(acc[i]), static_cast<float>(acc[i + 1]),
                        static_cast<float>(acc[i + 2]), static_cast<float>(acc[i + 3])};
-            store_f4(orow + col + i, o);
+            store_f4_stream(orow + col + i, o);  // the pooled rows are not read back here
           }
         }
       }
@@ -368,7 +368,7 @@ __global__ __launch_bounds__(kHistThreads) void fwd_hist_kernel(
       for (int x = lane; x < nbag * c4n; x += kWave) {
         const int i = x / c4n, c4 = x - i * c4n;
         const f32x4 v = *reinterpret_cast<const f32x4*>(&otile[i * kHistStride + 4 * c4]);
-        store_f4(out + (b0 + i) * out_width + col_base + c0 + 4 * c4, v);
+        store_f4_stream(out + (b0 + i) * out_width + col_base + c0 + 4 * c4, v);
       }
       __builtin_amdgcn_wave_barrier();
     }
