@@ -222,7 +222,7 @@ constexpr int kHistWStride = kHistRows + 4;
 constexpr int kHistStride = kHistRows + 4;
 
 template <typename IT, typename OT, bool REPAIR>
-__global__ __launch_bounds__(kHistThreads) void fwd_hist_kernel(
+__global__ __launch_bounds__(kHistThreads) __attribute__((amdgpu_waves_per_eu(6))) void fwd_hist_kernel(
     const uint16_t* __restrict__ Wt, IT* __restrict__ indices, const OT* __restrict__ offsets,
     float* __restrict__ out, int64_t bag0, int32_t B, int32_t E, int32_t D, int64_t col_base,
     int32_t out_width, int64_t N, int64_t* __restrict__ counts, uint16_t* __restrict__ save_counts) {
@@ -270,15 +270,27 @@ __global__ __launch_bounds__(kHistThreads) void fwd_hist_kernel(
     __builtin_amdgcn_wave_barrier();
     // each bag's first 256 ids, read as one coalesced range with kHistLoads loads in
     // flight per lane; positions only grow, so a lane's bag search continues from its last
-    // bag (off[16] = n ends it)
+    // bag (off[16] = n ends it).  The next round's ids are requested before this round is
+    // counted, so a tile waits on one load latency instead of one a round.
     int bcur = 0;
-    for (int32_t j0 = 0; j0 < n; j0 += kHistLoads * kWave) {
-      int64_t r[kHistLoads];
+    int64_t rn[kHistLoads];  // the round in flight
+    int32_t r[kHistLoads];   // the round being counted: its rows, -1 for an id outside the table
+    auto fetch = [&](int32_t j0) {
 #pragma unroll
       for (int u = 0; u < kHistLoads; ++u) {
         const int32_t j = j0 + u * kWave + lane;
-        r[u] = j < n ? static_cast<int64_t>(indices[o0 + j]) : 0;
+        rn[u] = j < n ? static_cast<int64_t>(indices[o0 + j]) : 0;
       }
+    };
+    auto take = [&]() {
+#pragma unroll
+      for (int u = 0; u < kHistLoads; ++u)
+        r[u] = static_cast<uint64_t>(rn[u]) < static_cast<uint64_t>(E) ? static_cast<int32_t>(rn[u]) : -1;
+    };
+    fetch(0);
+    take();
+    for (int32_t j0 = 0; j0 < n; j0 += kHistLoads * kWave) {
+      if (j0 + kHistLoads * kWave < n) fetch(j0 + kHistLoads * kWave);
 #pragma unroll
       for (int u = 0; u < kHistLoads; ++u) {
         const int32_t j = j0 + u * kWave + lane;
@@ -286,20 +298,19 @@ __global__ __launch_bounds__(kHistThreads) void fwd_hist_kernel(
           while (off[bcur + 1] <= j) ++bcur;
           const int b = bcur;
           if (j - off[b] < kHistHead) {
-            int64_t row = r[u];
-            if (static_cast<uint64_t>(row) >= static_cast<uint64_t>(E)) {
+            int32_t row = r[u];
+            if (row < 0) {
               if constexpr (REPAIR) {  // repaired to row 0, in place, and counted
                 indices[o0 + j] = 0;
                 ++fixed;
                 row = 0;
-              } else {
-                row = -1;  // contributes nothing
               }
             }
-            if (row >= 0) atomicAdd(&cnt[b * kHistStride + static_cast<int>(row)], 1u);
+            if (row >= 0) atomicAdd(&cnt[b * kHistStride + row], 1u);
           }
         }
       }
+      take();
     }
     __builtin_amdgcn_wave_barrier();
     if (save_counts) {  // 16 bags x 64 rows as u16 (the padding bags of the last tile hold zeros)
